@@ -1,0 +1,476 @@
+"""The CPU oracle: a plain interpreter that evaluates one primitive per graph
+node, materialising every node's value, with no fusion.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import or run anything under ``oracle/``. The library's
+compute path never does, and this module imports nothing from the library.
+
+What it follows:
+  * limn README, "Architecture": the numpy device interprets the graph one
+    numpy call per node with no fusion and is the reference every compiled
+    backend is diffed against; a matmul is a broadcast multiply and a reduce,
+    so the (m, n, k) intermediate is built rather than walked.
+  * limn README, "Architecture" (third rule) and "Reading the schedule": a
+    View is (shape, strides, offset, mask); reshape, permute, expand, pad and
+    shrink compose into it; a padded read is a range check on a loop
+    variable that yields a literal zero outside the range.
+  * limn README, "The op set": the primitive set and the dtype rules
+    (float16/bfloat16 are storage widths widened to compute; a reduce keeps a
+    float32 running total and rounds back once; narrow ints wrap modulo
+    2**width).
+  * limn README, "Reading the schedule" and "Backends": a reduce walks its
+    axis in order from the reduce identity.
+
+Readings where the pages leave a step open (each is listed in the design
+notes of the repository):
+  * float32 arithmetic is IEEE round-to-nearest-even per primitive; EXP and
+    LOG are evaluated in float64 and rounded once to float32 (correctly
+    rounded but for ties closer than 2**-29 ulp); SQRT and RECIP are the
+    correctly rounded float32 operations.
+  * a reduce folds in ascending row-major order over its reduce indices.
+  * a float32 running total whose length n has (n - 1) * 2**-24 >= 1/3 (the
+    point where the reduction-order bound gamma_{n-1} stops meaning
+    anything; Litmus README, "Support map and limits", item 7) is kept in
+    float64 instead and rounded once.
+  * CMPLT produces int8 0/1; WHERE treats any nonzero condition as true.
+  * MAX starts from -inf (ints: the smallest value of the width) and a NaN
+    anywhere in the row gives NaN.
+  * float -> bfloat16 CAST rounds to nearest even and keeps NaN a NaN;
+    float -> int truncates toward zero.
+  * a node too large to hold (the limn README warns that the reference runs
+    out of memory on a large matmul) is evaluated in slabs along dim 0 when
+    its consumer is a reduce that keeps dim 0. This changes no value: each
+    output cell is still produced by the same in-order fold.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_fold.so")
+
+STORAGE = {
+    "f32": np.float32, "f64": np.float64, "f16": np.float16, "bf16": np.uint16,
+    "i32": np.int32, "i16": np.int16, "i8": np.int8,
+}
+FLOATS = ("f32", "f64", "f16", "bf16")
+INTS = ("i32", "i16", "i8")
+ELEMENTWISE = ("NEG", "EXP", "LOG", "SQRT", "RECIP", "CAST", "ADD", "MUL", "CMPLT", "WHERE")
+
+
+class OracleError(Exception):
+    """A graph the oracle refuses (shape, dtype or op contract)."""
+
+
+# ---------------------------------------------------------------------------
+# the C folds
+# ---------------------------------------------------------------------------
+_lib = None
+
+
+def _fold_lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise OracleError(f"{_LIB_PATH} is not built; run oracle/build.py")
+        lib = ctypes.CDLL(_LIB_PATH)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        for name in ("fold_sum_f32", "fold_sum_f32_wide", "fold_sum_f32_to_f64", "fold_sum_f64",
+                     "fold_sum_i32", "fold_max_f32", "fold_max_f64"):
+            getattr(lib, name).argtypes = [p, i64, i64, p]
+            getattr(lib, name).restype = None
+        lib.fold_max_i32.argtypes = [p, i64, i64, ctypes.c_int32, p]
+        lib.fold_max_i32.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 <-> float32 (bfloat16 is the top half of a float32)
+# ---------------------------------------------------------------------------
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening: the 16 bits become the high half of a float32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32)
+
+
+def f32_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16, nearest with ties to even; NaN stays NaN
+    (quiet bit set), overflow rounds to infinity."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) & np.uint64(0xFFFF)
+    is_nan = (u & np.uint64(0x7FFFFFFF)) > np.uint64(0x7F800000)
+    r = np.where(is_nan, ((u >> np.uint64(16)) | np.uint64(0x0040)) & np.uint64(0xFFFF), r)
+    return r.astype(np.uint16)
+
+
+def _widen(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage -> compute width: float32 for the half widths, else itself."""
+    if dtype == "bf16":
+        return bf16_to_f32(arr)
+    if dtype == "f16":
+        return arr.astype(np.float32)
+    return arr
+
+
+def _narrow(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Compute width -> storage (one rounding for the half widths)."""
+    if dtype == "bf16":
+        return f32_to_bf16(x)
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.float32).astype(np.float16)
+    return np.asarray(x).astype(STORAGE[dtype], copy=False)
+
+
+def _to_dtype_from_float(x: np.ndarray, dtype: str) -> np.ndarray:
+    """CAST of float values (float32 or float64 array) to ``dtype``."""
+    if dtype in INTS:
+        with np.errstate(invalid="ignore"):
+            t = np.trunc(x.astype(np.float64))
+        return t.astype(np.int64).astype(STORAGE[dtype])
+    if dtype == "bf16":
+        return f32_to_bf16(x.astype(np.float32))
+    return x.astype(STORAGE[dtype])
+
+
+# ---------------------------------------------------------------------------
+# shape / dtype inference
+# ---------------------------------------------------------------------------
+
+def _movement_shape(shape, mv):
+    name, arg = mv
+    shape = tuple(shape)
+    if name == "reshape":
+        new = tuple(arg)
+        if any(s < 0 for s in new) or int(np.prod(new, dtype=np.int64)) != int(np.prod(shape, dtype=np.int64)):
+            raise OracleError(f"reshape {shape} -> {new}")
+        return new
+    if name == "permute":
+        perm = tuple(arg)
+        if sorted(perm) != list(range(len(shape))):
+            raise OracleError(f"permute {perm} of rank {len(shape)}")
+        return tuple(shape[p] for p in perm)
+    if name == "expand":
+        new = tuple(arg)
+        if len(new) != len(shape) or any(o != 1 and o != n for o, n in zip(shape, new)):
+            raise OracleError(f"expand {shape} -> {new}")
+        return new
+    if name == "pad":
+        widths = tuple(tuple(w) for w in arg)
+        if len(widths) != len(shape) or any(b < 0 or a < 0 for b, a in widths):
+            raise OracleError(f"pad {widths}")
+        return tuple(s + b + a for s, (b, a) in zip(shape, widths))
+    if name == "shrink":
+        rng = tuple(tuple(r) for r in arg)
+        if len(rng) != len(shape) or any(not (0 <= lo <= hi <= s) for s, (lo, hi) in zip(shape, rng)):
+            raise OracleError(f"shrink {rng} of {shape}")
+        return tuple(hi - lo for lo, hi in rng)
+    raise OracleError(f"unknown movement {name}")
+
+
+def infer(spec) -> list:
+    """(shape, dtype) of every node, checking the op contracts."""
+    out = []
+    for i, nd in enumerate(spec.nodes):
+        op = nd["op"]
+        src = nd.get("src", ())
+        for s in src:
+            if not (0 <= s < i):
+                raise OracleError(f"node {i}: source {s} is not an earlier node")
+        if op in ("BUFFER", "CONST"):
+            out.append((tuple(nd["shape"]), nd["dtype"]))
+        elif op == "VIEW":
+            shp, dt = out[src[0]]
+            if "raw" in nd and nd["raw"] is not None:
+                shp = tuple(nd["raw"]["shape"])
+            else:
+                for mv in nd["movement"]:
+                    shp = _movement_shape(shp, mv)
+            out.append((shp, dt))
+        elif op in ("NEG", "EXP", "LOG", "SQRT", "RECIP"):
+            shp, dt = out[src[0]]
+            if op != "NEG" and dt not in FLOATS:
+                raise OracleError(f"node {i}: {op} needs a float dtype")
+            out.append((shp, dt))
+        elif op == "CAST":
+            out.append((out[src[0]][0], nd["dtype"]))
+        elif op in ("ADD", "MUL", "CMPLT"):
+            (s0, d0), (s1, d1) = out[src[0]], out[src[1]]
+            if s0 != s1 or d0 != d1:
+                raise OracleError(f"node {i}: {op} of {s0}/{d0} and {s1}/{d1}")
+            out.append((s0, "i8" if op == "CMPLT" else d0))
+        elif op == "WHERE":
+            (sc, _), (s1, d1), (s2, d2) = out[src[0]], out[src[1]], out[src[2]]
+            if not (sc == s1 == s2) or d1 != d2:
+                raise OracleError(f"node {i}: WHERE shapes/dtypes")
+            out.append((s1, d1))
+        elif op in ("SUM", "MAX"):
+            shp, dt = out[src[0]]
+            axes = tuple(nd["axes"])
+            if any(not (0 <= a < len(shp)) for a in axes) or len(set(axes)) != len(axes):
+                raise OracleError(f"node {i}: axes {axes} of rank {len(shp)}")
+            out.append((tuple(1 if d in axes else s for d, s in enumerate(shp)), dt))
+        elif op == "CONTIGUOUS":
+            out.append(out[src[0]])
+        else:
+            raise OracleError(f"node {i}: op {op} is not evaluated by this oracle")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# primitive evaluation
+# ---------------------------------------------------------------------------
+
+def _apply_movement(arr: np.ndarray, mv) -> np.ndarray:
+    """One movement op with numpy's own routine; the result may be a
+    non-contiguous or broadcast numpy view (no copy is made where numpy can
+    avoid one)."""
+    name, arg = mv
+    if name == "reshape":
+        return arr.reshape(tuple(arg))
+    if name == "permute":
+        return np.transpose(arr, tuple(arg))
+    if name == "expand":
+        return np.broadcast_to(arr, tuple(arg))
+    if name == "pad":
+        return np.pad(arr, tuple(tuple(w) for w in arg), mode="constant", constant_values=0)
+    if name == "shrink":
+        return arr[tuple(slice(lo, hi) for lo, hi in arg)]
+    raise OracleError(name)
+
+
+def _raw_view(src: np.ndarray, raw: dict) -> np.ndarray:
+    """Explicit View descriptor: cell i reads src.flat[offset + sum_d i_d*s_d]
+    when lo_d <= i_d < hi_d for every d, else zero."""
+    flat = np.ascontiguousarray(src).reshape(-1)
+    shape = tuple(raw["shape"])
+    idx = np.full(shape, int(raw["offset"]), dtype=np.int64)
+    inside = np.ones(shape, dtype=bool)
+    grids = np.indices(shape, dtype=np.int64) if len(shape) else []
+    for d, g in enumerate(grids):
+        idx = idx + g * int(raw["strides"][d])
+        inside &= (g >= int(raw["mask_lo"][d])) & (g < int(raw["mask_hi"][d]))
+    if np.any(inside & ((idx < 0) | (idx >= flat.size))):
+        raise OracleError("raw view reads outside its buffer")
+    vals = flat[np.where(inside, idx, 0)] if flat.size else np.zeros(shape, flat.dtype)
+    return np.where(inside, vals, np.zeros((), flat.dtype)).astype(flat.dtype)
+
+
+def _unary(op: str, x: np.ndarray, dt: str) -> np.ndarray:
+    if dt in INTS:
+        if op == "NEG":
+            return np.negative(x).astype(x.dtype)
+        raise OracleError(f"{op} of an int")
+    w = _widen(x, dt)
+    with np.errstate(all="ignore"):
+        if op == "NEG":
+            r = np.negative(w)
+        elif op in ("EXP", "LOG"):
+            fn = np.exp if op == "EXP" else np.log
+            if w.dtype == np.float64:
+                r = fn(w)
+            else:
+                r = fn(w.astype(np.float64)).astype(np.float32)
+        elif op == "SQRT":
+            r = np.sqrt(w)
+        elif op == "RECIP":
+            r = np.asarray(1.0, dtype=w.dtype) / w
+        else:
+            raise OracleError(op)
+    return _narrow(r, dt)
+
+
+def _binary(op: str, x: np.ndarray, y: np.ndarray, dt: str) -> np.ndarray:
+    if dt in INTS:
+        with np.errstate(all="ignore"):
+            if op == "ADD":
+                return np.add(x, y, dtype=x.dtype)
+            if op == "MUL":
+                return np.multiply(x, y, dtype=x.dtype)
+            return (x < y).astype(np.int8)
+    a, b = _widen(x, dt), _widen(y, dt)
+    with np.errstate(all="ignore"):
+        if op == "ADD":
+            return _narrow(a + b, dt)
+        if op == "MUL":
+            return _narrow(a * b, dt)
+        return (a < b).astype(np.int8)
+
+
+def _cast(x: np.ndarray, src_dt: str, dst_dt: str) -> np.ndarray:
+    if src_dt == dst_dt:
+        return x.copy()
+    if src_dt in INTS:
+        if dst_dt in INTS:
+            return x.astype(np.int64).astype(STORAGE[dst_dt])
+        if dst_dt == "f64":
+            return x.astype(np.float64)
+        r = x.astype(np.float64).astype(np.float32) if dst_dt != "f32" else x.astype(np.float32)
+        return _narrow(r, dst_dt) if dst_dt in ("bf16", "f16") else r
+    w = _widen(x, src_dt)
+    return _to_dtype_from_float(w, dst_dt)
+
+
+def _reduce(op: str, x: np.ndarray, dt: str, axes) -> np.ndarray:
+    """Fold ``x`` over ``axes`` (kept as size 1) in ascending row-major order."""
+    shape = x.shape
+    nd = len(shape)
+    keep = [d for d in range(nd) if d not in axes]
+    moved = np.transpose(x, keep + list(axes))
+    cells = int(np.prod([shape[d] for d in keep], dtype=np.int64))
+    n = int(np.prod([shape[d] for d in axes], dtype=np.int64))
+    out_shape = tuple(1 if d in axes else shape[d] for d in range(nd))
+    lib = _fold_lib()
+    if dt in INTS:
+        flat = np.ascontiguousarray(moved.astype(np.int32)).reshape(cells, n)
+        res = np.empty(cells, dtype=np.int32)
+        if op == "SUM":
+            lib.fold_sum_i32(_ptr(flat), cells, n, _ptr(res))
+        else:
+            lib.fold_max_i32(_ptr(flat), cells, n, int(np.iinfo(STORAGE[dt]).min), _ptr(res))
+        return res.astype(STORAGE[dt]).reshape(out_shape)
+    if dt == "f64":
+        flat = np.ascontiguousarray(moved, dtype=np.float64).reshape(cells, n)
+        res = np.empty(cells, dtype=np.float64)
+        (lib.fold_sum_f64 if op == "SUM" else lib.fold_max_f64)(_ptr(flat), cells, n, _ptr(res))
+        return res.reshape(out_shape)
+    flat = np.ascontiguousarray(_widen(np.ascontiguousarray(moved), dt), dtype=np.float32).reshape(cells, n)
+    res = np.empty(cells, dtype=np.float32)
+    if op == "MAX":
+        lib.fold_max_f32(_ptr(flat), cells, n, _ptr(res))
+    elif (n - 1) * 2.0 ** -24 >= 1.0 / 3.0:
+        lib.fold_sum_f32_wide(_ptr(flat), cells, n, _ptr(res))
+    else:
+        lib.fold_sum_f32(_ptr(flat), cells, n, _ptr(res))
+    return _narrow(res, dt).reshape(out_shape)
+
+
+# ---------------------------------------------------------------------------
+# the interpreter
+# ---------------------------------------------------------------------------
+
+class Interpreter:
+    """Evaluates a workload graph node by node.
+
+    ``inputs`` maps each BUFFER slot to a numpy array in storage form
+    (bfloat16 as uint16 bit patterns). ``max_elems`` is the largest node the
+    interpreter materialises whole; ``slab_elems`` bounds one slab.
+    """
+
+    def __init__(self, spec, inputs: dict, max_elems: int = 1 << 28, slab_elems: int = 1 << 24):
+        self.spec = spec
+        self.inputs = inputs
+        self.meta = infer(spec)
+        self.max_elems = max_elems
+        self.slab_elems = slab_elems
+        self.memo: dict[int, np.ndarray] = {}
+
+    def size(self, i: int) -> int:
+        return int(np.prod(self.meta[i][0], dtype=np.int64))
+
+    def value(self, i: int) -> np.ndarray:
+        """The whole value of node ``i`` (memoised)."""
+        if i not in self.memo:
+            self.memo[i] = self._eval(i, None, {})
+        return self.memo[i]
+
+    def _eval(self, i: int, rows, cache: dict) -> np.ndarray:
+        """Node ``i``, or only rows [r0, r1) of its dim 0 when ``rows`` is set."""
+        if rows is not None and i in cache:
+            return cache[i]
+        nd = self.spec.nodes[i]
+        op = nd["op"]
+        shape, dt = self.meta[i]
+        src = nd.get("src", ())
+
+        def arg(j):
+            if rows is None:
+                return self.value(j)
+            return self._eval(j, rows, cache)
+
+        if op == "BUFFER":
+            arr = np.asarray(self.inputs[nd["slot"]])
+            if tuple(arr.shape) != shape or arr.dtype != STORAGE[dt]:
+                raise OracleError(f"input {nd['slot']}: {arr.shape}/{arr.dtype}, expected {shape}/{dt}")
+            r = arr
+            if rows is not None:
+                r = arr[rows[0]:rows[1]]
+        elif op == "CONST":
+            sh = shape if rows is None else (rows[1] - rows[0],) + tuple(shape[1:])
+            if dt == "bf16":
+                r = np.full(sh, f32_to_bf16(np.float32(nd["value"]).reshape(1))[0], dtype=np.uint16)
+            elif dt in INTS:
+                r = np.full(sh, np.int64(int(nd["value"])).astype(STORAGE[dt]), dtype=STORAGE[dt])
+            else:
+                r = np.full(sh, nd["value"], dtype=STORAGE[dt])
+        elif op == "VIEW":
+            base = self.value(src[0])
+            if nd.get("raw") is not None:
+                r = _raw_view(base, nd["raw"])
+            else:
+                r = base
+                for mv in nd["movement"]:
+                    r = _apply_movement(r, mv)
+            if rows is not None:
+                r = r[rows[0]:rows[1]]
+        elif op in ("NEG", "EXP", "LOG", "SQRT", "RECIP"):
+            r = _unary(op, np.ascontiguousarray(arg(src[0])), dt)
+        elif op == "CAST":
+            r = _cast(np.ascontiguousarray(arg(src[0])), self.meta[src[0]][1], dt)
+        elif op in ("ADD", "MUL", "CMPLT"):
+            r = _binary(op, np.ascontiguousarray(arg(src[0])), np.ascontiguousarray(arg(src[1])),
+                        self.meta[src[0]][1])
+        elif op == "WHERE":
+            c = arg(src[0])
+            r = np.where(c != 0, arg(src[1]), arg(src[2])).astype(STORAGE[dt])
+        elif op in ("SUM", "MAX"):
+            axes = tuple(nd["axes"])
+            sdt = self.meta[src[0]][1]
+            if rows is None and self.size(src[0]) > self.max_elems:
+                r = self._reduce_in_slabs(i, op, src[0], sdt, axes)
+            else:
+                if rows is not None and 0 in axes:
+                    raise OracleError("a slab cannot reduce over dim 0")
+                r = _reduce(op, np.ascontiguousarray(arg(src[0])), sdt, axes)
+        elif op == "CONTIGUOUS":
+            r = np.ascontiguousarray(arg(src[0])).copy()
+        else:
+            raise OracleError(f"op {op}")
+        r = np.ascontiguousarray(r) if op not in ("VIEW", "BUFFER") else r
+        if rows is not None:
+            cache[i] = r
+        return r
+
+    def _reduce_in_slabs(self, i, op, s, sdt, axes):
+        if 0 in axes:
+            raise OracleError(f"node {i}: too large to materialise and reduces dim 0")
+        shape = self.meta[s][0]
+        per_row = max(1, self.size(s) // max(1, shape[0]))
+        step = max(1, self.slab_elems // per_row)
+        parts = []
+        for r0 in range(0, shape[0], step):
+            r1 = min(shape[0], r0 + step)
+            x = self._eval(s, (r0, r1), {})
+            parts.append(_reduce(op, np.ascontiguousarray(x), sdt, axes))
+        return np.concatenate(parts, axis=0)
+
+
+def run(spec, inputs: dict, **kw) -> list:
+    """Evaluate ``spec`` and return its outputs in storage form."""
+    it = Interpreter(spec, inputs, **kw)
+    return [np.array(it.value(o), copy=True) for o in spec.outputs]
+
+
+def dtype_of(spec, node: int) -> str:
+    return infer(spec)[node][1]

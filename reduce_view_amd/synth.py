@@ -1,0 +1,338 @@
+"""Seeded synthetic inputs and declarative workload graphs.
+
+This module is shared by the tests, the benchmark and the CPU oracle's
+callers. It holds no arithmetic of the method: a graph here is only a record
+of which primitive is applied to which earlier node (the limn README,
+"Architecture" and "The op set"), with movement ops kept as the list the user
+wrote. Shape inference, View composition and every primitive's evaluation are
+implemented separately by the library (``reduce_view_amd``) and by the oracle
+(``oracle/``); neither imports the other.
+
+Random inputs: ``numpy.random.default_rng(seed)`` (PCG64), drawn in the order
+each workload lists them, as float64, rounded to float32 by numpy's cast
+(round-to-nearest-even) and, for bfloat16 storage, rounded again by torch's
+float32 -> bfloat16 conversion (round-to-nearest-even). ``normal(mu, s)`` takes
+``s`` as the standard deviation. bfloat16 arrays are carried as ``uint16``
+bit patterns.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# Names of the primitive ops a graph may hold (limn README, "The op set").
+OPS = (
+    "BUFFER", "CONST", "VIEW", "NEG", "EXP", "LOG", "SQRT", "RECIP", "CAST",
+    "ADD", "MUL", "CMPLT", "WHERE", "SUM", "MAX", "CONTIGUOUS",
+    "GATHER", "SCATTER", "ASSIGN", "CUSTOM",
+)
+DTYPES = ("f32", "bf16", "f16", "f64", "i32", "i16", "i8")
+MOVEMENT = ("reshape", "permute", "expand", "pad", "shrink")
+
+
+class Spec:
+    """A topologically ordered node list plus the ids of its outputs.
+
+    Every node is a plain dict. Keys used:
+      op        one of OPS
+      src       tuple of earlier node ids
+      slot      BUFFER: name of the input array; its shape and dtype
+      shape     BUFFER, CONST: shape (tuple)
+      dtype     BUFFER, CONST: storage dtype; CAST: target dtype
+      value     CONST: the scalar
+      axes      SUM, MAX: reduced axes (dims are kept with size 1)
+      movement  VIEW: tuple of (name, arg) movement ops applied in order
+      raw       VIEW: explicit descriptor dict(shape, strides, offset,
+                mask_lo, mask_hi) in elements over the source's row-major
+                storage, instead of ``movement``
+    """
+
+    def __init__(self, name: str = "graph"):
+        self.name = name
+        self.nodes: list[dict] = []
+        self.outputs: list[int] = []
+
+    # sources -----------------------------------------------------------
+    def _add(self, **kw) -> int:
+        kw.setdefault("src", ())
+        self.nodes.append(kw)
+        return len(self.nodes) - 1
+
+    def buffer(self, slot: str, shape, dtype: str) -> int:
+        return self._add(op="BUFFER", slot=slot, shape=tuple(shape), dtype=dtype)
+
+    def const(self, value: float, shape, dtype: str) -> int:
+        return self._add(op="CONST", value=float(value), shape=tuple(shape), dtype=dtype)
+
+    # movement ----------------------------------------------------------
+    def view(self, src: int, *movement) -> int:
+        mv = tuple((m[0], _freeze(m[1])) for m in movement)
+        for m in mv:
+            if m[0] not in MOVEMENT:
+                raise ValueError(f"unknown movement op {m[0]!r}")
+        return self._add(op="VIEW", src=(src,), movement=mv)
+
+    def raw_view(self, src: int, shape, strides, offset=0, mask_lo=None, mask_hi=None) -> int:
+        shape = tuple(int(s) for s in shape)
+        raw = dict(shape=shape, strides=tuple(int(s) for s in strides), offset=int(offset),
+                   mask_lo=tuple(mask_lo) if mask_lo is not None else tuple(0 for _ in shape),
+                   mask_hi=tuple(mask_hi) if mask_hi is not None else shape)
+        return self._add(op="VIEW", src=(src,), raw=raw)
+
+    # elementwise -------------------------------------------------------
+    def neg(self, x): return self._add(op="NEG", src=(x,))
+    def exp(self, x): return self._add(op="EXP", src=(x,))
+    def log(self, x): return self._add(op="LOG", src=(x,))
+    def sqrt(self, x): return self._add(op="SQRT", src=(x,))
+    def recip(self, x): return self._add(op="RECIP", src=(x,))
+    def cast(self, x, dtype): return self._add(op="CAST", src=(x,), dtype=dtype)
+    def add(self, x, y): return self._add(op="ADD", src=(x, y))
+    def mul(self, x, y): return self._add(op="MUL", src=(x, y))
+    def cmplt(self, x, y): return self._add(op="CMPLT", src=(x, y))
+    def where(self, c, x, y): return self._add(op="WHERE", src=(c, x, y))
+
+    # reduce / barriers -------------------------------------------------
+    def sum(self, x, axes): return self._add(op="SUM", src=(x,), axes=tuple(axes))
+    def max(self, x, axes): return self._add(op="MAX", src=(x,), axes=tuple(axes))
+    def contiguous(self, x): return self._add(op="CONTIGUOUS", src=(x,))
+
+    def output(self, *ids) -> None:
+        self.outputs.extend(ids)
+
+
+def _freeze(a):
+    if isinstance(a, (list, tuple)):
+        return tuple(_freeze(x) for x in a)
+    return int(a)
+
+
+# ---------------------------------------------------------------------------
+# workload graphs (the composed ops spelled in primitives: x - y is
+# ADD(x, NEG(y)), x / y is MUL(x, RECIP(y)), rsqrt is RECIP(SQRT(.)), a mean
+# is SUM times CONST(1/N), relu(y) is WHERE(CMPLT(0, y), y, 0)).
+# ---------------------------------------------------------------------------
+
+def matmul_broadcast(m: int, n: int, k: int, dtype: str = "f32") -> Spec:
+    """Y = SUM_k MUL(A viewed as (m,n,k) with n-stride 0, B viewed as (m,n,k)
+    with m-stride 0): the limn README's one-nest matmul and the Luminal IR
+    blog's naive matmul with a stride-0 loop."""
+    g = Spec(f"matmul_broadcast_{m}x{n}x{k}")
+    a = g.buffer("A", (m, k), dtype)
+    b = g.buffer("B", (k, n), dtype)
+    a3 = g.view(a, ("reshape", (m, 1, k)), ("expand", (m, n, k)))
+    b3 = g.view(b, ("permute", (1, 0)), ("reshape", (1, n, k)), ("expand", (m, n, k)))
+    y = g.sum(g.mul(a3, b3), (2,))
+    g.output(y)
+    return g
+
+
+def matmul_broadcast_raw(m: int, n: int, k: int) -> Spec:
+    """The same contraction with the two Views written as explicit
+    descriptors: A with strides (k, 0, 1), B with strides (0, 1, n)."""
+    g = Spec(f"matmul_raw_{m}x{n}x{k}")
+    a = g.buffer("A", (m, k), "f32")
+    b = g.buffer("B", (k, n), "f32")
+    a3 = g.raw_view(a, (m, n, k), (k, 0, 1))
+    b3 = g.raw_view(b, (m, n, k), (0, 1, n))
+    g.output(g.sum(g.mul(a3, b3), (2,)))
+    return g
+
+
+def ew_chain(rows: int, cols: int, masked: bool = False, edges=(3, 5)) -> Spec:
+    """out = WHERE(CMPLT(a, b), a*b, EXP(-a)) + c, with b a permuted view of
+    a (cols, rows) buffer and c a row vector expanded down the rows through a
+    stride-0 dim. With ``masked`` the operand a is a shrink-then-pad view of a
+    larger buffer whose border of ``edges`` rows/cols reads as zero."""
+    g = Spec(f"ew_chain_{rows}x{cols}{'_masked' if masked else ''}")
+    if masked:
+        er, ec = edges
+        big = g.buffer("Abig", (rows, cols), "f32")
+        a = g.view(big, ("shrink", ((er, rows - er), (ec, cols - ec))),
+                   ("pad", ((er, er), (ec, ec))))
+    else:
+        a = g.buffer("a", (rows, cols), "f32")
+    bb = g.buffer("Bb", (cols, rows), "f32")
+    b = g.view(bb, ("permute", (1, 0)))
+    cv = g.buffer("c", (cols,), "f32")
+    c = g.view(cv, ("reshape", (1, cols)), ("expand", (rows, cols)))
+    out = g.add(g.where(g.cmplt(a, b), g.mul(a, b), g.exp(g.neg(a))), c)
+    g.output(out)
+    return g
+
+
+def transpose(rows: int, cols: int, dtype: str = "f32") -> Spec:
+    """Y = CONTIGUOUS(VIEW(X, permute(1, 0))): X is (rows, cols), Y (cols, rows)."""
+    g = Spec(f"transpose_{rows}x{cols}")
+    x = g.buffer("X", (rows, cols), dtype)
+    g.output(g.contiguous(g.view(x, ("permute", (1, 0)))))
+    return g
+
+
+def softmax(rows: int, n: int) -> Spec:
+    """Row softmax with the max shift: m = MAX(x), e = EXP(x - m),
+    y = e * RECIP(SUM(e))."""
+    g = Spec(f"softmax_{rows}x{n}")
+    x = g.buffer("x", (rows, n), "f32")
+    m = g.max(x, (1,))
+    mb = g.view(m, ("expand", (rows, n)))
+    e = g.exp(g.add(x, g.neg(mb)))
+    s = g.sum(e, (1,))
+    rb = g.view(g.recip(s), ("expand", (rows, n)))
+    g.output(g.mul(e, rb))
+    return g
+
+
+def softmax_noshift(rows: int, n: int) -> Spec:
+    """Softmax written without the max shift (the Litmus README's
+    no_max_subtract family): overflows for large-magnitude rows."""
+    g = Spec(f"softmax_noshift_{rows}x{n}")
+    x = g.buffer("x", (rows, n), "f32")
+    e = g.exp(x)
+    s = g.sum(e, (1,))
+    g.output(g.mul(e, g.view(g.recip(s), ("expand", (rows, n)))))
+    return g
+
+
+def rmsnorm(rows: int, n: int, eps: float = 1e-6) -> Spec:
+    """y = (x * r) * w, r = RECIP(SQRT(SUM(x*x) * (1/n) + eps)) (Tiki README,
+    "Compile model code": float32 reduction, multiplication order x*inv*w)."""
+    g = Spec(f"rmsnorm_{rows}x{n}")
+    x = g.buffer("x", (rows, n), "f32")
+    w = g.buffer("w", (n,), "f32")
+    ss = g.sum(g.mul(x, x), (1,))
+    ms = g.mul(ss, g.const(1.0 / n, (rows, 1), "f32"))
+    r = g.recip(g.sqrt(g.add(ms, g.const(eps, (rows, 1), "f32"))))
+    rb = g.view(r, ("expand", (rows, n)))
+    wb = g.view(w, ("reshape", (1, n)), ("expand", (rows, n)))
+    g.output(g.mul(g.mul(x, rb), wb))
+    return g
+
+
+def layernorm(rows: int, n: int, eps: float = 1e-5, dtype: str = "bf16") -> Spec:
+    """torch-semantics LayerNorm (biased variance) with ``dtype`` storage and
+    float32 arithmetic: xf = CAST(x), mu = SUM(xf)/n, xc = xf - mu,
+    v = SUM(xc*xc)/n, r = RECIP(SQRT(v + eps)), y = CAST((xc*r)*g + b)."""
+    g = Spec(f"layernorm_{rows}x{n}")
+    x = g.buffer("x", (rows, n), dtype)
+    gm = g.buffer("gamma", (n,), dtype)
+    bt = g.buffer("beta", (n,), dtype)
+    xf = g.cast(x, "f32")
+    inv_n = g.const(1.0 / n, (rows, 1), "f32")
+    mu = g.mul(g.sum(xf, (1,)), inv_n)
+    xc = g.add(xf, g.neg(g.view(mu, ("expand", (rows, n)))))
+    v = g.mul(g.sum(g.mul(xc, xc), (1,)), inv_n)
+    r = g.recip(g.sqrt(g.add(v, g.const(eps, (rows, 1), "f32"))))
+    gf = g.view(g.cast(gm, "f32"), ("reshape", (1, n)), ("expand", (rows, n)))
+    bf = g.view(g.cast(bt, "f32"), ("reshape", (1, n)), ("expand", (rows, n)))
+    y = g.add(g.mul(g.mul(xc, g.view(r, ("expand", (rows, n)))), gf), bf)
+    g.output(g.cast(y, dtype))
+    return g
+
+
+def gemm_relu2_sum(m: int, n: int, k: int, emit_y: bool = False) -> Spec:
+    """S = SUM(relu(y)^2) with y = SUM_k CAST(A) * CAST(B) over bf16 A (m,k)
+    and B (k,n) viewed as (m,n,k) through stride-0 dims (limn README's
+    headline example ((x @ W).relu() ** 2).sum(), in primitives)."""
+    g = Spec(f"gemm_relu2_sum_{m}x{n}x{k}")
+    a = g.buffer("A", (m, k), "bf16")
+    b = g.buffer("B", (k, n), "bf16")
+    a3 = g.cast(g.view(a, ("reshape", (m, 1, k)), ("expand", (m, n, k))), "f32")
+    b3 = g.cast(g.view(b, ("permute", (1, 0)), ("reshape", (1, n, k)), ("expand", (m, n, k))), "f32")
+    y = g.sum(g.mul(a3, b3), (2,))
+    zero = g.const(0.0, (m, n, 1), "f32")
+    r = g.where(g.cmplt(zero, y), y, zero)
+    s = g.sum(g.mul(r, r), (0, 1, 2))
+    g.output(s)
+    if emit_y:
+        g.output(y)
+    return g
+
+
+def gemm_bf16(m: int, n: int, k: int) -> Spec:
+    """y = SUM_k CAST(A) * CAST(B), stored as float32 (m, n, 1)."""
+    g = Spec(f"gemm_bf16_{m}x{n}x{k}")
+    a = g.buffer("A", (m, k), "bf16")
+    b = g.buffer("B", (k, n), "bf16")
+    a3 = g.cast(g.view(a, ("reshape", (m, 1, k)), ("expand", (m, n, k))), "f32")
+    b3 = g.cast(g.view(b, ("permute", (1, 0)), ("reshape", (1, n, k)), ("expand", (m, n, k))), "f32")
+    g.output(g.sum(g.mul(a3, b3), (2,)))
+    return g
+
+
+# ---------------------------------------------------------------------------
+# seeded inputs
+# ---------------------------------------------------------------------------
+
+def to_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns by torch's conversion (RNE)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _f32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def inputs_matmul(m: int, n: int, k: int, seed: int = 0) -> dict:
+    rng = np.random.default_rng(seed)
+    return {"A": _f32(rng.normal(0.0, 1.0, (m, k))), "B": _f32(rng.normal(0.0, 1.0, (k, n)))}
+
+
+def inputs_ew(rows: int, cols: int, seed: int = 1) -> dict:
+    """Draw order: a, Bb, c, Abig, then the transpose input X."""
+    rng = np.random.default_rng(seed)
+    d = {}
+    d["a"] = _f32(rng.uniform(-4.0, 4.0, (rows, cols)))
+    d["Bb"] = _f32(rng.uniform(-4.0, 4.0, (cols, rows)))
+    d["c"] = _f32(rng.uniform(-4.0, 4.0, (cols,)))
+    d["Abig"] = _f32(rng.uniform(-4.0, 4.0, (rows, cols)))
+    d["X"] = _f32(rng.uniform(-1.0, 1.0, (rows, cols)))
+    return d
+
+
+def inputs_softmax(rows: int, n: int, seed: int = 2) -> dict:
+    rng = np.random.default_rng(seed)
+    return {"x": _f32(rng.uniform(-1e3, 1e3, (rows, n)))}
+
+
+def inputs_rmsnorm(rows: int, n: int, seed: int = 3) -> dict:
+    rng = np.random.default_rng(seed)
+    x = _f32(rng.normal(0.0, 1.0, (rows, n)))
+    w = _f32(rng.normal(1.0, 0.1, (n,)))
+    return {"x": x, "w": w}
+
+
+def inputs_layernorm(rows: int, n: int, seed: int = 4) -> dict:
+    rng = np.random.default_rng(seed)
+    x = to_bf16_bits(_f32(rng.normal(100.0, 1.0, (rows, n))))
+    gm = to_bf16_bits(_f32(rng.normal(1.0, 0.1, (n,))))
+    bt = to_bf16_bits(_f32(rng.normal(0.0, 0.1, (n,))))
+    return {"x": x, "gamma": gm, "beta": bt}
+
+
+def inputs_gemm(m: int, n: int, k: int, seed: int = 5) -> dict:
+    rng = np.random.default_rng(seed)
+    a = to_bf16_bits(_f32(rng.normal(0.0, 1.0 / np.sqrt(k), (m, k))))
+    b = to_bf16_bits(_f32(rng.normal(0.0, 1.0, (k, n))))
+    return {"A": a, "B": b}
+
+
+def inputs_gemm_integer(m: int, n: int, k: int, seed: int = 7, lo: int = -2, hi: int = 2) -> dict:
+    """Integer-valued bf16 operands in [lo, hi]: every partial sum is an
+    integer below 2^24, so any summation order gives the same float32."""
+    rng = np.random.default_rng(seed)
+    a = to_bf16_bits(rng.integers(lo, hi + 1, (m, k)).astype(np.float32))
+    b = to_bf16_bits(rng.integers(lo, hi + 1, (k, n)).astype(np.float32))
+    return {"A": a, "B": b}
+
+
+# Full-size workloads the measurements are quoted on (shape, seed).
+FULL = {
+    "matmul64": dict(m=64, n=64, k=64),
+    "ew_chain": dict(rows=4096, cols=4096),
+    "softmax": dict(rows=16384, n=4096),
+    "rmsnorm": dict(rows=16384, n=4096),
+    "layernorm": dict(rows=8192, n=8192),
+    "gemm": dict(m=4096, n=4096, k=4096),
+}
