@@ -1,0 +1,224 @@
+"""Benchmark of the fused view/reduce hot path on one MI355X.
+
+Default workload (the one the headline metric is quoted on): the 4096 x 4096
+float32 elementwise chain WHERE(CMPLT(a, b), a*b, EXP(-a)) + c with b a
+permuted View and c a stride-0 row vector, the same chain with a read through
+a shrink-then-pad masked View, and a standalone 4096 x 4096 transpose. One
+step runs all three programs once. ``--workload`` selects one of the other
+kernels instead (softmax, rmsnorm, layernorm, gemm, matmul64).
+
+Inputs are seeded, synthetic and already resident in HBM when timing starts;
+several input sets rotate so that consecutive launches never re-read data the
+previous launch left in the 256 MB Infinity Cache. Throughput counts
+ALGORITHMIC bytes (each input cell read once, masked cells not read, each
+output written once) or flops. Kernel times come from HIP events on the
+stream the kernels are launched on (torch's current stream).
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import resource
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused view/reduce kernels GB/s & % HBM peak; bf16 matmul TFLOP/s & % MFMA"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+F32 = 4
+
+
+def _bytes_ew(r, c):
+    chain = 3 * r * c * F32 + c * F32
+    masked_cells = (r - 6) * (c - 10)
+    masked = masked_cells * F32 + 2 * r * c * F32 + c * F32
+    transpose = 2 * r * c * F32
+    return chain, masked, transpose
+
+
+def workloads():
+    from reduce_view_amd import synth
+    r = c = 4096
+    chain_b, masked_b, tr_b = _bytes_ew(r, c)
+    return {
+        "ew_chain": dict(
+            desc=("4096x4096 fp32 chain WHERE(CMPLT(a,b), a*b, EXP(-a)) + c (b permuted view, c stride-0 "
+                  "row vector) + the chain with a shrink/pad masked view (edges 3,5) + 4096x4096 "
+                  "transpose; U(-4,4) / U(-1,1), seed 1"),
+            programs=[("chain", synth.ew_chain(r, c), chain_b),
+                      ("chain_masked", synth.ew_chain(r, c, masked=True), masked_b),
+                      ("transpose", synth.transpose(r, c), tr_b)],
+            inputs=lambda seed: synth.inputs_ew(r, c, seed),
+            unit="GB/s", dtype="f32", bound="hbm", seed=1),
+        "softmax": dict(
+            desc="row softmax with max shift, 16384x4096 fp32, x ~ U(-1e3,1e3), seed 2",
+            programs=[("softmax", synth.softmax(16384, 4096), 2 * 16384 * 4096 * F32)],
+            inputs=lambda seed: synth.inputs_softmax(16384, 4096, seed),
+            unit="GB/s", dtype="f32", bound="hbm", seed=2),
+        "rmsnorm": dict(
+            desc="RMSNorm 16384x4096 fp32, x ~ N(0,1), w ~ N(1,0.1), eps 1e-6, seed 3",
+            programs=[("rmsnorm", synth.rmsnorm(16384, 4096), 2 * 16384 * 4096 * F32 + 4096 * F32)],
+            inputs=lambda seed: synth.inputs_rmsnorm(16384, 4096, seed),
+            unit="GB/s", dtype="f32", bound="hbm", seed=3),
+        "layernorm": dict(
+            desc="LayerNorm 8192x8192 bf16 in/out, fp32 accumulation, x ~ N(100,1), eps 1e-5, seed 4",
+            programs=[("layernorm", synth.layernorm(8192, 8192), 2 * 8192 * 8192 * 2 + 2 * 8192 * 2)],
+            inputs=lambda seed: synth.inputs_layernorm(8192, 8192, seed),
+            unit="GB/s", dtype="f32", bound="hbm", seed=4),
+        "gemm": dict(
+            desc=("bf16 4096x4096x4096 MUL+SUM contraction on MFMA (fp32 accumulate), fused relu(y)^2 "
+                  "epilogue, full SUM to an fp32 scalar; A ~ N(0,1/64), B ~ N(0,1), seed 5"),
+            programs=[("gemm_relu2_sum", synth.gemm_relu2_sum(4096, 4096, 4096), 2 * 4096 ** 3)],
+            inputs=lambda seed: synth.inputs_gemm(4096, 4096, 4096, seed),
+            unit="TFLOP/s", dtype="f32", bound="mfma", seed=5),
+        "matmul64": dict(
+            desc="fp32 64x64x64 matmul as broadcast MUL over stride-0 views + in-order SUM over k, seed 0",
+            programs=[("matmul64", synth.matmul_broadcast(64, 64, 64), 3 * 64 * 64 * F32)],
+            inputs=lambda seed: synth.inputs_matmul(64, 64, 64, seed),
+            unit="GB/s", dtype="f32", bound="hbm", seed=0),
+    }
+
+
+def _cpu_baseline(wl, name, budget_s):
+    """The oracle, as it is, on the host cores: whole programs of the
+    workload until about ``budget_s`` seconds have passed (gemm: a row slab
+    of the contraction, scaled by rows)."""
+    import oracle
+    from reduce_view_amd import synth
+    t_wall = 0.0
+    work = 0.0
+    ru0 = resource.getrusage(resource.RUSAGE_SELF)
+    w0 = time.perf_counter()
+    sample = ""
+    if name == "gemm":
+        rows = 16
+        inp = synth.inputs_gemm(4096, 4096, 4096, 5)
+        sub = {"A": inp["A"][:rows], "B": inp["B"]}
+        spec = synth.gemm_relu2_sum(rows, 4096, 4096)
+        t = time.perf_counter()
+        oracle.run(spec, sub)
+        t_wall = time.perf_counter() - t
+        work = 2.0 * rows * 4096 * 4096
+        sample = f"{rows} of 4096 rows of A (the contraction's first {rows} row slabs), full B"
+    else:
+        inp = wl["inputs"](wl["seed"])
+        done = 0
+        while True:
+            for pname, spec, nbytes in wl["programs"]:
+                t = time.perf_counter()
+                oracle.run(spec, inp)
+                t_wall += time.perf_counter() - t
+                work += nbytes
+                done += 1
+            if t_wall >= budget_s or done >= 6 * len(wl["programs"]):
+                break
+        sample = f"{done} whole-program runs of the full-size workload"
+    wall = time.perf_counter() - w0
+    ru1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+    cores = max(1, int(round(cpu / max(wall, 1e-9))))
+    scale = 1e-12 if wl["unit"] == "TFLOP/s" else 1e-9
+    return {"value": work / t_wall * scale, "unit": wl["unit"], "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(t_wall, 3), "host_threads_available": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ew_chain")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (one GPU per box, "
+              "no collectives in this library)", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+    from reduce_view_amd import rv
+    from tests.harness import to_device
+
+    wl = workloads()[args.workload]
+    rv.rv_init(0)
+    progs = [(n, rv.compile_spec(s), b) for n, s, b in wl["programs"]]
+    # rotating input sets: enough that a launch never re-reads what the
+    # previous launches left in the 256 MB Infinity Cache
+    per_set = sum(v.nbytes for v in wl["inputs"](1).values()) if args.workload != "matmul64" else 1
+    nsets = 1 if args.workload == "matmul64" else max(2, int(np.ceil(1.0e9 / per_set)) + 1)
+    seed0 = wl["seed"]
+    host_sets = [wl["inputs"](seed0 + (0 if i == 0 else 1000 + i)) for i in range(nsets)]
+    dev_sets = [{k: to_device(v) for k, v in hs.items()} for hs in host_sets]
+    del host_sets
+    outs = [p.alloc_outputs() for _, p, _ in progs]
+    wss = [p.workspace() for _, p, _ in progs]
+    stream = torch.cuda.current_stream()
+
+    ev = {n: [] for n, _, _ in progs}
+
+    def step(i, timed):
+        for j, (n, p, _) in enumerate(progs):
+            inp = dev_sets[(i + j) % nsets]
+            if timed:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            p.launch(inp, outputs=outs[j], stream=stream, workspace=wss[j])
+            if timed:
+                e1.record(stream)
+                ev[n].append((e0, e1))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    # whole-step timing (no per-kernel events inside)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i, False)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    # per-kernel launch durations, same rotation
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    per_kernel = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in ev}
+
+    total_work = sum(b for _, _, b in progs)
+    scale = 1e-12 if wl["unit"] == "TFLOP/s" else 1e-9
+    value = total_work / (ms_step * 1e-3) * scale
+    dom = max(per_kernel, key=lambda n: per_kernel[n])
+    dom_work = [b for n, _, b in progs if n == dom][0]
+    achieved = dom_work / (per_kernel[dom] * 1e-3) * scale
+    peak = MFMA_BF16_PEAK_TFLOPS if wl["bound"] == "mfma" else HBM_PEAK_GBS
+    roofline = {"bound": wl["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": wl["unit"],
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "kernel_ms": round(per_kernel[dom], 5),
+                "per_kernel_ms": {n: round(v, 5) for n, v in per_kernel.items()}}
+    out = {"metric": METRIC, "value": round(value, 2), "unit": wl["unit"], "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": wl["dtype"] if args.workload != "gemm" else "bf16",
+           "data": "synthetic", "config": {"workload": args.workload + ": " + wl["desc"],
+                                          "input_sets_rotated": nsets},
+           "roofline": roofline}
+    if rank == 0 and not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(wl, args.workload, args.cpu_budget)
+    if rank == 0:
+        print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,80 @@
+"""Builds the reduce_view shared library in-tree.
+
+The host code (graph intake, View algebra, scheduler, lowering, code
+generation, runtime) is C++17 compiled by hipcc and linked against the HIP
+runtime and the HIP runtime compiler; the device skeleton header is embedded
+as a string and compiled per program for gfx950 at rv_compile time. A second
+step compiles the device header for gfx950 with hipcc as a build check.
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "_lib", "librv.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+HOST_SOURCES = ["view.cpp", "graph.cpp", "schedule.cpp", "lower.cpp", "codegen.cpp", "runtime.cpp", "abi.cpp"]
+# hipcc flag set for any GPU code it compiles (packed FP32 instructions off)
+GPU_FLAGS = ["--offload-arch=gfx950", "-O3", "-ffp-contract=off",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _embed_header(out_dir: str) -> str:
+    src = os.path.join(CSRC, "kernels", "rv_device.hpp")
+    text = open(src).read()
+    if ")RVHDR" in text:
+        raise RuntimeError("device header contains the raw-string delimiter")
+    path = os.path.join(out_dir, "rv_device_embed.cpp")
+    body = ('// generated from csrc/kernels/rv_device.hpp\n'
+            'namespace rv {\nextern const char* const kDeviceHeader;\n'
+            'const char* const kDeviceHeader = R"RVHDR(' + text + ')RVHDR";\n}\n')
+    if not os.path.exists(path) or open(path).read() != body:
+        with open(path, "w") as f:
+            f.write(body)
+    return path
+
+
+def check_device_header(verbose: bool = False) -> None:
+    """Compiles the device skeleton (with a template instantiation of the
+    contraction) for gfx950, so a broken skeleton fails the build here."""
+    out_dir = os.path.join(HERE, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    tu = os.path.join(out_dir, "device_check.hip")
+    with open(tu, "w") as f:
+        f.write('#include <hip/hip_runtime.h>\n#include "%s"\n' % os.path.join(CSRC, "kernels", "rv_device.hpp"))
+        f.write("struct E { __device__ float operator()(float a, int, int) const { return a; }\n"
+                "  __device__ void store(int, int, float) const {} };\n"
+                "extern \"C\" __global__ void __launch_bounds__(256) chk(const unsigned short* a, "
+                "const unsigned short* b, float* p) {\n"
+                "  rv_gemm_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p);\n"
+                "  rv_gemm_bf16<false, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p);\n"
+                "  p[0] += rv_fold_sum(p, 16); }\n")
+    cmd = [HIPCC] + GPU_FLAGS + ["--cuda-device-only", "-c", tu, "-o", os.path.join(out_dir, "device_check.o")]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False) -> str:
+    out_dir = os.path.join(HERE, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(LIB), exist_ok=True)
+    embed = _embed_header(out_dir)
+    srcs = [os.path.join(CSRC, "host", s) for s in HOST_SOURCES] + [embed]
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wno-unused-function",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(CSRC, "host")] + srcs + [
+           "-o", tmp, "-lhiprtc", "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    check_device_header(verbose)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

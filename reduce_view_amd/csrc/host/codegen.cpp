@@ -1,0 +1,1055 @@
+// Code generation: renders every lowered kernel as HIP source for gfx950.
+// Shapes, strides, offsets and masks are baked in as constants, so each View
+// becomes plain integer arithmetic and range checks (limn README, "Reading
+// the schedule": views lower to index arithmetic; the printed nest is exactly
+// what the compiled backends run).
+//
+// Numerics follow the pages' primitives one for one: every value has the
+// dtype of its graph node; float16/bfloat16 values are computed in float32
+// and rounded once per node; ints wrap; the source is compiled with
+// -ffp-contract=off so a MUL and the ADD after it stay two roundings.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <functional>
+#include <set>
+#include <sstream>
+
+#include "graph.hpp"
+
+namespace rv {
+
+extern const char* const kDeviceHeader;
+
+namespace {
+
+std::string st(int dt) {  // storage type
+    switch (dt) {
+        case RV_F32: return "float";
+        case RV_BF16: return "unsigned short";
+        case RV_F16: return "_Float16";
+        case RV_F64: return "double";
+        case RV_I32: return "int";
+        case RV_I16: return "short";
+        case RV_I8: return "signed char";
+    }
+    return "?";
+}
+
+std::string vt(int dt) {  // register type
+    if (dt == RV_F64) return "double";
+    if (is_int(dt)) return "int";
+    return "float";
+}
+
+std::string ld(int dt, const std::string& e) {  // storage -> register
+    if (dt == RV_BF16) return "rv_bf2f(" + e + ")";
+    if (dt == RV_F16) return "((float)(" + e + "))";
+    if (is_int(dt)) return "((int)(" + e + "))";
+    return e;
+}
+
+std::string sv(int dt, const std::string& e) {  // register -> storage
+    switch (dt) {
+        case RV_BF16: return "rv_f2bf(" + e + ")";
+        case RV_F16: return "((_Float16)(" + e + "))";
+        case RV_I16: return "((short)(" + e + "))";
+        case RV_I8: return "((signed char)(" + e + "))";
+    }
+    return e;
+}
+
+std::string round_to(int dt, const std::string& e) {  // float32 result -> node dtype
+    if (dt == RV_BF16) return "rv_rbf(" + e + ")";
+    if (dt == RV_F16) return "rv_rhf(" + e + ")";
+    return e;
+}
+
+std::string wrap_int(int dt, const std::string& e) {
+    if (dt == RV_I16) return "((int)(short)(" + e + "))";
+    if (dt == RV_I8) return "((int)(signed char)(" + e + "))";
+    return "((int)(" + e + "))";
+}
+
+std::string flit(double v) {  // exact float32 literal
+    float f = (float)v;
+    if (std::isnan(f)) return "__builtin_nanf(\"\")";
+    if (std::isinf(f)) return f > 0 ? "__builtin_inff()" : "(-__builtin_inff())";
+    char b[64];
+    snprintf(b, sizeof b, "%af", (double)f);
+    return b;
+}
+
+std::string dlit(double v) {
+    if (std::isnan(v)) return "__builtin_nan(\"\")";
+    if (std::isinf(v)) return v > 0 ? "__builtin_inf()" : "(-__builtin_inf())";
+    char b[64];
+    snprintf(b, sizeof b, "%a", v);
+    return b;
+}
+
+float round_bf16_host(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return f;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    u &= 0xffff0000u;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+std::string const_lit(int dt, double v) {
+    switch (dt) {
+        case RV_F32: return flit(v);
+        case RV_BF16: return flit(round_bf16_host((float)v));
+        case RV_F16: return flit((float)(_Float16)(float)v);
+        case RV_F64: return dlit(v);
+        case RV_I32: return fmt("((int)%lld)", (long long)(int32_t)(int64_t)v);
+        case RV_I16: return fmt("((int)%d)", (int)(int16_t)(int64_t)v);
+        case RV_I8: return fmt("((int)%d)", (int)(int8_t)(int64_t)v);
+    }
+    return "0";
+}
+
+std::string zero_of(int dt) { return dt == RV_F64 ? "0.0" : (is_int(dt) ? "0" : "0.0f"); }
+
+// Value of one elementwise op from operand expressions.
+std::string op_code(const Kernel& k, const Ex& e, const std::string& A, const std::string& B, const std::string& C) {
+    const int dt = e.dtype;
+    const bool fl = is_float(dt);
+    switch (e.op) {
+        case RV_NEG:
+            if (fl) return "(-(" + A + "))";
+            return dt == RV_I32 ? "((int)(0u - (unsigned)(" + A + ")))" : wrap_int(dt, "-(" + A + ")");
+        case RV_EXP: return dt == RV_F64 ? "exp(" + A + ")" : round_to(dt, "expf(" + A + ")");
+        case RV_LOG: return dt == RV_F64 ? "log(" + A + ")" : round_to(dt, "logf(" + A + ")");
+        case RV_SQRT: return dt == RV_F64 ? "sqrt(" + A + ")" : round_to(dt, "sqrtf(" + A + ")");
+        case RV_RECIP: return dt == RV_F64 ? "(1.0 / (" + A + "))" : round_to(dt, "(1.0f / (" + A + "))");
+        case RV_ADD:
+        case RV_MUL: {
+            const char* o = e.op == RV_ADD ? " + " : " * ";
+            if (fl) return round_to(dt, "((" + A + ")" + o + "(" + B + "))");
+            if (dt == RV_I32) return "((int)((unsigned)(" + A + ")" + o + "(unsigned)(" + B + ")))";
+            return wrap_int(dt, "(" + A + ")" + o + "(" + B + ")");
+        }
+        case RV_CMPLT: return "(((" + A + ") < (" + B + ")) ? 1 : 0)";
+        case RV_WHERE: return "(((" + A + ") != 0) ? (" + B + ") : (" + C + "))";
+        case RV_CAST: {
+            const int s = k.ex[e.a].dtype;
+            if (s == dt) return A;
+            if (is_int(dt)) {
+                if (is_int(s)) return wrap_int(dt, A);
+                return wrap_int(dt, "(int)(" + A + ")");
+            }
+            if (dt == RV_F64) return "((double)(" + A + "))";
+            if (s == RV_F64) {
+                if (dt == RV_F16) return "((float)(_Float16)(" + A + "))";
+                return round_to(dt, "((float)(" + A + "))");
+            }
+            if (is_int(s)) return round_to(dt, "((float)(" + A + "))");
+            return round_to(dt, A);
+        }
+    }
+    fail(RV_E_INVALID, fmt("internal: no code for op %d", e.op));
+}
+
+struct Gen {
+    const Program& p;
+    const Kernel& k;
+    std::ostringstream o;
+    std::vector<Loc> params;
+    std::vector<char> written;
+    std::vector<int> param_dtype;
+    std::vector<char> live;
+    std::string I;  // index type
+    int rank = 0;
+
+    Gen(const Program& p_, const Kernel& k_) : p(p_), k(k_) {
+        rank = (int)k.domain.size();
+        live.assign(k.ex.size(), 0);
+        std::function<void(int)> mark = [&](int e) {
+            if (e < 0 || live[e]) return;
+            live[e] = 1;
+            mark(k.ex[e].a);
+            mark(k.ex[e].b);
+            mark(k.ex[e].c);
+        };
+        for (auto& s : k.stores) mark(s.ex);
+        int64_t mx = numel(k.domain);
+        auto upd = [&](const rv_view& v) {
+            int64_t lo, hi;
+            if (view_addr_range(v, &lo, &hi)) mx = std::max({mx, hi + 1, -lo + 1});
+        };
+        for (auto& L : k.leaves)
+            if (!L.zero) upd(L.v);
+        for (auto& s : k.stores) upd(s.v);
+        I = mx < (int64_t(1) << 30) ? "int" : "long long";
+    }
+
+    int param_of(const Loc& L, int dtype, bool write) {
+        for (size_t i = 0; i < params.size(); ++i)
+            if (params[i] == L) {
+                written[i] = written[i] || write;
+                return (int)i;
+            }
+        params.push_back(L);
+        written.push_back(write);
+        param_dtype.push_back(dtype);
+        return (int)params.size() - 1;
+    }
+
+    std::string pname(const Loc& L, int dtype, bool write) { return fmt("p%d", param_of(L, dtype, write)); }
+
+    std::string lit(int64_t v) { return I == "int" ? std::to_string(v) : std::to_string(v) + "LL"; }
+
+    // address of leaf/store view at domain index expressions idx[d]
+    std::string addr(const rv_view& v, const std::vector<std::string>& idx) {
+        std::string s = lit(v.offset);
+        for (int d = 0; d < rank; ++d) {
+            if (v.strides[d] == 0 || idx[d].empty()) continue;
+            s += " + (" + idx[d] + ")" + (v.strides[d] == 1 ? "" : " * " + lit(v.strides[d]));
+        }
+        return s;
+    }
+
+    bool masked(const rv_view& v, int d) const { return !(v.mask_lo[d] == 0 && v.mask_hi[d] == k.domain[d]); }
+
+    // mask condition for dims in `dims` (empty string: always true)
+    std::string mask_cond(const rv_view& v, const std::vector<std::string>& idx, const std::vector<int>& dims) {
+        std::string s;
+        for (int d : dims) {
+            if (!masked(v, d)) continue;
+            if (!s.empty()) s += " && ";
+            s += fmt("(%s) >= %s && (%s) < %s", idx[d].c_str(), lit(v.mask_lo[d]).c_str(), idx[d].c_str(),
+                     lit(v.mask_hi[d]).c_str());
+        }
+        return s;
+    }
+
+    std::string signature() {
+        std::string s;
+        for (size_t i = 0; i < params.size(); ++i) {
+            s += i ? ", " : "";
+            s += (written[i] ? "" : "const ") + st(param_dtype[i]) + "* __restrict__ " + fmt("p%zu", i);
+        }
+        return s;
+    }
+
+    std::string header() {
+        return "extern \"C\" __global__ void __launch_bounds__(256) " + k.name + "(" + signature() + ")";
+    }
+
+    bool leaf_vec_ok(const Leaf& L, int along, int vw) {
+        if (vw <= 1 || L.v.strides[along] != 1) return false;
+        if (L.v.offset % vw) return false;
+        for (int d = 0; d < rank; ++d)
+            if (d != along && k.domain[d] > 1 && L.v.strides[d] % vw) return false;
+        return true;
+    }
+
+    std::string gen();
+    std::string gen_rowmajor();
+    std::string gen_tiled();
+    std::string gen_row();
+    std::string gen_cells();
+    std::string gen_fold();
+    std::string gen_gemm();
+};
+
+// ---------------------------------------------------------------------------
+// EW, row-major plan: every thread takes chunks of VW consecutive cells of
+// the innermost dim; operands that are contiguous along it are read as one
+// vector, stride-0 operands once, others cell by cell.
+// ---------------------------------------------------------------------------
+std::string Gen::gen_rowmajor() {
+    const int X = rank - 1;
+    int maxsz = 1;
+    for (auto& s : k.stores) maxsz = std::max(maxsz, dtype_size(s.dtype));
+    const int VW = std::max(1, std::min(8, 16 / maxsz));
+    const int U = 4;
+    const int64_t NX = k.domain[X];
+    const int64_t CPR = (NX + VW - 1) / VW;
+    const int64_t TOTAL = CPR * (numel(k.domain) / NX);
+    const bool full_chunks = NX % VW == 0;
+    std::ostringstream b;
+    b << "  const " << I << " TOTAL = " << lit(TOTAL) << ";\n";
+    b << "  const " << I << " STEP = (" << I << ")gridDim.x * " << 256 * U << ";\n";
+    b << "  for (" << I << " cb = (" << I << ")blockIdx.x * " << 256 * U << " + threadIdx.x; cb < TOTAL; cb += STEP) {\n";
+    std::vector<int> outer;
+    for (int d = 0; d < X; ++d) outer.push_back(d);
+    // loads for all U chunks first, then compute and store
+    for (int u = 0; u < U; ++u) {
+        b << "    const " << I << " c" << u << " = cb + " << 256 * u << ";\n";
+        b << "    const bool cv" << u << " = c" << u << " < TOTAL;\n";
+        b << "    const " << I << " row" << u << " = c" << u << " / " << lit(CPR) << ";\n";
+        b << "    const " << I << " x" << u << " = (c" << u << " - row" << u << " * " << lit(CPR) << ") * " << VW << ";\n";
+        // outer indices
+        std::string rem = "row" + std::to_string(u);
+        for (int d = X - 1; d >= 0; --d) {
+            b << "    const " << I << " i" << d << "_" << u << " = " << rem << " % " << lit(k.domain[d]) << ";\n";
+            if (d > 0) {
+                b << "    const " << I << " q" << d << "_" << u << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
+                rem = "q" + std::to_string(d) + "_" + std::to_string(u);
+            }
+        }
+    }
+    auto idx_of = [&](int u, const std::string& x) {
+        std::vector<std::string> idx(rank);
+        for (int d = 0; d < X; ++d) idx[d] = fmt("i%d_%d", d, u);
+        idx[X] = x;
+        return idx;
+    };
+    // leaf loads
+    for (size_t li = 0; li < k.leaves.size(); ++li) {
+        const Leaf& L = k.leaves[li];
+        bool used = false;
+        for (size_t e = 0; e < k.ex.size(); ++e)
+            if (live[e] && k.ex[e].op == RV_BUFFER && k.ex[e].leaf == (int)li) used = true;
+        if (!used || L.zero) continue;
+        std::string P = pname(L.loc, L.dtype, false);
+        for (int u = 0; u < U; ++u) {
+            std::string xs = "x" + std::to_string(u);
+            auto idx = idx_of(u, xs);
+            std::string base_idx_cond = mask_cond(L.v, idx, outer);
+            std::string rowok = "cv" + std::to_string(u) + (base_idx_cond.empty() ? "" : " && " + base_idx_cond);
+            std::string V = fmt("l%zu_%d", li, u);
+            b << "    " << vt(L.dtype) << " " << V << "[" << VW << "];\n";
+            auto idx0 = idx;
+            idx0[X] = "";
+            std::string base = addr(L.v, idx0);
+            if (L.v.strides[X] == 0 && !masked(L.v, X)) {
+                b << "    { const " << vt(L.dtype) << " s = (" << rowok << ") ? " << ld(L.dtype, P + "[" + base + "]")
+                  << " : " << zero_of(L.dtype) << ";\n";
+                b << "      for (int q = 0; q < " << VW << "; ++q) " << V << "[q] = s; }\n";
+                continue;
+            }
+            bool vec = leaf_vec_ok(L, X, VW);
+            std::string xm = masked(L.v, X) ? fmt(" && %s >= %s && %s + %d <= %s", xs.c_str(), lit(L.v.mask_lo[X]).c_str(),
+                                                  xs.c_str(), VW, lit(L.v.mask_hi[X]).c_str())
+                                            : "";
+            std::string fullc = full_chunks ? "" : fmt(" && %s + %d <= %s", xs.c_str(), VW, lit(NX).c_str());
+            b << "    {\n";
+            if (vec) {
+                b << "      if (" << rowok << xm << fullc << ") {\n";
+                b << "        const rv_pack<" << st(L.dtype) << ", " << VW << "> v = rv_ldv<" << st(L.dtype) << ", " << VW
+                  << ">(" << P << " + " << base << " + " << xs << ");\n";
+                b << "        for (int q = 0; q < " << VW << "; ++q) " << V << "[q] = " << ld(L.dtype, "v.v[q]") << ";\n";
+                b << "      } else\n";
+            }
+            b << "      for (int q = 0; q < " << VW << "; ++q) {\n";
+            b << "        const " << I << " x = " << xs << " + q;\n";
+            auto idxq = idx;
+            idxq[X] = "x";
+            std::string xc = mask_cond(L.v, idxq, {X});
+            b << "        " << V << "[q] = (" << rowok << " && x < " << lit(NX) << (xc.empty() ? "" : " && " + xc)
+              << ") ? " << ld(L.dtype, P + "[" + addr(L.v, idxq) + "]") << " : " << zero_of(L.dtype) << ";\n";
+            b << "      }\n    }\n";
+        }
+    }
+    // expressions
+    for (int u = 0; u < U; ++u) {
+        for (size_t e = 0; e < k.ex.size(); ++e) {
+            if (!live[e]) continue;
+            const Ex& x = k.ex[e];
+            std::string V = fmt("e%zu_%d", e, u);
+            b << "    " << vt(x.dtype) << " " << V << "[" << VW << "];\n";
+            b << "    for (int q = 0; q < " << VW << "; ++q) " << V << "[q] = ";
+            if (x.op == RV_BUFFER) {
+                if (k.leaves[x.leaf].zero)
+                    b << zero_of(x.dtype);
+                else
+                    b << fmt("l%d_%d[q]", x.leaf, u);
+            } else if (x.op == RV_CONST) {
+                b << const_lit(x.dtype, x.cval);
+            } else {
+                auto E = [&](int i) { return i < 0 ? std::string() : fmt("e%d_%d[q]", i, u); };
+                b << op_code(k, x, E(x.a), E(x.b), E(x.c));
+            }
+            b << ";\n";
+        }
+        // stores
+        for (const Store& s : k.stores) {
+            std::string P = pname(s.loc, s.dtype, true);
+            std::string xs = "x" + std::to_string(u);
+            auto idx = idx_of(u, xs);
+            auto idx0 = idx;
+            idx0[X] = "";
+            std::string base = addr(s.v, idx0);
+            std::string cv = "cv" + std::to_string(u);
+            std::string V = fmt("e%d_%d", s.ex, u);
+            bool vec = s.v.strides[X] == 1 && VW > 1 && s.v.offset % VW == 0;
+            for (int d = 0; d < X; ++d)
+                if (k.domain[d] > 1 && s.v.strides[d] % VW) vec = false;
+            std::string fullc = full_chunks ? "" : fmt(" && %s + %d <= %s", xs.c_str(), VW, lit(NX).c_str());
+            b << "    {\n";
+            if (vec) {
+                b << "      if (" << cv << fullc << ") {\n        rv_pack<" << st(s.dtype) << ", " << VW << "> v;\n";
+                b << "        for (int q = 0; q < " << VW << "; ++q) v.v[q] = " << sv(s.dtype, V + "[q]") << ";\n";
+                b << "        rv_stv<" << st(s.dtype) << ", " << VW << ">(" << P << " + " << base << " + " << xs << ", v);\n";
+                b << "      } else\n";
+            }
+            b << "      for (int q = 0; q < " << VW << "; ++q) {\n";
+            b << "        const " << I << " x = " << xs << " + q;\n";
+            auto idxq = idx;
+            idxq[X] = "x";
+            b << "        if (" << cv << " && x < " << lit(NX) << ") " << P << "[" << addr(s.v, idxq) << "] = "
+              << sv(s.dtype, V + "[q]") << ";\n";
+            b << "      }\n    }\n";
+        }
+    }
+    b << "  }\n";
+    return b.str();
+}
+
+// ---------------------------------------------------------------------------
+// EW, tiled plan (transpose and chains with a permuted operand): a 64 x 64
+// tile of the (Y, X) domain per workgroup. Operands contiguous along Y are
+// read along Y (coalesced) into an LDS tile padded by one element per row,
+// then read back along X; the others are read along X directly. Interior
+// tiles run without range checks; edge tiles check the domain and masks.
+// ---------------------------------------------------------------------------
+std::string Gen::gen_tiled() {
+    const int X = rank - 1, Y = rank - 2;
+    const int64_t NX = k.domain[X], NY = k.domain[Y];
+    std::ostringstream b;
+    std::vector<int> staged(k.leaves.size(), 0);
+    std::vector<int> used(k.leaves.size(), 0);
+    for (size_t e = 0; e < k.ex.size(); ++e)
+        if (live[e] && k.ex[e].op == RV_BUFFER) used[k.ex[e].leaf] = 1;
+    int ns = 0;
+    for (size_t l = 0; l < k.leaves.size(); ++l) {
+        const Leaf& L = k.leaves[l];
+        if (used[l] && !L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) {
+            staged[l] = 1;
+            b << "  __shared__ " << vt(L.dtype) << " t" << l << "[64][65];\n";
+            ++ns;
+        }
+    }
+    b << "  const int t = threadIdx.x;\n";
+    b << "  const " << I << " X0 = (" << I << ")blockIdx.x * 64, Y0 = (" << I << ")blockIdx.y * 64;\n";
+    std::vector<int> outer;
+    {
+        std::string rem = "(" + I + ")blockIdx.z";
+        for (int d = Y - 1; d >= 0; --d) {
+            outer.push_back(d);
+            b << "  const " << I << " i" << d << " = " << rem << " % " << lit(k.domain[d]) << ";\n";
+            if (d > 0) {
+                b << "  const " << I << " q" << d << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
+                rem = "q" + std::to_string(d);
+            }
+        }
+    }
+    auto idx_at = [&](const std::string& y, const std::string& x) {
+        std::vector<std::string> idx(rank);
+        for (int d = 0; d < Y; ++d) idx[d] = fmt("i%d", d);
+        idx[Y] = y;
+        idx[X] = x;
+        return idx;
+    };
+    // interior: whole tile inside the domain and inside every used leaf's mask
+    std::string inter = fmt("X0 + 64 <= %s && Y0 + 64 <= %s", lit(NX).c_str(), lit(NY).c_str());
+    for (size_t l = 0; l < k.leaves.size(); ++l) {
+        const Leaf& L = k.leaves[l];
+        if (!used[l] || L.zero) continue;
+        for (int d = 0; d < rank; ++d) {
+            if (!masked(L.v, d)) continue;
+            if (d == X)
+                inter += fmt(" && X0 >= %s && X0 + 64 <= %s", lit(L.v.mask_lo[d]).c_str(), lit(L.v.mask_hi[d]).c_str());
+            else if (d == Y)
+                inter += fmt(" && Y0 >= %s && Y0 + 64 <= %s", lit(L.v.mask_lo[d]).c_str(), lit(L.v.mask_hi[d]).c_str());
+            else
+                inter += fmt(" && i%d >= %s && i%d < %s", d, lit(L.v.mask_lo[d]).c_str(), d, lit(L.v.mask_hi[d]).c_str());
+        }
+    }
+    b << "  const bool interior = " << inter << ";\n";
+    // staged loads: thread reads 4 consecutive y at column lx
+    if (ns) {
+        b << "  {\n    const int ly = (t & 15) * 4, lx0 = t >> 4;\n";
+        for (size_t l = 0; l < k.leaves.size(); ++l) {
+            if (!staged[l]) continue;
+            const Leaf& L = k.leaves[l];
+            std::string P = pname(L.loc, L.dtype, false);
+            bool vec = leaf_vec_ok(L, Y, 4);
+            b << "    for (int j = 0; j < 4; ++j) {\n      const int lx = lx0 + 16 * j;\n";
+            auto idx = idx_at("Y0 + ly", "X0 + lx");
+            if (vec) {
+                b << "      if (interior) {\n";
+                b << "        const rv_pack<" << st(L.dtype) << ", 4> v = rv_ldv<" << st(L.dtype) << ", 4>(" << P << " + "
+                  << addr(L.v, idx) << ");\n";
+                b << "        for (int q = 0; q < 4; ++q) t" << l << "[lx][ly + q] = " << ld(L.dtype, "v.v[q]") << ";\n";
+                b << "      } else\n";
+            }
+            b << "      for (int q = 0; q < 4; ++q) {\n";
+            b << "        const " << I << " y = Y0 + ly + q, x = X0 + lx;\n";
+            auto idq = idx_at("y", "x");
+            std::vector<int> all;
+            for (int d = 0; d < rank; ++d) all.push_back(d);
+            std::string mc = mask_cond(L.v, idq, all);
+            b << "        t" << l << "[lx][ly + q] = (interior || (y < " << lit(NY) << " && x < " << lit(NX)
+              << (mc.empty() ? "" : " && " + mc) << ")) ? " << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << " : "
+              << zero_of(L.dtype) << ";\n";
+            b << "      }\n    }\n";
+        }
+        b << "  }\n  __syncthreads();\n";
+    }
+    b << "  const int tx = (t & 15) * 4, ty0 = t >> 4;\n";
+    // body, emitted twice: without range checks (interior) and with them
+    for (int edge = 0; edge < 2; ++edge) {
+        b << (edge ? "  else {\n" : "  if (interior) {\n");
+        b << "  for (int j = 0; j < 4; ++j) {\n";
+        b << "    const " << I << " y = Y0 + ty0 + 16 * j;\n";
+        // direct leaves
+        for (size_t l = 0; l < k.leaves.size(); ++l) {
+            const Leaf& L = k.leaves[l];
+            if (!used[l] || L.zero || staged[l]) continue;
+            std::string P = pname(L.loc, L.dtype, false);
+            std::string V = fmt("l%zu", l);
+            b << "    " << vt(L.dtype) << " " << V << "[4];\n";
+            auto idx = idx_at("y", "X0 + tx");
+            if (!edge && leaf_vec_ok(L, X, 4)) {
+                b << "    { const rv_pack<" << st(L.dtype) << ", 4> v = rv_ldv<" << st(L.dtype) << ", 4>(" << P << " + "
+                  << addr(L.v, idx) << ");\n";
+                b << "      for (int q = 0; q < 4; ++q) " << V << "[q] = " << ld(L.dtype, "v.v[q]") << "; }\n";
+            } else {
+                b << "    for (int q = 0; q < 4; ++q) {\n      const " << I << " x = X0 + tx + q;\n";
+                auto idq = idx_at("y", "x");
+                if (edge) {
+                    std::vector<int> all;
+                    for (int d = 0; d < rank; ++d) all.push_back(d);
+                    std::string mc = mask_cond(L.v, idq, all);
+                    b << "      " << V << "[q] = (y < " << lit(NY) << " && x < " << lit(NX) << (mc.empty() ? "" : " && " + mc)
+                      << ") ? " << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << " : " << zero_of(L.dtype) << ";\n";
+                } else {
+                    b << "      " << V << "[q] = " << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << ";\n";
+                }
+                b << "    }\n";
+            }
+        }
+        for (size_t e = 0; e < k.ex.size(); ++e) {
+            if (!live[e]) continue;
+            const Ex& x = k.ex[e];
+            b << "    " << vt(x.dtype) << " e" << e << "[4];\n    for (int q = 0; q < 4; ++q) e" << e << "[q] = ";
+            if (x.op == RV_BUFFER) {
+                const Leaf& L = k.leaves[x.leaf];
+                if (L.zero)
+                    b << zero_of(x.dtype);
+                else if (staged[x.leaf])
+                    b << "t" << x.leaf << "[tx + q][ty0 + 16 * j]";
+                else
+                    b << "l" << x.leaf << "[q]";
+            } else if (x.op == RV_CONST) {
+                b << const_lit(x.dtype, x.cval);
+            } else {
+                auto E = [&](int i) { return i < 0 ? std::string() : fmt("e%d[q]", i); };
+                b << op_code(k, x, E(x.a), E(x.b), E(x.c));
+            }
+            b << ";\n";
+        }
+        for (const Store& s : k.stores) {
+            std::string P = pname(s.loc, s.dtype, true);
+            auto idx = idx_at("y", "X0 + tx");
+            bool vec = !edge && s.v.strides[X] == 1 && s.v.offset % 4 == 0;
+            for (int d = 0; d < X; ++d)
+                if (k.domain[d] > 1 && s.v.strides[d] % 4) vec = false;
+            if (vec) {
+                b << "    { rv_pack<" << st(s.dtype) << ", 4> v;\n      for (int q = 0; q < 4; ++q) v.v[q] = "
+                  << sv(s.dtype, fmt("e%d[q]", s.ex)) << ";\n";
+                b << "      rv_stv<" << st(s.dtype) << ", 4>(" << P << " + " << addr(s.v, idx) << ", v); }\n";
+            } else {
+                b << "    for (int q = 0; q < 4; ++q) {\n      const " << I << " x = X0 + tx + q;\n";
+                auto idq = idx_at("y", "x");
+                b << "      " << (edge ? fmt("if (y < %s && x < %s) ", lit(NY).c_str(), lit(NX).c_str()) : "") << P << "["
+                  << addr(s.v, idq) << "] = " << sv(s.dtype, fmt("e%d[q]", s.ex)) << ";\n    }\n";
+            }
+        }
+        b << "  }\n  }\n";
+    }
+    return b.str();
+}
+
+// ---------------------------------------------------------------------------
+// ROW plan: T threads cooperate on one row (RPW rows per workgroup); a thread
+// keeps its E = NV * VW cells of every full-row value in registers, so the
+// row is read once. Reductions fold a thread's cells, then a butterfly over
+// the row's lanes, then (T > 64) the waves' totals in a fixed order in LDS.
+// Row-constant operands (weights) are read once per workgroup.
+// ---------------------------------------------------------------------------
+std::string Gen::gen_row() {
+    std::vector<int> rd, kd;
+    for (int d = 0; d < rank; ++d) ((k.rdims >> d) & 1u ? rd : kd).push_back(d);
+    int64_t NR = 1, NK = 1;
+    for (int d : rd) NR *= k.domain[d];
+    for (int d : kd) NK *= k.domain[d];
+    // plan values (mirrors lower.cpp)
+    int T = 0, VW = 0;
+    sscanf(k.plan_json.c_str(), "\"threads_per_row\":%d,\"rows_per_block\":%*d,\"vec\":%d", &T, &VW);
+    const int RPW = 256 / T;
+    const int NV = (int)((NR + (int64_t)T * VW - 1) / ((int64_t)T * VW));
+    const int E = NV * VW;
+    const bool ragged = NR % ((int64_t)T * VW) != 0;
+    const int W = T > 64 ? T / 64 : 1;
+    const int nred_ = [&] {
+        int n = 0;
+        for (size_t e = 0; e < k.ex.size(); ++e)
+            if (live[e] && (k.ex[e].op == RV_SUM || k.ex[e].op == RV_MAX)) ++n;
+        return n;
+    }();
+    const bool single = rd.size() == 1;
+    const int R = single ? rd[0] : -1;
+    // stat flags on lowered views
+    std::vector<char> stat(k.ex.size(), 0);
+    for (size_t e = 0; e < k.ex.size(); ++e) {
+        const Ex& x = k.ex[e];
+        if (x.op == RV_BUFFER) {
+            const Leaf& L = k.leaves[x.leaf];
+            bool s = true;
+            for (int d : rd)
+                if (!L.zero && (L.v.strides[d] != 0 || masked(L.v, d))) s = false;
+            stat[e] = s;
+        } else if (x.op == RV_CONST || x.op == RV_SUM || x.op == RV_MAX) {
+            stat[e] = 1;
+        } else {
+            stat[e] = (x.a < 0 || stat[x.a]) && (x.b < 0 || stat[x.b]) && (x.c < 0 || stat[x.c]);
+        }
+    }
+    // hoisted leaves: full along the row, constant across rows, unmasked across rows
+    auto hoistable = [&](const Leaf& L) {
+        for (int d : kd)
+            if (L.v.strides[d] != 0 || masked(L.v, d)) return false;
+        return true;
+    };
+    std::ostringstream b;
+    b << "  const int t = threadIdx.x, lt = t % " << T << ", lr = t / " << T << ";\n";
+    if (T > 64 && nred_) b << "  __shared__ float red[" << nred_ << "][" << RPW << "][" << W << "];\n";
+    // element index helpers: n(v, i) = (v * T + lt) * VW + i
+    auto nexpr = [&](const std::string& v, const std::string& i) {
+        return fmt("(((%s) * %d + lt) * %d + (%s))", v.c_str(), T, VW, i.c_str());
+    };
+    // reduced-dim index expressions from a flat in-row index n
+    auto red_idx = [&](std::vector<std::string>& idx, const std::string& n) {
+        if (single) {
+            idx[R] = n;
+            return;
+        }
+        std::string rem = n;
+        for (size_t j = rd.size(); j-- > 0;) {
+            int d = rd[j];
+            idx[d] = j ? fmt("((%s) %% %s)", rem.c_str(), lit(k.domain[d]).c_str()) : rem;
+            if (j) rem = fmt("((%s) / %s)", rem.c_str(), lit(k.domain[d]).c_str());
+        }
+    };
+    std::vector<int> used(k.leaves.size(), 0);
+    for (size_t e = 0; e < k.ex.size(); ++e)
+        if (live[e] && k.ex[e].op == RV_BUFFER) used[k.ex[e].leaf] = 1;
+    auto emit_full_load = [&](std::ostringstream& s, int l, const std::string& rowok, const std::vector<std::string>& kidx,
+                              const std::string& V) {
+        const Leaf& L = k.leaves[l];
+        std::string P = pname(L.loc, L.dtype, false);
+        s << "    " << vt(L.dtype) << " " << V << "[" << E << "];\n";
+        s << "    for (int v = 0; v < " << NV << "; ++v) {\n";
+        s << "      const " << I << " n0 = " << nexpr("v", "0") << ";\n";
+        std::vector<std::string> idx = kidx;
+        bool vec = single && leaf_vec_ok(L, R, VW);
+        if (vec) {
+            idx[R] = "n0";
+            std::string mc = masked(L.v, R) ? fmt(" && n0 >= %s && n0 + %d <= %s", lit(L.v.mask_lo[R]).c_str(), VW,
+                                                  lit(L.v.mask_hi[R]).c_str())
+                                            : "";
+            std::string rg = ragged ? fmt(" && n0 + %d <= %s", VW, lit(NR).c_str()) : "";
+            s << "      if (" << rowok << mc << rg << ") {\n";
+            s << "        const rv_pack<" << st(L.dtype) << ", " << VW << "> p = rv_ldv<" << st(L.dtype) << ", " << VW
+              << ">(" << P << " + " << addr(L.v, idx) << ");\n";
+            s << "        for (int i = 0; i < " << VW << "; ++i) " << V << "[v * " << VW << " + i] = " << ld(L.dtype, "p.v[i]")
+              << ";\n      } else\n";
+        }
+        s << "      for (int i = 0; i < " << VW << "; ++i) {\n";
+        s << "        const " << I << " n = n0 + i;\n";
+        red_idx(idx, "n");
+        std::string mc = mask_cond(L.v, idx, rd);
+        s << "        " << V << "[v * " << VW << " + i] = (" << rowok << " && n < " << lit(NR) << (mc.empty() ? "" : " && " + mc)
+          << ") ? " << ld(L.dtype, P + "[" + addr(L.v, idx) + "]") << " : " << zero_of(L.dtype) << ";\n";
+        s << "      }\n    }\n";
+    };
+    // hoisted loads
+    std::vector<int> hoisted(k.leaves.size(), 0);
+    {
+        std::vector<std::string> kidx(rank);
+        for (size_t l = 0; l < k.leaves.size(); ++l) {
+            const Leaf& L = k.leaves[l];
+            if (!used[l] || L.zero) continue;
+            bool full = false;
+            for (int d : rd)
+                if (L.v.strides[d] != 0 || masked(L.v, d)) full = true;
+            if (full && hoistable(L)) {
+                hoisted[l] = 1;
+                std::ostringstream s;
+                emit_full_load(s, (int)l, "true", kidx, fmt("h%zu", l));
+                b << s.str();
+            }
+        }
+    }
+    const int64_t NRG = (NK + RPW - 1) / RPW;
+    b << "  for (" << I << " rg = blockIdx.x; rg < " << lit(NRG) << "; rg += gridDim.x) {\n";
+    if (T > 64 && nred_) b << "    __syncthreads();\n";
+    b << "    const " << I << " r = rg * " << RPW << " + lr;\n";
+    b << "    const bool rv = r < " << lit(NK) << ";\n";
+    std::vector<std::string> kidx(rank);
+    {
+        std::string rem = "r";
+        for (size_t j = kd.size(); j-- > 0;) {
+            int d = kd[j];
+            b << "    const " << I << " i" << d << " = " << (j ? fmt("%s %% %s", rem.c_str(), lit(k.domain[d]).c_str()) : rem)
+              << ";\n";
+            kidx[d] = fmt("i%d", d);
+            if (j) {
+                b << "    const " << I << " q" << d << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
+                rem = fmt("q%d", d);
+            }
+        }
+    }
+    int red_slot = 0;
+    for (size_t e = 0; e < k.ex.size(); ++e) {
+        if (!live[e]) continue;
+        const Ex& x = k.ex[e];
+        std::string V = fmt("e%zu", e);
+        if (x.op == RV_BUFFER) {
+            const Leaf& L = k.leaves[x.leaf];
+            if (L.zero) {
+                b << "    const " << vt(x.dtype) << " " << V << " = " << zero_of(x.dtype) << ";\n";
+                stat[e] = 1;
+                continue;
+            }
+            if (hoisted[x.leaf]) {
+                b << "    " << vt(x.dtype) << "* " << V << " = h" << x.leaf << ";\n";
+                continue;
+            }
+            std::string kc = mask_cond(L.v, kidx, kd);
+            std::string rowok = "rv" + (kc.empty() ? std::string() : " && " + kc);
+            if (stat[e]) {
+                std::string P = pname(L.loc, L.dtype, false);
+                b << "    const " << vt(x.dtype) << " " << V << " = (" << rowok << ") ? "
+                  << ld(L.dtype, P + "[" + addr(L.v, kidx) + "]") << " : " << zero_of(x.dtype) << ";\n";
+            } else {
+                std::ostringstream s;
+                emit_full_load(s, x.leaf, rowok, kidx, V);
+                b << s.str();
+            }
+            continue;
+        }
+        if (x.op == RV_CONST) {
+            b << "    const " << vt(x.dtype) << " " << V << " = " << const_lit(x.dtype, x.cval) << ";\n";
+            continue;
+        }
+        auto opnd = [&](int i, const std::string& q) -> std::string {
+            if (i < 0) return "";
+            return stat[i] ? fmt("e%d", i) : fmt("e%d[%s]", i, q.c_str());
+        };
+        if (x.op == RV_SUM || x.op == RV_MAX) {
+            const bool sum = x.op == RV_SUM;
+            b << "    float " << V << ";\n    {\n";
+            b << "      float acc = " << (sum ? "0.0f" : "(-__builtin_inff())") << ";\n";
+            b << "      for (int q = 0; q < " << E << "; ++q) {\n";
+            std::string val = opnd(x.a, "q");
+            if (ragged)
+                b << "        if (" << nexpr("q / " + std::to_string(VW), "q % " + std::to_string(VW)) << " < " << lit(NR)
+                  << ") ";
+            else
+                b << "        ";
+            b << (sum ? "acc = acc + " + val : "acc = rv_maxf(acc, " + val + ")") << ";\n      }\n";
+            int g = std::min(T, 64);
+            b << "      acc = rv_group_" << (sum ? "sum" : "max") << "<" << g << ">(acc);\n";
+            if (T > 64) {
+                b << "      if ((t & 63) == 0) red[" << red_slot << "][lr][lt >> 6] = acc;\n      __syncthreads();\n";
+                b << "      acc = red[" << red_slot << "][lr][0];\n";
+                for (int w = 1; w < W; ++w)
+                    b << "      acc = " << (sum ? fmt("acc + red[%d][lr][%d]", red_slot, w)
+                                                : fmt("rv_maxf(acc, red[%d][lr][%d])", red_slot, w))
+                      << ";\n";
+                ++red_slot;
+            }
+            b << "      " << V << " = " << round_to(x.dtype, "acc") << ";\n    }\n";
+            continue;
+        }
+        if (stat[e]) {
+            b << "    const " << vt(x.dtype) << " " << V << " = " << op_code(k, x, opnd(x.a, ""), opnd(x.b, ""), opnd(x.c, ""))
+              << ";\n";
+        } else {
+            b << "    " << vt(x.dtype) << " " << V << "[" << E << "];\n";
+            b << "    for (int q = 0; q < " << E << "; ++q) " << V << "[q] = "
+              << op_code(k, x, opnd(x.a, "q"), opnd(x.b, "q"), opnd(x.c, "q")) << ";\n";
+        }
+    }
+    for (const Store& s : k.stores) {
+        std::string P = pname(s.loc, s.dtype, true);
+        bool sstat = true;
+        for (int d : rd)
+            if (s.v.strides[d] != 0) sstat = false;
+        if (sstat) {
+            std::string val = stat[s.ex] ? fmt("e%d", s.ex) : fmt("e%d[0]", s.ex);
+            b << "    if (lt == 0 && rv) " << P << "[" << addr(s.v, kidx) << "] = " << sv(s.dtype, val) << ";\n";
+            continue;
+        }
+        std::string val = stat[s.ex] ? fmt("e%d", s.ex) : fmt("e%d[v * %d + i]", s.ex, VW);
+        b << "    for (int v = 0; v < " << NV << "; ++v) {\n";
+        b << "      const " << I << " n0 = " << nexpr("v", "0") << ";\n";
+        std::vector<std::string> idx = kidx;
+        bool vec = single && s.v.strides[R] == 1 && s.v.offset % VW == 0;
+        for (int d : kd)
+            if (k.domain[d] > 1 && s.v.strides[d] % VW) vec = false;
+        if (vec) {
+            idx[R] = "n0";
+            std::string rg = ragged ? fmt(" && n0 + %d <= %s", VW, lit(NR).c_str()) : "";
+            b << "      if (rv" << rg << ") {\n        rv_pack<" << st(s.dtype) << ", " << VW << "> p;\n";
+            b << "        for (int i = 0; i < " << VW << "; ++i) p.v[i] = " << sv(s.dtype, val) << ";\n";
+            b << "        rv_stv<" << st(s.dtype) << ", " << VW << ">(" << P << " + " << addr(s.v, idx) << ", p);\n";
+            b << "      } else\n";
+        }
+        b << "      for (int i = 0; i < " << VW << "; ++i) {\n        const " << I << " n = n0 + i;\n";
+        red_idx(idx, "n");
+        b << "        if (rv && n < " << lit(NR) << ") " << P << "[" << addr(s.v, idx) << "] = " << sv(s.dtype, val) << ";\n";
+        b << "      }\n    }\n";
+    }
+    b << "  }\n";
+    return b.str();
+}
+
+// ---------------------------------------------------------------------------
+// REDUCE, cells plan: one lane per output cell (lanes walk the dim that is
+// stride-1 in the most buffers), the reduce dims walked in ascending order
+// inside the lane, so every cell folds exactly as the serial nest does.
+// ---------------------------------------------------------------------------
+std::string Gen::gen_cells() {
+    std::vector<int> rd, kd;
+    for (int d = 0; d < rank; ++d) ((k.rdims >> d) & 1u ? rd : kd).push_back(d);
+    int64_t cells = 1;
+    for (int d : kd) cells *= k.domain[d];
+    std::vector<int> order;  // decomposition order: other kept dims, lane dim innermost
+    for (int d : kd)
+        if (d != k.lane_dim) order.push_back(d);
+    if (k.lane_dim >= 0) order.push_back(k.lane_dim);
+    std::ostringstream b;
+    b << "  for (" << I << " cell = (" << I << ")blockIdx.x * 256 + threadIdx.x; cell < " << lit(cells)
+      << "; cell += (" << I << ")gridDim.x * 256) {\n";
+    std::vector<std::string> idx(rank);
+    {
+        std::string rem = "cell";
+        for (size_t j = order.size(); j-- > 0;) {
+            int d = order[j];
+            b << "    const " << I << " i" << d << " = " << (j ? fmt("%s %% %s", rem.c_str(), lit(k.domain[d]).c_str()) : rem)
+              << ";\n";
+            idx[d] = fmt("i%d", d);
+            if (j) {
+                b << "    const " << I << " q" << d << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
+                rem = fmt("q%d", d);
+            }
+        }
+    }
+    // the reduce at the root
+    int root = -1;
+    for (size_t e = 0; e < k.ex.size(); ++e)
+        if (live[e] && (k.ex[e].op == RV_SUM || k.ex[e].op == RV_MAX)) root = (int)e;
+    if (root < 0) fail(RV_E_INVALID, "internal: REDUCE kernel without a reduce");
+    const Ex& R = k.ex[root];
+    // invariant values (do not depend on reduce dims)
+    std::vector<char> inv(k.ex.size(), 0);
+    for (size_t e = 0; e < k.ex.size(); ++e) {
+        const Ex& x = k.ex[e];
+        if ((int)e == root) continue;
+        if (x.op == RV_BUFFER) {
+            const Leaf& L = k.leaves[x.leaf];
+            bool s = true;
+            for (int d : rd)
+                if (!L.zero && (L.v.strides[d] != 0 || masked(L.v, d))) s = false;
+            inv[e] = s;
+        } else if (x.op == RV_CONST) {
+            inv[e] = 1;
+        } else {
+            inv[e] = (x.a < 0 || inv[x.a]) && (x.b < 0 || inv[x.b]) && (x.c < 0 || inv[x.c]);
+        }
+    }
+    auto emit = [&](size_t e, const std::string& ind) {
+        const Ex& x = k.ex[e];
+        std::string V = fmt("e%zu", e);
+        if (x.op == RV_BUFFER) {
+            const Leaf& L = k.leaves[x.leaf];
+            if (L.zero) {
+                b << ind << "const " << vt(x.dtype) << " " << V << " = " << zero_of(x.dtype) << ";\n";
+                return;
+            }
+            std::string P = pname(L.loc, L.dtype, false);
+            std::vector<int> all;
+            for (int d = 0; d < rank; ++d) all.push_back(d);
+            std::string mc = mask_cond(L.v, idx, all);
+            b << ind << "const " << vt(x.dtype) << " " << V << " = " << (mc.empty() ? "" : "(" + mc + ") ? ")
+              << ld(L.dtype, P + "[" + addr(L.v, idx) + "]") << (mc.empty() ? "" : " : " + zero_of(x.dtype)) << ";\n";
+        } else if (x.op == RV_CONST) {
+            b << ind << "const " << vt(x.dtype) << " " << V << " = " << const_lit(x.dtype, x.cval) << ";\n";
+        } else {
+            auto E = [&](int i) { return i < 0 ? std::string() : fmt("e%d", i); };
+            b << ind << "const " << vt(x.dtype) << " " << V << " = " << op_code(k, x, E(x.a), E(x.b), E(x.c)) << ";\n";
+        }
+    };
+    for (size_t e = 0; e < k.ex.size(); ++e)
+        if (live[e] && inv[e] && (int)e != root) emit(e, "    ");
+    const int dt = R.dtype;
+    const bool sum = R.op == RV_SUM;
+    std::string acc_t = dt == RV_F64 ? "double" : (is_int(dt) ? (sum ? "unsigned" : "int") : "float");
+    std::string ident;
+    if (sum)
+        ident = dt == RV_F64 ? "0.0" : (is_int(dt) ? "0u" : "0.0f");
+    else if (is_float(dt))
+        ident = dt == RV_F64 ? "(-__builtin_inf())" : "(-__builtin_inff())";
+    else
+        ident = dt == RV_I32 ? "(-2147483647 - 1)" : (dt == RV_I16 ? "(-32768)" : "(-128)");
+    b << "    " << acc_t << " acc = " << ident << ";\n";
+    std::string ind = "    ";
+    for (int d : rd) {
+        b << ind << "for (" << I << " i" << d << " = 0; i" << d << " < " << lit(k.domain[d]) << "; ++i" << d << ") {\n";
+        idx[d] = fmt("i%d", d);
+        ind += "  ";
+    }
+    for (size_t e = 0; e < k.ex.size(); ++e)
+        if (live[e] && !inv[e] && (int)e != root) emit(e, ind);
+    std::string v = fmt("e%d", R.a);
+    if (sum)
+        b << ind << "acc = acc + " << (is_int(dt) ? "(unsigned)" + v : v) << ";\n";
+    else if (is_float(dt))
+        b << ind << "acc = " << (dt == RV_F64 ? "rv_maxd" : "rv_maxf") << "(acc, " << v << ");\n";
+    else
+        b << ind << "acc = " << v << " > acc ? " << v << " : acc;\n";
+    for (size_t j = 0; j < rd.size(); ++j) {
+        ind.resize(ind.size() - 2);
+        b << ind << "}\n";
+    }
+    std::string res = is_int(dt) ? wrap_int(dt, "acc") : round_to(dt, "acc");
+    b << "    const " << vt(dt) << " e" << root << " = " << res << ";\n";
+    for (int d : rd) idx[d] = "";
+    for (const Store& s : k.stores) {
+        std::string P = pname(s.loc, s.dtype, true);
+        b << "    " << P << "[" << addr(s.v, idx) << "] = " << sv(s.dtype, fmt("e%d", s.ex)) << ";\n";
+    }
+    b << "  }\n";
+    return b.str();
+}
+
+std::string Gen::gen_fold() {
+    const Ex& R = k.ex[0];
+    std::string src = pname(Loc{2, k.fold_src_region}, RV_F32, false);
+    std::ostringstream b;
+    b << "  const float s = rv_fold_sum(" << src << ", " << k.fold_count << "LL);\n";
+    for (const Store& s : k.stores) {
+        std::string P = pname(s.loc, s.dtype, true);
+        b << "  if (threadIdx.x == 0) " << P << "[" << s.v.offset << "] = " << sv(s.dtype, round_to(R.dtype, "s")) << ";\n";
+    }
+    return b.str();
+}
+
+// ---------------------------------------------------------------------------
+// MFMA: the hand-written contraction skeleton plus a generated epilogue
+// functor that evaluates the graph's elementwise tail on y at (m, n).
+// ---------------------------------------------------------------------------
+std::string Gen::gen_gemm() {
+    const Leaf& A = k.leaves[k.mfma_a];
+    const Leaf& B = k.leaves[k.mfma_b];
+    const bool kn = B.v.strides[1] == 1;
+    std::string pa = pname(A.loc, RV_BF16, false);
+    std::string pb = pname(B.loc, RV_BF16, false);
+    std::ostringstream f;  // functor body
+    std::string sname = k.name + "_epi";
+    std::vector<std::string> idx = {"m", "n", ""};
+    std::ostringstream body;
+    int final_ex = k.stores[0].ex;
+    for (size_t e = 0; e < k.ex.size(); ++e) {
+        if (!live[e]) continue;
+        const Ex& x = k.ex[e];
+        std::string V = fmt("e%zu", e);
+        if (x.op == EX_MFMA_ACC) {
+            body << "    const float " << V << " = acc;\n";
+        } else if (x.op == RV_BUFFER) {
+            const Leaf& L = k.leaves[x.leaf];
+            if (L.zero) {
+                body << "    const " << vt(x.dtype) << " " << V << " = " << zero_of(x.dtype) << ";\n";
+                continue;
+            }
+            std::string P = pname(L.loc, L.dtype, false);
+            std::string mc = mask_cond(L.v, idx, {0, 1});
+            body << "    const " << vt(x.dtype) << " " << V << " = " << (mc.empty() ? "" : "(" + mc + ") ? ")
+                 << ld(L.dtype, "P" + P + "[" + addr(L.v, idx) + "]") << (mc.empty() ? "" : " : " + zero_of(x.dtype))
+                 << ";\n";
+        } else if (x.op == RV_CONST) {
+            body << "    const " << vt(x.dtype) << " " << V << " = " << const_lit(x.dtype, x.cval) << ";\n";
+        } else {
+            auto E = [&](int i) { return i < 0 ? std::string() : fmt("e%d", i); };
+            body << "    const " << vt(x.dtype) << " " << V << " = " << op_code(k, x, E(x.a), E(x.b), E(x.c)) << ";\n";
+        }
+    }
+    std::ostringstream stores;
+    if (!k.mfma_partial)
+        for (const Store& s : k.stores) {
+            std::string P = pname(s.loc, s.dtype, true);
+            stores << "    P" << P << "[" << addr(s.v, idx) << "] = " << sv(s.dtype, "v") << ";\n";
+        }
+    std::string partials;
+    if (k.mfma_partial) partials = pname(Loc{2, k.partials_region}, RV_F32, true);
+    // functor holds every parameter pointer (prefixed P)
+    std::string sig = signature();
+    f << "struct " << sname << " {\n";
+    for (size_t i = 0; i < params.size(); ++i)
+        f << "  " << (written[i] ? "" : "const ") << st(param_dtype[i]) << "* __restrict__ Pp" << i << ";\n";
+    f << "  __device__ __forceinline__ float operator()(float acc, int m, int n) const {\n" << body.str();
+    f << "    return (float)(e" << final_ex << ");\n  }\n";
+    f << "  __device__ __forceinline__ void store(int m, int n, float v) const {\n" << stores.str() << "  }\n};\n";
+    std::ostringstream b;
+    b << "  const " << sname << " epi{";
+    for (size_t i = 0; i < params.size(); ++i) b << (i ? ", " : "") << "p" << i;
+    b << "};\n";
+    const int64_t M = k.domain[0], N = k.domain[1], K = k.domain[2];
+    const int64_t lda = A.v.strides[0];
+    const int64_t ldb = kn ? B.v.strides[2] : B.v.strides[1];
+    b << "  rv_gemm_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ">(" << pa << ", " << pb
+      << ", " << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", "
+      << K << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ");\n";
+    return f.str() + "@@BODY@@" + b.str();
+}
+
+std::string Gen::gen() {
+    std::string body;
+    std::string pre;
+    if (k.plan == "empty") return "";
+    switch (k.cls) {
+        case KClass::EW: body = k.plan == "tiled2d" ? gen_tiled() : gen_rowmajor(); break;
+        case KClass::ROW: body = gen_row(); break;
+        case KClass::REDUCE: body = gen_cells(); break;
+        case KClass::FOLD: body = gen_fold(); break;
+        case KClass::MFMA: {
+            std::string s = gen_gemm();
+            size_t at = s.find("@@BODY@@");
+            pre = s.substr(0, at);
+            body = s.substr(at + 8);
+            break;
+        }
+    }
+    return pre + header() + " {\n" + body + "}\n";
+}
+
+}  // namespace
+
+std::string codegen(const Program& p) {
+    std::string s = "// generated by reduce_view for gfx950\n";
+    s += kDeviceHeader;
+    s += "\n";
+    for (const Kernel& k : p.kernels) {
+        Gen g(p, k);
+        s += "\n" + g.gen();
+    }
+    return s;
+}
+
+// Parameter list of a kernel, in the order its generated signature uses.
+std::vector<Loc> kernel_param_locs(const Program& p, const Kernel& k) {
+    Gen g(p, k);
+    g.gen();
+    return g.params;
+}
+
+}  // namespace rv

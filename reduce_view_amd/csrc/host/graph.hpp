@@ -1,0 +1,158 @@
+// Internal graph, kernel plan and program structures of the library.
+#pragma once
+
+#include <cstdint>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.hpp"
+
+namespace rv {
+
+// ---------------------------------------------------------------------------
+// graph intake (graph.cpp)
+// ---------------------------------------------------------------------------
+struct Node {
+    int op = 0;
+    int dtype = 0;
+    int src[3] = {-1, -1, -1};
+    int nsrc = 0;
+    Shape shape;
+    int slot = -1;        // BUFFER
+    double cval = 0.0;    // CONST
+    rv_view view{};       // VIEW (over src[0]'s row-major storage)
+    uint32_t axes = 0;    // SUM / MAX
+};
+
+struct Graph {
+    std::vector<Node> nodes;
+    std::vector<int> outputs;
+    int n_inputs = 0;
+    std::vector<std::vector<int>> users;
+};
+
+Graph intake(const rv_node* nodes, int32_t n, const int32_t* outputs, int32_t nout);
+bool is_elementwise(int op);
+bool is_reduce(int op);
+// A VIEW of a value of `src_shape` that only adds/removes size-1 dims and
+// expands: each view dim either has stride 0 or walks one source dim of the
+// same size, in order, with no offset and no mask. On success fills
+// src_dim_of_view[d'] (source dim walked by view dim d', or -1).
+bool pure_broadcast(const rv_view& v, const Shape& src_shape, std::vector<int>* src_dim_of_view);
+
+// ---------------------------------------------------------------------------
+// kernels (schedule.cpp / lower.cpp / codegen.cpp)
+// ---------------------------------------------------------------------------
+enum class KClass { EW, ROW, REDUCE, MFMA, FOLD };
+constexpr int EX_MFMA_ACC = 1000;  // Ex op: the contraction's accumulator at (m, n)
+const char* kclass_name(KClass k);
+
+// Where a value lives in memory.
+struct Loc {
+    int kind = 0;  // 0 input slot, 1 output index, 2 workspace region
+    int index = 0;
+    bool operator==(const Loc& o) const { return kind == o.kind && index == o.index; }
+};
+
+// A load of one buffer through a View written over the kernel's iteration
+// domain (ndim == domain rank, strides per domain dim).
+struct Leaf {
+    Loc loc;
+    int dtype = RV_F32;
+    rv_view v{};
+    bool zero = false;  // every cell is outside the mask
+};
+
+// One value computed inside a kernel.
+struct Ex {
+    int op = 0;        // an rv_op; RV_BUFFER means "load leaf"
+    int dtype = 0;     // dtype of the value (storage semantics)
+    int a = -1, b = -1, c = -1;
+    int leaf = -1;
+    double cval = 0.0;
+    uint32_t axes = 0;  // reduce dims (domain dims) for SUM/MAX
+    bool stat = false;  // ROW kernels: constant along the reduced dims
+    int node = -1;      // graph node this value came from (for describe)
+};
+
+// One value the kernel writes: `ex` stored through view `v` (over the
+// domain; reduced dims have stride 0) into `loc`.
+struct Store {
+    int ex = -1;
+    Loc loc;
+    int dtype = RV_F32;
+    rv_view v{};
+    int node = -1;
+};
+
+struct Kernel {
+    KClass cls = KClass::EW;
+    std::string name;
+    Shape domain;
+    uint32_t rdims = 0;  // reduced domain dims (ROW / REDUCE / MFMA)
+    std::vector<Leaf> leaves;
+    std::vector<Ex> ex;
+    std::vector<Store> stores;
+    // lowering results
+    std::string plan;        // "rowmajor", "tiled2d", "row", "cells", "gemm", "fold"
+    std::string plan_json;   // extra plan fields for rv_describe
+    int lane_dim = -1;       // innermost (thread-consecutive) domain dim
+    unsigned grid[3] = {1, 1, 1};
+    unsigned block[3] = {256, 1, 1};
+    size_t lds = 0;
+    // MFMA pattern (a, b: leaves of the bf16 operands; y: the contraction)
+    int mfma_a = -1, mfma_b = -1, mfma_y = -1;
+    bool mfma_partial = false;  // epilogue reduced to one partial per workgroup
+    int partials_region = -1;   // workspace region of the partials
+    int64_t n_partials = 0;
+    // FOLD
+    int fold_src_region = -1;
+    int64_t fold_count = 0;
+};
+
+struct Region {
+    size_t offset = 0;
+    size_t bytes = 0;
+};
+
+struct OutputInfo {
+    Shape shape;
+    int dtype = RV_F32;
+    int node = -1;
+};
+
+struct Program {
+    Graph g;
+    std::vector<Kernel> kernels;
+    std::vector<Region> regions;
+    size_t ws_bytes = 0;
+    std::vector<OutputInfo> outputs;
+    std::vector<int64_t> input_nelems;  // required elements per input slot
+    std::vector<int> input_dtype;
+    std::string source;
+    std::string options;
+    std::string key;
+    std::vector<char> code;  // gfx950 code object
+    // per-device loaded module
+    std::mutex mu;
+    std::map<int, void*> modules;                        // device -> hipModule_t
+    std::map<int, std::vector<void*>> functions;         // device -> hipFunction_t per kernel
+    std::vector<std::vector<Loc>> kparams;               // kernel parameter order
+};
+
+void schedule(Program& p);                 // fills kernels + regions
+void lower(Program& p);                    // merges dims, picks plans and launch shapes
+std::string codegen(const Program& p);     // HIP source of every kernel
+std::string describe(const Program& p);    // JSON
+void compile_code(Program& p);             // hiprtc -> p.code (runtime.cpp)
+void launch(Program& p, const rv_buffer* bufs, int32_t nbufs, void* ws, size_t ws_bytes, void* stream);
+void device_check(int device);
+
+std::string json_view(const rv_view& v);
+std::vector<Loc> kernel_param_locs(const Program& p, const Kernel& k);
+bool mfma_supported(const Shape& dom, const rv_view& a, const rv_view& b, std::string* why);
+
+}  // namespace rv

@@ -1,0 +1,384 @@
+// View -> index lowering: turns each kernel's Views into the index arithmetic
+// its HIP code runs, and picks the tile plan and launch shape.
+//
+// limn README, "Reading the schedule": views become index arithmetic inside
+// the kernel; the innermost loop is the dim that is stride-1 in the most
+// buffers (here: the dim consecutive lanes walk); a padded read is a range
+// check, and cutting the innermost loop at the mask edges leaves pieces that
+// are wholly inside or outside the pad (here: interior tiles run without
+// range checks, edge tiles with them). Dims that chain in every View
+// (stride[d] == size[d+1] * stride[d+1], both unmasked) are merged first, so
+// e.g. a (4096, 4096) row-major chain runs as one flat loop.
+#include <algorithm>
+#include <cstdlib>
+
+#include "graph.hpp"
+
+namespace rv {
+
+std::string json_view(const rv_view& v) {
+    std::string s = "{\"shape\":[";
+    for (int d = 0; d < v.ndim; ++d) s += (d ? "," : "") + std::to_string(v.shape[d]);
+    s += "],\"strides\":[";
+    for (int d = 0; d < v.ndim; ++d) s += (d ? "," : "") + std::to_string(v.strides[d]);
+    s += "],\"offset\":" + std::to_string(v.offset) + ",\"mask_lo\":[";
+    for (int d = 0; d < v.ndim; ++d) s += (d ? "," : "") + std::to_string(v.mask_lo[d]);
+    s += "],\"mask_hi\":[";
+    for (int d = 0; d < v.ndim; ++d) s += (d ? "," : "") + std::to_string(v.mask_hi[d]);
+    return s + "]}";
+}
+
+static int env_int(const char* name, int def) {
+    const char* s = getenv(name);
+    return (s && *s) ? atoi(s) : def;
+}
+
+// Rewrites every View of `k` for a new domain made of groups of old dims:
+// groups[j] lists consecutive old dims (outermost first) forming new dim j.
+static void regroup(Kernel& k, const std::vector<std::vector<int>>& groups) {
+    auto apply = [&](rv_view& v) {
+        rv_view o{};
+        o.ndim = (int)groups.size();
+        o.offset = v.offset;
+        for (size_t j = 0; j < groups.size(); ++j) {
+            int64_t size = 1;
+            for (int d : groups[j]) size *= v.shape[d];
+            int last = groups[j].back();
+            o.shape[j] = size;
+            o.strides[j] = v.strides[last];
+            if (groups[j].size() == 1) {
+                o.mask_lo[j] = v.mask_lo[last];
+                o.mask_hi[j] = v.mask_hi[last];
+            } else {
+                o.mask_lo[j] = 0;
+                o.mask_hi[j] = size;
+            }
+        }
+        v = o;
+    };
+    for (auto& L : k.leaves) apply(L.v);
+    for (auto& s : k.stores) apply(s.v);
+    Shape dom;
+    uint32_t rd = 0;
+    for (size_t j = 0; j < groups.size(); ++j) {
+        int64_t size = 1;
+        for (int d : groups[j]) size *= k.domain[d];
+        dom.push_back(size);
+        if ((k.rdims >> groups[j][0]) & 1u) rd |= 1u << j;
+    }
+    k.domain = dom;
+    k.rdims = rd;
+}
+
+static bool full_mask(const rv_view& v, int d) { return v.mask_lo[d] == 0 && v.mask_hi[d] == v.shape[d]; }
+
+// Drops size-1 dims and merges adjacent dims that chain in every View.
+static void merge_dims(Kernel& k) {
+    const int r = (int)k.domain.size();
+    std::vector<int> keep;
+    for (int d = 0; d < r; ++d)
+        if (k.domain[d] != 1) keep.push_back(d);
+    if (keep.empty()) {
+        // every dim has size 1: one cell; keep dim 0 as a size-1 loop
+        if (r == 0) {
+            k.domain = Shape{1};
+            for (auto& L : k.leaves) {
+                L.v.ndim = 1; L.v.shape[0] = 1; L.v.strides[0] = 0; L.v.mask_lo[0] = 0; L.v.mask_hi[0] = 1;
+            }
+            for (auto& s : k.stores) {
+                s.v.ndim = 1; s.v.shape[0] = 1; s.v.strides[0] = 0; s.v.mask_lo[0] = 0; s.v.mask_hi[0] = 1;
+            }
+            return;
+        }
+        keep.push_back(0);
+    }
+    std::vector<std::vector<int>> groups;
+    for (int d : keep) {
+        if (!groups.empty()) {
+            int p = groups.back().back();
+            bool ok = ((k.rdims >> p) & 1u) == ((k.rdims >> d) & 1u);
+            auto chain = [&](const rv_view& v) {
+                return v.strides[p] == k.domain[d] * v.strides[d] && full_mask(v, p) && full_mask(v, d);
+            };
+            for (auto& L : k.leaves) ok = ok && (L.zero || chain(L.v));
+            for (auto& s : k.stores) ok = ok && chain(s.v);
+            if (ok) {
+                groups.back().push_back(d);
+                continue;
+            }
+        }
+        groups.push_back({d});
+    }
+    regroup(k, groups);
+}
+
+// Leaf or store addresses stay inside their buffer for every in-mask cell.
+static void prove_in_bounds(const Program& p, const Kernel& k) {
+    auto cap = [&](const Loc& L, int dtype) -> int64_t {
+        if (L.kind == 0) return p.input_nelems[L.index];
+        if (L.kind == 1) return numel(p.outputs[L.index].shape);
+        return (int64_t)(p.regions[L.index].bytes / dtype_size(dtype));
+    };
+    auto check = [&](const rv_view& v, const Loc& L, int dtype, const char* what) {
+        int64_t lo, hi;
+        if (!view_addr_range(v, &lo, &hi)) return;
+        if (lo < 0 || hi >= cap(L, dtype))
+            fail(RV_E_OUT_OF_BOUNDS, fmt("%s of kernel %s addresses [%lld, %lld] outside its %lld elements", what,
+                                         k.name.c_str(), (long long)lo, (long long)hi, (long long)cap(L, dtype)));
+    };
+    for (auto& L : k.leaves)
+        if (!L.zero && !(k.cls == KClass::FOLD)) check(L.v, L.loc, L.dtype, "a load");
+    for (auto& s : k.stores)
+        if (k.cls != KClass::FOLD && !(k.cls == KClass::MFMA && k.mfma_partial)) check(s.v, s.loc, s.dtype, "a store");
+}
+
+// MFMA tile plan. Operand A walks (m, k) with n-stride 0 and B walks (n, k)
+// with m-stride 0 over the (M, N, K) domain; A must be k-contiguous and B
+// either n-contiguous ([k][n] storage) or k-contiguous ([n][k] storage).
+bool mfma_supported(const Shape& dom, const rv_view& a, const rv_view& b, std::string* why) {
+    const int BM = 128, BN = 128, BK = 64;
+    auto no = [&](const char* w) {
+        if (why) *why = w;
+        return false;
+    };
+    if (dom.size() != 3) return no("rank");
+    if (dom[0] % BM || dom[1] % BN || dom[2] % BK) return no("M, N, K must be multiples of 128, 128, 64");
+    if (a.strides[2] != 1) return no("A must be contiguous along k");
+    if (a.offset % 8 || a.strides[0] % 8) return no("A rows must be 16-byte aligned");
+    bool kn = b.strides[1] == 1, nk = b.strides[2] == 1;
+    if (!kn && !nk) return no("B must be contiguous along n or k");
+    if (b.offset % 8) return no("B must be 16-byte aligned");
+    if (kn && b.strides[2] % 8) return no("B rows must be 16-byte aligned");
+    if (!kn && b.strides[1] % 8) return no("B rows must be 16-byte aligned");
+    return true;
+}
+
+static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
+    char buf[512];
+    switch (k.cls) {
+        case KClass::FOLD: {
+            k.plan = "fold";
+            k.fold_count = prev_partials;
+            k.grid[0] = 1;
+            k.block[0] = 256;
+            k.lds = 256 * 4;
+            snprintf(buf, sizeof buf, "\"partials\":%lld,\"src_region\":%d,\"sum_depth\":%lld",
+                     (long long)k.fold_count, k.fold_src_region, (long long)((k.fold_count + 255) / 256 + 8));
+            k.plan_json = buf;
+            return;
+        }
+        case KClass::MFMA: {
+            k.plan = "gemm";
+            const int BM = 128, BN = 128;
+            int64_t M = k.domain[0], N = k.domain[1];
+            k.grid[0] = (unsigned)((M / BM) * (N / BN));
+            k.block[0] = 256;
+            k.lds = 2 * (128 * 72 + 128 * 72) * 2;
+            k.n_partials = k.grid[0];
+            bool kn = k.leaves[k.mfma_b].v.strides[1] == 1;
+            // per lane: 64 values summed in order, 6 butterfly levels, 3
+            // cross-wave additions; the fold adds its own depth
+            snprintf(buf, sizeof buf,
+                     "\"tile\":[128,128,64],\"waves\":[2,2],\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
+                     "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d",
+                     kn ? "kn" : "nk", 63 + 6 + 3);
+            k.plan_json = buf;
+            if (k.mfma_partial) {
+                p.regions[k.partials_region].bytes = (size_t)k.n_partials * 4;
+                k.stores[0].loc = Loc{2, k.partials_region};
+            }
+            return;
+        }
+        default: break;
+    }
+    merge_dims(k);
+    const int rank = (int)k.domain.size();
+    if (numel(k.domain) == 0) {
+        k.plan = "empty";
+        k.grid[0] = 0;
+        return;
+    }
+    if (k.cls == KClass::EW) {
+        const int X = rank - 1, Y = rank - 2;
+        bool tiled = false;
+        if (rank >= 2 && k.domain[X] >= 8 && k.domain[Y] >= 8)
+            for (auto& L : k.leaves)
+                if (!L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) tiled = true;
+        k.lane_dim = X;
+        if (tiled) {
+            k.plan = "tiled2d";
+            int64_t B = numel(k.domain) / (k.domain[X] * k.domain[Y]);
+            k.grid[0] = (unsigned)((k.domain[X] + 63) / 64);
+            k.grid[1] = (unsigned)((k.domain[Y] + 63) / 64);
+            k.grid[2] = (unsigned)B;
+            k.block[0] = 256;
+            int nt = 0;
+            for (auto& L : k.leaves)
+                if (!L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) ++nt;
+            k.lds = (size_t)nt * 64 * 65 * 8;
+            snprintf(buf, sizeof buf, "\"tile\":[64,64],\"lds_pad\":1,\"staged_leaves\":%d", nt);
+        } else {
+            k.plan = "rowmajor";
+            int maxsz = 1;
+            for (auto& s : k.stores) maxsz = std::max(maxsz, dtype_size(s.dtype));
+            int vw = std::max(1, std::min(8, 16 / maxsz));
+            int64_t cpr = (k.domain[X] + vw - 1) / vw;
+            int64_t chunks = cpr * (numel(k.domain) / k.domain[X]);
+            const int U = 4;
+            int64_t blocks = (chunks + 256 * U - 1) / (256 * U);
+            k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 256 * 32));
+            k.block[0] = 256;
+            snprintf(buf, sizeof buf, "\"vec\":%d,\"unroll\":%d,\"chunks\":%lld", vw, U, (long long)chunks);
+        }
+        k.plan_json = buf;
+        return;
+    }
+    if (k.cls == KClass::ROW) {
+        k.plan = "row";
+        int64_t NR = 1, NK = 1;
+        for (int d = 0; d < rank; ++d) ((k.rdims >> d) & 1u ? NR : NK) *= k.domain[d];
+        bool two = true;
+        for (auto& L : k.leaves)
+            if (!L.zero && dtype_size(L.dtype) != 2) {
+                bool along = false;
+                for (int d = 0; d < rank; ++d)
+                    if (((k.rdims >> d) & 1u) && L.v.strides[d] != 0) along = true;
+                if (along) two = false;
+            }
+        for (auto& s : k.stores)
+            if (dtype_size(s.dtype) != 2) {
+                bool along = false;
+                for (int d = 0; d < rank; ++d)
+                    if (((k.rdims >> d) & 1u) && s.v.strides[d] != 0) along = true;
+                if (along) two = false;
+            }
+        int vw = two ? 8 : 4;
+        int T = 256;
+        while (T > 16 && (int64_t)T * vw * 2 > NR) T /= 2;
+        T = env_int("RV_ROW_THREADS", T);
+        if (T < 1 || T > 256 || (256 % T)) fail(RV_E_INVALID, "RV_ROW_THREADS must divide 256");
+        int rpw = 256 / T;
+        int64_t nrg = (NK + rpw - 1) / rpw;
+        k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>(nrg, env_int("RV_ROW_GRID", 2048)));
+        k.block[0] = 256;
+        k.lane_dim = rank - 1;
+        int nv = (int)((NR + (int64_t)T * vw - 1) / ((int64_t)T * vw));
+        int nred = 0;
+        for (auto& e : k.ex)
+            if (e.op == RV_SUM || e.op == RV_MAX) ++nred;
+        k.lds = T > 64 ? (size_t)nred * rpw * (T / 64) * 4 : 0;
+        snprintf(buf, sizeof buf, "\"threads_per_row\":%d,\"rows_per_block\":%d,\"vec\":%d,\"chunks\":%d,"
+                 "\"row_len\":%lld,\"rows\":%lld", T, rpw, vw, nv, (long long)NR, (long long)NK);
+        k.plan_json = buf;
+        return;
+    }
+    // REDUCE: one lane per output cell; lanes walk the kept dim that is
+    // stride-1 in the most buffers (a tie keeps the later dim)
+    k.plan = "cells";
+    int best = -1, best_votes = -1;
+    for (int d = 0; d < rank; ++d) {
+        if ((k.rdims >> d) & 1u) continue;
+        int votes = 0;
+        for (auto& L : k.leaves)
+            if (!L.zero && L.v.strides[d] == 1) ++votes;
+        for (auto& s : k.stores)
+            if (s.v.strides[d] == 1) ++votes;
+        if (votes >= best_votes) {
+            best = d;
+            best_votes = votes;
+        }
+    }
+    k.lane_dim = best;
+    int64_t cells = 1;
+    for (int d = 0; d < rank; ++d)
+        if (!((k.rdims >> d) & 1u)) cells *= k.domain[d];
+    k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>((cells + 255) / 256, 1 << 20));
+    k.block[0] = 256;
+    snprintf(buf, sizeof buf, "\"cells\":%lld,\"lane_dim\":%d", (long long)cells, best);
+    k.plan_json = buf;
+}
+
+void lower(Program& p) {
+    const Graph& g = p.g;
+    p.input_nelems.assign(g.n_inputs, 0);
+    p.input_dtype.assign(g.n_inputs, -1);
+    for (const Node& nd : g.nodes) {
+        if (nd.op != RV_BUFFER) continue;
+        int64_t ne = numel(nd.shape);
+        if (p.input_dtype[nd.slot] >= 0 && p.input_dtype[nd.slot] != nd.dtype)
+            fail(RV_E_DTYPE, fmt("input slot %d is declared with two dtypes", nd.slot));
+        p.input_dtype[nd.slot] = nd.dtype;
+        p.input_nelems[nd.slot] = std::max(p.input_nelems[nd.slot], ne);
+    }
+    p.outputs.clear();
+    for (int o : g.outputs) p.outputs.push_back(OutputInfo{g.nodes[o].shape, g.nodes[o].dtype, o});
+    int64_t prev_partials = 0;
+    for (auto& k : p.kernels) {
+        plan_kernel(p, k, prev_partials);
+        if (k.cls == KClass::MFMA) prev_partials = k.n_partials;
+    }
+    size_t off = 0;
+    for (auto& r : p.regions) {
+        r.offset = off;
+        off += (r.bytes + 255) / 256 * 256;
+    }
+    p.ws_bytes = off;
+    for (auto& k : p.kernels) prove_in_bounds(p, k);
+}
+
+// ---------------------------------------------------------------------------
+// rv_describe
+// ---------------------------------------------------------------------------
+static std::string json_loc(const Loc& L) {
+    static const char* kinds[] = {"input", "output", "workspace"};
+    return fmt("{\"kind\":\"%s\",\"index\":%d}", kinds[L.kind], L.index);
+}
+
+std::string describe(const Program& p) {
+    std::string s = "{\"n_inputs\":" + std::to_string(p.g.n_inputs) + ",\"workspace_bytes\":" +
+                    std::to_string(p.ws_bytes) + ",\"cache_key\":\"" + p.key + "\",\"kernels\":[";
+    for (size_t i = 0; i < p.kernels.size(); ++i) {
+        const Kernel& k = p.kernels[i];
+        if (i) s += ",";
+        s += "{\"name\":\"" + k.name + "\",\"class\":\"" + kclass_name(k.cls) + "\",\"plan\":\"" + k.plan +
+             "\",\"domain\":[";
+        for (size_t d = 0; d < k.domain.size(); ++d) s += (d ? "," : "") + std::to_string(k.domain[d]);
+        s += "],\"reduce_dims\":[";
+        bool first = true;
+        for (size_t d = 0; d < k.domain.size(); ++d)
+            if ((k.rdims >> d) & 1u) {
+                s += (first ? "" : ",") + std::to_string(d);
+                first = false;
+            }
+        s += "],\"lane_dim\":" + std::to_string(k.lane_dim);
+        s += fmt(",\"grid\":[%u,%u,%u],\"block\":[%u,%u,%u],\"lds_bytes\":%zu", k.grid[0], k.grid[1], k.grid[2],
+                 k.block[0], k.block[1], k.block[2], k.lds);
+        if (!k.plan_json.empty()) s += ",\"plan_detail\":{" + k.plan_json + "}";
+        s += ",\"leaves\":[";
+        for (size_t l = 0; l < k.leaves.size(); ++l) {
+            const Leaf& L = k.leaves[l];
+            s += (l ? "," : "") + std::string("{\"loc\":") + json_loc(L.loc) + ",\"dtype\":\"" + dtype_name(L.dtype) +
+                 "\",\"zero\":" + (L.zero ? "true" : "false") + ",\"view\":" + json_view(L.v) + "}";
+        }
+        s += "],\"stores\":[";
+        for (size_t l = 0; l < k.stores.size(); ++l) {
+            const Store& st = k.stores[l];
+            s += (l ? "," : "") + std::string("{\"loc\":") + json_loc(st.loc) + ",\"dtype\":\"" +
+                 dtype_name(st.dtype) + "\",\"node\":" + std::to_string(st.node) + ",\"ex\":" + std::to_string(st.ex) +
+                 ",\"view\":" + json_view(st.v) + "}";
+        }
+        s += "],\"ops\":[";
+        for (size_t e = 0; e < k.ex.size(); ++e) {
+            const Ex& x = k.ex[e];
+            const char* nm = x.op == EX_MFMA_ACC ? "MFMA_ACC" : op_name(x.op);
+            s += fmt("%s{\"op\":\"%s\",\"dtype\":\"%s\",\"a\":%d,\"b\":%d,\"c\":%d,\"leaf\":%d,\"node\":%d,"
+                     "\"cval\":\"%.17g\"}",
+                     e ? "," : "", x.op == RV_BUFFER ? "LOAD" : nm, dtype_name(x.dtype), x.a, x.b, x.c, x.leaf, x.node,
+                     x.cval);
+        }
+        s += "]}";
+    }
+    return s + "]}";
+}
+
+}  // namespace rv

@@ -1,0 +1,569 @@
+// Scheduler: cuts the graph into kernels and builds each kernel's
+// expression over its iteration domain.
+//
+// limn README, "Reading the schedule": elementwise work fuses into whatever
+// consumes it, and a cut falls wherever a value has to exist in memory (a
+// copy, an output, anything a View addresses). limn also cuts at every
+// reduce; here a reduce is not cut when its consumers can keep the reduced
+// value on chip:
+//   ROW    reduces over the trailing dims of one row space, with their
+//          elementwise producers and consumers (softmax, RMSNorm, LayerNorm):
+//          a row is read once and stays in registers.
+//   MFMA   SUM over k of CAST(bf16 A) * CAST(bf16 B) through stride-0 Views
+//          (limn README's one-nest matmul; Luminal IR blog, "Naive Matrix
+//          Multiplication"), with an elementwise epilogue on y and an
+//          optional SUM of it over every dim.
+//   REDUCE one thread per output cell, reduce loops run in order inside it
+//          (limn README, "Backends": one point of the non-reduce dims per
+//          thread, so results fold in the serial order).
+//   EW     elementwise (incl. CONTIGUOUS of a permuted View = transpose).
+// Values only differ from limn's per-reduce cuts in the order a fold
+// associates its additions.
+#include <algorithm>
+#include <functional>
+#include <map>
+#include <set>
+
+#include "graph.hpp"
+
+namespace rv {
+
+namespace {
+
+using Map = std::vector<int>;  // node dim -> domain dim, or -1 (index 0)
+
+constexpr int kRowMinLen = 128;  // shortest row handled by the ROW class
+
+struct Ctx {
+    Program& p;
+    Graph& g;
+    std::vector<char> mat;        // value exists in memory
+    std::vector<std::vector<Loc>> loc;  // where (first entry is read by consumers)
+};
+
+// Compose a View over a value's storage with a map from the value's dims to
+// the domain: the result addresses the same storage over the domain.
+static Leaf compose_leaf(const rv_view& v, const Map& m, int rank, Loc loc, int dtype) {
+    Leaf L;
+    L.loc = loc;
+    L.dtype = dtype;
+    rv_view& o = L.v;
+    o.ndim = rank;
+    o.offset = v.offset;
+    std::vector<int> hit(rank, 0);
+    for (int d = 0; d < rank; ++d) {
+        o.shape[d] = 0;  // filled by the caller (domain)
+        o.strides[d] = 0;
+        o.mask_lo[d] = 0;
+        o.mask_hi[d] = INT64_MAX;
+    }
+    for (int d = 0; d < v.ndim; ++d) {
+        int dd = m[d];
+        if (dd < 0) {
+            if (!(v.mask_lo[d] <= 0 && 0 < v.mask_hi[d])) L.zero = true;
+            continue;
+        }
+        if (hit[dd]++) fail(RV_E_INVALID, "internal: two dims of one value map to one domain dim");
+        o.strides[dd] = v.strides[d];
+        o.mask_lo[dd] = v.mask_lo[d];
+        o.mask_hi[dd] = v.mask_hi[d];
+    }
+    return L;
+}
+
+struct Builder {
+    Ctx& c;
+    Kernel& k;
+    int root;
+    enum Mode { EW, ROW, REDUCE, MFMA } mode;
+    uint32_t rmask = 0;  // ROW/REDUCE: reduced domain dims
+    int mfma_y = -1;     // MFMA: the contraction node
+    std::map<std::pair<int, Map>, int> memo;
+    std::map<std::pair<std::string, int>, int> leaf_memo;
+
+    int rank() const { return (int)k.domain.size(); }
+
+    int add(Ex e) {
+        k.ex.push_back(e);
+        return (int)k.ex.size() - 1;
+    }
+
+    int add_leaf(Leaf L) {
+        for (int d = 0; d < rank(); ++d) {
+            L.v.shape[d] = k.domain[d];
+            L.v.mask_lo[d] = std::max<int64_t>(L.v.mask_lo[d], 0);
+            L.v.mask_hi[d] = std::min<int64_t>(L.v.mask_hi[d], k.domain[d]);
+            if (L.v.mask_hi[d] <= L.v.mask_lo[d]) L.zero = true;
+        }
+        std::string key = json_view(L.v) + fmt("|%d|%d|%d|%d", L.loc.kind, L.loc.index, L.dtype, (int)L.zero);
+        auto it = leaf_memo.find({key, 0});
+        if (it != leaf_memo.end()) return it->second;
+        k.leaves.push_back(L);
+        int id = (int)k.leaves.size() - 1;
+        leaf_memo[{key, 0}] = id;
+        return id;
+    }
+
+    int load(const rv_view& v, const Map& m, Loc loc, int dtype, int node) {
+        Leaf L = compose_leaf(v, m, rank(), loc, dtype);
+        Ex e;
+        e.op = RV_BUFFER;
+        e.dtype = dtype;
+        e.leaf = add_leaf(L);
+        e.node = node;
+        return add(e);
+    }
+
+    int build(int i, const Map& m) {
+        auto key = std::make_pair(i, m);
+        auto it = memo.find(key);
+        if (it != memo.end()) return it->second;
+        int r = build_(i, m);
+        memo[key] = r;
+        return r;
+    }
+
+    int build_(int i, const Map& m) {
+        const Node& nd = c.g.nodes[i];
+        if (nd.op == RV_BUFFER)
+            return load(view_contiguous(nd.shape), m, Loc{0, nd.slot}, nd.dtype, i);
+        if (i != root && c.mat[i])
+            return load(view_contiguous(nd.shape), m, c.loc[i][0], nd.dtype, i);
+        switch (nd.op) {
+            case RV_CONST: {
+                Ex e;
+                e.op = RV_CONST;
+                e.dtype = nd.dtype;
+                e.cval = nd.cval;
+                e.node = i;
+                return add(e);
+            }
+            case RV_VIEW: {
+                int s = nd.src[0];
+                const Node& sn = c.g.nodes[s];
+                if (sn.op == RV_BUFFER) return load(nd.view, m, Loc{0, sn.slot}, sn.dtype, i);
+                if (c.mat[s]) return load(nd.view, m, c.loc[s][0], sn.dtype, i);
+                std::vector<int> sdv;
+                if (!pure_broadcast(nd.view, sn.shape, &sdv))
+                    fail(RV_E_INVALID, "internal: non-broadcast View of an unmaterialised value");
+                Map sm(sn.shape.size(), -1);
+                for (int dv = 0; dv < nd.view.ndim; ++dv)
+                    if (sdv[dv] >= 0) sm[sdv[dv]] = m[dv];
+                return build(s, sm);
+            }
+            case RV_CONTIGUOUS:
+                return build(nd.src[0], m);
+            case RV_SUM: case RV_MAX:
+                return build_reduce(i, m);
+            default: break;
+        }
+        if (!is_elementwise(nd.op)) fail(RV_E_INVALID, fmt("internal: op %s in a kernel", op_name(nd.op)));
+        Ex e;
+        e.op = nd.op;
+        e.dtype = nd.dtype;
+        e.node = i;
+        e.a = build(nd.src[0], m);
+        if (nd.nsrc > 1) e.b = build(nd.src[1], m);
+        if (nd.nsrc > 2) e.c = build(nd.src[2], m);
+        return add(e);
+    }
+
+    int build_reduce(int i, const Map& m) {
+        const Node& nd = c.g.nodes[i];
+        const Node& in = c.g.nodes[nd.src[0]];
+        if (mode == MFMA && i == mfma_y) {
+            Ex e;
+            e.op = EX_MFMA_ACC;
+            e.dtype = RV_F32;
+            e.node = i;
+            return add(e);
+        }
+        // ROW: the reduce must reduce exactly the domain's reduced dims of an
+        // input laid over the whole domain; REDUCE: only the root reduces.
+        if (!(mode == ROW || (mode == REDUCE && i == root))) throw 1;
+        if (mode == ROW && !(nd.dtype == RV_F32 || is_half(nd.dtype))) throw 1;
+        if (in.shape != k.domain) throw 1;
+        uint32_t ax = 0;
+        for (size_t d = 0; d < in.shape.size(); ++d)
+            if ((nd.axes >> d) & 1u) ax |= (in.shape[d] == 1 ? 0u : (1u << d));
+        if (ax != rmask) throw 1;
+        for (size_t d = 0; d < nd.shape.size(); ++d) {
+            bool red = (rmask >> d) & 1u;
+            if (red ? m[d] != -1 : (m[d] != (int)d && nd.shape[d] != 1)) throw 1;
+        }
+        Map id(in.shape.size());
+        for (size_t d = 0; d < id.size(); ++d) id[d] = (int)d;
+        Ex e;
+        e.op = nd.op;
+        e.dtype = nd.dtype;
+        e.node = i;
+        e.axes = rmask;
+        e.a = build(nd.src[0], id);
+        e.stat = true;
+        return add(e);
+    }
+};
+
+// Reduces reachable from `root` without passing through a value in memory.
+static void reach_reduces(Ctx& c, int root, std::set<int>& out, bool top_only) {
+    std::set<int> seen;
+    std::function<void(int)> go = [&](int i) {
+        if (!seen.insert(i).second) return;
+        const Node& nd = c.g.nodes[i];
+        if (nd.op == RV_BUFFER) return;
+        if (i != root && c.mat[i]) return;
+        if (is_reduce(nd.op) && i != root) {
+            out.insert(i);
+            if (top_only) return;
+        }
+        if (nd.op == RV_VIEW) {
+            int s = nd.src[0];
+            if (c.g.nodes[s].op == RV_BUFFER || c.mat[s]) return;
+            go(s);
+            return;
+        }
+        for (int k = 0; k < nd.nsrc; ++k) go(nd.src[k]);
+    };
+    go(root);
+}
+
+static Map identity(size_t n) {
+    Map m(n);
+    for (size_t d = 0; d < n; ++d) m[d] = (int)d;
+    return m;
+}
+
+static void add_stores(Ctx& c, Kernel& k, int root, int ex, const Map& m) {
+    const Node& nd = c.g.nodes[root];
+    for (const Loc& L : c.loc[root]) {
+        Store s;
+        s.ex = ex;
+        s.loc = L;
+        s.dtype = nd.dtype;
+        s.node = root;
+        Leaf lf = compose_leaf(view_contiguous(nd.shape), m, (int)k.domain.size(), L, nd.dtype);
+        s.v = lf.v;
+        for (size_t d = 0; d < k.domain.size(); ++d) {
+            s.v.shape[d] = k.domain[d];
+            s.v.mask_lo[d] = 0;
+            s.v.mask_hi[d] = k.domain[d];
+        }
+        k.stores.push_back(s);
+    }
+}
+
+// Map for a root of shape `shape` laid over `domain` (equal, or equal with
+// the reduced dims set to 1).
+static Map root_map(const Shape& shape, uint32_t rmask) {
+    Map m(shape.size());
+    for (size_t d = 0; d < shape.size(); ++d) m[d] = ((rmask >> d) & 1u) ? -1 : (int)d;
+    return m;
+}
+
+static bool try_ew(Ctx& c, int root, Kernel& k) {
+    std::set<int> red;
+    reach_reduces(c, root, red, true);
+    const Node& nd = c.g.nodes[root];
+    if (!red.empty() || is_reduce(nd.op)) return false;
+    k = Kernel{};
+    k.cls = KClass::EW;
+    k.domain = nd.shape;
+    Builder b{c, k, root, Builder::EW};
+    int e = b.build(root, identity(nd.shape.size()));
+    add_stores(c, k, root, e, identity(nd.shape.size()));
+    return true;
+}
+
+// Row space of a reduce: (input shape, reduced dims) with every reduced
+// non-size-1 dim after every kept non-size-1 dim.
+static bool row_space(const Node& r, const Node& in, uint32_t* rmask) {
+    uint32_t ax = 0;
+    int last_kept = -1, first_red = 1 << 20;
+    for (size_t d = 0; d < in.shape.size(); ++d) {
+        if (in.shape[d] == 1) continue;
+        if ((r.axes >> d) & 1u) {
+            ax |= 1u << d;
+            first_red = std::min(first_red, (int)d);
+        } else {
+            last_kept = (int)d;
+        }
+    }
+    if (ax == 0 || last_kept > first_red) return false;
+    *rmask = ax;
+    return true;
+}
+
+static bool try_row(Ctx& c, int root, Kernel& k) {
+    std::set<int> red;
+    reach_reduces(c, root, red, false);
+    const Node& rn = c.g.nodes[root];
+    if (is_reduce(rn.op)) red.insert(root);
+    if (red.empty()) return false;
+    int r0 = *red.begin();
+    const Node& in0 = c.g.nodes[c.g.nodes[r0].src[0]];
+    uint32_t rmask;
+    if (!row_space(c.g.nodes[r0], in0, &rmask)) return false;
+    int64_t n = 1;
+    for (size_t d = 0; d < in0.shape.size(); ++d)
+        if ((rmask >> d) & 1u) n *= in0.shape[d];
+    if (n < kRowMinLen) return false;
+    // the root is the full row space or its per-row statistics
+    Shape stat = in0.shape;
+    for (size_t d = 0; d < stat.size(); ++d)
+        if ((rmask >> d) & 1u) stat[d] = 1;
+    if (rn.shape != in0.shape && rn.shape != stat) return false;
+    Kernel kk;
+    kk.cls = KClass::ROW;
+    kk.domain = in0.shape;
+    kk.rdims = rmask;
+    Builder b{c, kk, root, Builder::ROW};
+    b.rmask = rmask;
+    Map m = rn.shape == in0.shape ? identity(rn.shape.size()) : root_map(rn.shape, rmask);
+    try {
+        int e = b.build(root, m);
+        add_stores(c, kk, root, e, m);
+    } catch (int) {
+        return false;
+    }
+    k = kk;
+    return true;
+}
+
+static bool try_reduce_cells(Ctx& c, int root, Kernel& k) {
+    const Node& rn = c.g.nodes[root];
+    if (!is_reduce(rn.op)) return false;
+    std::set<int> red;
+    reach_reduces(c, root, red, true);
+    if (!red.empty()) return false;
+    const Node& in = c.g.nodes[rn.src[0]];
+    uint32_t rmask = 0;
+    for (size_t d = 0; d < in.shape.size(); ++d)
+        if (((rn.axes >> d) & 1u) && in.shape[d] != 1) rmask |= 1u << d;
+    Kernel kk;
+    kk.cls = KClass::REDUCE;
+    kk.domain = in.shape;
+    kk.rdims = rmask;
+    Builder b{c, kk, root, Builder::REDUCE};
+    b.rmask = rmask;
+    Map m = root_map(rn.shape, rmask);
+    try {
+        int e = b.build(root, m);
+        add_stores(c, kk, root, e, m);
+    } catch (int) {
+        return false;
+    }
+    k = kk;
+    return true;
+}
+
+// ---- MFMA ----------------------------------------------------------------
+
+// Strips CASTs to f32 and returns the leaf-producing node (a bf16 BUFFER, or
+// a VIEW of one) under a f32 CAST, or -1.
+static int bf16_operand(Ctx& c, int i) {
+    const Node& nd = c.g.nodes[i];
+    if (nd.op != RV_CAST || nd.dtype != RV_F32 || c.mat[i]) return -1;
+    int s = nd.src[0];
+    const Node& sn = c.g.nodes[s];
+    if (sn.dtype != RV_BF16) return -1;
+    if (sn.op == RV_BUFFER) return s;
+    if (sn.op == RV_VIEW && !c.mat[s] && (c.g.nodes[sn.src[0]].op == RV_BUFFER || c.mat[sn.src[0]])) return s;
+    return -1;
+}
+
+static bool is_contraction(Ctx& c, int y) {
+    const Node& yn = c.g.nodes[y];
+    if (yn.op != RV_SUM) return false;
+    const Node& mul = c.g.nodes[yn.src[0]];
+    if (mul.op != RV_MUL || mul.dtype != RV_F32 || c.mat[yn.src[0]]) return false;
+    if (mul.shape.size() != 3 || yn.axes != 4u) return false;
+    return bf16_operand(c, mul.src[0]) >= 0 && bf16_operand(c, mul.src[1]) >= 0;
+}
+
+static bool try_mfma(Ctx& c, int root, std::vector<Kernel>& out, int& partial_region) {
+    const Node& rn = c.g.nodes[root];
+    int y = -1, epi_root = -1;
+    bool partial = false;
+    auto single_contraction_below = [&](int top) -> int {
+        std::set<int> red;
+        reach_reduces(c, top, red, false);
+        if (red.size() != 1) return -1;
+        int cand = *red.begin();
+        return is_contraction(c, cand) ? cand : -1;
+    };
+    if (is_contraction(c, root)) {
+        y = root;
+        epi_root = root;
+    } else if (rn.op == RV_SUM) {
+        const Node& in = c.g.nodes[rn.src[0]];
+        bool all = true;
+        for (size_t d = 0; d < in.shape.size(); ++d)
+            if (in.shape[d] != 1 && !((rn.axes >> d) & 1u)) all = false;
+        if (!all || c.mat[rn.src[0]]) return false;
+        y = single_contraction_below(rn.src[0]);
+        if (y < 0 || in.shape != c.g.nodes[y].shape) return false;
+        epi_root = rn.src[0];
+        partial = true;
+    } else if (!is_reduce(rn.op)) {
+        y = single_contraction_below(root);
+        if (y < 0 || rn.shape != c.g.nodes[y].shape) return false;
+        epi_root = root;
+    } else {
+        return false;
+    }
+    const Node& yn = c.g.nodes[y];
+    const Node& mul = c.g.nodes[yn.src[0]];
+    Kernel k;
+    k.cls = KClass::MFMA;
+    k.domain = mul.shape;  // (M, N, K)
+    k.rdims = 4u;
+    Builder b{c, k, root, Builder::MFMA};
+    b.mfma_y = y;
+    b.rmask = 4u;
+    // operand leaves over (M, N, K)
+    Map id3 = identity(3);
+    int ea = b.build(bf16_operand(c, mul.src[0]), id3);
+    int eb = b.build(bf16_operand(c, mul.src[1]), id3);
+    int la = k.ex[ea].leaf, lb = k.ex[eb].leaf;
+    auto sv = [&](int l, int d) { return k.leaves[l].v.strides[d]; };
+    // A walks (m, k) with n-stride 0; B walks (n, k) with m-stride 0
+    if (sv(la, 1) != 0 || sv(lb, 0) != 0) std::swap(la, lb);
+    if (sv(la, 1) != 0 || sv(lb, 0) != 0) return false;
+    for (int l : {la, lb}) {
+        const rv_view& v = k.leaves[l].v;
+        if (k.leaves[l].zero) return false;
+        for (int d = 0; d < 3; ++d)
+            if (v.mask_lo[d] != 0 || v.mask_hi[d] != v.shape[d]) return false;
+    }
+    if (!mfma_supported(k.domain, k.leaves[la].v, k.leaves[lb].v, nullptr)) return false;
+    k.mfma_a = la;
+    k.mfma_b = lb;
+    // the epilogue over (M, N, 1): built on the contraction's output map
+    Map ym = root_map(yn.shape, 4u);
+    int e;
+    try {
+        e = b.build(epi_root, ym);
+    } catch (int) {
+        return false;
+    }
+    k.mfma_y = y;
+    // epilogue leaves must not walk k
+    for (size_t l = 0; l < k.leaves.size(); ++l)
+        if ((int)l != la && (int)l != lb && k.leaves[l].v.strides[2] != 0) return false;
+    if (partial) {
+        k.mfma_partial = true;
+        Store s;
+        s.ex = e;
+        s.dtype = RV_F32;
+        s.node = root;
+        k.stores.push_back(s);  // target set in lower() (partials region)
+        partial_region = (int)c.p.regions.size();
+        c.p.regions.push_back(Region{});
+        k.partials_region = partial_region;
+    } else {
+        add_stores(c, k, root, e, ym);
+    }
+    out.push_back(k);
+    if (partial) {
+        Kernel f;
+        f.cls = KClass::FOLD;
+        f.domain = Shape{1};
+        f.fold_src_region = partial_region;
+        Ex acc;
+        acc.op = RV_SUM;
+        acc.dtype = rn.dtype;
+        acc.node = root;
+        f.ex.push_back(acc);
+        add_stores(c, f, root, 0, Map(rn.shape.size(), -1));
+        out.push_back(f);
+    }
+    return true;
+}
+
+}  // namespace
+
+void schedule(Program& p) {
+    Graph& g = p.g;
+    const int n = (int)g.nodes.size();
+    Ctx c{p, g, std::vector<char>(n, 0), std::vector<std::vector<Loc>>(n)};
+    for (int i = 0; i < n; ++i)
+        if (g.nodes[i].op == RV_BUFFER) {
+            c.mat[i] = 1;
+            c.loc[i].push_back(Loc{0, g.nodes[i].slot});
+        }
+    std::vector<char> is_out(n, 0);
+    for (size_t k = 0; k < g.outputs.size(); ++k) is_out[g.outputs[k]] = 1;
+    // values that must exist in memory
+    std::vector<char> need(n, 0);
+    for (int i = 0; i < n; ++i) {
+        const Node& nd = g.nodes[i];
+        if (is_out[i] || nd.op == RV_CONTIGUOUS) need[i] = 1;
+        if (nd.op == RV_VIEW) {
+            int s = nd.src[0];
+            const Node& sn = g.nodes[s];
+            if (sn.op == RV_BUFFER) continue;
+            if (!pure_broadcast(nd.view, sn.shape, nullptr)) need[s] = 1;
+        }
+    }
+    std::vector<Kernel> kernels;
+    // Fixed point: a root whose region cannot be one kernel has its topmost
+    // reduces cut (they get their own kernels) and is planned again.
+    for (int iter = 0; iter < 4 * n + 4; ++iter) {
+        for (int i = 0; i < n; ++i) c.mat[i] = (g.nodes[i].op == RV_BUFFER) || need[i];
+        kernels.clear();
+        p.regions.clear();
+        bool again = false;
+        for (int i = 0; i < n && !again; ++i) {
+            if (!need[i] || g.nodes[i].op == RV_BUFFER) continue;
+            // location of the value
+            c.loc[i].clear();
+            for (size_t k = 0; k < g.outputs.size(); ++k)
+                if (g.outputs[k] == i) c.loc[i].push_back(Loc{1, (int)k});
+            if (c.loc[i].empty()) {
+                c.loc[i].push_back(Loc{2, (int)p.regions.size()});
+                p.regions.push_back(Region{0, (size_t)numel(g.nodes[i].shape) * dtype_size(g.nodes[i].dtype)});
+            }
+            Kernel k;
+            int preg = -1;
+            std::vector<Kernel> mk;
+            if (try_ew(c, i, k)) {
+                kernels.push_back(k);
+            } else if (try_mfma(c, i, mk, preg)) {
+                for (auto& x : mk) kernels.push_back(x);
+            } else if (try_row(c, i, k)) {
+                kernels.push_back(k);
+            } else if (try_reduce_cells(c, i, k)) {
+                kernels.push_back(k);
+            } else {
+                std::set<int> top;
+                reach_reduces(c, i, top, true);
+                if (top.empty()) fail(RV_E_INVALID, fmt("internal: node %d cannot be scheduled", i));
+                for (int t : top) need[t] = 1;
+                again = true;
+            }
+        }
+        if (!again) {
+            p.kernels = kernels;
+            // outputs that are graph inputs: plain copies
+            for (size_t k = 0; k < g.outputs.size(); ++k) {
+                int o = g.outputs[k];
+                if (g.nodes[o].op != RV_BUFFER) continue;
+                Kernel kc;
+                kc.cls = KClass::EW;
+                kc.domain = g.nodes[o].shape;
+                Builder b{c, kc, o, Builder::EW};
+                int e = b.build(o, identity(kc.domain.size()));
+                std::vector<Loc> save = c.loc[o];
+                c.loc[o] = {Loc{1, (int)k}};
+                add_stores(c, kc, o, e, identity(kc.domain.size()));
+                c.loc[o] = save;
+                p.kernels.push_back(kc);
+            }
+            for (size_t k = 0; k < p.kernels.size(); ++k) p.kernels[k].name = fmt("rv_k%zu", k);
+            return;
+        }
+    }
+    fail(RV_E_INVALID, "internal: scheduling did not converge");
+}
+
+}  // namespace rv

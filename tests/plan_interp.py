@@ -1,0 +1,148 @@
+"""A CPU interpreter of the library's lowered kernels, read from rv_describe:
+every leaf is loaded through its lowered View (offset + sum_d i_d * stride_d
+over the kernel's iteration domain, zero outside the mask), the ops run in
+the listed order over the whole domain, reductions fold in ascending order
+over the reduced dims, and stores write through their lowered Views.
+
+This is the limn README's "Correctness" pattern for the scheduler and codegen
+layer: interpret the lowered program instruction by instruction and diff the
+numbers, so the plan means what it says. Primitive semantics come from the
+oracle's per-primitive helpers (test infrastructure)."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import interp as O
+
+STORAGE = O.STORAGE
+
+
+def _gather(flat: np.ndarray, view: dict, shape) -> np.ndarray:
+    shape = tuple(shape)
+    idx = np.full(shape, int(view["offset"]), dtype=np.int64)
+    inside = np.ones(shape, dtype=bool)
+    for d, g in enumerate(np.indices(shape, dtype=np.int64) if shape else []):
+        idx = idx + g * int(view["strides"][d])
+        inside &= (g >= view["mask_lo"][d]) & (g < view["mask_hi"][d])
+    assert not np.any(inside & ((idx < 0) | (idx >= flat.size))), "lowered view reads out of bounds"
+    vals = flat[np.where(inside, idx, 0)] if flat.size else np.zeros(shape, flat.dtype)
+    return np.where(inside, vals, np.zeros((), flat.dtype)).astype(flat.dtype)
+
+
+def _scatter(flat: np.ndarray, view: dict, shape, vals: np.ndarray) -> None:
+    shape = tuple(shape)
+    idx = np.full(shape, int(view["offset"]), dtype=np.int64)
+    for d, g in enumerate(np.indices(shape, dtype=np.int64) if shape else []):
+        idx = idx + g * int(view["strides"][d])
+    assert idx.min() >= 0 and idx.max() < flat.size, "lowered store out of bounds"
+    flat[idx.ravel()] = np.broadcast_to(vals, shape).ravel()
+
+
+def run_plan(desc: dict, inputs: list, out_specs: list) -> list:
+    """``inputs``: flat storage arrays per input slot; ``out_specs``: (shape,
+    dtype) per output. Returns the outputs (shaped)."""
+    outs = [np.zeros(int(np.prod(s)), dtype=STORAGE[dt]) for s, dt in out_specs]
+    ws: dict[int, np.ndarray] = {}
+
+    def mem(loc, dtype, size_hint=0):
+        if loc["kind"] == "input":
+            return inputs[loc["index"]]
+        if loc["kind"] == "output":
+            return outs[loc["index"]]
+        r = loc["index"]
+        if r not in ws or ws[r].size < size_hint:
+            ws[r] = np.zeros(max(size_hint, 1), dtype=STORAGE[dtype])
+        return ws[r]
+
+    for k in desc["kernels"]:
+        dom = tuple(k["domain"])
+        red = tuple(k["reduce_dims"])
+        ops = k["ops"]
+        if k["class"] == "FOLD":
+            part = ws[k["plan_detail"]["src_region"]]
+            s = np.float32(0.0)
+            for v in part[: k["plan_detail"]["partials"]]:
+                s = np.float32(s + v)
+            st = k["stores"][0]
+            o = mem(st["loc"], st["dtype"])
+            val = O._narrow(np.array([s], np.float32), st["dtype"]) if st["dtype"] in ("bf16", "f16") else \
+                np.array([s]).astype(STORAGE[st["dtype"]])
+            o[st["view"]["offset"]] = val[0]
+            continue
+        if k["plan"] == "empty":
+            continue
+        vals: dict[int, np.ndarray] = {}
+        leaves = k["leaves"]
+        for i, op in enumerate(ops):
+            name, dt = op["op"], op["dtype"]
+            if name == "LOAD":
+                L = leaves[op["leaf"]]
+                if L["zero"]:
+                    vals[i] = np.zeros(dom, STORAGE[dt])
+                else:
+                    vals[i] = _gather(mem(L["loc"], L["dtype"]), L["view"], dom)
+            elif name == "CONST":
+                v = np.array([float(op["cval"])], np.float64)
+                if dt == "bf16":
+                    c = O.f32_to_bf16(v.astype(np.float32))
+                elif dt in O.INTS:
+                    c = v.astype(np.int64).astype(STORAGE[dt])
+                else:
+                    c = v.astype(STORAGE[dt])
+                vals[i] = np.broadcast_to(c.reshape((1,) * len(dom)), dom)
+            elif name == "MFMA_ACC":
+                a_leaf = leaves[_mfma_leaf(k, "a")]
+                b_leaf = leaves[_mfma_leaf(k, "b")]
+                A = O.bf16_to_f32(_gather(mem(a_leaf["loc"], "bf16"), a_leaf["view"], dom))
+                B = O.bf16_to_f32(_gather(mem(b_leaf["loc"], "bf16"), b_leaf["view"], dom))
+                acc = np.zeros(dom[:2] + (1,), np.float32)
+                for kk in range(dom[2]):
+                    acc = (acc + (A[:, :, kk:kk + 1] * B[:, :, kk:kk + 1]).astype(np.float32)).astype(np.float32)
+                vals[i] = np.broadcast_to(acc, dom)
+            elif name in ("SUM", "MAX"):
+                x = np.ascontiguousarray(vals[op["a"]])
+                r = O._reduce(name, x, ops[op["a"]]["dtype"], tuple(red))
+                vals[i] = np.broadcast_to(r, dom)
+            elif name == "CAST":
+                vals[i] = O._cast(np.ascontiguousarray(vals[op["a"]]), ops[op["a"]]["dtype"], dt)
+            elif name in ("NEG", "EXP", "LOG", "SQRT", "RECIP"):
+                vals[i] = O._unary(name, np.ascontiguousarray(vals[op["a"]]), dt)
+            elif name in ("ADD", "MUL", "CMPLT"):
+                vals[i] = O._binary(name, np.ascontiguousarray(vals[op["a"]]), np.ascontiguousarray(vals[op["b"]]),
+                                    ops[op["a"]]["dtype"])
+            elif name == "WHERE":
+                vals[i] = np.where(vals[op["a"]] != 0, vals[op["b"]], vals[op["c"]]).astype(STORAGE[dt])
+            else:
+                raise AssertionError(name)
+        for st in k["stores"]:
+            v = vals[st_ex(k, st)]
+            if k["class"] == "MFMA" and st["loc"]["kind"] == "workspace":
+                # one partial: the epilogue summed over the whole (m, n) plane
+                plane = np.ascontiguousarray(v[:, :, :1]).astype(np.float32).ravel()
+                s = np.float32(0.0)
+                for x in plane:
+                    s = np.float32(s + x)
+                buf = mem(st["loc"], "f32", 1)
+                buf[:] = 0
+                buf[0] = s
+                continue
+            size = 1 + int(np.dot(np.array(dom) - 1, np.array(st["view"]["strides"]))) + st["view"]["offset"]
+            o = mem(st["loc"], st["dtype"], size)
+            if st["loc"]["kind"] == "workspace" and o.dtype != STORAGE[st["dtype"]]:
+                ws[st["loc"]["index"]] = o = np.zeros(size, STORAGE[st["dtype"]])
+            _scatter(o, st["view"], dom, v.astype(STORAGE[st["dtype"]]))
+    return [o.reshape(s) for o, (s, _) in zip(outs, out_specs)]
+
+
+def st_ex(k, st):
+    """The op a store writes."""
+    return st["ex"]
+
+
+def _mfma_leaf(k, which):
+    # the operand leaves are the bf16 loads that walk k (stride along dim 2 > 0)
+    cands = [i for i, L in enumerate(k["leaves"]) if L["dtype"] == "bf16" and L["view"]["strides"][2] != 0]
+    a = [i for i in cands if k["leaves"][i]["view"]["strides"][1] == 0]
+    b = [i for i in cands if k["leaves"][i]["view"]["strides"][0] == 0]
+    return a[0] if which == "a" else b[0]

@@ -1,0 +1,187 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, element by element, at sizes that span several tiles and
+a ragged tail, with each config's tolerance written here and its bound
+printed. Bit-exact where the pages' semantics leave one answer (movement,
+transpose, in-order folds, CMPLT/WHERE branches without transcendentals)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import interp
+from reduce_view_amd import synth
+from tests.harness import U, gamma, report, run, ulp32, ulp_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from reduce_view_amd import rv
+    rv.rv_init(0)
+
+
+def _prog(spec):
+    from reduce_view_amd import rv
+    return rv.compile_spec(spec)
+
+
+def _case(name):
+    print(f"CASE {name}", flush=True)
+
+
+# ---- config 1: broadcast MUL + SUM over k ------------------------------------
+
+@pytest.mark.parametrize("m,n,k", [(64, 64, 64), (4, 3, 5), (37, 70, 19), (1, 300, 7)])
+def test_matmul_broadcast_in_order_is_bit_exact(m, n, k):
+    _case(f"matmul {m}x{n}x{k}")
+    spec = synth.matmul_broadcast(m, n, k)
+    inp = synth.inputs_matmul(m, n, k, seed=0)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    absprod = np.abs(inp["A"]).astype(np.float64) @ np.abs(inp["B"]).astype(np.float64)
+    report(f"matmul_{m}x{n}x{k}", np.abs(got - ref)[:, :, 0], 4 * gamma(k - 1) * absprod)
+    assert got.tobytes() == ref.tobytes()
+
+
+def test_matmul_raw_descriptors():
+    spec = synth.matmul_broadcast_raw(33, 17, 29)
+    inp = synth.inputs_matmul(33, 17, 29, seed=3)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
+# ---- config 2: elementwise chain, masked chain, transpose --------------------
+
+def _chain_check(spec, inp, name):
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    assert got.shape == ref.shape
+    # where the EXP branch is not taken the chain is MUL then ADD: bit-exact;
+    # elsewhere one float32 expf (2 ulp) then the ADD's rounding
+    it = oracle.Interpreter(spec, inp)
+    e_node = [i for i, nd in enumerate(spec.nodes) if nd["op"] == "EXP"][0]
+    c_node = [i for i, nd in enumerate(spec.nodes) if nd["op"] == "CMPLT"][0]
+    e = it.value(e_node)
+    took_exp = it.value(c_node) == 0
+    bound = np.where(took_exp, 2 * ulp32(e) + ulp32(ref), 0.0)
+    report(name, np.abs(got.astype(np.float64) - ref), bound)
+    assert (got[~took_exp] == ref[~took_exp]).all()
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= bound)
+
+
+@pytest.mark.parametrize("r,c", [(256, 320), (131, 77), (4096, 4096)])
+def test_ew_chain(r, c):
+    _case(f"ew_chain {r}x{c}")
+    inp = synth.inputs_ew(r, c, seed=1)
+    _chain_check(synth.ew_chain(r, c), inp, f"ew_chain_{r}x{c}")
+
+
+@pytest.mark.parametrize("r,c", [(256, 320), (131, 77), (4096, 4096)])
+def test_ew_chain_masked(r, c):
+    _case(f"ew_chain masked {r}x{c}")
+    inp = synth.inputs_ew(r, c, seed=1)
+    _chain_check(synth.ew_chain(r, c, masked=True), inp, f"ew_chain_masked_{r}x{c}")
+
+
+@pytest.mark.parametrize("r,c", [(64, 64), (100, 37), (4096, 4096), (1, 513)])
+def test_transpose_bit_exact(r, c):
+    _case(f"transpose {r}x{c}")
+    x = synth.inputs_ew(r, c, seed=1)["X"]
+    got, = run(_prog(synth.transpose(r, c)), {"X": x})
+    assert got.tobytes() == np.ascontiguousarray(x.T).tobytes()
+
+
+# ---- config 3: softmax, RMSNorm ------------------------------------------------
+
+@pytest.mark.parametrize("rows,n", [(64, 4096), (33, 1000), (5, 128)])
+def test_softmax(rows, n):
+    _case(f"softmax {rows}x{n}")
+    spec = synth.softmax(rows, n)
+    inp = synth.inputs_softmax(rows, n)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    bound = ref * (4 * gamma(n - 1) + 2 * 2.0 ** -23 + 4 * U) + 3 * 2.0 ** -149
+    report(f"softmax_{rows}x{n}", np.abs(got - ref), bound)
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= bound)
+
+
+@pytest.mark.parametrize("rows,n", [(64, 4096), (33, 1000), (5, 128)])
+def test_rmsnorm(rows, n):
+    _case(f"rmsnorm {rows}x{n}")
+    spec = synth.rmsnorm(rows, n)
+    inp = synth.inputs_rmsnorm(rows, n)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    bound = np.abs(ref).astype(np.float64) * (0.5 * 4 * gamma(n - 1) + 6 * U)
+    report(f"rmsnorm_{rows}x{n}", np.abs(got - ref), bound)
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= bound)
+
+
+# ---- config 4: LayerNorm (bf16 in/out) -----------------------------------------
+
+@pytest.mark.parametrize("rows,n", [(16, 8192), (9, 1000), (3, 256)])
+def test_layernorm(rows, n):
+    _case(f"layernorm {rows}x{n}")
+    spec = synth.layernorm(rows, n)
+    inp = synth.inputs_layernorm(rows, n)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    g = interp.bf16_to_f32(got).astype(np.float64)
+    r = interp.bf16_to_f32(ref).astype(np.float64)
+    bound = ulp_bf16(r) + np.abs(r) * (2 * gamma(n - 1) + 8 * U) + 2.0 ** -133
+    report(f"layernorm_{rows}x{n}", np.abs(g - r), bound)
+    assert np.all(np.abs(g - r) <= bound)
+
+
+# ---- config 5: bf16 contraction on MFMA + relu^2 + full SUM ----------------------
+
+@pytest.mark.parametrize("m,n,k", [(128, 128, 64), (256, 384, 192)])
+def test_gemm_integer_valued_bit_exact(m, n, k):
+    _case(f"gemm int {m}x{n}x{k}")
+    inp = synth.inputs_gemm_integer(m, n, k)
+    spec = synth.gemm_bf16(m, n, k)
+    prog = _prog(spec)
+    assert [kk["class"] for kk in prog.describe()["kernels"]] == ["MFMA"]
+    got, = run(prog, inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+    # relu(y)^2 summed: exact in any order while the total stays below 2^24
+    # (every partial sum of non-negative integers is then a float32 integer)
+    inp = synth.inputs_gemm_integer(m, n, k, lo=-1, hi=1)
+    yi = (interp.bf16_to_f32(inp["A"]).astype(np.int64) @ interp.bf16_to_f32(inp["B"]).astype(np.int64))
+    assert (np.maximum(yi, 0) ** 2).sum() < 2 ** 24
+    spec = synth.gemm_relu2_sum(m, n, k)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 256, 256), (512, 384, 640)])
+def test_gemm_relu2_sum(m, n, k):
+    _case(f"gemm relu2 sum {m}x{n}x{k}")
+    inp = synth.inputs_gemm(m, n, k)
+    spec = synth.gemm_bf16(m, n, k)
+    y_gpu, = run(_prog(spec), inp)
+    y_ref, = oracle.run(spec, inp)
+    a = np.abs(interp.bf16_to_f32(inp["A"]).astype(np.float64))
+    b = np.abs(interp.bf16_to_f32(inp["B"]).astype(np.float64))
+    dy = 4 * gamma(k - 1) * (a @ b)
+    report(f"gemm_y_{m}x{n}x{k}", np.abs(y_gpu - y_ref)[:, :, 0], dy)
+    assert np.all(np.abs(y_gpu - y_ref)[:, :, 0] <= dy)
+    spec = synth.gemm_relu2_sum(m, n, k)
+    prog = _prog(spec)
+    desc = prog.describe()
+    s_gpu, = run(prog, inp)
+    s_ref, = oracle.run(spec, inp)
+    y = y_ref[:, :, 0].astype(np.float64)
+    q = np.maximum(y, 0) ** 2
+    depth = desc["kernels"][0]["plan_detail"]["partial_sum_depth"] + desc["kernels"][1]["plan_detail"]["sum_depth"]
+    ds = (np.sum((2 * np.abs(y) * dy + dy ** 2) * (y > -dy)) + U * q.sum() + 4 * gamma(depth) * q.sum()
+          + U * abs(float(s_ref.ravel()[0])))
+    report(f"gemm_S_{m}x{n}x{k}", np.array([abs(float(s_gpu.ravel()[0]) - float(s_ref.ravel()[0]))]), np.array([ds]))
+    assert abs(float(s_gpu.ravel()[0]) - float(s_ref.ravel()[0])) <= ds
