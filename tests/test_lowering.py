@@ -1,0 +1,163 @@
+"""Scheduler and lowering on the CPU (no GPU): the kernel classes each
+workload is cut into, the limn IR dump's structure for (4, 5) @ (5, 3), and
+a lowered-plan interpreter (tests/plan_interp.py) that executes what
+rv_describe says the kernels do and diffs it against the oracle."""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import interp as O
+from reduce_view_amd import rv, synth
+from tests.harness import U, gamma
+from tests.plan_interp import run_plan
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _golden(name):
+    facts = {}
+    for line in open(os.path.join(HERE, "golden", name)):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, *v = line.split()
+        facts[k] = v
+    return facts
+
+
+def test_limn_ir_dump_structure():
+    f = _golden("limn_ir_matmul_4x5x3.txt")
+    prog = rv.compile_spec(synth.matmul_broadcast(4, 3, 5))
+    d = prog.describe()
+    assert len(d["kernels"]) == int(f["kernels"][0])
+    k = d["kernels"][0]
+    assert k["class"] == "REDUCE"
+    assert k["domain"] == [int(x) for x in f["domain"]]
+    assert k["reduce_dims"] == [int(x) for x in f["reduce_dims"]]
+    strides = sorted(tuple(L["view"]["strides"]) for L in k["leaves"])
+    assert strides == sorted([tuple(int(x) for x in f["in0_strides"]), tuple(int(x) for x in f["in1_strides"])])
+    assert tuple(k["stores"][0]["view"]["strides"]) == tuple(int(x) for x in f["out_strides"])
+    assert prog.out_desc[0][0] == tuple(int(x) for x in f["out_shape"])
+    assert k["lane_dim"] == int(f["innermost_dim"][0])
+    ops = [o["op"] for o in k["ops"]]
+    assert ops.count("SUM") == 1 and "MUL" in ops
+    src = prog.source()
+    assert "float acc = 0.0f;" in src  # identity fill 0.0, then ACCUM ADD
+
+
+def _interp(spec, inputs):
+    prog = rv.compile_spec(spec)
+    d = prog.describe()
+    flat = [np.ascontiguousarray(inputs[s]).ravel() for s in prog.slots]
+    outs = run_plan(d, flat, prog.out_desc)
+    return d, outs
+
+
+CLASSES = {
+    "matmul": (lambda: synth.matmul_broadcast(7, 5, 9), lambda: synth.inputs_matmul(7, 5, 9), ["REDUCE"]),
+    "ew": (lambda: synth.ew_chain(19, 23), lambda: synth.inputs_ew(19, 23), ["EW"]),
+    "ew_masked": (lambda: synth.ew_chain(19, 23, masked=True), lambda: synth.inputs_ew(19, 23), ["EW"]),
+    "transpose": (lambda: synth.transpose(13, 29), lambda: {"X": synth.inputs_ew(13, 29)["X"]}, ["EW"]),
+    "softmax": (lambda: synth.softmax(6, 300), lambda: synth.inputs_softmax(6, 300), ["ROW"]),
+    "rmsnorm": (lambda: synth.rmsnorm(6, 300), lambda: synth.inputs_rmsnorm(6, 300), ["ROW"]),
+    "layernorm": (lambda: synth.layernorm(5, 256), lambda: synth.inputs_layernorm(5, 256), ["ROW"]),
+    "gemm": (lambda: synth.gemm_relu2_sum(128, 128, 64), lambda: synth.inputs_gemm(128, 128, 64),
+             ["MFMA", "FOLD"]),
+    "gemm_y": (lambda: synth.gemm_bf16(128, 256, 128), lambda: synth.inputs_gemm(128, 256, 128), ["MFMA"]),
+}
+
+
+@pytest.mark.parametrize("name", list(CLASSES))
+def test_plan_interpreter_matches_oracle(name):
+    mk_spec, mk_in, classes = CLASSES[name]
+    spec, inp = mk_spec(), mk_in()
+    d, got = _interp(spec, inp)
+    assert [k["class"] for k in d["kernels"]] == classes
+    ref = oracle.run(spec, inp)
+    for g, r in zip(got, ref):
+        assert g.shape == r.shape
+        if name in ("gemm",):
+            # the plan folds the epilogue in one order, the oracle widens: close
+            assert abs(float(g.ravel()[0]) - float(r.ravel()[0])) <= 1e-4 * abs(float(r.ravel()[0]))
+        else:
+            # the plan folds every reduce in ascending order, as the oracle does
+            assert g.tobytes() == r.tobytes(), name
+
+
+def test_cuts_and_workspace():
+    # a permute of a computed value is a cut: the value goes to workspace
+    g = synth.Spec()
+    a = g.buffer("a", (8, 12), "f32")
+    b = g.buffer("b", (8, 12), "f32")
+    s = g.add(a, b)
+    g.output(g.mul(g.view(s, ("permute", (1, 0))), g.view(s, ("permute", (1, 0)))))
+    inp = {"a": np.arange(96, dtype=np.float32).reshape(8, 12), "b": np.ones((8, 12), np.float32)}
+    d, got = _interp(g, inp)
+    assert [k["class"] for k in d["kernels"]] == ["EW", "EW"]
+    assert d["workspace_bytes"] >= 96 * 4
+    assert got[0].tobytes() == oracle.run(g, inp)[0].tobytes()
+    # reduces over different axes cannot share a row space: each is cut
+    g = synth.Spec()
+    x = g.buffer("x", (6, 7, 5), "f32")
+    s1 = g.sum(x, (2,))
+    s2 = g.max(s1, (0,))
+    g.output(s2)
+    xi = np.random.default_rng(1).standard_normal((6, 7, 5)).astype(np.float32)
+    d, got = _interp(g, {"x": xi})
+    assert [k["class"] for k in d["kernels"]] == ["REDUCE", "REDUCE"]
+    assert got[0].tobytes() == oracle.run(g, {"x": xi})[0].tobytes()
+    # an input returned as an output is a copy; several outputs
+    g = synth.Spec()
+    x = g.buffer("x", (5, 3), "f32")
+    m = g.max(x, (1,))
+    g.output(x, m, m)
+    xi = np.random.default_rng(2).standard_normal((5, 3)).astype(np.float32)
+    d, got = _interp(g, {"x": xi})
+    ref = oracle.run(g, {"x": xi})
+    for a, b in zip(got, ref):
+        assert a.tobytes() == b.tobytes()
+
+
+def test_empty_and_size_one_dims():
+    g = synth.Spec()
+    x = g.buffer("x", (0, 5), "f32")
+    g.output(g.exp(x))
+    d, got = _interp(g, {"x": np.zeros((0, 5), np.float32)})
+    assert d["kernels"][0]["plan"] == "empty" and got[0].shape == (0, 5)
+    g = synth.Spec()
+    x = g.buffer("x", (1, 7, 1, 3), "f32")
+    g.output(g.sum(x, (1, 3)))
+    xi = np.random.default_rng(3).standard_normal((1, 7, 1, 3)).astype(np.float32)
+    d, got = _interp(g, {"x": xi})
+    assert got[0].tobytes() == oracle.run(g, {"x": xi})[0].tobytes()
+
+
+def test_dims_merge_for_contiguous_chains():
+    prog = rv.compile_spec(synth.rmsnorm(64, 512))
+    k = prog.describe()["kernels"][0]
+    assert k["domain"] == [64, 512] and k["reduce_dims"] == [1]
+    g = synth.Spec()
+    a = g.buffer("a", (8, 16, 32), "f32")
+    g.output(g.exp(a))
+    k = rv.compile_spec(g).describe()["kernels"][0]
+    assert k["domain"] == [8 * 16 * 32] and k["plan"] == "rowmajor"
+
+
+def test_dtype_variants_through_the_plan():
+    rng = np.random.default_rng(4)
+    for dt, mk in (("i8", lambda s: rng.integers(-128, 128, s).astype(np.int8)),
+                   ("i32", lambda s: rng.integers(-2 ** 31, 2 ** 31, s, dtype=np.int64).astype(np.int32)),
+                   ("f64", lambda s: rng.standard_normal(s)),
+                   ("f16", lambda s: rng.standard_normal(s).astype(np.float16))):
+        g = synth.Spec()
+        a = g.buffer("a", (9, 11), dt)
+        b = g.buffer("b", (9, 11), dt)
+        s = g.add(g.mul(a, b), g.neg(b))
+        g.output(s, g.sum(s, (1,)), g.max(s, (0,)))
+        inp = {"a": mk((9, 11)), "b": mk((9, 11))}
+        d, got = _interp(g, inp)
+        ref = oracle.run(g, inp)
+        for x, y in zip(got, ref):
+            assert x.tobytes() == y.tobytes(), dt
