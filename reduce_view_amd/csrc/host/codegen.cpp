@@ -402,36 +402,55 @@ std::string Gen::gen_rowmajor() {
 }
 
 // ---------------------------------------------------------------------------
-// EW, tiled plan (transpose and chains with a permuted operand): a 64 x 64
-// tile of the (Y, X) domain per workgroup. Operands contiguous along Y are
-// read along Y (coalesced) into an LDS tile padded by one element per row,
-// then read back along X; the others are read along X directly. Interior
+// EW, tiled plan (transpose, and chains with a permuted operand): a 64 x 64
+// tile of the (Y, X) domain per workgroup, 2 x 2 waves of 8 x 8 lanes, each
+// lane owning a 4 x 4 block of cells. An operand contiguous along X is read
+// as 4 row vectors, one contiguous along Y as 4 column vectors; the 4 x 4
+// block is transposed in registers (it is only a choice of which register
+// feeds which cell), so no LDS round trip and no barrier is needed. Every
+// vector read and write of a wave covers whole 128-byte lines. Interior
 // tiles run without range checks; edge tiles check the domain and masks.
 // ---------------------------------------------------------------------------
 std::string Gen::gen_tiled() {
     const int X = rank - 1, Y = rank - 2;
     const int64_t NX = k.domain[X], NY = k.domain[Y];
     std::ostringstream b;
-    std::vector<int> staged(k.leaves.size(), 0);
     std::vector<int> used(k.leaves.size(), 0);
     for (size_t e = 0; e < k.ex.size(); ++e)
         if (live[e] && k.ex[e].op == RV_BUFFER) used[k.ex[e].leaf] = 1;
-    int ns = 0;
-    for (size_t l = 0; l < k.leaves.size(); ++l) {
-        const Leaf& L = k.leaves[l];
-        if (used[l] && !L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) {
-            staged[l] = 1;
-            b << "  __shared__ " << vt(L.dtype) << " t" << l << "[64][65];\n";
-            ++ns;
+    // tile plan: WX x WY waves of 8 x 8 lanes, 4 x 4 cells per lane
+    int WX = 2, WY = 2, ORDER = 0;
+    sscanf(k.plan_json.c_str(), "\"tile\":[%*d,%*d],\"waves\":[%d,%d],\"order\":%d", &WY, &WX, &ORDER);
+    const int TX = 32 * WX, TY = 32 * WY;
+    const int64_t GX = (NX + TX - 1) / TX, GY = (NY + TY - 1) / TY;
+    b << "  const int t = threadIdx.x, lane = t & 63, w = t >> 6;\n";
+    b << "  const " << I << " bid = blockIdx.x;\n";
+    switch (ORDER) {
+        case 1:  // consecutive workgroups walk Y
+            b << "  const " << I << " ty = bid % " << lit(GY) << ", tx = bid / " << lit(GY) << ";\n";
+            break;
+        case 2:  // diagonal: consecutive workgroups differ in both X and Y
+            b << "  const " << I << " tx = bid % " << lit(GX) << ", ty = (bid / " << lit(GX) << " + tx) % " << lit(GY)
+              << ";\n";
+            break;
+        case 3: {  // each XCD (bid % 8 under round-robin dispatch) owns a contiguous range of tiles
+            int64_t n = GX * GY;
+            if (n % 8 == 0) {
+                b << "  const " << I << " sb = (bid & 7) * " << lit(n / 8) << " + (bid >> 3);\n";
+                b << "  const " << I << " tx = sb % " << lit(GX) << ", ty = sb / " << lit(GX) << ";\n";
+                break;
+            }
         }
+        // fall through
+        default:
+            b << "  const " << I << " tx = bid % " << lit(GX) << ", ty = bid / " << lit(GX) << ";\n";
     }
-    b << "  const int t = threadIdx.x;\n";
-    b << "  const " << I << " X0 = (" << I << ")blockIdx.x * 64, Y0 = (" << I << ")blockIdx.y * 64;\n";
-    std::vector<int> outer;
+    b << "  const " << I << " X0 = tx * " << TX << ", Y0 = ty * " << TY << ";\n";
+    b << "  const " << I << " x = X0 + (w % " << WX << ") * 32 + (lane & 7) * 4;\n";
+    b << "  const " << I << " y = Y0 + (w / " << WX << ") * 32 + (lane >> 3) * 4;\n";
     {
         std::string rem = "(" + I + ")blockIdx.z";
         for (int d = Y - 1; d >= 0; --d) {
-            outer.push_back(d);
             b << "  const " << I << " i" << d << " = " << rem << " % " << lit(k.domain[d]) << ";\n";
             if (d > 0) {
                 b << "  const " << I << " q" << d << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
@@ -439,130 +458,115 @@ std::string Gen::gen_tiled() {
             }
         }
     }
-    auto idx_at = [&](const std::string& y, const std::string& x) {
+    auto idx_at = [&](const std::string& yy, const std::string& xx) {
         std::vector<std::string> idx(rank);
         for (int d = 0; d < Y; ++d) idx[d] = fmt("i%d", d);
-        idx[Y] = y;
-        idx[X] = x;
+        idx[Y] = yy;
+        idx[X] = xx;
         return idx;
     };
-    // interior: whole tile inside the domain and inside every used leaf's mask
-    std::string inter = fmt("X0 + 64 <= %s && Y0 + 64 <= %s", lit(NX).c_str(), lit(NY).c_str());
+    std::vector<int> all;
+    for (int d = 0; d < rank; ++d) all.push_back(d);
+    // interior: the whole workgroup tile is inside the domain and every mask
+    std::string inter = fmt("X0 + %d <= %s && Y0 + %d <= %s", TX, lit(NX).c_str(), TY, lit(NY).c_str());
     for (size_t l = 0; l < k.leaves.size(); ++l) {
         const Leaf& L = k.leaves[l];
         if (!used[l] || L.zero) continue;
         for (int d = 0; d < rank; ++d) {
             if (!masked(L.v, d)) continue;
             if (d == X)
-                inter += fmt(" && X0 >= %s && X0 + 64 <= %s", lit(L.v.mask_lo[d]).c_str(), lit(L.v.mask_hi[d]).c_str());
+                inter += fmt(" && X0 >= %s && X0 + %d <= %s", lit(L.v.mask_lo[d]).c_str(), TX, lit(L.v.mask_hi[d]).c_str());
             else if (d == Y)
-                inter += fmt(" && Y0 >= %s && Y0 + 64 <= %s", lit(L.v.mask_lo[d]).c_str(), lit(L.v.mask_hi[d]).c_str());
+                inter += fmt(" && Y0 >= %s && Y0 + %d <= %s", lit(L.v.mask_lo[d]).c_str(), TY, lit(L.v.mask_hi[d]).c_str());
             else
                 inter += fmt(" && i%d >= %s && i%d < %s", d, lit(L.v.mask_lo[d]).c_str(), d, lit(L.v.mask_hi[d]).c_str());
         }
     }
     b << "  const bool interior = " << inter << ";\n";
-    // staged loads: thread reads 4 consecutive y at column lx
-    if (ns) {
-        b << "  {\n    const int ly = (t & 15) * 4, lx0 = t >> 4;\n";
-        for (size_t l = 0; l < k.leaves.size(); ++l) {
-            if (!staged[l]) continue;
-            const Leaf& L = k.leaves[l];
-            std::string P = pname(L.loc, L.dtype, false);
-            bool vec = leaf_vec_ok(L, Y, 4);
-            b << "    for (int j = 0; j < 4; ++j) {\n      const int lx = lx0 + 16 * j;\n";
-            auto idx = idx_at("Y0 + ly", "X0 + lx");
-            if (vec) {
-                b << "      if (interior) {\n";
-                b << "        const rv_pack<" << st(L.dtype) << ", 4> v = rv_ldv<" << st(L.dtype) << ", 4>(" << P << " + "
-                  << addr(L.v, idx) << ");\n";
-                b << "        for (int q = 0; q < 4; ++q) t" << l << "[lx][ly + q] = " << ld(L.dtype, "v.v[q]") << ";\n";
-                b << "      } else\n";
-            }
-            b << "      for (int q = 0; q < 4; ++q) {\n";
-            b << "        const " << I << " y = Y0 + ly + q, x = X0 + lx;\n";
-            auto idq = idx_at("y", "x");
-            std::vector<int> all;
-            for (int d = 0; d < rank; ++d) all.push_back(d);
-            std::string mc = mask_cond(L.v, idq, all);
-            b << "        t" << l << "[lx][ly + q] = (interior || (y < " << lit(NY) << " && x < " << lit(NX)
-              << (mc.empty() ? "" : " && " + mc) << ")) ? " << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << " : "
-              << zero_of(L.dtype) << ";\n";
-            b << "      }\n    }\n";
-        }
-        b << "  }\n  __syncthreads();\n";
-    }
-    b << "  const int tx = (t & 15) * 4, ty0 = t >> 4;\n";
-    // body, emitted twice: without range checks (interior) and with them
     for (int edge = 0; edge < 2; ++edge) {
         b << (edge ? "  else {\n" : "  if (interior) {\n");
-        b << "  for (int j = 0; j < 4; ++j) {\n";
-        b << "    const " << I << " y = Y0 + ty0 + 16 * j;\n";
-        // direct leaves
+        // loads: cell (r, c) of the lane's block is (y + r, x + c)
         for (size_t l = 0; l < k.leaves.size(); ++l) {
             const Leaf& L = k.leaves[l];
-            if (!used[l] || L.zero || staged[l]) continue;
+            if (!used[l] || L.zero) continue;
             std::string P = pname(L.loc, L.dtype, false);
             std::string V = fmt("l%zu", l);
-            b << "    " << vt(L.dtype) << " " << V << "[4];\n";
-            auto idx = idx_at("y", "X0 + tx");
-            if (!edge && leaf_vec_ok(L, X, 4)) {
-                b << "    { const rv_pack<" << st(L.dtype) << ", 4> v = rv_ldv<" << st(L.dtype) << ", 4>(" << P << " + "
-                  << addr(L.v, idx) << ");\n";
-                b << "      for (int q = 0; q < 4; ++q) " << V << "[q] = " << ld(L.dtype, "v.v[q]") << "; }\n";
-            } else {
-                b << "    for (int q = 0; q < 4; ++q) {\n      const " << I << " x = X0 + tx + q;\n";
-                auto idq = idx_at("y", "x");
-                if (edge) {
-                    std::vector<int> all;
-                    for (int d = 0; d < rank; ++d) all.push_back(d);
-                    std::string mc = mask_cond(L.v, idq, all);
-                    b << "      " << V << "[q] = (y < " << lit(NY) << " && x < " << lit(NX) << (mc.empty() ? "" : " && " + mc)
-                      << ") ? " << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << " : " << zero_of(L.dtype) << ";\n";
+            const std::string T = st(L.dtype);
+            b << "    " << vt(L.dtype) << " " << V << "[4][4];\n";
+            const bool along_x = !edge && leaf_vec_ok(L, X, 4);
+            const bool along_y = !edge && !along_x && leaf_vec_ok(L, Y, 4);
+            const bool ybcast = L.v.strides[Y] == 0 && !masked(L.v, Y);
+            const bool xbcast = L.v.strides[X] == 0 && !masked(L.v, X);
+            if (along_x) {
+                if (ybcast) {
+                    b << "    { const rv_pack<" << T << ", 4> v = rv_ldv<" << T << ", 4>(" << P << " + "
+                      << addr(L.v, idx_at("y", "x")) << ");\n";
+                    b << "      for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) " << V << "[r][c] = "
+                      << ld(L.dtype, "v.v[c]") << "; }\n";
                 } else {
-                    b << "      " << V << "[q] = " << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << ";\n";
+                    b << "    for (int r = 0; r < 4; ++r) { const rv_pack<" << T << ", 4> v = rv_ldv<" << T << ", 4>("
+                      << P << " + " << addr(L.v, idx_at("y + r", "x")) << ");\n";
+                    b << "      for (int c = 0; c < 4; ++c) " << V << "[r][c] = " << ld(L.dtype, "v.v[c]") << "; }\n";
                 }
-                b << "    }\n";
+            } else if (along_y) {
+                if (xbcast) {
+                    b << "    { const rv_pack<" << T << ", 4> v = rv_ldv<" << T << ", 4>(" << P << " + "
+                      << addr(L.v, idx_at("y", "x")) << ");\n";
+                    b << "      for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) " << V << "[r][c] = "
+                      << ld(L.dtype, "v.v[r]") << "; }\n";
+                } else {
+                    b << "    for (int c = 0; c < 4; ++c) { const rv_pack<" << T << ", 4> v = rv_ldv<" << T << ", 4>("
+                      << P << " + " << addr(L.v, idx_at("y", "x + c")) << ");\n";
+                    b << "      for (int r = 0; r < 4; ++r) " << V << "[r][c] = " << ld(L.dtype, "v.v[r]") << "; }\n";
+                }
+            } else {
+                b << "    for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) {\n";
+                b << "      const " << I << " yy = y + r, xx = x + c;\n";
+                auto idq = idx_at("yy", "xx");
+                std::string mc = edge ? mask_cond(L.v, idq, all) : "";
+                std::string cond = edge ? fmt("yy < %s && xx < %s", lit(NY).c_str(), lit(NX).c_str()) +
+                                              (mc.empty() ? "" : " && " + mc)
+                                        : "";
+                b << "      " << V << "[r][c] = " << (cond.empty() ? "" : "(" + cond + ") ? ")
+                  << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << (cond.empty() ? "" : " : " + zero_of(L.dtype))
+                  << ";\n    }\n";
             }
         }
         for (size_t e = 0; e < k.ex.size(); ++e) {
             if (!live[e]) continue;
             const Ex& x = k.ex[e];
-            b << "    " << vt(x.dtype) << " e" << e << "[4];\n    for (int q = 0; q < 4; ++q) e" << e << "[q] = ";
+            b << "    " << vt(x.dtype) << " e" << e << "[4][4];\n    for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) e"
+              << e << "[r][c] = ";
             if (x.op == RV_BUFFER) {
-                const Leaf& L = k.leaves[x.leaf];
-                if (L.zero)
+                if (k.leaves[x.leaf].zero)
                     b << zero_of(x.dtype);
-                else if (staged[x.leaf])
-                    b << "t" << x.leaf << "[tx + q][ty0 + 16 * j]";
                 else
-                    b << "l" << x.leaf << "[q]";
+                    b << "l" << x.leaf << "[r][c]";
             } else if (x.op == RV_CONST) {
                 b << const_lit(x.dtype, x.cval);
             } else {
-                auto E = [&](int i) { return i < 0 ? std::string() : fmt("e%d[q]", i); };
+                auto E = [&](int i) { return i < 0 ? std::string() : fmt("e%d[r][c]", i); };
                 b << op_code(k, x, E(x.a), E(x.b), E(x.c));
             }
             b << ";\n";
         }
         for (const Store& s : k.stores) {
             std::string P = pname(s.loc, s.dtype, true);
-            auto idx = idx_at("y", "X0 + tx");
             bool vec = !edge && s.v.strides[X] == 1 && s.v.offset % 4 == 0;
             for (int d = 0; d < X; ++d)
                 if (k.domain[d] > 1 && s.v.strides[d] % 4) vec = false;
             if (vec) {
-                b << "    { rv_pack<" << st(s.dtype) << ", 4> v;\n      for (int q = 0; q < 4; ++q) v.v[q] = "
-                  << sv(s.dtype, fmt("e%d[q]", s.ex)) << ";\n";
-                b << "      rv_stv<" << st(s.dtype) << ", 4>(" << P << " + " << addr(s.v, idx) << ", v); }\n";
+                b << "    for (int r = 0; r < 4; ++r) { rv_pack<" << st(s.dtype) << ", 4> v;\n";
+                b << "      for (int c = 0; c < 4; ++c) v.v[c] = " << sv(s.dtype, fmt("e%d[r][c]", s.ex)) << ";\n";
+                b << "      rv_stv<" << st(s.dtype) << ", 4>(" << P << " + " << addr(s.v, idx_at("y + r", "x")) << ", v); }\n";
             } else {
-                b << "    for (int q = 0; q < 4; ++q) {\n      const " << I << " x = X0 + tx + q;\n";
-                auto idq = idx_at("y", "x");
-                b << "      " << (edge ? fmt("if (y < %s && x < %s) ", lit(NY).c_str(), lit(NX).c_str()) : "") << P << "["
-                  << addr(s.v, idq) << "] = " << sv(s.dtype, fmt("e%d[q]", s.ex)) << ";\n    }\n";
+                b << "    for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) {\n";
+                b << "      const " << I << " yy = y + r, xx = x + c;\n";
+                b << "      " << (edge ? fmt("if (yy < %s && xx < %s) ", lit(NY).c_str(), lit(NX).c_str()) : "") << P
+                  << "[" << addr(s.v, idx_at("yy", "xx")) << "] = " << sv(s.dtype, fmt("e%d[r][c]", s.ex)) << ";\n    }\n";
             }
         }
-        b << "  }\n  }\n";
+        b << "  }\n";
     }
     return b.str();
 }
@@ -642,10 +646,13 @@ std::string Gen::gen_row() {
     for (size_t e = 0; e < k.ex.size(); ++e)
         if (live[e] && k.ex[e].op == RV_BUFFER) used[k.ex[e].leaf] = 1;
     auto emit_full_load = [&](std::ostringstream& s, int l, const std::string& rowok, const std::vector<std::string>& kidx,
-                              const std::string& V) {
+                              const std::string& V, bool raw) {
         const Leaf& L = k.leaves[l];
         std::string P = pname(L.loc, L.dtype, false);
-        s << "    " << vt(L.dtype) << " " << V << "[" << E << "];\n";
+        // raw: keep the storage type in registers (hoisted weights: half the
+        // VGPRs for 2-byte dtypes), widened where they are used
+        auto ld = [&](int dt, const std::string& e) { return raw ? e : rv::ld(dt, e); };
+        s << "    " << (raw ? st(L.dtype) : vt(L.dtype)) << " " << V << "[" << E << "];\n";
         s << "    for (int v = 0; v < " << NV << "; ++v) {\n";
         s << "      const " << I << " n0 = " << nexpr("v", "0") << ";\n";
         std::vector<std::string> idx = kidx;
@@ -667,7 +674,7 @@ std::string Gen::gen_row() {
         red_idx(idx, "n");
         std::string mc = mask_cond(L.v, idx, rd);
         s << "        " << V << "[v * " << VW << " + i] = (" << rowok << " && n < " << lit(NR) << (mc.empty() ? "" : " && " + mc)
-          << ") ? " << ld(L.dtype, P + "[" + addr(L.v, idx) + "]") << " : " << zero_of(L.dtype) << ";\n";
+          << ") ? " << ld(L.dtype, P + "[" + addr(L.v, idx) + "]") << " : " << (raw ? "0" : zero_of(L.dtype)) << ";\n";
         s << "      }\n    }\n";
     };
     // hoisted loads
@@ -683,7 +690,7 @@ std::string Gen::gen_row() {
             if (full && hoistable(L)) {
                 hoisted[l] = 1;
                 std::ostringstream s;
-                emit_full_load(s, (int)l, "true", kidx, fmt("h%zu", l));
+                emit_full_load(s, (int)l, "true", kidx, fmt("h%zu", l), true);
                 b << s.str();
             }
         }
@@ -708,6 +715,14 @@ std::string Gen::gen_row() {
         }
     }
     int red_slot = 0;
+    // value of ex i at in-thread position q (a scalar for row-constant values)
+    auto fullv = [&](int i, const std::string& q) -> std::string {
+        if (i < 0) return "";
+        const Ex& x = k.ex[i];
+        if (x.op == RV_BUFFER && !k.leaves[x.leaf].zero && hoisted[x.leaf])
+            return ld(x.dtype, fmt("h%d[%s]", x.leaf, q.c_str()));
+        return stat[i] ? fmt("e%d", i) : fmt("e%d[%s]", i, q.c_str());
+    };
     for (size_t e = 0; e < k.ex.size(); ++e) {
         if (!live[e]) continue;
         const Ex& x = k.ex[e];
@@ -719,10 +734,7 @@ std::string Gen::gen_row() {
                 stat[e] = 1;
                 continue;
             }
-            if (hoisted[x.leaf]) {
-                b << "    " << vt(x.dtype) << "* " << V << " = h" << x.leaf << ";\n";
-                continue;
-            }
+            if (hoisted[x.leaf]) continue;  // read as h<leaf>[q] where used
             std::string kc = mask_cond(L.v, kidx, kd);
             std::string rowok = "rv" + (kc.empty() ? std::string() : " && " + kc);
             if (stat[e]) {
@@ -731,7 +743,7 @@ std::string Gen::gen_row() {
                   << ld(L.dtype, P + "[" + addr(L.v, kidx) + "]") << " : " << zero_of(x.dtype) << ";\n";
             } else {
                 std::ostringstream s;
-                emit_full_load(s, x.leaf, rowok, kidx, V);
+                emit_full_load(s, x.leaf, rowok, kidx, V, false);
                 b << s.str();
             }
             continue;
@@ -740,10 +752,7 @@ std::string Gen::gen_row() {
             b << "    const " << vt(x.dtype) << " " << V << " = " << const_lit(x.dtype, x.cval) << ";\n";
             continue;
         }
-        auto opnd = [&](int i, const std::string& q) -> std::string {
-            if (i < 0) return "";
-            return stat[i] ? fmt("e%d", i) : fmt("e%d[%s]", i, q.c_str());
-        };
+        auto opnd = [&](int i, const std::string& q) -> std::string { return fullv(i, q); };
         if (x.op == RV_SUM || x.op == RV_MAX) {
             const bool sum = x.op == RV_SUM;
             b << "    float " << V << ";\n    {\n";
@@ -785,11 +794,11 @@ std::string Gen::gen_row() {
         for (int d : rd)
             if (s.v.strides[d] != 0) sstat = false;
         if (sstat) {
-            std::string val = stat[s.ex] ? fmt("e%d", s.ex) : fmt("e%d[0]", s.ex);
+            std::string val = fullv(s.ex, "0");
             b << "    if (lt == 0 && rv) " << P << "[" << addr(s.v, kidx) << "] = " << sv(s.dtype, val) << ";\n";
             continue;
         }
-        std::string val = stat[s.ex] ? fmt("e%d", s.ex) : fmt("e%d[v * %d + i]", s.ex, VW);
+        std::string val = fullv(s.ex, fmt("v * %d + i", VW));
         b << "    for (int v = 0; v < " << NV << "; ++v) {\n";
         b << "      const " << I << " n0 = " << nexpr("v", "0") << ";\n";
         std::vector<std::string> idx = kidx;

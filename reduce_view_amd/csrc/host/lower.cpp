@@ -207,16 +207,23 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
         k.lane_dim = X;
         if (tiled) {
             k.plan = "tiled2d";
+            // waves stacked WY (along Y) x WX (along X); 8 x 8 lanes of 4 x 4 cells each
+            int WY = env_int("RV_EW_WAVES_Y", 2);
+            if (WY != 1 && WY != 2 && WY != 4) fail(RV_E_INVALID, "RV_EW_WAVES_Y must be 1, 2 or 4");
+            int WX = 4 / WY;
+            int order = env_int("RV_EW_ORDER", 0);
             int64_t B = numel(k.domain) / (k.domain[X] * k.domain[Y]);
-            k.grid[0] = (unsigned)((k.domain[X] + 63) / 64);
-            k.grid[1] = (unsigned)((k.domain[Y] + 63) / 64);
+            int64_t gx = (k.domain[X] + 32 * WX - 1) / (32 * WX), gy = (k.domain[Y] + 32 * WY - 1) / (32 * WY);
+            k.grid[0] = (unsigned)(gx * gy);
+            k.grid[1] = 1;
             k.grid[2] = (unsigned)B;
             k.block[0] = 256;
             int nt = 0;
             for (auto& L : k.leaves)
                 if (!L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) ++nt;
-            k.lds = (size_t)nt * 64 * 65 * 8;
-            snprintf(buf, sizeof buf, "\"tile\":[64,64],\"lds_pad\":1,\"staged_leaves\":%d", nt);
+            k.lds = 0;
+            snprintf(buf, sizeof buf, "\"tile\":[%d,%d],\"waves\":[%d,%d],\"order\":%d,\"lane_block\":[4,4],"
+                     "\"register_transposed_leaves\":%d", 32 * WY, 32 * WX, WY, WX, order, nt);
         } else {
             k.plan = "rowmajor";
             int maxsz = 1;

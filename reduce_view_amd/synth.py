@@ -336,3 +336,11 @@ FULL = {
     "layernorm": dict(rows=8192, n=8192),
     "gemm": dict(m=4096, n=4096, k=4096),
 }
+
+
+def copy(rows: int, cols: int) -> Spec:
+    """out = CONTIGUOUS(x): a plain copy, the bandwidth reference."""
+    g = Spec(f"copy_{rows}x{cols}")
+    x = g.buffer("X", (rows, cols), "f32")
+    g.output(g.contiguous(x))
+    return g
