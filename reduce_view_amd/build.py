@@ -47,11 +47,16 @@ def check_device_header(verbose: bool = False) -> None:
         f.write('#include <hip/hip_runtime.h>\n#include "%s"\n' % os.path.join(CSRC, "kernels", "rv_device.hpp"))
         f.write("struct E { __device__ float operator()(float a, int, int) const { return a; }\n"
                 "  __device__ void store(int, int, float) const {} };\n"
-                "extern \"C\" __global__ void __launch_bounds__(256) chk(const unsigned short* a, "
-                "const unsigned short* b, float* p) {\n"
-                "  rv_gemm_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p);\n"
-                "  rv_gemm_bf16<false, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p);\n"
-                "  p[0] += rv_fold_sum(p, 16); }\n")
+                "#define K extern \"C\" __global__ void __launch_bounds__(256)\n"
+                "K chk1(const unsigned short* a, const unsigned short* b, float* p) {\n"
+                "  rv_gemm_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "K chk2(const unsigned short* a, const unsigned short* b, float* p) {\n"
+                "  rv_gemm_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "K chk3(const unsigned short* a, const unsigned short* b, float* p) {\n"
+                "  rv_gemm256_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "K chk4(const unsigned short* a, const unsigned short* b, float* p) {\n"
+                "  rv_gemm256_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "K chk5(float* p) { p[0] = rv_fold_sum(p, 16); }\n")
     cmd = [HIPCC] + GPU_FLAGS + ["--cuda-device-only", "-c", tu, "-o", os.path.join(out_dir, "device_check.o")]
     if verbose:
         print(" ".join(cmd))

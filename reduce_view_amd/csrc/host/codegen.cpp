@@ -184,6 +184,8 @@ struct Gen {
             if (!L.zero) upd(L.v);
         for (auto& s : k.stores) upd(s.v);
         I = mx < (int64_t(1) << 30) ? "int" : "long long";
+        const char* nt = getenv("RV_NT");
+        nt_on = !(nt && std::string(nt) == "0");
     }
 
     int param_of(const Loc& L, int dtype, bool write) {
@@ -236,8 +238,28 @@ struct Gen {
     }
 
     std::string header() {
-        return "extern \"C\" __global__ void __launch_bounds__(256) " + k.name + "(" + signature() + ")";
+        return "extern \"C\" __global__ void __launch_bounds__(" + std::to_string(k.block[0]) + ") " + k.name + "(" +
+               signature() + ")";
     }
+
+    // a load is streaming (nontemporal) when no domain dim of size > 1 has
+    // stride 0, i.e. every cell is read once; stores always stream
+    bool streaming(const Leaf& L) const {
+        if (!nt_on) return false;
+        for (int d = 0; d < rank; ++d)
+            if (k.domain[d] > 1 && L.v.strides[d] == 0) return false;
+        return true;
+    }
+    std::string vload(const Leaf& L, int n, const std::string& ptr) const {
+        bool nt = streaming(L) && dtype_size(L.dtype) * n >= 4;
+        return std::string(nt ? "rv_ldv_nt<" : "rv_ldv<") + st(L.dtype) + ", " + std::to_string(n) + ">(" + ptr + ")";
+    }
+    std::string vstore(int dtype, int n, const std::string& ptr, const std::string& val) const {
+        bool nt = nt_on && dtype_size(dtype) * n >= 4;
+        return std::string(nt ? "rv_stv_nt<" : "rv_stv<") + st(dtype) + ", " + std::to_string(n) + ">(" + ptr + ", " + val +
+               ")";
+    }
+    bool nt_on = true;
 
     bool leaf_vec_ok(const Leaf& L, int along, int vw) {
         if (vw <= 1 || L.v.strides[along] != 1) return false;
@@ -331,8 +353,8 @@ std::string Gen::gen_rowmajor() {
             b << "    {\n";
             if (vec) {
                 b << "      if (" << rowok << xm << fullc << ") {\n";
-                b << "        const rv_pack<" << st(L.dtype) << ", " << VW << "> v = rv_ldv<" << st(L.dtype) << ", " << VW
-                  << ">(" << P << " + " << base << " + " << xs << ");\n";
+                b << "        const rv_pack<" << st(L.dtype) << ", " << VW << "> v = "
+                  << vload(L, VW, P + " + " + base + " + " + xs) << ";\n";
                 b << "        for (int q = 0; q < " << VW << "; ++q) " << V << "[q] = " << ld(L.dtype, "v.v[q]") << ";\n";
                 b << "      } else\n";
             }
@@ -385,7 +407,7 @@ std::string Gen::gen_rowmajor() {
             if (vec) {
                 b << "      if (" << cv << fullc << ") {\n        rv_pack<" << st(s.dtype) << ", " << VW << "> v;\n";
                 b << "        for (int q = 0; q < " << VW << "; ++q) v.v[q] = " << sv(s.dtype, V + "[q]") << ";\n";
-                b << "        rv_stv<" << st(s.dtype) << ", " << VW << ">(" << P << " + " << base << " + " << xs << ", v);\n";
+                b << "        " << vstore(s.dtype, VW, P + " + " + base + " + " + xs, "v") << ";\n";
                 b << "      } else\n";
             }
             b << "      for (int q = 0; q < " << VW << "; ++q) {\n";
@@ -499,24 +521,24 @@ std::string Gen::gen_tiled() {
             const bool xbcast = L.v.strides[X] == 0 && !masked(L.v, X);
             if (along_x) {
                 if (ybcast) {
-                    b << "    { const rv_pack<" << T << ", 4> v = rv_ldv<" << T << ", 4>(" << P << " + "
-                      << addr(L.v, idx_at("y", "x")) << ");\n";
+                    b << "    { const rv_pack<" << T << ", 4> v = " << vload(L, 4, P + " + " + addr(L.v, idx_at("y", "x")))
+                      << ";\n";
                     b << "      for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) " << V << "[r][c] = "
                       << ld(L.dtype, "v.v[c]") << "; }\n";
                 } else {
-                    b << "    for (int r = 0; r < 4; ++r) { const rv_pack<" << T << ", 4> v = rv_ldv<" << T << ", 4>("
-                      << P << " + " << addr(L.v, idx_at("y + r", "x")) << ");\n";
+                    b << "    for (int r = 0; r < 4; ++r) { const rv_pack<" << T << ", 4> v = "
+                      << vload(L, 4, P + " + " + addr(L.v, idx_at("y + r", "x"))) << ";\n";
                     b << "      for (int c = 0; c < 4; ++c) " << V << "[r][c] = " << ld(L.dtype, "v.v[c]") << "; }\n";
                 }
             } else if (along_y) {
                 if (xbcast) {
-                    b << "    { const rv_pack<" << T << ", 4> v = rv_ldv<" << T << ", 4>(" << P << " + "
-                      << addr(L.v, idx_at("y", "x")) << ");\n";
+                    b << "    { const rv_pack<" << T << ", 4> v = " << vload(L, 4, P + " + " + addr(L.v, idx_at("y", "x")))
+                      << ";\n";
                     b << "      for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) " << V << "[r][c] = "
                       << ld(L.dtype, "v.v[r]") << "; }\n";
                 } else {
-                    b << "    for (int c = 0; c < 4; ++c) { const rv_pack<" << T << ", 4> v = rv_ldv<" << T << ", 4>("
-                      << P << " + " << addr(L.v, idx_at("y", "x + c")) << ");\n";
+                    b << "    for (int c = 0; c < 4; ++c) { const rv_pack<" << T << ", 4> v = "
+                      << vload(L, 4, P + " + " + addr(L.v, idx_at("y", "x + c"))) << ";\n";
                     b << "      for (int r = 0; r < 4; ++r) " << V << "[r][c] = " << ld(L.dtype, "v.v[r]") << "; }\n";
                 }
             } else {
@@ -558,7 +580,7 @@ std::string Gen::gen_tiled() {
             if (vec) {
                 b << "    for (int r = 0; r < 4; ++r) { rv_pack<" << st(s.dtype) << ", 4> v;\n";
                 b << "      for (int c = 0; c < 4; ++c) v.v[c] = " << sv(s.dtype, fmt("e%d[r][c]", s.ex)) << ";\n";
-                b << "      rv_stv<" << st(s.dtype) << ", 4>(" << P << " + " << addr(s.v, idx_at("y + r", "x")) << ", v); }\n";
+                b << "      " << vstore(s.dtype, 4, P + " + " + addr(s.v, idx_at("y + r", "x")), "v") << "; }\n";
             } else {
                 b << "    for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) {\n";
                 b << "      const " << I << " yy = y + r, xx = x + c;\n";
@@ -587,7 +609,7 @@ std::string Gen::gen_row() {
     // plan values (mirrors lower.cpp)
     int T = 0, VW = 0;
     sscanf(k.plan_json.c_str(), "\"threads_per_row\":%d,\"rows_per_block\":%*d,\"vec\":%d", &T, &VW);
-    const int RPW = 256 / T;
+    const int RPW = (int)k.block[0] / T;
     const int NV = (int)((NR + (int64_t)T * VW - 1) / ((int64_t)T * VW));
     const int E = NV * VW;
     const bool ragged = NR % ((int64_t)T * VW) != 0;
@@ -664,8 +686,10 @@ std::string Gen::gen_row() {
                                             : "";
             std::string rg = ragged ? fmt(" && n0 + %d <= %s", VW, lit(NR).c_str()) : "";
             s << "      if (" << rowok << mc << rg << ") {\n";
-            s << "        const rv_pack<" << st(L.dtype) << ", " << VW << "> p = rv_ldv<" << st(L.dtype) << ", " << VW
-              << ">(" << P << " + " << addr(L.v, idx) << ");\n";
+            s << "        const rv_pack<" << st(L.dtype) << ", " << VW << "> p = "
+              << (raw ? "rv_ldv<" + st(L.dtype) + ", " + std::to_string(VW) + ">(" + P + " + " + addr(L.v, idx) + ")"
+                      : vload(L, VW, P + " + " + addr(L.v, idx)))
+              << ";\n";
             s << "        for (int i = 0; i < " << VW << "; ++i) " << V << "[v * " << VW << " + i] = " << ld(L.dtype, "p.v[i]")
               << ";\n      } else\n";
         }
@@ -810,7 +834,7 @@ std::string Gen::gen_row() {
             std::string rg = ragged ? fmt(" && n0 + %d <= %s", VW, lit(NR).c_str()) : "";
             b << "      if (rv" << rg << ") {\n        rv_pack<" << st(s.dtype) << ", " << VW << "> p;\n";
             b << "        for (int i = 0; i < " << VW << "; ++i) p.v[i] = " << sv(s.dtype, val) << ";\n";
-            b << "        rv_stv<" << st(s.dtype) << ", " << VW << ">(" << P << " + " << addr(s.v, idx) << ", p);\n";
+            b << "        " << vstore(s.dtype, VW, P + " + " + addr(s.v, idx), "p") << ";\n";
             b << "      } else\n";
         }
         b << "      for (int i = 0; i < " << VW << "; ++i) {\n        const " << I << " n = n0 + i;\n";
@@ -1015,7 +1039,7 @@ std::string Gen::gen_gemm() {
     const int64_t M = k.domain[0], N = k.domain[1], K = k.domain[2];
     const int64_t lda = A.v.strides[0];
     const int64_t ldb = kn ? B.v.strides[2] : B.v.strides[1];
-    b << "  rv_gemm_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ">(" << pa << ", " << pb
+    b << "  " << (k.plan == "gemm256" ? "rv_gemm256_bf16<" : "rv_gemm_bf16<") << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ">(" << pa << ", " << pb
       << ", " << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", "
       << K << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ");\n";
     return f.str() + "@@BODY@@" + b.str();

@@ -10,6 +10,7 @@
 // (stride[d] == size[d+1] * stride[d+1], both unmasked) are merged first, so
 // e.g. a (4096, 4096) row-major chain runs as one flat loop.
 #include <algorithm>
+#include <cctype>
 #include <cstdlib>
 
 #include "graph.hpp"
@@ -168,20 +169,22 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             return;
         }
         case KClass::MFMA: {
-            k.plan = "gemm";
-            const int BM = 128, BN = 128;
             int64_t M = k.domain[0], N = k.domain[1];
+            const bool big = M % 256 == 0 && N % 256 == 0 && env_int("RV_GEMM_TILE", 256) == 256;
+            k.plan = big ? "gemm256" : "gemm";
+            const int BM = big ? 256 : 128, BN = big ? 256 : 128;
             k.grid[0] = (unsigned)((M / BM) * (N / BN));
             k.block[0] = 256;
-            k.lds = 2 * (128 * 72 + 128 * 72) * 2;
+            k.lds = 2 * (BM * 72 + BN * 72) * 2 + 16;
             k.n_partials = k.grid[0];
             bool kn = k.leaves[k.mfma_b].v.strides[1] == 1;
-            // per lane: 64 values summed in order, 6 butterfly levels, 3
-            // cross-wave additions; the fold adds its own depth
+            // per lane: (BM * BN / 256) values summed in order, 6 butterfly
+            // levels, 3 cross-wave additions; the fold adds its own depth
+            const int per_lane = BM * BN / 256;
             snprintf(buf, sizeof buf,
-                     "\"tile\":[128,128,64],\"waves\":[2,2],\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
+                     "\"tile\":[%d,%d,64],\"waves\":[2,2],\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
                      "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d",
-                     kn ? "kn" : "nk", 63 + 6 + 3);
+                     BM, BN, kn ? "kn" : "nk", per_lane - 1 + 6 + 3);
             k.plan_json = buf;
             if (k.mfma_partial) {
                 p.regions[k.partials_region].bytes = (size_t)k.n_partials * 4;
@@ -208,10 +211,10 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
         if (tiled) {
             k.plan = "tiled2d";
             // waves stacked WY (along Y) x WX (along X); 8 x 8 lanes of 4 x 4 cells each
-            int WY = env_int("RV_EW_WAVES_Y", 2);
+            int WY = env_int("RV_EW_WAVES_Y", 1);
             if (WY != 1 && WY != 2 && WY != 4) fail(RV_E_INVALID, "RV_EW_WAVES_Y must be 1, 2 or 4");
             int WX = 4 / WY;
-            int order = env_int("RV_EW_ORDER", 0);
+            int order = env_int("RV_EW_ORDER", 3);
             int64_t B = numel(k.domain) / (k.domain[X] * k.domain[Y]);
             int64_t gx = (k.domain[X] + 32 * WX - 1) / (32 * WX), gy = (k.domain[Y] + 32 * WY - 1) / (32 * WY);
             k.grid[0] = (unsigned)(gx * gy);
@@ -260,14 +263,18 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
                 if (along) two = false;
             }
         int vw = two ? 8 : 4;
-        int T = 256;
-        while (T > 16 && (int64_t)T * vw * 2 > NR) T /= 2;
+        // about 16 cells per lane: enough bytes in flight per lane, few
+        // enough VGPRs for high occupancy
+        int T = 1024;
+        while (T > 16 && (int64_t)T * 16 > NR) T /= 2;
         T = env_int("RV_ROW_THREADS", T);
-        if (T < 1 || T > 256 || (256 % T)) fail(RV_E_INVALID, "RV_ROW_THREADS must divide 256");
-        int rpw = 256 / T;
+        if (T < 1 || T > 1024 || (T & (T - 1))) fail(RV_E_INVALID, "RV_ROW_THREADS must be a power of two <= 1024");
+        const int block = std::max(256, T);
+        int rpw = block / T;
         int64_t nrg = (NK + rpw - 1) / rpw;
-        k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>(nrg, env_int("RV_ROW_GRID", 2048)));
-        k.block[0] = 256;
+        // one workgroup per row group (a persistent grid measured slower)
+        k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>(nrg, env_int("RV_ROW_GRID", 1 << 30)));
+        k.block[0] = (unsigned)block;
         k.lane_dim = rank - 1;
         int nv = (int)((NR + (int64_t)T * vw - 1) / ((int64_t)T * vw));
         int nred = 0;
@@ -330,6 +337,24 @@ void lower(Program& p) {
         off += (r.bytes + 255) / 256 * 256;
     }
     p.ws_bytes = off;
+    // kernel names say what they are (class, plan, a hash of the lowered
+    // kernel) so profiles of different programs can be told apart
+    for (size_t i = 0; i < p.kernels.size(); ++i) {
+        Kernel& k = p.kernels[i];
+        std::string sig = std::string(kclass_name(k.cls)) + k.plan + k.plan_json;
+        for (int64_t d : k.domain) sig += "," + std::to_string(d);
+        for (auto& L : k.leaves) sig += json_view(L.v) + dtype_name(L.dtype);
+        for (auto& st : k.stores) sig += json_view(st.v) + dtype_name(st.dtype);
+        for (auto& e : k.ex) sig += fmt("|%d,%d,%d,%d,%d,%d,%.17g", e.op, e.dtype, e.a, e.b, e.c, e.leaf, e.cval);
+        uint64_t h = 1469598103934665603ull;
+        for (unsigned char ch : sig) {
+            h ^= ch;
+            h *= 1099511628211ull;
+        }
+        std::string cls = kclass_name(k.cls);
+        for (auto& ch : cls) ch = (char)tolower(ch);
+        k.name = fmt("rv_%s_%s_%08x_%zu", cls.c_str(), k.plan.c_str(), (unsigned)(h & 0xffffffffu), i);
+    }
     for (auto& k : p.kernels) prove_in_bounds(p, k);
 }
 

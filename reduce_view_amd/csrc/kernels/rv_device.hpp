@@ -11,13 +11,9 @@
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float rv_bf2f(unsigned short b) { return __uint_as_float(((unsigned)b) << 16); }
 
-// float32 -> bfloat16, round to nearest even; NaN stays NaN (quiet bit).
-__device__ __forceinline__ unsigned short rv_f2bf(float f) {
-    unsigned u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (unsigned short)(u >> 16);
-}
+// float32 -> bfloat16, round to nearest even; NaN stays a (quiet) NaN.
+// gfx950 converts in one instruction (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned short rv_f2bf(float f) { return __builtin_bit_cast(unsigned short, (__bf16)f); }
 
 __device__ __forceinline__ float rv_rbf(float x) { return rv_bf2f(rv_f2bf(x)); }
 __device__ __forceinline__ float rv_rhf(float x) { return (float)(_Float16)x; }
@@ -47,6 +43,40 @@ __device__ __forceinline__ rv_pack<T, N> rv_ldv(const T* p) {
 template <class T, int N>
 __device__ __forceinline__ void rv_stv(T* p, const rv_pack<T, N>& x) {
     *reinterpret_cast<rv_pack<T, N>*>(p) = x;
+}
+
+// Streaming variants: the nontemporal hint for data touched exactly once, so
+// it does not evict reused lines (weights, broadcast rows) from the caches.
+template <int B>
+struct rv_words;
+template <>
+struct rv_words<4> {
+    typedef unsigned type;
+};
+template <>
+struct rv_words<8> {
+    typedef __attribute__((ext_vector_type(2))) unsigned type;
+};
+template <>
+struct rv_words<16> {
+    typedef __attribute__((ext_vector_type(4))) unsigned type;
+};
+
+template <class T, int N>
+__device__ __forceinline__ rv_pack<T, N> rv_ldv_nt(const T* p) {
+    typedef typename rv_words<sizeof(T) * N>::type W;
+    const W w = __builtin_nontemporal_load(reinterpret_cast<const W*>(p));
+    rv_pack<T, N> r;
+    __builtin_memcpy(&r, &w, sizeof r);
+    return r;
+}
+
+template <class T, int N>
+__device__ __forceinline__ void rv_stv_nt(T* p, const rv_pack<T, N>& x) {
+    typedef typename rv_words<sizeof(T) * N>::type W;
+    W w;
+    __builtin_memcpy(&w, &x, sizeof w);
+    __builtin_nontemporal_store(w, reinterpret_cast<W*>(p));
 }
 
 // ---------------------------------------------------------------------------
@@ -240,6 +270,192 @@ __device__ __forceinline__ void rv_gemm_bf16(const unsigned short* __restrict__ 
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+                const float v = epi(acc[i][j][r], m, n);
+                if (MODE == 0)
+                    epi.store(m, n, v);
+                else
+                    part = part + v;
+            }
+    if (MODE == 1) {
+        part = rv_group_sum<64>(part);
+        if (lane == 0) lds_red[wave] = part;
+        __syncthreads();
+        if (tid == 0) partials[blockIdx.x] = ((lds_red[0] + lds_red[1]) + lds_red[2]) + lds_red[3];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The large-tile contraction: 256 x 256 x 64 per workgroup of 4 waves (one per
+// SIMD), each wave a 128 x 128 patch as 4 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16 (256 float32 accumulators per lane). Per k16 step a
+// wave reads 8 operand fragments from LDS for 16 MFMAs, half the LDS traffic
+// per MFMA of the 128 x 128 tile. The next k-tile's global loads are issued
+// before the current tile's MFMAs and written to the other LDS stage halfway
+// through them. A 4096^3 problem is 256 workgroups: one per CU; each XCD gets
+// a 4 x 8 block of tiles so its L2 holds the A rows and B columns it shares.
+// ---------------------------------------------------------------------------
+#define RV_G2_BM 256
+#define RV_G2_BN 256
+#define RV_G2_BK 64
+#define RV_G2_LDK 72
+
+template <bool B_KN>
+struct rv_g2_regs {
+    rv_u32x4 a[8];
+    rv_u32x4 b[8];
+};
+
+template <bool B_KN>
+__device__ __forceinline__ void rv_g2_load(rv_g2_regs<B_KN>& s, const unsigned short* __restrict__ A,
+                                           const unsigned short* __restrict__ B, long long a_base, long long lda,
+                                           long long b_base, long long ldb, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int v = tid + 256 * i;
+        int row = v >> 3, kc = (v & 7) * 8;
+        s.a[i] = *reinterpret_cast<const rv_u32x4*>(A + a_base + (long long)row * lda + k0 + kc);
+    }
+    if (B_KN) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            int unit = tid + 256 * u;
+            int nc = (unit & 31) * 8, kg = (unit >> 5) * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                s.b[u * 4 + j] = *reinterpret_cast<const rv_u32x4*>(B + b_base + (long long)(k0 + kg + j) * ldb + nc);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int v = tid + 256 * i;
+            int row = v >> 3, kc = (v & 7) * 8;
+            s.b[i] = *reinterpret_cast<const rv_u32x4*>(B + b_base + (long long)row * ldb + k0 + kc);
+        }
+    }
+}
+
+// Writes half `h` (0 or 1) of the prefetched registers into an LDS stage.
+template <bool B_KN>
+__device__ __forceinline__ void rv_g2_store(const rv_g2_regs<B_KN>& s, unsigned short* As, unsigned short* Bs, int tid,
+                                            int h) {
+#pragma unroll
+    for (int i = 4 * h; i < 4 * h + 4; ++i) {
+        int v = tid + 256 * i;
+        int row = v >> 3, kc = (v & 7) * 8;
+        *reinterpret_cast<rv_u32x4*>(As + row * RV_G2_LDK + kc) = s.a[i];
+    }
+    if (B_KN) {
+        const int u = h;
+        int unit = tid + 256 * u;
+        int nc = (unit & 31) * 8, kg = (unit >> 5) * 4;
+        typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int w = e >> 1;
+            unsigned x0 = s.b[u * 4 + 0][w], x1 = s.b[u * 4 + 1][w], x2 = s.b[u * 4 + 2][w], x3 = s.b[u * 4 + 3][w];
+            u32x2 pk;
+            if (e & 1) {
+                pk[0] = (x0 >> 16) | (x1 & 0xffff0000u);
+                pk[1] = (x2 >> 16) | (x3 & 0xffff0000u);
+            } else {
+                pk[0] = (x0 & 0xffffu) | (x1 << 16);
+                pk[1] = (x2 & 0xffffu) | (x3 << 16);
+            }
+            *reinterpret_cast<u32x2*>(Bs + (nc + e) * RV_G2_LDK + kg) = pk;
+        }
+    } else {
+#pragma unroll
+        for (int i = 4 * h; i < 4 * h + 4; ++i) {
+            int v = tid + 256 * i;
+            int row = v >> 3, kc = (v & 7) * 8;
+            *reinterpret_cast<rv_u32x4*>(Bs + row * RV_G2_LDK + kc) = s.b[i];
+        }
+    }
+}
+
+template <class Acc>
+__device__ __forceinline__ void rv_g2_mma(Acc& acc, const unsigned short* As, const unsigned short* Bs, int wm, int wn,
+                                          int lane, int kk) {
+    rv_bf16x8 af[4], bf[4];
+    const int kq = kk + (lane >> 5) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const rv_bf16x8*>(As + (wm * 128 + i * 32 + (lane & 31)) * RV_G2_LDK + kq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        bf[j] = *reinterpret_cast<const rv_bf16x8*>(Bs + (wn * 128 + j * 32 + (lane & 31)) * RV_G2_LDK + kq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+}
+
+template <bool B_KN, int MODE, class Epi>
+__device__ __forceinline__ void rv_gemm256_bf16(const unsigned short* __restrict__ A,
+                                                const unsigned short* __restrict__ B, long long a_off, long long lda,
+                                                long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
+                                                float* __restrict__ partials) {
+    __shared__ __attribute__((aligned(16))) unsigned short lds_a[2][RV_G2_BM * RV_G2_LDK];
+    __shared__ __attribute__((aligned(16))) unsigned short lds_b[2][RV_G2_BN * RV_G2_LDK];
+    __shared__ float lds_red[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = M / RV_G2_BM, tiles_n = N / RV_G2_BN;
+    const int ntiles = tiles_m * tiles_n;
+    int tm, tn;
+    {
+        int bid = blockIdx.x;
+        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
+            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
+            const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
+            tm = group * 4 + (within & 3);
+            tn = within >> 2;
+        } else {
+            tm = bid / tiles_n;
+            tn = bid % tiles_n;
+        }
+    }
+    const int m0 = tm * RV_G2_BM, n0 = tn * RV_G2_BN;
+    const long long a_base = a_off + (long long)m0 * lda;
+    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
+
+    rv_f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    rv_g2_regs<B_KN> st;
+    rv_g2_load<B_KN>(st, A, B, a_base, lda, b_base, ldb, 0, tid);
+    rv_g2_store<B_KN>(st, lds_a[0], lds_b[0], tid, 0);
+    rv_g2_store<B_KN>(st, lds_a[0], lds_b[0], tid, 1);
+    __syncthreads();
+    const int KT = K / RV_G2_BK;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < KT;
+        if (more) rv_g2_load<B_KN>(st, A, B, a_base, lda, b_base, ldb, (kt + 1) * RV_G2_BK, tid);
+        rv_g2_mma(acc, lds_a[cur], lds_b[cur], wm, wn, lane, 0);
+        rv_g2_mma(acc, lds_a[cur], lds_b[cur], wm, wn, lane, 16);
+        if (more) rv_g2_store<B_KN>(st, lds_a[cur ^ 1], lds_b[cur ^ 1], tid, 0);
+        rv_g2_mma(acc, lds_a[cur], lds_b[cur], wm, wn, lane, 32);
+        rv_g2_mma(acc, lds_a[cur], lds_b[cur], wm, wn, lane, 48);
+        if (more) rv_g2_store<B_KN>(st, lds_a[cur ^ 1], lds_b[cur ^ 1], tid, 1);
+        __syncthreads();
+    }
+
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int n = n0 + wn * 128 + j * 32 + (lane & 31);
                 const float v = epi(acc[i][j][r], m, n);
                 if (MODE == 0)
                     epi.store(m, n, v);

@@ -150,5 +150,5 @@ def test_program_io_and_describe():
     assert prog.out_desc == [((32, 512), "f32")]
     d = prog.describe()
     assert [k["class"] for k in d["kernels"]] == ["ROW"]
-    assert "rv_k0" in prog.source()
+    assert d["kernels"][0]["name"].startswith("rv_row_row_") and d["kernels"][0]["name"] in prog.source()
     assert rv.rv_last_error() == ""

@@ -140,7 +140,7 @@ def test_layernorm(rows, n):
 
 # ---- config 5: bf16 contraction on MFMA + relu^2 + full SUM ----------------------
 
-@pytest.mark.parametrize("m,n,k", [(128, 128, 64), (256, 384, 192)])
+@pytest.mark.parametrize("m,n,k", [(128, 128, 64), (256, 384, 192), (256, 512, 128)])
 def test_gemm_integer_valued_bit_exact(m, n, k):
     _case(f"gemm int {m}x{n}x{k}")
     inp = synth.inputs_gemm_integer(m, n, k)
@@ -161,7 +161,7 @@ def test_gemm_integer_valued_bit_exact(m, n, k):
     assert got.tobytes() == ref.tobytes()
 
 
-@pytest.mark.parametrize("m,n,k", [(256, 256, 256), (512, 384, 640)])
+@pytest.mark.parametrize("m,n,k", [(256, 256, 256), (512, 384, 640), (512, 768, 320)])
 def test_gemm_relu2_sum(m, n, k):
     _case(f"gemm relu2 sum {m}x{n}x{k}")
     inp = synth.inputs_gemm(m, n, k)
