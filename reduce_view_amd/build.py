@@ -56,7 +56,13 @@ def check_device_header(verbose: bool = False) -> None:
                 "  rv_gemm256_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
                 "K chk4(const unsigned short* a, const unsigned short* b, float* p) {\n"
                 "  rv_gemm256_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
-                "K chk5(float* p) { p[0] = rv_fold_sum(p, 16); }\n")
+                "K chk5(float* p) { p[0] = rv_fold_sum(p, 16); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(512) chk6(const unsigned short* a, "
+                "const unsigned short* b, float* p) {\n"
+                "  rv_gemm_lds_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(512) chk7(const unsigned short* a, "
+                "const unsigned short* b, float* p) {\n"
+                "  rv_gemm_lds_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n")
     cmd = [HIPCC] + GPU_FLAGS + ["--cuda-device-only", "-c", tu, "-o", os.path.join(out_dir, "device_check.o")]
     if verbose:
         print(" ".join(cmd))

@@ -170,21 +170,39 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
         }
         case KClass::MFMA: {
             int64_t M = k.domain[0], N = k.domain[1];
-            const bool big = M % 256 == 0 && N % 256 == 0 && env_int("RV_GEMM_TILE", 256) == 256;
-            k.plan = big ? "gemm256" : "gemm";
-            const int BM = big ? 256 : 128, BN = big ? 256 : 128;
+            // 256 x 256 tiles when the shape allows: direct-to-LDS copies and
+            // 8 waves ("lds", the default) or register-staged copies and 4
+            // waves ("reg"); otherwise 128 x 128 register-staged tiles
+            const bool big = M % 256 == 0 && N % 256 == 0;
+            const char* kind = getenv("RV_GEMM_KERNEL");
+            std::string kd = kind && *kind ? kind : "lds";
+            if (!big) kd = "reg128";
+            int BM = 128, BN = 128, waves = 4;
+            if (kd == "lds") {
+                k.plan = "gemm_lds";
+                BM = BN = 256;
+                waves = 8;
+                k.lds = 4 * 256 * 64 * 2 + 32;
+            } else if (kd == "reg") {
+                k.plan = "gemm256";
+                BM = BN = 256;
+                k.lds = 2 * (BM * 72 + BN * 72) * 2 + 16;
+            } else {
+                k.plan = "gemm";
+                k.lds = 2 * (BM * 72 + BN * 72) * 2 + 16;
+            }
             k.grid[0] = (unsigned)((M / BM) * (N / BN));
-            k.block[0] = 256;
-            k.lds = 2 * (BM * 72 + BN * 72) * 2 + 16;
+            k.block[0] = 64 * waves;
             k.n_partials = k.grid[0];
             bool kn = k.leaves[k.mfma_b].v.strides[1] == 1;
-            // per lane: (BM * BN / 256) values summed in order, 6 butterfly
-            // levels, 3 cross-wave additions; the fold adds its own depth
-            const int per_lane = BM * BN / 256;
+            // per lane: (BM * BN / threads) values summed in order, 6
+            // butterfly levels, (waves - 1) cross-wave additions; the fold
+            // adds its own depth
+            const int per_lane = BM * BN / (64 * waves);
             snprintf(buf, sizeof buf,
-                     "\"tile\":[%d,%d,64],\"waves\":[2,2],\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
+                     "\"tile\":[%d,%d,64],\"waves\":%d,\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
                      "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d",
-                     BM, BN, kn ? "kn" : "nk", per_lane - 1 + 6 + 3);
+                     BM, BN, waves, kn ? "kn" : "nk", per_lane - 1 + 6 + waves - 1);
             k.plan_json = buf;
             if (k.mfma_partial) {
                 p.regions[k.partials_region].bytes = (size_t)k.n_partials * 4;

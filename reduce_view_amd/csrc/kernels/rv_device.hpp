@@ -470,6 +470,198 @@ __device__ __forceinline__ void rv_gemm256_bf16(const unsigned short* __restrict
     }
 }
 
+// ---------------------------------------------------------------------------
+// The direct-to-LDS contraction: 256 x 256 x 64 per workgroup of 8 waves (2
+// per SIMD: one issues MFMAs while the other waits on LDS), each wave a
+// 64 x 128 patch as 2 x 4 tiles of v_mfma_f32_32x32x16_bf16 (128 float32
+// accumulators per lane). Operands go global -> LDS with
+// global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS base +
+// 16 * lane), so no VGPRs stage them and no VALU work rearranges them:
+//   - A (and a [n][k] B) keep [row][k] rows of 128 bytes in LDS with the 16-byte
+//     chunks XOR-swizzled by (row ^ row >> 3) & 7, so 16 consecutive rows
+//     read at one k-chunk hit distinct banks; a fragment is one ds_read_b128.
+//   - a [k][n] B keeps its [k][n] rows of 512 bytes with chunks XOR-swizzled by
+//     4 * (k & 3); a fragment (8 consecutive k of one column) is two
+//     ds_read_b64_tr_b16, the gfx950 transposing LDS read: within each 16-lane
+//     group, lane i receives element i of the 4 x 16 block whose rows the 16
+//     lanes' 8-byte addresses name.
+// Two LDS stages held in four distinct arrays (the k loop is unrolled by two
+// so every access names its array), the next k-tile's copies in flight while
+// the current one is multiplied.
+// ---------------------------------------------------------------------------
+#define RV_G3_BM 256
+#define RV_G3_BN 256
+#define RV_G3_BK 64
+
+typedef __attribute__((address_space(3))) void rv_lds_void;
+typedef __attribute__((ext_vector_type(4))) short rv_s16x4;
+
+__device__ __forceinline__ int rv_g3_swz_rows(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int rv_g3_swz_kn(int kr) { return (kr & 3) * 4; }
+
+// Global -> LDS copy of one k-tile: A rows [m0, m0+256) x [k0, k0+64) into
+// As (256 x 64), B into Bs ([k][n] 64 x 256, or [n][k] 256 x 64).
+template <bool B_KN>
+__device__ __forceinline__ void rv_g3_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
+                                           const unsigned short* __restrict__ B, long long a_base, long long lda,
+                                           long long b_base, long long ldb, int k0, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r0 = wave * 32 + i * 8;
+        const int r = r0 + (lane >> 3);
+        const int c = (lane & 7) ^ rv_g3_swz_rows(r);
+        __builtin_amdgcn_global_load_lds((const void*)(A + a_base + (long long)r * lda + k0 + c * 8),
+                                         (rv_lds_void*)(As + r0 * 64), 16, 0, 0);
+    }
+    if (B_KN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kr0 = wave * 8 + i * 2;
+            const int kr = kr0 + (lane >> 5);
+            const int c = (lane & 31) ^ rv_g3_swz_kn(kr);
+            __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)(k0 + kr) * ldb + c * 8),
+                                             (rv_lds_void*)(Bs + kr0 * 256), 16, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r0 = wave * 32 + i * 8;
+            const int r = r0 + (lane >> 3);
+            const int c = (lane & 7) ^ rv_g3_swz_rows(r);
+            __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)r * ldb + k0 + c * 8),
+                                             (rv_lds_void*)(Bs + r0 * 64), 16, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ rv_bf16x8 rv_g3_frag_rows(const unsigned short* S, int r, int c) {
+    return *reinterpret_cast<const rv_bf16x8*>(S + r * 64 + ((c ^ rv_g3_swz_rows(r)) << 3));
+}
+
+// B fragment from a [k][n] tile: 8 consecutive k (kk + (lane >> 5) * 8 ..) of
+// column nt + (lane & 31), as two transposing reads of 4 k each.
+__device__ __forceinline__ rv_bf16x8 rv_g3_frag_kn(const unsigned short* S, int nt, int kk, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int nb = nt + (g & 1) * 16, kb = kk + (g >> 1) * 8;
+    const int n = nb + (j & 3) * 4;
+    rv_s16x4 h[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int kr = kb + half * 4 + (j >> 2);
+        const int off = kr * 256 + (((n >> 3) ^ rv_g3_swz_kn(kr)) << 3) + (n & 7);
+        h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) rv_s16x4*)((__attribute__((address_space(3))) unsigned short*)S + off));
+    }
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(rv_bf16x8, v);
+}
+
+template <bool B_KN>
+__device__ __forceinline__ void rv_g3_mma(rv_f32x16 (&acc)[2][4], const unsigned short* As, const unsigned short* Bs,
+                                          int wm, int wn, int lane) {
+#pragma unroll
+    for (int kk = 0; kk < RV_G3_BK; kk += 16) {
+        rv_bf16x8 af[2], bf[4];
+        const int c = (kk >> 3) + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) af[i] = rv_g3_frag_rows(As, wm * 64 + i * 32 + (lane & 31), c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bf[j] = B_KN ? rv_g3_frag_kn(Bs, wn * 128 + j * 32, kk, lane)
+                         : rv_g3_frag_rows(Bs, wn * 128 + j * 32 + (lane & 31), c);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <bool B_KN, int MODE, class Epi>
+__device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restrict__ A,
+                                                 const unsigned short* __restrict__ B, long long a_off, long long lda,
+                                                 long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
+                                                 float* __restrict__ partials) {
+    __shared__ __attribute__((aligned(1024))) unsigned short a0[RV_G3_BM * RV_G3_BK];
+    __shared__ __attribute__((aligned(1024))) unsigned short a1[RV_G3_BM * RV_G3_BK];
+    __shared__ __attribute__((aligned(1024))) unsigned short b0[RV_G3_BN * RV_G3_BK];
+    __shared__ __attribute__((aligned(1024))) unsigned short b1[RV_G3_BN * RV_G3_BK];
+    __shared__ float lds_red[8];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = M / RV_G3_BM, tiles_n = N / RV_G3_BN;
+    const int ntiles = tiles_m * tiles_n;
+    int tm, tn;
+    {
+        int bid = blockIdx.x;
+        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
+            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
+            const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
+            tm = group * 4 + (within & 3);
+            tn = within >> 2;
+        } else {
+            tm = bid / tiles_n;
+            tn = bid % tiles_n;
+        }
+    }
+    const int m0 = tm * RV_G3_BM, n0 = tn * RV_G3_BN;
+    const long long a_base = a_off + (long long)m0 * lda;
+    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
+
+    rv_f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int KT = K / RV_G3_BK;
+    rv_g3_copy<B_KN>(a0, b0, A, B, a_base, lda, b_base, ldb, 0, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; kt += 2) {
+        if (kt + 1 < KT) rv_g3_copy<B_KN>(a1, b1, A, B, a_base, lda, b_base, ldb, (kt + 1) * RV_G3_BK, wave, lane);
+        rv_g3_mma<B_KN>(acc, a0, b0, wm, wn, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 >= KT) break;
+        if (kt + 2 < KT) rv_g3_copy<B_KN>(a0, b0, A, B, a_base, lda, b_base, ldb, (kt + 2) * RV_G3_BK, wave, lane);
+        rv_g3_mma<B_KN>(acc, a1, b1, wm, wn, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+                const float v = epi(acc[i][j][r], m, n);
+                if (MODE == 0)
+                    epi.store(m, n, v);
+                else
+                    part = part + v;
+            }
+    if (MODE == 1) {
+        part = rv_group_sum<64>(part);
+        if (lane == 0) lds_red[wave] = part;
+        __syncthreads();
+        if (tid == 0) {
+            float s = lds_red[0];
+#pragma unroll
+            for (int w = 1; w < 8; ++w) s = s + lds_red[w];
+            partials[blockIdx.x] = s;
+        }
+    }
+}
+
 // Deterministic fold of `count` float partials into one value: each thread
 // adds a strided subset in ascending order, then a fixed binary tree in LDS.
 // No atomics, so two runs give the same bits.

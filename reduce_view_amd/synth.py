@@ -344,3 +344,15 @@ def copy(rows: int, cols: int) -> Spec:
     x = g.buffer("X", (rows, cols), "f32")
     g.output(g.contiguous(x))
     return g
+
+
+def gemm_bf16_bt(m: int, n: int, k: int) -> Spec:
+    """y = SUM_k CAST(A) * CAST(Bt) with the second operand stored [n][k]
+    (k-contiguous), viewed as (m, n, k) with m-stride 0."""
+    g = Spec(f"gemm_bf16_bt_{m}x{n}x{k}")
+    a = g.buffer("A", (m, k), "bf16")
+    bt = g.buffer("Bt", (n, k), "bf16")
+    a3 = g.cast(g.view(a, ("reshape", (m, 1, k)), ("expand", (m, n, k))), "f32")
+    b3 = g.cast(g.view(bt, ("reshape", (1, n, k)), ("expand", (m, n, k))), "f32")
+    g.output(g.sum(g.mul(a3, b3), (2,)))
+    return g

@@ -185,3 +185,63 @@ def test_gemm_relu2_sum(m, n, k):
           + U * abs(float(s_ref.ravel()[0])))
     report(f"gemm_S_{m}x{n}x{k}", np.array([abs(float(s_gpu.ravel()[0]) - float(s_ref.ravel()[0]))]), np.array([ds]))
     assert abs(float(s_gpu.ravel()[0]) - float(s_ref.ravel()[0])) <= ds
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 256, 128), (128, 256, 64), (512, 256, 320)])
+def test_gemm_k_contiguous_second_operand_bit_exact(m, n, k):
+    _case(f"gemm bt int {m}x{n}x{k}")
+    inp = synth.inputs_gemm_integer(m, n, k)
+    inp = {"A": inp["A"], "Bt": np.ascontiguousarray(inp["B"].T)}
+    spec = synth.gemm_bf16_bt(m, n, k)
+    prog = _prog(spec)
+    assert [kk["class"] for kk in prog.describe()["kernels"]] == ["MFMA"]
+    got, = run(prog, inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
+# ---- full sizes, in the launch configuration the benchmark times -------------
+
+def test_softmax_full_size():
+    _case("softmax full 16384x4096")
+    test_softmax(16384, 4096)
+
+
+def test_rmsnorm_full_size():
+    _case("rmsnorm full 16384x4096")
+    test_rmsnorm(16384, 4096)
+
+
+def test_layernorm_full_size():
+    _case("layernorm full 8192x8192")
+    test_layernorm(8192, 8192)
+
+
+def test_gemm_full_size_sampled_rows_and_scalar():
+    """4096^3: y on sampled rows against the oracle computed for those rows
+    only, and S = SUM(relu(y)^2) against the stored oracle value."""
+    import json
+    import os
+    _case("gemm full 4096^3")
+    m = n = k = 4096
+    inp = synth.inputs_gemm(m, n, k, seed=5)
+    y_gpu, = run(_prog(synth.gemm_bf16(m, n, k)), inp)
+    rows = [0, 1, 2047, 4095]
+    sub = {"A": inp["A"][rows], "B": inp["B"]}
+    y_ref, = oracle.run(synth.gemm_bf16(len(rows), n, k), sub)
+    a = np.abs(interp.bf16_to_f32(sub["A"]).astype(np.float64))
+    b = np.abs(interp.bf16_to_f32(inp["B"]).astype(np.float64))
+    dy = 4 * gamma(k - 1) * (a @ b)
+    err = np.abs(y_gpu[rows, :, 0].astype(np.float64) - y_ref[:, :, 0])
+    report("gemm_full_y_rows", err, dy)
+    assert np.all(err <= dy)
+    path = os.path.join(os.path.dirname(__file__), "golden", "gemm_relu2_sum_4096.json")
+    gold = json.load(open(path))
+    prog = _prog(synth.gemm_relu2_sum(m, n, k))
+    desc = prog.describe()
+    s_gpu, = run(prog, inp)
+    depth = desc["kernels"][0]["plan_detail"]["partial_sum_depth"] + desc["kernels"][1]["plan_detail"]["sum_depth"]
+    ds = gold["propagated_y_term"] + U * gold["sum_q"] + 4 * gamma(depth) * gold["sum_q"] + U * abs(gold["S"])
+    e = abs(float(s_gpu.ravel()[0]) - gold["S"])
+    report("gemm_full_S", np.array([e]), np.array([ds]))
+    assert e <= ds
