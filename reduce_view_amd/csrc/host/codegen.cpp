@@ -1039,7 +1039,10 @@ std::string Gen::gen_gemm() {
     const int64_t M = k.domain[0], N = k.domain[1], K = k.domain[2];
     const int64_t lda = A.v.strides[0];
     const int64_t ldb = kn ? B.v.strides[2] : B.v.strides[1];
-    const char* fn = k.plan == "gemm_lds" ? "rv_gemm_lds_bf16<" : (k.plan == "gemm256" ? "rv_gemm256_bf16<" : "rv_gemm_bf16<");
+    const char* fn = k.plan == "gemm_lds"    ? "rv_gemm_lds_bf16<"
+                     : k.plan == "gemm_lds4" ? "rv_gemm_lds4_bf16<"
+                     : k.plan == "gemm256"   ? "rv_gemm256_bf16<"
+                                             : "rv_gemm_bf16<";
     b << "  " << fn << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ">(" << pa << ", " << pb
       << ", " << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", "
       << K << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ");\n";

@@ -178,8 +178,8 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             std::string kd = kind && *kind ? kind : "lds";
             if (!big) kd = "reg128";
             int BM = 128, BN = 128, waves = 4;
-            if (kd == "lds") {
-                k.plan = "gemm_lds";
+            if (kd == "lds" || kd == "lds4") {
+                k.plan = kd == "lds" ? "gemm_lds" : "gemm_lds4";
                 BM = BN = 256;
                 waves = 8;
                 k.lds = 4 * 256 * 64 * 2 + 32;

@@ -662,6 +662,168 @@ __device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// Four-stage variant of the direct-to-LDS contraction: k-tiles of 32, four
+// LDS stages of 32 KB (eight distinct arrays, the k loop unrolled by four),
+// copies issued three k-tiles ahead; a stage is waited for with an exact
+// vmcnt (the copies of the later in-flight stages may stay outstanding).
+// A rows are 64 bytes (4 chunks) with chunks XOR-swizzled by (row >> 2) & 3,
+// so 16 consecutive rows read at one chunk cover all 64 banks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int rv_g4_swz_rows(int r) { return (r >> 2) & 3; }
+
+// s_waitcnt vmcnt(N) leaving the LDS/export counters free (gfx9 encoding).
+#define RV_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | ((((N) >> 4) & 3) << 14))
+
+template <bool B_KN>
+__device__ __forceinline__ void rv_g4_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
+                                           const unsigned short* __restrict__ B, long long a_base, long long lda,
+                                           long long b_base, long long ldb, int k0, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r0 = wave * 32 + i * 16;
+        const int r = r0 + (lane >> 2);
+        const int c = (lane & 3) ^ rv_g4_swz_rows(r);
+        __builtin_amdgcn_global_load_lds((const void*)(A + a_base + (long long)r * lda + k0 + c * 8),
+                                         (rv_lds_void*)(As + r0 * 32), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (B_KN) {
+            const int kr0 = wave * 4 + i * 2;
+            const int kr = kr0 + (lane >> 5);
+            const int c = (lane & 31) ^ rv_g3_swz_kn(kr);
+            __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)(k0 + kr) * ldb + c * 8),
+                                             (rv_lds_void*)(Bs + kr0 * 256), 16, 0, 0);
+        } else {
+            const int r0 = wave * 32 + i * 16;
+            const int r = r0 + (lane >> 2);
+            const int c = (lane & 3) ^ rv_g4_swz_rows(r);
+            __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)r * ldb + k0 + c * 8),
+                                             (rv_lds_void*)(Bs + r0 * 32), 16, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ rv_bf16x8 rv_g4_frag_rows(const unsigned short* S, int r, int c) {
+    return *reinterpret_cast<const rv_bf16x8*>(S + r * 32 + ((c ^ rv_g4_swz_rows(r)) << 3));
+}
+
+template <bool B_KN>
+__device__ __forceinline__ void rv_g4_mma(rv_f32x16 (&acc)[2][4], const unsigned short* As, const unsigned short* Bs,
+                                          int wm, int wn, int lane) {
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 16) {
+        rv_bf16x8 af[2], bf[4];
+        const int c = (kk >> 3) + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) af[i] = rv_g4_frag_rows(As, wm * 64 + i * 32 + (lane & 31), c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bf[j] = B_KN ? rv_g3_frag_kn(Bs, wn * 128 + j * 32, kk, lane)
+                         : rv_g4_frag_rows(Bs, wn * 128 + j * 32 + (lane & 31), c);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <bool B_KN, int MODE, class Epi>
+__device__ __forceinline__ void rv_gemm_lds4_bf16(const unsigned short* __restrict__ A,
+                                                  const unsigned short* __restrict__ B, long long a_off, long long lda,
+                                                  long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
+                                                  float* __restrict__ partials) {
+    __shared__ __attribute__((aligned(1024))) unsigned short a0[256 * 32], a1[256 * 32], a2[256 * 32], a3[256 * 32];
+    __shared__ __attribute__((aligned(1024))) unsigned short b0[256 * 32], b1[256 * 32], b2[256 * 32], b3[256 * 32];
+    __shared__ float lds_red[8];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = M / 256, tiles_n = N / 256;
+    const int ntiles = tiles_m * tiles_n;
+    int tm, tn;
+    {
+        int bid = blockIdx.x;
+        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
+            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
+            const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
+            tm = group * 4 + (within & 3);
+            tn = within >> 2;
+        } else {
+            tm = bid / tiles_n;
+            tn = bid % tiles_n;
+        }
+    }
+    const int m0 = tm * 256, n0 = tn * 256;
+    const long long a_base = a_off + (long long)m0 * lda;
+    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
+
+    rv_f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int KT = K / 32;
+    rv_g4_copy<B_KN>(a0, b0, A, B, a_base, lda, b_base, ldb, 0, wave, lane);
+    if (KT > 1) rv_g4_copy<B_KN>(a1, b1, A, B, a_base, lda, b_base, ldb, 32, wave, lane);
+    if (KT > 2) rv_g4_copy<B_KN>(a2, b2, A, B, a_base, lda, b_base, ldb, 64, wave, lane);
+#define RV_G4_STEP(CA, CB, NA, NB, T)                                                                  \
+    {                                                                                                  \
+        const int t_ = (T);                                                                            \
+        if (t_ >= KT) break;                                                                           \
+        const int after = KT - 1 - t_;                                                                 \
+        if (after >= 2)                                                                                \
+            RV_WAIT_VM(8);                                                                             \
+        else if (after == 1)                                                                           \
+            RV_WAIT_VM(4);                                                                             \
+        else                                                                                           \
+            RV_WAIT_VM(0);                                                                             \
+        __syncthreads();                                                                               \
+        if (t_ + 3 < KT) rv_g4_copy<B_KN>(NA, NB, A, B, a_base, lda, b_base, ldb, (t_ + 3) * 32, wave, lane); \
+        rv_g4_mma<B_KN>(acc, CA, CB, wm, wn, lane);                                                   \
+    }
+    for (int kt = 0; kt < KT; kt += 4) {
+        RV_G4_STEP(a0, b0, a3, b3, kt)
+        RV_G4_STEP(a1, b1, a0, b0, kt + 1)
+        RV_G4_STEP(a2, b2, a1, b1, kt + 2)
+        RV_G4_STEP(a3, b3, a2, b2, kt + 3)
+    }
+#undef RV_G4_STEP
+    __syncthreads();
+
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+                const float v = epi(acc[i][j][r], m, n);
+                if (MODE == 0)
+                    epi.store(m, n, v);
+                else
+                    part = part + v;
+            }
+    if (MODE == 1) {
+        part = rv_group_sum<64>(part);
+        if (lane == 0) lds_red[wave] = part;
+        __syncthreads();
+        if (tid == 0) {
+            float s = lds_red[0];
+#pragma unroll
+            for (int w = 1; w < 8; ++w) s = s + lds_red[w];
+            partials[blockIdx.x] = s;
+        }
+    }
+}
+
 // Deterministic fold of `count` float partials into one value: each thread
 // adds a strided subset in ascending order, then a fixed binary tree in LDS.
 // No atomics, so two runs give the same bits.

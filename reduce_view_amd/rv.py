@@ -332,6 +332,33 @@ class Program:
             self._ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         return self._ws
 
+    def prepare(self, inputs: dict, outputs, stream, workspace=None):
+        """Marshal the buffers once; the returned callable enqueues the
+        program with no per-call Python work beyond the C call (for launch
+        loops and graph capture)."""
+        bufs = []
+        for name in self.slots:
+            t = inputs[name]
+            if not t.is_contiguous():
+                raise RVError(-1, f"input {name} must be contiguous")
+            bufs.append(rv_buffer(t.data_ptr(), t.numel(), DTYPE[_dtype_name(t.dtype)], 0))
+        for t in outputs:
+            bufs.append(rv_buffer(t.data_ptr(), t.numel(), DTYPE[_dtype_name(t.dtype)], 0))
+        arr = (rv_buffer * max(1, len(bufs)))(*bufs)
+        n = len(bufs)
+        ws = workspace if workspace is not None else self.workspace(outputs[0].device if outputs else "cuda")
+        wptr = ctypes.c_void_p(ws.data_ptr() if ws is not None else None)
+        wsb = self.ws_bytes
+        sptr = ctypes.c_void_p(stream.cuda_stream or None)
+        h = self.h
+        fn = _lib.rv_launch
+        keep = (inputs, outputs, ws)
+
+        def go():
+            _check(fn(h, arr, n, wptr, wsb, sptr))
+        go.keep = keep
+        return go
+
     def launch(self, inputs: dict, outputs=None, stream=None, workspace=None):
         """Enqueue on ``stream`` (default: torch's current stream). ``inputs``
         maps slot names to device tensors (contiguous, of the declared dtype).
