@@ -507,7 +507,9 @@ std::string Gen::gen_tiled() {
     b << "  const bool interior = " << inter << ";\n";
     for (int edge = 0; edge < 2; ++edge) {
         b << (edge ? "  else {\n" : "  if (interior) {\n");
-        // loads: cell (r, c) of the lane's block is (y + r, x + c)
+        // loads: cell (r, c) of the lane's block is (y + r, x + c). In edge
+        // tiles a lane whose 4 x 4 block lies inside the domain and the mask
+        // still takes the vector path; only blocks on a boundary go cell by cell.
         for (size_t l = 0; l < k.leaves.size(); ++l) {
             const Leaf& L = k.leaves[l];
             if (!used[l] || L.zero) continue;
@@ -515,43 +517,63 @@ std::string Gen::gen_tiled() {
             std::string V = fmt("l%zu", l);
             const std::string T = st(L.dtype);
             b << "    " << vt(L.dtype) << " " << V << "[4][4];\n";
-            const bool along_x = !edge && leaf_vec_ok(L, X, 4);
-            const bool along_y = !edge && !along_x && leaf_vec_ok(L, Y, 4);
+            const bool along_x = leaf_vec_ok(L, X, 4);
+            const bool along_y = !along_x && leaf_vec_ok(L, Y, 4);
             const bool ybcast = L.v.strides[Y] == 0 && !masked(L.v, Y);
             const bool xbcast = L.v.strides[X] == 0 && !masked(L.v, X);
+            std::ostringstream vec;
             if (along_x) {
                 if (ybcast) {
-                    b << "    { const rv_pack<" << T << ", 4> v = " << vload(L, 4, P + " + " + addr(L.v, idx_at("y", "x")))
-                      << ";\n";
-                    b << "      for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) " << V << "[r][c] = "
-                      << ld(L.dtype, "v.v[c]") << "; }\n";
+                    vec << "    { const rv_pack<" << T << ", 4> v = " << vload(L, 4, P + " + " + addr(L.v, idx_at("y", "x")))
+                        << ";\n";
+                    vec << "      for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) " << V << "[r][c] = "
+                        << ld(L.dtype, "v.v[c]") << "; }\n";
                 } else {
-                    b << "    for (int r = 0; r < 4; ++r) { const rv_pack<" << T << ", 4> v = "
-                      << vload(L, 4, P + " + " + addr(L.v, idx_at("y + r", "x"))) << ";\n";
-                    b << "      for (int c = 0; c < 4; ++c) " << V << "[r][c] = " << ld(L.dtype, "v.v[c]") << "; }\n";
+                    vec << "    for (int r = 0; r < 4; ++r) { const rv_pack<" << T << ", 4> v = "
+                        << vload(L, 4, P + " + " + addr(L.v, idx_at("y + r", "x"))) << ";\n";
+                    vec << "      for (int c = 0; c < 4; ++c) " << V << "[r][c] = " << ld(L.dtype, "v.v[c]") << "; }\n";
                 }
             } else if (along_y) {
                 if (xbcast) {
-                    b << "    { const rv_pack<" << T << ", 4> v = " << vload(L, 4, P + " + " + addr(L.v, idx_at("y", "x")))
-                      << ";\n";
-                    b << "      for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) " << V << "[r][c] = "
-                      << ld(L.dtype, "v.v[r]") << "; }\n";
+                    vec << "    { const rv_pack<" << T << ", 4> v = " << vload(L, 4, P + " + " + addr(L.v, idx_at("y", "x")))
+                        << ";\n";
+                    vec << "      for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) " << V << "[r][c] = "
+                        << ld(L.dtype, "v.v[r]") << "; }\n";
                 } else {
-                    b << "    for (int c = 0; c < 4; ++c) { const rv_pack<" << T << ", 4> v = "
-                      << vload(L, 4, P + " + " + addr(L.v, idx_at("y", "x + c"))) << ";\n";
-                    b << "      for (int r = 0; r < 4; ++r) " << V << "[r][c] = " << ld(L.dtype, "v.v[r]") << "; }\n";
+                    vec << "    for (int c = 0; c < 4; ++c) { const rv_pack<" << T << ", 4> v = "
+                        << vload(L, 4, P + " + " + addr(L.v, idx_at("y", "x + c"))) << ";\n";
+                    vec << "      for (int r = 0; r < 4; ++r) " << V << "[r][c] = " << ld(L.dtype, "v.v[r]") << "; }\n";
                 }
+            }
+            std::ostringstream sc;
+            sc << "    for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) {\n";
+            sc << "      const " << I << " yy = y + r, xx = x + c;\n";
+            auto idq = idx_at("yy", "xx");
+            std::string mc = edge ? mask_cond(L.v, idq, all) : "";
+            std::string cond = edge ? fmt("yy < %s && xx < %s", lit(NY).c_str(), lit(NX).c_str()) +
+                                          (mc.empty() ? "" : " && " + mc)
+                                    : "";
+            sc << "      " << V << "[r][c] = " << (cond.empty() ? "" : "(" + cond + ") ? ")
+               << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << (cond.empty() ? "" : " : " + zero_of(L.dtype))
+               << ";\n    }\n";
+            if (!along_x && !along_y) {
+                b << sc.str();
+            } else if (!edge) {
+                b << vec.str();
             } else {
-                b << "    for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) {\n";
-                b << "      const " << I << " yy = y + r, xx = x + c;\n";
-                auto idq = idx_at("yy", "xx");
-                std::string mc = edge ? mask_cond(L.v, idq, all) : "";
-                std::string cond = edge ? fmt("yy < %s && xx < %s", lit(NY).c_str(), lit(NX).c_str()) +
-                                              (mc.empty() ? "" : " && " + mc)
-                                        : "";
-                b << "      " << V << "[r][c] = " << (cond.empty() ? "" : "(" + cond + ") ? ")
-                  << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << (cond.empty() ? "" : " : " + zero_of(L.dtype))
-                  << ";\n    }\n";
+                // the block is inside the domain and the leaf's mask
+                std::string in = fmt("y + 4 <= %s && x + 4 <= %s", lit(NY).c_str(), lit(NX).c_str());
+                for (int d = 0; d < rank; ++d) {
+                    if (!masked(L.v, d)) continue;
+                    if (d == X)
+                        in += fmt(" && x >= %s && x + 4 <= %s", lit(L.v.mask_lo[d]).c_str(), lit(L.v.mask_hi[d]).c_str());
+                    else if (d == Y)
+                        in += fmt(" && y >= %s && y + 4 <= %s", lit(L.v.mask_lo[d]).c_str(), lit(L.v.mask_hi[d]).c_str());
+                    else
+                        in += fmt(" && i%d >= %s && i%d < %s", d, lit(L.v.mask_lo[d]).c_str(), d,
+                                  lit(L.v.mask_hi[d]).c_str());
+                }
+                b << "    if (" << in << ") {\n" << vec.str() << "    } else {\n" << sc.str() << "    }\n";
             }
         }
         for (size_t e = 0; e < k.ex.size(); ++e) {
@@ -574,13 +596,21 @@ std::string Gen::gen_tiled() {
         }
         for (const Store& s : k.stores) {
             std::string P = pname(s.loc, s.dtype, true);
-            bool vec = !edge && s.v.strides[X] == 1 && s.v.offset % 4 == 0;
+            bool vec = s.v.strides[X] == 1 && s.v.offset % 4 == 0;
             for (int d = 0; d < X; ++d)
                 if (k.domain[d] > 1 && s.v.strides[d] % 4) vec = false;
             if (vec) {
+                if (edge) b << "    if (y + 4 <= " << lit(NY) << " && x + 4 <= " << lit(NX) << ") {\n";
                 b << "    for (int r = 0; r < 4; ++r) { rv_pack<" << st(s.dtype) << ", 4> v;\n";
                 b << "      for (int c = 0; c < 4; ++c) v.v[c] = " << sv(s.dtype, fmt("e%d[r][c]", s.ex)) << ";\n";
                 b << "      " << vstore(s.dtype, 4, P + " + " + addr(s.v, idx_at("y + r", "x")), "v") << "; }\n";
+                if (edge) {
+                    b << "    } else\n";
+                    b << "    for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) {\n";
+                    b << "      const " << I << " yy = y + r, xx = x + c;\n";
+                    b << "      if (yy < " << lit(NY) << " && xx < " << lit(NX) << ") " << P << "["
+                      << addr(s.v, idx_at("yy", "xx")) << "] = " << sv(s.dtype, fmt("e%d[r][c]", s.ex)) << ";\n    }\n";
+                }
             } else {
                 b << "    for (int r = 0; r < 4; ++r) for (int c = 0; c < 4; ++c) {\n";
                 b << "      const " << I << " yy = y + r, xx = x + c;\n";
@@ -1043,7 +1073,13 @@ std::string Gen::gen_gemm() {
                      : k.plan == "gemm_lds4" ? "rv_gemm_lds4_bf16<"
                      : k.plan == "gemm256"   ? "rv_gemm256_bf16<"
                                              : "rv_gemm_bf16<";
-    b << "  " << fn << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ">(" << pa << ", " << pb
+    int TM = 2, TN = 4;
+    {
+        size_t at = k.plan_json.find("\"wave_tiles\":[");
+        if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"wave_tiles\":[%d,%d]", &TM, &TN);
+    }
+    const std::string targs = k.plan == "gemm_lds" ? fmt(", %s, %d, %d", sname.c_str(), TM, TN) : "";
+    b << "  " << fn << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << targs << ">(" << pa << ", " << pb
       << ", " << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", "
       << K << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ");\n";
     return f.str() + "@@BODY@@" + b.str();

@@ -178,11 +178,14 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             std::string kd = kind && *kind ? kind : "lds";
             if (!big) kd = "reg128";
             int BM = 128, BN = 128, waves = 4;
+            int TM = 2, TN = 4;
             if (kd == "lds" || kd == "lds4") {
                 k.plan = kd == "lds" ? "gemm_lds" : "gemm_lds4";
                 BM = BN = 256;
                 waves = 8;
                 k.lds = 4 * 256 * 64 * 2 + 32;
+                const char* wv = getenv("RV_GEMM_WAVES");
+                if (wv && std::string(wv) == "4x2") TM = 4, TN = 2;
             } else if (kd == "reg") {
                 k.plan = "gemm256";
                 BM = BN = 256;
@@ -200,9 +203,9 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             // adds its own depth
             const int per_lane = BM * BN / (64 * waves);
             snprintf(buf, sizeof buf,
-                     "\"tile\":[%d,%d,64],\"waves\":%d,\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
+                     "\"tile\":[%d,%d,64],\"waves\":%d,\"wave_tiles\":[%d,%d],\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
                      "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d",
-                     BM, BN, waves, kn ? "kn" : "nk", per_lane - 1 + 6 + waves - 1);
+                     BM, BN, waves, TM, TN, kn ? "kn" : "nk", per_lane - 1 + 6 + waves - 1);
             k.plan_json = buf;
             if (k.mfma_partial) {
                 p.regions[k.partials_region].bytes = (size_t)k.n_partials * 4;
@@ -232,7 +235,7 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             int WY = env_int("RV_EW_WAVES_Y", 1);
             if (WY != 1 && WY != 2 && WY != 4) fail(RV_E_INVALID, "RV_EW_WAVES_Y must be 1, 2 or 4");
             int WX = 4 / WY;
-            int order = env_int("RV_EW_ORDER", 3);
+            int order = env_int("RV_EW_ORDER", 0);
             int64_t B = numel(k.domain) / (k.domain[X] * k.domain[Y]);
             int64_t gx = (k.domain[X] + 32 * WX - 1) / (32 * WX), gy = (k.domain[Y] + 32 * WY - 1) / (32 * WY);
             k.grid[0] = (unsigned)(gx * gy);

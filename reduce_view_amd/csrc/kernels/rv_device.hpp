@@ -557,28 +557,42 @@ __device__ __forceinline__ rv_bf16x8 rv_g3_frag_kn(const unsigned short* S, int 
     return __builtin_bit_cast(rv_bf16x8, v);
 }
 
-template <bool B_KN>
-__device__ __forceinline__ void rv_g3_mma(rv_f32x16 (&acc)[2][4], const unsigned short* As, const unsigned short* Bs,
-                                          int wm, int wn, int lane) {
+// Operand fragments of one k16 step for a wave owning TM x TN 32 x 32 tiles
+// at rows r0.., cols c0...
+template <bool B_KN, int TM, int TN>
+__device__ __forceinline__ void rv_g3_frags(rv_bf16x8 (&af)[TM], rv_bf16x8 (&bf)[TN], const unsigned short* As,
+                                            const unsigned short* Bs, int r0, int c0, int lane, int kk) {
+    const int c = (kk >> 3) + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = rv_g3_frag_rows(As, r0 + i * 32 + (lane & 31), c);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+        bf[j] = B_KN ? rv_g3_frag_kn(Bs, c0 + j * 32, kk, lane) : rv_g3_frag_rows(Bs, c0 + j * 32 + (lane & 31), c);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void rv_g3_step(rv_f32x16 (&acc)[TM][TN], const rv_bf16x8 (&af)[TM],
+                                           const rv_bf16x8 (&bf)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+}
+
+// The four k16 steps of a 64-deep k-tile.
+template <bool B_KN, int TM, int TN>
+__device__ __forceinline__ void rv_g3_mma(rv_f32x16 (&acc)[TM][TN], const unsigned short* As, const unsigned short* Bs,
+                                          int r0, int c0, int lane) {
 #pragma unroll
     for (int kk = 0; kk < RV_G3_BK; kk += 16) {
-        rv_bf16x8 af[2], bf[4];
-        const int c = (kk >> 3) + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = rv_g3_frag_rows(As, wm * 64 + i * 32 + (lane & 31), c);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bf[j] = B_KN ? rv_g3_frag_kn(Bs, wn * 128 + j * 32, kk, lane)
-                         : rv_g3_frag_rows(Bs, wn * 128 + j * 32 + (lane & 31), c);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        rv_bf16x8 af[TM], bf[TN];
+        rv_g3_frags<B_KN, TM, TN>(af, bf, As, Bs, r0, c0, lane, kk);
+        rv_g3_step<TM, TN>(acc, af, bf);
     }
 }
 
-template <bool B_KN, int MODE, class Epi>
+template <bool B_KN, int MODE, class Epi, int TM = 2, int TN = 4>
 __device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restrict__ A,
                                                  const unsigned short* __restrict__ B, long long a_off, long long lda,
                                                  long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
@@ -588,9 +602,10 @@ __device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restric
     __shared__ __attribute__((aligned(1024))) unsigned short b0[RV_G3_BN * RV_G3_BK];
     __shared__ __attribute__((aligned(1024))) unsigned short b1[RV_G3_BN * RV_G3_BK];
     __shared__ float lds_red[8];
+    constexpr int WAVES_N = RV_G3_BN / (32 * TN);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int r0 = (wave / WAVES_N) * (32 * TM), c0 = (wave % WAVES_N) * (32 * TN);
     const int tiles_m = M / RV_G3_BM, tiles_n = N / RV_G3_BN;
     const int ntiles = tiles_m * tiles_n;
     int tm, tn;
@@ -610,11 +625,11 @@ __device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restric
     const long long a_base = a_off + (long long)m0 * lda;
     const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
 
-    rv_f32x16 acc[2][4];
+    rv_f32x16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -624,25 +639,25 @@ __device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restric
     __syncthreads();
     for (int kt = 0; kt < KT; kt += 2) {
         if (kt + 1 < KT) rv_g3_copy<B_KN>(a1, b1, A, B, a_base, lda, b_base, ldb, (kt + 1) * RV_G3_BK, wave, lane);
-        rv_g3_mma<B_KN>(acc, a0, b0, wm, wn, lane);
+        rv_g3_mma<B_KN, TM, TN>(acc, a0, b0, r0, c0, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (kt + 1 >= KT) break;
         if (kt + 2 < KT) rv_g3_copy<B_KN>(a0, b0, A, B, a_base, lda, b_base, ldb, (kt + 2) * RV_G3_BK, wave, lane);
-        rv_g3_mma<B_KN>(acc, a1, b1, wm, wn, lane);
+        rv_g3_mma<B_KN, TM, TN>(acc, a1, b1, r0, c0, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
     float part = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+                const int m = m0 + r0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int n = n0 + c0 + j * 32 + (lane & 31);
                 const float v = epi(acc[i][j][r], m, n);
                 if (MODE == 0)
                     epi.store(m, n, v);
