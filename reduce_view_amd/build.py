@@ -68,7 +68,13 @@ def check_device_header(verbose: bool = False) -> None:
                 "  rv_gemm_lds4_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(512) chk9(const unsigned short* a, "
                 "const unsigned short* b, float* p) {\n"
-                "  rv_gemm_lds4_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n")
+                "  rv_gemm_lds4_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(512) chk10(const unsigned short* a, "
+                "const unsigned short* b, float* p) {\n"
+                "  rv_gemm_pp_bf16<true, 1, E>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(512) chk11(const unsigned short* a, "
+                "const unsigned short* b, float* p) {\n"
+                "  rv_gemm_pp_bf16<false, 0, E, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n")
     cmd = [HIPCC] + GPU_FLAGS + ["--cuda-device-only", "-c", tu, "-o", os.path.join(out_dir, "device_check.o")]
     if verbose:
         print(" ".join(cmd))

@@ -1070,6 +1070,7 @@ std::string Gen::gen_gemm() {
     const int64_t lda = A.v.strides[0];
     const int64_t ldb = kn ? B.v.strides[2] : B.v.strides[1];
     const char* fn = k.plan == "gemm_lds"    ? "rv_gemm_lds_bf16<"
+                     : k.plan == "gemm_pp"   ? "rv_gemm_pp_bf16<"
                      : k.plan == "gemm_lds4" ? "rv_gemm_lds4_bf16<"
                      : k.plan == "gemm256"   ? "rv_gemm256_bf16<"
                                              : "rv_gemm_bf16<";
@@ -1078,7 +1079,14 @@ std::string Gen::gen_gemm() {
         size_t at = k.plan_json.find("\"wave_tiles\":[");
         if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"wave_tiles\":[%d,%d]", &TM, &TN);
     }
-    const std::string targs = k.plan == "gemm_lds" ? fmt(", %s, %d, %d", sname.c_str(), TM, TN) : "";
+    int KH = 2;
+    {
+        size_t at = k.plan_json.find("\"phase_k16\":");
+        if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"phase_k16\":%d", &KH);
+    }
+    const std::string targs = k.plan == "gemm_lds"  ? fmt(", %s, %d, %d", sname.c_str(), TM, TN)
+                              : k.plan == "gemm_pp" ? fmt(", %s, %d", sname.c_str(), KH)
+                                                    : "";
     b << "  " << fn << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << targs << ">(" << pa << ", " << pb
       << ", " << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", "
       << K << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ");\n";

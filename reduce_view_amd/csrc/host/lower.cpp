@@ -171,21 +171,25 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
         case KClass::MFMA: {
             int64_t M = k.domain[0], N = k.domain[1];
             // 256 x 256 tiles when the shape allows: direct-to-LDS copies and
-            // 8 waves ("lds", the default) or register-staged copies and 4
-            // waves ("reg"); otherwise 128 x 128 register-staged tiles
+            // 8 waves ("lds", the default; "lds4" with four 32-deep stages;
+            // "pp" with the two wave groups in ping-pong) or register-staged
+            // copies and 4 waves ("reg"); otherwise 128 x 128 register-staged
+            // tiles. RV_GEMM_WAVES=4x4 (four waves of 128 x 128) spills.
             const bool big = M % 256 == 0 && N % 256 == 0;
             const char* kind = getenv("RV_GEMM_KERNEL");
             std::string kd = kind && *kind ? kind : "lds";
             if (!big) kd = "reg128";
             int BM = 128, BN = 128, waves = 4;
             int TM = 2, TN = 4;
-            if (kd == "lds" || kd == "lds4") {
-                k.plan = kd == "lds" ? "gemm_lds" : "gemm_lds4";
+            if (kd == "lds" || kd == "lds4" || kd == "pp") {
+                k.plan = kd == "lds" ? "gemm_lds" : kd == "pp" ? "gemm_pp" : "gemm_lds4";
                 BM = BN = 256;
                 waves = 8;
                 k.lds = 4 * 256 * 64 * 2 + 32;
                 const char* wv = getenv("RV_GEMM_WAVES");
                 if (wv && std::string(wv) == "4x2") TM = 4, TN = 2;
+                if (wv && std::string(wv) == "4x4") TM = 4, TN = 4, waves = 4;
+                if (kd == "pp") TM = 2, TN = 4, waves = 8;
             } else if (kd == "reg") {
                 k.plan = "gemm256";
                 BM = BN = 256;
@@ -207,6 +211,11 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
                      "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d",
                      BM, BN, waves, TM, TN, kn ? "kn" : "nk", per_lane - 1 + 6 + waves - 1);
             k.plan_json = buf;
+            if (k.plan == "gemm_pp") {
+                // k16 steps per ping-pong phase (2, or 1 with RV_GEMM_KH=1)
+                const char* kh = getenv("RV_GEMM_KH");
+                k.plan_json += (kh && atoi(kh) == 1) ? ",\"phase_k16\":1" : ",\"phase_k16\":2";
+            }
             if (k.mfma_partial) {
                 p.regions[k.partials_region].bytes = (size_t)k.n_partials * 4;
                 k.stores[0].loc = Loc{2, k.partials_region};

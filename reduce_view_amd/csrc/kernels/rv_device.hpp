@@ -499,24 +499,27 @@ typedef __attribute__((ext_vector_type(4))) short rv_s16x4;
 __device__ __forceinline__ int rv_g3_swz_rows(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int rv_g3_swz_kn(int kr) { return (kr & 3) * 4; }
 
-// Global -> LDS copy of one k-tile: A rows [m0, m0+256) x [k0, k0+64) into
-// As (256 x 64), B into Bs ([k][n] 64 x 256, or [n][k] 256 x 64).
-template <bool B_KN>
+// Global -> LDS copy of one k-tile by NW waves: A rows [m0, m0+256) x
+// [k0, k0+64) into As (256 x 64), B into Bs ([k][n] 64 x 256, or [n][k]
+// 256 x 64). Each instruction moves 1 KB (8 A rows, or 2 B k-rows).
+template <bool B_KN, int NW>
 __device__ __forceinline__ void rv_g3_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
                                            const unsigned short* __restrict__ B, long long a_base, long long lda,
                                            long long b_base, long long ldb, int k0, int wave, int lane) {
+    constexpr int AR = 256 / NW;  // A rows per wave
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r0 = wave * 32 + i * 8;
+    for (int i = 0; i < AR / 8; ++i) {
+        const int r0 = wave * AR + i * 8;
         const int r = r0 + (lane >> 3);
         const int c = (lane & 7) ^ rv_g3_swz_rows(r);
         __builtin_amdgcn_global_load_lds((const void*)(A + a_base + (long long)r * lda + k0 + c * 8),
                                          (rv_lds_void*)(As + r0 * 64), 16, 0, 0);
     }
     if (B_KN) {
+        constexpr int BR = 64 / NW;  // B k-rows per wave
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kr0 = wave * 8 + i * 2;
+        for (int i = 0; i < BR / 2; ++i) {
+            const int kr0 = wave * BR + i * 2;
             const int kr = kr0 + (lane >> 5);
             const int c = (lane & 31) ^ rv_g3_swz_kn(kr);
             __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)(k0 + kr) * ldb + c * 8),
@@ -524,8 +527,8 @@ __device__ __forceinline__ void rv_g3_copy(unsigned short* As, unsigned short* B
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r0 = wave * 32 + i * 8;
+        for (int i = 0; i < AR / 8; ++i) {
+            const int r0 = wave * AR + i * 8;
             const int r = r0 + (lane >> 3);
             const int c = (lane & 7) ^ rv_g3_swz_rows(r);
             __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)r * ldb + k0 + c * 8),
@@ -601,8 +604,9 @@ __device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restric
     __shared__ __attribute__((aligned(1024))) unsigned short a1[RV_G3_BM * RV_G3_BK];
     __shared__ __attribute__((aligned(1024))) unsigned short b0[RV_G3_BN * RV_G3_BK];
     __shared__ __attribute__((aligned(1024))) unsigned short b1[RV_G3_BN * RV_G3_BK];
-    __shared__ float lds_red[8];
     constexpr int WAVES_N = RV_G3_BN / (32 * TN);
+    constexpr int NW = WAVES_N * (RV_G3_BM / (32 * TM));
+    __shared__ float lds_red[NW];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int r0 = (wave / WAVES_N) * (32 * TM), c0 = (wave % WAVES_N) * (32 * TN);
@@ -634,16 +638,21 @@ __device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restric
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int KT = K / RV_G3_BK;
-    rv_g3_copy<B_KN>(a0, b0, A, B, a_base, lda, b_base, ldb, 0, wave, lane);
+    rv_g3_copy<B_KN, NW>(a0, b0, A, B, a_base, lda, b_base, ldb, 0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // the scheduling barriers keep the next k-tile's copies at the top of the
+    // step: left alone, the scheduler sinks them below the LDS reads of the
+    // other stage (they cannot alias) and the copy latency is exposed
     for (int kt = 0; kt < KT; kt += 2) {
-        if (kt + 1 < KT) rv_g3_copy<B_KN>(a1, b1, A, B, a_base, lda, b_base, ldb, (kt + 1) * RV_G3_BK, wave, lane);
+        if (kt + 1 < KT) rv_g3_copy<B_KN, NW>(a1, b1, A, B, a_base, lda, b_base, ldb, (kt + 1) * RV_G3_BK, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
         rv_g3_mma<B_KN, TM, TN>(acc, a0, b0, r0, c0, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (kt + 1 >= KT) break;
-        if (kt + 2 < KT) rv_g3_copy<B_KN>(a0, b0, A, B, a_base, lda, b_base, ldb, (kt + 2) * RV_G3_BK, wave, lane);
+        if (kt + 2 < KT) rv_g3_copy<B_KN, NW>(a0, b0, A, B, a_base, lda, b_base, ldb, (kt + 2) * RV_G3_BK, wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
         rv_g3_mma<B_KN, TM, TN>(acc, a1, b1, r0, c0, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -671,7 +680,7 @@ __device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restric
         if (tid == 0) {
             float s = lds_red[0];
 #pragma unroll
-            for (int w = 1; w < 8; ++w) s = s + lds_red[w];
+            for (int w = 1; w < NW; ++w) s = s + lds_red[w];
             partials[blockIdx.x] = s;
         }
     }
@@ -689,6 +698,12 @@ __device__ __forceinline__ int rv_g4_swz_rows(int r) { return (r >> 2) & 3; }
 
 // s_waitcnt vmcnt(N) leaving the LDS/export counters free (gfx9 encoding).
 #define RV_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | ((((N) >> 4) & 3) << 14))
+// Workgroup barrier that does not drain the vector-memory counter (a
+// __syncthreads() fence waits for every outstanding copy into LDS): this
+// wave's LDS reads finish, then s_barrier; the memory clobber keeps the
+// compiler from moving LDS accesses across it. Copies the barrier must cover
+// are waited for explicitly with RV_WAIT_VM before it.
+#define RV_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 template <bool B_KN>
 __device__ __forceinline__ void rv_g4_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
@@ -784,22 +799,21 @@ __device__ __forceinline__ void rv_gemm_lds4_bf16(const unsigned short* __restri
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int KT = K / 32;
-    rv_g4_copy<B_KN>(a0, b0, A, B, a_base, lda, b_base, ldb, 0, wave, lane);
-    if (KT > 1) rv_g4_copy<B_KN>(a1, b1, A, B, a_base, lda, b_base, ldb, 32, wave, lane);
-    if (KT > 2) rv_g4_copy<B_KN>(a2, b2, A, B, a_base, lda, b_base, ldb, 64, wave, lane);
+    // every step issues exactly one stage of copies (past the end it reloads
+    // the last k-tile into a stage nobody reads), so "this stage is done" is
+    // always vmcnt <= 8: the two later stages' 4 + 4 copies may stay in flight
+#define RV_G4_KT(t) (((t) < KT ? (t) : KT - 1) * 32)
+    rv_g4_copy<B_KN>(a0, b0, A, B, a_base, lda, b_base, ldb, RV_G4_KT(0), wave, lane);
+    rv_g4_copy<B_KN>(a1, b1, A, B, a_base, lda, b_base, ldb, RV_G4_KT(1), wave, lane);
+    rv_g4_copy<B_KN>(a2, b2, A, B, a_base, lda, b_base, ldb, RV_G4_KT(2), wave, lane);
 #define RV_G4_STEP(CA, CB, NA, NB, T)                                                                  \
     {                                                                                                  \
         const int t_ = (T);                                                                            \
         if (t_ >= KT) break;                                                                           \
-        const int after = KT - 1 - t_;                                                                 \
-        if (after >= 2)                                                                                \
-            RV_WAIT_VM(8);                                                                             \
-        else if (after == 1)                                                                           \
-            RV_WAIT_VM(4);                                                                             \
-        else                                                                                           \
-            RV_WAIT_VM(0);                                                                             \
-        __syncthreads();                                                                               \
-        if (t_ + 3 < KT) rv_g4_copy<B_KN>(NA, NB, A, B, a_base, lda, b_base, ldb, (t_ + 3) * 32, wave, lane); \
+        RV_WAIT_VM(8);                                                                                 \
+        RV_LDS_BARRIER();                                                                              \
+        rv_g4_copy<B_KN>(NA, NB, A, B, a_base, lda, b_base, ldb, RV_G4_KT(t_ + 3), wave, lane);        \
+        __builtin_amdgcn_sched_barrier(0);                                                             \
         rv_g4_mma<B_KN>(acc, CA, CB, wm, wn, lane);                                                   \
     }
     for (int kt = 0; kt < KT; kt += 4) {
@@ -809,6 +823,8 @@ __device__ __forceinline__ void rv_gemm_lds4_bf16(const unsigned short* __restri
         RV_G4_STEP(a3, b3, a2, b2, kt + 3)
     }
 #undef RV_G4_STEP
+#undef RV_G4_KT
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     float part = 0.0f;
@@ -838,6 +854,137 @@ __device__ __forceinline__ void rv_gemm_lds4_bf16(const unsigned short* __restri
         }
     }
 }
+
+// ---------------------------------------------------------------------------
+// Ping-pong variant of the direct-to-LDS contraction (256 x 256 tile, 64-deep
+// k-tiles, two LDS stages, 8 waves of 64 x 128). The waves form two groups,
+// one wave of each per SIMD; group 1 starts one barrier late, so at every
+// barrier-delimited phase one group reads its operand fragments from LDS
+// while the other runs a pure MFMA burst on fragments already in registers,
+// and each SIMD's matrix unit is fed by alternating waves. A phase covers KH
+// k16 steps. Group 0 alone copies k-tiles: tile T+1 is issued in group 0's
+// first read phase of tile T (T >= 1; tiles 0 and 1 in the prologue), after
+// group 1 has finished reading tile T-1 from that stage, and is waited for at
+// the end of group 0's last MFMA phase of tile T, before anyone reads it.
+// ---------------------------------------------------------------------------
+#define RV_PP_BARRIER()                    \
+    do {                                   \
+        __builtin_amdgcn_sched_barrier(0); \
+        RV_LDS_BARRIER();                  \
+        __builtin_amdgcn_sched_barrier(0); \
+    } while (0)
+
+template <bool B_KN, int MODE, class Epi, int KH = 2>
+__device__ __forceinline__ void rv_gemm_pp_bf16(const unsigned short* __restrict__ A,
+                                                const unsigned short* __restrict__ B, long long a_off, long long lda,
+                                                long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
+                                                float* __restrict__ partials) {
+    constexpr int TM = 2, TN = 4, NW = 8;
+    constexpr int HALVES = (RV_G3_BK / 16) / KH;  // phases per k-tile and group
+    static_assert(HALVES * KH * 16 == RV_G3_BK, "KH must divide the k16 steps of a k-tile");
+    __shared__ __attribute__((aligned(1024))) unsigned short a0[RV_G3_BM * RV_G3_BK];
+    __shared__ __attribute__((aligned(1024))) unsigned short a1[RV_G3_BM * RV_G3_BK];
+    __shared__ __attribute__((aligned(1024))) unsigned short b0[RV_G3_BN * RV_G3_BK];
+    __shared__ __attribute__((aligned(1024))) unsigned short b1[RV_G3_BN * RV_G3_BK];
+    __shared__ float lds_red[NW];
+    const int tid = threadIdx.x;
+    // the wave index in a scalar register: the group tests below are then
+    // scalar branches, so a wave outside a group never reaches its s_barrier
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int group = wave >> 2, gw = wave & 3;
+    const int r0 = (wave >> 1) * (32 * TM), c0 = (wave & 1) * (32 * TN);
+    const int tiles_m = M / RV_G3_BM, tiles_n = N / RV_G3_BN;
+    const int ntiles = tiles_m * tiles_n;
+    int tm, tn;
+    {
+        int bid = blockIdx.x;
+        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
+            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
+            const int grp = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
+            tm = grp * 4 + (within & 3);
+            tn = within >> 2;
+        } else {
+            tm = bid / tiles_n;
+            tn = bid % tiles_n;
+        }
+    }
+    const int m0 = tm * RV_G3_BM, n0 = tn * RV_G3_BN;
+    const long long a_base = a_off + (long long)m0 * lda;
+    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
+
+    rv_f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int KT = K / RV_G3_BK;
+    if (group == 0) {
+        // 16 copies per wave and k-tile: tile 0 is complete at vmcnt <= 16
+        rv_g3_copy<B_KN, 4>(a0, b0, A, B, a_base, lda, b_base, ldb, 0, gw, lane);
+        if (KT > 1) {
+            rv_g3_copy<B_KN, 4>(a1, b1, A, B, a_base, lda, b_base, ldb, RV_G3_BK, gw, lane);
+            RV_WAIT_VM(16);
+        } else {
+            RV_WAIT_VM(0);
+        }
+    }
+    RV_PP_BARRIER();
+    if (group == 1) RV_PP_BARRIER();
+    for (int t = 0; t < KT; ++t) {
+        const unsigned short* As = (t & 1) ? a1 : a0;
+        const unsigned short* Bs = (t & 1) ? b1 : b0;
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) {
+            if (h == 0 && group == 0 && t >= 1 && t + 1 < KT) {
+                if (t & 1)
+                    rv_g3_copy<B_KN, 4>(a0, b0, A, B, a_base, lda, b_base, ldb, (t + 1) * RV_G3_BK, gw, lane);
+                else
+                    rv_g3_copy<B_KN, 4>(a1, b1, A, B, a_base, lda, b_base, ldb, (t + 1) * RV_G3_BK, gw, lane);
+            }
+            rv_bf16x8 af[KH][TM], bf[KH][TN];
+#pragma unroll
+            for (int q = 0; q < KH; ++q)
+                rv_g3_frags<B_KN, TM, TN>(af[q], bf[q], As, Bs, r0, c0, lane, (h * KH + q) * 16);
+            RV_PP_BARRIER();
+#pragma unroll
+            for (int q = 0; q < KH; ++q) rv_g3_step<TM, TN>(acc, af[q], bf[q]);
+            if (h == HALVES - 1 && group == 0) RV_WAIT_VM(0);
+            RV_PP_BARRIER();
+        }
+    }
+    if (group == 0) RV_PP_BARRIER();
+
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + r0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int n = n0 + c0 + j * 32 + (lane & 31);
+                const float v = epi(acc[i][j][r], m, n);
+                if (MODE == 0)
+                    epi.store(m, n, v);
+                else
+                    part = part + v;
+            }
+    if (MODE == 1) {
+        part = rv_group_sum<64>(part);
+        if (lane == 0) lds_red[wave] = part;
+        __syncthreads();
+        if (tid == 0) {
+            float s = lds_red[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) s = s + lds_red[w];
+            partials[blockIdx.x] = s;
+        }
+    }
+}
+#undef RV_PP_BARRIER
 
 // Deterministic fold of `count` float partials into one value: each thread
 // adds a strided subset in ascending order, then a fixed binary tree in LDS.
