@@ -63,6 +63,13 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                           "(or python reduce_view_amd/build.py)")
+    # One HIP runtime per process: torch ships its own libamdhip64 (same
+    # SONAME as the system one the library names), so torch goes first and
+    # the library binds to the runtime torch's tensors and streams live in.
+    # Loaded the other way round, the process holds two runtimes and the
+    # library's sees no device.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     vp = ctypes.c_void_p
