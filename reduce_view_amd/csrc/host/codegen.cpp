@@ -750,8 +750,68 @@ std::string Gen::gen_row() {
         }
     }
     const int64_t NRG = (NK + RPW - 1) / RPW;
+    // prefetch (persistent grid): a streamed leaf whose row is one run of
+    // aligned vectors is loaded one row group ahead into registers of its
+    // storage type, so its next row is in flight while this one is reduced
+    const bool pf = k.plan_json.find("\"prefetch\":1") != std::string::npos && single && !ragged;
+    std::vector<int> pfl(k.leaves.size(), 0);
+    if (pf)
+        for (size_t l = 0; l < k.leaves.size(); ++l) {
+            const Leaf& L = k.leaves[l];
+            if (!used[l] || L.zero || hoisted[l] || masked(L.v, R) || !leaf_vec_ok(L, R, VW)) continue;
+            if (L.v.strides[R] == 0) continue;
+            pfl[l] = 1;
+        }
+    // row index variables r<sfx>, rv<sfx>, i<d><sfx> of row group rgx
+    auto row_vars = [&](std::ostringstream& s, const std::string& sfx, const std::string& rgx,
+                        const std::string& ind) {
+        std::vector<std::string> kx(rank);
+        s << ind << "const " << I << " r" << sfx << " = (" << rgx << ") * " << RPW << " + lr;\n";
+        s << ind << "const bool rv" << sfx << " = (" << rgx << ") < " << lit(NRG) << " && r" << sfx << " < " << lit(NK)
+          << ";\n";
+        std::string rem = "r" + sfx;
+        for (size_t j = kd.size(); j-- > 0;) {
+            int d = kd[j];
+            s << ind << "const " << I << " i" << d << sfx << " = "
+              << (j ? fmt("%s %% %s", rem.c_str(), lit(k.domain[d]).c_str()) : rem) << ";\n";
+            kx[d] = fmt("i%d%s", d, sfx.c_str());
+            if (j) {
+                s << ind << "const " << I << " q" << d << sfx << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
+                rem = fmt("q%d%s", d, sfx.c_str());
+            }
+        }
+        return kx;
+    };
+    auto emit_pf_loads = [&](std::ostringstream& s, const std::string& sfx, const std::vector<std::string>& kx,
+                             const std::string& ind) {
+        for (size_t l = 0; l < k.leaves.size(); ++l) {
+            if (!pfl[l]) continue;
+            const Leaf& L = k.leaves[l];
+            std::string kc = mask_cond(L.v, kx, kd);
+            std::string rowok = "rv" + sfx + (kc.empty() ? std::string() : " && " + kc);
+            std::vector<std::string> idx = kx;
+            idx[R] = "n0";
+            s << ind << "for (int v = 0; v < " << NV << "; ++v) {\n";
+            s << ind << "  const " << I << " n0 = " << nexpr("v", "0") << ";\n";
+            s << ind << "  if (" << rowok << ") f" << l << "[v] = " << vload(L, VW, pname(L.loc, L.dtype, false) + " + " + addr(L.v, idx))
+              << ";\n";
+            s << ind << "  else f" << l << "[v] = rv_pack<" << st(L.dtype) << ", " << VW << ">{};\n";
+            s << ind << "}\n";
+        }
+    };
+    bool any_pf = false;
+    for (int x : pfl) any_pf = any_pf || x;
+    if (any_pf) {
+        for (size_t l = 0; l < k.leaves.size(); ++l)
+            if (pfl[l]) b << "  rv_pack<" << st(k.leaves[l].dtype) << ", " << VW << "> f" << l << "[" << NV << "];\n";
+        b << "  {\n";
+        std::ostringstream s;
+        auto kx = row_vars(s, "", "blockIdx.x", "    ");
+        emit_pf_loads(s, "", kx, "    ");
+        b << s.str() << "  }\n";
+    }
     b << "  for (" << I << " rg = blockIdx.x; rg < " << lit(NRG) << "; rg += gridDim.x) {\n";
-    if (T > 64 && nred_) b << "    __syncthreads();\n";
+    if (T > 64 && nred_) b << "    rv_lds_barrier();\n";
     b << "    const " << I << " r = rg * " << RPW << " + lr;\n";
     b << "    const bool rv = r < " << lit(NK) << ";\n";
     std::vector<std::string> kidx(rank);
@@ -767,6 +827,18 @@ std::string Gen::gen_row() {
                 rem = fmt("q%d", d);
             }
         }
+    }
+    if (any_pf) {
+        for (size_t l = 0; l < k.leaves.size(); ++l)
+            if (pfl[l]) {
+                b << "    rv_pack<" << st(k.leaves[l].dtype) << ", " << VW << "> c" << l << "[" << NV << "];\n";
+                b << "    for (int v = 0; v < " << NV << "; ++v) c" << l << "[v] = f" << l << "[v];\n";
+            }
+        b << "    {\n";
+        std::ostringstream s;
+        auto kx = row_vars(s, "n", "rg + gridDim.x", "      ");
+        emit_pf_loads(s, "n", kx, "      ");
+        b << s.str() << "    }\n";
     }
     int red_slot = 0;
     // value of ex i at in-thread position q (a scalar for row-constant values)
@@ -789,6 +861,12 @@ std::string Gen::gen_row() {
                 continue;
             }
             if (hoisted[x.leaf]) continue;  // read as h<leaf>[q] where used
+            if (pfl[x.leaf]) {
+                b << "    " << vt(x.dtype) << " " << V << "[" << E << "];\n";
+                b << "    for (int v = 0; v < " << NV << "; ++v)\n      for (int i = 0; i < " << VW << "; ++i) " << V
+                  << "[v * " << VW << " + i] = " << ld(L.dtype, fmt("c%d[v].v[i]", x.leaf)) << ";\n";
+                continue;
+            }
             std::string kc = mask_cond(L.v, kidx, kd);
             std::string rowok = "rv" + (kc.empty() ? std::string() : " && " + kc);
             if (stat[e]) {
@@ -822,7 +900,7 @@ std::string Gen::gen_row() {
             int g = std::min(T, 64);
             b << "      acc = rv_group_" << (sum ? "sum" : "max") << "<" << g << ">(acc);\n";
             if (T > 64) {
-                b << "      if ((t & 63) == 0) red[" << red_slot << "][lr][lt >> 6] = acc;\n      __syncthreads();\n";
+                b << "      if ((t & 63) == 0) red[" << red_slot << "][lr][lt >> 6] = acc;\n      rv_lds_barrier();\n";
                 b << "      acc = red[" << red_slot << "][lr][0];\n";
                 for (int w = 1; w < W; ++w)
                     b << "      acc = " << (sum ? fmt("acc + red[%d][lr][%d]", red_slot, w)

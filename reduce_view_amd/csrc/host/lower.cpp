@@ -302,8 +302,27 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
         const int block = std::max(256, T);
         int rpw = block / T;
         int64_t nrg = (NK + rpw - 1) / rpw;
-        // one workgroup per row group (a persistent grid measured slower)
-        k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>(nrg, env_int("RV_ROW_GRID", 1 << 30)));
+        // A row-long leaf that is the same for every row (a norm's weights)
+        // is loaded once per workgroup; then the grid is persistent, two
+        // workgroups per CU, each loading its next row group while it
+        // reduces the current one. Otherwise one workgroup per row group
+        // (measured faster without reused weights). RV_ROW_PREFETCH=0/1 and
+        // RV_ROW_GRID override.
+        bool reused = false;
+        for (auto& L : k.leaves) {
+            if (L.zero) continue;
+            bool along = false, across = false;
+            for (int d = 0; d < rank; ++d) {
+                const bool red = (k.rdims >> d) & 1u;
+                const bool m = !full_mask(L.v, d);
+                if (red && (L.v.strides[d] != 0 || m)) along = true;
+                if (!red && k.domain[d] > 1 && (L.v.strides[d] != 0 || m)) across = true;
+            }
+            if (along && !across) reused = true;
+        }
+        const bool prefetch = env_int("RV_ROW_PREFETCH", reused ? 1 : 0) != 0;
+        k.grid[0] = (unsigned)std::max<int64_t>(
+            1, std::min<int64_t>(nrg, env_int("RV_ROW_GRID", prefetch ? 2 * 256 : 1 << 30)));
         k.block[0] = (unsigned)block;
         k.lane_dim = rank - 1;
         int nv = (int)((NR + (int64_t)T * vw - 1) / ((int64_t)T * vw));
@@ -312,7 +331,8 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             if (e.op == RV_SUM || e.op == RV_MAX) ++nred;
         k.lds = T > 64 ? (size_t)nred * rpw * (T / 64) * 4 : 0;
         snprintf(buf, sizeof buf, "\"threads_per_row\":%d,\"rows_per_block\":%d,\"vec\":%d,\"chunks\":%d,"
-                 "\"row_len\":%lld,\"rows\":%lld", T, rpw, vw, nv, (long long)NR, (long long)NK);
+                 "\"row_len\":%lld,\"rows\":%lld,\"prefetch\":%d", T, rpw, vw, nv, (long long)NR, (long long)NK,
+                 prefetch ? 1 : 0);
         k.plan_json = buf;
         return;
     }

@@ -91,6 +91,14 @@ __device__ __forceinline__ float rv_group_sum(float v) {
     return v;
 }
 
+// Workgroup barrier for exchanges through LDS: this wave's LDS accesses
+// complete, then s_barrier; the memory clobber keeps the compiler from moving
+// memory accesses across it. Unlike __syncthreads() (whose fence waits for
+// every outstanding global access) it leaves global loads in flight, so a
+// row prefetched before a reduction is still arriving while the row before
+// it is reduced.
+__device__ __forceinline__ void rv_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int W>
 __device__ __forceinline__ float rv_group_max(float v) {
 #pragma unroll
@@ -703,7 +711,7 @@ __device__ __forceinline__ int rv_g4_swz_rows(int r) { return (r >> 2) & 3; }
 // wave's LDS reads finish, then s_barrier; the memory clobber keeps the
 // compiler from moving LDS accesses across it. Copies the barrier must cover
 // are waited for explicitly with RV_WAIT_VM before it.
-#define RV_LDS_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+#define RV_LDS_BARRIER() rv_lds_barrier()
 
 template <bool B_KN>
 __device__ __forceinline__ void rv_g4_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
