@@ -226,7 +226,17 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
     }
     merge_dims(k);
     const int rank = (int)k.domain.size();
-    if (numel(k.domain) == 0) {
+    // nothing to compute unless a reduce over an empty range still has
+    // cells to write (each gets the reduce identity, limn README, "The op
+    // set": a reduce starts from its identity)
+    bool any_store = false;
+    for (auto& s : k.stores) {
+        int64_t cells = 1;  // a reduced dim (stride 0 in the store) counts once
+        for (int d = 0; d < s.v.ndim; ++d)
+            if (!(((k.rdims >> d) & 1u) && s.v.strides[d] == 0)) cells *= s.v.shape[d];
+        any_store = any_store || cells > 0;
+    }
+    if (numel(k.domain) == 0 && !any_store) {
         k.plan = "empty";
         k.grid[0] = 0;
         return;

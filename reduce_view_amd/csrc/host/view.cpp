@@ -48,6 +48,13 @@ bool view_empty_mask(const rv_view& v) {
 
 bool view_is_contiguous(const rv_view& v) {
     if (v.offset != 0) return false;
+    bool empty = false;
+    for (int d = 0; d < v.ndim; ++d) empty = empty || v.shape[d] == 0;
+    if (empty) {  // no element is addressed: the strides do not matter
+        for (int d = 0; d < v.ndim; ++d)
+            if (v.mask_lo[d] != 0 || v.mask_hi[d] != v.shape[d]) return false;
+        return true;
+    }
     int64_t s = 1;
     for (int d = v.ndim - 1; d >= 0; --d) {
         if (v.mask_lo[d] != 0 || v.mask_hi[d] != v.shape[d]) return false;

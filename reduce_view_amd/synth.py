@@ -346,6 +346,23 @@ def copy(rows: int, cols: int) -> Spec:
     return g
 
 
+def unary_map(op: str, n: int, dtype: str = "f32") -> Spec:
+    """y = OP(x) over a flat (n,) buffer (one of NEG, EXP, LOG, SQRT, RECIP)."""
+    if op not in ("NEG", "EXP", "LOG", "SQRT", "RECIP"):
+        raise ValueError(op)
+    g = Spec(f"{op.lower()}_{n}")
+    x = g.buffer("x", (n,), dtype)
+    g.output(g._add(op=op, src=(x,)))
+    return g
+
+
+def fp32_sweep(lo_bits: int, hi_bits: int, step: int = 1) -> np.ndarray:
+    """Every ``step``-th float32 whose bit pattern lies in [lo_bits, hi_bits)
+    (unsigned order: 0x00000000.. are +0 upward, 0x80000000.. are -0
+    downward), as a float32 array. No randomness."""
+    return np.arange(lo_bits, hi_bits, step, dtype=np.uint32).view(np.float32)
+
+
 def gemm_bf16_bt(m: int, n: int, k: int) -> Spec:
     """y = SUM_k CAST(A) * CAST(Bt) with the second operand stored [n][k]
     (k-contiguous), viewed as (m, n, k) with m-stride 0."""

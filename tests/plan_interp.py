@@ -81,7 +81,13 @@ def run_plan(desc: dict, inputs: list, out_specs: list) -> list:
                 if L["zero"]:
                     vals[i] = np.zeros(dom, STORAGE[dt])
                 else:
-                    vals[i] = _gather(mem(L["loc"], L["dtype"]), L["view"], dom)
+                    # constant along a reduced dim (stride 0, unmasked): one
+                    # copy there, broadcast where used (a cell whose reduce
+                    # range is empty still sees it)
+                    v = L["view"]
+                    gshape = tuple(1 if (d in red and v["strides"][d] == 0 and v["mask_lo"][d] == 0
+                                         and v["mask_hi"][d] == dom[d]) else dom[d] for d in range(len(dom)))
+                    vals[i] = _gather(mem(L["loc"], L["dtype"]), v, gshape)
             elif name == "CONST":
                 v = np.array([float(op["cval"])], np.float64)
                 if dt == "bf16":
@@ -101,9 +107,8 @@ def run_plan(desc: dict, inputs: list, out_specs: list) -> list:
                     acc = (acc + (A[:, :, kk:kk + 1] * B[:, :, kk:kk + 1]).astype(np.float32)).astype(np.float32)
                 vals[i] = np.broadcast_to(acc, dom)
             elif name in ("SUM", "MAX"):
-                x = np.ascontiguousarray(vals[op["a"]])
-                r = O._reduce(name, x, ops[op["a"]]["dtype"], tuple(red))
-                vals[i] = np.broadcast_to(r, dom)
+                x = np.ascontiguousarray(np.broadcast_to(vals[op["a"]], dom))
+                vals[i] = O._reduce(name, x, ops[op["a"]]["dtype"], tuple(red))  # reduced dims kept as 1
             elif name == "CAST":
                 vals[i] = O._cast(np.ascontiguousarray(vals[op["a"]]), ops[op["a"]]["dtype"], dt)
             elif name in ("NEG", "EXP", "LOG", "SQRT", "RECIP"):
@@ -127,11 +132,19 @@ def run_plan(desc: dict, inputs: list, out_specs: list) -> list:
                 buf[:] = 0
                 buf[0] = s
                 continue
-            size = 1 + int(np.dot(np.array(dom) - 1, np.array(st["view"]["strides"]))) + st["view"]["offset"]
+            # a reduced dim the store does not walk (stride 0) is written once
+            sshape = tuple(1 if (d in red and st["view"]["strides"][d] == 0) else dom[d] for d in range(len(dom)))
+            if any(sshape[d] == 1 and v.shape[d] != 1 for d in range(len(dom))):
+                v = v[tuple(slice(0, 1) if (sshape[d] == 1 and v.shape[d] != 1) else slice(None)
+                            for d in range(len(dom)))]
+            v = np.broadcast_to(v, sshape)
+            if int(np.prod(sshape)) == 0:
+                continue
+            size = 1 + int(np.dot(np.array(sshape) - 1, np.array(st["view"]["strides"]))) + st["view"]["offset"]
             o = mem(st["loc"], st["dtype"], size)
             if st["loc"]["kind"] == "workspace" and o.dtype != STORAGE[st["dtype"]]:
                 ws[st["loc"]["index"]] = o = np.zeros(size, STORAGE[st["dtype"]])
-            _scatter(o, st["view"], dom, v.astype(STORAGE[st["dtype"]]))
+            _scatter(o, st["view"], sshape, v.astype(STORAGE[st["dtype"]]))
     return [o.reshape(s) for o, (s, _) in zip(outs, out_specs)]
 
 

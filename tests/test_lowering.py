@@ -134,6 +134,21 @@ def test_empty_and_size_one_dims():
     assert got[0].tobytes() == oracle.run(g, {"x": xi})[0].tobytes()
 
 
+@pytest.mark.parametrize("shape,axes", [((3, 0), (1,)), ((0, 4), (0,)), ((2, 3, 0), (1, 2)), ((2, 0, 3), (1,))])
+def test_reduce_over_empty_range_writes_identity(shape, axes):
+    # the kernel still runs for its output cells, which get 0 (SUM) / -inf (MAX)
+    g = synth.Spec()
+    x = g.buffer("x", shape, "f32")
+    g.output(g.sum(x, axes), g.max(x, axes))
+    inp = {"x": np.zeros(shape, np.float32)}
+    d, got = _interp(g, inp)
+    assert all(k["plan"] != "empty" for k in d["kernels"])
+    ref = oracle.run(g, inp)
+    assert np.all(ref[0] == 0) and np.all(ref[1] == -np.inf)
+    for a, b in zip(got, ref):
+        assert a.shape == b.shape and a.tobytes() == b.tobytes()
+
+
 def test_dims_merge_for_contiguous_chains():
     prog = rv.compile_spec(synth.rmsnorm(64, 512))
     k = prog.describe()["kernels"][0]
