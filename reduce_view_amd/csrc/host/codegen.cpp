@@ -238,8 +238,11 @@ struct Gen {
     }
 
     std::string header() {
-        return "extern \"C\" __global__ void __launch_bounds__(" + std::to_string(k.block[0]) + ") " + k.name + "(" +
-               signature() + ")";
+        // a 256 x 256 contraction tile on 4 waves keeps 256 accumulators per
+        // lane: one wave per SIMD, so the whole register file is the wave's
+        const bool one_wave = k.cls == KClass::MFMA && k.plan == "gemm_lds" && k.block[0] == 256;
+        return "extern \"C\" __global__ void __launch_bounds__(" + std::to_string(k.block[0]) + ") " +
+               (one_wave ? "__attribute__((amdgpu_waves_per_eu(1, 1))) " : "") + k.name + "(" + signature() + ")";
     }
 
     // a load is streaming (nontemporal) when no domain dim of size > 1 has
