@@ -5,7 +5,8 @@ float32 elementwise chain WHERE(CMPLT(a, b), a*b, EXP(-a)) + c with b a
 permuted View and c a stride-0 row vector, the same chain with a read through
 a shrink-then-pad masked View, and a standalone 4096 x 4096 transpose. One
 step runs all three programs once. ``--workload`` selects one of the other
-kernels instead (softmax, rmsnorm, layernorm, gemm, matmul64).
+kernels instead (softmax, softmax_long, rmsnorm, layernorm, gemm, matmul64,
+copy).
 
 Inputs are seeded, synthetic and already resident in HBM when timing starts;
 several input sets rotate so that consecutive launches never re-read data the
@@ -64,6 +65,12 @@ def workloads():
             programs=[("softmax", synth.softmax(16384, 4096), 2 * 16384 * 4096 * F32)],
             inputs=lambda seed: synth.inputs_softmax(16384, 4096, seed),
             unit="GB/s", dtype="f32", bound="hbm", seed=2),
+        "softmax_long": dict(
+            desc=("row softmax with max shift over rows too long for on-chip storage, 256x262144 fp32 "
+                  "(1 MB rows; streaming plan, online max/denominator), x ~ U(-1e3,1e3), seed 2"),
+            programs=[("softmax_long", synth.softmax(256, 262144), 2 * 256 * 262144 * F32)],
+            inputs=lambda seed: synth.inputs_softmax(256, 262144, seed),
+            unit="GB/s", dtype="f32", bound="hbm", seed=2),
         "rmsnorm": dict(
             desc="RMSNorm 16384x4096 fp32, x ~ N(0,1), w ~ N(1,0.1), eps 1e-6, seed 3",
             programs=[("rmsnorm", synth.rmsnorm(16384, 4096), 2 * 16384 * 4096 * F32 + 4096 * F32)],
@@ -79,7 +86,7 @@ def workloads():
                   "epilogue, full SUM to an fp32 scalar; A ~ N(0,1/64), B ~ N(0,1), seed 5"),
             programs=[("gemm_relu2_sum", synth.gemm_relu2_sum(4096, 4096, 4096), 2 * 4096 ** 3)],
             inputs=lambda seed: synth.inputs_gemm(4096, 4096, 4096, seed),
-            unit="TFLOP/s", dtype="f32", bound="mfma", seed=5),
+            unit="TFLOP/s", dtype="bf16", bound="mfma", seed=5),
         "copy": dict(
             desc="plain 4096x4096 fp32 copy (bandwidth reference; not a hot-path workload)",
             programs=[("copy", synth.copy(4096, 4096), 2 * 4096 * 4096 * F32)],
@@ -241,7 +248,7 @@ def main():
                 "per_program_ms": {n: round(v, 5) for n, v in per_kernel.items()}}
     out = {"metric": METRIC, "value": round(value, 2), "unit": wl["unit"], "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": wl["dtype"] if args.workload != "gemm" else "bf16",
+           "scaling": "weak", "vs_baseline": None, "dtype": wl["dtype"],
            "data": "synthetic", "config": {"workload": args.workload + ": " + wl["desc"],
                                           "input_sets_rotated": nsets},
            "roofline": roofline}

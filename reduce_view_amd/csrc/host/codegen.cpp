@@ -276,6 +276,7 @@ struct Gen {
     std::string gen_rowmajor();
     std::string gen_tiled();
     std::string gen_row();
+    std::string gen_row_stream();
     std::string gen_cells();
     std::string gen_fold();
     std::string gen_gemm();
@@ -958,6 +959,313 @@ std::string Gen::gen_row() {
 }
 
 // ---------------------------------------------------------------------------
+// ROW, streaming plan: for rows too long to keep in registers. The row is
+// walked in chunks of T * VW * U cells (each lane U vectors of VW), once per
+// reduce and once more for the full-row outputs, with O(1) state per lane;
+// each reduce's result is a row constant for the passes after it. A MAX and
+// a SUM of EXP(X - MAX(X)) share one pass through the online recurrence
+// (Tiki README, "Fused attention": running maximum and denominator, the
+// denominator rescaled by exp(m_old - m_new) whenever the maximum grows),
+// so softmax reads its row twice instead of three times. A range whose
+// values are all -inf so far keeps m = -inf and adds nothing, so masked
+// entries never produce -inf - (-inf).
+// ---------------------------------------------------------------------------
+std::string Gen::gen_row_stream() {
+    std::vector<int> rd, kd;
+    for (int d = 0; d < rank; ++d) ((k.rdims >> d) & 1u ? rd : kd).push_back(d);
+    int64_t NR = 1, NK = 1;
+    for (int d : rd) NR *= k.domain[d];
+    for (int d : kd) NK *= k.domain[d];
+    int T = 0, VW = 0, U = 4;
+    sscanf(k.plan_json.c_str(), "\"threads_per_row\":%d,\"rows_per_block\":%*d,\"vec\":%d", &T, &VW);
+    {
+        size_t at = k.plan_json.find("\"unroll\":");
+        if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"unroll\":%d", &U);
+    }
+    const int RPW = (int)k.block[0] / T;
+    const int W = T > 64 ? T / 64 : 1;
+    const int E = VW * U;
+    const int64_t CH = (int64_t)T * E;
+    const int64_t NCH = (NR + CH - 1) / CH;
+    const bool ragged = NR % CH != 0;
+    const bool single = rd.size() == 1;
+    const int R = single ? rd[0] : -1;
+    const auto pairs = online_softmax_pairs(k);
+    std::vector<int> pair_of(k.ex.size(), -1);  // max -> sum, sum -> max
+    for (auto& pr : pairs) pair_of[pr.first] = pr.second, pair_of[pr.second] = pr.first;
+    // row-constant values
+    std::vector<char> stat(k.ex.size(), 0);
+    for (size_t e = 0; e < k.ex.size(); ++e) {
+        const Ex& x = k.ex[e];
+        if (x.op == RV_BUFFER) {
+            const Leaf& L = k.leaves[x.leaf];
+            bool st_ = true;
+            for (int d : rd)
+                if (!L.zero && (L.v.strides[d] != 0 || masked(L.v, d))) st_ = false;
+            stat[e] = st_;
+        } else if (x.op == RV_CONST || x.op == RV_SUM || x.op == RV_MAX) {
+            stat[e] = 1;
+        } else {
+            stat[e] = (x.a < 0 || stat[x.a]) && (x.b < 0 || stat[x.b]) && (x.c < 0 || stat[x.c]);
+        }
+    }
+    // passes: one per reduce, a MAX and its paired SUM together
+    std::vector<std::vector<int>> passes;
+    for (size_t e = 0; e < k.ex.size(); ++e) {
+        if (!live[e] || (k.ex[e].op != RV_SUM && k.ex[e].op != RV_MAX)) continue;
+        if (k.ex[e].op == RV_SUM && pair_of[e] >= 0) continue;  // folded with its MAX
+        if (k.ex[e].op == RV_MAX && pair_of[e] >= 0)
+            passes.push_back({(int)e, pair_of[e]});
+        else
+            passes.push_back({(int)e});
+    }
+    const int nslots = (int)passes.size() + (int)pairs.size();
+    std::ostringstream b;
+    b << "  const int t = threadIdx.x, lt = t % " << T << ", lr = t / " << T << ";\n";
+    if (T > 64 && nslots) b << "  __shared__ float red[" << nslots << "][" << RPW << "][" << W << "];\n";
+    auto nexpr = [&](const std::string& v, const std::string& i) {
+        return fmt("(cb + ((%s) * %d + lt) * %d + (%s))", v.c_str(), T, VW, i.c_str());
+    };
+    auto red_idx = [&](std::vector<std::string>& idx, const std::string& n) {
+        if (single) {
+            idx[R] = n;
+            return;
+        }
+        std::string rem = n;
+        for (size_t j = rd.size(); j-- > 0;) {
+            int d = rd[j];
+            idx[d] = j ? fmt("((%s) %% %s)", rem.c_str(), lit(k.domain[d]).c_str()) : rem;
+            if (j) rem = fmt("((%s) / %s)", rem.c_str(), lit(k.domain[d]).c_str());
+        }
+    };
+    const std::string inrow = fmt("%s < %s", nexpr("q / " + std::to_string(VW), "q % " + std::to_string(VW)).c_str(),
+                                  lit(NR).c_str());
+    const int64_t NRG = (NK + RPW - 1) / RPW;
+    b << "  for (" << I << " rg = blockIdx.x; rg < " << lit(NRG) << "; rg += gridDim.x) {\n";
+    if (T > 64 && nslots) b << "    rv_lds_barrier();\n";
+    b << "    const " << I << " r = rg * " << RPW << " + lr;\n";
+    b << "    const bool rv = r < " << lit(NK) << ";\n";
+    std::vector<std::string> kidx(rank);
+    {
+        std::string rem = "r";
+        for (size_t j = kd.size(); j-- > 0;) {
+            int d = kd[j];
+            b << "    const " << I << " i" << d << " = " << (j ? fmt("%s %% %s", rem.c_str(), lit(k.domain[d]).c_str()) : rem)
+              << ";\n";
+            kidx[d] = fmt("i%d", d);
+            if (j) {
+                b << "    const " << I << " q" << d << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
+                rem = fmt("q%d", d);
+            }
+        }
+    }
+    auto V = [&](int i, const std::string& q) -> std::string {
+        return stat[i] ? fmt("e%d", i) : fmt("e%d[%s]", i, q.c_str());
+    };
+    // row constants whose inputs are ready
+    std::vector<char> done(k.ex.size(), 0);
+    auto emit_ready = [&](const std::string& ind) {
+        for (size_t e = 0; e < k.ex.size(); ++e) {
+            const Ex& x = k.ex[e];
+            if (!live[e] || !stat[e] || done[e] || x.op == RV_SUM || x.op == RV_MAX) continue;
+            if ((x.a >= 0 && !done[x.a]) || (x.b >= 0 && !done[x.b]) || (x.c >= 0 && !done[x.c])) continue;
+            std::string Vn = fmt("e%zu", e);
+            if (x.op == RV_BUFFER) {
+                const Leaf& L = k.leaves[x.leaf];
+                if (L.zero) {
+                    b << ind << "const " << vt(x.dtype) << " " << Vn << " = " << zero_of(x.dtype) << ";\n";
+                } else {
+                    std::string kc = mask_cond(L.v, kidx, kd);
+                    std::string rowok = "rv" + (kc.empty() ? std::string() : " && " + kc);
+                    b << ind << "const " << vt(x.dtype) << " " << Vn << " = (" << rowok << ") ? "
+                      << ld(L.dtype, pname(L.loc, L.dtype, false) + "[" + addr(L.v, kidx) + "]") << " : "
+                      << zero_of(x.dtype) << ";\n";
+                }
+            } else if (x.op == RV_CONST) {
+                b << ind << "const " << vt(x.dtype) << " " << Vn << " = " << const_lit(x.dtype, x.cval) << ";\n";
+            } else {
+                b << ind << "const " << vt(x.dtype) << " " << Vn << " = "
+                  << op_code(k, x, V(x.a, ""), x.b >= 0 ? V(x.b, "") : "", x.c >= 0 ? V(x.c, "") : "") << ";\n";
+            }
+            done[e] = 1;
+        }
+    };
+    // the full-row values a set of roots needs, in order
+    auto needed = [&](const std::vector<int>& roots) {
+        std::vector<char> need(k.ex.size(), 0);
+        std::function<void(int)> go = [&](int e) {
+            if (e < 0 || need[e] || stat[e]) return;
+            need[e] = 1;
+            go(k.ex[e].a), go(k.ex[e].b), go(k.ex[e].c);
+        };
+        for (int r0 : roots) go(r0);
+        return need;
+    };
+    // one chunk's full-row values (E cells per lane). Loads before the last
+    // pass are plain (cacheable): the row is read again by a later pass.
+    auto emit_chunk = [&](const std::vector<char>& need, const std::string& ind, bool last) {
+        for (size_t e = 0; e < k.ex.size(); ++e) {
+            if (!need[e]) continue;
+            const Ex& x = k.ex[e];
+            std::string Vn = fmt("e%zu", e);
+            if (x.op == RV_BUFFER) {
+                const Leaf& L = k.leaves[x.leaf];
+                std::string P = pname(L.loc, L.dtype, false);
+                std::string kc = mask_cond(L.v, kidx, kd);
+                std::string rowok = "rv" + (kc.empty() ? std::string() : " && " + kc);
+                b << ind << vt(x.dtype) << " " << Vn << "[" << E << "];\n";
+                b << ind << "for (int v = 0; v < " << U << "; ++v) {\n";
+                b << ind << "  const " << I << " n0 = " << nexpr("v", "0") << ";\n";
+                std::vector<std::string> idx = kidx;
+                if (single && leaf_vec_ok(L, R, VW)) {
+                    idx[R] = "n0";
+                    std::string mc = masked(L.v, R) ? fmt(" && n0 >= %s && n0 + %d <= %s", lit(L.v.mask_lo[R]).c_str(), VW,
+                                                          lit(L.v.mask_hi[R]).c_str())
+                                                    : "";
+                    b << ind << "  if (" << rowok << mc << " && n0 + " << VW << " <= " << lit(NR) << ") {\n";
+                    const std::string ptr = P + " + " + addr(L.v, idx);
+                    b << ind << "    const rv_pack<" << st(L.dtype) << ", " << VW << "> p = "
+                      << (last ? vload(L, VW, ptr) : "rv_ldv<" + st(L.dtype) + ", " + std::to_string(VW) + ">(" + ptr + ")")
+                      << ";\n";
+                    b << ind << "    for (int i = 0; i < " << VW << "; ++i) " << Vn << "[v * " << VW << " + i] = " << ld(L.dtype, "p.v[i]")
+                      << ";\n";
+                    b << ind << "  } else\n";
+                }
+                b << ind << "  for (int i = 0; i < " << VW << "; ++i) {\n";
+                b << ind << "    const " << I << " n = n0 + i;\n";
+                red_idx(idx, "n");
+                std::string mc = mask_cond(L.v, idx, rd);
+                b << ind << "    " << Vn << "[v * " << VW << " + i] = (" << rowok << " && n < " << lit(NR)
+                  << (mc.empty() ? "" : " && " + mc) << ") ? " << ld(L.dtype, P + "[" + addr(L.v, idx) + "]") << " : "
+                  << zero_of(L.dtype == RV_BF16 || L.dtype == RV_F16 ? RV_F32 : L.dtype) << ";\n";
+                b << ind << "  }\n" << ind << "}\n";
+                continue;
+            }
+            b << ind << vt(x.dtype) << " " << Vn << "[" << E << "];\n";
+            b << ind << "for (int q = 0; q < " << E << "; ++q) " << Vn << "[q] = "
+              << op_code(k, x, V(x.a, "q"), x.b >= 0 ? V(x.b, "q") : "", x.c >= 0 ? V(x.c, "q") : "") << ";\n";
+        }
+    };
+    const std::string guard = ragged ? "if (" + inrow + ") " : "";
+    int slot = 0;
+    emit_ready("    ");
+    for (const auto& pass : passes) {
+        const int r0 = pass[0];
+        const Ex& R0 = k.ex[r0];
+        const bool online = pass.size() == 2;
+        // operand of the fold: the MAX's operand X for the online pass
+        const int X = R0.a;
+        b << "    // pass: " << (online ? "online MAX + SUM(EXP(x - max))" : (R0.op == RV_SUM ? "SUM" : "MAX")) << "\n";
+        if (online)
+            b << "    float om = -__builtin_inff(), ol = 0.0f;\n";
+        else
+            b << "    float acc" << r0 << " = " << (R0.op == RV_SUM ? "0.0f" : "(-__builtin_inff())") << ";\n";
+        b << "    for (" << I << " c = 0; c < " << lit(NCH) << "; ++c) {\n";
+        b << "      const " << I << " cb = c * " << lit(CH) << ";\n";
+        emit_chunk(needed({X}), "      ", false);
+        const std::string xv = V(X, "q");
+        if (online) {
+            b << "      float cm = -__builtin_inff();\n";
+            b << "      for (int q = 0; q < " << E << "; ++q) " << guard << "cm = rv_maxf(cm, " << xv << ");\n";
+            b << "      const float mn = rv_maxf(om, cm);\n";
+            b << "      const float alpha = (om == mn) ? 1.0f : expf(om - mn);\n";
+            b << "      float ps = 0.0f;\n";
+            b << "      if (mn != -__builtin_inff())\n";
+            b << "        for (int q = 0; q < " << E << "; ++q) " << guard << "ps = ps + expf(" << xv << " + (-mn));\n";
+            b << "      ol = ol * alpha + ps;\n      om = mn;\n";
+        } else if (R0.op == RV_SUM) {
+            b << "      for (int q = 0; q < " << E << "; ++q) " << guard << "acc" << r0 << " = acc" << r0 << " + " << xv << ";\n";
+        } else {
+            b << "      for (int q = 0; q < " << E << "; ++q) " << guard << "acc" << r0 << " = rv_maxf(acc" << r0 << ", " << xv
+              << ");\n";
+        }
+        b << "    }\n";
+        const int g = std::min(T, 64);
+        if (online) {
+            b << "    for (int o = " << g / 2 << "; o >= 1; o >>= 1) rv_online_merge(om, ol, __shfl_xor(om, o, 64), __shfl_xor(ol, o, 64));\n";
+            if (T > 64) {
+                b << "    if ((t & 63) == 0) { red[" << slot << "][lr][lt >> 6] = om; red[" << slot + 1 << "][lr][lt >> 6] = ol; }\n";
+                b << "    rv_lds_barrier();\n";
+                b << "    om = red[" << slot << "][lr][0];\n    ol = red[" << slot + 1 << "][lr][0];\n";
+                b << "    for (int w = 1; w < " << W << "; ++w) rv_online_merge(om, ol, red[" << slot << "][lr][w], red[" << slot + 1
+                  << "][lr][w]);\n";
+                slot += 2;
+            }
+            b << "    const float e" << r0 << " = om;\n";
+            b << "    const float e" << pass[1] << " = ol;\n";
+            done[r0] = done[pass[1]] = 1;
+        } else {
+            b << "    float e" << r0 << ";\n    {\n      float acc = acc" << r0 << ";\n";
+            b << "      acc = rv_group_" << (R0.op == RV_SUM ? "sum" : "max") << "<" << g << ">(acc);\n";
+            if (T > 64) {
+                b << "      if ((t & 63) == 0) red[" << slot << "][lr][lt >> 6] = acc;\n      rv_lds_barrier();\n";
+                b << "      acc = red[" << slot << "][lr][0];\n";
+                for (int w = 1; w < W; ++w)
+                    b << "      acc = " << (R0.op == RV_SUM ? fmt("acc + red[%d][lr][%d]", slot, w)
+                                                           : fmt("rv_maxf(acc, red[%d][lr][%d])", slot, w))
+                      << ";\n";
+                ++slot;
+            }
+            b << "      e" << r0 << " = " << round_to(R0.dtype, "acc") << ";\n    }\n";
+            done[r0] = 1;
+        }
+        emit_ready("    ");
+    }
+    // full-row outputs
+    std::vector<int> full_roots;
+    for (const Store& s_ : k.stores) {
+        bool sstat = true;
+        for (int d : rd)
+            if (s_.v.strides[d] != 0) sstat = false;
+        if (!sstat) full_roots.push_back(s_.ex);
+    }
+    if (!full_roots.empty()) {
+        b << "    // pass: outputs\n";
+        b << "    for (" << I << " c = 0; c < " << lit(NCH) << "; ++c) {\n";
+        b << "      const " << I << " cb = c * " << lit(CH) << ";\n";
+        emit_chunk(needed(full_roots), "      ", true);
+        for (const Store& s_ : k.stores) {
+            bool sstat = true;
+            for (int d : rd)
+                if (s_.v.strides[d] != 0) sstat = false;
+            if (sstat) continue;
+            std::string P = pname(s_.loc, s_.dtype, true);
+            std::string val = V(s_.ex, fmt("v * %d + i", VW));
+            b << "      for (int v = 0; v < " << U << "; ++v) {\n";
+            b << "        const " << I << " n0 = " << nexpr("v", "0") << ";\n";
+            std::vector<std::string> idx = kidx;
+            bool vec = single && s_.v.strides[R] == 1 && s_.v.offset % VW == 0;
+            for (int d : kd)
+                if (k.domain[d] > 1 && s_.v.strides[d] % VW) vec = false;
+            if (vec) {
+                idx[R] = "n0";
+                b << "        if (rv && n0 + " << VW << " <= " << lit(NR) << ") {\n          rv_pack<" << st(s_.dtype) << ", " << VW
+                  << "> p;\n";
+                b << "          for (int i = 0; i < " << VW << "; ++i) p.v[i] = " << sv(s_.dtype, val) << ";\n";
+                b << "          " << vstore(s_.dtype, VW, P + " + " + addr(s_.v, idx), "p") << ";\n";
+                b << "        } else\n";
+            }
+            b << "        for (int i = 0; i < " << VW << "; ++i) {\n          const " << I << " n = n0 + i;\n";
+            red_idx(idx, "n");
+            b << "          if (rv && n < " << lit(NR) << ") " << P << "[" << addr(s_.v, idx) << "] = " << sv(s_.dtype, val)
+              << ";\n";
+            b << "        }\n      }\n";
+        }
+        b << "    }\n";
+    }
+    for (const Store& s_ : k.stores) {
+        bool sstat = true;
+        for (int d : rd)
+            if (s_.v.strides[d] != 0) sstat = false;
+        if (!sstat) continue;
+        std::string P = pname(s_.loc, s_.dtype, true);
+        b << "    if (lt == 0 && rv) " << P << "[" << addr(s_.v, kidx) << "] = " << sv(s_.dtype, V(s_.ex, "0")) << ";\n";
+    }
+    b << "  }\n";
+    return b.str();
+}
+
+// ---------------------------------------------------------------------------
 // REDUCE, cells plan: one lane per output cell (lanes walk the dim that is
 // stride-1 in the most buffers), the reduce dims walked in ascending order
 // inside the lane, so every cell folds exactly as the serial nest does.
@@ -1180,7 +1488,7 @@ std::string Gen::gen() {
     if (k.plan == "empty") return "";
     switch (k.cls) {
         case KClass::EW: body = k.plan == "tiled2d" ? gen_tiled() : gen_rowmajor(); break;
-        case KClass::ROW: body = gen_row(); break;
+        case KClass::ROW: body = k.plan == "row_stream" ? gen_row_stream() : gen_row(); break;
         case KClass::REDUCE: body = gen_cells(); break;
         case KClass::FOLD: body = gen_fold(); break;
         case KClass::MFMA: {

@@ -153,6 +153,10 @@ void device_check(int device);
 
 std::string json_view(const rv_view& v);
 std::vector<Loc> kernel_param_locs(const Program& p, const Kernel& k);
+// ROW kernels: (MAX, SUM) value pairs whose SUM adds EXP(X - MAX(X)) over
+// float32, which the streaming plan folds in one pass with the online
+// max/denominator recurrence.
+std::vector<std::pair<int, int>> online_softmax_pairs(const Kernel& k);
 bool mfma_supported(const Shape& dom, const rv_view& a, const rv_view& b, std::string* why);
 
 }  // namespace rv

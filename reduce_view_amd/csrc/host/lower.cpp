@@ -154,6 +154,29 @@ bool mfma_supported(const Shape& dom, const rv_view& a, const rv_view& b, std::s
     return true;
 }
 
+std::vector<std::pair<int, int>> online_softmax_pairs(const Kernel& k) {
+    std::vector<std::pair<int, int>> out;
+    auto f32 = [&](int e) { return e >= 0 && k.ex[e].dtype == RV_F32; };
+    for (size_t s = 0; s < k.ex.size(); ++s) {
+        const Ex& S = k.ex[s];
+        if (S.op != RV_SUM || !f32((int)s) || S.a < 0) continue;
+        const Ex& Ex_ = k.ex[S.a];
+        if (Ex_.op != RV_EXP || !f32(S.a) || Ex_.a < 0) continue;
+        const Ex& A = k.ex[Ex_.a];
+        if (A.op != RV_ADD || !f32(Ex_.a)) continue;
+        for (int side = 0; side < 2; ++side) {
+            const int X = side ? A.b : A.a, N = side ? A.a : A.b;
+            if (X < 0 || N < 0 || k.ex[N].op != RV_NEG) continue;
+            const int M = k.ex[N].a;
+            if (M < 0 || k.ex[M].op != RV_MAX || k.ex[M].a != X || !f32(M) || !f32(X)) continue;
+            if (k.ex[M].axes != S.axes) continue;
+            out.emplace_back(M, (int)s);
+            break;
+        }
+    }
+    return out;
+}
+
 static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
     char buf[512];
     switch (k.cls) {
@@ -336,6 +359,31 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
         k.block[0] = (unsigned)block;
         k.lane_dim = rank - 1;
         int nv = (int)((NR + (int64_t)T * vw - 1) / ((int64_t)T * vw));
+        // a row longer than about 32 cells per lane at 1024 lanes does not
+        // fit in registers: stream it (RV_ROW_STREAM=1 forces, =0 forbids)
+        const int stream_env = env_int("RV_ROW_STREAM", -1);
+        if (stream_env == 1 || (stream_env != 0 && (int64_t)nv * vw > 32)) {
+            k.plan = "row_stream";
+            const int U = 4;
+            k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>(nrg, env_int("RV_ROW_GRID", 1 << 30)));
+            k.block[0] = (unsigned)block;
+            k.lane_dim = rank - 1;
+            const int64_t ch = (int64_t)T * vw * U;
+            const auto pairs = online_softmax_pairs(k);
+            int nred = 0;
+            for (auto& e : k.ex)
+                if (e.op == RV_SUM || e.op == RV_MAX) ++nred;
+            k.lds = T > 64 ? (size_t)(nred + pairs.size()) * rpw * (T / 64) * 4 : 0;
+            std::string on = "[";
+            for (size_t i = 0; i < pairs.size(); ++i)
+                on += fmt("%s[%d,%d]", i ? "," : "", pairs[i].first, pairs[i].second);
+            on += "]";
+            snprintf(buf, sizeof buf, "\"threads_per_row\":%d,\"rows_per_block\":%d,\"vec\":%d,\"unroll\":%d,"
+                     "\"chunks\":%lld,\"row_len\":%lld,\"rows\":%lld,\"online\":%s", T, rpw, vw, U,
+                     (long long)((NR + ch - 1) / ch), (long long)NR, (long long)NK, on.c_str());
+            k.plan_json = buf;
+            return;
+        }
         int nred = 0;
         for (auto& e : k.ex)
             if (e.op == RV_SUM || e.op == RV_MAX) ++nred;

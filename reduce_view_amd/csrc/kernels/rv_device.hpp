@@ -99,6 +99,19 @@ __device__ __forceinline__ float rv_group_sum(float v) {
 // it is reduced.
 __device__ __forceinline__ void rv_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Merge of two online-softmax states (running maximum m, denominator l
+// relative to m): both denominators are rescaled to the larger maximum. The
+// expression is symmetric in its two operands, so the lanes of a butterfly
+// end with the same bits; a state whose maximum is already the result keeps
+// its denominator exactly (no -inf - (-inf) for empty or masked ranges).
+__device__ __forceinline__ void rv_online_merge(float& m, float& l, float m2, float l2) {
+    const float mn = rv_maxf(m, m2);
+    const float a1 = (m == mn) ? 1.0f : expf(m - mn);
+    const float a2 = (m2 == mn) ? 1.0f : expf(m2 - mn);
+    l = l * a1 + l2 * a2;
+    m = mn;
+}
+
 template <int W>
 __device__ __forceinline__ float rv_group_max(float v) {
 #pragma unroll
