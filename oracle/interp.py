@@ -223,6 +223,15 @@ def infer(spec) -> list:
             out.append((tuple(1 if d in axes else s for d, s in enumerate(shp)), dt))
         elif op == "CONTIGUOUS":
             out.append(out[src[0]])
+        elif op == "CUSTOM" and nd.get("kind") == "sdpa_fwd":
+            (sq, dq), (sk, dk), (sv, dv) = out[src[0]], out[src[1]], out[src[2]]
+            if len(sq) != 3 or sk != sv or len(sk) != 3 or sq[0] != sk[0] or sq[2] != sk[2] or \
+                    (dq, dk, dv) != ("bf16", "bf16", "bf16"):
+                raise OracleError(f"node {i}: sdpa_fwd of {sq}/{dq}, {sk}/{dk}, {sv}/{dv}")
+            if nd["out"] == 0:
+                out.append((sq, nd["dtype"]))
+            else:
+                out.append(((sq[0], sq[1], 1), "f32"))
         else:
             raise OracleError(f"node {i}: op {op} is not evaluated by this oracle")
     return out
@@ -356,6 +365,51 @@ def _reduce(op: str, x: np.ndarray, dt: str, axes) -> np.ndarray:
     return _narrow(res, dt).reshape(out_shape)
 
 
+def sdpa_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool, out_dtype: str = "f32",
+             block: int = 64):
+    """Fused attention forward evaluated as the composition of primitives it
+    stands for (limn README, "The op set": a device without the CUSTOM
+    kernel composes it from primitives, and the numpy device's evaluation
+    is the reference). bfloat16 q (H, Tq, D), k and v (H, Tk, D); per head
+    and block of query rows, every step one primitive with its rounding:
+      S = SUM_d CAST(q) * CAST(k)        (products exact, folded in order)
+      S = S * CONST(scale)               (scale rounded to float32)
+      S = S where key j <= query i, else -inf   (causal only; exact)
+      m = MAX_j S;  e = EXP(S + NEG(m));  s = SUM_j e;  P = e * RECIP(s)
+      O = SUM_j P * CAST(v)              (folded over keys in order)
+      L = m + LOG(s)                     (the row's logsumexp)
+    Returns (O in ``out_dtype``, L float32 (H, Tq, 1))."""
+    H, Tq, D = q.shape
+    Tk = k.shape[1]
+    sc = np.float32(scale).reshape(1, 1, 1)
+    O = np.empty((H, Tq, D), np.float32)
+    L = np.empty((H, Tq, 1), np.float32)
+    for h in range(H):
+        kf = bf16_to_f32(k[h])[None, :, :]
+        vf = bf16_to_f32(v[h])[None, :, :]
+        for i0 in range(0, Tq, block):
+            i1 = min(Tq, i0 + block)
+            qf = bf16_to_f32(q[h, i0:i1])[:, None, :]
+            prod = _binary("MUL", np.broadcast_to(qf, (i1 - i0, Tk, D)).copy(),
+                           np.broadcast_to(kf, (i1 - i0, Tk, D)).copy(), "f32")
+            S = _reduce("SUM", prod, "f32", (2,))[:, :, 0]
+            S = _binary("MUL", S, np.broadcast_to(sc[0], S.shape).copy(), "f32")
+            if causal:
+                qi = np.arange(i0, i1)[:, None]
+                kj = np.arange(Tk)[None, :]
+                S = np.where(kj <= qi, S, np.float32(-np.inf)).astype(np.float32)
+            m = _reduce("MAX", S, "f32", (1,))
+            e = _unary("EXP", _binary("ADD", S, np.broadcast_to(_unary("NEG", m, "f32"), S.shape).copy(), "f32"),
+                       "f32")
+            ssum = _reduce("SUM", e, "f32", (1,))
+            P = _binary("MUL", e, np.broadcast_to(_unary("RECIP", ssum, "f32"), e.shape).copy(), "f32")
+            pv = _binary("MUL", np.broadcast_to(P[:, :, None], (i1 - i0, Tk, D)).copy(),
+                         np.broadcast_to(vf, (i1 - i0, Tk, D)).copy(), "f32")
+            O[h, i0:i1] = _reduce("SUM", pv, "f32", (1,))[:, 0, :]
+            L[h, i0:i1] = _binary("ADD", m, _unary("LOG", ssum, "f32"), "f32")
+    return (O if out_dtype == "f32" else _cast(O, "f32", out_dtype)), L
+
+
 # ---------------------------------------------------------------------------
 # the interpreter
 # ---------------------------------------------------------------------------
@@ -375,6 +429,7 @@ class Interpreter:
         self.max_elems = max_elems
         self.slab_elems = slab_elems
         self.memo: dict[int, np.ndarray] = {}
+        self.memo_custom: dict = {}
 
     def size(self, i: int) -> int:
         return int(np.prod(self.meta[i][0], dtype=np.int64))
@@ -445,6 +500,23 @@ class Interpreter:
                 r = _reduce(op, np.ascontiguousarray(arg(src[0])), sdt, axes)
         elif op == "CONTIGUOUS":
             r = np.ascontiguousarray(arg(src[0])).copy()
+        elif op == "CUSTOM":
+            if rows is not None:
+                raise OracleError("a CUSTOM node is not evaluated in slabs")
+            key = ("sdpa_fwd", tuple(src), nd["scale"], nd["causal"])
+            if key not in self.memo_custom:
+                self.memo_custom[key] = {}
+            got = self.memo_custom[key]
+            if nd["out"] not in got:
+                o, lse = sdpa_fwd(np.asarray(self.value(src[0])), np.asarray(self.value(src[1])),
+                                  np.asarray(self.value(src[2])), nd["scale"], nd["causal"],
+                                  dt if nd["out"] == 0 else "f32")
+                got[0] = o if nd["out"] == 0 else got.get(0)
+                got[1] = lse
+            r = got[nd["out"]]
+            if r is None:  # O was asked in another dtype than a sibling's
+                r = sdpa_fwd(np.asarray(self.value(src[0])), np.asarray(self.value(src[1])),
+                             np.asarray(self.value(src[2])), nd["scale"], nd["causal"], dt)[0]
         else:
             raise OracleError(f"op {op}")
         r = np.ascontiguousarray(r) if op not in ("VIEW", "BUFFER") else r

@@ -96,6 +96,19 @@ class Spec:
     def max(self, x, axes): return self._add(op="MAX", src=(x,), axes=tuple(axes))
     def contiguous(self, x): return self._add(op="CONTIGUOUS", src=(x,))
 
+    # the one CUSTOM kernel: fused attention forward --------------------
+    def sdpa(self, q, k, v, scale: float, causal: bool = False, out_dtype: str = "f32"):
+        """Fused attention forward as CUSTOM ``sdpa_fwd`` (limn README, "The op
+        set", escape hatch: a kernel a device supplies whole, one node per
+        output, the siblings sharing their sources). q (H, Tq, D), k and v
+        (H, Tk, D), all bfloat16. Returns the ids of O = softmax(scale * q k^T,
+        keys j > query i masked when ``causal``) v, shape (H, Tq, D), and of
+        L, the logsumexp of each query row, shape (H, Tq, 1) float32."""
+        kw = dict(kind="sdpa_fwd", src=(q, k, v), scale=float(scale), causal=bool(causal))
+        o = self._add(op="CUSTOM", out=0, dtype=out_dtype, **kw)
+        lse = self._add(op="CUSTOM", out=1, dtype="f32", **kw)
+        return o, lse
+
     def output(self, *ids) -> None:
         self.outputs.extend(ids)
 
@@ -344,6 +357,27 @@ def copy(rows: int, cols: int) -> Spec:
     x = g.buffer("X", (rows, cols), "f32")
     g.output(g.contiguous(x))
     return g
+
+
+def attention(h: int, tq: int, tk: int, d: int, causal: bool = True, out_dtype: str = "f32",
+              outputs: str = "ol") -> Spec:
+    """Fused attention forward over bfloat16 q (h, tq, d), k, v (h, tk, d),
+    scale 1/sqrt(d): outputs O (and L when ``outputs`` has an 'l')."""
+    g = Spec(f"attention_{h}x{tq}x{tk}x{d}{'_causal' if causal else ''}")
+    q = g.buffer("Q", (h, tq, d), "bf16")
+    k = g.buffer("K", (h, tk, d), "bf16")
+    v = g.buffer("V", (h, tk, d), "bf16")
+    o, lse = g.sdpa(q, k, v, 1.0 / float(np.sqrt(d)), causal, out_dtype)
+    g.output(*([o] if "o" in outputs else []), *([lse] if "l" in outputs else []))
+    return g
+
+
+def inputs_attention(h: int, tq: int, tk: int, d: int, seed: int = 6) -> dict:
+    """Q, K, V ~ N(0, 1) drawn in that order, rounded to bfloat16."""
+    rng = np.random.default_rng(seed)
+    return {"Q": to_bf16_bits(_f32(rng.standard_normal((h, tq, d)))),
+            "K": to_bf16_bits(_f32(rng.standard_normal((h, tk, d)))),
+            "V": to_bf16_bits(_f32(rng.standard_normal((h, tk, d))))}
 
 
 def unary_map(op: str, n: int, dtype: str = "f32") -> Spec:

@@ -517,3 +517,81 @@ def test_planted_unbiased_variance_is_caught(monkeypatch):
     with pytest.raises(AssertionError) as e:
         test_layernorm_mean_is_exact_and_matches_torch_float64()
     assert seen["n"] >= 2
+
+
+# ---------------------------------------------------------------------------
+# fused attention forward (CUSTOM sdpa_fwd), evaluated as its primitives
+# ---------------------------------------------------------------------------
+
+def _attention_f64(q, k, v, scale, causal):
+    """Textbook attention in float64, written independently of the oracle:
+    softmax(scale q k^T) v with the row max subtracted, and the logsumexp."""
+    qd, kd, vd = (interp.bf16_to_f32(a).astype(np.float64) for a in (q, k, v))
+    s = np.einsum("hid,hjd->hij", qd, kd) * scale
+    if causal:
+        s = np.where(np.arange(s.shape[2])[None, None, :] <= np.arange(s.shape[1])[None, :, None], s, -np.inf)
+    m = s.max(axis=2, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=2, keepdims=True)
+    return (e / z) @ vd, m + np.log(z)
+
+
+@pytest.mark.parametrize("h,tq,tk,d,causal", [(2, 37, 37, 32, True), (3, 20, 45, 64, False), (1, 64, 64, 16, True)])
+def test_sdpa_matches_float64_attention(h, tq, tk, d, causal):
+    spec = synth.attention(h, tq, tk, d, causal)
+    inp = synth.inputs_attention(h, tq, tk, d)
+    o, lse = oracle.run(spec, inp)
+    o64, l64 = _attention_f64(inp["Q"], inp["K"], inp["V"], 1.0 / np.sqrt(d), causal)
+    # float32 per primitive against float64: a few hundred ulps at most here
+    assert np.abs(o - o64).max() <= 1e-5 * np.abs(o64).max()
+    assert np.abs(lse - l64).max() <= 1e-5 * (np.abs(l64).max() + 1)
+
+
+def test_sdpa_closed_forms():
+    h, t, d = 2, 16, 32
+    inp = synth.inputs_attention(h, t, t, d)
+    o, lse = oracle.run(synth.attention(h, t, t, d, causal=True), inp)
+    # causal row 0 sees key 0 only: O = V[0] and L = the one scaled score
+    assert o[:, 0].tobytes() == interp.bf16_to_f32(inp["V"][:, 0]).tobytes()
+    s00 = (interp.bf16_to_f32(inp["Q"][:, 0]) * interp.bf16_to_f32(inp["K"][:, 0])).astype(np.float32)
+    s00 = np.array([interp._reduce("SUM", s00[i:i + 1], "f32", (1,))[0, 0] for i in range(h)], np.float32)
+    assert lse[:, 0, 0].tobytes() == (s00 * np.float32(1.0 / np.sqrt(d))).astype(np.float32).tobytes()
+    # all scores equal (K = 0): uniform weights, O is the mean of V's rows and
+    # L is log(Tk) (sum of ones is exact, 1/Tk exact for a power of two)
+    inp0 = dict(inp, K=np.zeros_like(inp["K"]))
+    o, lse = oracle.run(synth.attention(h, t, t, d, causal=False), inp0)
+    vm = interp.bf16_to_f32(inp["V"]).astype(np.float64).mean(axis=1)
+    assert np.abs(o - vm[:, None, :]).max() <= 4 * gamma(t - 1) * np.abs(interp.bf16_to_f32(inp["V"])).sum(axis=1).max() / t
+    assert np.all(lse == np.float32(np.log(np.float32(t))))
+
+
+def test_sdpa_large_scores_need_the_max_shift():
+    # scores near 1e4: exp without the max shift overflows; with it the
+    # result is finite and matches float64
+    h, t, d = 1, 24, 32
+    inp = synth.inputs_attention(h, t, t, d)
+    inp["Q"] = synth.to_bf16_bits(interp.bf16_to_f32(inp["Q"]) * np.float32(300.0))
+    o, lse = oracle.run(synth.attention(h, t, t, d, causal=False), inp)
+    o64, l64 = _attention_f64(inp["Q"], inp["K"], inp["V"], 1.0 / np.sqrt(d), False)
+    assert np.all(np.isfinite(o)) and np.abs(o - o64).max() <= 1e-4 * np.abs(o64).max()
+    assert np.abs(lse - l64).max() <= 1e-5 * np.abs(l64).max()
+
+
+def test_planted_transposed_attention_scores_are_caught(monkeypatch):
+    real = interp.sdpa_fwd
+
+    def bad(q, k, v, scale, causal, out_dtype="f32", block=64):
+        # softmax over the wrong axis: swap the roles of q and k
+        return real(k, q, v, scale, causal, out_dtype, block) if q.shape == k.shape else real(q, k, v, scale, causal,
+                                                                                               out_dtype, block)
+    monkeypatch.setattr(interp, "sdpa_fwd", bad)
+    with pytest.raises(AssertionError):
+        test_sdpa_matches_float64_attention(2, 37, 37, 32, True)
+
+
+def test_planted_missing_causal_mask_is_caught(monkeypatch):
+    real = interp.sdpa_fwd
+    monkeypatch.setattr(interp, "sdpa_fwd", lambda q, k, v, scale, causal, out_dtype="f32", block=64:
+                        real(q, k, v, scale, False, out_dtype, block))
+    with pytest.raises(AssertionError):
+        test_sdpa_closed_forms()
