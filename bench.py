@@ -5,8 +5,8 @@ float32 elementwise chain WHERE(CMPLT(a, b), a*b, EXP(-a)) + c with b a
 permuted View and c a stride-0 row vector, the same chain with a read through
 a shrink-then-pad masked View, and a standalone 4096 x 4096 transpose. One
 step runs all three programs once. ``--workload`` selects one of the other
-kernels instead (softmax, softmax_long, rmsnorm, layernorm, gemm, matmul64,
-copy).
+kernels instead (softmax, softmax_long, rmsnorm, layernorm, gemm, attention,
+matmul64, copy).
 
 Inputs are seeded, synthetic and already resident in HBM when timing starts;
 several input sets rotate so that consecutive launches never re-read data the
@@ -87,6 +87,12 @@ def workloads():
             programs=[("gemm_relu2_sum", synth.gemm_relu2_sum(4096, 4096, 4096), 2 * 4096 ** 3)],
             inputs=lambda seed: synth.inputs_gemm(4096, 4096, 4096, seed),
             unit="TFLOP/s", dtype="bf16", bound="mfma", seed=5),
+        "attention": dict(
+            desc=("fused attention forward (CUSTOM sdpa_fwd), 6 heads x 8192 tokens x 32, causal, bf16 q/k/v, "
+                  "f32 O and logsumexp; q, k, v ~ N(0,1), seed 6"),
+            programs=[("attention", synth.attention(6, 8192, 8192, 32, True), 4 * 32 * 6 * 8192 * 8193 // 2)],
+            inputs=lambda seed: synth.inputs_attention(6, 8192, 8192, 32, seed),
+            unit="TFLOP/s", dtype="bf16", bound="mfma", seed=6),
         "copy": dict(
             desc="plain 4096x4096 fp32 copy (bandwidth reference; not a hot-path workload)",
             programs=[("copy", synth.copy(4096, 4096), 2 * 4096 * 4096 * F32)],
@@ -141,6 +147,17 @@ def _cpu_baseline(wl, name, budget_s):
         t_wall = time.perf_counter() - t
         work = 2.0 * rows * 4096 * 4096
         sample = f"{rows} of 4096 rows of A (the contraction's first {rows} row slabs), full B"
+    elif name == "attention":
+        rows, t, d = 256, 8192, 32
+        inp = synth.inputs_attention(6, t, t, d, 6)
+        sub = {"Q": inp["Q"][:1, t - rows:], "K": inp["K"][:1], "V": inp["V"][:1]}
+        spec = synth.attention(1, rows, t, d, causal=False)
+        t0 = time.perf_counter()
+        oracle.run(spec, sub)
+        t_wall = time.perf_counter() - t0
+        work = 4.0 * d * rows * t
+        sample = (f"the last {rows} query rows of head 0 against all {t} keys (a causal row there sees all "
+                  "but a few of them), full composition")
     else:
         inp = wl["inputs"](wl["seed"])
         done = 0

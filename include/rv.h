@@ -70,8 +70,8 @@ typedef enum rv_dtype {
 } rv_dtype;
 
 /* limn README, "The op set". CMPLT yields RV_I8 0/1; WHERE treats a nonzero
- * condition as true. GATHER, SCATTER, ASSIGN and CUSTOM are declined with
- * RV_E_UNSUPPORTED_OP. */
+ * condition as true. GATHER, SCATTER and ASSIGN are declined with
+ * RV_E_UNSUPPORTED_OP; so is CUSTOM unless it names RV_CUSTOM_SDPA_FWD. */
 typedef enum rv_op {
     RV_BUFFER = 0, RV_CONST = 1, RV_VIEW = 2,
     RV_NEG = 3, RV_EXP = 4, RV_LOG = 5, RV_SQRT = 6, RV_RECIP = 7, RV_CAST = 8,
@@ -79,6 +79,30 @@ typedef enum rv_op {
     RV_SUM = 13, RV_MAX = 14, RV_CONTIGUOUS = 15,
     RV_GATHER = 16, RV_SCATTER = 17, RV_ASSIGN = 18, RV_CUSTOM = 19
 } rv_op;
+
+/* CUSTOM kernels (limn README, "The op set", escape hatch: a kernel the
+ * device supplies whole; a kernel with several outputs is one node per
+ * output, the nodes sharing their sources).
+ *
+ * RV_CUSTOM_SDPA_FWD, in `rv_node.buf`: fused attention forward (limn README,
+ * "The op set": the forward saves one number per row besides the answer,
+ * the logsumexp L; Tiki README, "Fused attention": running maximum,
+ * denominator and accumulator per query row over tiles of keys).
+ *   src[0..2] = q (H, Tq, D), k (H, Tk, D), v (H, Tk, D), all RV_BF16, with
+ *               D one of 32, 64, 128; H <= 65535.
+ *   cval       = the score scale (finite).
+ *   reduce_axes = RV_SDPA_CAUSAL (key j hidden from query i when j > i) OR'd
+ *               with (output index << 16): output 0 is
+ *               O = softmax(scale * q k^T) v, shape (H, Tq, D), dtype RV_F32 or
+ *               RV_BF16; output 1 is L = the row logsumexp (max + log of the
+ *               sum), shape (H, Tq, 1), RV_F32.
+ * Nodes with the same sources, scale and causal flag are one kernel launch.
+ * The probabilities enter the second contraction rounded to bfloat16 (the
+ * matrix cores' operand type); the result agrees with the primitive
+ * composition (scores, max-shifted softmax, contraction over keys) within
+ * the bound that rounding implies. */
+#define RV_CUSTOM_SDPA_FWD 1
+#define RV_SDPA_CAUSAL 1u
 
 /* A View (limn README, "Architecture"): cell i of `shape` reads element
  * offset + sum_d i_d * strides[d] of its source's row-major storage when

@@ -74,7 +74,13 @@ def check_device_header(verbose: bool = False) -> None:
                 "  rv_gemm_pp_bf16<true, 1, E>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(512) chk11(const unsigned short* a, "
                 "const unsigned short* b, float* p) {\n"
-                "  rv_gemm_pp_bf16<false, 0, E, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n")
+                "  rv_gemm_pp_bf16<false, 0, E, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(512) chk12(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
+                "float* l) { rv_attn_fwd_bf16<32, true, false>(q, k, v, o, l, 1000, 1000, 0.25f); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(512) chk13(const unsigned short* q, const unsigned short* k, const unsigned short* v, "
+                "unsigned short* o, float* l) { rv_attn_fwd_bf16<64, false, true>(q, k, v, o, l, 100, 333, 0.18f); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(512) chk14(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
+                "float* l) { rv_attn_fwd_bf16<128, true, false>(q, k, v, o, nullptr, 130, 130, 0.1f); }\n")
     cmd = [HIPCC] + GPU_FLAGS + ["--cuda-device-only", "-c", tu, "-o", os.path.join(out_dir, "device_check.o")]
     if verbose:
         print(" ".join(cmd))

@@ -277,6 +277,7 @@ struct Gen {
     std::string gen_tiled();
     std::string gen_row();
     std::string gen_row_stream();
+    std::string gen_attn();
     std::string gen_cells();
     std::string gen_fold();
     std::string gen_gemm();
@@ -1384,6 +1385,37 @@ std::string Gen::gen_cells() {
     return b.str();
 }
 
+// ATTN: the fused attention forward skeleton (kernels/rv_device.hpp) with
+// the head width, causal flag, output dtype and the base-2 score scale
+// baked in.
+std::string Gen::gen_attn() {
+    const int64_t Tq = k.domain[1], D = k.domain[2];
+    const int64_t Tk = k.leaves[1].v.shape[1];
+    const std::string q = pname(k.leaves[0].loc, RV_BF16, false);
+    const std::string kp = pname(k.leaves[1].loc, RV_BF16, false);
+    const std::string v = pname(k.leaves[2].loc, RV_BF16, false);
+    std::string o = "nullptr", l = "nullptr";
+    int odt = RV_F32;
+    int no = 0, nl = 0;
+    for (const Store& st_ : k.stores) {
+        if (st_.out_index == 0) {
+            o = pname(st_.loc, st_.dtype, true);
+            odt = st_.dtype;
+            ++no;
+        } else {
+            l = pname(st_.loc, RV_F32, true);
+            ++nl;
+        }
+    }
+    if (no > 1 || nl > 1) fail(RV_E_UNSUPPORTED_LAYOUT, "sdpa_fwd: one output requested twice");
+    const float sl2 = (float)(k.attn_scale * 1.4426950408889634);  // scale * log2(e)
+    std::ostringstream b;
+    b << "  rv_attn_fwd_bf16<" << D << ", " << (k.attn_causal ? "true" : "false") << ", "
+      << (odt == RV_BF16 ? "true" : "false") << ">(" << q << ", " << kp << ", " << v << ", " << o << ", " << l << ", "
+      << Tq << ", " << Tk << ", " << fmt("%a", sl2) << "f);\n";
+    return b.str();
+}
+
 std::string Gen::gen_fold() {
     const Ex& R = k.ex[0];
     std::string src = pname(Loc{2, k.fold_src_region}, RV_F32, false);
@@ -1491,6 +1523,7 @@ std::string Gen::gen() {
         case KClass::ROW: body = k.plan == "row_stream" ? gen_row_stream() : gen_row(); break;
         case KClass::REDUCE: body = gen_cells(); break;
         case KClass::FOLD: body = gen_fold(); break;
+        case KClass::ATTN: body = gen_attn(); break;
         case KClass::MFMA: {
             std::string s = gen_gemm();
             size_t at = s.find("@@BODY@@");

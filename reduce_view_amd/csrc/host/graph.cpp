@@ -23,7 +23,7 @@ static int arity(int op) {
     switch (op) {
         case RV_BUFFER: case RV_CONST: return 0;
         case RV_ADD: case RV_MUL: case RV_CMPLT: return 2;
-        case RV_WHERE: return 3;
+        case RV_WHERE: case RV_CUSTOM: return 3;
         default: return 1;
     }
 }
@@ -71,8 +71,9 @@ Graph intake(const rv_node* nodes, int32_t n, const int32_t* outputs, int32_t no
         Node& nd = g.nodes[i];
         nd.op = in.op;
         if (in.op < 0 || in.op > RV_CUSTOM) fail(RV_E_INVALID, fmt("node %d: unknown op %d", i, in.op));
-        if (in.op >= RV_GATHER)
-            fail(RV_E_UNSUPPORTED_OP, fmt("node %d: %s is not supported by this library", i, op_name(in.op)));
+        if (in.op >= RV_GATHER && !(in.op == RV_CUSTOM && in.buf == RV_CUSTOM_SDPA_FWD))
+            fail(RV_E_UNSUPPORTED_OP, fmt("node %d: %s%s is not supported by this library", i, op_name(in.op),
+                                          in.op == RV_CUSTOM ? fmt(" kernel %d", in.buf).c_str() : ""));
         nd.nsrc = arity(in.op);
         for (int k = 0; k < nd.nsrc; ++k) {
             nd.src[k] = in.src[k];
@@ -156,6 +157,41 @@ Graph intake(const rv_node* nodes, int32_t n, const int32_t* outputs, int32_t no
                 nd.shape = S(0).shape;
                 nd.dtype = S(0).dtype;
                 break;
+            case RV_CUSTOM: {  // sdpa_fwd (the only CUSTOM kernel)
+                const Shape &q = S(0).shape, &k = S(1).shape, &v = S(2).shape;
+                for (int j = 0; j < 3; ++j)
+                    if (S(j).dtype != RV_BF16) fail(RV_E_DTYPE, fmt("node %d: sdpa_fwd operands must be bf16", i));
+                if (q.size() != 3 || k.size() != 3 || k != v || q[0] != k[0] || q[2] != k[2])
+                    fail(RV_E_INVALID, fmt("node %d: sdpa_fwd needs q (H, Tq, D), k and v (H, Tk, D); got %s, %s, %s", i,
+                                           shape_str(q).c_str(), shape_str(k).c_str(), shape_str(v).c_str()));
+                if (q[2] != 32 && q[2] != 64 && q[2] != 128)
+                    fail(RV_E_UNSUPPORTED_LAYOUT, fmt("node %d: sdpa_fwd head width %lld (32, 64 or 128)", i,
+                                                      (long long)q[2]));
+                if (q[1] < 1 || k[1] < 1 || q[0] < 1) fail(RV_E_INVALID, fmt("node %d: sdpa_fwd of an empty tensor", i));
+                if (q[0] > 65535 || q[1] >= (int64_t(1) << 31) / q[2] || k[1] >= (int64_t(1) << 31) / k[2])
+                    fail(RV_E_INVALID, fmt("node %d: sdpa_fwd too large", i));
+                if ((in.reduce_axes & ~(RV_SDPA_CAUSAL | (0xffu << 16))) != 0)
+                    fail(RV_E_INVALID, fmt("node %d: sdpa_fwd flags 0x%x", i, in.reduce_axes));
+                nd.custom = in.buf;
+                nd.cout = (int)((in.reduce_axes >> 16) & 0xff);
+                nd.causal = (in.reduce_axes & RV_SDPA_CAUSAL) != 0;
+                nd.cval = in.cval;
+                if (!(in.cval == in.cval) || in.cval == 1.0 / 0.0 || in.cval == -1.0 / 0.0)
+                    fail(RV_E_INVALID, fmt("node %d: sdpa_fwd scale must be finite", i));
+                if (nd.cout == 0) {
+                    if (in.dtype != RV_F32 && in.dtype != RV_BF16)
+                        fail(RV_E_DTYPE, fmt("node %d: sdpa_fwd output must be f32 or bf16", i));
+                    nd.shape = q;
+                    nd.dtype = in.dtype;
+                } else if (nd.cout == 1) {
+                    if (in.dtype != RV_F32) fail(RV_E_DTYPE, fmt("node %d: sdpa_fwd logsumexp is f32", i));
+                    nd.shape = {q[0], q[1], 1};
+                    nd.dtype = RV_F32;
+                } else {
+                    fail(RV_E_INVALID, fmt("node %d: sdpa_fwd has outputs 0 and 1, not %d", i, nd.cout));
+                }
+                break;
+            }
         }
     }
     for (int k = 0; k < nout; ++k) {
@@ -175,6 +211,7 @@ const char* kclass_name(KClass k) {
         case KClass::REDUCE: return "REDUCE";
         case KClass::MFMA: return "MFMA";
         case KClass::FOLD: return "FOLD";
+        case KClass::ATTN: return "ATTN";
     }
     return "?";
 }

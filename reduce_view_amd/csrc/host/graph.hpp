@@ -25,6 +25,10 @@ struct Node {
     double cval = 0.0;    // CONST
     rv_view view{};       // VIEW (over src[0]'s row-major storage)
     uint32_t axes = 0;    // SUM / MAX
+    // CUSTOM: kernel id, which of its outputs this node is, flags
+    int custom = 0;
+    int cout = 0;
+    bool causal = false;
 };
 
 struct Graph {
@@ -46,7 +50,7 @@ bool pure_broadcast(const rv_view& v, const Shape& src_shape, std::vector<int>* 
 // ---------------------------------------------------------------------------
 // kernels (schedule.cpp / lower.cpp / codegen.cpp)
 // ---------------------------------------------------------------------------
-enum class KClass { EW, ROW, REDUCE, MFMA, FOLD };
+enum class KClass { EW, ROW, REDUCE, MFMA, FOLD, ATTN };
 constexpr int EX_MFMA_ACC = 1000;  // Ex op: the contraction's accumulator at (m, n)
 const char* kclass_name(KClass k);
 
@@ -86,6 +90,7 @@ struct Store {
     int dtype = RV_F32;
     rv_view v{};
     int node = -1;
+    int out_index = 0;  // ATTN: 0 the attention output, 1 the row logsumexp
 };
 
 struct Kernel {
@@ -111,6 +116,9 @@ struct Kernel {
     // FOLD
     int fold_src_region = -1;
     int64_t fold_count = 0;
+    // ATTN (leaves q, k, v; domain (H, Tq, D); Tk = leaves[1].v.shape[1])
+    double attn_scale = 0.0;
+    bool attn_causal = false;
 };
 
 struct Region {

@@ -191,6 +191,25 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             k.plan_json = buf;
             return;
         }
+        case KClass::ATTN: {
+            const int64_t H = k.domain[0], Tq = k.domain[1], D = k.domain[2];
+            const int64_t Tk = k.leaves[1].v.shape[1];
+            k.plan = "attn_fwd";
+            k.grid[0] = (unsigned)((Tq + 127) / 128);  // 128 queries (4 waves of 32) per workgroup
+            k.grid[1] = (unsigned)H;
+            k.block[0] = 512;  // 2 groups of 4 waves splitting the keys
+            const int KT = D <= 64 ? 128 : 64;  // keys staged per step (the device skeleton's default)
+            k.lds = (size_t)(2 * KT * (D + 8) + 2 * KT * (D + 16)) * 2;
+            snprintf(buf, sizeof buf,
+                     "\"queries_per_workgroup\":128,\"queries_per_wave\":32,\"key_groups\":2,\"key_tile\":%d,"
+                     "\"key_step\":64,"
+                     "\"head_dim\":%lld,"
+                     "\"keys\":%lld,\"causal\":%s,\"scale\":%.17g,\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
+                     "\"scores\":\"transposed (K q^T): one query per lane pair\",\"p_operand\":\"bf16\"",
+                     KT, (long long)D, (long long)Tk, k.attn_causal ? "true" : "false", k.attn_scale);
+            k.plan_json = buf;
+            return;
+        }
         case KClass::MFMA: {
             int64_t M = k.domain[0], N = k.domain[1];
             // 256 x 256 tiles when the shape allows: direct-to-LDS copies and

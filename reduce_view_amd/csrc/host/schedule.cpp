@@ -274,6 +274,45 @@ static bool try_ew(Ctx& c, int root, Kernel& k) {
     return true;
 }
 
+// CUSTOM sdpa_fwd: one kernel for a node and its siblings (same sources,
+// scale and causal flag), reading q, k, v where they live (contiguous) and
+// writing each sibling's output.
+static bool same_sdpa(const Node& a, const Node& b) {
+    return a.op == RV_CUSTOM && b.op == RV_CUSTOM && a.custom == b.custom && a.src[0] == b.src[0] &&
+           a.src[1] == b.src[1] && a.src[2] == b.src[2] && a.cval == b.cval && a.causal == b.causal;
+}
+
+static void attn_kernel(Ctx& c, const std::vector<int>& nodes, Kernel& k) {
+    const Node& nd = c.g.nodes[nodes[0]];
+    k = Kernel{};
+    k.cls = KClass::ATTN;
+    const Shape& q = c.g.nodes[nd.src[0]].shape;
+    k.domain = q;
+    k.attn_scale = nd.cval;
+    k.attn_causal = nd.causal;
+    for (int j = 0; j < 3; ++j) {
+        const Node& sn = c.g.nodes[nd.src[j]];
+        Leaf L;
+        L.loc = c.loc[nd.src[j]][0];
+        L.dtype = sn.dtype;
+        L.v = view_contiguous(sn.shape, 0);
+        k.leaves.push_back(L);
+    }
+    for (int o : nodes) {
+        const Node& on = c.g.nodes[o];
+        for (const Loc& L : c.loc[o]) {
+            Store st;
+            st.ex = -1;
+            st.loc = L;
+            st.dtype = on.dtype;
+            st.node = o;
+            st.out_index = on.cout;
+            st.v = view_contiguous(on.shape, 0);
+            k.stores.push_back(st);
+        }
+    }
+}
+
 // Row space of a reduce: (input shape, reduced dims) with every reduced
 // non-size-1 dim after every kept non-size-1 dim.
 static bool row_space(const Node& r, const Node& in, uint32_t* rmask) {
@@ -498,6 +537,9 @@ void schedule(Program& p) {
     for (int i = 0; i < n; ++i) {
         const Node& nd = g.nodes[i];
         if (is_out[i] || nd.op == RV_CONTIGUOUS) need[i] = 1;
+        if (nd.op == RV_CUSTOM)  // the kernel reads its operands from memory
+            for (int j = 0; j < nd.nsrc; ++j)
+                if (g.nodes[nd.src[j]].op != RV_BUFFER) need[nd.src[j]] = 1;
         if (nd.op == RV_VIEW) {
             int s = nd.src[0];
             const Node& sn = g.nodes[s];
@@ -513,9 +555,8 @@ void schedule(Program& p) {
         kernels.clear();
         p.regions.clear();
         bool again = false;
-        for (int i = 0; i < n && !again; ++i) {
-            if (!need[i] || g.nodes[i].op == RV_BUFFER) continue;
-            // location of the value
+        std::vector<char> covered(n, 0);  // CUSTOM siblings written by an earlier node's kernel
+        auto place = [&](int i) {  // location of the value
             c.loc[i].clear();
             for (size_t k = 0; k < g.outputs.size(); ++k)
                 if (g.outputs[k] == i) c.loc[i].push_back(Loc{1, (int)k});
@@ -523,10 +564,24 @@ void schedule(Program& p) {
                 c.loc[i].push_back(Loc{2, (int)p.regions.size()});
                 p.regions.push_back(Region{0, (size_t)numel(g.nodes[i].shape) * dtype_size(g.nodes[i].dtype)});
             }
+        };
+        for (int i = 0; i < n && !again; ++i) {
+            if (!need[i] || g.nodes[i].op == RV_BUFFER || covered[i]) continue;
+            place(i);
             Kernel k;
             int preg = -1;
             std::vector<Kernel> mk;
-            if (try_ew(c, i, k)) {
+            if (g.nodes[i].op == RV_CUSTOM) {
+                std::vector<int> sib{i};
+                for (int j = i + 1; j < n; ++j)
+                    if (need[j] && same_sdpa(g.nodes[i], g.nodes[j])) {
+                        place(j);
+                        covered[j] = 1;
+                        sib.push_back(j);
+                    }
+                attn_kernel(c, sib, k);
+                kernels.push_back(k);
+            } else if (try_ew(c, i, k)) {
                 kernels.push_back(k);
             } else if (try_mfma(c, i, mk, preg)) {
                 for (auto& x : mk) kernels.push_back(x);

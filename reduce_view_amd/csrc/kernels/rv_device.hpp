@@ -1007,6 +1007,274 @@ __device__ __forceinline__ void rv_gemm_pp_bf16(const unsigned short* __restrict
 }
 #undef RV_PP_BARRIER
 
+// ---------------------------------------------------------------------------
+// Fused attention forward, the CUSTOM sdpa_fwd kernel (limn README, "The op
+// set": the one CUSTOM kernel, saving the row's logsumexp beside the output;
+// Tiki README, "Fused attention": a running maximum m, denominator l and
+// output accumulator per query row, updated tile of keys by tile of keys).
+//
+// The scores are formed transposed, S^T = K Q^T on v_mfma_f32_32x32x16_bf16,
+// so a lane of the 32 x 32 result holds 16 scores of ONE query (its column):
+// a query's max and sum need one exchange with lane ^ 32, and rescaling the
+// output accumulator (also transposed, O^T += V^T P^T) is a scalar per lane.
+// The probabilities never leave registers: rounded to bfloat16 they are the
+// B operand of the second product as they stand. The key order the result
+// layout leaves in a lane (keys 4 h .. 4 h + 3 and 8 + 4 h .. of each 16,
+// h = lane / 32) is matched by reading V^T from LDS in that order.
+// Scores are carried in base 2: the running maximum is max(s) * scale *
+// log2 e, and each exponential is v_exp_f32 of one fma.
+//
+// Workgroup: 8 waves. Waves w and w + 4 own the same 32 queries and split
+// the keys: 64-key steps alternate between the two groups, each keeping its
+// own (m, l, accumulator); at the end the second group hands its state
+// through LDS and the first merges the two (rescaling both to the larger
+// maximum) and writes O and L. K and V tiles of KT keys (128 for head widths
+// up to 64) are staged in LDS (K key-major with a padded pitch, V
+// transposed), double buffered. With CAUSAL, key j is hidden from query i
+// when j > i: a workgroup stops at the tile holding its last query, a wave
+// skips steps past its queries, and the workgroups with the most keys are
+// started first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rv_attn_merge(float& m, float& l, float m2, float l2, float& a1, float& a2) {
+    const float mn = fmaxf(m, m2);
+    a1 = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+    a2 = (m2 == mn) ? 1.0f : __builtin_amdgcn_exp2f(m2 - mn);
+    l = l * a1 + l2 * a2;
+    m = mn;
+}
+
+template <int D, bool CAUSAL, bool OUT_BF16, int KT = (D <= 64 ? 128 : 64)>  // KT: a multiple of 64
+__device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restrict__ Q,
+                                                 const unsigned short* __restrict__ K,
+                                                 const unsigned short* __restrict__ V, void* __restrict__ O,
+                                                 float* __restrict__ L, int Tq, int Tk, float sl2) {
+    constexpr int NT = 512;                   // threads: 2 groups x 4 waves
+    constexpr int KP = D + 8;                 // K tile pitch (bf16): conflict-free 16-byte fragment reads
+    constexpr int VP = D + 16;                // V tile pitch (bf16): the 4 rows of a transposing read hit
+                                              // disjoint banks (row stride D/2 + 8 banks)
+    constexpr int CH = KT * D / 8;            // 16-byte chunks per tile
+    constexpr int NCH = (CH + NT - 1) / NT;   // chunks per thread
+    constexpr int TILE_BYTES = 2 * (KT * KP + KT * VP) * 2;
+    constexpr int MERGE_BYTES = 4 * 64 * (16 * (D / 32) + 2) * 4;
+    static_assert(MERGE_BYTES <= TILE_BYTES, "the merge reuses the tile buffers");
+    __shared__ __attribute__((aligned(16))) unsigned short smem[TILE_BYTES / 2];
+    unsigned short* ks = smem;                     // [2][KT * KP]
+    unsigned short* vs = smem + 2 * KT * KP;       // [2][KT * VP], key-major
+    // the wave index in a scalar register: the per-wave bounds below are
+    // scalar branches, with no divergent control flow around the MFMAs
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wq = wave & 3;
+    const int ql = lane & 31, hh = lane >> 5;
+    // the longest rows first: under CAUSAL the last query block has the most keys
+    const int qb = (CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x) * 128;
+    const int q0 = qb + wq * 32;
+    const int qi = q0 + ql;
+    const long long qbase = (long long)blockIdx.y * Tq;
+    const long long kbase = (long long)blockIdx.y * Tk;
+    const rv_u32x4 zero4 = {0u, 0u, 0u, 0u};
+    const float ninf = -__builtin_inff();
+
+    // Loads are unconditional, with rows clamped into range, so no branch
+    // surrounds them: a query row past Tq computes on row Tq - 1 and is never
+    // stored; a key past Tk is masked to -inf (its V row is stored as zeros).
+    rv_bf16x8 qf[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        rv_u32x4 w = *reinterpret_cast<const rv_u32x4*>(Q + (qbase + min(qi, Tq - 1)) * D + 16 * s + 8 * hh);
+        // pinned here (an empty asm that takes the value): q must have arrived
+        // before the key loop, or the wait for it inside the loop would also
+        // wait for the next tile's loads
+        asm volatile("" : "+v"(w));
+        qf[s] = __builtin_bit_cast(rv_bf16x8, w);
+    }
+
+    rv_u32x4 kr[NCH], vr[NCH];
+    auto load_tile = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + NT * i;
+            if (CH % NT == 0 || c < CH) {
+                const int key = c / (D / 8), dc = c % (D / 8);
+                const long long off = (kbase + min(kb + key, Tk - 1)) * D + dc * 8;
+                kr[i] = *reinterpret_cast<const rv_u32x4*>(K + off);
+                vr[i] = *reinterpret_cast<const rv_u32x4*>(V + off);
+            }
+        }
+    };
+    auto store_tile = [&](int b, int kb) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + NT * i;
+            if (CH % NT == 0 || c < CH) {
+                const int key = c / (D / 8), dc = c % (D / 8);
+                *reinterpret_cast<rv_u32x4*>(&ks[b * KT * KP + key * KP + dc * 8]) = kr[i];
+                const rv_u32x4 vv = kb + key < Tk ? vr[i] : zero4;
+                *reinterpret_cast<rv_u32x4*>(&vs[b * KT * VP + key * VP + dc * 8]) = vv;
+            }
+        }
+    };
+
+    int kend = Tk;
+    if (CAUSAL) kend = min(Tk, min(Tq, qb + 128));
+    const int nt = (kend + KT - 1) / KT;
+    rv_f32x16 oacc[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+    float m = ninf, l = 0.0f;
+
+    load_tile(0);
+    store_tile(0, 0);
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+        const int b = t & 1;
+        if (t + 1 < nt) load_tile((t + 1) * KT);
+#pragma unroll
+        for (int sub = 0; sub < KT / 64; ++sub) {
+            const int step = t * (KT / 64) + sub;
+            const int kb = step * 64;
+            // alternate 64-key steps between the two groups; skip steps whose
+            // keys are all hidden from this wave's queries (both wave-uniform)
+            if ((step & 1) != grp || kb >= kend || (CAUSAL && kb > q0 + 31)) continue;
+            const unsigned short* kt = ks + b * KT * KP + sub * 64 * KP;
+            const unsigned short* vt = vs + b * KT * VP + sub * 64 * VP;
+            // S^T for 64 keys as two 32 x 32 tiles: A = K rows (lane: key ql
+            // of the tile, head dims 16 s + 8 hh ..), B = Q^T
+            rv_f32x16 sacc[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[u][r] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) {
+                    const rv_bf16x8 af = *reinterpret_cast<const rv_bf16x8*>(&kt[(u * 32 + ql) * KP + 16 * s + 8 * hh]);
+                    sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[u], 0, 0, 0);
+                }
+            }
+            // online softmax of this lane's query over the 64 keys
+            float sv[32];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sv[16 * u + r] = sacc[u][r];
+            if (kb + 64 > Tk || (CAUSAL && kb + 63 > q0)) {  // wave-uniform
+#pragma unroll
+                for (int r = 0; r < 32; ++r) {
+                    const int key = kb + (r >> 4) * 32 + ((r & 15) >> 2) * 8 + hh * 4 + (r & 3);
+                    if (key >= Tk || (CAUSAL && key > qi)) sv[r] = ninf;
+                }
+            }
+            float cm = sv[0];
+#pragma unroll
+            for (int r = 1; r < 32; ++r) cm = fmaxf(cm, sv[r]);
+            cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+            // max(s) * c equals max(s * c) for c > 0 (rounding is monotonic)
+            const float mn = fmaxf(m, cm * sl2);
+            const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+            float pr[32];
+            float ps = 0.0f;
+            if (mn != ninf) {
+#pragma unroll
+                for (int r = 0; r < 32; ++r) {
+                    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sl2, -mn));
+                    ps = ps + pr[r];
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 32; ++r) pr[r] = 0.0f;
+            }
+            ps = ps + __shfl_xor(ps, 32, 64);
+            l = l * alpha + ps;
+            m = mn;
+            // multiplying by 1 changes nothing: skip the rescale when no lane's
+            // maximum grew (most steps of a long row)
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            }
+            // O^T += V^T P^T over the 64 keys (four k16 steps)
+            rv_bf16x8 pb[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pb[s][i] = (__bf16)pr[8 * s + i];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    // k16 step s covers the tile u = s / 2, keys 16 (s % 2) + 4 hh + 0..3
+                    // and + 8: two transposing reads of the key-major V tile, in
+                    // each group of 16 lanes one row of 4 keys per 4 lanes and one
+                    // column (head dim) per lane
+                    const int g = lane >> 4, j = lane & 15;
+                    const int row = (s >> 1) * 32 + 16 * (s & 1) + 4 * (g >> 1) + (j >> 2);
+                    const int col = dt * 32 + (g & 1) * 16 + (j & 3) * 4;
+                    typedef __attribute__((address_space(3))) rv_s16x4 lds_s16x4;
+                    typedef __attribute__((address_space(3))) unsigned short lds_u16;
+                    const rv_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)((lds_u16*)vt + row * VP + col));
+                    const rv_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4*)((lds_u16*)vt + (row + 8) * VP + col));
+                    typedef __attribute__((ext_vector_type(8))) short s16x8;
+                    const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(rv_bf16x8, a8), pb[s],
+                                                                       oacc[dt], 0, 0, 0);
+                }
+        }
+        if (t + 1 < nt) store_tile(b ^ 1, (t + 1) * KT);
+        __syncthreads();
+    }
+    // merge: group 1 hands (m, l, accumulator) to group 0 through LDS (the
+    // tile buffers are free after the loop's last barrier)
+    float* xs = reinterpret_cast<float*>(smem);
+    constexpr int PER = 16 * (D / 32) + 2;
+    float* mine = xs + (wq * 64 + lane) * PER;
+    if (grp == 1) {
+        mine[0] = m;
+        mine[1] = l;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mine[2 + 16 * dt + r] = oacc[dt][r];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    {
+        float a1, a2;
+        rv_attn_merge(m, l, mine[0], mine[1], a1, a2);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * a1 + mine[2 + 16 * dt + r] * a2;
+    }
+    if (qi < Tq) {
+        const float inv = 1.0f / l;
+        if (O != nullptr) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const long long at = (qbase + qi) * D + dt * 32 + g * 8 + hh * 4;
+                    if (OUT_BF16) {
+                        rv_pack<unsigned short, 4> pk;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pk.v[i] = rv_f2bf(oacc[dt][4 * g + i] * inv);
+                        rv_stv<unsigned short, 4>(reinterpret_cast<unsigned short*>(O) + at, pk);
+                    } else {
+                        rv_pack<float, 4> pk;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pk.v[i] = oacc[dt][4 * g + i] * inv;
+                        rv_stv<float, 4>(reinterpret_cast<float*>(O) + at, pk);
+                    }
+                }
+        }
+        if (L != nullptr && hh == 0) L[qbase + qi] = m * 0.693147180559945309f + logf(l);
+    }
+}
+
 // Deterministic fold of `count` float partials into one value: each thread
 // adds a strided subset in ascending order, then a fixed binary tree in LDS.
 // No atomics, so two runs give the same bits.

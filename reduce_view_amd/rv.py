@@ -232,6 +232,11 @@ def _blank_view() -> rv_view:
     return rv_view()
 
 
+# CUSTOM kernel ids and flags (include/rv.h)
+CUSTOM_SDPA_FWD = 1
+SDPA_CAUSAL = 1
+
+
 def nodes_from_spec(spec):
     """rv_node array and slot names for a ``synth.Spec``. Movement ops are
     composed by the library's own rv_view_* calls; shapes of computed
@@ -289,6 +294,13 @@ def nodes_from_spec(spec):
                     elif name == "shrink":
                         v = rv_view_shrink(v, [w[0] for w in a], [w[1] for w in a])
             x.view = v
+        elif op == "CUSTOM":
+            if nd.get("kind") != "sdpa_fwd":
+                raise RVError(-2, f"CUSTOM kernel {nd.get('kind')!r} is not supported")
+            x.buf = CUSTOM_SDPA_FWD
+            x.dtype = DTYPE[nd["dtype"]]
+            x.cval = nd["scale"]
+            x.reduce_axes = (SDPA_CAUSAL if nd["causal"] else 0) | (int(nd["out"]) << 16)
     return arr, slots
 
 

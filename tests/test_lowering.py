@@ -176,3 +176,54 @@ def test_dtype_variants_through_the_plan():
         ref = oracle.run(g, inp)
         for x, y in zip(got, ref):
             assert x.tobytes() == y.tobytes(), dt
+
+
+def test_attention_is_one_custom_kernel():
+    # the two CUSTOM sdpa_fwd nodes (output and logsumexp) share one launch
+    prog = rv.compile_spec(synth.attention(3, 200, 333, 64, causal=False, out_dtype="bf16"))
+    ks = prog.describe()["kernels"]
+    assert [k["class"] for k in ks] == ["ATTN"]
+    k = ks[0]
+    assert k["grid"] == [2, 3, 1] and k["block"] == [512, 1, 1]
+    assert k["plan_detail"]["head_dim"] == 64 and k["plan_detail"]["keys"] == 333
+    assert sorted(s["loc"]["index"] for s in k["stores"]) == [0, 1]
+    assert prog.out_desc == [((3, 200, 64), "bf16"), ((3, 200, 1), "f32")]
+
+
+def test_attention_operand_view_is_materialised():
+    # k given as a permuted View of a (H, D, Tk) buffer: copied to workspace first
+    g = synth.Spec()
+    q = g.buffer("Q", (2, 40, 32), "bf16")
+    kt = g.buffer("Kt", (2, 32, 50), "bf16")
+    v = g.buffer("V", (2, 50, 32), "bf16")
+    o, _ = g.sdpa(q, g.view(kt, ("permute", (0, 2, 1))), v, 0.25, causal=False)
+    g.output(o)
+    ks = rv.compile_spec(g).describe()
+    assert [k["class"] for k in ks["kernels"]] == ["EW", "ATTN"]
+    assert ks["workspace_bytes"] >= 2 * 50 * 32 * 2
+
+
+def test_attention_contract_errors():
+    def status(spec, patch=None):
+        nodes, _ = rv.nodes_from_spec(spec)
+        if patch:
+            patch(nodes)
+        with pytest.raises(rv.RVError) as e:
+            rv.rv_compile(nodes, list(spec.outputs))
+        return e.value.name
+
+    g = synth.Spec()
+    q = g.buffer("Q", (1, 8, 32), "f32")
+    k = g.buffer("K", (1, 8, 32), "f32")
+    o, _ = g.sdpa(q, k, k, 0.1)
+    g.output(o)
+    assert status(g) == "RV_E_DTYPE"
+    g = synth.Spec()
+    q = g.buffer("Q", (1, 8, 48), "bf16")
+    o, _ = g.sdpa(q, q, q, 0.1)
+    g.output(o)
+    assert status(g) == "RV_E_UNSUPPORTED_LAYOUT"
+    g = synth.attention(1, 8, 8, 32, outputs="o")
+    assert status(g, lambda n: setattr(n[3], "buf", 7)) == "RV_E_UNSUPPORTED_OP"
+    g = synth.attention(1, 8, 8, 32, outputs="o")
+    assert status(g, lambda n: setattr(n[3], "reduce_axes", 5 << 16)) == "RV_E_INVALID"
