@@ -197,16 +197,19 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             k.plan = "attn_fwd";
             k.grid[0] = (unsigned)((Tq + 127) / 128);  // 128 queries (4 waves of 32) per workgroup
             k.grid[1] = (unsigned)H;
-            k.block[0] = 512;  // 2 groups of 4 waves splitting the keys
-            const int KT = D <= 64 ? 128 : 64;  // keys staged per step (the device skeleton's default)
-            k.lds = (size_t)(2 * KT * (D + 8) + 2 * KT * (D + 16)) * 2;
+            // the device skeleton's defaults: NG groups of 4 waves split the
+            // keys, tiles of KT keys
+            const int NG = 2, KT = D <= 64 ? 128 : 64;
+            k.block[0] = (unsigned)(256 * NG);
+            k.lds = std::max<size_t>((size_t)(2 * KT * (D + 8) + 2 * KT * (D + 16)) * 2,
+                                     (size_t)(NG - 1) * 4 * 64 * (16 * (D / 32) + 2) * 4);
             snprintf(buf, sizeof buf,
-                     "\"queries_per_workgroup\":128,\"queries_per_wave\":32,\"key_groups\":2,\"key_tile\":%d,"
+                     "\"queries_per_workgroup\":128,\"queries_per_wave\":32,\"key_groups\":%d,\"key_tile\":%d,"
                      "\"key_step\":64,"
                      "\"head_dim\":%lld,"
                      "\"keys\":%lld,\"causal\":%s,\"scale\":%.17g,\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
                      "\"scores\":\"transposed (K q^T): one query per lane pair\",\"p_operand\":\"bf16\"",
-                     KT, (long long)D, (long long)Tk, k.attn_causal ? "true" : "false", k.attn_scale);
+                     NG, KT, (long long)D, (long long)Tk, k.attn_causal ? "true" : "false", k.attn_scale);
             k.plan_json = buf;
             return;
         }

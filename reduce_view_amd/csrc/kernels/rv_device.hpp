@@ -1015,7 +1015,8 @@ __device__ __forceinline__ void rv_gemm_pp_bf16(const unsigned short* __restrict
 //
 // The scores are formed transposed, S^T = K Q^T on v_mfma_f32_32x32x16_bf16,
 // so a lane of the 32 x 32 result holds 16 scores of ONE query (its column):
-// a query's max and sum need one exchange with lane ^ 32, and rescaling the
+// a query's max and sum need one exchange with lane ^ 32 (v_permlane32_swap),
+// and rescaling the
 // output accumulator (also transposed, O^T += V^T P^T) is a scalar per lane.
 // The probabilities never leave registers: rounded to bfloat16 they are the
 // B operand of the second product as they stand. The key order the result
@@ -1024,17 +1025,31 @@ __device__ __forceinline__ void rv_gemm_pp_bf16(const unsigned short* __restrict
 // Scores are carried in base 2: the running maximum is max(s) * scale *
 // log2 e, and each exponential is v_exp_f32 of one fma.
 //
-// Workgroup: 8 waves. Waves w and w + 4 own the same 32 queries and split
-// the keys: 64-key steps alternate between the two groups, each keeping its
-// own (m, l, accumulator); at the end the second group hands its state
-// through LDS and the first merges the two (rescaling both to the larger
-// maximum) and writes O and L. K and V tiles of KT keys (128 for head widths
-// up to 64) are staged in LDS (K key-major with a padded pitch, V
-// transposed), double buffered. With CAUSAL, key j is hidden from query i
+// Workgroup: NG groups of 4 waves (NG = 2; 4 measured no faster). Waves
+// w, w + 4, .. own the same 32 queries and split the keys: 64-key steps go
+// round the groups, each keeping its own (m, l, accumulator); at the end the
+// other groups hand their states through LDS and the first merges them in
+// group order (rescaling to the larger maximum) and writes O and L. K and V
+// tiles of KT keys (128 for head widths up to 64) are staged in LDS
+// key-major with padded pitches, double buffered; the V^T operand comes out
+// of the transposing LDS read. With CAUSAL, key j is hidden from query i
 // when j > i: a workgroup stops at the tile holding its last query, a wave
 // skips steps past its queries, and the workgroups with the most keys are
 // started first.
 // ---------------------------------------------------------------------------
+// max and sum over the lane pair (l, l ^ 32) with v_permlane32_swap (no LDS
+// round trip): swapped with itself, the pair of results is (lower half's
+// value, upper half's value) in every lane, so both lanes compute the same
+// expression and get the same bits.
+__device__ __forceinline__ float rv_pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rv_pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void rv_attn_merge(float& m, float& l, float m2, float l2, float& a1, float& a2) {
     const float mn = fmaxf(m, m2);
     a1 = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
@@ -1043,27 +1058,28 @@ __device__ __forceinline__ void rv_attn_merge(float& m, float& l, float m2, floa
     m = mn;
 }
 
-template <int D, bool CAUSAL, bool OUT_BF16, int KT = (D <= 64 ? 128 : 64)>  // KT: a multiple of 64
+template <int D, bool CAUSAL, bool OUT_BF16, int NG = 2, int KT = (D <= 64 ? 128 : 64)>
 __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restrict__ Q,
                                                  const unsigned short* __restrict__ K,
                                                  const unsigned short* __restrict__ V, void* __restrict__ O,
                                                  float* __restrict__ L, int Tq, int Tk, float sl2) {
-    constexpr int NT = 512;                   // threads: 2 groups x 4 waves
+    // NG groups of 4 waves split the keys; KT (a multiple of 64) keys per tile
+    constexpr int NT = 256 * NG;              // threads
     constexpr int KP = D + 8;                 // K tile pitch (bf16): conflict-free 16-byte fragment reads
     constexpr int VP = D + 16;                // V tile pitch (bf16): the 4 rows of a transposing read hit
                                               // disjoint banks (row stride D/2 + 8 banks)
     constexpr int CH = KT * D / 8;            // 16-byte chunks per tile
     constexpr int NCH = (CH + NT - 1) / NT;   // chunks per thread
     constexpr int TILE_BYTES = 2 * (KT * KP + KT * VP) * 2;
-    constexpr int MERGE_BYTES = 4 * 64 * (16 * (D / 32) + 2) * 4;
-    static_assert(MERGE_BYTES <= TILE_BYTES, "the merge reuses the tile buffers");
-    __shared__ __attribute__((aligned(16))) unsigned short smem[TILE_BYTES / 2];
+    constexpr int MERGE_BYTES = (NG - 1) * 4 * 64 * (16 * (D / 32) + 2) * 4;
+    constexpr int SMEM_BYTES = TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES;
+    __shared__ __attribute__((aligned(16))) unsigned short smem[SMEM_BYTES / 2];
     unsigned short* ks = smem;                     // [2][KT * KP]
     unsigned short* vs = smem + 2 * KT * KP;       // [2][KT * VP], key-major
     // the wave index in a scalar register: the per-wave bounds below are
     // scalar branches, with no divergent control flow around the MFMAs
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2, wq = wave & 3;
+    const int grp = wave >> 2, wq = wave & 3;  // key group, query wave
     const int ql = lane & 31, hh = lane >> 5;
     // the longest rows first: under CAUSAL the last query block has the most keys
     const int qb = (CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x) * 128;
@@ -1136,7 +1152,7 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
             const int kb = step * 64;
             // alternate 64-key steps between the two groups; skip steps whose
             // keys are all hidden from this wave's queries (both wave-uniform)
-            if ((step & 1) != grp || kb >= kend || (CAUSAL && kb > q0 + 31)) continue;
+            if (step % NG != grp || kb >= kend || (CAUSAL && kb > q0 + 31)) continue;
             const unsigned short* kt = ks + b * KT * KP + sub * 64 * KP;
             const unsigned short* vt = vs + b * KT * VP + sub * 64 * VP;
             // S^T for 64 keys as two 32 x 32 tiles: A = K rows (lane: key ql
@@ -1168,7 +1184,7 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
             float cm = sv[0];
 #pragma unroll
             for (int r = 1; r < 32; ++r) cm = fmaxf(cm, sv[r]);
-            cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+            cm = rv_pair_max(cm);
             // max(s) * c equals max(s * c) for c > 0 (rounding is monotonic)
             const float mn = fmaxf(m, cm * sl2);
             const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
@@ -1184,7 +1200,7 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
 #pragma unroll
                 for (int r = 0; r < 32; ++r) pr[r] = 0.0f;
             }
-            ps = ps + __shfl_xor(ps, 32, 64);
+            ps = rv_pair_sum(ps);
             l = l * alpha + ps;
             m = mn;
             // multiplying by 1 changes nothing: skip the rescale when no lane's
@@ -1227,12 +1243,13 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
         if (t + 1 < nt) store_tile(b ^ 1, (t + 1) * KT);
         __syncthreads();
     }
-    // merge: group 1 hands (m, l, accumulator) to group 0 through LDS (the
-    // tile buffers are free after the loop's last barrier)
+    // merge: groups 1 .. NG-1 hand (m, l, accumulator) to group 0 through
+    // LDS (the tile buffers are free after the loop's last barrier), which
+    // folds them in group order
     float* xs = reinterpret_cast<float*>(smem);
     constexpr int PER = 16 * (D / 32) + 2;
-    float* mine = xs + (wq * 64 + lane) * PER;
-    if (grp == 1) {
+    if (grp > 0) {
+        float* mine = xs + (((grp - 1) * 4 + wq) * 64 + lane) * PER;
         mine[0] = m;
         mine[1] = l;
 #pragma unroll
@@ -1241,14 +1258,16 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
             for (int r = 0; r < 16; ++r) mine[2 + 16 * dt + r] = oacc[dt][r];
     }
     __syncthreads();
-    if (grp == 1) return;
-    {
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < NG; ++g) {
+        const float* other = xs + (((g - 1) * 4 + wq) * 64 + lane) * PER;
         float a1, a2;
-        rv_attn_merge(m, l, mine[0], mine[1], a1, a2);
+        rv_attn_merge(m, l, other[0], other[1], a1, a2);
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * a1 + mine[2 + 16 * dt + r] * a2;
+            for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * a1 + other[2 + 16 * dt + r] * a2;
     }
     if (qi < Tq) {
         const float inv = 1.0f / l;
