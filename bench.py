@@ -5,8 +5,8 @@ float32 elementwise chain WHERE(CMPLT(a, b), a*b, EXP(-a)) + c with b a
 permuted View and c a stride-0 row vector, the same chain with a read through
 a shrink-then-pad masked View, and a standalone 4096 x 4096 transpose. One
 step runs all three programs once. ``--workload`` selects one of the other
-kernels instead (softmax, softmax_long, rmsnorm, layernorm, gemm, attention,
-matmul64, copy).
+kernels instead (softmax, softmax_long, rmsnorm, rmsnorm_f16, rmsnorm_f64,
+chain_i8, layernorm, gemm, attention, matmul64, copy).
 
 Inputs are seeded, synthetic and already resident in HBM when timing starts;
 several input sets rotate so that consecutive launches never re-read data the
@@ -76,6 +76,21 @@ def workloads():
             programs=[("rmsnorm", synth.rmsnorm(16384, 4096), 2 * 16384 * 4096 * F32 + 4096 * F32)],
             inputs=lambda seed: synth.inputs_rmsnorm(16384, 4096, seed),
             unit="GB/s", dtype="f32", bound="hbm", seed=3),
+        "rmsnorm_f16": dict(
+            desc="RMSNorm 16384x4096 with float16 storage and per-node float16 rounding, x ~ N(0,1), w ~ N(1,0.1), seed 3",
+            programs=[("rmsnorm_f16", synth.rmsnorm(16384, 4096, dtype="f16"), 2 * 16384 * 4096 * 2 + 4096 * 2)],
+            inputs=lambda seed: synth.inputs_rmsnorm(16384, 4096, seed, "f16"),
+            unit="GB/s", dtype="f16", bound="hbm", seed=3),
+        "rmsnorm_f64": dict(
+            desc="RMSNorm 16384x4096 float64, x ~ N(0,1), w ~ N(1,0.1), seed 3",
+            programs=[("rmsnorm_f64", synth.rmsnorm(16384, 4096, dtype="f64"), 2 * 16384 * 4096 * 8 + 4096 * 8)],
+            inputs=lambda seed: synth.inputs_rmsnorm(16384, 4096, seed, "f64"),
+            unit="GB/s", dtype="f64", bound="hbm", seed=3),
+        "chain_i8": dict(
+            desc="int8 y = a*b + c wrapping modulo 256, 8192x8192, uniform over the int8 range, seed 8",
+            programs=[("chain_i8", synth.chain_int(8192, 8192, "i8"), 4 * 8192 * 8192)],
+            inputs=lambda seed: synth.inputs_chain_int(8192, 8192, "i8", seed),
+            unit="GB/s", dtype="i8", bound="hbm", seed=8),
         "layernorm": dict(
             desc="LayerNorm 8192x8192 bf16 in/out, fp32 accumulation, x ~ N(100,1), eps 1e-5, seed 4",
             programs=[("layernorm", synth.layernorm(8192, 8192), 2 * 8192 * 8192 * 2 + 2 * 8192 * 2)],

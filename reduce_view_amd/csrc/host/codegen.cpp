@@ -153,6 +153,37 @@ std::string op_code(const Kernel& k, const Ex& e, const std::string& A, const st
     fail(RV_E_INVALID, fmt("internal: no code for op %d", e.op));
 }
 
+// Accumulator of a SUM / MAX in a row kernel: float for float32 and the
+// half widths (widened), double for float64, and for ints an unsigned total
+// (a SUM wraps modulo 2^32, exactly as the serial fold does) or an int (MAX).
+struct RedType {
+    std::string t, ident, fin;
+    bool sum = true, isint = false, isdbl = false;
+    RedType(int op, int dt) {
+        sum = op == RV_SUM;
+        isint = is_int(dt);
+        isdbl = dt == RV_F64;
+        if (isdbl) {
+            t = "double";
+            ident = sum ? "0.0" : "(-__builtin_inf())";
+        } else if (isint) {
+            t = sum ? "unsigned" : "int";
+            ident = sum ? "0u" : (dt == RV_I32 ? "(-2147483647 - 1)" : (dt == RV_I16 ? "(-32768)" : "(-128)"));
+        } else {
+            t = "float";
+            ident = sum ? "0.0f" : "(-__builtin_inff())";
+        }
+    }
+    // acc (op) v for a value v of the register type
+    std::string fold(const std::string& acc, const std::string& v) const {
+        if (sum) return acc + " + " + (isint ? "(unsigned)(" + v + ")" : "(" + v + ")");
+        if (isdbl) return "rv_maxd(" + acc + ", " + v + ")";
+        if (isint) return "((" + v + ") > " + acc + " ? (" + v + ") : " + acc + ")";
+        return "rv_maxf(" + acc + ", " + v + ")";
+    }
+    std::string result(int dt, const std::string& acc) const { return isint ? wrap_int(dt, acc) : round_to(dt, acc); }
+};
+
 struct Gen {
     const Program& p;
     const Kernel& k;
@@ -290,10 +321,8 @@ struct Gen {
 // ---------------------------------------------------------------------------
 std::string Gen::gen_rowmajor() {
     const int X = rank - 1;
-    int maxsz = 1;
-    for (auto& s : k.stores) maxsz = std::max(maxsz, dtype_size(s.dtype));
-    const int VW = std::max(1, std::min(8, 16 / maxsz));
-    const int U = 4;
+    int VW = 1, U = 4;  // plan values (lower.cpp)
+    sscanf(k.plan_json.c_str(), "\"vec\":%d,\"unroll\":%d", &VW, &U);
     const int64_t NX = k.domain[X];
     const int64_t CPR = (NX + VW - 1) / VW;
     const int64_t TOTAL = CPR * (numel(k.domain) / NX);
@@ -681,7 +710,12 @@ std::string Gen::gen_row() {
     };
     std::ostringstream b;
     b << "  const int t = threadIdx.x, lt = t % " << T << ", lr = t / " << T << ";\n";
-    if (T > 64 && nred_) b << "  __shared__ float red[" << nred_ << "][" << RPW << "][" << W << "];\n";
+    bool wide_red = false;  // a float64 or int reduce: its partials travel through LDS as double
+    for (size_t e = 0; e < k.ex.size(); ++e)
+        if (live[e] && (k.ex[e].op == RV_SUM || k.ex[e].op == RV_MAX) && !(k.ex[e].dtype == RV_F32 || is_half(k.ex[e].dtype)))
+            wide_red = true;
+    if (T > 64 && nred_)
+        b << "  __shared__ " << (wide_red ? "double" : "float") << " red[" << nred_ << "][" << RPW << "][" << W << "];\n";
     // element index helpers: n(v, i) = (v * T + lt) * VW + i
     auto nexpr = [&](const std::string& v, const std::string& i) {
         return fmt("(((%s) * %d + lt) * %d + (%s))", v.c_str(), T, VW, i.c_str());
@@ -892,8 +926,9 @@ std::string Gen::gen_row() {
         auto opnd = [&](int i, const std::string& q) -> std::string { return fullv(i, q); };
         if (x.op == RV_SUM || x.op == RV_MAX) {
             const bool sum = x.op == RV_SUM;
-            b << "    float " << V << ";\n    {\n";
-            b << "      float acc = " << (sum ? "0.0f" : "(-__builtin_inff())") << ";\n";
+            const RedType rt(x.op, x.dtype);
+            b << "    " << vt(x.dtype) << " " << V << ";\n    {\n";
+            b << "      " << rt.t << " acc = " << rt.ident << ";\n";
             b << "      for (int q = 0; q < " << E << "; ++q) {\n";
             std::string val = opnd(x.a, "q");
             if (ragged)
@@ -901,19 +936,17 @@ std::string Gen::gen_row() {
                   << ") ";
             else
                 b << "        ";
-            b << (sum ? "acc = acc + " + val : "acc = rv_maxf(acc, " + val + ")") << ";\n      }\n";
+            b << "acc = " << rt.fold("acc", val) << ";\n      }\n";
             int g = std::min(T, 64);
             b << "      acc = rv_group_" << (sum ? "sum" : "max") << "<" << g << ">(acc);\n";
             if (T > 64) {
                 b << "      if ((t & 63) == 0) red[" << red_slot << "][lr][lt >> 6] = acc;\n      rv_lds_barrier();\n";
-                b << "      acc = red[" << red_slot << "][lr][0];\n";
+                b << "      acc = (" << rt.t << ")red[" << red_slot << "][lr][0];\n";
                 for (int w = 1; w < W; ++w)
-                    b << "      acc = " << (sum ? fmt("acc + red[%d][lr][%d]", red_slot, w)
-                                                : fmt("rv_maxf(acc, red[%d][lr][%d])", red_slot, w))
-                      << ";\n";
+                    b << "      acc = " << rt.fold("acc", fmt("(%s)red[%d][lr][%d]", rt.t.c_str(), red_slot, w)) << ";\n";
                 ++red_slot;
             }
-            b << "      " << V << " = " << round_to(x.dtype, "acc") << ";\n    }\n";
+            b << "      " << V << " = " << rt.result(x.dtype, "acc") << ";\n    }\n";
             continue;
         }
         if (stat[e]) {
@@ -1023,7 +1056,12 @@ std::string Gen::gen_row_stream() {
     const int nslots = (int)passes.size() + (int)pairs.size();
     std::ostringstream b;
     b << "  const int t = threadIdx.x, lt = t % " << T << ", lr = t / " << T << ";\n";
-    if (T > 64 && nslots) b << "  __shared__ float red[" << nslots << "][" << RPW << "][" << W << "];\n";
+    bool wide_red = false;  // a float64 or int reduce: its partials travel through LDS as double
+    for (size_t e = 0; e < k.ex.size(); ++e)
+        if (live[e] && (k.ex[e].op == RV_SUM || k.ex[e].op == RV_MAX) && !(k.ex[e].dtype == RV_F32 || is_half(k.ex[e].dtype)))
+            wide_red = true;
+    if (T > 64 && nslots)
+        b << "  __shared__ " << (wide_red ? "double" : "float") << " red[" << nslots << "][" << RPW << "][" << W << "];\n";
     auto nexpr = [&](const std::string& v, const std::string& i) {
         return fmt("(cb + ((%s) * %d + lt) * %d + (%s))", v.c_str(), T, VW, i.c_str());
     };
@@ -1160,7 +1198,7 @@ std::string Gen::gen_row_stream() {
         if (online)
             b << "    float om = -__builtin_inff(), ol = 0.0f;\n";
         else
-            b << "    float acc" << r0 << " = " << (R0.op == RV_SUM ? "0.0f" : "(-__builtin_inff())") << ";\n";
+            b << "    " << RedType(R0.op, R0.dtype).t << " acc" << r0 << " = " << RedType(R0.op, R0.dtype).ident << ";\n";
         b << "    for (" << I << " c = 0; c < " << lit(NCH) << "; ++c) {\n";
         b << "      const " << I << " cb = c * " << lit(CH) << ";\n";
         emit_chunk(needed({X}), "      ", false);
@@ -1174,11 +1212,10 @@ std::string Gen::gen_row_stream() {
             b << "      if (mn != -__builtin_inff())\n";
             b << "        for (int q = 0; q < " << E << "; ++q) " << guard << "ps = ps + expf(" << xv << " + (-mn));\n";
             b << "      ol = ol * alpha + ps;\n      om = mn;\n";
-        } else if (R0.op == RV_SUM) {
-            b << "      for (int q = 0; q < " << E << "; ++q) " << guard << "acc" << r0 << " = acc" << r0 << " + " << xv << ";\n";
         } else {
-            b << "      for (int q = 0; q < " << E << "; ++q) " << guard << "acc" << r0 << " = rv_maxf(acc" << r0 << ", " << xv
-              << ");\n";
+            const std::string a = fmt("acc%d", r0);
+            b << "      for (int q = 0; q < " << E << "; ++q) " << guard << a << " = "
+              << RedType(R0.op, R0.dtype).fold(a, xv) << ";\n";
         }
         b << "    }\n";
         const int g = std::min(T, 64);
@@ -1196,18 +1233,17 @@ std::string Gen::gen_row_stream() {
             b << "    const float e" << pass[1] << " = ol;\n";
             done[r0] = done[pass[1]] = 1;
         } else {
-            b << "    float e" << r0 << ";\n    {\n      float acc = acc" << r0 << ";\n";
+            const RedType rt(R0.op, R0.dtype);
+            b << "    " << vt(R0.dtype) << " e" << r0 << ";\n    {\n      " << rt.t << " acc = acc" << r0 << ";\n";
             b << "      acc = rv_group_" << (R0.op == RV_SUM ? "sum" : "max") << "<" << g << ">(acc);\n";
             if (T > 64) {
                 b << "      if ((t & 63) == 0) red[" << slot << "][lr][lt >> 6] = acc;\n      rv_lds_barrier();\n";
-                b << "      acc = red[" << slot << "][lr][0];\n";
+                b << "      acc = (" << rt.t << ")red[" << slot << "][lr][0];\n";
                 for (int w = 1; w < W; ++w)
-                    b << "      acc = " << (R0.op == RV_SUM ? fmt("acc + red[%d][lr][%d]", slot, w)
-                                                           : fmt("rv_maxf(acc, red[%d][lr][%d])", slot, w))
-                      << ";\n";
+                    b << "      acc = " << rt.fold("acc", fmt("(%s)red[%d][lr][%d]", rt.t.c_str(), slot, w)) << ";\n";
                 ++slot;
             }
-            b << "      e" << r0 << " = " << round_to(R0.dtype, "acc") << ";\n    }\n";
+            b << "      e" << r0 << " = " << rt.result(R0.dtype, "acc") << ";\n    }\n";
             done[r0] = 1;
         }
         emit_ready("    ");

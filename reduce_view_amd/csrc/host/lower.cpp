@@ -316,10 +316,12 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             k.plan = "rowmajor";
             int maxsz = 1;
             for (auto& s : k.stores) maxsz = std::max(maxsz, dtype_size(s.dtype));
-            int vw = std::max(1, std::min(8, 16 / maxsz));
+            // 16-byte accesses per lane; about 32 cells of every value in
+            // flight per lane (4 vectors of float32, 2 of int8)
+            int vw = std::max(1, std::min(16, 16 / maxsz));
             int64_t cpr = (k.domain[X] + vw - 1) / vw;
             int64_t chunks = cpr * (numel(k.domain) / k.domain[X]);
-            const int U = 4;
+            const int U = std::max(1, std::min(4, 32 / vw));
             int64_t blocks = (chunks + 256 * U - 1) / (256 * U);
             k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 256 * 32));
             k.block[0] = 256;

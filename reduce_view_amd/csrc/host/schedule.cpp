@@ -181,7 +181,8 @@ struct Builder {
         // ROW: the reduce must reduce exactly the domain's reduced dims of an
         // input laid over the whole domain; REDUCE: only the root reduces.
         if (!(mode == ROW || (mode == REDUCE && i == root))) throw 1;
-        if (mode == ROW && !(nd.dtype == RV_F32 || is_half(nd.dtype))) throw 1;
+        // (ROW reduces accumulate float32 for float32 and the half widths,
+        // float64 for float64, and an exact wrapping total for ints)
         if (in.shape != k.domain) throw 1;
         uint32_t ax = 0;
         for (size_t d = 0; d < in.shape.size(); ++d)

@@ -61,6 +61,10 @@ template <>
 struct rv_words<16> {
     typedef __attribute__((ext_vector_type(4))) unsigned type;
 };
+template <>
+struct rv_words<32> {  // 4 doubles: two 16-byte accesses
+    typedef __attribute__((ext_vector_type(8))) unsigned type;
+};
 
 template <class T, int N>
 __device__ __forceinline__ rv_pack<T, N> rv_ldv_nt(const T* p) {
@@ -116,6 +120,37 @@ template <int W>
 __device__ __forceinline__ float rv_group_max(float v) {
 #pragma unroll
     for (int o = W / 2; o >= 1; o >>= 1) v = rv_maxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// The same over float64 (folded in float64) and over ints (a SUM wraps in an
+// unsigned total: int arithmetic is exact modulo 2^32, so any order gives the
+// same bits).
+template <int W>
+__device__ __forceinline__ double rv_group_sum(double v) {
+#pragma unroll
+    for (int o = W / 2; o >= 1; o >>= 1) v = v + __shfl_xor(v, o, 64);
+    return v;
+}
+template <int W>
+__device__ __forceinline__ double rv_group_max(double v) {
+#pragma unroll
+    for (int o = W / 2; o >= 1; o >>= 1) v = rv_maxd(v, __shfl_xor(v, o, 64));
+    return v;
+}
+template <int W>
+__device__ __forceinline__ unsigned rv_group_sum(unsigned v) {
+#pragma unroll
+    for (int o = W / 2; o >= 1; o >>= 1) v = v + (unsigned)__shfl_xor((int)v, o, 64);
+    return v;
+}
+template <int W>
+__device__ __forceinline__ int rv_group_max(int v) {
+#pragma unroll
+    for (int o = W / 2; o >= 1; o >>= 1) {
+        const int u = __shfl_xor(v, o, 64);
+        v = u > v ? u : v;
+    }
     return v;
 }
 

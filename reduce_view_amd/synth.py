@@ -206,15 +206,17 @@ def softmax_noshift(rows: int, n: int) -> Spec:
     return g
 
 
-def rmsnorm(rows: int, n: int, eps: float = 1e-6) -> Spec:
+def rmsnorm(rows: int, n: int, eps: float = 1e-6, dtype: str = "f32") -> Spec:
     """y = (x * r) * w, r = RECIP(SQRT(SUM(x*x) * (1/n) + eps)) (Tiki README,
-    "Compile model code": float32 reduction, multiplication order x*inv*w)."""
-    g = Spec(f"rmsnorm_{rows}x{n}")
-    x = g.buffer("x", (rows, n), "f32")
-    w = g.buffer("w", (n,), "f32")
+    "Compile model code": float32 reduction, multiplication order x*inv*w).
+    Every value in ``dtype`` (f16: each primitive computes in float32 and
+    rounds back, the SUM keeps a float32 total; f64 throughout)."""
+    g = Spec(f"rmsnorm_{rows}x{n}" + ("" if dtype == "f32" else f"_{dtype}"))
+    x = g.buffer("x", (rows, n), dtype)
+    w = g.buffer("w", (n,), dtype)
     ss = g.sum(g.mul(x, x), (1,))
-    ms = g.mul(ss, g.const(1.0 / n, (rows, 1), "f32"))
-    r = g.recip(g.sqrt(g.add(ms, g.const(eps, (rows, 1), "f32"))))
+    ms = g.mul(ss, g.const(1.0 / n, (rows, 1), dtype))
+    r = g.recip(g.sqrt(g.add(ms, g.const(eps, (rows, 1), dtype))))
     rb = g.view(r, ("expand", (rows, n)))
     wb = g.view(w, ("reshape", (1, n)), ("expand", (rows, n)))
     g.output(g.mul(g.mul(x, rb), wb))
@@ -309,11 +311,34 @@ def inputs_softmax(rows: int, n: int, seed: int = 2) -> dict:
     return {"x": _f32(rng.uniform(-1e3, 1e3, (rows, n)))}
 
 
-def inputs_rmsnorm(rows: int, n: int, seed: int = 3) -> dict:
+def inputs_rmsnorm(rows: int, n: int, seed: int = 3, dtype: str = "f32") -> dict:
+    """x ~ N(0, 1) then w ~ N(1, 0.1), float64 draws rounded once (RNE) to
+    ``dtype`` (f32, f16 or f64)."""
     rng = np.random.default_rng(seed)
-    x = _f32(rng.normal(0.0, 1.0, (rows, n)))
-    w = _f32(rng.normal(1.0, 0.1, (n,)))
+    to = {"f32": np.float32, "f16": np.float16, "f64": np.float64}[dtype]
+    x = rng.normal(0.0, 1.0, (rows, n)).astype(to)
+    w = rng.normal(1.0, 0.1, (n,)).astype(to)
     return {"x": x, "w": w}
+
+
+def chain_int(rows: int, cols: int, dtype: str = "i8") -> Spec:
+    """y = a * b + c in an int dtype (wraps modulo 2^width, limn README, "The
+    op set")."""
+    g = Spec(f"chain_{dtype}_{rows}x{cols}")
+    a = g.buffer("a", (rows, cols), dtype)
+    b = g.buffer("b", (rows, cols), dtype)
+    c = g.buffer("c", (rows, cols), dtype)
+    y = g.add(g.mul(a, b), c)
+    g.output(y)
+    return g
+
+
+def inputs_chain_int(rows: int, cols: int, dtype: str = "i8", seed: int = 8) -> dict:
+    """a, b, c uniform over the whole range of ``dtype``, in that order."""
+    rng = np.random.default_rng(seed)
+    info = np.iinfo({"i8": np.int8, "i16": np.int16, "i32": np.int32}[dtype])
+    mk = lambda: rng.integers(info.min, info.max + 1, (rows, cols), dtype=np.int64).astype(info.dtype)  # noqa: E731
+    return {"a": mk(), "b": mk(), "c": mk()}
 
 
 def inputs_layernorm(rows: int, n: int, seed: int = 4) -> dict:

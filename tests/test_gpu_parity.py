@@ -122,6 +122,38 @@ def test_rmsnorm(rows, n):
     assert np.all(np.abs(got.astype(np.float64) - ref) <= bound)
 
 
+@pytest.mark.parametrize("rows,n,dt", [(64, 4096, "f16"), (33, 1000, "f16"), (64, 4096, "f64"), (33, 1000, "f64")])
+def test_rmsnorm_dtype_variants(rows, n, dt):
+    """f64: the same bound in float64's unit. f16: every primitive rounds to
+    float16, so only the float32 square sum's order differs; it can move the
+    rounded sum by one float16 ulp (2^-10 relative), halved by SQRT, then
+    the few per-node roundings: 4 float16 ulps of y plus |y| 2^-10."""
+    _case(f"rmsnorm {dt} {rows}x{n}")
+    spec = synth.rmsnorm(rows, n, dtype=dt)
+    inp = synth.inputs_rmsnorm(rows, n, dtype=dt)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    g, r = got.astype(np.float64), ref.astype(np.float64)
+    if dt == "f64":
+        u = 2.0 ** -53
+        bound = np.abs(r) * (0.5 * 4 * gamma(n - 1, u) + 6 * u)
+    else:
+        ulp16 = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+        bound = 4 * ulp16 + np.abs(r) * 2.0 ** -10
+    report(f"rmsnorm_{dt}_{rows}x{n}", np.abs(g - r), bound)
+    assert np.all(np.abs(g - r) <= bound)
+
+
+@pytest.mark.parametrize("rows,cols,dt", [(256, 320, "i8"), (131, 77, "i16"), (64, 1000, "i32"), (8192, 8192, "i8")])
+def test_chain_int_wraps_bit_exact(rows, cols, dt):
+    _case(f"chain {dt} {rows}x{cols}")
+    spec = synth.chain_int(rows, cols, dt)
+    inp = synth.inputs_chain_int(rows, cols, dt)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    assert got.dtype == ref.dtype and got.tobytes() == ref.tobytes()
+
+
 # ---- config 4: LayerNorm (bf16 in/out) -----------------------------------------
 
 @pytest.mark.parametrize("rows,n", [(16, 8192), (9, 1000), (3, 256)])
@@ -222,6 +254,12 @@ def test_softmax_full_size():
 def test_rmsnorm_full_size():
     _case("rmsnorm full 16384x4096")
     test_rmsnorm(16384, 4096)
+
+
+def test_rmsnorm_dtype_variants_full_size():
+    _case("rmsnorm f16 and f64 full 16384x4096")
+    test_rmsnorm_dtype_variants(16384, 4096, "f16")
+    test_rmsnorm_dtype_variants(16384, 4096, "f64")
 
 
 def test_layernorm_full_size():
