@@ -37,6 +37,14 @@ notes of the repository):
     anywhere in the row gives NaN.
   * float -> bfloat16 CAST rounds to nearest even and keeps NaN a NaN;
     float -> int truncates toward zero.
+  * GATHER along an axis reads data at the position with that axis
+    coordinate replaced by the index (the index has the output's shape); an
+    index outside the axis reads zero, as a read outside a View's mask does.
+  * SCATTER along an axis adds each value into a copy of base at the
+    position with that axis coordinate replaced by the index; colliding adds
+    fold in ascending row-major order of the index positions, each one the
+    dtype's ADD (rounded to the dtype, wrapping for ints); an index outside
+    the axis drops its value.
   * a node too large to hold (the limn README warns that the reference runs
     out of memory on a large matmul) is evaluated in slabs along dim 0 when
     its consumer is a reduce that keeps dim 0. This changes no value: each
@@ -223,6 +231,20 @@ def infer(spec) -> list:
             out.append((tuple(1 if d in axes else s for d, s in enumerate(shp)), dt))
         elif op == "CONTIGUOUS":
             out.append(out[src[0]])
+        elif op == "GATHER":
+            (sd, dd), (si, di) = out[src[0]], out[src[1]]
+            ax = nd["axis"]
+            if di != "i32" or len(sd) != len(si) or not (0 <= ax < len(sd)) or \
+                    any(sd[d] != si[d] for d in range(len(sd)) if d != ax):
+                raise OracleError(f"node {i}: GATHER of {sd}/{dd} by {si}/{di} along {ax}")
+            out.append((si, dd))
+        elif op == "SCATTER":
+            (sb, db), (si, di), (sv, dv) = out[src[0]], out[src[1]], out[src[2]]
+            ax = nd["axis"]
+            if di != "i32" or sv != si or dv != db or len(sb) != len(si) or not (0 <= ax < len(sb)) or \
+                    any(sb[d] != si[d] for d in range(len(sb)) if d != ax):
+                raise OracleError(f"node {i}: SCATTER into {sb}/{db} of {sv}/{dv} by {si}/{di} along {ax}")
+            out.append((sb, db))
         elif op == "CUSTOM" and nd.get("kind") == "sdpa_fwd":
             (sq, dq), (sk, dk), (sv, dv) = out[src[0]], out[src[1]], out[src[2]]
             if len(sq) != 3 or sk != sv or len(sk) != 3 or sq[0] != sk[0] or sq[2] != sk[2] or \
@@ -365,6 +387,40 @@ def _reduce(op: str, x: np.ndarray, dt: str, axes) -> np.ndarray:
     return _narrow(res, dt).reshape(out_shape)
 
 
+def gather(data: np.ndarray, index: np.ndarray, axis: int, dt: str) -> np.ndarray:
+    """GATHER (limn README, "The op set", indexed): out[p] = data[p with its
+    ``axis`` coordinate replaced by index[p]]; an index outside the axis
+    reads the zero of the dtype (the reading for an out-of-range index, as
+    an out-of-mask View cell reads zero)."""
+    n = data.shape[axis]
+    ok = (index >= 0) & (index < n)
+    picked = np.take_along_axis(data, np.where(ok, index, 0).astype(np.int64), axis=axis)
+    return np.where(ok, picked, np.zeros((), data.dtype)).astype(data.dtype)
+
+
+def scatter(base: np.ndarray, index: np.ndarray, values: np.ndarray, axis: int, dt: str) -> np.ndarray:
+    """SCATTER (limn README, "The op set", indexed; "Backends": the C device
+    folds a scatter's colliding adds serially): a copy of base, then for
+    every position p of index in ascending row-major order, values[p] is
+    ADDed (the dtype's ADD, one rounding each) at p with its ``axis``
+    coordinate replaced by index[p]; an index outside the axis drops its
+    value. Positions that differ only off ``axis`` never collide, so the
+    loop runs over the ``axis`` coordinate in order with the rest at once."""
+    out = np.array(base, copy=True)
+    n = base.shape[axis]
+    idx = np.moveaxis(index, axis, 0)
+    val = np.moveaxis(values, axis, 0)
+    o = np.moveaxis(out, axis, 0)  # a view: writes land in out
+    rest = np.indices(idx.shape[1:]) if idx.ndim > 1 else np.zeros((0,), np.int64)
+    for k in range(idx.shape[0]):
+        sel = (idx[k] >= 0) & (idx[k] < n)
+        tgt = (np.where(sel, idx[k], 0),) + tuple(rest)
+        cur = np.asarray(o[tgt])
+        new = np.reshape(_binary("ADD", np.ascontiguousarray(cur), np.ascontiguousarray(val[k]), dt), cur.shape)
+        o[tgt] = np.where(sel, new, cur)
+    return out
+
+
 def sdpa_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool, out_dtype: str = "f32",
              block: int = 64):
     """Fused attention forward evaluated as the composition of primitives it
@@ -500,6 +556,15 @@ class Interpreter:
                 r = _reduce(op, np.ascontiguousarray(arg(src[0])), sdt, axes)
         elif op == "CONTIGUOUS":
             r = np.ascontiguousarray(arg(src[0])).copy()
+        elif op == "GATHER":
+            if rows is not None:
+                raise OracleError("GATHER is not evaluated in slabs")
+            r = gather(np.asarray(self.value(src[0])), np.asarray(self.value(src[1])), nd["axis"], dt)
+        elif op == "SCATTER":
+            if rows is not None:
+                raise OracleError("SCATTER is not evaluated in slabs")
+            r = scatter(np.asarray(self.value(src[0])), np.asarray(self.value(src[1])),
+                        np.asarray(self.value(src[2])), nd["axis"], dt)
         elif op == "CUSTOM":
             if rows is not None:
                 raise OracleError("a CUSTOM node is not evaluated in slabs")

@@ -96,6 +96,21 @@ class Spec:
     def max(self, x, axes): return self._add(op="MAX", src=(x,), axes=tuple(axes))
     def contiguous(self, x): return self._add(op="CONTIGUOUS", src=(x,))
 
+    # indexed (limn README, "The op set": GATHER, SCATTER) -------------
+    def gather(self, data, index, axis: int):
+        """out[p] = data[p with its ``axis`` coordinate replaced by index[p]]
+        (index int32, shaped like data but along ``axis``; an index outside
+        [0, data.shape[axis]) reads zero)."""
+        return self._add(op="GATHER", src=(data, index), axis=int(axis))
+
+    def scatter(self, base, index, values, axis: int, atomic: bool = False):
+        """base with values[p] added at p with its ``axis`` coordinate replaced
+        by index[p], for every p of index's shape in ascending row-major
+        order (colliding adds in that order; an index outside the axis drops
+        its value). ``atomic`` asks the device for unordered atomic adds
+        (the same value up to the order of colliding float adds)."""
+        return self._add(op="SCATTER", src=(base, index, values), axis=int(axis), atomic=bool(atomic))
+
     # the one CUSTOM kernel: fused attention forward --------------------
     def sdpa(self, q, k, v, scale: float, causal: bool = False, out_dtype: str = "f32"):
         """Fused attention forward as CUSTOM ``sdpa_fwd`` (limn README, "The op
@@ -403,6 +418,39 @@ def inputs_attention(h: int, tq: int, tk: int, d: int, seed: int = 6) -> dict:
     return {"Q": to_bf16_bits(_f32(rng.standard_normal((h, tq, d)))),
             "K": to_bf16_bits(_f32(rng.standard_normal((h, tk, d)))),
             "V": to_bf16_bits(_f32(rng.standard_normal((h, tk, d))))}
+
+
+def embedding_gather(vocab: int, dim: int, n: int, dtype: str = "f32") -> Spec:
+    """Rows of a (vocab, dim) table picked by n int32 ids: GATHER along axis 0
+    with the ids broadcast across the row (an (n, 1) id column expanded to
+    (n, dim))."""
+    g = Spec(f"embedding_gather_{vocab}x{dim}_{n}")
+    table = g.buffer("table", (vocab, dim), dtype)
+    ids = g.buffer("ids", (n, 1), "i32")
+    g.output(g.gather(table, g.view(ids, ("expand", (n, dim))), 0))
+    return g
+
+
+def embedding_scatter(vocab: int, dim: int, n: int, dtype: str = "f32", atomic: bool = False) -> Spec:
+    """The gather's transpose: n rows of values added into a zero (vocab, dim)
+    table at rows given by n int32 ids (repeated ids add up, in order)."""
+    g = Spec(f"embedding_scatter_{vocab}x{dim}_{n}" + ("_atomic" if atomic else ""))
+    vals = g.buffer("values", (n, dim), dtype)
+    ids = g.buffer("ids", (n, 1), "i32")
+    zero = g.const(0.0, (vocab, dim), dtype)
+    g.output(g.scatter(zero, g.view(ids, ("expand", (n, dim))), vals, 0, atomic))
+    return g
+
+
+def inputs_embedding(vocab: int, dim: int, n: int, seed: int = 9, dtype: str = "f32") -> dict:
+    """table ~ N(0, 1) (vocab, dim), ids uniform in [0, vocab) (n, 1), values
+    ~ N(0, 1) (n, dim), drawn in that order."""
+    rng = np.random.default_rng(seed)
+    to = {"f32": np.float32, "f16": np.float16, "f64": np.float64}[dtype]
+    table = rng.standard_normal((vocab, dim)).astype(to)
+    ids = rng.integers(0, vocab, (n, 1)).astype(np.int32)
+    values = rng.standard_normal((n, dim)).astype(to)
+    return {"table": table, "ids": ids, "values": values}
 
 
 def unary_map(op: str, n: int, dtype: str = "f32") -> Spec:

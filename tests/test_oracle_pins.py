@@ -595,3 +595,166 @@ def test_planted_missing_causal_mask_is_caught(monkeypatch):
                         real(q, k, v, scale, False, out_dtype, block))
     with pytest.raises(AssertionError):
         test_sdpa_closed_forms()
+
+
+# ---------------------------------------------------------------------------
+# indexed primitives: GATHER and SCATTER (limn README, "The op set", indexed;
+# "Backends": the C device folds a scatter's colliding adds serially)
+# ---------------------------------------------------------------------------
+
+def _gather_loops(data, index, axis):
+    """Brute force over every output position, written from the definition."""
+    out = np.zeros(index.shape, data.dtype)
+    for p in np.ndindex(*index.shape):
+        t = int(index[p])
+        if 0 <= t < data.shape[axis]:
+            q = list(p)
+            q[axis] = t
+            out[p] = data[tuple(q)]
+    return out
+
+
+def _scatter_loops(base, index, values, axis):
+    """Brute force: positions in row-major order, one float32 add each."""
+    out = base.copy()
+    for p in np.ndindex(*index.shape):
+        t = int(index[p])
+        if 0 <= t < base.shape[axis]:
+            q = list(p)
+            q[axis] = t
+            out[tuple(q)] = np.float32(out[tuple(q)] + values[p])
+    return out
+
+
+def _indexed_spec(kind, dshape, ishape, axis, dtype="f32"):
+    g = synth.Spec()
+    d = g.buffer("data", dshape, dtype)
+    i = g.buffer("index", ishape, "i32")
+    if kind == "gather":
+        g.output(g.gather(d, i, axis))
+    else:
+        v = g.buffer("values", ishape, dtype)
+        g.output(g.scatter(d, i, v, axis))
+    return g
+
+
+@pytest.mark.parametrize("axis", [0, 1, 2])
+def test_gather_brute_force_with_out_of_range(axis):
+    rng = np.random.default_rng(40 + axis)
+    data = rng.standard_normal((3, 4, 5)).astype(np.float32)
+    ishape = [3, 4, 5]
+    ishape[axis] = 7
+    index = rng.integers(-2, data.shape[axis] + 2, ishape).astype(np.int32)
+    got, = oracle.run(_indexed_spec("gather", data.shape, tuple(ishape), axis), {"data": data, "index": index})
+    assert got.tobytes() == _gather_loops(data, index, axis).tobytes()
+    assert np.all(got[(index < 0) | (index >= data.shape[axis])] == 0)
+
+
+def test_gather_identity_index_is_the_data():
+    data = np.arange(60, dtype=np.float32).reshape(3, 4, 5)
+    for axis in range(3):
+        shp = [1, 1, 1]
+        shp[axis] = data.shape[axis]
+        index = np.broadcast_to(np.arange(data.shape[axis], dtype=np.int32).reshape(shp), data.shape).copy()
+        got, = oracle.run(_indexed_spec("gather", data.shape, data.shape, axis), {"data": data, "index": index})
+        assert got.tobytes() == data.tobytes()
+
+
+def test_embedding_gather_picks_rows():
+    inp = synth.inputs_embedding(50, 6, 30)
+    got, = oracle.run(synth.embedding_gather(50, 6, 30), {k: inp[k] for k in ("table", "ids")})
+    for r in range(30):
+        assert got[r].tobytes() == inp["table"][inp["ids"][r, 0]].tobytes()
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_scatter_brute_force_with_collisions(axis):
+    rng = np.random.default_rng(50 + axis)
+    base = rng.standard_normal((6, 5)).astype(np.float32)
+    ishape = [6, 5]
+    ishape[axis] = 9
+    index = rng.integers(-1, base.shape[axis] + 1, ishape).astype(np.int32)
+    values = rng.standard_normal(ishape).astype(np.float32)
+    got, = oracle.run(_indexed_spec("scatter", base.shape, tuple(ishape), axis),
+                      {"data": base, "index": index, "values": values})
+    assert got.tobytes() == _scatter_loops(base, index, values, axis).tobytes()
+
+
+def test_scatter_of_ones_is_a_histogram():
+    rng = np.random.default_rng(60)
+    ids = rng.integers(0, 40, (500, 1)).astype(np.int32)
+    g = synth.Spec()
+    i = g.buffer("index", (500, 1), "i32")
+    g.output(g.scatter(g.const(0, (40, 1), "i32"), i, g.const(1, (500, 1), "i32"), 0))
+    got, = oracle.run(g, {"index": ids})
+    assert np.array_equal(got[:, 0], np.bincount(ids[:, 0], minlength=40))
+
+
+def test_scatter_collisions_fold_in_index_order():
+    """Three adds into one float32 cell: 1, then 1e8 (1e8 + 1 rounds to 1e8,
+    the spacing there being 8), then -1e8: 0 exactly. Any other order that
+    adds -1e8 before the 1 gives 1."""
+    g = _indexed_spec("scatter", (2,), (3,), 0)
+    got, = oracle.run(g, {"data": np.zeros(2, np.float32), "index": np.array([1, 1, 1], np.int32),
+                          "values": np.array([1.0, 1e8, -1e8], np.float32)})
+    assert got.tolist() == [0.0, 0.0]
+    got, = oracle.run(g, {"data": np.zeros(2, np.float32), "index": np.array([1, 1, 1], np.int32),
+                          "values": np.array([1e8, -1e8, 1.0], np.float32)})
+    assert got.tolist() == [0.0, 1.0]
+
+
+def test_scatter_drops_out_of_range_and_keeps_base():
+    g = _indexed_spec("scatter", (3,), (4,), 0)
+    got, = oracle.run(g, {"data": np.array([5, 6, 7], np.float32), "index": np.array([-1, 3, 99, 1], np.int32),
+                          "values": np.array([100, 200, 300, 0.5], np.float32)})
+    assert got.tolist() == [5.0, 6.5, 7.0]
+
+
+def test_scatter_narrow_dtypes_round_and_wrap_per_add():
+    """int8: 100 + 100 wraps to -56. float16: 2048 + 1 ties to even (2048),
+    three times over; one rounding of 2048 + 3 would give 2052."""
+    g = _indexed_spec("scatter", (1,), (2,), 0, "i8")
+    got, = oracle.run(g, {"data": np.zeros(1, np.int8), "index": np.zeros(2, np.int32),
+                          "values": np.array([100, 100], np.int8)})
+    assert got.tolist() == [-56]
+    g = _indexed_spec("scatter", (1,), (3,), 0, "f16")
+    got, = oracle.run(g, {"data": np.array([2048], np.float16), "index": np.zeros(3, np.int32),
+                          "values": np.ones(3, np.float16)})
+    assert got.tolist() == [2048.0]
+
+
+def test_gather_then_scatter_of_a_permutation_is_the_identity():
+    rng = np.random.default_rng(61)
+    data = rng.standard_normal((8, 3)).astype(np.float32)
+    perm = rng.permutation(8).astype(np.int32)
+    index = np.repeat(perm[:, None], 3, axis=1)
+    gathered, = oracle.run(_indexed_spec("gather", (8, 3), (8, 3), 0), {"data": data, "index": index})
+    back, = oracle.run(_indexed_spec("scatter", (8, 3), (8, 3), 0),
+                       {"data": np.zeros((8, 3), np.float32), "index": index, "values": gathered})
+    assert back.tobytes() == data.tobytes()
+
+
+def test_planted_reversed_scatter_order_is_caught(monkeypatch):
+    real = interp.scatter
+
+    def bad(base, index, values, axis, dt):
+        return real(base, np.flip(index, axis), np.flip(values, axis), axis, dt)
+    monkeypatch.setattr(interp, "scatter", bad)
+    with pytest.raises(AssertionError):
+        test_scatter_collisions_fold_in_index_order()
+
+
+def test_planted_gather_axis_mixup_is_caught(monkeypatch):
+    real = interp.gather
+    monkeypatch.setattr(interp, "gather", lambda data, index, axis, dt:
+                        real(data, index, (axis + 1) % data.ndim, dt) if data.ndim > 1 else real(data, index, axis, dt))
+    with pytest.raises(Exception):
+        test_gather_brute_force_with_out_of_range(0)
+
+
+def test_planted_scatter_without_base_is_caught(monkeypatch):
+    real = interp.scatter
+    monkeypatch.setattr(interp, "scatter", lambda base, index, values, axis, dt:
+                        real(np.zeros_like(base), index, values, axis, dt))
+    with pytest.raises(AssertionError):
+        test_scatter_drops_out_of_range_and_keeps_base()
