@@ -53,7 +53,7 @@ extern "C" {
 typedef enum rv_status {
     RV_OK = 0,
     RV_E_INVALID = -1,            /* malformed argument or graph */
-    RV_E_UNSUPPORTED_OP = -2,     /* GATHER, SCATTER, ASSIGN, CUSTOM, unknown */
+    RV_E_UNSUPPORTED_OP = -2,     /* ASSIGN, an unknown CUSTOM kernel, a narrow atomic scatter */
     RV_E_UNSUPPORTED_LAYOUT = -3, /* e.g. a reshape that does not compose into one View */
     RV_E_DTYPE = -4,              /* dtype rule broken (mixed operands, EXP of an int, ...) */
     RV_E_OUT_OF_BOUNDS = -5,      /* a View can address outside its buffer */
@@ -70,8 +70,8 @@ typedef enum rv_dtype {
 } rv_dtype;
 
 /* limn README, "The op set". CMPLT yields RV_I8 0/1; WHERE treats a nonzero
- * condition as true. GATHER, SCATTER and ASSIGN are declined with
- * RV_E_UNSUPPORTED_OP; so is CUSTOM unless it names RV_CUSTOM_SDPA_FWD. */
+ * condition as true. ASSIGN is declined with RV_E_UNSUPPORTED_OP; so is
+ * CUSTOM unless it names RV_CUSTOM_SDPA_FWD. */
 typedef enum rv_op {
     RV_BUFFER = 0, RV_CONST = 1, RV_VIEW = 2,
     RV_NEG = 3, RV_EXP = 4, RV_LOG = 5, RV_SQRT = 6, RV_RECIP = 7, RV_CAST = 8,
@@ -103,6 +103,30 @@ typedef enum rv_op {
  * the bound that rounding implies. */
 #define RV_CUSTOM_SDPA_FWD 1
 #define RV_SDPA_CAUSAL 1u
+
+/* Indexed ops (limn README, "The op set", indexed). `reduce_axes` holds
+ * exactly one bit: the axis a.
+ *   GATHER : src[0] = data, src[1] = index (RV_I32) shaped like data except
+ *            along a. out[p] = data[p with coordinate a replaced by
+ *            index[p]]; shape and a of the index, dtype of the data; an
+ *            index outside [0, data extent along a) reads zero.
+ *   SCATTER: src[0] = base, src[1] = index (RV_I32) shaped like base except
+ *            along a, src[2] = values (the index's shape, the base's dtype).
+ *            out = base, then values[p] is added at p with coordinate a
+ *            replaced by index[p]; an index outside the axis drops its value.
+ *            `buf` picks how colliding adds combine:
+ *              RV_SCATTER_ORDERED: in ascending row-major order of p, each
+ *                add rounded to the dtype (limn README, "Backends": the C
+ *                device folds a scatter's colliding adds serially); the
+ *                same bits on every run, every dtype;
+ *              RV_SCATTER_ATOMIC: hardware atomic adds in whatever order
+ *                they land (limn README, "Backends": the cuda device's
+ *                scatter); f32, f64 and i32 only (RV_E_UNSUPPORTED_OP
+ *                otherwise); ints are exact, floats agree with the ordered
+ *                result up to the order of colliding adds.
+ * Index cells, and each dim, must fit in 32 bits (RV_E_INVALID otherwise). */
+#define RV_SCATTER_ORDERED 0
+#define RV_SCATTER_ATOMIC 1
 
 /* A View (limn README, "Architecture"): cell i of `shape` reads element
  * offset + sum_d i_d * strides[d] of its source's row-major storage when

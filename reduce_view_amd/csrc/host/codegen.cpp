@@ -214,6 +214,13 @@ struct Gen {
         for (auto& L : k.leaves)
             if (!L.zero) upd(L.v);
         for (auto& s : k.stores) upd(s.v);
+        for (auto& e : k.ex) {  // a gathered read reaches index * g_stride further
+            int64_t lo, hi;
+            if (e.op != RV_GATHER || k.leaves[e.leaf].zero || !view_addr_range(k.leaves[e.leaf].v, &lo, &hi)) continue;
+            const int64_t far = (e.g_hi - e.g_lo) * std::abs(e.g_stride);
+            mx = std::max({mx, hi + far + 1, -(lo - far) + 1});
+        }
+        if (k.cls == KClass::SCATTER) mx = std::max(mx, numel(k.sc_out_shape) + 1);
         I = mx < (int64_t(1) << 30) ? "int" : "long long";
         const char* nt = getenv("RV_NT");
         nt_on = !(nt && std::string(nt) == "0");
@@ -303,7 +310,49 @@ struct Gen {
         return true;
     }
 
+    // Scalar code for value `e` (its operands first, each once) at domain
+    // index expressions idx; the value is named s<e><sfx>.
+    void scalar(std::ostringstream& b, int e, const std::vector<std::string>& idx, const std::string& ind,
+                const std::string& sfx, std::vector<char>& done) {
+        if (e < 0 || done[e]) return;
+        const Ex& x = k.ex[e];
+        scalar(b, x.a, idx, ind, sfx, done);
+        scalar(b, x.b, idx, ind, sfx, done);
+        scalar(b, x.c, idx, ind, sfx, done);
+        done[e] = 1;
+        const std::string V = fmt("s%d%s", e, sfx.c_str());
+        auto E = [&](int i) { return i < 0 ? std::string() : fmt("s%d%s", i, sfx.c_str()); };
+        std::vector<int> all;
+        for (int d = 0; d < rank; ++d) all.push_back(d);
+        b << ind << "const " << vt(x.dtype) << " " << V << " = ";
+        if (x.op == RV_BUFFER || x.op == RV_GATHER) {
+            const Leaf& L = k.leaves[x.leaf];
+            if (L.zero || (x.op == RV_GATHER && x.g_hi <= x.g_lo)) {
+                b << zero_of(x.dtype) << ";\n";
+                return;
+            }
+            std::string mc = mask_cond(L.v, idx, all);
+            std::string a = addr(L.v, idx);
+            if (x.op == RV_GATHER) {
+                const std::string T = E(x.a);
+                mc = fmt("(%s) >= %lld && (%s) < %lld", T.c_str(), (long long)x.g_lo, T.c_str(), (long long)x.g_hi) +
+                     (mc.empty() ? "" : " && " + mc);
+                a += " + (" + I + ")((" + T + ") - " + std::to_string(x.g_lo) + ") * " + lit(x.g_stride);
+            }
+            const std::string P = pname(L.loc, L.dtype, false);
+            b << (mc.empty() ? "" : "(" + mc + ") ? ") << ld(L.dtype, P + "[" + a + "]")
+              << (mc.empty() ? "" : " : " + zero_of(x.dtype)) << ";\n";
+        } else if (x.op == RV_CONST) {
+            b << const_lit(x.dtype, x.cval) << ";\n";
+        } else {
+            b << op_code(k, x, E(x.a), E(x.b), E(x.c)) << ";\n";
+        }
+    }
+
+    void gather_rowmajor(std::ostringstream& b, const Ex& x, int u, const std::string& V, int VW, int64_t NX,
+                         bool full_chunks, const std::vector<int>& outer, const std::vector<std::string>& idx);
     std::string gen();
+    std::string gen_scatter();
     std::string gen_rowmajor();
     std::string gen_tiled();
     std::string gen_row();
@@ -319,6 +368,52 @@ struct Gen {
 // the innermost dim; operands that are contiguous along it are read as one
 // vector, stride-0 operands once, others cell by cell.
 // ---------------------------------------------------------------------------
+// GATHER in the row-major plan: cell by cell, the data read at its View's
+// address plus index * g_stride; when the index is the same across the
+// chunk (constant along the lane dim) and the data is contiguous along it,
+// one vector read.
+void Gen::gather_rowmajor(std::ostringstream& b, const Ex& x, int u, const std::string& V, int VW, int64_t NX,
+                          bool full_chunks, const std::vector<int>& outer, const std::vector<std::string>& idx) {
+    const int X = rank - 1;
+    const Leaf& L = k.leaves[x.leaf];
+    if (L.zero || x.g_hi <= x.g_lo) return;  // every cell reads zero
+    const std::string P = pname(L.loc, L.dtype, false);
+    const std::string xs = "x" + std::to_string(u);
+    const std::string T = fmt("e%d_%d", x.a, u);
+    std::string rowok = "cv" + std::to_string(u);
+    const std::string oc = mask_cond(L.v, idx, outer);
+    if (!oc.empty()) rowok += " && " + oc;
+    auto idx0 = idx;
+    idx0[X] = "";
+    const std::string base = addr(L.v, idx0);
+    const std::string inr = fmt("%s >= %lld && %s < %lld", "t", (long long)x.g_lo, "t", (long long)x.g_hi);
+    b << "    {\n";
+    const int64_t gs = x.g_stride;
+    if (VW > 1 && ex_invariant(k, x.a, X) && leaf_vec_ok(L, X, VW) && gs % VW == 0) {
+        std::string xm = masked(L.v, X) ? fmt(" && %s >= %s && %s + %d <= %s", xs.c_str(), lit(L.v.mask_lo[X]).c_str(),
+                                              xs.c_str(), VW, lit(L.v.mask_hi[X]).c_str())
+                                        : "";
+        std::string fullc = full_chunks ? "" : fmt(" && %s + %d <= %s", xs.c_str(), VW, lit(NX).c_str());
+        b << "      const int t = " << T << "[0];\n";
+        b << "      if (" << rowok << " && " << inr << xm << fullc << ") {\n";
+        b << "        const rv_pack<" << st(L.dtype) << ", " << VW << "> v = rv_ldv<" << st(L.dtype) << ", " << VW << ">("
+          << P << " + " << base << " + " << xs << " + (" << I << ")(t - " << x.g_lo << ") * " << lit(gs) << ");\n";
+        b << "        for (int q = 0; q < " << VW << "; ++q) " << V << "[q] = " << ld(L.dtype, "v.v[q]") << ";\n";
+        b << "      } else\n";
+    }
+    b << "      for (int q = 0; q < " << VW << "; ++q) {\n";
+    b << "        const " << I << " x = " << xs << " + q;\n";
+    b << "        const int t = " << T << "[q];\n";
+    auto idxq = idx;
+    idxq[X] = "x";
+    std::string xc = mask_cond(L.v, idxq, {X});
+    b << "        if (" << rowok << " && x < " << lit(NX) << (xc.empty() ? "" : " && " + xc) << " && " << inr << ") "
+      << V << "[q] = " << ld(L.dtype, P + "[" + addr(L.v, idxq) + " + (" + I + ")(t - " + std::to_string(x.g_lo) +
+                             ") * " + lit(gs) + "]")
+      << ";\n";
+    b << "      }\n    }\n";
+}
+
 std::string Gen::gen_rowmajor() {
     const int X = rank - 1;
     int VW = 1, U = 4;  // plan values (lower.cpp)
@@ -410,6 +505,11 @@ std::string Gen::gen_rowmajor() {
             std::string V = fmt("e%zu_%d", e, u);
             b << "    " << vt(x.dtype) << " " << V << "[" << VW << "];\n";
             b << "    for (int q = 0; q < " << VW << "; ++q) " << V << "[q] = ";
+            if (x.op == RV_GATHER) {
+                b << zero_of(x.dtype) << ";\n";
+                gather_rowmajor(b, x, u, V, VW, NX, full_chunks, outer, idx_of(u, "x" + std::to_string(u)));
+                continue;
+            }
             if (x.op == RV_BUFFER) {
                 if (k.leaves[x.leaf].zero)
                     b << zero_of(x.dtype);
@@ -1421,6 +1521,214 @@ std::string Gen::gen_cells() {
     return b.str();
 }
 
+// ---------------------------------------------------------------------------
+// SCATTER steps (limn README, "The op set", indexed; "Backends": the C
+// device folds colliding adds serially, the cuda device adds atomically).
+// The target already holds the base. Domain: the index's shape.
+// ---------------------------------------------------------------------------
+std::string Gen::gen_scatter() {
+    std::ostringstream b;
+    const Shape& osh = k.sc_out_shape;
+    const int A = k.sc_axis, dt = k.sc_dtype;
+    const int64_t CELLS = k.sc_cells, KN = k.sc_keys_n, NB = (CELLS + 2047) / 2048;
+    std::vector<int64_t> os(osh.size());
+    for (int64_t d = (int64_t)osh.size() - 1, st_ = 1; d >= 0; --d) {
+        os[d] = st_;
+        st_ *= osh[d];
+    }
+    std::vector<int> cd, fd;  // dims of an index cell / carried dims
+    for (int d = 0; d < rank; ++d) ((k.sc_fdims >> d) & 1u ? fd : cd).push_back(d);
+    auto ureg = [&](int r, bool write) {
+        std::string P = pname(Loc{2, r}, RV_I32, write);
+        return std::string(write ? "((unsigned*)" : "((const unsigned*)") + P + ")";
+    };
+    // decompose integer expression `v` over `dims` (row-major) into
+    // variables <pfx><d>
+    auto decompose = [&](const std::string& v, const std::vector<int>& dims, const std::string& pfx,
+                         const std::string& ind) {
+        std::string rem = v;
+        for (size_t j = dims.size(); j-- > 0;) {
+            const int d = dims[j];
+            const int64_t n = k.domain[d];
+            b << ind << "const long long " << pfx << d << " = " << (j ? fmt("(%s) %% %lldLL", rem.c_str(), (long long)n)
+                                                                      : rem)
+              << ";\n";
+            if (j) {
+                b << ind << "const long long " << pfx << "q" << d << " = (" << rem << ") / " << n << "LL;\n";
+                rem = pfx + "q" + std::to_string(d);
+            }
+        }
+    };
+    const std::string& part = k.sc_part;
+    const int cur = k.sc_pass % 2, nxt = 1 - cur;
+    if (part == "hist") {
+        b << "  rv_rs_hist(" << ureg(k.sc_reg_keys[cur], false) << ", " << ureg(k.sc_reg_counts, true) << ", " << CELLS
+          << "LL, " << NB << "u, " << 8 * k.sc_pass << ");\n";
+        return b.str();
+    }
+    if (part == "scan") {
+        b << "  rv_rs_scan(" << ureg(k.sc_reg_counts, true) << ", " << NB << "u);\n";
+        return b.str();
+    }
+    if (part == "move") {
+        b << "  rv_rs_move(" << ureg(k.sc_reg_keys[cur], false) << ", " << ureg(k.sc_reg_vals[cur], false) << ", "
+          << ureg(k.sc_reg_keys[nxt], true) << ", " << ureg(k.sc_reg_vals[nxt], true) << ", "
+          << ureg(k.sc_reg_counts, false) << ", " << CELLS << "LL, " << NB << "u, " << 8 * k.sc_pass << ");\n";
+        return b.str();
+    }
+    const std::string OUT = pname(k.sc_out, dt, true);
+    if (part == "atomic") {
+        std::vector<int> all;
+        for (int d = 0; d < rank; ++d) all.push_back(d);
+        b << "  for (long long p = (long long)blockIdx.x * 256 + threadIdx.x; p < " << numel(k.domain)
+          << "LL; p += (long long)gridDim.x * 256) {\n";
+        decompose("p", all, "i", "    ");
+        std::vector<std::string> idx;
+        for (int d = 0; d < rank; ++d) idx.push_back(fmt("i%d", d));
+        std::vector<char> done(k.ex.size(), 0);
+        scalar(b, k.sc_index, idx, "    ", "", done);
+        scalar(b, k.sc_values, idx, "    ", "", done);
+        std::string a = fmt("(long long)t * %lldLL", (long long)os[A]);
+        for (int d = 0; d < rank; ++d)
+            if (d != A) a += fmt(" + i%d * %lldLL", d, (long long)os[d]);
+        b << "    const int t = s" << k.sc_index << ";\n";
+        b << "    if (t >= 0 && t < " << osh[A] << ") rv_atomic_add(" << OUT << " + (" << a << "), s" << k.sc_values
+          << ");\n";
+        b << "  }\n";
+        return b.str();
+    }
+    std::vector<int> idims;  // the dims a key walks besides the axis
+    int64_t PI = 1;
+    for (int d : cd)
+        if (d != A) {
+            idims.push_back(d);
+            PI *= k.domain[d];
+        }
+    if (part == "keys") {
+        b << "  for (long long c = (long long)blockIdx.x * 256 + threadIdx.x; c < " << CELLS
+          << "LL; c += (long long)gridDim.x * 256) {\n";
+        decompose("c", cd, "i", "    ");
+        std::vector<std::string> idx(rank, "0");
+        for (int d : cd) idx[d] = fmt("i%d", d);
+        std::vector<char> done(k.ex.size(), 0);
+        scalar(b, k.sc_index, idx, "    ", "", done);
+        std::string lin = "0LL";
+        int64_t m = 1;
+        for (size_t j = idims.size(); j-- > 0;) {
+            lin += fmt(" + i%d * %lldLL", idims[j], (long long)m);
+            m *= k.domain[idims[j]];
+        }
+        b << "    const int t = s" << k.sc_index << ";\n";
+        b << "    const unsigned key = (t >= 0 && t < " << osh[A] << ") ? (unsigned)((long long)t * " << PI << "LL + "
+          << lin << ") : " << KN << "u;\n";
+        b << "    " << ureg(k.sc_reg_keys[0], true) << "[c] = key;\n";
+        b << "    " << ureg(k.sc_reg_vals[0], true) << "[c] = (unsigned)c;\n";
+        b << "  }\n";
+        return b.str();
+    }
+    // fold: a group of TPS lanes per sorted position; a group whose position
+    // starts a run of equal keys adds the run's values, in sorted (= index)
+    // order, to the target cells of every carried position, JU cells at a
+    // time, CB carried positions per lane
+    const int fin = k.sc_passes % 2;
+    const int64_t NF = numel(k.domain) / CELLS;
+    int TPS = 1;
+    while (TPS < 256 && TPS < NF) TPS *= 2;
+    const int SPB = 256 / TPS;
+    const int CB = (int)std::min<int64_t>(8, (NF + TPS - 1) / TPS);
+    const int JU = 4;
+    const std::string K = "K", VV = "VV";
+    b << "  const unsigned* __restrict__ K = " << ureg(k.sc_reg_keys[fin], false) << ";\n";
+    b << "  const unsigned* __restrict__ VV = " << ureg(k.sc_reg_vals[fin], false) << ";\n";
+    b << "  const int l = threadIdx.x % " << TPS << ";\n";
+    b << "  for (long long s = (long long)blockIdx.x * " << SPB << " + threadIdx.x / " << TPS << "; s < " << CELLS
+      << "LL; s += (long long)gridDim.x * " << SPB << ") {\n";
+    b << "    const unsigned key = K[s];\n";
+    b << "    if (key >= " << KN << "u || (s > 0 && K[s - 1] == key)) continue;\n";
+    b << "    long long e = s + 1;\n";
+    if (TPS >= 64) {
+        // the whole wave is one group: 64 keys per step
+        b << "    for (;;) {\n";
+        b << "      const long long j = e + (threadIdx.x & 63);\n";
+        b << "      const unsigned kj = j < " << CELLS << "LL ? K[j] : 0xffffffffu;\n";
+        b << "      const unsigned long long m = __builtin_amdgcn_ballot_w64(kj != key);\n";
+        b << "      if (m != 0ull) { e += __ffsll((long long)m) - 1; break; }\n";
+        b << "      e += 64;\n";
+        b << "    }\n";
+    } else {
+        b << "    while (e < " << CELLS << "LL && K[e] == key) ++e;\n";
+    }
+    b << "    const long long t = key / " << PI << "u;\n";
+    b << "    const long long r = key % " << PI << "u;\n";
+    {
+        std::string rem = "r";
+        for (size_t j = idims.size(); j-- > 0;) {
+            const int d = idims[j];
+            b << "    const long long o" << d << " = " << (j ? fmt("%s %% %lldLL", rem.c_str(), (long long)k.domain[d]) : rem)
+              << ";\n";
+            if (j) {
+                b << "    const long long oq" << d << " = " << rem << " / " << k.domain[d] << "LL;\n";
+                rem = fmt("oq%d", d);
+            }
+        }
+    }
+    std::string ob = fmt("t * %lldLL", (long long)os[A]);
+    for (int d : idims) ob += fmt(" + o%d * %lldLL", d, (long long)os[d]);
+    b << "    const long long ob = " << ob << ";\n";
+    b << "    for (long long f0 = l; f0 < " << NF << "LL; f0 += " << (int64_t)TPS * CB << "LL) {\n";
+    b << "      " << vt(dt) << " acc[" << CB << "];\n";
+    b << "      long long fo[" << CB << "];\n";
+    for (int d : fd) b << "      long long fc" << d << "[" << CB << "];\n";
+    b << "#pragma unroll\n";
+    b << "      for (int cb = 0; cb < " << CB << "; ++cb) {\n";
+    b << "        const long long f = f0 + (long long)cb * " << TPS << ";\n";
+    b << "        const long long fcl = f < " << NF << "LL ? f : " << NF - 1 << "LL;\n";
+    decompose("fcl", fd, "fi", "        ");
+    std::string fo = "0LL";
+    for (int d : fd) {
+        b << "        fc" << d << "[cb] = fi" << d << ";\n";
+        fo += fmt(" + fi%d * %lldLL", d, (long long)os[d]);
+    }
+    b << "        fo[cb] = " << fo << ";\n";
+    b << "        acc[cb] = f < " << NF << "LL ? " << ld(dt, OUT + "[ob + fo[cb]]") << " : " << zero_of(dt) << ";\n";
+    b << "      }\n";
+    b << "      for (long long j0 = s; j0 < e; j0 += " << JU << ") {\n";
+    b << "        unsigned cj[" << JU << "];\n";
+    b << "#pragma unroll\n";
+    b << "        for (int u = 0; u < " << JU << "; ++u) cj[u] = j0 + u < e ? min(VV[j0 + u], " << CELLS - 1
+      << "u) : 0u;\n";
+    b << "        " << vt(dt) << " vv[" << JU << "][" << CB << "];\n";
+    b << "#pragma unroll\n";
+    b << "        for (int u = 0; u < " << JU << "; ++u) {\n";
+    decompose("(long long)cj[u]", cd, "i", "          ");
+    b << "#pragma unroll\n";
+    b << "          for (int cb = 0; cb < " << CB << "; ++cb) {\n";
+    std::vector<std::string> idx(rank);
+    for (int d : cd) idx[d] = fmt("i%d", d);
+    for (int d : fd) idx[d] = fmt("fc%d[cb]", d);
+    std::vector<char> done(k.ex.size(), 0);
+    scalar(b, k.sc_values, idx, "            ", "", done);
+    b << "            vv[u][cb] = s" << k.sc_values << ";\n";
+    b << "          }\n";
+    b << "        }\n";
+    Ex add;
+    add.op = RV_ADD;
+    add.dtype = dt;
+    b << "#pragma unroll\n";
+    b << "        for (int u = 0; u < " << JU << "; ++u)\n";
+    b << "#pragma unroll\n";
+    b << "          for (int cb = 0; cb < " << CB << "; ++cb)\n";
+    b << "            if (j0 + u < e) acc[cb] = " << op_code(k, add, "acc[cb]", "vv[u][cb]", "") << ";\n";
+    b << "      }\n";
+    b << "#pragma unroll\n";
+    b << "      for (int cb = 0; cb < " << CB << "; ++cb)\n";
+    b << "        if (f0 + (long long)cb * " << TPS << " < " << NF << "LL) " << OUT << "[ob + fo[cb]] = "
+      << sv(dt, "acc[cb]") << ";\n";
+    b << "    }\n";
+    b << "  }\n";
+    return b.str();
+}
+
 // ATTN: the fused attention forward skeleton (kernels/rv_device.hpp) with
 // the head width, causal flag, output dtype and the base-2 score scale
 // baked in.
@@ -1560,6 +1868,7 @@ std::string Gen::gen() {
         case KClass::REDUCE: body = gen_cells(); break;
         case KClass::FOLD: body = gen_fold(); break;
         case KClass::ATTN: body = gen_attn(); break;
+        case KClass::SCATTER: body = gen_scatter(); break;
         case KClass::MFMA: {
             std::string s = gen_gemm();
             size_t at = s.find("@@BODY@@");

@@ -4,8 +4,9 @@
 // limn README, "The op set": the primitives and the dtype rules (equal
 // dtypes for binary ops here: promotion between dtypes is a frontend concern,
 // so a mixed pair is RV_E_DTYPE). "Reading the schedule": a reduce keeps its
-// reduced dims with size 1. GATHER/SCATTER/ASSIGN/CUSTOM are declined with a
-// typed error (Tiki README, "Compile model code").
+// reduced dims with size 1. ASSIGN, and CUSTOM kernels other than the
+// attention forward, are declined with a typed error (Tiki README, "Compile
+// model code").
 #include <algorithm>
 
 #include "graph.hpp"
@@ -22,8 +23,8 @@ bool is_reduce(int op) { return op == RV_SUM || op == RV_MAX; }
 static int arity(int op) {
     switch (op) {
         case RV_BUFFER: case RV_CONST: return 0;
-        case RV_ADD: case RV_MUL: case RV_CMPLT: return 2;
-        case RV_WHERE: case RV_CUSTOM: return 3;
+        case RV_ADD: case RV_MUL: case RV_CMPLT: case RV_GATHER: return 2;
+        case RV_WHERE: case RV_CUSTOM: case RV_SCATTER: return 3;
         default: return 1;
     }
 }
@@ -71,7 +72,7 @@ Graph intake(const rv_node* nodes, int32_t n, const int32_t* outputs, int32_t no
         Node& nd = g.nodes[i];
         nd.op = in.op;
         if (in.op < 0 || in.op > RV_CUSTOM) fail(RV_E_INVALID, fmt("node %d: unknown op %d", i, in.op));
-        if (in.op >= RV_GATHER && !(in.op == RV_CUSTOM && in.buf == RV_CUSTOM_SDPA_FWD))
+        if (in.op == RV_ASSIGN || (in.op == RV_CUSTOM && in.buf != RV_CUSTOM_SDPA_FWD))
             fail(RV_E_UNSUPPORTED_OP, fmt("node %d: %s%s is not supported by this library", i, op_name(in.op),
                                           in.op == RV_CUSTOM ? fmt(" kernel %d", in.buf).c_str() : ""));
         nd.nsrc = arity(in.op);
@@ -157,6 +158,55 @@ Graph intake(const rv_node* nodes, int32_t n, const int32_t* outputs, int32_t no
                 nd.shape = S(0).shape;
                 nd.dtype = S(0).dtype;
                 break;
+            case RV_GATHER: case RV_SCATTER: {
+                // index (src 1) has the data's / base's shape but along the
+                // axis; SCATTER's values (src 2) have the index's shape
+                const char* nm = op_name(in.op);
+                const Shape& d = S(0).shape;
+                const Shape& ix = S(1).shape;
+                uint32_t ax = in.reduce_axes;
+                if (ax == 0 || (ax & (ax - 1)) != 0 || (d.size() < 32 && (ax >> d.size()) != 0))
+                    fail(RV_E_INVALID, fmt("node %d: %s needs exactly one axis bit inside rank %zu, got 0x%x", i, nm,
+                                           d.size(), ax));
+                int a = 0;
+                while (!((ax >> a) & 1u)) ++a;
+                if (S(1).dtype != RV_I32)
+                    fail(RV_E_DTYPE, fmt("node %d: %s index must be i32, got %s", i, nm, dtype_name(S(1).dtype)));
+                bool ok = ix.size() == d.size();
+                for (size_t k = 0; ok && k < d.size(); ++k) ok = (int)k == a || ix[k] == d[k];
+                if (!ok)
+                    fail(RV_E_INVALID, fmt("node %d: %s index shape %s must equal %s but along axis %d", i, nm,
+                                           shape_str(ix).c_str(), shape_str(d).c_str(), a));
+                nd.axis = a;
+                if (in.op == RV_GATHER) {
+                    if (in.buf != 0) fail(RV_E_INVALID, fmt("node %d: GATHER takes no flags", i));
+                    nd.shape = ix;
+                    nd.dtype = S(0).dtype;
+                } else {
+                    if (S(2).shape != ix)
+                        fail(RV_E_INVALID, fmt("node %d: SCATTER values shape %s differs from the index's %s", i,
+                                               shape_str(S(2).shape).c_str(), shape_str(ix).c_str()));
+                    if (S(2).dtype != S(0).dtype)
+                        fail(RV_E_DTYPE, fmt("node %d: SCATTER values %s into a %s base", i, dtype_name(S(2).dtype),
+                                             dtype_name(S(0).dtype)));
+                    if (in.buf != RV_SCATTER_ORDERED && in.buf != RV_SCATTER_ATOMIC)
+                        fail(RV_E_INVALID, fmt("node %d: SCATTER mode %d", i, in.buf));
+                    nd.atomic = in.buf == RV_SCATTER_ATOMIC;
+                    const int dt = S(0).dtype;
+                    if (nd.atomic && dt != RV_F32 && dt != RV_F64 && dt != RV_I32)
+                        fail(RV_E_UNSUPPORTED_OP,
+                             fmt("node %d: an atomic SCATTER of %s would also rewrite neighbouring cells of the word; "
+                                 "atomic adds cover f32, f64 and i32 (the ordered mode covers every dtype)",
+                                 i, dtype_name(dt)));
+                    nd.shape = d;
+                    nd.dtype = dt;
+                }
+                for (int64_t e : nd.shape)
+                    if (e > (int64_t(1) << 31) - 1) fail(RV_E_INVALID, fmt("node %d: %s dims must fit in int32", i, nm));
+                if (numel(ix) >= (int64_t(1) << 32) - 1)
+                    fail(RV_E_INVALID, fmt("node %d: %s of 2^32 or more index cells", i, nm));
+                break;
+            }
             case RV_CUSTOM: {  // sdpa_fwd (the only CUSTOM kernel)
                 const Shape &q = S(0).shape, &k = S(1).shape, &v = S(2).shape;
                 for (int j = 0; j < 3; ++j)
@@ -212,6 +262,7 @@ const char* kclass_name(KClass k) {
         case KClass::MFMA: return "MFMA";
         case KClass::FOLD: return "FOLD";
         case KClass::ATTN: return "ATTN";
+        case KClass::SCATTER: return "SCATTER";
     }
     return "?";
 }

@@ -29,6 +29,9 @@ struct Node {
     int custom = 0;
     int cout = 0;
     bool causal = false;
+    // GATHER / SCATTER: the indexed axis; SCATTER: unordered atomic adds
+    int axis = 0;
+    bool atomic = false;
 };
 
 struct Graph {
@@ -50,7 +53,7 @@ bool pure_broadcast(const rv_view& v, const Shape& src_shape, std::vector<int>* 
 // ---------------------------------------------------------------------------
 // kernels (schedule.cpp / lower.cpp / codegen.cpp)
 // ---------------------------------------------------------------------------
-enum class KClass { EW, ROW, REDUCE, MFMA, FOLD, ATTN };
+enum class KClass { EW, ROW, REDUCE, MFMA, FOLD, ATTN, SCATTER };
 constexpr int EX_MFMA_ACC = 1000;  // Ex op: the contraction's accumulator at (m, n)
 const char* kclass_name(KClass k);
 
@@ -80,6 +83,10 @@ struct Ex {
     uint32_t axes = 0;  // reduce dims (domain dims) for SUM/MAX
     bool stat = false;  // ROW kernels: constant along the reduced dims
     int node = -1;      // graph node this value came from (for describe)
+    // GATHER: a = the index, leaf = the data at index g_lo along the
+    // gathered axis (stride 0 there); the cell read is
+    // leaf + (index - g_lo) * g_stride when g_lo <= index < g_hi, else zero
+    int64_t g_stride = 0, g_lo = 0, g_hi = 0;
 };
 
 // One value the kernel writes: `ex` stored through view `v` (over the
@@ -119,6 +126,26 @@ struct Kernel {
     // ATTN (leaves q, k, v; domain (H, Tq, D); Tk = leaves[1].v.shape[1])
     double attn_scale = 0.0;
     bool attn_causal = false;
+    // SCATTER: one step of a scatter-add into `sc_out` (already holding the
+    // base). Domain: the index's shape; ex sc_index / sc_values over it.
+    //   "atomic": every position adds its value with an atomic add
+    //   "keys":   one key per index cell (the target along the axis and the
+    //             dims the index varies along), sentinel sc_keys_n when the
+    //             index is outside the axis
+    //   "hist", "scan", "move": one stable 8-bit radix pass over the keys
+    //   "fold":   each run of equal sorted keys adds its values, in index
+    //             order, into the target cells
+    std::string sc_part;
+    int sc_index = -1, sc_values = -1;
+    int sc_axis = 0;
+    Loc sc_out;
+    Shape sc_out_shape;
+    int sc_dtype = RV_F32;
+    uint32_t sc_fdims = 0;      // dims the index is constant along (carried)
+    int64_t sc_cells = 0;       // index cells (positions with the carried dims at 0)
+    int64_t sc_keys_n = 0;      // valid keys: out extent along the axis x varying dims
+    int sc_pass = 0, sc_passes = 0;
+    int sc_reg_keys[2] = {-1, -1}, sc_reg_vals[2] = {-1, -1}, sc_reg_counts = -1;
 };
 
 struct Region {
@@ -165,6 +192,8 @@ std::vector<Loc> kernel_param_locs(const Program& p, const Kernel& k);
 // float32, which the streaming plan folds in one pass with the online
 // max/denominator recurrence.
 std::vector<std::pair<int, int>> online_softmax_pairs(const Kernel& k);
+// Value `e` of kernel `k` is the same at every index along domain dim `d`.
+bool ex_invariant(const Kernel& k, int e, int d);
 bool mfma_supported(const Shape& dom, const rv_view& a, const rv_view& b, std::string* why);
 
 }  // namespace rv

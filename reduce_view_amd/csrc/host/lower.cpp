@@ -129,6 +129,21 @@ static void prove_in_bounds(const Program& p, const Kernel& k) {
     };
     for (auto& L : k.leaves)
         if (!L.zero && !(k.cls == KClass::FOLD)) check(L.v, L.loc, L.dtype, "a load");
+    // a gathered read adds index * g_stride for an index in [g_lo, g_hi)
+    for (auto& e : k.ex) {
+        if (e.op != RV_GATHER || e.g_hi <= e.g_lo || k.leaves[e.leaf].zero) continue;
+        const Leaf& L = k.leaves[e.leaf];
+        int64_t lo, hi;
+        if (!view_addr_range(L.v, &lo, &hi)) continue;
+        const int64_t a = 0, b = (e.g_hi - 1 - e.g_lo) * e.g_stride;
+        lo += std::min(a, b);
+        hi += std::max(a, b);
+        if (lo < 0 || hi >= cap(L.loc, L.dtype))
+            fail(RV_E_OUT_OF_BOUNDS, fmt("a gathered load of kernel %s addresses [%lld, %lld] outside its %lld elements",
+                                         k.name.c_str(), (long long)lo, (long long)hi, (long long)cap(L.loc, L.dtype)));
+    }
+    if (k.cls == KClass::SCATTER && cap(k.sc_out, k.sc_dtype) < numel(k.sc_out_shape))
+        fail(RV_E_OUT_OF_BOUNDS, fmt("the scatter target of kernel %s is smaller than its shape", k.name.c_str()));
     for (auto& s : k.stores)
         if (k.cls != KClass::FOLD && !(k.cls == KClass::MFMA && k.mfma_partial)) check(s.v, s.loc, s.dtype, "a store");
 }
@@ -267,6 +282,36 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             }
             return;
         }
+        case KClass::SCATTER: {
+            const int64_t cells = k.sc_cells, nb = (cells + 2047) / 2048;
+            const int64_t nf = k.sc_cells ? numel(k.domain) / k.sc_cells : 0;
+            k.plan = "scatter_" + k.sc_part;
+            k.block[0] = 256;
+            auto cap_grid = [](int64_t g) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>(g, 1 << 20)); };
+            if (k.sc_part == "atomic") {
+                k.grid[0] = cap_grid((numel(k.domain) + 255) / 256);
+            } else if (k.sc_part == "keys") {
+                k.grid[0] = cap_grid((cells + 255) / 256);
+            } else if (k.sc_part == "hist" || k.sc_part == "move") {
+                k.grid[0] = (unsigned)nb;
+                k.lds = k.sc_part == "hist" ? 256 * 4 : (256 + 4 * 256 + 8) * 4;
+            } else if (k.sc_part == "scan") {
+                k.grid[0] = 256;
+            } else {  // fold: a group of TPS lanes per run of equal keys
+                int tps = 1;
+                while (tps < 256 && tps < nf) tps *= 2;
+                k.grid[0] = cap_grid((cells + 256 / tps - 1) / (256 / tps));
+            }
+            int tps = 1;
+            while (tps < 256 && tps < nf) tps *= 2;
+            snprintf(buf, sizeof buf,
+                     "\"part\":\"%s\",\"axis\":%d,\"carried_dims\":%u,\"index_cells\":%lld,\"keys\":%lld,"
+                     "\"radix_passes\":%d,\"pass\":%d,\"tile\":2048,\"lanes_per_run\":%d,\"ordered\":%s",
+                     k.sc_part.c_str(), k.sc_axis, k.sc_fdims, (long long)cells, (long long)k.sc_keys_n, k.sc_passes,
+                     k.sc_pass, tps, k.sc_part == "atomic" ? "false" : "true");
+            k.plan_json = buf;
+            return;
+        }
         default: break;
     }
     merge_dims(k);
@@ -288,8 +333,9 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
     }
     if (k.cls == KClass::EW) {
         const int X = rank - 1, Y = rank - 2;
-        bool tiled = false;
-        if (rank >= 2 && k.domain[X] >= 8 && k.domain[Y] >= 8)
+        bool tiled = false, gathers = false;
+        for (auto& e : k.ex) gathers = gathers || e.op == RV_GATHER;
+        if (rank >= 2 && k.domain[X] >= 8 && k.domain[Y] >= 8 && !gathers)
             for (auto& L : k.leaves)
                 if (!L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) tiled = true;
         k.lane_dim = X;
@@ -477,7 +523,12 @@ void lower(Program& p) {
         for (int64_t d : k.domain) sig += "," + std::to_string(d);
         for (auto& L : k.leaves) sig += json_view(L.v) + dtype_name(L.dtype);
         for (auto& st : k.stores) sig += json_view(st.v) + dtype_name(st.dtype);
-        for (auto& e : k.ex) sig += fmt("|%d,%d,%d,%d,%d,%d,%.17g", e.op, e.dtype, e.a, e.b, e.c, e.leaf, e.cval);
+        for (auto& e : k.ex)
+            sig += fmt("|%d,%d,%d,%d,%d,%d,%.17g,%lld,%lld,%lld", e.op, e.dtype, e.a, e.b, e.c, e.leaf, e.cval,
+                       (long long)e.g_stride, (long long)e.g_lo, (long long)e.g_hi);
+        if (k.cls == KClass::SCATTER)
+            sig += fmt("|%d,%d,%d,%d,%d,%d,%d", k.sc_index, k.sc_values, k.sc_out.kind, k.sc_out.index, k.sc_dtype,
+                       k.sc_passes, k.sc_pass) + shape_str(k.sc_out_shape);
         uint64_t h = 1469598103934665603ull;
         for (unsigned char ch : sig) {
             h ^= ch;
@@ -536,11 +587,23 @@ std::string describe(const Program& p) {
             const Ex& x = k.ex[e];
             const char* nm = x.op == EX_MFMA_ACC ? "MFMA_ACC" : op_name(x.op);
             s += fmt("%s{\"op\":\"%s\",\"dtype\":\"%s\",\"a\":%d,\"b\":%d,\"c\":%d,\"leaf\":%d,\"node\":%d,"
-                     "\"cval\":\"%.17g\"}",
+                     "\"cval\":\"%.17g\"",
                      e ? "," : "", x.op == RV_BUFFER ? "LOAD" : nm, dtype_name(x.dtype), x.a, x.b, x.c, x.leaf, x.node,
                      x.cval);
+            if (x.op == RV_GATHER)
+                s += fmt(",\"gather\":{\"stride\":%lld,\"lo\":%lld,\"hi\":%lld}", (long long)x.g_stride,
+                         (long long)x.g_lo, (long long)x.g_hi);
+            s += "}";
         }
-        s += "]}";
+        s += "]";
+        if (k.cls == KClass::SCATTER) {
+            s += ",\"scatter\":{\"index\":" + std::to_string(k.sc_index) + ",\"values\":" +
+                 std::to_string(k.sc_values) + ",\"out\":" + json_loc(k.sc_out) + ",\"out_shape\":[";
+            for (size_t d = 0; d < k.sc_out_shape.size(); ++d)
+                s += (d ? "," : "") + std::to_string(k.sc_out_shape[d]);
+            s += "],\"dtype\":\"" + std::string(dtype_name(k.sc_dtype)) + "\"}";
+        }
+        s += "}";
     }
     return s + "]}";
 }

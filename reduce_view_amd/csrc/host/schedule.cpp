@@ -155,6 +155,8 @@ struct Builder {
                 return build(nd.src[0], m);
             case RV_SUM: case RV_MAX:
                 return build_reduce(i, m);
+            case RV_GATHER:
+                return build_gather(i, m);
             default: break;
         }
         if (!is_elementwise(nd.op)) fail(RV_E_INVALID, fmt("internal: op %s in a kernel", op_name(nd.op)));
@@ -165,6 +167,51 @@ struct Builder {
         e.a = build(nd.src[0], m);
         if (nd.nsrc > 1) e.b = build(nd.src[1], m);
         if (nd.nsrc > 2) e.c = build(nd.src[2], m);
+        return add(e);
+    }
+
+    // GATHER (a value in memory, so only its own elementwise kernel builds
+    // it): the data is read where it lives, through its View with the
+    // gathered axis left out; the index is fused.
+    int build_gather(int i, const Map& m) {
+        if (mode != EW) throw 1;
+        const Node& nd = c.g.nodes[i];
+        const int ds = nd.src[0];
+        const Node& dn = c.g.nodes[ds];
+        rv_view dv;
+        Loc dl;
+        if (dn.op == RV_BUFFER) {
+            dv = view_contiguous(dn.shape);
+            dl = Loc{0, dn.slot};
+        } else if (c.mat[ds]) {
+            dv = view_contiguous(dn.shape);
+            dl = c.loc[ds][0];
+        } else if (dn.op == RV_VIEW && (c.g.nodes[dn.src[0]].op == RV_BUFFER || c.mat[dn.src[0]])) {
+            const Node& sn = c.g.nodes[dn.src[0]];
+            dv = dn.view;
+            dl = sn.op == RV_BUFFER ? Loc{0, sn.slot} : c.loc[dn.src[0]][0];
+        } else {
+            fail(RV_E_INVALID, "internal: GATHER data not in memory");
+        }
+        const int a = nd.axis;
+        Ex e;
+        e.op = RV_GATHER;
+        e.dtype = nd.dtype;
+        e.node = i;
+        e.g_stride = dv.strides[a];
+        e.g_lo = std::max<int64_t>(0, dv.mask_lo[a]);
+        e.g_hi = std::min<int64_t>(dv.shape[a], dv.mask_hi[a]);
+        rv_view v = dv;
+        if (e.g_hi > e.g_lo) v.offset += e.g_lo * e.g_stride;
+        v.strides[a] = 0;
+        v.mask_lo[a] = 0;
+        v.mask_hi[a] = 1;
+        Map dm = m;
+        dm[a] = -1;
+        Leaf L = compose_leaf(v, dm, rank(), dl, dn.dtype);
+        L.zero = L.zero || e.g_hi <= e.g_lo;
+        e.leaf = add_leaf(L);
+        e.a = build(nd.src[1], m);
         return add(e);
     }
 
@@ -520,7 +567,144 @@ static bool try_mfma(Ctx& c, int root, std::vector<Kernel>& out, int& partial_re
     return true;
 }
 
+// ---- SCATTER ---------------------------------------------------------------
+
+static int bit_width(uint64_t x) {
+    int b = 0;
+    while (x) {
+        ++b;
+        x >>= 1;
+    }
+    return b;
+}
+
+// The kernels of one SCATTER node: a fill (out = base, elementwise), then
+// either one atomic-add kernel or the ordered chain (keys, stable radix
+// passes, in-order fold), then copies to any further output locations.
+// Returns false (after marking what must exist in memory first) when a
+// source cannot be fused.
+static bool scatter_kernels(Ctx& c, int i, std::vector<Kernel>& out, std::vector<char>& need) {
+    const Node& nd = c.g.nodes[i];
+    const Shape& osh = nd.shape;
+    const Shape& ish = c.g.nodes[nd.src[1]].shape;
+    const std::vector<Loc> all = c.loc[i];
+    const Loc target = all[0];
+    std::vector<Kernel> ks;
+    // fill
+    {
+        Kernel f;
+        f.cls = KClass::EW;
+        f.domain = osh;
+        Builder b{c, f, i, Builder::EW};
+        c.loc[i] = {target};
+        try {
+            int e = b.build(nd.src[0], identity(osh.size()));
+            add_stores(c, f, i, e, identity(osh.size()));
+        } catch (int) {
+            c.loc[i] = all;
+            need[nd.src[0]] = 1;
+            return false;
+        }
+        c.loc[i] = all;
+        ks.push_back(f);
+    }
+    Kernel k;
+    k.cls = KClass::SCATTER;
+    k.domain = ish;
+    Builder b{c, k, i, Builder::EW};
+    for (int j = 1; j <= 2; ++j) {
+        try {
+            int e = b.build(nd.src[j], identity(ish.size()));
+            (j == 1 ? k.sc_index : k.sc_values) = e;
+        } catch (int) {
+            need[nd.src[j]] = 1;
+            return false;
+        }
+    }
+    k.sc_axis = nd.axis;
+    k.sc_out = target;
+    k.sc_out_shape = osh;
+    k.sc_dtype = nd.dtype;
+    int64_t cells = 1, keys = osh[nd.axis];
+    for (size_t d = 0; d < ish.size(); ++d) {
+        const bool carried = (int)d != nd.axis && ish[d] > 1 && ex_invariant(k, k.sc_index, (int)d);
+        if (carried) {
+            k.sc_fdims |= 1u << d;
+            continue;
+        }
+        cells *= ish[d];
+        if ((int)d != nd.axis) keys *= ish[d];
+    }
+    k.sc_cells = cells;
+    k.sc_keys_n = keys;
+    if (numel(ish) > 0) {
+        if (nd.atomic) {
+            k.sc_part = "atomic";
+            ks.push_back(k);
+        } else {
+            if (keys >= (int64_t(1) << 32) - 1)
+                fail(RV_E_INVALID, fmt("SCATTER into %s: %lld target keys do not fit in 32 bits",
+                                       shape_str(osh).c_str(), (long long)keys));
+            const int passes = std::max(1, (bit_width((uint64_t)keys) + 7) / 8);
+            const int64_t nb = (cells + 2047) / 2048;
+            auto region = [&](int64_t bytes) {
+                c.p.regions.push_back(Region{0, (size_t)bytes});
+                return (int)c.p.regions.size() - 1;
+            };
+            for (int q = 0; q < 2; ++q) {
+                k.sc_reg_keys[q] = region(cells * 4);
+                k.sc_reg_vals[q] = region(cells * 4);
+            }
+            k.sc_reg_counts = region((256 * nb + 256) * 4);
+            k.sc_passes = passes;
+            Kernel kk = k;
+            kk.sc_part = "keys";
+            ks.push_back(kk);
+            for (int q = 0; q < passes; ++q)
+                for (const char* part : {"hist", "scan", "move"}) {
+                    Kernel r = k;
+                    r.leaves.clear();
+                    r.ex.clear();
+                    r.sc_index = r.sc_values = -1;
+                    r.sc_part = part;
+                    r.sc_pass = q;
+                    ks.push_back(r);
+                }
+            Kernel fo = k;
+            fo.sc_part = "fold";
+            ks.push_back(fo);
+        }
+    }
+    // further locations of the same output: copies of the first
+    if (all.size() > 1) {
+        Kernel kc;
+        kc.cls = KClass::EW;
+        kc.domain = osh;
+        Builder bc{c, kc, i, Builder::EW};
+        int e = bc.load(view_contiguous(osh), identity(osh.size()), target, nd.dtype, i);
+        c.loc[i] = std::vector<Loc>(all.begin() + 1, all.end());
+        add_stores(c, kc, i, e, identity(osh.size()));
+        c.loc[i] = all;
+        ks.push_back(kc);
+    }
+    for (auto& x : ks) out.push_back(x);
+    return true;
+}
+
 }  // namespace
+
+bool ex_invariant(const Kernel& k, int e, int d) {
+    if (e < 0) return true;
+    const Ex& x = k.ex[e];
+    auto leaf_inv = [&](int l) {
+        const Leaf& L = k.leaves[l];
+        return L.zero || (L.v.strides[d] == 0 && L.v.mask_lo[d] <= 0 && L.v.mask_hi[d] >= L.v.shape[d]);
+    };
+    if (x.op == RV_BUFFER) return leaf_inv(x.leaf);
+    if (x.op == RV_CONST) return true;
+    if (x.op == RV_GATHER && !leaf_inv(x.leaf)) return false;
+    return ex_invariant(k, x.a, d) && ex_invariant(k, x.b, d) && ex_invariant(k, x.c, d);
+}
 
 void schedule(Program& p) {
     Graph& g = p.g;
@@ -537,7 +721,16 @@ void schedule(Program& p) {
     std::vector<char> need(n, 0);
     for (int i = 0; i < n; ++i) {
         const Node& nd = g.nodes[i];
-        if (is_out[i] || nd.op == RV_CONTIGUOUS) need[i] = 1;
+        if (is_out[i] || nd.op == RV_CONTIGUOUS || nd.op == RV_GATHER || nd.op == RV_SCATTER) need[i] = 1;
+        if (nd.op == RV_GATHER) {  // the data is read where it lives
+            const int ds = nd.src[0];
+            const Node& dn = g.nodes[ds];
+            if (dn.op == RV_VIEW) {
+                if (g.nodes[dn.src[0]].op != RV_BUFFER) need[dn.src[0]] = 1;
+            } else if (dn.op != RV_BUFFER) {
+                need[ds] = 1;
+            }
+        }
         if (nd.op == RV_CUSTOM)  // the kernel reads its operands from memory
             for (int j = 0; j < nd.nsrc; ++j)
                 if (g.nodes[nd.src[j]].op != RV_BUFFER) need[nd.src[j]] = 1;
@@ -582,6 +775,8 @@ void schedule(Program& p) {
                     }
                 attn_kernel(c, sib, k);
                 kernels.push_back(k);
+            } else if (g.nodes[i].op == RV_SCATTER) {
+                if (!scatter_kernels(c, i, kernels, need)) again = true;
             } else if (try_ew(c, i, k)) {
                 kernels.push_back(k);
             } else if (try_mfma(c, i, mk, preg)) {

@@ -1346,3 +1346,118 @@ __device__ __forceinline__ float rv_fold_sum(const float* __restrict__ part, lon
     }
     return s[0];
 }
+
+// ---------------------------------------------------------------------------
+// Scatter-add helpers.
+//
+// Stable LSD radix sort of (key, value) u32 pairs with 8-bit digits, in
+// tiles of 2048 pairs (256 lanes, 8 rounds of 256 consecutive pairs). Per
+// pass: a digit histogram per tile, an exclusive scan of each digit's tile
+// counts, and a move that places every pair at
+//   (pairs of smaller digits) + (pairs of its digit in earlier tiles)
+//   + (pairs of its digit earlier in this tile),
+// the last from wave ballots, so pairs with equal digits keep their order.
+// Counts are integers (LDS atomics only count), so every run places every
+// pair at the same position.
+// ---------------------------------------------------------------------------
+#define RV_RS_TILE 2048
+
+__device__ __forceinline__ void rv_rs_hist(const unsigned* __restrict__ keys, unsigned* __restrict__ counts,
+                                           long long n, unsigned nb, int shift) {
+    __shared__ unsigned h[256];
+    const unsigned t = threadIdx.x;
+    h[t] = 0u;
+    __syncthreads();
+    const long long base = (long long)blockIdx.x * RV_RS_TILE;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const long long j = base + r * 256 + t;
+        if (j < n) atomicAdd(&h[(keys[j] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    counts[(size_t)t * nb + blockIdx.x] = h[t];
+}
+
+// Exclusive scan of v over the 256 lanes of the workgroup; `tot` gets the
+// total. `w` is 4 words of LDS.
+__device__ __forceinline__ unsigned rv_scan256(unsigned v, unsigned* w, unsigned& tot) {
+    const unsigned lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    unsigned x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned y = (unsigned)__shfl_up((int)x, o, 64);
+        if (lane >= (unsigned)o) x += y;
+    }
+    if (lane == 63u) w[wave] = x;
+    __syncthreads();
+    unsigned pre = 0u;
+    for (unsigned q = 0; q < wave; ++q) pre += w[q];
+    tot = w[0] + w[1] + w[2] + w[3];
+    __syncthreads();
+    return pre + x - v;
+}
+
+// One workgroup per digit (blockIdx.x): counts[d * nb + b] becomes the
+// number of pairs of digit d in tiles before b; counts[256 * nb + d] gets the
+// digit's total.
+__device__ __forceinline__ void rv_rs_scan(unsigned* __restrict__ counts, unsigned nb) {
+    __shared__ unsigned w[4];
+    unsigned* row = counts + (size_t)blockIdx.x * nb;
+    unsigned carry = 0u;
+    for (unsigned c0 = 0; c0 < nb; c0 += 256u) {
+        const unsigned j = c0 + threadIdx.x;
+        const unsigned v = j < nb ? row[j] : 0u;
+        unsigned tot;
+        const unsigned ex = rv_scan256(v, w, tot);
+        if (j < nb) row[j] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) counts[(size_t)256 * nb + blockIdx.x] = carry;
+}
+
+__device__ __forceinline__ void rv_rs_move(const unsigned* __restrict__ keys, const unsigned* __restrict__ vals,
+                                           unsigned* __restrict__ okeys, unsigned* __restrict__ ovals,
+                                           const unsigned* __restrict__ counts, long long n, unsigned nb, int shift) {
+    __shared__ unsigned run[256];
+    __shared__ unsigned wc[4][256];
+    __shared__ unsigned w[4];
+    const unsigned t = threadIdx.x, lane = t & 63u, wave = t >> 6;
+    unsigned tot;
+    const unsigned start = rv_scan256(counts[(size_t)256 * nb + t], w, tot);
+    run[t] = start + counts[(size_t)t * nb + blockIdx.x];
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int r = 0; r < 8; ++r) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wc[q][t] = 0u;
+        __syncthreads();
+        const long long j = (long long)blockIdx.x * RV_RS_TILE + r * 256 + t;
+        const bool ok = j < n;
+        const unsigned key = ok ? keys[j] : 0u, val = ok ? vals[j] : 0u;
+        const unsigned d = (key >> shift) & 255u;
+        unsigned long long same = __builtin_amdgcn_ballot_w64(ok);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (d >> b) & 1u;
+            const unsigned long long m = __builtin_amdgcn_ballot_w64(bit);
+            same &= bit ? m : ~m;
+        }
+        const unsigned rank = (unsigned)__popcll(same & below);
+        if (ok && rank == 0u) wc[wave][d] = (unsigned)__popcll(same);
+        __syncthreads();
+        if (ok) {
+            unsigned pos = run[d] + rank;
+            for (unsigned q = 0; q < wave; ++q) pos += wc[q][d];
+            if ((long long)pos < n) {  // always, when the counts match the keys
+                okeys[pos] = key;
+                ovals[pos] = val;
+            }
+        }
+        __syncthreads();
+        run[t] += wc[0][t] + wc[1][t] + wc[2][t] + wc[3][t];
+    }
+}
+
+// Unordered scatter-add: hardware atomic adds (device scope, relaxed).
+__device__ __forceinline__ void rv_atomic_add(float* p, float v) { unsafeAtomicAdd(p, v); }
+__device__ __forceinline__ void rv_atomic_add(double* p, double v) { unsafeAtomicAdd(p, v); }
+__device__ __forceinline__ void rv_atomic_add(int* p, int v) { atomicAdd(p, v); }

@@ -234,6 +234,7 @@ def _blank_view() -> rv_view:
 
 # CUSTOM kernel ids and flags (include/rv.h)
 CUSTOM_SDPA_FWD = 1
+SCATTER_ORDERED, SCATTER_ATOMIC = 0, 1
 SDPA_CAUSAL = 1
 
 
@@ -294,6 +295,9 @@ def nodes_from_spec(spec):
                     elif name == "shrink":
                         v = rv_view_shrink(v, [w[0] for w in a], [w[1] for w in a])
             x.view = v
+        elif op in ("GATHER", "SCATTER"):
+            x.reduce_axes = 1 << int(nd["axis"])
+            x.buf = SCATTER_ATOMIC if nd.get("atomic") else SCATTER_ORDERED
         elif op == "CUSTOM":
             if nd.get("kind") != "sdpa_fwd":
                 raise RVError(-2, f"CUSTOM kernel {nd.get('kind')!r} is not supported")

@@ -118,8 +118,44 @@ def run_plan(desc: dict, inputs: list, out_specs: list) -> list:
                                     ops[op["a"]]["dtype"])
             elif name == "WHERE":
                 vals[i] = np.where(vals[op["a"]] != 0, vals[op["b"]], vals[op["c"]]).astype(STORAGE[dt])
+            elif name == "GATHER":
+                L, gp = leaves[op["leaf"]], op["gather"]
+                t = np.broadcast_to(vals[op["a"]], dom).astype(np.int64)
+                if L["zero"]:
+                    vals[i] = np.zeros(dom, STORAGE[dt])
+                    continue
+                v = L["view"]
+                idx = np.full(dom, int(v["offset"]), dtype=np.int64) + (t - int(gp["lo"])) * int(gp["stride"])
+                inside = (t >= gp["lo"]) & (t < gp["hi"])
+                for d, g in enumerate(np.indices(dom, dtype=np.int64) if dom else []):
+                    idx = idx + g * int(v["strides"][d])
+                    inside &= (g >= v["mask_lo"][d]) & (g < v["mask_hi"][d])
+                flat = mem(L["loc"], L["dtype"])
+                assert not np.any(inside & ((idx < 0) | (idx >= flat.size))), "gathered read out of bounds"
+                vals[i] = np.where(inside, flat[np.where(inside, idx, 0)], np.zeros((), flat.dtype)).astype(flat.dtype)
             else:
                 raise AssertionError(name)
+        if k["class"] == "SCATTER":
+            part = k["plan_detail"]["part"]
+            if part in ("fold", "atomic"):  # keys and radix passes only order the adds
+                sc = k["scatter"]
+                axis = k["plan_detail"]["axis"]
+                oshape = tuple(sc["out_shape"])
+                o = mem(sc["out"], sc["dtype"], int(np.prod(oshape))).reshape(oshape)
+                index = np.broadcast_to(vals[sc["index"]], dom)
+                values = np.broadcast_to(vals[sc["values"]], dom)
+                rest = np.indices(tuple(dom[d] for d in range(len(dom)) if d != axis))
+                for kk in range(dom[axis]):
+                    t = np.take(index, kk, axis=axis)
+                    v = np.take(values, kk, axis=axis)
+                    sel = (t >= 0) & (t < oshape[axis])
+                    tgt = list(rest)
+                    tgt.insert(axis, np.where(sel, t, 0))
+                    cur = np.asarray(o[tuple(tgt)])
+                    new = np.reshape(O._binary("ADD", np.ascontiguousarray(cur), np.ascontiguousarray(v), sc["dtype"]),
+                                     cur.shape)
+                    o[tuple(tgt)] = np.where(sel, new, cur)
+            continue
         for st in k["stores"]:
             v = vals[st_ex(k, st)]
             if k["class"] == "MFMA" and st["loc"]["kind"] == "workspace":

@@ -79,11 +79,47 @@ def test_graph_errors():
     b = g.buffer("b", (5,), "f32")
     g.output(g.mul(a, b))
     assert _compile_status(g) == "RV_E_INVALID"
-    for op in ("GATHER", "SCATTER", "ASSIGN", "CUSTOM"):
+    for op in ("ASSIGN", "CUSTOM"):
         g = synth.Spec()
         a = g.buffer("a", (4,), "f32")
         g.output(g._add(op=op, src=(a,)))
         assert _compile_status(g) == "RV_E_UNSUPPORTED_OP", op
+
+
+def _indexed(kind, dshape=(4, 5), ishape=(3, 5), axis=0, idt="i32", dt="f32", vdt=None, vshape=None, atomic=False):
+    g = synth.Spec()
+    d = g.buffer("d", dshape, dt)
+    i = g.buffer("i", ishape, idt)
+    if kind == "gather":
+        g.output(g.gather(d, i, axis))
+    else:
+        v = g.buffer("v", vshape or ishape, vdt or dt)
+        g.output(g.scatter(d, i, v, axis, atomic))
+    return g
+
+
+def _status_or_ok(spec):
+    try:
+        rv.compile_spec(spec)
+    except rv.RVError as e:
+        return e.name
+    return "OK"
+
+
+def test_indexed_op_contract_errors():
+    for kind in ("gather", "scatter"):
+        assert _status_or_ok(_indexed(kind)) == "OK"
+        assert _status_or_ok(_indexed(kind, idt="i16")) == "RV_E_DTYPE"
+        assert _status_or_ok(_indexed(kind, ishape=(3, 4))) == "RV_E_INVALID"  # differs off the axis
+        assert _status_or_ok(_indexed(kind, ishape=(3, 5, 1))) == "RV_E_INVALID"  # rank
+        assert _status_or_ok(_indexed(kind, axis=2)) == "RV_E_INVALID"  # axis outside the rank
+    assert _status_or_ok(_indexed("scatter", vdt="f64")) == "RV_E_DTYPE"
+    assert _status_or_ok(_indexed("scatter", vshape=(2, 5))) == "RV_E_INVALID"
+    for dt in ("f32", "f64", "i32"):
+        assert _status_or_ok(_indexed("scatter", dt=dt, atomic=True)) == "OK", dt
+    for dt in ("f16", "bf16", "i16", "i8"):
+        assert _status_or_ok(_indexed("scatter", dt=dt, atomic=True)) == "RV_E_UNSUPPORTED_OP", dt
+        assert _status_or_ok(_indexed("scatter", dt=dt)) == "OK", dt
 
 
 def test_no_device_is_a_typed_error():

@@ -66,7 +66,45 @@ CLASSES = {
     "gemm": (lambda: synth.gemm_relu2_sum(128, 128, 64), lambda: synth.inputs_gemm(128, 128, 64),
              ["MFMA", "FOLD"]),
     "gemm_y": (lambda: synth.gemm_bf16(128, 256, 128), lambda: synth.inputs_gemm(128, 256, 128), ["MFMA"]),
+    "gather": (lambda: synth.embedding_gather(50, 6, 30), lambda: synth.inputs_embedding(50, 6, 30), ["EW"]),
+    "gather_general": (lambda: _gather_general(), lambda: _indexed_inputs(), ["EW", "EW"]),
+    "scatter": (lambda: synth.embedding_scatter(20, 6, 100), lambda: synth.inputs_embedding(20, 6, 100),
+                ["EW"] + ["SCATTER"] * 5),
+    "scatter_atomic": (lambda: synth.embedding_scatter(20, 6, 100, atomic=True),
+                       lambda: synth.inputs_embedding(20, 6, 100), ["EW", "SCATTER"]),
+    "scatter_general": (lambda: _scatter_general(), lambda: _indexed_inputs(), ["EW"] + ["SCATTER"] * 5),
 }
+
+
+def _indexed_inputs():
+    rng = np.random.default_rng(70)
+    return {"D": rng.standard_normal((4, 9, 5)).astype(np.float32),
+            "I": rng.integers(-3, 12, (4, 7, 5)).astype(np.int32),
+            "V": rng.standard_normal((4, 7, 5)).astype(np.float32)}
+
+
+def _gather_general():
+    """GATHER along axis 1 of a permuted, padded View of the data, by a
+    computed index (index + 1), then an elementwise consumer."""
+    g = synth.Spec("gather_general")
+    d = g.buffer("D", (4, 9, 5), "f32")
+    dv = g.view(d, ("permute", (2, 1, 0)), ("pad", ((0, 0), (1, 1), (0, 0))), ("permute", (2, 1, 0)),
+                ("shrink", ((0, 4), (0, 9), (0, 5))))
+    i = g.buffer("I", (4, 7, 5), "i32")
+    idx = g.add(i, g.const(1, (4, 7, 5), "i32"))
+    g.output(g.mul(g.gather(dv, idx, 1), g.const(2.0, (4, 7, 5), "f32")))
+    return g
+
+
+def _scatter_general():
+    """SCATTER along axis 1 with an index that varies along every dim (no
+    carried dims), a computed base and computed values."""
+    g = synth.Spec("scatter_general")
+    d = g.buffer("D", (4, 9, 5), "f32")
+    i = g.buffer("I", (4, 7, 5), "i32")
+    v = g.buffer("V", (4, 7, 5), "f32")
+    g.output(g.scatter(g.exp(d), i, g.mul(v, v), 1))
+    return g
 
 
 @pytest.mark.parametrize("name", list(CLASSES))
