@@ -6,7 +6,8 @@ permuted View and c a stride-0 row vector, the same chain with a read through
 a shrink-then-pad masked View, and a standalone 4096 x 4096 transpose. One
 step runs all three programs once. ``--workload`` selects one of the other
 kernels instead (softmax, softmax_long, rmsnorm, rmsnorm_f16, rmsnorm_f64,
-chain_i8, layernorm, gemm, attention, matmul64, copy).
+chain_i8, layernorm, gemm, attention, gather, scatter, scatter_atomic,
+matmul64, copy).
 
 Inputs are seeded, synthetic and already resident in HBM when timing starts;
 several input sets rotate so that consecutive launches never re-read data the
@@ -108,6 +109,30 @@ def workloads():
             programs=[("attention", synth.attention(6, 8192, 8192, 32, True), 4 * 32 * 6 * 8192 * 8193 // 2)],
             inputs=lambda seed: synth.inputs_attention(6, 8192, 8192, 32, seed),
             unit="TFLOP/s", dtype="bf16", bound="mfma", seed=6),
+        "gather": dict(
+            desc=("GATHER along axis 0: 32768 int32 ids (uniform) pick rows of a (65536, 1024) fp32 table "
+                  "(embedding lookup), table ~ N(0,1), seed 9"),
+            programs=[("gather", synth.embedding_gather(65536, 1024, 32768), 2 * 32768 * 1024 * F32 + 32768 * 4)],
+            inputs=lambda seed: {k: v for k, v in synth.inputs_embedding(65536, 1024, 32768, seed).items()
+                                 if k in ("table", "ids")},
+            unit="GB/s", dtype="f32", bound="hbm", seed=9),
+        "scatter": dict(
+            desc=("ordered SCATTER-add along axis 0: 32768 rows of 1024 fp32 values added into a zero (65536, 1024) "
+                  "table at int32 ids (uniform; colliding rows fold in index order, bit-exact), values ~ N(0,1), "
+                  "seed 9"),
+            programs=[("scatter", synth.embedding_scatter(65536, 1024, 32768),
+                       65536 * 1024 * F32 + 32768 * 1024 * F32 + 32768 * 4)],
+            inputs=lambda seed: {k: v for k, v in synth.inputs_embedding(65536, 1024, 32768, seed).items()
+                                 if k in ("values", "ids")},
+            unit="GB/s", dtype="f32", bound="hbm", seed=9),
+        "scatter_atomic": dict(
+            desc=("atomic SCATTER-add along axis 0 (colliding float adds in arrival order): 32768 rows of 1024 "
+                  "fp32 values into a zero (65536, 1024) table at int32 ids (uniform), values ~ N(0,1), seed 9"),
+            programs=[("scatter_atomic", synth.embedding_scatter(65536, 1024, 32768, atomic=True),
+                       65536 * 1024 * F32 + 32768 * 1024 * F32 + 32768 * 4)],
+            inputs=lambda seed: {k: v for k, v in synth.inputs_embedding(65536, 1024, 32768, seed).items()
+                                 if k in ("values", "ids")},
+            unit="GB/s", dtype="f32", bound="hbm", seed=9),
         "copy": dict(
             desc="plain 4096x4096 fp32 copy (bandwidth reference; not a hot-path workload)",
             programs=[("copy", synth.copy(4096, 4096), 2 * 4096 * 4096 * F32)],

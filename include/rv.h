@@ -124,7 +124,8 @@ typedef enum rv_op {
  *                scatter); f32, f64 and i32 only (RV_E_UNSUPPORTED_OP
  *                otherwise); ints are exact, floats agree with the ordered
  *                result up to the order of colliding adds.
- * Index cells, and each dim, must fit in 32 bits (RV_E_INVALID otherwise). */
+ * The index must have fewer than 2^31 cells and every dim must fit in int32
+ * (RV_E_INVALID otherwise). */
 #define RV_SCATTER_ORDERED 0
 #define RV_SCATTER_ATOMIC 1
 

@@ -1571,9 +1571,39 @@ std::string Gen::gen_scatter() {
         return b.str();
     }
     if (part == "move") {
-        b << "  rv_rs_move(" << ureg(k.sc_reg_keys[cur], false) << ", " << ureg(k.sc_reg_vals[cur], false) << ", "
-          << ureg(k.sc_reg_keys[nxt], true) << ", " << ureg(k.sc_reg_vals[nxt], true) << ", "
-          << ureg(k.sc_reg_counts, false) << ", " << CELLS << "LL, " << NB << "u, " << 8 * k.sc_pass << ");\n";
+        const bool self = NB <= kScanInline;
+        b << "  rv_rs_move<" << (self ? "true" : "false") << ">(" << ureg(k.sc_reg_keys[cur], false) << ", "
+          << ureg(k.sc_reg_vals[cur], false) << ", " << ureg(k.sc_reg_keys[nxt], true) << ", "
+          << ureg(k.sc_reg_vals[nxt], true) << ", "
+          << (self ? std::string("nullptr") : ureg(k.sc_reg_counts, false)) << ", " << CELLS << "LL, " << NB
+          << "u, " << 8 * k.sc_pass << ");\n";
+        return b.str();
+    }
+    if (part == "bounds") {
+        // a wave per 64 sorted positions: the keys between the one before
+        // the chunk and the chunk's last (positions past the end count as
+        // key KN) start at the first position of the chunk whose key is not
+        // smaller, found by a search over the wave's 64 keys
+        b << "  const unsigned* __restrict__ K = " << ureg(k.sc_reg_keys[k.sc_passes % 2], false) << ";\n";
+        b << "  unsigned* __restrict__ B = " << ureg(k.sc_reg_bounds, true) << ";\n";
+        b << "  const int lane = threadIdx.x & 63;\n";
+        b << "  for (long long ch = ((long long)blockIdx.x * 256 + threadIdx.x) >> 6; ch <= " << CELLS / 64
+          << "LL; ch += (long long)gridDim.x * 4) {\n";
+        b << "    const long long p = ch * 64 + lane;\n";
+        b << "    const long long key = p < " << CELLS << "LL ? (long long)K[p] : " << KN << "LL;\n";
+        b << "    const long long prev = ch == 0 ? -1LL : (long long)K[ch * 64 - 1];\n";
+        b << "    const long long hi = __shfl(key, 63, 64);\n";
+        b << "    for (long long kb = prev + 1; kb <= hi; kb += 64) {  // uniform: every lane shuffles\n";
+        b << "      const long long k = kb + lane;\n";
+        b << "      int lo = 0;\n";
+        b << "#pragma unroll\n";
+        b << "      for (int w = 32; w >= 1; w >>= 1) {\n";
+        b << "        const long long kw = __shfl(key, lo + w - 1, 64);\n";
+        b << "        if (kw < k) lo += w;\n";
+        b << "      }\n";
+        b << "      if (k <= hi) B[k] = (unsigned)(ch * 64 + lo);\n";
+        b << "    }\n";
+        b << "  }\n";
         return b.str();
     }
     const std::string OUT = pname(k.sc_out, dt, true);
@@ -1605,6 +1635,8 @@ std::string Gen::gen_scatter() {
             PI *= k.domain[d];
         }
     if (part == "keys") {
+        // an index outside the axis: the last key, and the cell id flagged
+        // (bit 31) so that the fold adds nothing for it
         b << "  for (long long c = (long long)blockIdx.x * 256 + threadIdx.x; c < " << CELLS
           << "LL; c += (long long)gridDim.x * 256) {\n";
         decompose("c", cd, "i", "    ");
@@ -1614,69 +1646,71 @@ std::string Gen::gen_scatter() {
         scalar(b, k.sc_index, idx, "    ", "", done);
         std::string lin = "0LL";
         int64_t m = 1;
-        for (size_t j = idims.size(); j-- > 0;) {
-            lin += fmt(" + i%d * %lldLL", idims[j], (long long)m);
-            m *= k.domain[idims[j]];
+        for (size_t j2 = idims.size(); j2-- > 0;) {
+            lin += fmt(" + i%d * %lldLL", idims[j2], (long long)m);
+            m *= k.domain[idims[j2]];
         }
         b << "    const int t = s" << k.sc_index << ";\n";
-        b << "    const unsigned key = (t >= 0 && t < " << osh[A] << ") ? (unsigned)((long long)t * " << PI << "LL + "
-          << lin << ") : " << KN << "u;\n";
-        b << "    " << ureg(k.sc_reg_keys[0], true) << "[c] = key;\n";
-        b << "    " << ureg(k.sc_reg_vals[0], true) << "[c] = (unsigned)c;\n";
+        b << "    const bool in = t >= 0 && t < " << osh[A] << ";\n";
+        b << "    " << ureg(k.sc_reg_keys[0], true) << "[c] = in ? (unsigned)((long long)t * " << PI << "LL + " << lin
+          << ") : " << KN - 1 << "u;\n";
+        b << "    " << ureg(k.sc_reg_vals[0], true) << "[c] = (unsigned)c | (in ? 0u : 0x80000000u);\n";
         b << "  }\n";
         return b.str();
     }
-    // fold: a group of TPS lanes per sorted position; a group whose position
-    // starts a run of equal keys adds the run's values, in sorted (= index)
-    // order, to the target cells of every carried position, JU cells at a
-    // time, CB carried positions per lane
+    // fold: a group of TPS lanes per R consecutive target keys (every
+    // output cell is one key and one carried position); a key's run of
+    // sorted cells is bounds[key] .. bounds[key + 1]. For CB carried
+    // positions per lane the group writes the base plus each run's values
+    // in sorted (= index) order, JU cells of every key per step, so that
+    // R * JU * CB loads are in flight per lane.
     const int fin = k.sc_passes % 2;
     const int64_t NF = numel(k.domain) / CELLS;
     int TPS = 1;
     while (TPS < 256 && TPS < NF) TPS *= 2;
     const int SPB = 256 / TPS;
-    const int CB = (int)std::min<int64_t>(8, (NF + TPS - 1) / TPS);
-    const int JU = 4;
-    const std::string K = "K", VV = "VV";
-    b << "  const unsigned* __restrict__ K = " << ureg(k.sc_reg_keys[fin], false) << ";\n";
-    b << "  const unsigned* __restrict__ VV = " << ureg(k.sc_reg_vals[fin], false) << ";\n";
-    b << "  const int l = threadIdx.x % " << TPS << ";\n";
-    b << "  for (long long s = (long long)blockIdx.x * " << SPB << " + threadIdx.x / " << TPS << "; s < " << CELLS
-      << "LL; s += (long long)gridDim.x * " << SPB << ") {\n";
-    b << "    const unsigned key = K[s];\n";
-    b << "    if (key >= " << KN << "u || (s > 0 && K[s - 1] == key)) continue;\n";
-    b << "    long long e = s + 1;\n";
-    if (TPS >= 64) {
-        // the whole wave is one group: 64 keys per step
-        b << "    for (;;) {\n";
-        b << "      const long long j = e + (threadIdx.x & 63);\n";
-        b << "      const unsigned kj = j < " << CELLS << "LL ? K[j] : 0xffffffffu;\n";
-        b << "      const unsigned long long m = __builtin_amdgcn_ballot_w64(kj != key);\n";
-        b << "      if (m != 0ull) { e += __ffsll((long long)m) - 1; break; }\n";
-        b << "      e += 64;\n";
-        b << "    }\n";
-    } else {
-        b << "    while (e < " << CELLS << "LL && K[e] == key) ++e;\n";
-    }
-    b << "    const long long t = key / " << PI << "u;\n";
-    b << "    const long long r = key % " << PI << "u;\n";
+    const int CB = (int)std::min<int64_t>(4, (NF + TPS - 1) / TPS);
+    const int JU = env_int("RV_SCATTER_JU", 1);
+    int R = 4;  // plan value (lower.cpp)
     {
-        std::string rem = "r";
-        for (size_t j = idims.size(); j-- > 0;) {
-            const int d = idims[j];
-            b << "    const long long o" << d << " = " << (j ? fmt("%s %% %lldLL", rem.c_str(), (long long)k.domain[d]) : rem)
-              << ";\n";
-            if (j) {
-                b << "    const long long oq" << d << " = " << rem << " / " << k.domain[d] << "LL;\n";
-                rem = fmt("oq%d", d);
-            }
+        const char* q = strstr(k.plan_json.c_str(), "\"keys_per_group\":");
+        if (q) R = atoi(q + strlen("\"keys_per_group\":"));
+    }
+    b << "  const unsigned* __restrict__ VV = " << ureg(k.sc_reg_vals[fin], false) << ";\n";
+    b << "  const unsigned* __restrict__ B = " << ureg(k.sc_reg_bounds, false) << ";\n";
+    b << "  const int l = threadIdx.x % " << TPS << ";\n";
+    b << "  for (long long k0 = ((long long)blockIdx.x * " << SPB << " + threadIdx.x / " << TPS << ") * " << R
+      << "; k0 < " << KN << "LL; k0 += (long long)gridDim.x * " << SPB * R << ") {\n";
+    b << "    int s[" << R << "], n[" << R << "];\n";
+    b << "    long long ob[" << R << "], tk[" << R << "];\n";
+    for (int d : idims) b << "    long long o" << d << "[" << R << "];\n";
+    b << "    bool kv[" << R << "];\n";
+    b << "    int mx = 0;\n";
+    b << "#pragma unroll\n";
+    b << "    for (int r = 0; r < " << R << "; ++r) {\n";
+    b << "      const long long kk = k0 + r;\n";
+    b << "      kv[r] = kk < " << KN << "LL;\n";
+    b << "      const long long kc = kv[r] ? kk : k0;\n";
+    b << "      s[r] = (int)B[kc];\n";
+    b << "      n[r] = kv[r] ? (int)B[kc + 1] - s[r] : 0;\n";
+    b << "      mx = n[r] > mx ? n[r] : mx;\n";
+    b << "      tk[r] = kc / " << PI << "LL;\n";
+    b << "      long long rem = kc % " << PI << "LL;\n";
+    for (size_t j2 = idims.size(); j2-- > 0;) {
+        const int d = idims[j2];
+        if (j2) {
+            b << "      o" << d << "[r] = rem % " << k.domain[d] << "LL;\n";
+            b << "      rem = rem / " << k.domain[d] << "LL;\n";
+        } else {
+            b << "      o" << d << "[r] = rem;\n";
         }
     }
-    std::string ob = fmt("t * %lldLL", (long long)os[A]);
-    for (int d : idims) ob += fmt(" + o%d * %lldLL", d, (long long)os[d]);
-    b << "    const long long ob = " << ob << ";\n";
+    std::string obs = fmt("tk[r] * %lldLL", (long long)os[A]);
+    for (int d : idims) obs += fmt(" + o%d[r] * %lldLL", d, (long long)os[d]);
+    b << "      ob[r] = " << obs << ";\n";
+    b << "    }\n";
     b << "    for (long long f0 = l; f0 < " << NF << "LL; f0 += " << (int64_t)TPS * CB << "LL) {\n";
-    b << "      " << vt(dt) << " acc[" << CB << "];\n";
+    b << "      " << vt(dt) << " acc[" << R << "][" << CB << "];\n";
     b << "      long long fo[" << CB << "];\n";
     for (int d : fd) b << "      long long fc" << d << "[" << CB << "];\n";
     b << "#pragma unroll\n";
@@ -1690,40 +1724,69 @@ std::string Gen::gen_scatter() {
         fo += fmt(" + fi%d * %lldLL", d, (long long)os[d]);
     }
     b << "        fo[cb] = " << fo << ";\n";
-    b << "        acc[cb] = f < " << NF << "LL ? " << ld(dt, OUT + "[ob + fo[cb]]") << " : " << zero_of(dt) << ";\n";
-    b << "      }\n";
-    b << "      for (long long j0 = s; j0 < e; j0 += " << JU << ") {\n";
-    b << "        unsigned cj[" << JU << "];\n";
     b << "#pragma unroll\n";
-    b << "        for (int u = 0; u < " << JU << "; ++u) cj[u] = j0 + u < e ? min(VV[j0 + u], " << CELLS - 1
-      << "u) : 0u;\n";
-    b << "        " << vt(dt) << " vv[" << JU << "][" << CB << "];\n";
+    b << "        for (int r = 0; r < " << R << "; ++r) {\n";
+    {
+        std::vector<std::string> bidx(rank);
+        bidx[A] = "tk[r]";
+        for (int d : idims) bidx[d] = fmt("o%d[r]", d);
+        for (int d : fd) bidx[d] = fmt("fi%d", d);
+        std::vector<char> done(k.ex.size(), 0);
+        scalar(b, k.sc_base, bidx, "          ", "b", done);
+        b << "          acc[r][cb] = s" << k.sc_base << "b;\n";
+    }
+    b << "        }\n";
+    b << "      }\n";
+    b << "      for (int j0 = 0; j0 < mx; j0 += " << JU << ") {\n";
+    b << "        unsigned cj[" << R << "][" << JU << "];\n";
+    b << "        bool add[" << R << "][" << JU << "];\n";
+    b << "#pragma unroll\n";
+    b << "        for (int r = 0; r < " << R << "; ++r)\n";
+    b << "#pragma unroll\n";
+    b << "          for (int u = 0; u < " << JU << "; ++u) {\n";
+    b << "            const unsigned c = j0 + u < n[r] ? VV[s[r] + j0 + u] : 0x80000000u;\n";
+    b << "            add[r][u] = !(c & 0x80000000u);\n";
+    b << "            cj[r][u] = min(c & 0x7fffffffu, " << CELLS - 1 << "u);\n";
+    b << "          }\n";
+    b << "        " << vt(dt) << " vv[" << R << "][" << JU << "][" << CB << "];\n";
+    b << "#pragma unroll\n";
+    b << "        for (int r = 0; r < " << R << "; ++r)\n";
     b << "#pragma unroll\n";
     b << "        for (int u = 0; u < " << JU << "; ++u) {\n";
-    decompose("(long long)cj[u]", cd, "i", "          ");
+    decompose("(long long)cj[r][u]", cd, "i", "          ");
     b << "#pragma unroll\n";
     b << "          for (int cb = 0; cb < " << CB << "; ++cb) {\n";
-    std::vector<std::string> idx(rank);
-    for (int d : cd) idx[d] = fmt("i%d", d);
-    for (int d : fd) idx[d] = fmt("fc%d[cb]", d);
-    std::vector<char> done(k.ex.size(), 0);
-    scalar(b, k.sc_values, idx, "            ", "", done);
-    b << "            vv[u][cb] = s" << k.sc_values << ";\n";
+    {
+        std::vector<std::string> idx(rank);
+        for (int d : cd) idx[d] = fmt("i%d", d);
+        for (int d : fd) idx[d] = fmt("fc%d[cb]", d);
+        std::vector<char> done(k.ex.size(), 0);
+        b << "            if (add[r][u]) {\n";
+        scalar(b, k.sc_values, idx, "              ", "", done);
+        b << "              vv[r][u][cb] = s" << k.sc_values << ";\n";
+        b << "            } else {\n";
+        b << "              vv[r][u][cb] = " << zero_of(dt) << ";\n";
+        b << "            }\n";
+    }
     b << "          }\n";
     b << "        }\n";
     Ex add;
     add.op = RV_ADD;
     add.dtype = dt;
     b << "#pragma unroll\n";
-    b << "        for (int u = 0; u < " << JU << "; ++u)\n";
+    b << "        for (int r = 0; r < " << R << "; ++r)\n";
     b << "#pragma unroll\n";
-    b << "          for (int cb = 0; cb < " << CB << "; ++cb)\n";
-    b << "            if (j0 + u < e) acc[cb] = " << op_code(k, add, "acc[cb]", "vv[u][cb]", "") << ";\n";
+    b << "          for (int u = 0; u < " << JU << "; ++u)\n";
+    b << "#pragma unroll\n";
+    b << "            for (int cb = 0; cb < " << CB << "; ++cb)\n";
+    b << "              if (add[r][u]) acc[r][cb] = " << op_code(k, add, "acc[r][cb]", "vv[r][u][cb]", "") << ";\n";
     b << "      }\n";
     b << "#pragma unroll\n";
-    b << "      for (int cb = 0; cb < " << CB << "; ++cb)\n";
-    b << "        if (f0 + (long long)cb * " << TPS << " < " << NF << "LL) " << OUT << "[ob + fo[cb]] = "
-      << sv(dt, "acc[cb]") << ";\n";
+    b << "      for (int r = 0; r < " << R << "; ++r)\n";
+    b << "#pragma unroll\n";
+    b << "        for (int cb = 0; cb < " << CB << "; ++cb)\n";
+    b << "          if (kv[r] && f0 + (long long)cb * " << TPS << " < " << NF << "LL) " << OUT << "[ob[r] + fo[cb]] = "
+      << sv(dt, "acc[r][cb]") << ";\n";
     b << "    }\n";
     b << "  }\n";
     return b.str();

@@ -64,6 +64,12 @@ inline int64_t numel(const Shape& s) {
     return n;
 }
 
+// A tuning knob from the environment (unset or empty: the default).
+inline int env_int(const char* name, int def) {
+    const char* s = getenv(name);
+    return (s && *s) ? atoi(s) : def;
+}
+
 inline std::string shape_str(const Shape& s) {
     std::string r = "(";
     for (size_t i = 0; i < s.size(); ++i) r += (i ? "," : "") + std::to_string(s[i]);

@@ -203,8 +203,8 @@ Graph intake(const rv_node* nodes, int32_t n, const int32_t* outputs, int32_t no
                 }
                 for (int64_t e : nd.shape)
                     if (e > (int64_t(1) << 31) - 1) fail(RV_E_INVALID, fmt("node %d: %s dims must fit in int32", i, nm));
-                if (numel(ix) >= (int64_t(1) << 32) - 1)
-                    fail(RV_E_INVALID, fmt("node %d: %s of 2^32 or more index cells", i, nm));
+                if (numel(ix) >= (int64_t(1) << 31))
+                    fail(RV_E_INVALID, fmt("node %d: %s of 2^31 or more index cells", i, nm));
                 break;
             }
             case RV_CUSTOM: {  // sdpa_fwd (the only CUSTOM kernel)

@@ -126,17 +126,23 @@ struct Kernel {
     // ATTN (leaves q, k, v; domain (H, Tq, D); Tk = leaves[1].v.shape[1])
     double attn_scale = 0.0;
     bool attn_causal = false;
-    // SCATTER: one step of a scatter-add into `sc_out` (already holding the
-    // base). Domain: the index's shape; ex sc_index / sc_values over it.
-    //   "atomic": every position adds its value with an atomic add
-    //   "keys":   one key per index cell (the target along the axis and the
-    //             dims the index varies along), sentinel sc_keys_n when the
-    //             index is outside the axis
-    //   "hist", "scan", "move": one stable 8-bit radix pass over the keys
-    //   "fold":   each run of equal sorted keys adds its values, in index
-    //             order, into the target cells
+    // SCATTER: one step of a scatter-add into `sc_out`. Domain: the index's
+    // shape; ex sc_index / sc_values over it, sc_base over the output's.
+    //   "atomic": every position adds its value with an atomic add (the
+    //             target already holds the base)
+    //   "keys":   one key per index cell: the target along the axis and
+    //             the dims the index varies along (an index outside the axis
+    //             gets the last key and a flagged cell id, and adds nothing)
+    //   "hist", "scan": per-tile digit counts of a radix pass and their
+    //             exclusive scan (only with more than kScanInline tiles;
+    //             otherwise the move counts every tile itself)
+    //   "move":   one stable 8-bit radix pass
+    //   "bounds": the first sorted position of every key (its run is
+    //             bounds[key] .. bounds[key + 1])
+    //   "fold":   per target key, the base plus its run of sorted values
+    //             folded in index order; every output cell written once
     std::string sc_part;
-    int sc_index = -1, sc_values = -1;
+    int sc_index = -1, sc_values = -1, sc_base = -1;
     int sc_axis = 0;
     Loc sc_out;
     Shape sc_out_shape;
@@ -145,8 +151,14 @@ struct Kernel {
     int64_t sc_cells = 0;       // index cells (positions with the carried dims at 0)
     int64_t sc_keys_n = 0;      // valid keys: out extent along the axis x varying dims
     int sc_pass = 0, sc_passes = 0;
-    int sc_reg_keys[2] = {-1, -1}, sc_reg_vals[2] = {-1, -1}, sc_reg_counts = -1;
+    int sc_reg_keys[2] = {-1, -1}, sc_reg_vals[2] = {-1, -1};
+    int sc_reg_counts = -1;  // per-tile digit counts (more than kScanInline tiles)
+    int sc_reg_bounds = -1;  // first sorted position of every key, and of key sc_keys_n
 };
+
+// Radix passes over at most this many tiles count their digits inside the
+// move kernel (every workgroup counts every tile, in LDS).
+constexpr int64_t kScanInline = 64;
 
 struct Region {
     size_t offset = 0;

@@ -29,10 +29,6 @@ std::string json_view(const rv_view& v) {
     return s + "]}";
 }
 
-static int env_int(const char* name, int def) {
-    const char* s = getenv(name);
-    return (s && *s) ? atoi(s) : def;
-}
 
 // Rewrites every View of `k` for a new domain made of groups of old dims:
 // groups[j] lists consecutive old dims (outermost first) forming new dim j.
@@ -288,27 +284,36 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             k.plan = "scatter_" + k.sc_part;
             k.block[0] = 256;
             auto cap_grid = [](int64_t g) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>(g, 1 << 20)); };
+            int tps = 1;
+            while (tps < 256 && tps < nf) tps *= 2;
             if (k.sc_part == "atomic") {
                 k.grid[0] = cap_grid((numel(k.domain) + 255) / 256);
             } else if (k.sc_part == "keys") {
                 k.grid[0] = cap_grid((cells + 255) / 256);
-            } else if (k.sc_part == "hist" || k.sc_part == "move") {
+            } else if (k.sc_part == "hist") {
                 k.grid[0] = (unsigned)nb;
-                k.lds = k.sc_part == "hist" ? 256 * 4 : (256 + 4 * 256 + 8) * 4;
+                k.lds = 256 * 4;
+            } else if (k.sc_part == "move") {  // 16 waves per tile
+                k.grid[0] = (unsigned)nb;
+                k.block[0] = 1024;
+                k.lds = (256 + 16 * 256 + 16 + (nb <= kScanInline ? 256 * 64 : 0)) * 4;
             } else if (k.sc_part == "scan") {
                 k.grid[0] = 256;
-            } else {  // fold: a group of TPS lanes per run of equal keys
-                int tps = 1;
-                while (tps < 256 && tps < nf) tps *= 2;
-                k.grid[0] = cap_grid((cells + 256 / tps - 1) / (256 / tps));
+            } else if (k.sc_part == "bounds") {  // a wave per 64 sorted positions, one more past the end
+                k.grid[0] = cap_grid((cells / 64 + 1 + 3) / 4);
             }
-            int tps = 1;
-            while (tps < 256 && tps < nf) tps *= 2;
+            // fold: a group of tps lanes takes R keys at a time
+            const int R = env_int("RV_SCATTER_R", 4);
+            if (R < 1 || R > 16) fail(RV_E_INVALID, "RV_SCATTER_R must be in 1..16");
+            const int64_t kpb = (int64_t)R * (256 / tps);
+            if (k.sc_part == "fold") k.grid[0] = cap_grid((k.sc_keys_n + kpb - 1) / kpb);
             snprintf(buf, sizeof buf,
                      "\"part\":\"%s\",\"axis\":%d,\"carried_dims\":%u,\"index_cells\":%lld,\"keys\":%lld,"
-                     "\"radix_passes\":%d,\"pass\":%d,\"tile\":2048,\"lanes_per_run\":%d,\"ordered\":%s",
+                     "\"radix_passes\":%d,\"pass\":%d,\"tile\":2048,\"tiles\":%lld,\"scan_inline\":%s,"
+                     "\"lanes_per_key\":%d,\"keys_per_group\":%d,\"keys_per_workgroup\":%lld,\"ordered\":%s",
                      k.sc_part.c_str(), k.sc_axis, k.sc_fdims, (long long)cells, (long long)k.sc_keys_n, k.sc_passes,
-                     k.sc_pass, tps, k.sc_part == "atomic" ? "false" : "true");
+                     k.sc_pass, (long long)nb, nb <= kScanInline ? "true" : "false", tps, R, (long long)kpb,
+                     k.sc_part == "atomic" ? "false" : "true");
             k.plan_json = buf;
             return;
         }
@@ -527,8 +532,8 @@ void lower(Program& p) {
             sig += fmt("|%d,%d,%d,%d,%d,%d,%.17g,%lld,%lld,%lld", e.op, e.dtype, e.a, e.b, e.c, e.leaf, e.cval,
                        (long long)e.g_stride, (long long)e.g_lo, (long long)e.g_hi);
         if (k.cls == KClass::SCATTER)
-            sig += fmt("|%d,%d,%d,%d,%d,%d,%d", k.sc_index, k.sc_values, k.sc_out.kind, k.sc_out.index, k.sc_dtype,
-                       k.sc_passes, k.sc_pass) + shape_str(k.sc_out_shape);
+            sig += fmt("|%d,%d,%d,%d,%d,%d,%d,%d", k.sc_index, k.sc_values, k.sc_base, k.sc_out.kind, k.sc_out.index,
+                       k.sc_dtype, k.sc_passes, k.sc_pass) + shape_str(k.sc_out_shape);
         uint64_t h = 1469598103934665603ull;
         for (unsigned char ch : sig) {
             h ^= ch;
@@ -598,7 +603,8 @@ std::string describe(const Program& p) {
         s += "]";
         if (k.cls == KClass::SCATTER) {
             s += ",\"scatter\":{\"index\":" + std::to_string(k.sc_index) + ",\"values\":" +
-                 std::to_string(k.sc_values) + ",\"out\":" + json_loc(k.sc_out) + ",\"out_shape\":[";
+                 std::to_string(k.sc_values) + ",\"base\":" + std::to_string(k.sc_base) +
+                 ",\"out\":" + json_loc(k.sc_out) + ",\"out_shape\":[";
             for (size_t d = 0; d < k.sc_out_shape.size(); ++d)
                 s += (d ? "," : "") + std::to_string(k.sc_out_shape[d]);
             s += "],\"dtype\":\"" + std::string(dtype_name(k.sc_dtype)) + "\"}";

@@ -578,9 +578,10 @@ static int bit_width(uint64_t x) {
     return b;
 }
 
-// The kernels of one SCATTER node: a fill (out = base, elementwise), then
-// either one atomic-add kernel or the ordered chain (keys, stable radix
-// passes, in-order fold), then copies to any further output locations.
+// The kernels of one SCATTER node. Ordered: keys, stable radix passes, and
+// a fold that writes every output cell once (the base, plus the cell's run
+// of values in index order). Atomic: a fill (out = base, elementwise) and
+// one atomic-add kernel. Then copies to any further output locations.
 // Returns false (after marking what must exist in memory first) when a
 // source cannot be fused.
 static bool scatter_kernels(Ctx& c, int i, std::vector<Kernel>& out, std::vector<char>& need) {
@@ -589,9 +590,9 @@ static bool scatter_kernels(Ctx& c, int i, std::vector<Kernel>& out, std::vector
     const Shape& ish = c.g.nodes[nd.src[1]].shape;
     const std::vector<Loc> all = c.loc[i];
     const Loc target = all[0];
+    const bool ordered = !nd.atomic && numel(ish) > 0;
     std::vector<Kernel> ks;
-    // fill
-    {
+    if (!ordered) {  // fill
         Kernel f;
         f.cls = KClass::EW;
         f.domain = osh;
@@ -621,6 +622,18 @@ static bool scatter_kernels(Ctx& c, int i, std::vector<Kernel>& out, std::vector
             return false;
         }
     }
+    if (ordered) {  // the base, over the output's shape (its own memo: a
+                    // source shared with the values is another domain here)
+        k.domain = osh;
+        Builder bb{c, k, i, Builder::EW};
+        try {
+            k.sc_base = bb.build(nd.src[0], identity(osh.size()));
+        } catch (int) {
+            need[nd.src[0]] = 1;
+            return false;
+        }
+        k.domain = ish;
+    }
     k.sc_axis = nd.axis;
     k.sc_out = target;
     k.sc_out_shape = osh;
@@ -642,10 +655,10 @@ static bool scatter_kernels(Ctx& c, int i, std::vector<Kernel>& out, std::vector
             k.sc_part = "atomic";
             ks.push_back(k);
         } else {
-            if (keys >= (int64_t(1) << 32) - 1)
+            if (keys > (int64_t(1) << 32))
                 fail(RV_E_INVALID, fmt("SCATTER into %s: %lld target keys do not fit in 32 bits",
                                        shape_str(osh).c_str(), (long long)keys));
-            const int passes = std::max(1, (bit_width((uint64_t)keys) + 7) / 8);
+            const int passes = std::max(1, (bit_width((uint64_t)keys - 1) + 7) / 8);
             const int64_t nb = (cells + 2047) / 2048;
             auto region = [&](int64_t bytes) {
                 c.p.regions.push_back(Region{0, (size_t)bytes});
@@ -655,21 +668,29 @@ static bool scatter_kernels(Ctx& c, int i, std::vector<Kernel>& out, std::vector
                 k.sc_reg_keys[q] = region(cells * 4);
                 k.sc_reg_vals[q] = region(cells * 4);
             }
-            k.sc_reg_counts = region((256 * nb + 256) * 4);
+            if (nb > kScanInline) k.sc_reg_counts = region((256 * nb + 256) * 4);
+            k.sc_reg_bounds = region((keys + 1) * 4);
             k.sc_passes = passes;
             Kernel kk = k;
             kk.sc_part = "keys";
             ks.push_back(kk);
             for (int q = 0; q < passes; ++q)
                 for (const char* part : {"hist", "scan", "move"}) {
+                    if (std::string(part) != "move" && nb <= kScanInline) continue;
                     Kernel r = k;
                     r.leaves.clear();
                     r.ex.clear();
-                    r.sc_index = r.sc_values = -1;
+                    r.sc_index = r.sc_values = r.sc_base = -1;
                     r.sc_part = part;
                     r.sc_pass = q;
                     ks.push_back(r);
                 }
+            Kernel bd = k;
+            bd.leaves.clear();
+            bd.ex.clear();
+            bd.sc_index = bd.sc_values = bd.sc_base = -1;
+            bd.sc_part = "bounds";
+            ks.push_back(bd);
             Kernel fo = k;
             fo.sc_part = "fold";
             ks.push_back(fo);

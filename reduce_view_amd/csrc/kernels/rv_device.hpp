@@ -1352,7 +1352,7 @@ __device__ __forceinline__ float rv_fold_sum(const float* __restrict__ part, lon
 //
 // Stable LSD radix sort of (key, value) u32 pairs with 8-bit digits, in
 // tiles of 2048 pairs (256 lanes, 8 rounds of 256 consecutive pairs). Per
-// pass: a digit histogram per tile, an exclusive scan of each digit's tile
+// pass: digit counts per tile, an exclusive scan of each digit's tile
 // counts, and a move that places every pair at
 //   (pairs of smaller digits) + (pairs of its digit in earlier tiles)
 //   + (pairs of its digit earlier in this tile),
@@ -1361,22 +1361,6 @@ __device__ __forceinline__ float rv_fold_sum(const float* __restrict__ part, lon
 // pair at the same position.
 // ---------------------------------------------------------------------------
 #define RV_RS_TILE 2048
-
-__device__ __forceinline__ void rv_rs_hist(const unsigned* __restrict__ keys, unsigned* __restrict__ counts,
-                                           long long n, unsigned nb, int shift) {
-    __shared__ unsigned h[256];
-    const unsigned t = threadIdx.x;
-    h[t] = 0u;
-    __syncthreads();
-    const long long base = (long long)blockIdx.x * RV_RS_TILE;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const long long j = base + r * 256 + t;
-        if (j < n) atomicAdd(&h[(keys[j] >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    counts[(size_t)t * nb + blockIdx.x] = h[t];
-}
 
 // Exclusive scan of v over the 256 lanes of the workgroup; `tot` gets the
 // total. `w` is 4 words of LDS.
@@ -1415,22 +1399,95 @@ __device__ __forceinline__ void rv_rs_scan(unsigned* __restrict__ counts, unsign
     if (threadIdx.x == 0) counts[(size_t)256 * nb + blockIdx.x] = carry;
 }
 
+// Digit counts of one tile (one workgroup per tile): counts[d * nb + tile].
+__device__ __forceinline__ void rv_rs_hist(const unsigned* __restrict__ keys, unsigned* __restrict__ counts,
+                                           long long n, unsigned nb, int shift) {
+    __shared__ unsigned h[256];
+    const unsigned t = threadIdx.x;
+    h[t] = 0u;
+    __syncthreads();
+    const long long base = (long long)blockIdx.x * RV_RS_TILE;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const long long j = base + r * 256 + t;
+        if (j < n) atomicAdd(&h[(keys[j] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    counts[(size_t)t * nb + blockIdx.x] = h[t];
+}
+
+// Exclusive scan of v over the 1024 lanes of the workgroup (16 waves);
+// `tot` gets the total. `w` is 16 words of LDS.
+__device__ __forceinline__ unsigned rv_scan1024(unsigned v, unsigned* w, unsigned& tot) {
+    const unsigned lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    unsigned x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned y = (unsigned)__shfl_up((int)x, o, 64);
+        if (lane >= (unsigned)o) x += y;
+    }
+    if (lane == 63u) w[wave] = x;
+    __syncthreads();
+    unsigned pre = 0u, all = 0u;
+    for (unsigned q = 0; q < 16u; ++q) {
+        pre += q < wave ? w[q] : 0u;
+        all += w[q];
+    }
+    tot = all;
+    __syncthreads();
+    return pre + x - v;
+}
+
+// The move of one radix pass, 1024 lanes (16 waves) per tile of 2048 pairs
+// in 2 rounds. SELF (at most 64 tiles): every workgroup counts the digits
+// of every tile in LDS; otherwise `counts` holds the per-tile prefixes and
+// digit totals from rv_rs_hist and rv_rs_scan.
+template <bool SELF>
 __device__ __forceinline__ void rv_rs_move(const unsigned* __restrict__ keys, const unsigned* __restrict__ vals,
                                            unsigned* __restrict__ okeys, unsigned* __restrict__ ovals,
                                            const unsigned* __restrict__ counts, long long n, unsigned nb, int shift) {
     __shared__ unsigned run[256];
-    __shared__ unsigned wc[4][256];
-    __shared__ unsigned w[4];
+    __shared__ unsigned wc[16][256];
+    __shared__ unsigned w[16];
     const unsigned t = threadIdx.x, lane = t & 63u, wave = t >> 6;
-    unsigned tot;
-    const unsigned start = rv_scan256(counts[(size_t)256 * nb + t], w, tot);
-    run[t] = start + counts[(size_t)t * nb + blockIdx.x];
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int r = 0; r < 8; ++r) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) wc[q][t] = 0u;
+    unsigned total = 0u, pre = 0u;
+    if (SELF) {
+        __shared__ unsigned hc[256 * 64];
+        for (unsigned q = t; q < 256u * nb; q += 1024u) hc[q] = 0u;
         __syncthreads();
-        const long long j = (long long)blockIdx.x * RV_RS_TILE + r * 256 + t;
+        for (long long j0 = t; j0 < n; j0 += 1024 * 8) {  // 8 loads in flight per lane
+            unsigned kv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kv[u] = j0 + u * 1024 < n ? keys[j0 + u * 1024] : 0u;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (j0 + u * 1024 < n)
+                    atomicAdd(&hc[((kv[u] >> shift) & 255u) * nb + (unsigned)((j0 + u * 1024) >> 11)], 1u);
+        }
+        __syncthreads();
+        if (t < 256u)
+            for (unsigned b = 0; b < nb; ++b) {
+                const unsigned v = hc[t * nb + b];
+                total += v;
+                pre += b < blockIdx.x ? v : 0u;
+            }
+    } else if (t < 256u) {
+        total = counts[(size_t)256 * nb + t];
+        pre = counts[(size_t)t * nb + blockIdx.x];
+    }
+    unsigned tot;
+    const unsigned start = rv_scan1024(total, w, tot);
+    // lane t < 256 owns digit t: its running position and its column of
+    // the per-wave counts (cleared by the owner only, after every reader)
+    if (t < 256u) {
+        run[t] = start + pre;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) wc[q][t] = 0u;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int r = 0; r < 2; ++r) {
+        __syncthreads();
+        const long long j = (long long)blockIdx.x * RV_RS_TILE + r * 1024 + t;
         const bool ok = j < n;
         const unsigned key = ok ? keys[j] : 0u, val = ok ? vals[j] : 0u;
         const unsigned d = (key >> shift) & 255u;
@@ -1453,7 +1510,15 @@ __device__ __forceinline__ void rv_rs_move(const unsigned* __restrict__ keys, co
             }
         }
         __syncthreads();
-        run[t] += wc[0][t] + wc[1][t] + wc[2][t] + wc[3][t];
+        if (t < 256u) {
+            unsigned add = 0u;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                add += wc[q][t];
+                wc[q][t] = 0u;
+            }
+            run[t] += add;
+        }
     }
 }
 

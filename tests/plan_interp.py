@@ -73,89 +73,10 @@ def run_plan(desc: dict, inputs: list, out_specs: list) -> list:
         if k["plan"] == "empty":
             continue
         vals: dict[int, np.ndarray] = {}
-        leaves = k["leaves"]
-        for i, op in enumerate(ops):
-            name, dt = op["op"], op["dtype"]
-            if name == "LOAD":
-                L = leaves[op["leaf"]]
-                if L["zero"]:
-                    vals[i] = np.zeros(dom, STORAGE[dt])
-                else:
-                    # constant along a reduced dim (stride 0, unmasked): one
-                    # copy there, broadcast where used (a cell whose reduce
-                    # range is empty still sees it)
-                    v = L["view"]
-                    gshape = tuple(1 if (d in red and v["strides"][d] == 0 and v["mask_lo"][d] == 0
-                                         and v["mask_hi"][d] == dom[d]) else dom[d] for d in range(len(dom)))
-                    vals[i] = _gather(mem(L["loc"], L["dtype"]), v, gshape)
-            elif name == "CONST":
-                v = np.array([float(op["cval"])], np.float64)
-                if dt == "bf16":
-                    c = O.f32_to_bf16(v.astype(np.float32))
-                elif dt in O.INTS:
-                    c = v.astype(np.int64).astype(STORAGE[dt])
-                else:
-                    c = v.astype(STORAGE[dt])
-                vals[i] = np.broadcast_to(c.reshape((1,) * len(dom)), dom)
-            elif name == "MFMA_ACC":
-                a_leaf = leaves[_mfma_leaf(k, "a")]
-                b_leaf = leaves[_mfma_leaf(k, "b")]
-                A = O.bf16_to_f32(_gather(mem(a_leaf["loc"], "bf16"), a_leaf["view"], dom))
-                B = O.bf16_to_f32(_gather(mem(b_leaf["loc"], "bf16"), b_leaf["view"], dom))
-                acc = np.zeros(dom[:2] + (1,), np.float32)
-                for kk in range(dom[2]):
-                    acc = (acc + (A[:, :, kk:kk + 1] * B[:, :, kk:kk + 1]).astype(np.float32)).astype(np.float32)
-                vals[i] = np.broadcast_to(acc, dom)
-            elif name in ("SUM", "MAX"):
-                x = np.ascontiguousarray(np.broadcast_to(vals[op["a"]], dom))
-                vals[i] = O._reduce(name, x, ops[op["a"]]["dtype"], tuple(red))  # reduced dims kept as 1
-            elif name == "CAST":
-                vals[i] = O._cast(np.ascontiguousarray(vals[op["a"]]), ops[op["a"]]["dtype"], dt)
-            elif name in ("NEG", "EXP", "LOG", "SQRT", "RECIP"):
-                vals[i] = O._unary(name, np.ascontiguousarray(vals[op["a"]]), dt)
-            elif name in ("ADD", "MUL", "CMPLT"):
-                vals[i] = O._binary(name, np.ascontiguousarray(vals[op["a"]]), np.ascontiguousarray(vals[op["b"]]),
-                                    ops[op["a"]]["dtype"])
-            elif name == "WHERE":
-                vals[i] = np.where(vals[op["a"]] != 0, vals[op["b"]], vals[op["c"]]).astype(STORAGE[dt])
-            elif name == "GATHER":
-                L, gp = leaves[op["leaf"]], op["gather"]
-                t = np.broadcast_to(vals[op["a"]], dom).astype(np.int64)
-                if L["zero"]:
-                    vals[i] = np.zeros(dom, STORAGE[dt])
-                    continue
-                v = L["view"]
-                idx = np.full(dom, int(v["offset"]), dtype=np.int64) + (t - int(gp["lo"])) * int(gp["stride"])
-                inside = (t >= gp["lo"]) & (t < gp["hi"])
-                for d, g in enumerate(np.indices(dom, dtype=np.int64) if dom else []):
-                    idx = idx + g * int(v["strides"][d])
-                    inside &= (g >= v["mask_lo"][d]) & (g < v["mask_hi"][d])
-                flat = mem(L["loc"], L["dtype"])
-                assert not np.any(inside & ((idx < 0) | (idx >= flat.size))), "gathered read out of bounds"
-                vals[i] = np.where(inside, flat[np.where(inside, idx, 0)], np.zeros((), flat.dtype)).astype(flat.dtype)
-            else:
-                raise AssertionError(name)
         if k["class"] == "SCATTER":
-            part = k["plan_detail"]["part"]
-            if part in ("fold", "atomic"):  # keys and radix passes only order the adds
-                sc = k["scatter"]
-                axis = k["plan_detail"]["axis"]
-                oshape = tuple(sc["out_shape"])
-                o = mem(sc["out"], sc["dtype"], int(np.prod(oshape))).reshape(oshape)
-                index = np.broadcast_to(vals[sc["index"]], dom)
-                values = np.broadcast_to(vals[sc["values"]], dom)
-                rest = np.indices(tuple(dom[d] for d in range(len(dom)) if d != axis))
-                for kk in range(dom[axis]):
-                    t = np.take(index, kk, axis=axis)
-                    v = np.take(values, kk, axis=axis)
-                    sel = (t >= 0) & (t < oshape[axis])
-                    tgt = list(rest)
-                    tgt.insert(axis, np.where(sel, t, 0))
-                    cur = np.asarray(o[tuple(tgt)])
-                    new = np.reshape(O._binary("ADD", np.ascontiguousarray(cur), np.ascontiguousarray(v), sc["dtype"]),
-                                     cur.shape)
-                    o[tuple(tgt)] = np.where(sel, new, cur)
+            _scatter_step(k, dom, mem)
             continue
+        _evaluate(k, dom, red, mem, vals)
         for st in k["stores"]:
             v = vals[st_ex(k, st)]
             if k["class"] == "MFMA" and st["loc"]["kind"] == "workspace":
@@ -182,6 +103,119 @@ def run_plan(desc: dict, inputs: list, out_specs: list) -> list:
                 ws[st["loc"]["index"]] = o = np.zeros(size, STORAGE[st["dtype"]])
             _scatter(o, st["view"], sshape, v.astype(STORAGE[st["dtype"]]))
     return [o.reshape(s) for o, (s, _) in zip(outs, out_specs)]
+
+
+def _evaluate(k, dom, red, mem, vals, only=None):
+    """Every op of kernel ``k`` (or those in ``only``) over the domain
+    ``dom``, in order."""
+    ops, leaves = k["ops"], k["leaves"]
+    for i, op in enumerate(ops):
+        if only is not None and i not in only:
+            continue
+        name, dt = op["op"], op["dtype"]
+        if name == "LOAD":
+            L = leaves[op["leaf"]]
+            if L["zero"]:
+                vals[i] = np.zeros(dom, STORAGE[dt])
+            else:
+                # constant along a reduced dim (stride 0, unmasked): one
+                # copy there, broadcast where used (a cell whose reduce
+                # range is empty still sees it)
+                v = L["view"]
+                gshape = tuple(1 if (d in red and v["strides"][d] == 0 and v["mask_lo"][d] == 0
+                                     and v["mask_hi"][d] == dom[d]) else dom[d] for d in range(len(dom)))
+                vals[i] = _gather(mem(L["loc"], L["dtype"]), v, gshape)
+        elif name == "CONST":
+            v = np.array([float(op["cval"])], np.float64)
+            if dt == "bf16":
+                c = O.f32_to_bf16(v.astype(np.float32))
+            elif dt in O.INTS:
+                c = v.astype(np.int64).astype(STORAGE[dt])
+            else:
+                c = v.astype(STORAGE[dt])
+            vals[i] = np.broadcast_to(c.reshape((1,) * len(dom)), dom)
+        elif name == "MFMA_ACC":
+            a_leaf = leaves[_mfma_leaf(k, "a")]
+            b_leaf = leaves[_mfma_leaf(k, "b")]
+            A = O.bf16_to_f32(_gather(mem(a_leaf["loc"], "bf16"), a_leaf["view"], dom))
+            B = O.bf16_to_f32(_gather(mem(b_leaf["loc"], "bf16"), b_leaf["view"], dom))
+            acc = np.zeros(dom[:2] + (1,), np.float32)
+            for kk in range(dom[2]):
+                acc = (acc + (A[:, :, kk:kk + 1] * B[:, :, kk:kk + 1]).astype(np.float32)).astype(np.float32)
+            vals[i] = np.broadcast_to(acc, dom)
+        elif name in ("SUM", "MAX"):
+            x = np.ascontiguousarray(np.broadcast_to(vals[op["a"]], dom))
+            vals[i] = O._reduce(name, x, ops[op["a"]]["dtype"], tuple(red))  # reduced dims kept as 1
+        elif name == "CAST":
+            vals[i] = O._cast(np.ascontiguousarray(vals[op["a"]]), ops[op["a"]]["dtype"], dt)
+        elif name in ("NEG", "EXP", "LOG", "SQRT", "RECIP"):
+            vals[i] = O._unary(name, np.ascontiguousarray(vals[op["a"]]), dt)
+        elif name in ("ADD", "MUL", "CMPLT"):
+            vals[i] = O._binary(name, np.ascontiguousarray(vals[op["a"]]), np.ascontiguousarray(vals[op["b"]]),
+                                ops[op["a"]]["dtype"])
+        elif name == "WHERE":
+            vals[i] = np.where(vals[op["a"]] != 0, vals[op["b"]], vals[op["c"]]).astype(STORAGE[dt])
+        elif name == "GATHER":
+            L, gp = leaves[op["leaf"]], op["gather"]
+            t = np.broadcast_to(vals[op["a"]], dom).astype(np.int64)
+            if L["zero"]:
+                vals[i] = np.zeros(dom, STORAGE[dt])
+                continue
+            v = L["view"]
+            idx = np.full(dom, int(v["offset"]), dtype=np.int64) + (t - int(gp["lo"])) * int(gp["stride"])
+            inside = (t >= gp["lo"]) & (t < gp["hi"])
+            for d, g in enumerate(np.indices(dom, dtype=np.int64) if dom else []):
+                idx = idx + g * int(v["strides"][d])
+                inside &= (g >= v["mask_lo"][d]) & (g < v["mask_hi"][d])
+            flat = mem(L["loc"], L["dtype"])
+            assert not np.any(inside & ((idx < 0) | (idx >= flat.size))), "gathered read out of bounds"
+            vals[i] = np.where(inside, flat[np.where(inside, idx, 0)], np.zeros((), flat.dtype)).astype(flat.dtype)
+        else:
+            raise AssertionError(name)
+
+
+def _reach(ops, root):
+    out, stack = set(), [root]
+    while stack:
+        i = stack.pop()
+        if i is None or i < 0 or i in out:
+            continue
+        out.add(i)
+        stack += [ops[i]["a"], ops[i]["b"], ops[i]["c"]]
+    return out
+
+
+def _scatter_step(k, dom, mem):
+    """A scatter step as the additions it stands for: the ordered fold is the
+    base plus every value at its target in index order; the atomic step the
+    same adds into the target, which already holds the base. Keys and radix
+    passes only order the adds."""
+    part = k["plan_detail"]["part"]
+    if part not in ("fold", "atomic"):
+        return
+    sc = k["scatter"]
+    axis = k["plan_detail"]["axis"]
+    oshape = tuple(sc["out_shape"])
+    o = mem(sc["out"], sc["dtype"], int(np.prod(oshape))).reshape(oshape)
+    ops = k["ops"]
+    vals: dict[int, np.ndarray] = {}
+    if part == "fold":
+        _evaluate(k, oshape, (), mem, vals, only=_reach(ops, sc["base"]))
+        o[...] = np.broadcast_to(vals[sc["base"]], oshape)
+        vals = {}
+    _evaluate(k, dom, (), mem, vals, only=_reach(ops, sc["index"]) | _reach(ops, sc["values"]))
+    index = np.broadcast_to(vals[sc["index"]], dom)
+    values = np.broadcast_to(vals[sc["values"]], dom)
+    rest = np.indices(tuple(dom[d] for d in range(len(dom)) if d != axis))
+    for kk in range(dom[axis]):
+        t = np.take(index, kk, axis=axis)
+        v = np.take(values, kk, axis=axis)
+        sel = (t >= 0) & (t < oshape[axis])
+        tgt = list(rest)
+        tgt.insert(axis, np.where(sel, t, 0))
+        cur = np.asarray(o[tuple(tgt)])
+        new = np.reshape(O._binary("ADD", np.ascontiguousarray(cur), np.ascontiguousarray(v), sc["dtype"]), cur.shape)
+        o[tuple(tgt)] = np.where(sel, new, cur)
 
 
 def st_ex(k, st):

@@ -148,10 +148,11 @@ def test_embedding_scatter_ordered_dtypes(dt):
            {k: inp[k] for k in ("values", "ids")})
 
 
-@pytest.mark.parametrize("keys,cells", [(200, 5000), (70000, 9000), (300, 100000)])
+@pytest.mark.parametrize("keys,cells", [(200, 5000), (70000, 9000), (300, 100000), (1000, 300000)])
 def test_scatter_ordered_radix_passes_and_tiles(keys, cells):
-    """One, three and two radix passes; 3, 5 and 49 tiles of 2048 cells, so
-    equal keys cross tile boundaries and must keep their order."""
+    """One, three, two and two radix passes; 3, 5, 49 and 147 tiles of 2048
+    cells, so equal keys cross tile boundaries and must keep their order
+    (147 tiles: the digit counts are scanned by a kernel of their own)."""
     _case(f"scatter ordered keys={keys} cells={cells}")
     rng = np.random.default_rng(86)
     base = rng.standard_normal((keys, 3)).astype(np.float32)
@@ -164,7 +165,8 @@ def test_scatter_ordered_radix_passes_and_tiles(keys, cells):
     kd = _prog(g).describe()["kernels"]
     detail = kd[1]["plan_detail"]
     assert detail["keys"] == keys and detail["index_cells"] == cells  # the 3 columns are carried
-    assert detail["radix_passes"] == (int(keys).bit_length() + 7) // 8
+    assert detail["radix_passes"] == (int(keys - 1).bit_length() + 7) // 8
+    assert ("scatter_scan" in [x["plan"] for x in kd]) == (cells > 64 * 2048)
     _exact(f"scatter_k{keys}_c{cells}", g, {"data": base, "index": index, "values": values})
 
 
