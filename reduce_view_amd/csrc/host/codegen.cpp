@@ -1666,11 +1666,21 @@ std::string Gen::gen_scatter() {
     // R * JU * CB loads are in flight per lane.
     const int fin = k.sc_passes % 2;
     const int64_t NF = numel(k.domain) / CELLS;
+    // vector mode: CB consecutive cells of the last dim per lane (it is
+    // carried and CB divides it), stored as one 16-byte (or narrower) write
+    const int last = rank - 1;
+    const int vcb = std::max(1, std::min(4, 16 / dtype_size(dt)));
+    const bool VEC = ((k.sc_fdims >> last) & 1u) && vcb > 1 && k.domain[last] % vcb == 0;
     int TPS = 1;
-    while (TPS < 256 && TPS < NF) TPS *= 2;
+    while (TPS < 256 && TPS * (VEC ? vcb : 1) < NF) TPS *= 2;
     const int SPB = 256 / TPS;
-    const int CB = (int)std::min<int64_t>(4, (NF + TPS - 1) / TPS);
+    const int CB = VEC ? vcb : (int)std::min<int64_t>(4, (NF + TPS - 1) / TPS);
     const int JU = env_int("RV_SCATTER_JU", 1);
+    // values read as one vector per cell when they are a plain load that is
+    // contiguous and aligned along the last dim
+    const Ex& VX = k.ex[k.sc_values];
+    const bool VLD = VEC && VX.op == RV_BUFFER && !k.leaves[VX.leaf].zero &&
+                     !masked(k.leaves[VX.leaf].v, last) && leaf_vec_ok(k.leaves[VX.leaf], last, CB);
     int R = 4;  // plan value (lower.cpp)
     {
         const char* q = strstr(k.plan_json.c_str(), "\"keys_per_group\":");
@@ -1709,13 +1719,14 @@ std::string Gen::gen_scatter() {
     for (int d : idims) obs += fmt(" + o%d[r] * %lldLL", d, (long long)os[d]);
     b << "      ob[r] = " << obs << ";\n";
     b << "    }\n";
-    b << "    for (long long f0 = l; f0 < " << NF << "LL; f0 += " << (int64_t)TPS * CB << "LL) {\n";
+    b << "    for (long long f0 = (long long)l" << (VEC ? fmt(" * %d", CB) : std::string()) << "; f0 < " << NF
+      << "LL; f0 += " << (int64_t)TPS * CB << "LL) {\n";
     b << "      " << vt(dt) << " acc[" << R << "][" << CB << "];\n";
     b << "      long long fo[" << CB << "];\n";
     for (int d : fd) b << "      long long fc" << d << "[" << CB << "];\n";
     b << "#pragma unroll\n";
     b << "      for (int cb = 0; cb < " << CB << "; ++cb) {\n";
-    b << "        const long long f = f0 + (long long)cb * " << TPS << ";\n";
+    b << "        const long long f = f0 + (long long)cb" << (VEC ? std::string() : fmt(" * %d", TPS)) << ";\n";
     b << "        const long long fcl = f < " << NF << "LL ? f : " << NF - 1 << "LL;\n";
     decompose("fcl", fd, "fi", "        ");
     std::string fo = "0LL";
@@ -1754,9 +1765,26 @@ std::string Gen::gen_scatter() {
     b << "#pragma unroll\n";
     b << "        for (int u = 0; u < " << JU << "; ++u) {\n";
     decompose("(long long)cj[r][u]", cd, "i", "          ");
-    b << "#pragma unroll\n";
-    b << "          for (int cb = 0; cb < " << CB << "; ++cb) {\n";
-    {
+    if (VLD) {
+        const Leaf& L = k.leaves[VX.leaf];
+        std::vector<std::string> idx(rank);
+        for (int d : cd) idx[d] = fmt("i%d", d);
+        for (int d : fd) idx[d] = fmt("fc%d[0]", d);
+        std::vector<int> all;
+        for (int d = 0; d < rank; ++d) all.push_back(d);
+        const std::string mc = mask_cond(L.v, idx, all);
+        b << "          if (add[r][u]" << (mc.empty() ? "" : " && " + mc) << ") {\n";
+        b << "            const rv_pack<" << st(dt) << ", " << CB << "> v = "
+          << vload(L, CB, pname(L.loc, L.dtype, false) + " + " + addr(L.v, idx)) << ";\n";
+        b << "#pragma unroll\n";
+        b << "            for (int cb = 0; cb < " << CB << "; ++cb) vv[r][u][cb] = " << ld(dt, "v.v[cb]") << ";\n";
+        b << "          } else {\n";
+        b << "#pragma unroll\n";
+        b << "            for (int cb = 0; cb < " << CB << "; ++cb) vv[r][u][cb] = " << zero_of(dt) << ";\n";
+        b << "          }\n";
+    } else {
+        b << "#pragma unroll\n";
+        b << "          for (int cb = 0; cb < " << CB << "; ++cb) {\n";
         std::vector<std::string> idx(rank);
         for (int d : cd) idx[d] = fmt("i%d", d);
         for (int d : fd) idx[d] = fmt("fc%d[cb]", d);
@@ -1767,8 +1795,8 @@ std::string Gen::gen_scatter() {
         b << "            } else {\n";
         b << "              vv[r][u][cb] = " << zero_of(dt) << ";\n";
         b << "            }\n";
+        b << "          }\n";
     }
-    b << "          }\n";
     b << "        }\n";
     Ex add;
     add.op = RV_ADD;
@@ -1783,10 +1811,19 @@ std::string Gen::gen_scatter() {
     b << "      }\n";
     b << "#pragma unroll\n";
     b << "      for (int r = 0; r < " << R << "; ++r)\n";
-    b << "#pragma unroll\n";
-    b << "        for (int cb = 0; cb < " << CB << "; ++cb)\n";
-    b << "          if (kv[r] && f0 + (long long)cb * " << TPS << " < " << NF << "LL) " << OUT << "[ob[r] + fo[cb]] = "
-      << sv(dt, "acc[r][cb]") << ";\n";
+    if (VEC) {  // CB divides NF: every lane's CB cells are in range together
+        b << "        if (kv[r]) {\n";
+        b << "          rv_pack<" << st(dt) << ", " << CB << "> v;\n";
+        b << "#pragma unroll\n";
+        b << "          for (int cb = 0; cb < " << CB << "; ++cb) v.v[cb] = " << sv(dt, "acc[r][cb]") << ";\n";
+        b << "          " << vstore(dt, CB, OUT + " + ob[r] + fo[0]", "v") << ";\n";
+        b << "        }\n";
+    } else {
+        b << "#pragma unroll\n";
+        b << "        for (int cb = 0; cb < " << CB << "; ++cb)\n";
+        b << "          if (kv[r] && f0 + (long long)cb * " << TPS << " < " << NF << "LL) " << OUT
+          << "[ob[r] + fo[cb]] = " << sv(dt, "acc[r][cb]") << ";\n";
+    }
     b << "    }\n";
     b << "  }\n";
     return b.str();

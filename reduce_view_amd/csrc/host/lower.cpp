@@ -284,8 +284,13 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             k.plan = "scatter_" + k.sc_part;
             k.block[0] = 256;
             auto cap_grid = [](int64_t g) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>(g, 1 << 20)); };
+            // lanes per key: enough for the carried cells, CB consecutive
+            // cells per lane when the last dim is carried and CB divides it
+            const int last = (int)k.domain.size() - 1;
+            const int vcb = std::max(1, std::min(4, 16 / dtype_size(k.sc_dtype)));
+            const bool vec = ((k.sc_fdims >> last) & 1u) && vcb > 1 && k.domain[last] % vcb == 0;
             int tps = 1;
-            while (tps < 256 && tps < nf) tps *= 2;
+            while (tps < 256 && tps * (vec ? vcb : 1) < nf) tps *= 2;
             if (k.sc_part == "atomic") {
                 k.grid[0] = cap_grid((numel(k.domain) + 255) / 256);
             } else if (k.sc_part == "keys") {
