@@ -1835,9 +1835,12 @@ std::string Gen::gen_scatter() {
 std::string Gen::gen_attn() {
     const int64_t Tq = k.domain[1], D = k.domain[2];
     const int64_t Tk = k.leaves[1].v.shape[1];
-    const std::string q = pname(k.leaves[0].loc, RV_BF16, false);
-    const std::string kp = pname(k.leaves[1].loc, RV_BF16, false);
-    const std::string v = pname(k.leaves[2].loc, RV_BF16, false);
+    std::string q, kp, v;
+    if (!k.attn_merge) {
+        q = pname(k.leaves[0].loc, RV_BF16, false);
+        kp = pname(k.leaves[1].loc, RV_BF16, false);
+        v = pname(k.leaves[2].loc, RV_BF16, false);
+    }
     std::string o = "nullptr", l = "nullptr";
     int odt = RV_F32;
     int no = 0, nl = 0;
@@ -1853,11 +1856,36 @@ std::string Gen::gen_attn() {
     }
     if (no > 1 || nl > 1) fail(RV_E_UNSUPPORTED_LAYOUT, "sdpa_fwd: one output requested twice");
     const float sl2 = (float)(k.attn_scale * 1.4426950408889634);  // scale * log2(e)
-    std::ostringstream b;
-    b << "  rv_attn_fwd_bf16<" << D << ", " << (k.attn_causal ? "true" : "false") << ", "
-      << (odt == RV_BF16 ? "true" : "false") << ">(" << q << ", " << kp << ", " << v << ", " << o << ", " << l << ", "
-      << Tq << ", " << Tk << ", " << fmt("%a", sl2) << "f);\n";
-    return b.str();
+    const std::string causal = k.attn_causal ? "true" : "false", obf = odt == RV_BF16 ? "true" : "false";
+    std::ostringstream pre, b;
+    if (k.attn_merge) {
+        const std::string op = pname(Loc{2, k.attn_reg_o}, RV_F32, false);
+        const std::string ml = pname(Loc{2, k.attn_reg_ml}, RV_F32, false);
+        b << "  rv_attn_merge_chunks<" << D << ", " << causal << ", " << obf << ">(" << o << ", " << l << ", " << op
+          << ", " << ml << ", " << Tq << ", " << Tk << ", " << k.attn_chunk << ", " << k.attn_cmax << ");\n";
+        return "@@BODY@@" + b.str();
+    }
+    int NG = 2, KT = 64;  // plan values (lower.cpp)
+    {
+        const char* c = k.plan_json.c_str();
+        const char* at = strstr(c, "\"key_groups\":");
+        if (at) NG = atoi(at + strlen("\"key_groups\":"));
+        at = strstr(c, "\"key_tile\":");
+        if (at) KT = atoi(at + strlen("\"key_tile\":"));
+    }
+    b << "  rv_attn_fwd_bf16<" << D << ", " << causal << ", " << obf << ", " << NG << ", " << KT << ">(" << q << ", "
+      << kp << ", " << v << ", " << o << ", " << l << ", " << Tq << ", " << Tk << ", " << fmt("%a", sl2) << "f";
+    if (k.attn_chunk > 0) {
+        // the (query block, key chunk) of every workgroup, longest blocks first
+        pre << "__constant__ unsigned " << k.name << "_map[" << k.attn_map.size() << "] = {";
+        for (size_t i = 0; i < k.attn_map.size(); ++i) pre << (i ? (i % 16 ? ", " : ",\n  ") : "") << k.attn_map[i] << "u";
+        pre << "};\n";
+        const std::string op = pname(Loc{2, k.attn_reg_o}, RV_F32, true);
+        const std::string ml = pname(Loc{2, k.attn_reg_ml}, RV_F32, true);
+        b << ", " << k.name << "_map, " << k.attn_chunk << ", " << op << ", " << ml << ", " << k.attn_cmax;
+    }
+    b << ");\n";
+    return pre.str() + "@@BODY@@" + b.str();
 }
 
 std::string Gen::gen_fold() {
@@ -1967,7 +1995,13 @@ std::string Gen::gen() {
         case KClass::ROW: body = k.plan == "row_stream" ? gen_row_stream() : gen_row(); break;
         case KClass::REDUCE: body = gen_cells(); break;
         case KClass::FOLD: body = gen_fold(); break;
-        case KClass::ATTN: body = gen_attn(); break;
+        case KClass::ATTN: {
+            std::string s = gen_attn();
+            size_t at = s.find("@@BODY@@");
+            pre = s.substr(0, at);
+            body = s.substr(at + 8);
+            break;
+        }
         case KClass::SCATTER: body = gen_scatter(); break;
         case KClass::MFMA: {
             std::string s = gen_gemm();

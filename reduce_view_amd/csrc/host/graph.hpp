@@ -126,6 +126,15 @@ struct Kernel {
     // ATTN (leaves q, k, v; domain (H, Tq, D); Tk = leaves[1].v.shape[1])
     double attn_scale = 0.0;
     bool attn_causal = false;
+    // keys split into chunks of attn_chunk over workgroups (0: one
+    // workgroup per query block); attn_map[w] = (query block << 16) | chunk;
+    // chunk partials in workspace regions attn_reg_o, attn_reg_ml; the
+    // merge kernel (attn_merge) folds them
+    int64_t attn_chunk = 0;
+    int attn_cmax = 1;
+    std::vector<unsigned> attn_map;
+    int attn_reg_o = -1, attn_reg_ml = -1;
+    bool attn_merge = false;
     // SCATTER: one step of a scatter-add into `sc_out`. Domain: the index's
     // shape; ex sc_index / sc_values over it, sc_base over the output's.
     //   "atomic": every position adds its value with an atomic add (the

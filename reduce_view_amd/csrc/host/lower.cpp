@@ -205,22 +205,38 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
         case KClass::ATTN: {
             const int64_t H = k.domain[0], Tq = k.domain[1], D = k.domain[2];
             const int64_t Tk = k.leaves[1].v.shape[1];
+            if (k.attn_merge) {  // one lane per query, a workgroup per query block and head
+                k.plan = "attn_merge";
+                k.grid[0] = (unsigned)((Tq + 127) / 128);
+                k.grid[1] = (unsigned)H;
+                k.block[0] = 128;
+                k.lds = 0;
+                snprintf(buf, sizeof buf, "\"key_chunk\":%lld,\"chunks_max\":%d,\"head_dim\":%lld",
+                         (long long)k.attn_chunk, k.attn_cmax, (long long)D);
+                k.plan_json = buf;
+                return;
+            }
             k.plan = "attn_fwd";
-            k.grid[0] = (unsigned)((Tq + 127) / 128);  // 128 queries (4 waves of 32) per workgroup
+            // 128 queries (4 waves of 32) per workgroup, or one workgroup per
+            // (query block, key chunk) when the keys are split
+            k.grid[0] = k.attn_chunk > 0 ? (unsigned)k.attn_map.size() : (unsigned)((Tq + 127) / 128);
             k.grid[1] = (unsigned)H;
-            // the device skeleton's defaults: NG groups of 4 waves split the
-            // keys, tiles of KT keys
-            const int NG = 2, KT = D <= 64 ? 128 : 64;
+            // NG groups of 4 waves split the keys (RV_ATTN_GROUPS), tiles of
+            // KT keys (RV_ATTN_TILE, a multiple of 64)
+            const int NG = env_int("RV_ATTN_GROUPS", 2), KT = env_int("RV_ATTN_TILE", 64);
+            if (NG < 1 || NG > 4 || KT < 64 || KT % 64 || KT > 256)
+                fail(RV_E_INVALID, "RV_ATTN_GROUPS must be 1..4 and RV_ATTN_TILE 64, 128, 192 or 256");
             k.block[0] = (unsigned)(256 * NG);
             k.lds = std::max<size_t>((size_t)(2 * KT * (D + 8) + 2 * KT * (D + 16)) * 2,
                                      (size_t)(NG - 1) * 4 * 64 * (16 * (D / 32) + 2) * 4);
             snprintf(buf, sizeof buf,
                      "\"queries_per_workgroup\":128,\"queries_per_wave\":32,\"key_groups\":%d,\"key_tile\":%d,"
-                     "\"key_step\":64,"
+                     "\"key_step\":64,\"key_chunk\":%lld,\"chunks_max\":%d,"
                      "\"head_dim\":%lld,"
                      "\"keys\":%lld,\"causal\":%s,\"scale\":%.17g,\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
                      "\"scores\":\"transposed (K q^T): one query per lane pair\",\"p_operand\":\"bf16\"",
-                     NG, KT, (long long)D, (long long)Tk, k.attn_causal ? "true" : "false", k.attn_scale);
+                     NG, KT, (long long)k.attn_chunk, k.attn_cmax, (long long)D, (long long)Tk,
+                     k.attn_causal ? "true" : "false", k.attn_scale);
             k.plan_json = buf;
             return;
         }

@@ -359,6 +359,34 @@ static void attn_kernel(Ctx& c, const std::vector<int>& nodes, Kernel& k) {
             k.stores.push_back(st);
         }
     }
+    // Keys split into chunks of CK over workgroups when a query block has
+    // more: more workgroups than query blocks (a 128-query block of 8192
+    // keys is 8 workgroups at CK = 1024), and under the causal mask the
+    // long blocks no longer set the time alone. RV_ATTN_CHUNK = 0: no split.
+    const int64_t H = q[0], Tq = q[1], Tk = c.g.nodes[nd.src[1]].shape[1], D = q[2];
+    int64_t CK = env_int("RV_ATTN_CHUNK", 1024);
+    if (CK < 0) fail(RV_E_INVALID, "RV_ATTN_CHUNK must be 0 or positive");
+    if (CK > 0) {
+        CK = (CK + 127) / 128 * 128;
+        const int64_t nqb = (Tq + 127) / 128;
+        std::vector<unsigned> map;
+        int64_t cmax = 1;
+        for (int64_t j = nqb - 1; j >= 0; --j) {
+            const int64_t kend = k.attn_causal ? std::min(Tk, std::min(Tq, 128 * (j + 1))) : Tk;
+            const int64_t nch = std::max<int64_t>(1, (kend + CK - 1) / CK);
+            cmax = std::max(cmax, nch);
+            for (int64_t ch = 0; ch < nch; ++ch) map.push_back((unsigned)((j << 16) | ch));
+        }
+        if (cmax > 1 && cmax < 65536 && nqb < 65536 && (int64_t)map.size() <= 65535) {
+            k.attn_chunk = CK;
+            k.attn_cmax = (int)cmax;
+            k.attn_map = map;
+            k.attn_reg_o = (int)c.p.regions.size();
+            c.p.regions.push_back(Region{0, (size_t)(H * nqb * cmax * 128 * D * 4)});
+            k.attn_reg_ml = (int)c.p.regions.size();
+            c.p.regions.push_back(Region{0, (size_t)(H * nqb * cmax * 128 * 2 * 4)});
+        }
+    }
 }
 
 // Row space of a reduce: (input shape, reduced dims) with every reduced
@@ -796,6 +824,12 @@ void schedule(Program& p) {
                     }
                 attn_kernel(c, sib, k);
                 kernels.push_back(k);
+                if (k.attn_chunk > 0) {  // fold the chunk partials
+                    Kernel mk = k;
+                    mk.attn_merge = true;
+                    mk.attn_map.clear();
+                    kernels.push_back(mk);
+                }
             } else if (g.nodes[i].op == RV_SCATTER) {
                 if (!scatter_kernels(c, i, kernels, need)) again = true;
             } else if (try_ew(c, i, k)) {

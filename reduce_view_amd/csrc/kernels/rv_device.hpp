@@ -1093,11 +1093,14 @@ __device__ __forceinline__ void rv_attn_merge(float& m, float& l, float m2, floa
     m = mn;
 }
 
-template <int D, bool CAUSAL, bool OUT_BF16, int NG = 2, int KT = (D <= 64 ? 128 : 64)>
+template <int D, bool CAUSAL, bool OUT_BF16, int NG = 2, int KT = 64>
 __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restrict__ Q,
                                                  const unsigned short* __restrict__ K,
                                                  const unsigned short* __restrict__ V, void* __restrict__ O,
-                                                 float* __restrict__ L, int Tq, int Tk, float sl2) {
+                                                 float* __restrict__ L, int Tq, int Tk, float sl2,
+                                                 const unsigned* __restrict__ wmap = nullptr, int CK = 0,
+                                                 float* __restrict__ opart = nullptr,
+                                                 float* __restrict__ mlpart = nullptr, int CMAX = 1) {
     // NG groups of 4 waves split the keys; KT (a multiple of 64) keys per tile
     constexpr int NT = 256 * NG;              // threads
     constexpr int KP = D + 8;                 // K tile pitch (bf16): conflict-free 16-byte fragment reads
@@ -1116,8 +1119,18 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wave >> 2, wq = wave & 3;  // key group, query wave
     const int ql = lane & 31, hh = lane >> 5;
-    // the longest rows first: under CAUSAL the last query block has the most keys
-    const int qb = (CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x) * 128;
+    // which query block and which chunk of its keys: from the map when the
+    // keys are split over workgroups (longest blocks first), else one
+    // workgroup per block, the longest (under CAUSAL, the last) first
+    int jb, ch = 0;
+    if (wmap != nullptr) {
+        const unsigned e = wmap[blockIdx.x];
+        jb = (int)(e >> 16);
+        ch = (int)(e & 0xffffu);
+    } else {
+        jb = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+    }
+    const int qb = jb * 128;
     const int q0 = qb + wq * 32;
     const int qi = q0 + ql;
     const long long qbase = (long long)blockIdx.y * Tq;
@@ -1167,7 +1180,11 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
 
     int kend = Tk;
     if (CAUSAL) kend = min(Tk, min(Tq, qb + 128));
-    const int nt = (kend + KT - 1) / KT;
+    // this workgroup's keys: [k0, k1)
+    const int nchunks = wmap != nullptr ? (kend + CK - 1) / CK : 1;
+    const int k0 = wmap != nullptr ? ch * CK : 0;
+    const int k1 = wmap != nullptr ? min(kend, k0 + CK) : kend;
+    const int nt = (k1 - k0 + KT - 1) / KT;
     rv_f32x16 oacc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -1175,19 +1192,19 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
     float m = ninf, l = 0.0f;
 
-    load_tile(0);
-    store_tile(0, 0);
+    load_tile(k0);
+    store_tile(0, k0);
     __syncthreads();
     for (int t = 0; t < nt; ++t) {
         const int b = t & 1;
-        if (t + 1 < nt) load_tile((t + 1) * KT);
+        if (t + 1 < nt) load_tile(k0 + (t + 1) * KT);
 #pragma unroll
         for (int sub = 0; sub < KT / 64; ++sub) {
             const int step = t * (KT / 64) + sub;
-            const int kb = step * 64;
+            const int kb = k0 + step * 64;
             // alternate 64-key steps between the two groups; skip steps whose
             // keys are all hidden from this wave's queries (both wave-uniform)
-            if (step % NG != grp || kb >= kend || (CAUSAL && kb > q0 + 31)) continue;
+            if (step % NG != grp || kb >= k1 || (CAUSAL && kb > q0 + 31)) continue;
             const unsigned short* kt = ks + b * KT * KP + sub * 64 * KP;
             const unsigned short* vt = vs + b * KT * VP + sub * 64 * VP;
             // S^T for 64 keys as two 32 x 32 tiles: A = K rows (lane: key ql
@@ -1209,11 +1226,11 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sv[16 * u + r] = sacc[u][r];
-            if (kb + 64 > Tk || (CAUSAL && kb + 63 > q0)) {  // wave-uniform
+            if (kb + 64 > k1 || (CAUSAL && kb + 63 > q0)) {  // wave-uniform
 #pragma unroll
                 for (int r = 0; r < 32; ++r) {
                     const int key = kb + (r >> 4) * 32 + ((r & 15) >> 2) * 8 + hh * 4 + (r & 3);
-                    if (key >= Tk || (CAUSAL && key > qi)) sv[r] = ninf;
+                    if (key >= k1 || (CAUSAL && key > qi)) sv[r] = ninf;
                 }
             }
             float cm = sv[0];
@@ -1223,17 +1240,15 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
             // max(s) * c equals max(s * c) for c > 0 (rounding is monotonic)
             const float mn = fmaxf(m, cm * sl2);
             const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+            // while every key seen is hidden (mn = -inf) every score is -inf
+            // and exp2(-inf - 0) = 0: no branch, no separate zero fill
+            const float mns = mn == ninf ? 0.0f : mn;
             float pr[32];
             float ps = 0.0f;
-            if (mn != ninf) {
 #pragma unroll
-                for (int r = 0; r < 32; ++r) {
-                    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sl2, -mn));
-                    ps = ps + pr[r];
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 32; ++r) pr[r] = 0.0f;
+            for (int r = 0; r < 32; ++r) {
+                pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sl2, -mns));
+                ps = ps + pr[r];
             }
             ps = rv_pair_sum(ps);
             l = l * alpha + ps;
@@ -1247,11 +1262,19 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
                     for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
             }
             // O^T += V^T P^T over the 64 keys (four k16 steps)
+            // P to bf16 two at a time (one v_cvt_pk_bf16_f32 per pair)
             rv_bf16x8 pb[4];
+            typedef __attribute__((ext_vector_type(2))) float f32x2;
+            typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pb[s][i] = (__bf16)pr[8 * s + i];
+                for (int i = 0; i < 4; ++i) {
+                    const f32x2 f = {pr[8 * s + 2 * i], pr[8 * s + 2 * i + 1]};
+                    const bf16x2 h = __builtin_convertvector(f, bf16x2);
+                    pb[s][2 * i] = h[0];
+                    pb[s][2 * i + 1] = h[1];
+                }
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -1275,7 +1298,7 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
                                                                        oacc[dt], 0, 0, 0);
                 }
         }
-        if (t + 1 < nt) store_tile(b ^ 1, (t + 1) * KT);
+        if (t + 1 < nt) store_tile(b ^ 1, k0 + (t + 1) * KT);
         __syncthreads();
     }
     // merge: groups 1 .. NG-1 hand (m, l, accumulator) to group 0 through
@@ -1304,6 +1327,24 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * a1 + other[2 + 16 * dt + r] * a2;
     }
+    if (qi < Tq && nchunks > 1) {  // a partial: (m, l) and the unnormalised accumulator
+        const long long slot = ((long long)blockIdx.y * ((Tq + 127) / 128) + jb) * CMAX + ch;
+        float* op = opart + (slot * 128 + (qi - qb)) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                rv_pack<float, 4> pk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk.v[i] = oacc[dt][4 * g + i];
+                rv_stv<float, 4>(op + dt * 32 + g * 8 + hh * 4, pk);
+            }
+        if (hh == 0) {
+            mlpart[(slot * 128 + (qi - qb)) * 2] = m;
+            mlpart[(slot * 128 + (qi - qb)) * 2 + 1] = l;
+        }
+        return;
+    }
     if (qi < Tq) {
         const float inv = 1.0f / l;
         if (O != nullptr) {
@@ -1327,6 +1368,62 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
         }
         if (L != nullptr && hh == 0) L[qbase + qi] = m * 0.693147180559945309f + logf(l);
     }
+}
+
+// Merge of the key chunks of a query block (grid: query blocks x heads, 128
+// lanes, one query each): the chunks' (m, l, accumulator) folded in chunk
+// order, as the key groups of one workgroup are, then O = acc / l and
+// L = m ln 2 + log l. Blocks with one chunk were written whole.
+template <int D, bool CAUSAL, bool OUT_BF16>
+__device__ __forceinline__ void rv_attn_merge_chunks(void* __restrict__ O, float* __restrict__ L,
+                                                     const float* __restrict__ opart,
+                                                     const float* __restrict__ mlpart, int Tq, int Tk, int CK,
+                                                     int CMAX) {
+    const int jb = blockIdx.x, qb = jb * 128, qi = qb + threadIdx.x;
+    const int kend = CAUSAL ? min(Tk, min(Tq, qb + 128)) : Tk;
+    const int nchunks = (kend + CK - 1) / CK;
+    if (nchunks <= 1 || qi >= Tq) return;
+    const long long slot0 = ((long long)blockIdx.y * gridDim.x + jb) * CMAX;
+    float m = mlpart[(slot0 * 128 + threadIdx.x) * 2], l = mlpart[(slot0 * 128 + threadIdx.x) * 2 + 1];
+    float acc[D];
+    const float* p0 = opart + (slot0 * 128 + threadIdx.x) * D;
+#pragma unroll
+    for (int d = 0; d < D; d += 4) {
+        const rv_pack<float, 4> v = rv_ldv<float, 4>(p0 + d);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[d + i] = v.v[i];
+    }
+    for (int c = 1; c < nchunks; ++c) {
+        const long long sl = (slot0 + c) * 128 + threadIdx.x;
+        float a1, a2;
+        rv_attn_merge(m, l, mlpart[sl * 2], mlpart[sl * 2 + 1], a1, a2);
+        const float* pc = opart + sl * D;
+#pragma unroll
+        for (int d = 0; d < D; d += 4) {
+            const rv_pack<float, 4> v = rv_ldv<float, 4>(pc + d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[d + i] = acc[d + i] * a1 + v.v[i] * a2;
+        }
+    }
+    const float inv = 1.0f / l;
+    const long long at = ((long long)blockIdx.y * Tq + qi) * D;
+    if (O != nullptr) {
+#pragma unroll
+        for (int d = 0; d < D; d += 4) {
+            if (OUT_BF16) {
+                rv_pack<unsigned short, 4> pk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk.v[i] = rv_f2bf(acc[d + i] * inv);
+                rv_stv<unsigned short, 4>(reinterpret_cast<unsigned short*>(O) + at + d, pk);
+            } else {
+                rv_pack<float, 4> pk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pk.v[i] = acc[d + i] * inv;
+                rv_stv<float, 4>(reinterpret_cast<float*>(O) + at + d, pk);
+            }
+        }
+    }
+    if (L != nullptr) L[(long long)blockIdx.y * Tq + qi] = m * 0.693147180559945309f + logf(l);
 }
 
 // Deterministic fold of `count` float partials into one value: each thread

@@ -66,7 +66,7 @@ def _f64_parts(q, k, v, scale, causal):
 def _check(name, spec, inp, h, tq, tk, d, causal, out_dtype="f32", outputs="ol"):
     prog = _prog(spec)
     kd = prog.describe()["kernels"]
-    assert [k["class"] for k in kd] == ["ATTN"], kd
+    assert {k["class"] for k in kd} == {"ATTN"}, kd
     got = run(prog, inp)
     ref = oracle.run(spec, inp)
     scale = 1.0 / np.sqrt(d)
@@ -110,6 +110,26 @@ def test_attention_matches_composition(h, tq, tk, d, causal, odt):
     spec = synth.attention(h, tq, tk, d, causal, odt)
     inp = synth.inputs_attention(h, tq, tk, d)
     _check(f"attention_{h}x{tq}x{tk}x{d}", spec, inp, h, tq, tk, d, causal, odt)
+
+
+@pytest.mark.parametrize("chunk", [128, 256])
+@pytest.mark.parametrize("h,tq,tk,d,causal,odt", [
+    (2, 300, 300, 64, True, "bf16"),
+    (3, 64, 1000, 32, False, "f32"),
+    (1, 513, 700, 128, True, "f32"),
+    (2, 1024, 1024, 32, True, "f32"),
+])
+def test_attention_key_chunks_merge(monkeypatch, chunk, h, tq, tk, d, causal, odt):
+    """Keys split over workgroups in chunks of 128 or 256 (the long-row
+    split, forced onto small shapes): partials (m, l, accumulator) per chunk,
+    folded in chunk order by the merge kernel."""
+    monkeypatch.setenv("RV_ATTN_CHUNK", str(chunk))
+    _case(f"attention chunks of {chunk}: {h}x{tq}x{tk}x{d} causal={causal} out={odt}")
+    spec = synth.attention(h, tq, tk, d, causal, odt)
+    plans = [k["plan"] for k in _prog(spec).describe()["kernels"]]
+    assert plans == ["attn_fwd", "attn_merge"], plans
+    inp = synth.inputs_attention(h, tq, tk, d)
+    _check(f"attention_chunk{chunk}_{h}x{tq}x{tk}x{d}", spec, inp, h, tq, tk, d, causal, odt)
 
 
 @pytest.mark.parametrize("outputs", ["o", "l"])
