@@ -222,8 +222,10 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             k.grid[0] = k.attn_chunk > 0 ? (unsigned)k.attn_map.size() : (unsigned)((Tq + 127) / 128);
             k.grid[1] = (unsigned)H;
             // NG groups of 4 waves split the keys (RV_ATTN_GROUPS), tiles of
-            // KT keys (RV_ATTN_TILE, a multiple of 64)
-            const int NG = env_int("RV_ATTN_GROUPS", 2), KT = env_int("RV_ATTN_TILE", 64);
+            // KT keys (RV_ATTN_TILE, a multiple of 64): 64 for key chunks,
+            // 128 for whole rows (measured)
+            const int NG = env_int("RV_ATTN_GROUPS", 2);
+            const int KT = env_int("RV_ATTN_TILE", k.attn_chunk > 0 ? 64 : 128);
             if (NG < 1 || NG > 4 || KT < 64 || KT % 64 || KT > 256)
                 fail(RV_E_INVALID, "RV_ATTN_GROUPS must be 1..4 and RV_ATTN_TILE 64, 128, 192 or 256");
             k.block[0] = (unsigned)(256 * NG);
