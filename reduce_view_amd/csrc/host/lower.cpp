@@ -205,11 +205,11 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
         case KClass::ATTN: {
             const int64_t H = k.domain[0], Tq = k.domain[1], D = k.domain[2];
             const int64_t Tk = k.leaves[1].v.shape[1];
-            if (k.attn_merge) {  // one lane per query, a workgroup per query block and head
+            if (k.attn_merge) {  // D / 4 lanes per query, 256 / (D / 4) queries per workgroup
                 k.plan = "attn_merge";
-                k.grid[0] = (unsigned)((Tq + 127) / 128);
+                k.grid[0] = (unsigned)((Tq + 127) / 128 * (128 / (256 / (D / 4))));
                 k.grid[1] = (unsigned)H;
-                k.block[0] = 128;
+                k.block[0] = 256;
                 k.lds = 0;
                 snprintf(buf, sizeof buf, "\"key_chunk\":%lld,\"chunks_max\":%d,\"head_dim\":%lld",
                          (long long)k.attn_chunk, k.attn_cmax, (long long)D);

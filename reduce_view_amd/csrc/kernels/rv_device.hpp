@@ -1370,60 +1370,52 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
     }
 }
 
-// Merge of the key chunks of a query block (grid: query blocks x heads, 128
-// lanes, one query each): the chunks' (m, l, accumulator) folded in chunk
-// order, as the key groups of one workgroup are, then O = acc / l and
-// L = m ln 2 + log l. Blocks with one chunk were written whole.
+// Merge of the key chunks of a query block: D / 4 lanes per query, each
+// folding 4 accumulator columns (and the query's (m, l)) over the chunks in
+// chunk order, as the key groups of one workgroup are folded, then
+// O = acc / l and L = m ln 2 + log l. Grid: (query blocks x 128 / QPB, heads)
+// with QPB = 256 / (D / 4) queries per workgroup. Blocks with one chunk were
+// written whole by the forward kernel.
 template <int D, bool CAUSAL, bool OUT_BF16>
 __device__ __forceinline__ void rv_attn_merge_chunks(void* __restrict__ O, float* __restrict__ L,
                                                      const float* __restrict__ opart,
                                                      const float* __restrict__ mlpart, int Tq, int Tk, int CK,
                                                      int CMAX) {
-    const int jb = blockIdx.x, qb = jb * 128, qi = qb + threadIdx.x;
+    constexpr int TQ = D / 4, QPB = 256 / TQ;
+    const int sub = (int)blockIdx.x % (128 / QPB), jb = (int)blockIdx.x / (128 / QPB);
+    const int ql = sub * QPB + (int)threadIdx.x / TQ, d0 = ((int)threadIdx.x % TQ) * 4;
+    const int qb = jb * 128, qi = qb + ql;
     const int kend = CAUSAL ? min(Tk, min(Tq, qb + 128)) : Tk;
     const int nchunks = (kend + CK - 1) / CK;
     if (nchunks <= 1 || qi >= Tq) return;
-    const long long slot0 = ((long long)blockIdx.y * gridDim.x + jb) * CMAX;
-    float m = mlpart[(slot0 * 128 + threadIdx.x) * 2], l = mlpart[(slot0 * 128 + threadIdx.x) * 2 + 1];
-    float acc[D];
-    const float* p0 = opart + (slot0 * 128 + threadIdx.x) * D;
-#pragma unroll
-    for (int d = 0; d < D; d += 4) {
-        const rv_pack<float, 4> v = rv_ldv<float, 4>(p0 + d);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[d + i] = v.v[i];
-    }
+    const long long slot0 = ((long long)blockIdx.y * ((Tq + 127) / 128) + jb) * CMAX;
+    float m = mlpart[(slot0 * 128 + ql) * 2], l = mlpart[(slot0 * 128 + ql) * 2 + 1];
+    rv_pack<float, 4> acc = rv_ldv<float, 4>(opart + (slot0 * 128 + ql) * D + d0);
+#pragma unroll 4
     for (int c = 1; c < nchunks; ++c) {
-        const long long sl = (slot0 + c) * 128 + threadIdx.x;
+        const long long sl = (slot0 + c) * 128 + ql;
+        const rv_pack<float, 4> v = rv_ldv<float, 4>(opart + sl * D + d0);
         float a1, a2;
         rv_attn_merge(m, l, mlpart[sl * 2], mlpart[sl * 2 + 1], a1, a2);
-        const float* pc = opart + sl * D;
 #pragma unroll
-        for (int d = 0; d < D; d += 4) {
-            const rv_pack<float, 4> v = rv_ldv<float, 4>(pc + d);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[d + i] = acc[d + i] * a1 + v.v[i] * a2;
-        }
+        for (int i = 0; i < 4; ++i) acc.v[i] = acc.v[i] * a1 + v.v[i] * a2;
     }
     const float inv = 1.0f / l;
-    const long long at = ((long long)blockIdx.y * Tq + qi) * D;
+    const long long at = ((long long)blockIdx.y * Tq + qi) * D + d0;
     if (O != nullptr) {
+        if (OUT_BF16) {
+            rv_pack<unsigned short, 4> pk;
 #pragma unroll
-        for (int d = 0; d < D; d += 4) {
-            if (OUT_BF16) {
-                rv_pack<unsigned short, 4> pk;
+            for (int i = 0; i < 4; ++i) pk.v[i] = rv_f2bf(acc.v[i] * inv);
+            rv_stv<unsigned short, 4>(reinterpret_cast<unsigned short*>(O) + at, pk);
+        } else {
+            rv_pack<float, 4> pk;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pk.v[i] = rv_f2bf(acc[d + i] * inv);
-                rv_stv<unsigned short, 4>(reinterpret_cast<unsigned short*>(O) + at + d, pk);
-            } else {
-                rv_pack<float, 4> pk;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pk.v[i] = acc[d + i] * inv;
-                rv_stv<float, 4>(reinterpret_cast<float*>(O) + at + d, pk);
-            }
+            for (int i = 0; i < 4; ++i) pk.v[i] = acc.v[i] * inv;
+            rv_stv<float, 4>(reinterpret_cast<float*>(O) + at, pk);
         }
     }
-    if (L != nullptr) L[(long long)blockIdx.y * Tq + qi] = m * 0.693147180559945309f + logf(l);
+    if (L != nullptr && d0 == 0) L[(long long)blockIdx.y * Tq + qi] = m * 0.693147180559945309f + logf(l);
 }
 
 // Deterministic fold of `count` float partials into one value: each thread
