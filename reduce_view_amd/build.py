@@ -75,6 +75,12 @@ def check_device_header(verbose: bool = False) -> None:
                 "extern \"C\" __global__ void __launch_bounds__(512) chk11(const unsigned short* a, "
                 "const unsigned short* b, float* p) {\n"
                 "  rv_gemm_pp_bf16<false, 0, E, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
+                "chk15(const unsigned short* a, const unsigned short* b, float* p) {\n"
+                "  rv_gemm_w4_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
+                "chk16(const unsigned short* a, const unsigned short* b, float* p) {\n"
+                "  rv_gemm_w4_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(512) chk12(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
                 "float* l) { rv_attn_fwd_bf16<32, true, false>(q, k, v, o, l, 1000, 1000, 0.25f); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(512) chk13(const unsigned short* q, const unsigned short* k, const unsigned short* v, "

@@ -278,7 +278,8 @@ struct Gen {
     std::string header() {
         // a 256 x 256 contraction tile on 4 waves keeps 256 accumulators per
         // lane: one wave per SIMD, so the whole register file is the wave's
-        const bool one_wave = k.cls == KClass::MFMA && k.plan == "gemm_lds" && k.block[0] == 256;
+        const bool one_wave =
+            k.cls == KClass::MFMA && ((k.plan == "gemm_lds" && k.block[0] == 256) || k.plan == "gemm_w4");
         return "extern \"C\" __global__ void __launch_bounds__(" + std::to_string(k.block[0]) + ") " +
                (one_wave ? "__attribute__((amdgpu_waves_per_eu(1, 1))) " : "") + k.name + "(" + signature() + ")";
     }
@@ -1965,6 +1966,7 @@ std::string Gen::gen_gemm() {
     const char* fn = k.plan == "gemm_lds"    ? "rv_gemm_lds_bf16<"
                      : k.plan == "gemm_pp"   ? "rv_gemm_pp_bf16<"
                      : k.plan == "gemm_lds4" ? "rv_gemm_lds4_bf16<"
+                     : k.plan == "gemm_w4"   ? "rv_gemm_w4_bf16<"
                      : k.plan == "gemm256"   ? "rv_gemm256_bf16<"
                                              : "rv_gemm_bf16<";
     int TM = 2, TN = 4;
@@ -1977,8 +1979,18 @@ std::string Gen::gen_gemm() {
         size_t at = k.plan_json.find("\"phase_k16\":");
         if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"phase_k16\":%d", &KH);
     }
+    int NV0 = 8, PIN = 1, NS = 4;
+    {
+        size_t st = k.plan_json.find("\"stages\":");
+        if (st != std::string::npos) sscanf(k.plan_json.c_str() + st, "\"stages\":%d", &NS);
+        size_t at = k.plan_json.find("\"copies_first_step\":");
+        if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"copies_first_step\":%d", &NV0);
+        PIN = k.plan_json.find("\"pinned_interleave\":false") == std::string::npos;
+    }
     const std::string targs = k.plan == "gemm_lds"  ? fmt(", %s, %d, %d", sname.c_str(), TM, TN)
                               : k.plan == "gemm_pp" ? fmt(", %s, %d", sname.c_str(), KH)
+                              : k.plan == "gemm_w4"
+                                  ? fmt(", %s, %d, %s, %d", sname.c_str(), NV0, PIN ? "true" : "false", NS)
                                                     : "";
     b << "  " << fn << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << targs << ">(" << pa << ", " << pb
       << ", " << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", "

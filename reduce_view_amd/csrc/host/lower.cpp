@@ -244,18 +244,33 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
         }
         case KClass::MFMA: {
             int64_t M = k.domain[0], N = k.domain[1];
-            // 256 x 256 tiles when the shape allows: direct-to-LDS copies and
-            // 8 waves ("lds", the default; "lds4" with four 32-deep stages;
-            // "pp" with the two wave groups in ping-pong) or register-staged
-            // copies and 4 waves ("reg"); otherwise 128 x 128 register-staged
-            // tiles. RV_GEMM_WAVES=4x4 (four waves of 128 x 128) spills.
+            // 256 x 256 tiles when the shape allows, operands copied straight
+            // into LDS: 4 waves of 128 x 128 with their own software pipeline
+            // ("w4", the default), 8 waves of 64 x 128 ("lds"; "lds4" with four
+            // 32-deep stages; "pp" with the two wave groups in ping-pong), or
+            // register-staged copies and 4 waves ("reg"); otherwise 128 x 128
+            // register-staged tiles.
             const bool big = M % 256 == 0 && N % 256 == 0;
             const char* kind = getenv("RV_GEMM_KERNEL");
-            std::string kd = kind && *kind ? kind : "lds";
+            std::string kd = kind && *kind ? kind : "w4";
             if (!big) kd = "reg128";
             int BM = 128, BN = 128, waves = 4;
             int TM = 2, TN = 4;
-            if (kd == "lds" || kd == "lds4" || kd == "pp") {
+            int nv0 = 8, pin = 1, stages = 4;
+            if (kd == "w4") {
+                k.plan = "gemm_w4";
+                BM = BN = 256;
+                TM = TN = 4;
+                // copies issued in a k-tile's first k16 step (the rest after
+                // its barrier), and whether the MFMA/LDS/copy interleaving is pinned
+                const char* sp = getenv("RV_GEMM_W4_SPLIT");
+                if (sp && *sp) nv0 = std::max(0, std::min(8, atoi(sp)));
+                const char* pn = getenv("RV_GEMM_W4_PIN");
+                if (pn && *pn) pin = atoi(pn) != 0;
+                const char* st = getenv("RV_GEMM_W4_STAGES");
+                if (st && atoi(st) == 5) stages = 5;
+                k.lds = 2 * stages * 256 * 32 * 2;
+            } else if (kd == "lds" || kd == "lds4" || kd == "pp") {
                 k.plan = kd == "lds" ? "gemm_lds" : kd == "pp" ? "gemm_pp" : "gemm_lds4";
                 BM = BN = 256;
                 waves = 8;
@@ -285,6 +300,11 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
                      "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d",
                      BM, BN, waves, TM, TN, kn ? "kn" : "nk", per_lane - 1 + 6 + waves - 1);
             k.plan_json = buf;
+            if (k.plan == "gemm_w4") {
+                snprintf(buf, sizeof buf, ",\"stages\":%d,\"copies_first_step\":%d,\"pinned_interleave\":%s",
+                         stages, nv0, pin ? "true" : "false");
+                k.plan_json += buf;
+            }
             if (k.plan == "gemm_pp") {
                 // k16 steps per ping-pong phase (2, or 1 with RV_GEMM_KH=1)
                 const char* kh = getenv("RV_GEMM_KH");
