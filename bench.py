@@ -223,8 +223,8 @@ def _cpu_baseline(wl, name, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="ew_chain")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -282,11 +282,15 @@ def main():
     # host enqueues faster than the kernels drain; HIP graph replay was
     # measured slower than these direct launches on this stack)
     ms_step = timed(step, args.steps)
-    # per-program launch duration: events around K back-to-back launches of
-    # that program alone (same input rotation), on the launch stream
+    # per-program launch duration: events around back-to-back launches of
+    # that program alone (same input rotation), on the launch stream; at
+    # least K launches and at least 30 ms of them, since the clock under a
+    # sustained load settles over milliseconds and a short burst times the
+    # ramp rather than the kernel
     per_kernel = {}
     for j, (n, p, _) in enumerate(progs):
-        per_kernel[n] = timed(lambda i: launch[j][(i + j) % nsets](), args.steps)
+        reps = max(args.steps, int(np.ceil(30.0 / max(ms_step, 1e-3))))
+        per_kernel[n] = timed(lambda i: launch[j][(i + j) % nsets](), reps)
 
     total_work = sum(b for _, _, b in progs)
     scale = 1e-12 if wl["unit"] == "TFLOP/s" else 1e-9

@@ -1985,12 +1985,13 @@ std::string Gen::gen_gemm() {
         if (st != std::string::npos) sscanf(k.plan_json.c_str() + st, "\"stages\":%d", &NS);
         size_t at = k.plan_json.find("\"copies_first_step\":");
         if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"copies_first_step\":%d", &NV0);
-        PIN = k.plan_json.find("\"pinned_interleave\":false") == std::string::npos;
+        size_t il = k.plan_json.find("\"interleave\":");
+        if (il != std::string::npos) sscanf(k.plan_json.c_str() + il, "\"interleave\":%d", &PIN);
     }
     const std::string targs = k.plan == "gemm_lds"  ? fmt(", %s, %d, %d", sname.c_str(), TM, TN)
                               : k.plan == "gemm_pp" ? fmt(", %s, %d", sname.c_str(), KH)
                               : k.plan == "gemm_w4"
-                                  ? fmt(", %s, %d, %s, %d", sname.c_str(), NV0, PIN ? "true" : "false", NS)
+                                  ? fmt(", %s, %d, %d, %d", sname.c_str(), NV0, PIN, NS)
                                                     : "";
     b << "  " << fn << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << targs << ">(" << pa << ", " << pb
       << ", " << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", "

@@ -256,19 +256,22 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             if (!big) kd = "reg128";
             int BM = 128, BN = 128, waves = 4;
             int TM = 2, TN = 4;
-            int nv0 = 8, pin = 1, stages = 4;
+            int nv0 = 2, pin = 1, stages = 5;
             if (kd == "w4") {
                 k.plan = "gemm_w4";
                 BM = BN = 256;
                 TM = TN = 4;
-                // copies issued in a k-tile's first k16 step (the rest after
-                // its barrier), and whether the MFMA/LDS/copy interleaving is pinned
+                // LDS stages (5: copies four k-tiles ahead; 4), copies issued in a
+                // k-tile's first k16 step (the rest after its barrier), and the
+                // MFMA/LDS/copy interleaving (1 pinned, 2 reads front-loaded, 0 free).
+                // Measured on cold operands: 5 stages with 2 or 3 early copies
+                // take 15% fewer cycles than 4 stages with all 8 early.
                 const char* sp = getenv("RV_GEMM_W4_SPLIT");
                 if (sp && *sp) nv0 = std::max(0, std::min(8, atoi(sp)));
                 const char* pn = getenv("RV_GEMM_W4_PIN");
-                if (pn && *pn) pin = atoi(pn) != 0;
+                if (pn && *pn) pin = std::max(0, std::min(2, atoi(pn)));
                 const char* st = getenv("RV_GEMM_W4_STAGES");
-                if (st && atoi(st) == 5) stages = 5;
+                if (st && (atoi(st) == 4 || atoi(st) == 5)) stages = atoi(st);
                 k.lds = 2 * stages * 256 * 32 * 2;
             } else if (kd == "lds" || kd == "lds4" || kd == "pp") {
                 k.plan = kd == "lds" ? "gemm_lds" : kd == "pp" ? "gemm_pp" : "gemm_lds4";
@@ -301,8 +304,8 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
                      BM, BN, waves, TM, TN, kn ? "kn" : "nk", per_lane - 1 + 6 + waves - 1);
             k.plan_json = buf;
             if (k.plan == "gemm_w4") {
-                snprintf(buf, sizeof buf, ",\"stages\":%d,\"copies_first_step\":%d,\"pinned_interleave\":%s",
-                         stages, nv0, pin ? "true" : "false");
+                snprintf(buf, sizeof buf, ",\"stages\":%d,\"copies_first_step\":%d,\"interleave\":%d", stages, nv0,
+                         pin);
                 k.plan_json += buf;
             }
             if (k.plan == "gemm_pp") {

@@ -919,15 +919,16 @@ __device__ __forceinline__ void rv_gemm_lds4_bf16(const unsigned short* __restri
 // 8, so the LDS moves 192 KB per 64 of k (64 KB copied in, 128 KB read out)
 // instead of 256 KB, against the same 2048 MFMA cycles per SIMD.
 // With one wave per SIMD nothing else hides latency, so the wave pipelines
-// itself: k-tiles of 32 in four LDS stages (as the four-stage kernel, copies
-// three k-tiles ahead), and the fragments double buffered in registers (x for
-// a k-tile's first k16 step, y for its second). Step 0 multiplies x while
-// reading y and issuing the copies of the k-tile three ahead; step 1 waits
-// for its own copies of the next stage, passes the barrier (after which every
-// wave's copies of that stage have landed and nobody reads the stage that
-// step 0 of the next k-tile overwrites), and multiplies y while reading the
-// next stage's x. sched_group_barrier pins one LDS read and one copy after
-// each MFMA so the reads hide under the matrix work.
+// itself: k-tiles of 32 in NS LDS stages of 32 KB (five fill the LDS; the
+// copies run NS - 1 k-tiles ahead), and the fragments double buffered in
+// registers (x for a k-tile's first k16 step, y for its second). Step 0
+// multiplies x while reading y and issuing NV0 of the 8 copies of the k-tile
+// NS - 1 ahead; step 1 waits for its own copies of the next stage, passes the
+// barrier (after which every wave's copies of that stage have landed and
+// nobody reads the stage the copies overwrite), and multiplies y while
+// reading the next stage's x and issuing the other copies.
+// sched_group_barrier pins one LDS read and one copy after each MFMA so the
+// reads hide under the matrix work.
 // ---------------------------------------------------------------------------
 // Per-lane byte offsets of the fragment reads inside one stage (loop
 // invariant; the stage's array base, the 32-row tile i (2048 bytes) and, for a
@@ -1017,14 +1018,29 @@ __device__ __forceinline__ void rv_g5_copy(unsigned short* As, unsigned short* B
 }
 
 // interleaving of one k16 step's 16 MFMAs with its NDS LDS reads and NVM
-// copies (mask 0x008 MFMA, 0x100 LDS read, 0x010 vector memory)
-template <int NDS, int NVM>
+// copies (mask 0x008 MFMA, 0x100 LDS read, 0x010 vector memory). MODE 1: one
+// LDS read and one copy after each MFMA while any remain. MODE 2: the LDS
+// reads two per MFMA up front (they feed the next step: landing early keeps
+// its first MFMA from waiting), the copies one per MFMA after them.
+template <int NDS, int NVM, int MODE = 1>
 __device__ __forceinline__ void rv_g5_pin() {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (i < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        if (MODE == 1) {
+            if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        } else {
+            constexpr int R = (NDS + 1) / 2;  // MFMAs that carry LDS reads
+            if (2 * i + 1 < NDS)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            else if (2 * i < NDS)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i >= R && i - R < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            if (i == 15)
+#pragma unroll
+                for (int c = 16 - R; c < NVM; ++c) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        }
     }
 }
 
@@ -1040,7 +1056,7 @@ __device__ __forceinline__ void rv_g5_keep(rv_f32x16 (&acc)[4][4]) {
         for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
-template <bool B_KN, int MODE, class Epi, int NV0 = 8, bool PIN = true, int NS = 4>
+template <bool B_KN, int MODE, class Epi, int NV0 = 8, int PIN = 1, int NS = 4>
 __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict__ A,
                                                 const unsigned short* __restrict__ B, long long a_off, long long lda,
                                                 long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
@@ -1120,7 +1136,7 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
         rv_g5_frags<B_KN, 1>(ya, yb, CA, CB, fo);                                                     \
         rv_g5_copy<B_KN, 0, NV0>(WA, WB, A, B, a_base, lda, b_base, ldb, RV_G5_KT(t_ + NS - 1), wave, va, vb); \
         rv_g3_step<4, 4>(acc, xa, xb);                                                                 \
-        if (PIN) rv_g5_pin<NDS, NV0>();                                                                \
+        if (PIN) rv_g5_pin<NDS, NV0, PIN>();                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                             \
         RV_WAIT_VM(8 * (NS - 2) + NV0);                                                                \
         RV_LDS_BARRIER();                                                                              \
@@ -1128,7 +1144,7 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
         rv_g5_frags<B_KN, 0>(xa, xb, XA, XB, fo);                                                     \
         rv_g5_copy<B_KN, NV0, 8>(WA, WB, A, B, a_base, lda, b_base, ldb, RV_G5_KT(t_ + NS - 1), wave, va, vb); \
         rv_g3_step<4, 4>(acc, ya, yb);                                                                 \
-        if (PIN) rv_g5_pin<NDS, 8 - NV0>();                                                            \
+        if (PIN) rv_g5_pin<NDS, 8 - NV0, PIN>();                                                       \
         __builtin_amdgcn_sched_barrier(0);                                                             \
         rv_g5_keep(acc);                                                                               \
     }
