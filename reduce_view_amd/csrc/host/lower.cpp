@@ -447,10 +447,15 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
                 if (along) two = false;
             }
         int vw = two ? 8 : 4;
-        // about 16 cells per lane: enough bytes in flight per lane, few
-        // enough VGPRs for high occupancy
+        // about 64 bytes per lane of each row-long operand (16 cells of 4
+        // bytes or more, 32 of 2 bytes): enough bytes in flight per lane, few
+        // enough VGPRs for high occupancy (16 two-byte cells per lane left
+        // RMSNorm over float16 rows 17% slower); never so few lanes that a
+        // lane holds more than 32 cells, the most kept in registers
+        const int cells = two ? 32 : 16;
         int T = 1024;
-        while (T > 16 && (int64_t)T * 16 > NR) T /= 2;
+        while (T > 16 && (int64_t)T * cells > NR) T /= 2;
+        while (T < 1024 && (NR + (int64_t)T * vw - 1) / ((int64_t)T * vw) * vw > 32) T *= 2;
         T = env_int("RV_ROW_THREADS", T);
         if (T < 1 || T > 1024 || (T & (T - 1))) fail(RV_E_INVALID, "RV_ROW_THREADS must be a power of two <= 1024");
         const int block = std::max(256, T);
