@@ -184,7 +184,11 @@ def test_layernorm(rows, n):
 
 # ---- config 5: bf16 contraction on MFMA + relu^2 + full SUM ----------------------
 
-@pytest.mark.parametrize("m,n,k", [(128, 128, 64), (256, 384, 192), (256, 512, 128)])
+# 256-multiples run the 256 x 256 four-wave kernel (five 32-deep LDS stages):
+# k of 64, 192, 128 (and 256, 320 below) leave 2, 1, 4, 3 and 0 k-tiles after
+# its whole rounds of five
+@pytest.mark.parametrize("m,n,k", [(128, 128, 64), (256, 384, 192), (256, 512, 128), (256, 256, 64),
+                                   (512, 256, 192)])
 def test_gemm_integer_valued_bit_exact(m, n, k):
     _case(f"gemm int {m}x{n}x{k}")
     inp = synth.inputs_gemm_integer(m, n, k)

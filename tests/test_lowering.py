@@ -265,3 +265,19 @@ def test_attention_contract_errors():
     assert status(g, lambda n: setattr(n[3], "buf", 7)) == "RV_E_UNSUPPORTED_OP"
     g = synth.attention(1, 8, 8, 32, outputs="o")
     assert status(g, lambda n: setattr(n[3], "reduce_axes", 5 << 16)) == "RV_E_INVALID"
+
+
+def test_contraction_plans():
+    """256-multiples take the four-wave 256 x 256 kernel (five 32-deep LDS
+    stages, 160 KB), other shapes the 128 x 128 one; float16 rows give each
+    ROW lane 32 cells, float32 rows 16."""
+    big = rv.compile_spec(synth.gemm_relu2_sum(4096, 4096, 4096)).describe()["kernels"][0]
+    assert big["plan"] == "gemm_w4" and big["block"][0] == 256 and big["grid"][0] == 256
+    pd = big["plan_detail"]
+    assert pd["tile"] == [256, 256, 64] and pd["wave_tiles"] == [4, 4] and pd["stages"] == 5
+    assert pd["copies_first_step"] == 2 and big["lds_bytes"] == 5 * 2 * 256 * 32 * 2
+    small = rv.compile_spec(synth.gemm_bf16(256, 384, 192)).describe()["kernels"][0]
+    assert small["plan"] == "gemm" and small["grid"][0] == 2 * 3
+    f16 = rv.compile_spec(synth.rmsnorm(64, 4096, dtype="f16")).describe()["kernels"][0]
+    f32 = rv.compile_spec(synth.rmsnorm(64, 4096)).describe()["kernels"][0]
+    assert f16["plan_detail"]["threads_per_row"] == 128 and f32["plan_detail"]["threads_per_row"] == 256
