@@ -254,6 +254,15 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             const char* kind = getenv("RV_GEMM_KERNEL");
             std::string kd = kind && *kind ? kind : "w4";
             if (!big) kd = "reg128";
+            // the four-wave kernel keeps each lane's part of a copy address as
+            // a 32-bit byte offset (up to 15 A rows, or B rows): row pitches
+            // of 2^27 elements or more take the 8-wave kernel
+            {
+                const rv_view& av = k.leaves[k.mfma_a].v;
+                const rv_view& bv = k.leaves[k.mfma_b].v;
+                const int64_t ldb_ = bv.strides[1] == 1 ? bv.strides[2] : bv.strides[1];
+                if (kd == "w4" && (av.strides[0] >= ((int64_t)1 << 27) || ldb_ >= ((int64_t)1 << 27))) kd = "lds";
+            }
             int BM = 128, BN = 128, waves = 4;
             int TM = 2, TN = 4;
             int nv0 = 2, pin = 1, stages = 5;
