@@ -1853,19 +1853,22 @@ __device__ __forceinline__ void rv_rs_move(const unsigned* __restrict__ keys, co
         __shared__ unsigned hc[256 * 64];
         for (unsigned q = t; q < 256u * nb; q += 1024u) hc[q] = 0u;
         __syncthreads();
-        for (long long j0 = t; j0 < n; j0 += 1024 * 8) {  // 8 loads in flight per lane
-            unsigned kv[8];
+        // 32 loads in flight per lane (32768 keys in one round trip); the
+        // counts are tile-major, so the 64 lanes of a wave (one tile, random
+        // digits) spread over the banks instead of meeting in a few
+        for (long long j0 = t; j0 < n; j0 += 1024 * 32) {
+            unsigned kv[32];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) kv[u] = j0 + u * 1024 < n ? keys[j0 + u * 1024] : 0u;
+            for (int u = 0; u < 32; ++u) kv[u] = j0 + u * 1024 < n ? keys[j0 + u * 1024] : 0u;
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < 32; ++u)
                 if (j0 + u * 1024 < n)
-                    atomicAdd(&hc[((kv[u] >> shift) & 255u) * nb + (unsigned)((j0 + u * 1024) >> 11)], 1u);
+                    atomicAdd(&hc[(unsigned)((j0 + u * 1024) >> 11) * 256u + ((kv[u] >> shift) & 255u)], 1u);
         }
         __syncthreads();
         if (t < 256u)
             for (unsigned b = 0; b < nb; ++b) {
-                const unsigned v = hc[t * nb + b];
+                const unsigned v = hc[b * 256u + t];
                 total += v;
                 pre += b < blockIdx.x ? v : 0u;
             }
@@ -1883,11 +1886,20 @@ __device__ __forceinline__ void rv_rs_move(const unsigned* __restrict__ keys, co
         for (int q = 0; q < 16; ++q) wc[q][t] = 0u;
     }
     const unsigned long long below = (1ull << lane) - 1ull;
+    // both rounds' pairs loaded up front (one round trip instead of two)
+    unsigned rk[2], rvv[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const long long j = (long long)blockIdx.x * RV_RS_TILE + r * 1024 + t;
+        rk[r] = j < n ? keys[j] : 0u;
+        rvv[r] = j < n ? vals[j] : 0u;
+    }
+#pragma unroll
     for (int r = 0; r < 2; ++r) {
         __syncthreads();
         const long long j = (long long)blockIdx.x * RV_RS_TILE + r * 1024 + t;
         const bool ok = j < n;
-        const unsigned key = ok ? keys[j] : 0u, val = ok ? vals[j] : 0u;
+        const unsigned key = rk[r], val = rvv[r];
         const unsigned d = (key >> shift) & 255u;
         unsigned long long same = __builtin_amdgcn_ballot_w64(ok);
 #pragma unroll
