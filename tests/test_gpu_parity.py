@@ -209,6 +209,37 @@ def test_gemm_integer_valued_bit_exact(m, n, k):
     assert got.tobytes() == ref.tobytes()
 
 
+# the contraction kernels and pipeline settings the plan's environment knobs
+# select (the default is the four-wave kernel, five stages, 2 early copies,
+# pinned interleaving): every one stays bit-exact on integer-valued operands,
+# with B stored [k][n] and [n][k]
+@pytest.mark.parametrize("knobs", [
+    {"RV_GEMM_W4_STAGES": "4", "RV_GEMM_W4_SPLIT": "8"},
+    {"RV_GEMM_W4_SPLIT": "0"},
+    {"RV_GEMM_W4_PIN": "0"},
+    {"RV_GEMM_W4_PIN": "2"},
+    {"RV_GEMM_KERNEL": "lds"},
+    {"RV_GEMM_KERNEL": "lds4"},
+    {"RV_GEMM_KERNEL": "pp"},
+    {"RV_GEMM_KERNEL": "reg"},
+])
+def test_gemm_kernel_variants_bit_exact(monkeypatch, knobs):
+    m, n, k = 512, 256, 448
+    _case(f"gemm variant {knobs} {m}x{n}x{k}")
+    for key, val in knobs.items():
+        monkeypatch.setenv(key, val)
+    inp = synth.inputs_gemm_integer(m, n, k)
+    spec = synth.gemm_bf16(m, n, k)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+    inp = {"A": inp["A"], "Bt": np.ascontiguousarray(inp["B"].T)}
+    spec = synth.gemm_bf16_bt(m, n, k)
+    got, = run(_prog(spec), inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
 @pytest.mark.parametrize("m,n,k", [(256, 256, 256), (512, 384, 640), (512, 768, 320)])
 def test_gemm_relu2_sum(m, n, k):
     _case(f"gemm relu2 sum {m}x{n}x{k}")
