@@ -986,10 +986,11 @@ __device__ __forceinline__ void rv_g5_frags(rv_bf16x8 (&af)[4], rv_bf16x8 (&bf)[
     }
 }
 
-// Global -> LDS copy of one 32-deep k-tile by 4 waves (4 + 4 instructions of
-// 1 KB per wave; this call issues those numbered [C0, C1), A's first). The row part of each address is a wave-uniform base; the
-// lane part (row within 16 A rows or 2 B k-rows, swizzled chunk) is a loop
-// invariant 32-bit offset, so the copies take the scalar-base form.
+// Global -> LDS copy of one 32-deep k-tile by 4 waves: 4 + 4 instructions of
+// 1 KB per wave, of which this call issues those numbered [C0, C1), A's
+// first. The row part of each address is a wave-uniform base; the lane part
+// (row within 16 A rows or 2 B k-rows, swizzled chunk) is a loop-invariant
+// 32-bit offset, so the copies take the scalar-base form.
 template <bool B_KN, int C0, int C1>
 __device__ __forceinline__ void rv_g5_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
                                            const unsigned short* __restrict__ B, long long a_base, long long lda,
