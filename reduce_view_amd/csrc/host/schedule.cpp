@@ -478,7 +478,8 @@ static bool try_reduce_cells(Ctx& c, int root, Kernel& k) {
 // ---- MFMA ----------------------------------------------------------------
 
 // Strips CASTs to f32 and returns the leaf-producing node (a bf16 BUFFER, or
-// a VIEW of one) under a f32 CAST, or -1.
+// a chain of VIEWs over one or over a value in memory, which the builder
+// composes into one View) under a f32 CAST, or -1.
 static int bf16_operand(Ctx& c, int i) {
     const Node& nd = c.g.nodes[i];
     if (nd.op != RV_CAST || nd.dtype != RV_F32 || c.mat[i]) return -1;
@@ -486,7 +487,11 @@ static int bf16_operand(Ctx& c, int i) {
     const Node& sn = c.g.nodes[s];
     if (sn.dtype != RV_BF16) return -1;
     if (sn.op == RV_BUFFER) return s;
-    if (sn.op == RV_VIEW && !c.mat[s] && (c.g.nodes[sn.src[0]].op == RV_BUFFER || c.mat[sn.src[0]])) return s;
+    for (int v = s; c.g.nodes[v].op == RV_VIEW && !c.mat[v];) {
+        const int src = c.g.nodes[v].src[0];
+        if (c.g.nodes[src].op == RV_BUFFER || c.mat[src]) return s;
+        v = src;
+    }
     return -1;
 }
 

@@ -282,18 +282,34 @@ def nodes_from_spec(spec):
                     v.mask_hi[d] = r["mask_hi"][d]
                 v.offset = r["offset"]
             else:
-                v = rv_view_contiguous(src_shape)
-                for name, a in nd["movement"]:
-                    if name == "reshape":
-                        v = rv_view_reshape(v, a)
-                    elif name == "permute":
-                        v = rv_view_permute(v, a)
-                    elif name == "expand":
-                        v = rv_view_expand(v, a)
-                    elif name == "pad":
-                        v = rv_view_pad(v, [w[0] for w in a], [w[1] for w in a])
-                    elif name == "shrink":
-                        v = rv_view_shrink(v, [w[0] for w in a], [w[1] for w in a])
+                def moved(v):
+                    for name, a in nd["movement"]:
+                        if name == "reshape":
+                            v = rv_view_reshape(v, a)
+                        elif name == "permute":
+                            v = rv_view_permute(v, a)
+                        elif name == "expand":
+                            v = rv_view_expand(v, a)
+                        elif name == "pad":
+                            v = rv_view_pad(v, [w[0] for w in a], [w[1] for w in a])
+                        elif name == "shrink":
+                            v = rv_view_shrink(v, [w[0] for w in a], [w[1] for w in a])
+                    return v
+                v = None
+                s0 = nd["src"][0]
+                if arr[s0].op == OP["VIEW"]:
+                    # a View of a View: the movements applied to the inner
+                    # View give one View of the inner's source, when they
+                    # compose (else the inner value stays a node of its own)
+                    try:
+                        v = moved(rv_view.from_buffer_copy(arr[s0].view))
+                        x.src[0] = arr[s0].src[0]
+                    except RVError as e:
+                        if e.name != "RV_E_UNSUPPORTED_LAYOUT":
+                            raise
+                        v = None
+                if v is None:
+                    v = moved(rv_view_contiguous(src_shape))
             x.view = v
         elif op in ("GATHER", "SCATTER"):
             x.reduce_axes = 1 << int(nd["axis"])

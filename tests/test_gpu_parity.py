@@ -209,6 +209,38 @@ def test_gemm_integer_valued_bit_exact(m, n, k):
     assert got.tobytes() == ref.tobytes()
 
 
+def _gemm_strided(m, n, k, pa, pb, oa, ob):
+    """A and B as windows of wider buffers: A rows of pitch k + pa starting
+    at column oa, B rows of pitch n + pb starting at column ob."""
+    g = synth.Spec(f"gemm_strided_{m}x{n}x{k}")
+    a = g.buffer("A", (m, k + pa), "bf16")
+    b = g.buffer("B", (k, n + pb), "bf16")
+    aw = g.view(a, ("shrink", ((0, m), (oa, oa + k))))
+    bw = g.view(b, ("shrink", ((0, k), (ob, ob + n))))
+    a3 = g.cast(g.view(aw, ("reshape", (m, 1, k)), ("expand", (m, n, k))), "f32")
+    b3 = g.cast(g.view(bw, ("permute", (1, 0)), ("reshape", (1, n, k)), ("expand", (m, n, k))), "f32")
+    g.output(g.sum(g.mul(a3, b3), (2,)))
+    return g
+
+
+# operand windows with row pitches wider than the rows and nonzero offsets:
+# the copy addresses' row pitch and base offsets are the View's, not k or n
+@pytest.mark.parametrize("m,n,k,pa,pb,oa,ob", [(256, 256, 192, 64, 256, 8, 16), (512, 512, 320, 8, 24, 0, 8),
+                                               (256, 512, 64, 1000, 8, 992, 0)])
+def test_gemm_operand_windows_bit_exact(m, n, k, pa, pb, oa, ob):
+    _case(f"gemm windows {m}x{n}x{k} pitches +{pa} +{pb} offsets {oa} {ob}")
+    spec = _gemm_strided(m, n, k, pa, pb, oa, ob)
+    prog = _prog(spec)
+    kd = prog.describe()["kernels"][0]
+    assert kd["class"] == "MFMA" and kd["plan"] == "gemm_w4"
+    rng = np.random.default_rng(17)
+    inp = {"A": synth.to_bf16_bits(rng.integers(-2, 3, (m, k + pa)).astype(np.float32)),
+           "B": synth.to_bf16_bits(rng.integers(-2, 3, (k, n + pb)).astype(np.float32))}
+    got, = run(prog, inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
 # the contraction kernels and pipeline settings the plan's environment knobs
 # select (the default is the four-wave kernel, five stages, 2 early copies,
 # pinned interleaving): every one stays bit-exact on integer-valued operands,

@@ -66,6 +66,9 @@ CLASSES = {
     "gemm": (lambda: synth.gemm_relu2_sum(128, 128, 64), lambda: synth.inputs_gemm(128, 128, 64),
              ["MFMA", "FOLD"]),
     "gemm_y": (lambda: synth.gemm_bf16(128, 256, 128), lambda: synth.inputs_gemm(128, 256, 128), ["MFMA"]),
+    # operands as windows of wider buffers, each a View of a View: the two
+    # compose into one View of the buffer, so nothing is copied first
+    "gemm_windows": (lambda: _gemm_windows(), lambda: _gemm_windows_inputs(), ["MFMA"]),
     "gather": (lambda: synth.embedding_gather(50, 6, 30), lambda: synth.inputs_embedding(50, 6, 30), ["EW"]),
     "gather_general": (lambda: _gather_general(), lambda: _indexed_inputs(), ["EW", "EW"]),
     "scatter": (lambda: synth.embedding_scatter(20, 6, 100), lambda: synth.inputs_embedding(20, 6, 100),
@@ -105,6 +108,24 @@ def _scatter_general():
     v = g.buffer("V", (4, 7, 5), "f32")
     g.output(g.scatter(g.exp(d), i, g.mul(v, v), 1))
     return g
+
+
+def _gemm_windows():
+    g = synth.Spec("gemm_windows")
+    a = g.buffer("A", (128, 96), "bf16")
+    b = g.buffer("B", (64, 160), "bf16")
+    aw = g.view(a, ("shrink", ((0, 128), (16, 80))))
+    bw = g.view(b, ("shrink", ((0, 64), (8, 136))))
+    a3 = g.cast(g.view(aw, ("reshape", (128, 1, 64)), ("expand", (128, 128, 64))), "f32")
+    b3 = g.cast(g.view(bw, ("permute", (1, 0)), ("reshape", (1, 128, 64)), ("expand", (128, 128, 64))), "f32")
+    g.output(g.sum(g.mul(a3, b3), (2,)))
+    return g
+
+
+def _gemm_windows_inputs():
+    rng = np.random.default_rng(23)
+    return {"A": synth.to_bf16_bits(rng.integers(-2, 3, (128, 96)).astype(np.float32)),
+            "B": synth.to_bf16_bits(rng.integers(-2, 3, (64, 160)).astype(np.float32))}
 
 
 @pytest.mark.parametrize("name", list(CLASSES))
