@@ -90,5 +90,9 @@ bool view_is_contiguous(const rv_view& v);              // row-major, offset 0, 
 // Returns false when no cell is in the mask.
 bool view_addr_range(const rv_view& v, int64_t* lo, int64_t* hi);
 Shape view_shape(const rv_view& v);
+// A View `outer` over the row-major cells of the View `inner`, as one View
+// of inner's source; false when no single View expresses it (a carry across
+// an inner dim, or one inner mask reached by several outer dims)
+bool view_compose(const rv_view& inner, const rv_view& outer, rv_view* out);
 
 }  // namespace rv

@@ -767,6 +767,20 @@ bool ex_invariant(const Kernel& k, int e, int d) {
 void schedule(Program& p) {
     Graph& g = p.g;
     const int n = (int)g.nodes.size();
+    // a View of a View reads the inner View's source directly when the two
+    // compose into one View (nodes are in order, so chains collapse whole);
+    // otherwise the inner value is materialised below
+    for (int i = 0; i < n; ++i) {
+        Node& nd = g.nodes[i];
+        if (nd.op != RV_VIEW) continue;
+        const Node& s = g.nodes[nd.src[0]];
+        if (s.op != RV_VIEW) continue;
+        rv_view c;
+        if (view_compose(s.view, nd.view, &c)) {
+            nd.src[0] = s.src[0];
+            nd.view = c;
+        }
+    }
     Ctx c{p, g, std::vector<char>(n, 0), std::vector<std::vector<Loc>>(n)};
     for (int i = 0; i < n; ++i)
         if (g.nodes[i].op == RV_BUFFER) {

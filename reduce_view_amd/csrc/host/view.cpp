@@ -76,6 +76,95 @@ bool view_addr_range(const rv_view& v, int64_t* lo, int64_t* hi) {
     return true;
 }
 
+// The outer View addresses cells of inner's shape by their row-major index.
+// Starting from the lowest unmasked outer cell (index base, inner cell j0),
+// each outer dim with more than one unmasked step must move exactly one inner
+// dim by a whole multiple of that dim's pitch, and the inner dim must not
+// carry over its size anywhere in the unmasked range; then every inner index
+// is affine in the outer one and the composition is one View. An inner mask
+// becomes a range on the one outer dim that moves that inner dim (or, with
+// none moving it, either no constraint or an empty View).
+bool view_compose(const rv_view& inner, const rv_view& outer, rv_view* out) {
+    view_check(inner);
+    view_check(outer);
+    const int ni = inner.ndim, no = outer.ndim;
+    rv_view r = outer;
+    if (view_empty_mask(outer)) {  // nothing is read: any source address will do
+        for (int d = 0; d < no; ++d) r.strides[d] = 0;
+        r.offset = inner.offset;
+        *out = r;
+        return true;
+    }
+    int64_t pitch[RV_MAX_DIMS], total = 1;
+    for (int e = ni - 1; e >= 0; --e) {
+        pitch[e] = total;
+        total = mul_checked(total, inner.shape[e]);
+    }
+    int64_t base = outer.offset;
+    for (int d = 0; d < no; ++d) base = add_checked(base, mul_checked(outer.mask_lo[d], outer.strides[d]));
+    if (base < 0 || base >= total) return false;
+    int64_t j0[RV_MAX_DIMS], rem = base;
+    for (int e = 0; e < ni; ++e) {
+        j0[e] = rem / pitch[e];
+        rem %= pitch[e];
+    }
+    int map[RV_MAX_DIMS];
+    int64_t coef[RV_MAX_DIMS], span[RV_MAX_DIMS];
+    int movers[RV_MAX_DIMS];
+    for (int e = 0; e < ni; ++e) span[e] = j0[e], movers[e] = 0;
+    for (int d = 0; d < no; ++d) {
+        map[d] = -1;
+        coef[d] = 0;
+        const int64_t steps = outer.mask_hi[d] - outer.mask_lo[d];
+        if (steps <= 1 || outer.strides[d] == 0) continue;
+        int e = -1;
+        for (int x = ni - 1; x >= 0; --x)
+            if (inner.shape[x] > 1 && outer.strides[d] % pitch[x] == 0 && outer.strides[d] / pitch[x] < inner.shape[x]) {
+                e = x;
+                break;
+            }
+        if (e < 0) return false;
+        map[d] = e;
+        coef[d] = outer.strides[d] / pitch[e];
+        span[e] = add_checked(span[e], mul_checked(coef[d], steps - 1));
+        ++movers[e];
+    }
+    for (int e = 0; e < ni; ++e)
+        if (span[e] >= inner.shape[e]) return false;  // a carry: not affine
+    int64_t off = inner.offset;
+    for (int e = 0; e < ni; ++e) off = add_checked(off, mul_checked(j0[e], inner.strides[e]));
+    for (int d = 0; d < no; ++d) {
+        r.strides[d] = map[d] < 0 ? 0 : mul_checked(coef[d], inner.strides[map[d]]);
+        off = add_checked(off, -mul_checked(outer.mask_lo[d], r.strides[d]));
+    }
+    r.offset = off;
+    bool empty = false;
+    for (int e = 0; e < ni; ++e) {
+        const int64_t lo = inner.mask_lo[e], hi = inner.mask_hi[e];
+        if (lo == 0 && hi == inner.shape[e]) continue;
+        if (movers[e] == 0) {
+            if (j0[e] < lo || j0[e] >= hi) empty = true;
+            continue;
+        }
+        if (movers[e] > 1) return false;
+        int d = 0;
+        while (map[d] != e) ++d;
+        // lo <= j0 + c (i - mlo) < hi  <=>  i in [mlo + ceil((lo - j0) / c), mlo + ceil((hi - j0) / c))
+        const int64_t c = coef[d], m0 = outer.mask_lo[d];
+        auto ceil_div = [](int64_t a, int64_t b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); };
+        const int64_t a = m0 + ceil_div(lo - j0[e], c), b = m0 + ceil_div(hi - j0[e], c);
+        r.mask_lo[d] = std::max(r.mask_lo[d], std::min(a, r.shape[d]));
+        r.mask_hi[d] = std::min(r.mask_hi[d], std::max(b, (int64_t)0));
+        if (r.mask_hi[d] < r.mask_lo[d]) r.mask_hi[d] = r.mask_lo[d];
+    }
+    if (empty) {
+        if (no == 0) return false;
+        r.mask_lo[0] = r.mask_hi[0] = 0;
+    }
+    *out = r;
+    return true;
+}
+
 rv_view view_contiguous(const Shape& shape, int64_t offset) {
     if (shape.size() > RV_MAX_DIMS) fail(RV_E_INVALID, fmt("rank %zu > 8", shape.size()));
     rv_view v{};

@@ -302,3 +302,75 @@ def test_contraction_plans():
     f16 = rv.compile_spec(synth.rmsnorm(64, 4096, dtype="f16")).describe()["kernels"][0]
     f32 = rv.compile_spec(synth.rmsnorm(64, 4096)).describe()["kernels"][0]
     assert f16["plan_detail"]["threads_per_row"] == 128 and f32["plan_detail"]["threads_per_row"] == 256
+
+
+def _random_view(rng, shape):
+    """A View over row-major `shape` from 1-4 random movements (the
+    library's own View algebra), as raw (shape, strides, offset, mask)."""
+    v = rv.rv_view_contiguous(shape)
+    for _ in range(int(rng.integers(1, 5))):
+        cur = [v.shape[d] for d in range(v.ndim)]
+        kind = rng.choice(["permute", "shrink", "pad", "expand", "reshape"])
+        try:
+            if kind == "permute":
+                v = rv.rv_view_permute(v, list(rng.permutation(len(cur))))
+            elif kind == "shrink":
+                lo = [int(rng.integers(0, max(1, c // 2))) for c in cur]
+                hi = [int(rng.integers(l + 1, c + 1)) if c > l else c for l, c in zip(lo, cur)]
+                v = rv.rv_view_shrink(v, lo, hi)
+            elif kind == "pad":
+                v = rv.rv_view_pad(v, [int(rng.integers(0, 3)) for _ in cur], [int(rng.integers(0, 3)) for _ in cur])
+            elif kind == "expand":
+                ones = [d for d, c in enumerate(cur) if c == 1]
+                if ones:
+                    new = list(cur)
+                    new[ones[0]] = int(rng.integers(2, 4))
+                    v = rv.rv_view_expand(v, new)
+            else:
+                n = int(np.prod(cur))
+                for cand in ([n], [1] + cur, cur + [1], [cur[0] * cur[1]] + cur[2:] if len(cur) > 1 else cur):
+                    try:
+                        v = rv.rv_view_reshape(v, cand)
+                        break
+                    except rv.RVError:
+                        continue
+        except rv.RVError:
+            pass
+    d = v.to_dict()
+    return d
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_view_of_view_composes_exactly(seed):
+    """Random raw Views of random raw Views over one buffer (movement only):
+    the scheduler composes each pair into one View of the buffer where a
+    single View expresses it, else materialises the inner value; either way
+    the planned kernels reproduce the oracle bit for bit."""
+    rng = np.random.default_rng(seed)
+    shape = [int(x) for x in rng.integers(1, 7, int(rng.integers(1, 4)))]
+    inner = _random_view(rng, shape)
+    outer = _random_view(rng, list(inner["shape"]))
+    g = synth.Spec(f"view_of_view_{seed}")
+    x = g.buffer("X", tuple(shape), "f32")
+    a = g.raw_view(x, inner["shape"], inner["strides"], inner["offset"], inner["mask_lo"], inner["mask_hi"])
+    b = g.raw_view(a, outer["shape"], outer["strides"], outer["offset"], outer["mask_lo"], outer["mask_hi"])
+    g.output(g.contiguous(b))
+    inp = {"X": rng.standard_normal(shape).astype(np.float32) + 3.0}
+    d, got = _interp(g, inp)
+    ref = oracle.run(g, inp)
+    assert got[0].tobytes() == ref[0].tobytes()
+    assert len(d["kernels"]) in (1, 2)
+
+
+def test_view_of_view_window_is_one_kernel():
+    """A column window of a permuted buffer, then a broadcast of it: one View
+    of the buffer, one kernel."""
+    g = synth.Spec("window")
+    x = g.buffer("X", (6, 10), "f32")
+    a = g.raw_view(x, (10, 6), (1, 10), 0)                   # permute
+    b = g.raw_view(a, (4, 2, 6), (6, 0, 1), 12, None, None)  # rows 2..5, a broadcast dim
+    g.output(g.contiguous(b))
+    inp = {"X": np.arange(60, dtype=np.float32).reshape(6, 10)}
+    d, got = _interp(g, inp)
+    assert len(d["kernels"]) == 1
+    assert got[0].tobytes() == oracle.run(g, inp)[0].tobytes()
