@@ -405,7 +405,16 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
             int WY = env_int("RV_EW_WAVES_Y", 1);
             if (WY != 1 && WY != 2 && WY != 4) fail(RV_E_INVALID, "RV_EW_WAVES_Y must be 1, 2 or 4");
             int WX = 4 / WY;
-            int order = env_int("RV_EW_ORDER", 0);
+            // tile order: x-major, or diagonal when every streamed operand is
+            // read transposed (a pure transpose: consecutive workgroups then
+            // read different source columns instead of the same ones, 2.6%
+            // faster on 4096^2; the chains with a row-major operand are not)
+            bool all_t = true;
+            for (auto& L : k.leaves)
+                if (!L.zero && (L.v.strides[X] != 0 || L.v.strides[Y] != 0) &&
+                    !(L.v.strides[Y] == 1 && L.v.strides[X] != 1))
+                    all_t = false;
+            int order = env_int("RV_EW_ORDER", all_t ? 2 : 0);
             int64_t B = numel(k.domain) / (k.domain[X] * k.domain[Y]);
             int64_t gx = (k.domain[X] + 32 * WX - 1) / (32 * WX), gy = (k.domain[Y] + 32 * WY - 1) / (32 * WY);
             k.grid[0] = (unsigned)(gx * gy);
