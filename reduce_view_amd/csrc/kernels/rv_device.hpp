@@ -1367,8 +1367,9 @@ __device__ __forceinline__ void rv_gemm_pp_bf16(const unsigned short* __restrict
 // B operand of the second product as they stand. The key order the result
 // layout leaves in a lane (keys 4 h .. 4 h + 3 and 8 + 4 h .. of each 16,
 // h = lane / 32) is matched by reading V^T from LDS in that order.
-// Scores are carried in base 2: the running maximum is max(s) * scale *
-// log2 e, and each exponential is v_exp_f32 of one fma.
+// Scores are carried in base 2: the reference m follows the running maximum
+// of s * scale * log2 e (moved only when a score passes it by more than 8),
+// and each exponential is v_exp_f32 of one fma.
 //
 // Workgroup: NG groups of 4 waves (NG = 2; 4 measured no faster). Waves
 // w, w + 4, .. own the same 32 queries and split the keys: 64-key steps go
@@ -1548,11 +1549,28 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
             for (int r = 1; r < 32; ++r) cm = fmaxf(cm, sv[r]);
             cm = rv_pair_max(cm);
             // max(s) * c equals max(s * c) for c > 0 (rounding is monotonic)
-            const float mn = fmaxf(m, cm * sl2);
-            const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
-            // while every key seen is hidden (mn = -inf) every score is -inf
+            const float cm2 = cm * sl2;
+            // The reference m moves only when a score passes it by more than
+            // 8 (base 2): below that the probabilities stay under 2^8, which
+            // float32 sums and the bf16 operand carry with the same relative
+            // rounding, and O / l and m + log2 l do not depend on which m was
+            // used. So the rescale (an exponential and a multiply per
+            // accumulator) runs only on the rare steps that move m; the first
+            // step with a visible key always does (m = -inf).
+            const bool grow = cm2 > m + 8.0f;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
+                const float mn = grow ? cm2 : m;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;  // exp2(-inf) = 0
+                l = l * alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+                m = mn;
+            }
+            // while every key seen is hidden (m = -inf) every score is -inf
             // and exp2(-inf - 0) = 0: no branch, no separate zero fill
-            const float mns = mn == ninf ? 0.0f : mn;
+            const float mns = m == ninf ? 0.0f : m;
             float pr[32];
             float ps = 0.0f;
 #pragma unroll
@@ -1561,16 +1579,7 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
                 ps = ps + pr[r];
             }
             ps = rv_pair_sum(ps);
-            l = l * alpha + ps;
-            m = mn;
-            // multiplying by 1 changes nothing: skip the rescale when no lane's
-            // maximum grew (most steps of a long row)
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-            }
+            l = l + ps;
             // O^T += V^T P^T over the 64 keys (four k16 steps)
             // P to bf16 two at a time (one v_cvt_pk_bf16_f32 per pair)
             rv_bf16x8 pb[4];
