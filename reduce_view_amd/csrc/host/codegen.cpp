@@ -1571,6 +1571,43 @@ std::string Gen::gen_scatter() {
         b << "  rv_rs_scan(" << ureg(k.sc_reg_counts, true) << ", " << NB << "u);\n";
         return b.str();
     }
+    std::vector<int> idims;  // the dims a key walks besides the axis
+    int64_t PI = 1;
+    for (int d : cd)
+        if (d != A) {
+            idims.push_back(d);
+            PI *= k.domain[d];
+        }
+    // the keys: target index t times the index-cell count plus the cell's
+    // linear position over the index dims; an index outside the axis gets
+    // the last key and its cell id flagged (bit 31) so the fold adds nothing
+    auto emit_key = [&](const std::string& ind, const std::string& kout, const std::string& vout) {
+        decompose("c", cd, "i", ind);
+        std::vector<std::string> idx(rank, "0");
+        for (int d : cd) idx[d] = fmt("i%d", d);
+        std::vector<char> done(k.ex.size(), 0);
+        scalar(b, k.sc_index, idx, ind, "", done);
+        std::string lin = "0LL";
+        int64_t m = 1;
+        for (size_t j2 = idims.size(); j2-- > 0;) {
+            lin += fmt(" + i%d * %lldLL", idims[j2], (long long)m);
+            m *= k.domain[idims[j2]];
+        }
+        b << ind << "const int t = s" << k.sc_index << ";\n";
+        b << ind << "const bool in = t >= 0 && t < " << osh[A] << ";\n";
+        b << ind << kout << " = in ? (unsigned)((long long)t * " << PI << "LL + " << lin << ") : " << KN - 1
+          << "u;\n";
+        b << ind << vout << " = (unsigned)c | (in ? 0u : 0x80000000u);\n";
+    };
+    if (part == "move" && k.sc_fused_keys) {
+        b << "  auto kf = [&](long long c, unsigned& key_, unsigned& val_) {\n";
+        emit_key("    ", "key_", "val_");
+        b << "  };\n";
+        b << "  rv_rs_move_kv<true>(rv_rs_fn<decltype(kf)>{kf}, " << ureg(k.sc_reg_keys[nxt], true) << ", "
+          << ureg(k.sc_reg_vals[nxt], true) << ", nullptr, " << CELLS << "LL, " << NB << "u, " << 8 * k.sc_pass
+          << ");\n";
+        return b.str();
+    }
     if (part == "move") {
         const bool self = NB <= kScanInline;
         b << "  rv_rs_move<" << (self ? "true" : "false") << ">(" << ureg(k.sc_reg_keys[cur], false) << ", "
@@ -1628,34 +1665,10 @@ std::string Gen::gen_scatter() {
         b << "  }\n";
         return b.str();
     }
-    std::vector<int> idims;  // the dims a key walks besides the axis
-    int64_t PI = 1;
-    for (int d : cd)
-        if (d != A) {
-            idims.push_back(d);
-            PI *= k.domain[d];
-        }
     if (part == "keys") {
-        // an index outside the axis: the last key, and the cell id flagged
-        // (bit 31) so that the fold adds nothing for it
         b << "  for (long long c = (long long)blockIdx.x * 256 + threadIdx.x; c < " << CELLS
           << "LL; c += (long long)gridDim.x * 256) {\n";
-        decompose("c", cd, "i", "    ");
-        std::vector<std::string> idx(rank, "0");
-        for (int d : cd) idx[d] = fmt("i%d", d);
-        std::vector<char> done(k.ex.size(), 0);
-        scalar(b, k.sc_index, idx, "    ", "", done);
-        std::string lin = "0LL";
-        int64_t m = 1;
-        for (size_t j2 = idims.size(); j2-- > 0;) {
-            lin += fmt(" + i%d * %lldLL", idims[j2], (long long)m);
-            m *= k.domain[idims[j2]];
-        }
-        b << "    const int t = s" << k.sc_index << ";\n";
-        b << "    const bool in = t >= 0 && t < " << osh[A] << ";\n";
-        b << "    " << ureg(k.sc_reg_keys[0], true) << "[c] = in ? (unsigned)((long long)t * " << PI << "LL + " << lin
-          << ") : " << KN - 1 << "u;\n";
-        b << "    " << ureg(k.sc_reg_vals[0], true) << "[c] = (unsigned)c | (in ? 0u : 0x80000000u);\n";
+        emit_key("    ", ureg(k.sc_reg_keys[0], true) + "[c]", ureg(k.sc_reg_vals[0], true) + "[c]");
         b << "  }\n";
         return b.str();
     }

@@ -160,6 +160,7 @@ struct Kernel {
     int64_t sc_cells = 0;       // index cells (positions with the carried dims at 0)
     int64_t sc_keys_n = 0;      // valid keys: out extent along the axis x varying dims
     int sc_pass = 0, sc_passes = 0;
+    bool sc_fused_keys = false;  // first move computes the keys from the index (no keys kernel)
     int sc_reg_keys[2] = {-1, -1}, sc_reg_vals[2] = {-1, -1};
     int sc_reg_counts = -1;  // per-tile digit counts (more than kScanInline tiles)
     int sc_reg_bounds = -1;  // first sorted position of every key, and of key sc_keys_n

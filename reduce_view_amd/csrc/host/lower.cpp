@@ -370,6 +370,7 @@ static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
                      k.sc_pass, (long long)nb, nb <= kScanInline ? "true" : "false", tps, R, (long long)kpb,
                      k.sc_part == "atomic" ? "false" : "true");
             k.plan_json = buf;
+            if (k.sc_part == "move") k.plan_json += k.sc_fused_keys ? ",\"keys_from_index\":true" : "";
             return;
         }
         default: break;

@@ -708,16 +708,26 @@ static bool scatter_kernels(Ctx& c, int i, std::vector<Kernel>& out, std::vector
             if (nb > kScanInline) k.sc_reg_counts = region((256 * nb + 256) * 4);
             k.sc_reg_bounds = region((keys + 1) * 4);
             k.sc_passes = passes;
-            Kernel kk = k;
-            kk.sc_part = "keys";
-            ks.push_back(kk);
+            // with the digit counts done inside the moves (few tiles), the
+            // first move computes its keys from the index itself
+            const bool fuse = nb <= kScanInline;
+            if (!fuse) {
+                Kernel kk = k;
+                kk.sc_part = "keys";
+                ks.push_back(kk);
+            }
             for (int q = 0; q < passes; ++q)
                 for (const char* part : {"hist", "scan", "move"}) {
                     if (std::string(part) != "move" && nb <= kScanInline) continue;
                     Kernel r = k;
-                    r.leaves.clear();
-                    r.ex.clear();
-                    r.sc_index = r.sc_values = r.sc_base = -1;
+                    if (fuse && q == 0) {
+                        r.sc_values = r.sc_base = -1;
+                        r.sc_fused_keys = true;
+                    } else {
+                        r.leaves.clear();
+                        r.ex.clear();
+                        r.sc_index = r.sc_values = r.sc_base = -1;
+                    }
                     r.sc_part = part;
                     r.sc_pass = q;
                     ks.push_back(r);

@@ -1850,10 +1850,39 @@ __device__ __forceinline__ unsigned rv_scan1024(unsigned v, unsigned* w, unsigne
 // in 2 rounds. SELF (at most 64 tiles): every workgroup counts the digits
 // of every tile in LDS; otherwise `counts` holds the per-tile prefixes and
 // digit totals from rv_rs_hist and rv_rs_scan.
+// (key, value) pairs of a radix pass: from the previous pass's arrays, or
+// (first pass) computed where they are needed from the index by a functor
+// f(j, key, value), so no kernel writes them first
+struct rv_rs_mem {
+    const unsigned* __restrict__ k;
+    const unsigned* __restrict__ v;
+    __device__ __forceinline__ void get(long long j, unsigned& key, unsigned& val) const {
+        key = k[j];
+        val = v[j];
+    }
+};
+template <class F>
+struct rv_rs_fn {
+    F f;
+    __device__ __forceinline__ void get(long long j, unsigned& key, unsigned& val) const { f(j, key, val); }
+};
+
+template <bool SELF, class KV>
+__device__ __forceinline__ void rv_rs_move_kv(const KV& src, unsigned* __restrict__ okeys,
+                                              unsigned* __restrict__ ovals, const unsigned* __restrict__ counts,
+                                              long long n, unsigned nb, int shift);
+
 template <bool SELF>
 __device__ __forceinline__ void rv_rs_move(const unsigned* __restrict__ keys, const unsigned* __restrict__ vals,
                                            unsigned* __restrict__ okeys, unsigned* __restrict__ ovals,
                                            const unsigned* __restrict__ counts, long long n, unsigned nb, int shift) {
+    rv_rs_move_kv<SELF>(rv_rs_mem{keys, vals}, okeys, ovals, counts, n, nb, shift);
+}
+
+template <bool SELF, class KV>
+__device__ __forceinline__ void rv_rs_move_kv(const KV& src, unsigned* __restrict__ okeys,
+                                              unsigned* __restrict__ ovals, const unsigned* __restrict__ counts,
+                                              long long n, unsigned nb, int shift) {
     __shared__ unsigned run[256];
     __shared__ unsigned wc[16][256];
     __shared__ unsigned w[16];
@@ -1869,7 +1898,11 @@ __device__ __forceinline__ void rv_rs_move(const unsigned* __restrict__ keys, co
         for (long long j0 = t; j0 < n; j0 += 1024 * 32) {
             unsigned kv[32];
 #pragma unroll
-            for (int u = 0; u < 32; ++u) kv[u] = j0 + u * 1024 < n ? keys[j0 + u * 1024] : 0u;
+            for (int u = 0; u < 32; ++u) {
+                unsigned vv;
+                kv[u] = 0u;
+                if (j0 + u * 1024 < n) src.get(j0 + u * 1024, kv[u], vv);
+            }
 #pragma unroll
             for (int u = 0; u < 32; ++u)
                 if (j0 + u * 1024 < n)
@@ -1901,8 +1934,8 @@ __device__ __forceinline__ void rv_rs_move(const unsigned* __restrict__ keys, co
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const long long j = (long long)blockIdx.x * RV_RS_TILE + r * 1024 + t;
-        rk[r] = j < n ? keys[j] : 0u;
-        rvv[r] = j < n ? vals[j] : 0u;
+        rk[r] = rvv[r] = 0u;
+        if (j < n) src.get(j, rk[r], rvv[r]);
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {

@@ -72,10 +72,10 @@ CLASSES = {
     "gather": (lambda: synth.embedding_gather(50, 6, 30), lambda: synth.inputs_embedding(50, 6, 30), ["EW"]),
     "gather_general": (lambda: _gather_general(), lambda: _indexed_inputs(), ["EW", "EW"]),
     "scatter": (lambda: synth.embedding_scatter(20, 6, 100), lambda: synth.inputs_embedding(20, 6, 100),
-                ["SCATTER"] * 4),
+                ["SCATTER"] * 3),
     "scatter_atomic": (lambda: synth.embedding_scatter(20, 6, 100, atomic=True),
                        lambda: synth.inputs_embedding(20, 6, 100), ["EW", "SCATTER"]),
-    "scatter_general": (lambda: _scatter_general(), lambda: _indexed_inputs(), ["SCATTER"] * 4),
+    "scatter_general": (lambda: _scatter_general(), lambda: _indexed_inputs(), ["SCATTER"] * 3),
 }
 
 
