@@ -374,3 +374,62 @@ def test_view_of_view_window_is_one_kernel():
     d, got = _interp(g, inp)
     assert len(d["kernels"]) == 1
     assert got[0].tobytes() == oracle.run(g, inp)[0].tobytes()
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_graphs_plan_matches_oracle(seed):
+    """Random small regions: two or three buffers read directly, transposed,
+    as a broadcast row, or through a shrunk window of a larger buffer; a
+    random mix of ADD / MUL / NEG / CMPLT / WHERE; then nothing, a SUM or MAX
+    over one axis, or a row reduce expanded back and combined with the
+    region (a ROW chain). Integer-valued float32 inputs make every order of
+    additions give the same bits, so the planned kernels (through the CPU
+    plan interpreter) must reproduce the oracle exactly."""
+    rng = np.random.default_rng(1000 + seed)
+    rank = 2 if rng.random() < 0.6 else 3
+    shape = tuple(int(x) for x in rng.integers(8, 21, rank))
+    g = synth.Spec(f"random_{seed}")
+    inputs, vals = {}, []
+    for b in range(int(rng.integers(2, 4))):
+        name = f"B{b}"
+        mode = ["direct", "transposed", "row", "window"][int(rng.integers(0, 4))]
+        if mode == "direct":
+            bshape = shape
+            v = g.buffer(name, bshape, "f32")
+        elif mode == "transposed":
+            bshape = shape[::-1]
+            v = g.view(g.buffer(name, bshape, "f32"), ("permute", tuple(range(rank))[::-1]))
+        elif mode == "row":
+            bshape = (shape[-1],)
+            v = g.view(g.buffer(name, bshape, "f32"), ("reshape", (1,) * (rank - 1) + (shape[-1],)), ("expand", shape))
+        else:
+            bshape = tuple(d + 3 for d in shape)
+            lo = tuple(int(rng.integers(0, 4)) for _ in shape)
+            v = g.view(g.buffer(name, bshape, "f32"), ("shrink", tuple((l, l + d) for l, d in zip(lo, shape))))
+            if rng.random() < 0.5:  # and pad one side back with zeros
+                pad = tuple((1, 0) if dd == 0 else (0, 0) for dd in range(rank))
+                v = g.view(v, ("pad", pad), ("shrink", tuple((0, d) for d in shape)))
+        inputs[name] = rng.integers(-3, 4, bshape).astype(np.float32)
+        vals.append(v)
+    x = vals[0]
+    for v in vals[1:]:
+        op = rng.choice(["add", "mul", "where"])
+        if op == "add":
+            x = g.add(x, v)
+        elif op == "mul":
+            x = g.mul(x, v)
+        else:
+            x = g.where(g.cmplt(x, v), x, g.neg(v))
+    tail = rng.choice(["none", "reduce", "row"])
+    if tail == "reduce":
+        ax = int(rng.integers(0, rank))
+        x = g.sum(x, (ax,)) if rng.random() < 0.5 else g.max(x, (ax,))
+    elif tail == "row":
+        r = g.max(x, (rank - 1,)) if rng.random() < 0.5 else g.sum(x, (rank - 1,))
+        x = g.add(x, g.neg(g.view(r, ("expand", shape))))
+        if rng.random() < 0.5:
+            x = g.sum(g.mul(x, x), (rank - 1,))
+    g.output(x)
+    d, got = _interp(g, inputs)
+    ref = oracle.run(g, inputs)
+    assert got[0].tobytes() == ref[0].tobytes()
