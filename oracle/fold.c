@@ -80,7 +80,8 @@ void fold_max_f32(const float* x, int64_t cells, int64_t n, float* out) {
         for (int64_t i = 0; i < n; ++i) {
             float v = row[i];
             if (isnan(acc)) break;
-            if (isnan(v) || v > acc) acc = v;
+            /* -0 orders below +0, so the result does not depend on the order */
+            if (isnan(v) || v > acc || (v == acc && signbit(acc) && !signbit(v))) acc = v;
         }
         out[c] = acc;
     }
@@ -94,7 +95,8 @@ void fold_max_f64(const double* x, int64_t cells, int64_t n, double* out) {
         for (int64_t i = 0; i < n; ++i) {
             double v = row[i];
             if (isnan(acc)) break;
-            if (isnan(v) || v > acc) acc = v;
+            /* -0 orders below +0, so the result does not depend on the order */
+            if (isnan(v) || v > acc || (v == acc && signbit(acc) && !signbit(v))) acc = v;
         }
         out[c] = acc;
     }

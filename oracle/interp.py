@@ -33,8 +33,9 @@ notes of the repository):
     anything; Litmus README, "Support map and limits", item 7) is kept in
     float64 instead and rounded once.
   * CMPLT produces int8 0/1; WHERE treats any nonzero condition as true.
-  * MAX starts from -inf (ints: the smallest value of the width) and a NaN
-    anywhere in the row gives NaN.
+  * MAX starts from -inf (ints: the smallest value of the width), a NaN
+    anywhere in the row gives NaN, and -0 orders below +0 (IEEE 754-2019
+    maximum), so the result's bits do not depend on the fold order.
   * float -> bfloat16 CAST rounds to nearest even and keeps NaN a NaN;
     float -> int truncates toward zero.
   * GATHER along an axis reads data at the position with that axis

@@ -19,11 +19,13 @@ __device__ __forceinline__ float rv_rbf(float x) { return rv_bf2f(rv_f2bf(x)); }
 __device__ __forceinline__ float rv_rhf(float x) { return (float)(_Float16)x; }
 
 // MAX with NaN propagation (a NaN anywhere makes the result NaN).
+// MAX: a NaN wins, and -0 orders below +0, so a fold gives the same bits in
+// any order
 __device__ __forceinline__ float rv_maxf(float a, float b) {
-    return (a != a) ? a : ((b != b) ? b : (a > b ? a : b));
+    return (a != a) ? a : ((b != b) ? b : (a > b ? a : (b > a ? b : (__builtin_signbit(a) ? b : a))));
 }
 __device__ __forceinline__ double rv_maxd(double a, double b) {
-    return (a != a) ? a : ((b != b) ? b : (a > b ? a : b));
+    return (a != a) ? a : ((b != b) ? b : (a > b ? a : (b > a ? b : (__builtin_signbit(a) ? b : a))));
 }
 
 // ---------------------------------------------------------------------------

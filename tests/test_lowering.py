@@ -376,15 +376,13 @@ def test_view_of_view_window_is_one_kernel():
     assert got[0].tobytes() == oracle.run(g, inp)[0].tobytes()
 
 
-@pytest.mark.parametrize("seed", range(40))
-def test_random_graphs_plan_matches_oracle(seed):
-    """Random small regions: two or three buffers read directly, transposed,
-    as a broadcast row, or through a shrunk window of a larger buffer; a
-    random mix of ADD / MUL / NEG / CMPLT / WHERE; then nothing, a SUM or MAX
-    over one axis, or a row reduce expanded back and combined with the
-    region (a ROW chain). Integer-valued float32 inputs make every order of
-    additions give the same bits, so the planned kernels (through the CPU
-    plan interpreter) must reproduce the oracle exactly."""
+def random_region(seed):
+    """A random small region: two or three buffers read directly,
+    transposed, as a broadcast row, or through a shrunk (and partly padded)
+    window of a larger buffer; a random mix of ADD / MUL / NEG / CMPLT /
+    WHERE; then nothing, a SUM or MAX over one axis, or a row reduce expanded
+    back and combined with the region. Integer-valued float32 inputs make
+    every order of additions give the same bits. Returns (spec, inputs)."""
     rng = np.random.default_rng(1000 + seed)
     rank = 2 if rng.random() < 0.6 else 3
     shape = tuple(int(x) for x in rng.integers(8, 21, rank))
@@ -430,6 +428,14 @@ def test_random_graphs_plan_matches_oracle(seed):
         if rng.random() < 0.5:
             x = g.sum(g.mul(x, x), (rank - 1,))
     g.output(x)
+    return g, inputs
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_graphs_plan_matches_oracle(seed):
+    """Random regions (random_region) planned and run through the CPU plan
+    interpreter reproduce the oracle exactly."""
+    g, inputs = random_region(seed)
     d, got = _interp(g, inputs)
     ref = oracle.run(g, inputs)
     assert got[0].tobytes() == ref[0].tobytes()

@@ -412,6 +412,27 @@ def test_max_propagates_nan():
     assert np.isnan(m[0, 0]) and m[1, 0] == 5
 
 
+@pytest.mark.parametrize("dt", ["f32", "f64"])
+def test_max_signed_zeros_do_not_depend_on_order(dt):
+    """-0 orders below +0 (IEEE 754-2019 maximum): every arrangement of
+    signed zeros (and negatives) gives +0 whenever a +0 is present, -0 when
+    only -0 and negatives are."""
+    import itertools
+    npdt = np.float32 if dt == "f32" else np.float64
+    rows = []
+    for perm in itertools.permutations([-0.0, 0.0, -1.0]):
+        rows.append(perm)
+    rows.append((-0.0, -2.0, -0.0))
+    xv = np.array(rows, npdt)
+    g = synth.Spec()
+    x = g.buffer("x", xv.shape, dt)
+    g.output(g.max(x, (1,)))
+    m, = oracle.run(g, {"x": xv})
+    m = m[:, 0]
+    assert all(v == 0 and not np.signbit(v) for v in m[:-1])
+    assert m[-1] == 0 and np.signbit(m[-1])
+
+
 def test_sum_order_is_ascending():
     """A fold in ascending order gives a specific, order-revealing result."""
     g = synth.Spec()
