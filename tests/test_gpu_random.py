@@ -29,3 +29,16 @@ def test_random_region_matches_oracle(seed):
     got = run(rv.compile_spec(g), inputs)
     ref = oracle.run(g, inputs)
     assert got[0].tobytes() == ref[0].tobytes()
+
+
+# the same regions stored in bfloat16, float16 and int32 (small integers:
+# exact in every dtype; narrow floats round once at the store, as the oracle)
+@pytest.mark.parametrize("dt", ["bf16", "f16", "i32"])
+@pytest.mark.parametrize("seed", range(12))
+def test_random_region_dtypes_match_oracle(dt, seed):
+    from reduce_view_amd import rv
+    print(f"CASE random region {dt} {seed}", flush=True)
+    g, inputs = random_region(seed, dt)
+    got = run(rv.compile_spec(g), inputs)
+    ref = oracle.run(g, inputs)
+    assert got[0].tobytes() == ref[0].tobytes()

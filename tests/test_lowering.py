@@ -376,7 +376,15 @@ def test_view_of_view_window_is_one_kernel():
     assert got[0].tobytes() == oracle.run(g, inp)[0].tobytes()
 
 
-def random_region(seed):
+def _random_values(rng, shape, dt):
+    """Small integers in the storage of dtype ``dt`` (bfloat16 as bits)."""
+    v = rng.integers(-3, 4, shape)
+    if dt == "bf16":
+        return synth.to_bf16_bits(v.astype(np.float32))
+    return v.astype({"f32": np.float32, "f16": np.float16, "f64": np.float64, "i32": np.int32}[dt])
+
+
+def random_region(seed, dt="f32"):
     """A random small region: two or three buffers read directly,
     transposed, as a broadcast row, or through a shrunk (and partly padded)
     window of a larger buffer; a random mix of ADD / MUL / NEG / CMPLT /
@@ -386,28 +394,28 @@ def random_region(seed):
     rng = np.random.default_rng(1000 + seed)
     rank = 2 if rng.random() < 0.6 else 3
     shape = tuple(int(x) for x in rng.integers(8, 21, rank))
-    g = synth.Spec(f"random_{seed}")
+    g = synth.Spec(f"random_{dt}_{seed}")
     inputs, vals = {}, []
     for b in range(int(rng.integers(2, 4))):
         name = f"B{b}"
         mode = ["direct", "transposed", "row", "window"][int(rng.integers(0, 4))]
         if mode == "direct":
             bshape = shape
-            v = g.buffer(name, bshape, "f32")
+            v = g.buffer(name, bshape, dt)
         elif mode == "transposed":
             bshape = shape[::-1]
-            v = g.view(g.buffer(name, bshape, "f32"), ("permute", tuple(range(rank))[::-1]))
+            v = g.view(g.buffer(name, bshape, dt), ("permute", tuple(range(rank))[::-1]))
         elif mode == "row":
             bshape = (shape[-1],)
-            v = g.view(g.buffer(name, bshape, "f32"), ("reshape", (1,) * (rank - 1) + (shape[-1],)), ("expand", shape))
+            v = g.view(g.buffer(name, bshape, dt), ("reshape", (1,) * (rank - 1) + (shape[-1],)), ("expand", shape))
         else:
             bshape = tuple(d + 3 for d in shape)
             lo = tuple(int(rng.integers(0, 4)) for _ in shape)
-            v = g.view(g.buffer(name, bshape, "f32"), ("shrink", tuple((l, l + d) for l, d in zip(lo, shape))))
+            v = g.view(g.buffer(name, bshape, dt), ("shrink", tuple((l, l + d) for l, d in zip(lo, shape))))
             if rng.random() < 0.5:  # and pad one side back with zeros
                 pad = tuple((1, 0) if dd == 0 else (0, 0) for dd in range(rank))
                 v = g.view(v, ("pad", pad), ("shrink", tuple((0, d) for d in shape)))
-        inputs[name] = rng.integers(-3, 4, bshape).astype(np.float32)
+        inputs[name] = _random_values(rng, bshape, dt)
         vals.append(v)
     x = vals[0]
     for v in vals[1:]:
