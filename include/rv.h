@@ -86,11 +86,12 @@ typedef enum rv_op {
  *
  * RV_CUSTOM_SDPA_FWD, in `rv_node.buf`: fused attention forward (limn README,
  * "The op set": the forward saves one number per row besides the answer,
- * the logsumexp L; Tiki README, "Fused attention": running maximum,
- * denominator and accumulator per query row over tiles of keys).
+ * the logsumexp L; Tiki README, "Write the attention kernel at the
+ * algorithm level": running maximum, denominator and accumulator per query
+ * row over tiles of keys).
  *   src[0..2] = q (H, Tq, D), k (H, Tk, D), v (H, Tk, D), all RV_BF16, with
  *               D one of 32, 64, 128; H <= 65535.
- *   cval       = the score scale (finite).
+ *   cval       = the score scale (finite and > 0; RV_E_INVALID otherwise).
  *   reduce_axes = RV_SDPA_CAUSAL (key j hidden from query i when j > i) OR'd
  *               with (output index << 16): output 0 is
  *               O = softmax(scale * q k^T) v, shape (H, Tq, D), dtype RV_F32 or
@@ -124,8 +125,10 @@ typedef enum rv_op {
  *                scatter); f32, f64 and i32 only (RV_E_UNSUPPORTED_OP
  *                otherwise); ints are exact, floats agree with the ordered
  *                result up to the order of colliding adds.
- * The index must have fewer than 2^31 cells and every dim must fit in int32
- * (RV_E_INVALID otherwise). */
+ * The index must have fewer than 2^31 cells and every dim must fit in int32;
+ * an ordered SCATTER also needs fewer than 2^31 target keys (the base's
+ * extent along a times the index's extents along the dims the index varies
+ * in besides a). RV_E_INVALID otherwise. */
 #define RV_SCATTER_ORDERED 0
 #define RV_SCATTER_ATOMIC 1
 

@@ -1099,8 +1099,9 @@ std::string Gen::gen_row() {
 // reduce and once more for the full-row outputs, with O(1) state per lane;
 // each reduce's result is a row constant for the passes after it. A MAX and
 // a SUM of EXP(X - MAX(X)) share one pass through the online recurrence
-// (Tiki README, "Fused attention": running maximum and denominator, the
-// denominator rescaled by exp(m_old - m_new) whenever the maximum grows),
+// (Tiki README, "Write the attention kernel at the algorithm level":
+// running maximum and denominator, the denominator rescaled by
+// exp(m_old - m_new) whenever the maximum grows),
 // so softmax reads its row twice instead of three times. A range whose
 // values are all -inf so far keeps m = -inf and adds nothing, so masked
 // entries never produce -inf - (-inf).

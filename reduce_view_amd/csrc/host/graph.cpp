@@ -226,8 +226,11 @@ Graph intake(const rv_node* nodes, int32_t n, const int32_t* outputs, int32_t no
                 nd.cout = (int)((in.reduce_axes >> 16) & 0xff);
                 nd.causal = (in.reduce_axes & RV_SDPA_CAUSAL) != 0;
                 nd.cval = in.cval;
-                if (!(in.cval == in.cval) || in.cval == 1.0 / 0.0 || in.cval == -1.0 / 0.0)
-                    fail(RV_E_INVALID, fmt("node %d: sdpa_fwd scale must be finite", i));
+                // the kernel carries max(s) * scale as the running maximum of
+                // the scaled scores and masks keys to -inf before scaling:
+                // both hold only for a positive scale
+                if (!(in.cval > 0.0) || in.cval == 1.0 / 0.0)
+                    fail(RV_E_INVALID, fmt("node %d: sdpa_fwd scale must be finite and positive (got %g)", i, in.cval));
                 if (nd.cout == 0) {
                     if (in.dtype != RV_F32 && in.dtype != RV_BF16)
                         fail(RV_E_DTYPE, fmt("node %d: sdpa_fwd output must be f32 or bf16", i));

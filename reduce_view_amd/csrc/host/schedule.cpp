@@ -692,8 +692,10 @@ static bool scatter_kernels(Ctx& c, int i, std::vector<Kernel>& out, std::vector
             k.sc_part = "atomic";
             ks.push_back(k);
         } else {
-            if (keys > (int64_t(1) << 32))
-                fail(RV_E_INVALID, fmt("SCATTER into %s: %lld target keys do not fit in 32 bits",
+            // keys, sorted positions and cell ids travel as 32-bit words whose
+            // bit 31 flags a dropped cell, and the run bounds are read as int
+            if (keys >= (int64_t(1) << 31))
+                fail(RV_E_INVALID, fmt("SCATTER into %s: %lld target keys (2^31 or more)",
                                        shape_str(osh).c_str(), (long long)keys));
             const int passes = std::max(1, (bit_width((uint64_t)keys - 1) + 7) / 8);
             const int64_t nb = (cells + 2047) / 2048;

@@ -1357,8 +1357,9 @@ __device__ __forceinline__ void rv_gemm_pp_bf16(const unsigned short* __restrict
 // ---------------------------------------------------------------------------
 // Fused attention forward, the CUSTOM sdpa_fwd kernel (limn README, "The op
 // set": the one CUSTOM kernel, saving the row's logsumexp beside the output;
-// Tiki README, "Fused attention": a running maximum m, denominator l and
-// output accumulator per query row, updated tile of keys by tile of keys).
+// Tiki README, "Write the attention kernel at the algorithm level": a
+// running maximum m, denominator l and output accumulator per query row,
+// updated tile of keys by tile of keys).
 //
 // The scores are formed transposed, S^T = K Q^T on v_mfma_f32_32x32x16_bf16,
 // so a lane of the 32 x 32 result holds 16 scores of ONE query (its column):

@@ -344,7 +344,9 @@ class Program:
         self.n_inputs, self.n_outputs = rv_program_io(handle)
         self.out_desc = [rv_output_desc(handle, i) for i in range(self.n_outputs)]
         self.ws_bytes = rv_workspace_size(handle)
-        self._ws = None
+        # one cached workspace per (device, stream): launches on different
+        # streams may overlap, and the kernels keep scratch state there
+        self._ws = {}
 
     def __del__(self):
         try:
@@ -365,11 +367,28 @@ class Program:
         import torch
         return [torch.empty(shape, dtype=_torch_dtype(dt), device=device) for shape, dt in self.out_desc]
 
-    def workspace(self, device="cuda"):
+    def workspace(self, device="cuda", stream=None):
+        """The cached workspace for launches on ``stream`` (None if the
+        program needs none). Launches that may overlap must not share one:
+        each stream gets its own."""
         import torch
-        if self.ws_bytes and (self._ws is None or self._ws.device != torch.device(device)):
-            self._ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
-        return self._ws
+        if not self.ws_bytes:
+            return None
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        key = (str(dev), int(stream.cuda_stream) if stream is not None else 0)
+        ws = self._ws.get(key)
+        if ws is None:
+            ws = self._ws[key] = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        return ws
+
+    @staticmethod
+    def _ws_args(ws):
+        """(pointer, size in bytes) of a workspace tensor, or (0, 0)."""
+        if ws is None:
+            return 0, 0
+        return ws.data_ptr(), ws.numel() * ws.element_size()
 
     def prepare(self, inputs: dict, outputs, stream, workspace=None):
         """Marshal the buffers once; the returned callable enqueues the
@@ -385,9 +404,9 @@ class Program:
             bufs.append(rv_buffer(t.data_ptr(), t.numel(), DTYPE[_dtype_name(t.dtype)], 0))
         arr = (rv_buffer * max(1, len(bufs)))(*bufs)
         n = len(bufs)
-        ws = workspace if workspace is not None else self.workspace(outputs[0].device if outputs else "cuda")
-        wptr = ctypes.c_void_p(ws.data_ptr() if ws is not None else None)
-        wsb = self.ws_bytes
+        ws = workspace if workspace is not None else self.workspace(outputs[0].device if outputs else "cuda", stream)
+        wp, wsb = self._ws_args(ws)
+        wptr = ctypes.c_void_p(wp or None)
         sptr = ctypes.c_void_p(stream.cuda_stream or None)
         h = self.h
         fn = _lib.rv_launch
@@ -413,11 +432,11 @@ class Program:
             bufs.append(rv_buffer(t.data_ptr(), t.numel(), DTYPE[_dtype_name(t.dtype)], 0))
         for t in outputs:
             bufs.append(rv_buffer(t.data_ptr(), t.numel(), DTYPE[_dtype_name(t.dtype)], 0))
-        ws = workspace if workspace is not None else self.workspace(outputs[0].device if outputs else "cuda")
-        wptr = ws.data_ptr() if ws is not None else 0
         if stream is None:
             stream = torch.cuda.current_stream()
-        rv_launch(self.h, bufs, wptr, self.ws_bytes, stream.cuda_stream)
+        ws = workspace if workspace is not None else self.workspace(outputs[0].device if outputs else "cuda", stream)
+        wptr, wsb = self._ws_args(ws)
+        rv_launch(self.h, bufs, wptr, wsb, stream.cuda_stream)
         return outputs
 
 

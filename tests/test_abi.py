@@ -188,3 +188,50 @@ def test_program_io_and_describe():
     assert [k["class"] for k in d["kernels"]] == ["ROW"]
     assert d["kernels"][0]["name"].startswith("rv_row_row_") and d["kernels"][0]["name"] in prog.source()
     assert rv.rv_last_error() == ""
+
+
+def test_attention_scale_must_be_positive():
+    # the kernel's running maximum of the scaled scores is max(s) * scale and
+    # masked keys are set to -inf before scaling: a scale <= 0 is refused
+    for scale, want in ((0.25, "OK"), (0.0, "RV_E_INVALID"), (-0.25, "RV_E_INVALID"),
+                        (float("inf"), "RV_E_INVALID"), (float("nan"), "RV_E_INVALID")):
+        g = synth.Spec()
+        q = g.buffer("q", (1, 16, 32), "bf16")
+        k = g.buffer("k", (1, 16, 32), "bf16")
+        v = g.buffer("v", (1, 16, 32), "bf16")
+        g.output(g.sdpa(q, k, v, scale, causal=True)[0])
+        assert _status_or_ok(g) == want, scale
+
+
+def test_ordered_scatter_key_count_limit():
+    # 65536 targets along the axis times 32768 index columns the index varies
+    # along: 2^31 keys do not fit the 31-bit key words
+    def spec(cols):
+        g = synth.Spec()
+        base = g.const(0.0, (65536, cols), "f32")
+        i = g.buffer("i", (1, cols), "i32")
+        v = g.buffer("v", (1, cols), "f32")
+        g.output(g.scatter(base, i, v, 0))
+        return g
+    assert _status_or_ok(spec(32767)) == "OK"
+    assert _status_or_ok(spec(32768)) == "RV_E_INVALID"
+
+
+def test_caller_workspace_size_is_checked():
+    # a caller-supplied workspace smaller than the program needs is refused
+    # before anything reaches the device (host tensors stand in for buffers)
+    import torch
+    prog = rv.compile_spec(synth.gemm_relu2_sum(128, 128, 64))
+    prog.slots = ["A", "B"]
+    inputs = {"A": torch.zeros(128 * 64, dtype=torch.bfloat16), "B": torch.zeros(64 * 128, dtype=torch.bfloat16)}
+    out = [torch.zeros(1, dtype=torch.float32)]
+
+    class _Stream:
+        cuda_stream = 0
+    small = torch.empty(16, dtype=torch.uint8)
+    with pytest.raises(rv.RVError) as e:
+        prog.launch(inputs, out, stream=_Stream(), workspace=small)
+    assert e.value.name == "RV_E_WORKSPACE"
+    with pytest.raises(rv.RVError) as e:
+        prog.prepare(inputs, out, _Stream(), workspace=small)()
+    assert e.value.name == "RV_E_WORKSPACE"
