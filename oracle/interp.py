@@ -36,8 +36,11 @@ notes of the repository):
   * MAX starts from -inf (ints: the smallest value of the width), a NaN
     anywhere in the row gives NaN, and -0 orders below +0 (IEEE 754-2019
     maximum), so the result's bits do not depend on the fold order.
-  * float -> bfloat16 CAST rounds to nearest even and keeps NaN a NaN;
-    float -> int truncates toward zero.
+  * CAST rounds to nearest even and keeps NaN a NaN; a value cast to a half
+    width (float16, bfloat16) is a float32 first, so a float64 or a large
+    int32 source is rounded twice; float -> int truncates toward zero and
+    wraps modulo 2**width (undefined beyond int32, for NaN and infinities);
+    int -> int wraps.
   * GATHER along an axis reads data at the position with that axis
     coordinate replaced by the index (the index has the output's shape); an
     index outside the axis reads zero, as a read outside a View's mask does.
@@ -143,14 +146,24 @@ def _narrow(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _to_dtype_from_float(x: np.ndarray, dtype: str) -> np.ndarray:
-    """CAST of float values (float32 or float64 array) to ``dtype``."""
+    """CAST of float values (float32 or float64 array) to ``dtype``.
+
+    * to an int: truncate toward zero, then wrap modulo 2**width (defined
+      where the truncated value fits in int32; NaN, infinities and larger
+      magnitudes are left undefined);
+    * to float32 / float64: one rounding to nearest even;
+    * to a half width (float16, bfloat16): the value is a float32 first and
+      is rounded once from there (limn README, "The op set": the half widths
+      are storage computed in float32), so a float64 source is rounded twice,
+      to float32 and then to the half width."""
     if dtype in INTS:
         with np.errstate(invalid="ignore"):
             t = np.trunc(x.astype(np.float64))
-        return t.astype(np.int64).astype(STORAGE[dtype])
-    if dtype == "bf16":
-        return f32_to_bf16(x.astype(np.float32))
-    return x.astype(STORAGE[dtype])
+            return t.astype(np.int64).astype(STORAGE[dtype])
+    with np.errstate(over="ignore", invalid="ignore"):
+        if dtype in ("bf16", "f16"):
+            return _narrow(x.astype(np.float32), dtype)
+        return x.astype(STORAGE[dtype])
 
 
 # ---------------------------------------------------------------------------
@@ -341,6 +354,10 @@ def _binary(op: str, x: np.ndarray, y: np.ndarray, dt: str) -> np.ndarray:
 
 
 def _cast(x: np.ndarray, src_dt: str, dst_dt: str) -> np.ndarray:
+    """CAST (limn README, "The op set", dtype paragraph). int -> int wraps
+    modulo 2**width; int -> float64 is exact; int -> float32 rounds once to
+    nearest even; int -> a half width goes through float32 (two roundings);
+    float sources follow ``_to_dtype_from_float``."""
     if src_dt == dst_dt:
         return x.copy()
     if src_dt in INTS:
@@ -349,7 +366,8 @@ def _cast(x: np.ndarray, src_dt: str, dst_dt: str) -> np.ndarray:
         if dst_dt == "f64":
             return x.astype(np.float64)
         r = x.astype(np.float64).astype(np.float32) if dst_dt != "f32" else x.astype(np.float32)
-        return _narrow(r, dst_dt) if dst_dt in ("bf16", "f16") else r
+        with np.errstate(over="ignore"):
+            return _narrow(r, dst_dt) if dst_dt in ("bf16", "f16") else r
     w = _widen(x, src_dt)
     return _to_dtype_from_float(w, dst_dt)
 

@@ -142,10 +142,9 @@ std::string op_code(const Kernel& k, const Ex& e, const std::string& A, const st
                 return wrap_int(dt, "(int)(" + A + ")");
             }
             if (dt == RV_F64) return "((double)(" + A + "))";
-            if (s == RV_F64) {
-                if (dt == RV_F16) return "((float)(_Float16)(" + A + "))";
-                return round_to(dt, "((float)(" + A + "))");
-            }
+            // a value headed for a half width is a float32 first (float64
+            // and int sources round twice, as the oracle and torch do)
+            if (s == RV_F64) return round_to(dt, "((float)(" + A + "))");
             if (is_int(s)) return round_to(dt, "((float)(" + A + "))");
             return round_to(dt, A);
         }

@@ -67,6 +67,16 @@ template <>
 struct rv_words<32> {  // 4 doubles: two 16-byte accesses
     typedef __attribute__((ext_vector_type(8))) unsigned type;
 };
+// a wide operand beside a narrow output (16 floats or doubles feeding 16
+// int8 cells): four or eight 16-byte accesses
+template <>
+struct rv_words<64> {
+    typedef __attribute__((ext_vector_type(16))) unsigned type;
+};
+template <>
+struct rv_words<128> {
+    typedef __attribute__((ext_vector_type(32))) unsigned type;
+};
 
 template <class T, int N>
 __device__ __forceinline__ rv_pack<T, N> rv_ldv_nt(const T* p) {

@@ -480,3 +480,77 @@ def gemm_bf16_bt(m: int, n: int, k: int) -> Spec:
     b3 = g.cast(g.view(bt, ("reshape", (1, n, k)), ("expand", (m, n, k))), "f32")
     g.output(g.sum(g.mul(a3, b3), (2,)))
     return g
+
+
+def cast_matrix(n: int) -> Spec:
+    """Every CAST between the seven dtypes: one (n,) input ``x_<src>`` per
+    dtype and 49 outputs CAST(x_src, dst), source-major in ``DTYPES`` order
+    (a CAST to the source's own dtype is a copy)."""
+    g = Spec(f"cast_matrix_{n}")
+    xs = {dt: g.buffer(f"x_{dt}", (n,), dt) for dt in DTYPES}
+    for src in DTYPES:
+        for dst in DTYPES:
+            g.output(g.cast(xs[src], dst))
+    return g
+
+
+# Values a CAST must get right at the edges: halfway cases of every float
+# width, overflow to infinity, subnormals, float64 values that round twice on
+# their way to a half width, truncation toward zero and wraparound of ints.
+CAST_FLOAT_WITNESSES = (
+    0.0, -0.0, 0.5, -0.5, 1.5, -1.5, 2.5, -2.5, 2.9999, -2.9999, 127.9, 128.0, -128.0, -129.5, 255.5,
+    300.0, -300.7, 32767.5, 32768.0, -32769.9, 40000.0, 65504.0, 65519.99, 65520.0, 1e5, 16777217.0,
+    2147483520.0, -2147483648.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -11, 1 + 3 * 2 ** -11,
+    1 + 2 ** -8 + 2 ** -30, 1 + 2 ** -11 + 2 ** -40, 1 + 2 ** -24, 1 + 2 ** -24 + 2 ** -50, 2 ** -24,
+    2 ** -25, 1.5 * 2 ** -25, 2 ** -14, 2 ** -126, 2 ** -133, 2 ** -149, 2 ** -150, 3.0e38, 3.389e38,
+    3.4e38, 3.5e38, 1e300, -1e300, 1e-300, float("inf"), float("-inf"), float("nan"), 0.1, 1 / 3,
+)
+CAST_INT_WITNESSES = (
+    0, 1, -1, 127, 128, -128, -129, 255, 256, 300, 2049, 2051, 32767, 32768, -32768, -32769, 40000,
+    65504, 65519, 65520, 65535, 16777217, 16777219, 2 ** 24 + 2 ** 16 + 1, 2 ** 31 - 1, -2 ** 31,
+    2 ** 31 - 64, 123456789, -987654321,
+)
+_INT_RANGE = {"i32": (-2 ** 31, 2 ** 31 - 1), "i16": (-2 ** 15, 2 ** 15 - 1), "i8": (-128, 127)}
+
+
+def inputs_cast(n: int = 1024, seed: int = 10) -> dict:
+    """``x_<dt>`` for every dtype: the witnesses above that the dtype holds
+    (floats rounded into it by numpy's or torch's RNE cast, ints in range),
+    then seeded fill: for the float widths half uniformly random bit
+    patterns (every class: NaN, infinities, subnormals) and half
+    N(0, 1) * 10^U(-3, 6); for the ints uniform over the whole range.
+    Draw order: the dtypes in ``DTYPES`` order."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    fw = np.array(CAST_FLOAT_WITNESSES, dtype=np.float64)
+    for dt in DTYPES:
+        if dt in _INT_RANGE:
+            lo, hi = _INT_RANGE[dt]
+            w = np.array([v for v in CAST_INT_WITNESSES if lo <= v <= hi], dtype=np.int64)
+            fill = rng.integers(lo, hi, size=n, endpoint=True, dtype=np.int64)
+            store = {"i32": np.int32, "i16": np.int16, "i8": np.int8}[dt]
+            out[f"x_{dt}"] = np.concatenate([w, fill])[:n].astype(store)
+            continue
+        nb = {"f64": 64, "f32": 32, "f16": 16, "bf16": 16}[dt]
+        half = n // 2
+        bits = rng.integers(0, 2 ** nb if nb < 64 else 2 ** 63, size=half, dtype=np.uint64)
+        if nb == 64:
+            bits = bits | (rng.integers(0, 2, size=half, dtype=np.uint64) << np.uint64(63))
+        mags = rng.standard_normal(n - half) * 10.0 ** rng.uniform(-3.0, 6.0, n - half)
+        with np.errstate(over="ignore", invalid="ignore"):
+            if dt == "f64":
+                vals = np.concatenate([fw, bits.view(np.float64), mags])
+                out[f"x_{dt}"] = vals[:n].astype(np.float64)
+            elif dt == "f32":
+                vals = np.concatenate([fw.astype(np.float32), bits.astype(np.uint32).view(np.float32),
+                                       mags.astype(np.float32)])
+                out[f"x_{dt}"] = vals[:n]
+            elif dt == "f16":
+                vals = np.concatenate([fw.astype(np.float16), bits.astype(np.uint16).view(np.float16),
+                                       mags.astype(np.float16)])
+                out[f"x_{dt}"] = vals[:n]
+            else:
+                wb = to_bf16_bits(fw.astype(np.float32))
+                mb = to_bf16_bits(mags.astype(np.float32))
+                out[f"x_{dt}"] = np.concatenate([wb, bits.astype(np.uint16), mb])[:n]
+    return out
