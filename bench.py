@@ -1,20 +1,27 @@
 """Benchmark of the fused view/reduce hot path on one MI355X.
 
-Default workload (the one the headline metric is quoted on): the 4096 x 4096
+Default run (``--workload ew_chain``): the headline is the 4096 x 4096
 float32 elementwise chain WHERE(CMPLT(a, b), a*b, EXP(-a)) + c with b a
 permuted View and c a stride-0 row vector, the same chain with a read through
-a shrink-then-pad masked View, and a standalone 4096 x 4096 transpose. One
-step runs all three programs once. ``--workload`` selects one of the other
-kernels instead (softmax, softmax_long, rmsnorm, rmsnorm_f16, rmsnorm_f64,
-chain_i8, layernorm, gemm, attention, gather, scatter, scatter_atomic,
-matmul64, copy).
+a shrink-then-pad masked View, and a standalone 4096 x 4096 transpose; one
+step runs all three programs once. The same JSON line then carries a
+``configs`` object with every one of the five seeded workloads (64^3 matmul
+as a broadcast MUL + SUM, the chain / masked chain / transpose, row softmax
+and RMSNorm, LayerNorm, the 4096^3 bf16 contraction with its relu^2 + SUM
+epilogue): per program its time, throughput, roofline fraction, the kernel
+classes it compiled to (checked), and its parity against the CPU oracle run
+in the CPU-baseline leg (max |err|, max bound, max err/bound).
+
+``--workload`` times one other kernel alone instead (softmax, softmax_long,
+rmsnorm, rmsnorm_f16, rmsnorm_f64, chain_i8, layernorm, gemm, attention,
+gather, scatter, scatter_atomic, sum_full, sum_cols, matmul64, copy).
 
 Inputs are seeded, synthetic and already resident in HBM when timing starts;
 several input sets rotate so that consecutive launches never re-read data the
 previous launch left in the 256 MB Infinity Cache. Throughput counts
 ALGORITHMIC bytes (each input cell read once, masked cells not read, each
 output written once) or flops. Kernel times come from HIP events on the
-stream the kernels are launched on (torch's current stream).
+stream the kernels are launched on.
 
 Prints one JSON line.
 """
@@ -133,6 +140,16 @@ def workloads():
             inputs=lambda seed: {k: v for k, v in synth.inputs_embedding(65536, 1024, 32768, seed).items()
                                  if k in ("values", "ids")},
             unit="GB/s", dtype="f32", bound="hbm", seed=9),
+        "sum_full": dict(
+            desc="full SUM of 2^24 fp32 to a scalar (split reduce: partials + fold), x ~ N(0,1), seed 11",
+            programs=[("sum_full", synth.reduce((1 << 24,), (0,)), (1 << 24) * F32 + F32)],
+            inputs=lambda seed: synth.inputs_reduce((1 << 24,), seed=seed),
+            unit="GB/s", dtype="f32", bound="hbm", seed=11),
+        "sum_cols": dict(
+            desc="SUM over axis 0 of a (16384, 4096) fp32 matrix (split reduce over 4096 cells), x ~ N(0,1), seed 12",
+            programs=[("sum_cols", synth.reduce((16384, 4096), (0,)), 16384 * 4096 * F32 + 4096 * F32)],
+            inputs=lambda seed: synth.inputs_reduce((16384, 4096), seed=seed),
+            unit="GB/s", dtype="f32", bound="hbm", seed=12),
         "copy": dict(
             desc="plain 4096x4096 fp32 copy (bandwidth reference; not a hot-path workload)",
             programs=[("copy", synth.copy(4096, 4096), 2 * 4096 * 4096 * F32)],
@@ -164,6 +181,161 @@ def _recorded_traffic(program_key: str):
             except ValueError:
                 return None
     return None
+
+
+# ---------------------------------------------------------------------------
+# the five seeded configurations (default run): (config, program name, graph,
+# inputs, algorithmic work, unit, bound, kernel classes it must compile to)
+# ---------------------------------------------------------------------------
+
+def _to_device(arr):
+    import torch
+    if arr.dtype == np.uint16:  # bfloat16 bit patterns
+        return torch.from_numpy(arr.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def _to_host(t):
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def config_programs():
+    from reduce_view_amd import synth
+    r = c = 4096
+    chain_b, masked_b, tr_b = _bytes_ew(r, c)
+    ew = lambda: synth.inputs_ew(r, c, 1)  # noqa: E731
+    return [
+        ("c1", "matmul64", synth.matmul_broadcast(64, 64, 64), lambda: synth.inputs_matmul(64, 64, 64, 0),
+         3 * 64 * 64 * F32, "GB/s", "latency", ["REDUCE"]),
+        ("c2", "chain", synth.ew_chain(r, c), ew, chain_b, "GB/s", "hbm", ["EW"]),
+        ("c2", "chain_masked", synth.ew_chain(r, c, masked=True), ew, masked_b, "GB/s", "hbm", ["EW"]),
+        ("c2", "transpose", synth.transpose(r, c), ew, tr_b, "GB/s", "hbm", ["EW"]),
+        ("c3", "softmax", synth.softmax(16384, 4096), lambda: synth.inputs_softmax(16384, 4096, 2),
+         2 * 16384 * 4096 * F32, "GB/s", "hbm", ["ROW"]),
+        ("c3", "rmsnorm", synth.rmsnorm(16384, 4096), lambda: synth.inputs_rmsnorm(16384, 4096, 3),
+         2 * 16384 * 4096 * F32 + 4096 * F32, "GB/s", "hbm", ["ROW"]),
+        ("c4", "layernorm", synth.layernorm(8192, 8192), lambda: synth.inputs_layernorm(8192, 8192, 4),
+         2 * 8192 * 8192 * 2 + 2 * 8192 * 2, "GB/s", "hbm", ["ROW"]),
+        ("c5", "gemm_relu2_sum", synth.gemm_relu2_sum(4096, 4096, 4096), lambda: synth.inputs_gemm(4096, 4096, 4096, 5),
+         2 * 4096 ** 3, "TFLOP/s", "mfma", ["MFMA", "FOLD"]),
+    ]
+
+
+# ---------------------------------------------------------------------------
+# parity bounds (the reduction-order bound 4 gamma_{N-1} sum |x| plus 2 ulp
+# per transcendental; Litmus README, ToleranceBound), computed in float64
+# from the inputs; the oracle's values come from the CPU-baseline leg
+# ---------------------------------------------------------------------------
+U = 2.0 ** -24
+
+
+def _gamma(n, u=U):
+    return n * u / (1.0 - n * u) if n * u < 1 else float("inf")
+
+
+def _ulp32(x):
+    return np.spacing(np.abs(np.asarray(x, dtype=np.float32))).astype(np.float64)
+
+
+def _bf16_f64(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _report(err, bound):
+    err = np.asarray(err, dtype=np.float64)
+    bound = np.asarray(bound, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
+    return {"max_err": float(err.max(initial=0.0)), "max_bound": float(bound.max(initial=0.0)),
+            "max_err_over_bound": float(ratio.max(initial=0.0)), "within": bool(np.all(err <= bound))}
+
+
+def _parity(name, inp, got, ref, extra):
+    """max |err|, max bound, max err/bound of one program's GPU output
+    against the oracle's, with the bound each workload's arithmetic implies."""
+    g = got.astype(np.float64)
+    r = ref.astype(np.float64)
+    if name == "matmul64":
+        ab = np.abs(inp["A"].astype(np.float64)) @ np.abs(inp["B"].astype(np.float64))
+        return _report(np.abs(g - r).reshape(ab.shape), 4 * _gamma(63) * ab)
+    if name in ("chain", "chain_masked"):
+        # bit-exact where a < b (MUL then ADD, contraction off); elsewhere
+        # one float32 EXP (2 ulp) and the ADD's rounding
+        a = inp["a"]
+        if name == "chain_masked":
+            a = np.zeros_like(inp["Abig"])
+            a[3:-3, 5:-5] = inp["Abig"][3:-3, 5:-5]
+        took_exp = ~(a < inp["Bb"].T)
+        e = np.exp(-a.astype(np.float64)).astype(np.float32)
+        return _report(np.abs(g - r), np.where(took_exp, 2 * _ulp32(e) + _ulp32(ref), 0.0))
+    if name == "transpose":
+        return _report(np.abs(g - r), np.zeros_like(r))
+    if name == "softmax":
+        n = ref.shape[1]
+        return _report(np.abs(g - r), r * (4 * _gamma(n - 1) + 2 * 2.0 ** -23 + 4 * U) + 3 * 2.0 ** -149)
+    if name == "rmsnorm":
+        n = ref.shape[1]
+        return _report(np.abs(g - r), np.abs(r) * (0.5 * 4 * _gamma(n - 1) + 6 * U))
+    if name == "layernorm":
+        # the variance's order term through |xc r gamma|, float32 roundings,
+        # one bfloat16 ulp for the final CAST
+        n = ref.shape[1]
+        x = _bf16_f64(inp["x"])
+        gam, bet = _bf16_f64(inp["gamma"]), _bf16_f64(inp["beta"])
+        xc = x - x.mean(axis=1, keepdims=True)
+        ssq = (xc * xc).sum(axis=1, keepdims=True)
+        rr = 1.0 / np.sqrt(ssq / n + 1e-5)
+        prod = np.abs(xc * rr * gam)
+        y32 = xc * rr * gam + bet
+        gg, rb = _bf16_f64(got), _bf16_f64(ref)
+        m = np.maximum(np.abs(gg), np.abs(rb))
+        ulpb = 2.0 ** (np.floor(np.log2(np.maximum(m, 2.0 ** -133))) - 7)
+        bound = prod * (0.5 * 4 * _gamma(n - 1) * ssq / (ssq + n * 1e-5) + 4 * U) + 2 * U * np.abs(y32) + ulpb + 2.0 ** -133
+        return _report(np.abs(gg - rb), bound)
+    if name == "gemm_relu2_sum":
+        # y on sampled rows against the oracle's rows; S against the oracle's
+        # stored value for these inputs (its fp64 tolerance ingredients too)
+        rows, y_gpu, y_ref, gold, depth = extra
+        a = np.abs(_bf16_f64(inp["A"][rows]))
+        b = np.abs(_bf16_f64(inp["B"]))
+        dy = 4 * _gamma(4095) * (a @ b)
+        ry = _report(np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64)), dy)
+        ds = gold["propagated_y_term"] + U * gold["sum_q"] + 4 * _gamma(depth) * gold["sum_q"] + U * abs(gold["S"])
+        rs = _report(np.array([abs(float(got.ravel()[0]) - gold["S"])]), np.array([ds]))
+        rs["y_sampled_rows"] = ry
+        rs["S_bound_depth"] = depth
+        return rs
+    raise KeyError(name)
+
+
+def _cpu_leg(cases, budget_s):
+    """The CPU-baseline leg: the oracle, as it is, on the host cores, on the
+    workloads' seeded inputs (the contraction: a few sampled rows of y). Its
+    outputs are kept for the parity check. Returns (per-program oracle
+    seconds and outputs, cores used)."""
+    import oracle
+    from reduce_view_amd import synth
+    ru0 = resource.getrusage(resource.RUSAGE_SELF)
+    w0 = time.perf_counter()
+    res = {}
+    for name, spec, inp in cases:
+        t = time.perf_counter()
+        if name == "gemm_relu2_sum":
+            rows = [0, 1, 2047, 4095]
+            out = oracle.run(synth.gemm_bf16(len(rows), 4096, 4096), {"A": inp["A"][rows], "B": inp["B"]})
+        else:
+            out = oracle.run(spec, inp)
+        res[name] = (time.perf_counter() - t, out)
+        if time.perf_counter() - w0 > budget_s * 4:
+            break
+    wall = time.perf_counter() - w0
+    ru1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+    return res, max(1, int(round(cpu / max(wall, 1e-9))))
 
 
 def _cpu_baseline(wl, name, budget_s):
@@ -220,6 +392,95 @@ def _cpu_baseline(wl, name, budget_s):
             "sample": sample, "seconds": round(t_wall, 3), "host_threads_available": os.cpu_count()}
 
 
+class _Timer:
+    """Back-to-back launches on one stream, bracketed by HIP events on it."""
+
+    def __init__(self, stream):
+        self.stream = stream
+
+    def __call__(self, fn, reps):
+        import torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+
+def _rotating_sets(inputs, slots):
+    """The seeded inputs on the device, plus copies in distinct buffers so a
+    launch never re-reads what the launches before it left in the 256 MB
+    Infinity Cache (at least 1 GB across the sets)."""
+    first = {k: _to_device(v) for k, v in inputs.items() if k in slots}
+    per_set = sum(t.numel() * t.element_size() for t in first.values())
+    nsets = max(2, int(np.ceil(1.0e9 / max(per_set, 1))) + 1) if per_set > (1 << 20) else 1
+    return [first] + [{k: v.clone() for k, v in first.items()} for _ in range(nsets - 1)]
+
+
+def measure_configs(args, stream, timer, headline_ms):
+    """Every program of the five configurations: classes checked, time per
+    launch (at least K launches and 30 ms of them, after a warm-up of the
+    same length), one launch on the seeded inputs kept for parity."""
+    import json as _json
+    import torch
+    from reduce_view_amd import rv, synth
+    entries, keep = {}, {}
+    for cfg, name, spec, mk_inputs, work, unit, bound, classes in config_programs():
+        prog = rv.compile_spec(spec)
+        desc = prog.describe()
+        got_classes = [k["class"] for k in desc["kernels"]]
+        if got_classes != classes:
+            raise SystemExit(f"{name}: compiled to {got_classes}, expected {classes}")
+        inputs = mk_inputs()
+        sets = _rotating_sets(inputs, prog.slots)
+        out = prog.alloc_outputs()
+        ws = prog.workspace(stream=stream)
+        go = [prog.prepare(d, out, stream, ws) for d in sets]
+        if name in headline_ms:
+            ms = headline_ms[name]
+        else:
+            reps = max(args.steps, 50)
+            t_probe = timer(lambda i: go[i % len(go)](), 5)
+            reps = max(reps, int(np.ceil(30.0 / max(t_probe, 1e-3))))
+            timer(lambda i: go[i % len(go)](), reps)  # warm-up: clocks settle under the load
+            ms = timer(lambda i: go[i % len(go)](), reps)
+        go[0]()
+        torch.cuda.synchronize()
+        host_out = [_to_host(t) for t in out]
+        extra = None
+        if name == "gemm_relu2_sum":
+            yprog = rv.compile_spec(synth.gemm_bf16(4096, 4096, 4096))
+            y_out = yprog.alloc_outputs()
+            yprog.prepare(sets[0], y_out, stream, yprog.workspace(stream=stream))()
+            torch.cuda.synchronize()
+            rows = [0, 1, 2047, 4095]
+            y_rows = _to_host(y_out[0])[rows, :, 0]
+            del y_out
+            gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "gemm_relu2_sum_4096.json")))
+            depth = desc["kernels"][0]["plan_detail"]["partial_sum_depth"] + desc["kernels"][1]["plan_detail"]["sum_depth"]
+            extra = (rows, y_rows, gold, depth)
+        scale = 1e-12 if unit == "TFLOP/s" else 1e-9
+        achieved = work / (ms * 1e-3) * scale
+        peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBS
+        e = {"config": cfg, "ms": round(ms, 5), "value": round(achieved, 2), "unit": unit, "classes": got_classes,
+             "kernels": [k["name"] for k in desc["kernels"]],
+             "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                          "frac": round(achieved / peak, 4), "traffic": _recorded_traffic(desc["cache_key"]),
+                          "work_per_launch": work}}
+        if name == "gemm_relu2_sum":
+            e["note"] = "time per launch of the contraction and its fold (two kernels)"
+        if bound == "latency":
+            e["note"] = "48 KB of data: bound by launch latency, not a roofline"
+        entries[name] = e
+        keep[name] = (spec, inputs, host_out, extra)
+        del sets, go, out, ws
+        torch.cuda.empty_cache()
+    return entries, keep
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,6 +491,7 @@ def main():
     ap.add_argument("--workload", default="ew_chain")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="headline workload only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (one GPU per box, "
@@ -239,7 +501,6 @@ def main():
 
     import torch
     from reduce_view_amd import rv
-    from tests.harness import to_device
 
     wl = workloads()[args.workload]
     rv.rv_init(0)
@@ -250,13 +511,13 @@ def main():
     nsets = 1 if args.workload == "matmul64" else max(2, int(np.ceil(1.0e9 / per_set)) + 1)
     # the sets hold the same seeded values in distinct device buffers: what
     # matters for the cache is the addresses, not the values
-    first = {k: to_device(v) for k, v in wl["inputs"](wl["seed"]).items()}
+    first = {k: _to_device(v) for k, v in wl["inputs"](wl["seed"]).items()}
     dev_sets = [first] + [{k: v.clone() for k, v in first.items()} for _ in range(nsets - 1)]
-    outs = [p.alloc_outputs() for _, p, _ in progs]
-    wss = [p.workspace() for _, p, _ in progs]
     # a stream of its own (default priority)
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
+    outs = [p.alloc_outputs() for _, p, _ in progs]
+    wss = [p.workspace(stream=stream) for _, p, _ in progs]
 
     # launches marshalled once per (program, input set)
     launch = [[p.prepare(dev_sets[si], outs[j], stream, wss[j]) for si in range(nsets)]
@@ -269,16 +530,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
-    def timed(fn, reps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+    timed = _Timer(stream)
 
     # events around exactly K steps (launches marshalled beforehand, so the
     # host enqueues faster than the kernels drain; HIP graph replay was
@@ -315,8 +567,42 @@ def main():
            "data": "synthetic", "config": {"workload": args.workload + ": " + wl["desc"],
                                           "input_sets_rotated": nsets},
            "roofline": roofline}
+    del launch, dev_sets, first, outs, wss
+    torch.cuda.empty_cache()
+
+    configs = args.workload == "ew_chain" and not args.no_configs
+    if configs:
+        entries, keep = measure_configs(args, stream, timed, per_kernel)
+        out["configs"] = entries
     if rank == 0 and not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline(wl, args.workload, args.cpu_budget)
+        if configs:
+            # the oracle on every configuration's seeded inputs: its time is
+            # the baseline, its outputs the parity reference
+            res, cores = _cpu_leg([(n, keep[n][0], keep[n][1]) for n in keep], args.cpu_budget)
+            work = t_o = 0.0
+            for n, _, b in wl["programs"]:
+                if n in res:
+                    work += b
+                    t_o += res[n][0]
+            out["cpu_baseline"] = {"value": work / t_o * 1e-9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                                   "sample": ("one whole-program run of each of the chain, masked chain and "
+                                              "transpose at full size (the oracle also ran every other "
+                                              "configuration's program for the parity check; the contraction "
+                                              "on 4 sampled rows of y)"),
+                                   "seconds": round(t_o, 3), "host_threads_available": os.cpu_count()}
+            for n, e in out["configs"].items():
+                if n not in res:
+                    continue
+                spec, inputs, host_out, extra = keep[n]
+                t_n, ref = res[n]
+                if n == "gemm_relu2_sum":
+                    rows, y_rows, gold, depth = extra
+                    e["parity"] = _parity(n, inputs, host_out[0], None, (rows, y_rows, ref[0][:, :, 0], gold, depth))
+                else:
+                    e["parity"] = _parity(n, inputs, host_out[0], ref[0], None)
+                e["oracle_seconds"] = round(t_n, 3)
+        else:
+            out["cpu_baseline"] = _cpu_baseline(wl, args.workload, args.cpu_budget)
     if rank == 0:
         print(json.dumps(out), flush=True)
 

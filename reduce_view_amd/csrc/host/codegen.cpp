@@ -205,6 +205,9 @@ struct Gen {
             mark(k.ex[e].c);
         };
         for (auto& s : k.stores) mark(s.ex);
+        if (k.cls == KClass::SPLIT)  // its one reduce feeds the partials, not a store
+            for (size_t e = 0; e < k.ex.size(); ++e)
+                if (k.ex[e].op == RV_SUM || k.ex[e].op == RV_MAX) mark((int)e);
         int64_t mx = numel(k.domain);
         auto upd = [&](const rv_view& v) {
             int64_t lo, hi;
@@ -359,6 +362,8 @@ struct Gen {
     std::string gen_row_stream();
     std::string gen_attn();
     std::string gen_cells();
+    std::string gen_split_cols();
+    std::string gen_fold_cells();
     std::string gen_fold();
     std::string gen_gemm();
 };
@@ -1117,6 +1122,17 @@ std::string Gen::gen_row_stream() {
         size_t at = k.plan_json.find("\"unroll\":");
         if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"unroll\":%d", &U);
     }
+    // a split reduce: workgroup (row, piece) folds chunks
+    // [piece * CPP, (piece + 1) * CPP) and writes its raw total to the
+    // partials ([row][piece]) instead of finishing the row
+    const bool split = k.cls == KClass::SPLIT;
+    int64_t SP = 1, CPP = 0;
+    if (split) {
+        size_t at = k.plan_json.find("\"pieces\":");
+        if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"pieces\":%lld,\"chunks_per_piece\":%lld",
+                                            (long long*)&SP, (long long*)&CPP);
+        if (SP < 1 || CPP < 1) fail(RV_E_INVALID, "internal: split plan without pieces");
+    }
     const int RPW = (int)k.block[0] / T;
     const int W = T > 64 ? T / 64 : 1;
     const int E = VW * U;
@@ -1181,7 +1197,15 @@ std::string Gen::gen_row_stream() {
     const std::string inrow = fmt("%s < %s", nexpr("q / " + std::to_string(VW), "q % " + std::to_string(VW)).c_str(),
                                   lit(NR).c_str());
     const int64_t NRG = (NK + RPW - 1) / RPW;
-    b << "  for (" << I << " rg = blockIdx.x; rg < " << lit(NRG) << "; rg += gridDim.x) {\n";
+    if (split) {
+        b << "  {\n    const " << I << " rg = (" << I << ")blockIdx.x / " << lit(SP) << ";\n";
+        b << "    const " << I << " piece = (" << I << ")blockIdx.x % " << lit(SP) << ";\n";
+        b << "    const " << I << " c0 = piece * " << lit(CPP) << ";\n";
+        b << "    const " << I << " c1 = c0 + " << lit(CPP) << " < " << lit(NCH) << " ? c0 + " << lit(CPP) << " : "
+          << lit(NCH) << ";\n";
+    } else {
+        b << "  for (" << I << " rg = blockIdx.x; rg < " << lit(NRG) << "; rg += gridDim.x) {\n";
+    }
     if (T > 64 && nslots) b << "    rv_lds_barrier();\n";
     b << "    const " << I << " r = rg * " << RPW << " + lr;\n";
     b << "    const bool rv = r < " << lit(NK) << ";\n";
@@ -1300,9 +1324,12 @@ std::string Gen::gen_row_stream() {
             b << "    float om = -__builtin_inff(), ol = 0.0f;\n";
         else
             b << "    " << RedType(R0.op, R0.dtype).t << " acc" << r0 << " = " << RedType(R0.op, R0.dtype).ident << ";\n";
-        b << "    for (" << I << " c = 0; c < " << lit(NCH) << "; ++c) {\n";
+        if (split)
+            b << "    for (" << I << " c = c0; c < c1; ++c) {\n";
+        else
+            b << "    for (" << I << " c = 0; c < " << lit(NCH) << "; ++c) {\n";
         b << "      const " << I << " cb = c * " << lit(CH) << ";\n";
-        emit_chunk(needed({X}), "      ", false);
+        emit_chunk(needed({X}), "      ", split);
         const std::string xv = V(X, "q");
         if (online) {
             b << "      float cm = -__builtin_inff();\n";
@@ -1344,7 +1371,14 @@ std::string Gen::gen_row_stream() {
                     b << "      acc = " << rt.fold("acc", fmt("(%s)red[%d][lr][%d]", rt.t.c_str(), slot, w)) << ";\n";
                 ++slot;
             }
-            b << "      e" << r0 << " = " << rt.result(R0.dtype, "acc") << ";\n    }\n";
+            if (split) {
+                const int pdt = rt.isdbl ? RV_F64 : (rt.isint ? RV_I32 : RV_F32);
+                const std::string P = pname(Loc{2, k.partials_region}, pdt, true);
+                b << "      if (t == 0 && rv) " << P << "[r * " << lit(SP) << " + piece] = " << (rt.isint ? "(int)acc" : "acc")
+                  << ";\n      e" << r0 << " = " << zero_of(R0.dtype) << ";\n    }\n";
+            } else {
+                b << "      e" << r0 << " = " << rt.result(R0.dtype, "acc") << ";\n    }\n";
+            }
             done[r0] = 1;
         }
         emit_ready("    ");
@@ -1519,6 +1553,154 @@ std::string Gen::gen_cells() {
         b << "    " << P << "[" << addr(s.v, idx) << "] = " << sv(s.dtype, fmt("e%d", s.ex)) << ";\n";
     }
     b << "  }\n";
+    return b.str();
+}
+
+// ---------------------------------------------------------------------------
+// SPLIT, column plan: one lane per output cell (lanes walk the kept dim that
+// is stride-1 in the most buffers), workgroup row blockIdx.y takes piece
+// [piece * L, piece * L + L) of the reduce range (row-major over the reduced
+// dims) and folds it in ascending order into its partial, written to
+// partials[piece][cell] (cell = the row-major index over the kept dims).
+// ---------------------------------------------------------------------------
+std::string Gen::gen_split_cols() {
+    std::vector<int> rd, kd;
+    for (int d = 0; d < rank; ++d) ((k.rdims >> d) & 1u ? rd : kd).push_back(d);
+    int64_t C = 1, N = 1;
+    for (int d : kd) C *= k.domain[d];
+    for (int d : rd) N *= k.domain[d];
+    const int64_t P = k.split_pieces, L = (N + P - 1) / P;
+    std::vector<int> order;  // other kept dims, the lane dim innermost
+    for (int d : kd)
+        if (d != k.lane_dim) order.push_back(d);
+    if (k.lane_dim >= 0) order.push_back(k.lane_dim);
+    std::ostringstream b;
+    b << "  const " << I << " cell = (" << I << ")blockIdx.x * 256 + threadIdx.x;\n";
+    b << "  const " << I << " piece = blockIdx.y;\n";
+    b << "  if (cell >= " << lit(C) << ") return;\n";
+    std::vector<std::string> idx(rank);
+    {
+        std::string rem = "cell";
+        for (size_t j = order.size(); j-- > 0;) {
+            int d = order[j];
+            b << "  const " << I << " i" << d << " = " << (j ? fmt("%s %% %s", rem.c_str(), lit(k.domain[d]).c_str()) : rem)
+              << ";\n";
+            idx[d] = fmt("i%d", d);
+            if (j) {
+                b << "  const " << I << " q" << d << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
+                rem = fmt("q%d", d);
+            }
+        }
+    }
+    std::string lin = "0";  // row-major cell index over the kept dims
+    {
+        int64_t m = 1;
+        for (size_t j = kd.size(); j-- > 0;) {
+            lin += fmt(" + i%d * %s", kd[j], lit(m).c_str());
+            m *= k.domain[kd[j]];
+        }
+    }
+    int root = -1;
+    for (size_t e = 0; e < k.ex.size(); ++e)
+        if (live[e] && (k.ex[e].op == RV_SUM || k.ex[e].op == RV_MAX)) root = (int)e;
+    if (root < 0) fail(RV_E_INVALID, "internal: SPLIT kernel without a reduce");
+    const Ex& R = k.ex[root];
+    const RedType rt(R.op, R.dtype);
+    b << "  " << rt.t << " acc = " << rt.ident << ";\n";
+    b << "  const " << I << " n0 = piece * " << lit(L) << ";\n";
+    const bool ragged = N % L != 0;
+    b << "#pragma unroll 4\n";
+    b << "  for (" << I << " j = 0; j < " << lit(L) << "; ++j) {\n";
+    b << "    const " << I << " n = n0 + j;\n";
+    if (ragged) b << "    if (n >= " << lit(N) << ") break;\n";
+    {
+        std::string rem = "n";
+        for (size_t j = rd.size(); j-- > 0;) {
+            int d = rd[j];
+            b << "    const " << I << " i" << d << " = " << (j ? fmt("%s %% %s", rem.c_str(), lit(k.domain[d]).c_str()) : rem)
+              << ";\n";
+            idx[d] = fmt("i%d", d);
+            if (j) {
+                b << "    const " << I << " r" << d << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
+                rem = fmt("r%d", d);
+            }
+        }
+    }
+    std::vector<char> done(k.ex.size(), 0);
+    done[root] = 1;
+    scalar(b, R.a, idx, "    ", "", done);
+    b << "    acc = " << rt.fold("acc", fmt("s%d", R.a)) << ";\n";
+    b << "  }\n";
+    const int pdt = rt.isdbl ? RV_F64 : (rt.isint ? RV_I32 : RV_F32);
+    const std::string Pp = pname(Loc{2, k.partials_region}, pdt, true);
+    b << "  " << Pp << "[piece * " << lit(C) << " + (" << lin << ")] = " << (rt.isint ? "(int)acc" : "acc") << ";\n";
+    return b.str();
+}
+
+// ---------------------------------------------------------------------------
+// FOLD of a split reduce: each output cell's P partials in piece order, the
+// reduce's one rounding to its dtype, then the region's elementwise tail at
+// that cell and its stores. Cell-major partials: a wave per cell (lane l
+// folds pieces l, l + 64, ... in order, then a butterfly); piece-major: a
+// lane per cell.
+// ---------------------------------------------------------------------------
+std::string Gen::gen_fold_cells() {
+    const int64_t C = k.split_cells, P = k.split_pieces;
+    const RedType rt(k.red_op, k.red_dtype);
+    const int pdt = rt.isdbl ? RV_F64 : (rt.isint ? RV_I32 : RV_F32);
+    const std::string Pp = pname(Loc{2, k.fold_src_region}, pdt, false);
+    auto rd_part = [&](const std::string& i) {
+        return rt.isint && rt.sum ? "(unsigned)" + Pp + "[" + i + "]" : Pp + "[" + i + "]";
+    };
+    std::ostringstream b;
+    std::string ind = "  ";
+    if (k.split_cell_major) {
+        b << "  const " << I << " cell = (" << I << ")blockIdx.x * 4 + (threadIdx.x >> 6);\n";
+        b << "  const int lane = threadIdx.x & 63;\n";
+        b << "  if (cell >= " << lit(C) << ") return;\n";
+        b << "  " << rt.t << " acc = " << rt.ident << ";\n";
+        b << "  for (" << I << " q = lane; q < " << lit(P) << "; q += 64) acc = "
+          << rt.fold("acc", rd_part("cell * " + lit(P) + " + q")) << ";\n";
+        if (rt.isdbl || rt.isint) {
+            b << "  for (int o = 32; o >= 1; o >>= 1) { const " << rt.t << " w = __shfl_xor(acc, o, 64); acc = "
+              << rt.fold("acc", "w") << "; }\n";
+        } else {
+            b << "  acc = rv_group_" << (rt.sum ? "sum" : "max") << "<64>(acc);\n";
+        }
+        b << "  if (lane != 0) return;\n";
+    } else {
+        b << "  const " << I << " cell = (" << I << ")blockIdx.x * 256 + threadIdx.x;\n";
+        b << "  if (cell >= " << lit(C) << ") return;\n";
+        b << "  " << rt.t << " acc = " << rt.ident << ";\n";
+        b << "#pragma unroll 8\n";
+        b << "  for (" << I << " q = 0; q < " << lit(P) << "; ++q) acc = "
+          << rt.fold("acc", rd_part("q * " + lit(C) + " + cell")) << ";\n";
+    }
+    // the cell's domain indices (row-major over the output shape)
+    std::vector<std::string> idx(rank);
+    {
+        std::string rem = "cell";
+        for (int d = rank; d-- > 0;) {
+            b << ind << "const " << I << " i" << d << " = " << (d ? fmt("%s %% %s", rem.c_str(), lit(k.domain[d]).c_str()) : rem)
+              << ";\n";
+            idx[d] = fmt("i%d", d);
+            if (d) {
+                b << ind << "const " << I << " q" << d << " = " << rem << " / " << lit(k.domain[d]) << ";\n";
+                rem = fmt("q%d", d);
+            }
+        }
+    }
+    std::vector<char> done(k.ex.size(), 0);
+    for (size_t e = 0; e < k.ex.size(); ++e)
+        if (k.ex[e].op == EX_FOLD_ACC) {
+            b << ind << "const " << vt(k.ex[e].dtype) << " s" << e << " = " << rt.result(k.ex[e].dtype, "acc") << ";\n";
+            done[e] = 1;
+        }
+    for (const Store& st_ : k.stores) {
+        scalar(b, st_.ex, idx, ind, "", done);
+        std::string P2 = pname(st_.loc, st_.dtype, true);
+        b << ind << P2 << "[" << addr(st_.v, idx) << "] = " << sv(st_.dtype, fmt("s%d", st_.ex)) << ";\n";
+    }
     return b.str();
 }
 
@@ -2020,7 +2202,8 @@ std::string Gen::gen() {
         case KClass::EW: body = k.plan == "tiled2d" ? gen_tiled() : gen_rowmajor(); break;
         case KClass::ROW: body = k.plan == "row_stream" ? gen_row_stream() : gen_row(); break;
         case KClass::REDUCE: body = gen_cells(); break;
-        case KClass::FOLD: body = gen_fold(); break;
+        case KClass::FOLD: body = k.plan == "fold_cells" ? gen_fold_cells() : gen_fold(); break;
+        case KClass::SPLIT: body = k.plan == "split_row" ? gen_row_stream() : gen_split_cols(); break;
         case KClass::ATTN: {
             std::string s = gen_attn();
             size_t at = s.find("@@BODY@@");

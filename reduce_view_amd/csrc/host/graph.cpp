@@ -266,6 +266,7 @@ const char* kclass_name(KClass k) {
         case KClass::FOLD: return "FOLD";
         case KClass::ATTN: return "ATTN";
         case KClass::SCATTER: return "SCATTER";
+        case KClass::SPLIT: return "SPLIT";
     }
     return "?";
 }

@@ -53,8 +53,9 @@ bool pure_broadcast(const rv_view& v, const Shape& src_shape, std::vector<int>* 
 // ---------------------------------------------------------------------------
 // kernels (schedule.cpp / lower.cpp / codegen.cpp)
 // ---------------------------------------------------------------------------
-enum class KClass { EW, ROW, REDUCE, MFMA, FOLD, ATTN, SCATTER };
+enum class KClass { EW, ROW, REDUCE, MFMA, FOLD, ATTN, SCATTER, SPLIT };
 constexpr int EX_MFMA_ACC = 1000;  // Ex op: the contraction's accumulator at (m, n)
+constexpr int EX_FOLD_ACC = 1001;  // Ex op: a split reduce's folded partials at this cell
 const char* kclass_name(KClass k);
 
 // Where a value lives in memory.
@@ -120,9 +121,19 @@ struct Kernel {
     bool mfma_partial = false;  // epilogue reduced to one partial per workgroup
     int partials_region = -1;   // workspace region of the partials
     int64_t n_partials = 0;
-    // FOLD
+    // FOLD ("fold": the contraction's partials to one scalar; "fold_cells":
+    // a split reduce's partials, fold_count per output cell, then the
+    // region's elementwise tail on the folded value)
     int fold_src_region = -1;
     int64_t fold_count = 0;
+    // SPLIT: the reduce (op, dtype) whose partials it writes; the matching
+    // FOLD carries the same. split_pieces partials per output cell, laid out
+    // cell-major ([cell][piece], split_row) or piece-major ([piece][cell],
+    // split_cols) in region partials_region.
+    int red_op = 0, red_dtype = 0;
+    int64_t split_pieces = 0, split_cells = 0;
+    bool split_cell_major = false;
+    int64_t split_depth = 0;  // additions any term passes through in the partial
     // ATTN (leaves q, k, v; domain (H, Tq, D); Tk = leaves[1].v.shape[1])
     double attn_scale = 0.0;
     bool attn_causal = false;

@@ -124,7 +124,7 @@ static void prove_in_bounds(const Program& p, const Kernel& k) {
                                          k.name.c_str(), (long long)lo, (long long)hi, (long long)cap(L, dtype)));
     };
     for (auto& L : k.leaves)
-        if (!L.zero && !(k.cls == KClass::FOLD)) check(L.v, L.loc, L.dtype, "a load");
+        if (!L.zero && k.plan != "fold") check(L.v, L.loc, L.dtype, "a load");
     // a gathered read adds index * g_stride for an index in [g_lo, g_hi)
     for (auto& e : k.ex) {
         if (e.op != RV_GATHER || e.g_hi <= e.g_lo || k.leaves[e.leaf].zero) continue;
@@ -141,7 +141,7 @@ static void prove_in_bounds(const Program& p, const Kernel& k) {
     if (k.cls == KClass::SCATTER && cap(k.sc_out, k.sc_dtype) < numel(k.sc_out_shape))
         fail(RV_E_OUT_OF_BOUNDS, fmt("the scatter target of kernel %s is smaller than its shape", k.name.c_str()));
     for (auto& s : k.stores)
-        if (k.cls != KClass::FOLD && !(k.cls == KClass::MFMA && k.mfma_partial)) check(s.v, s.loc, s.dtype, "a store");
+        if (k.plan != "fold" && !(k.cls == KClass::MFMA && k.mfma_partial)) check(s.v, s.loc, s.dtype, "a store");
 }
 
 // MFMA tile plan. Operand A walks (m, k) with n-stride 0 and B walks (n, k)
@@ -188,12 +188,133 @@ std::vector<std::pair<int, int>> online_softmax_pairs(const Kernel& k) {
     return out;
 }
 
-static void plan_kernel(Program& p, Kernel& k, int64_t prev_partials) {
+// Accumulator width of a reduce: float64 totals for float64, 4 bytes else
+// (float32 for float32 and the half widths, a wrapping uint32 / int32 for
+// the ints).
+static int acc_bytes(int dtype) { return dtype == RV_F64 ? 8 : 4; }
+
+// SPLIT plans. The reduce range (the reduced dims, row-major) is cut into P
+// pieces; workgroup (cells, piece) folds its piece in a fixed order.
+//   split_row  (a reduced dim is the one stride-1 in the most buffers): 256
+//              lanes per (cell, piece), each lane VW consecutive elements of
+//              U vectors per chunk of 256 * VW * U, chunks of a piece in
+//              order; lane totals through a butterfly and the 4 waves in
+//              order. Partials [cell][piece].
+//   split_cols (a kept dim is): one lane per cell, 256 cells per
+//              workgroup, the lane walks its piece's L reduce positions in
+//              order. Partials [piece][cell].
+// About 2048 workgroups (8 per CU), so each CU keeps enough loads in flight.
+static void plan_split(Program& p, Kernel& k) {
+    char buf[512];
+    merge_dims(k);
+    const int rank = (int)k.domain.size();
+    int64_t C = 1, N = 1;
+    for (int d = 0; d < rank; ++d) ((k.rdims >> d) & 1u ? N : C) *= k.domain[d];
+    int best = -1, best_votes = -1;
+    for (int d = 0; d < rank; ++d) {
+        int votes = 0;
+        for (auto& L : k.leaves)
+            if (!L.zero && L.v.strides[d] == 1) ++votes;
+        if (votes > best_votes || (votes == best_votes && d > best)) {
+            best = d;
+            best_votes = votes;
+        }
+    }
+    const int64_t target = env_int("RV_SPLIT_WORKGROUPS", 2048);
+    const bool rowp = (k.rdims >> best) & 1u;
+    int64_t P, depth;
+    if (rowp) {
+        k.plan = "split_row";
+        bool two = true, eight = false;
+        for (auto& L : k.leaves)
+            if (!L.zero) {
+                bool along = false;
+                for (int d = 0; d < rank; ++d)
+                    if (((k.rdims >> d) & 1u) && L.v.strides[d] != 0) along = true;
+                if (along && dtype_size(L.dtype) != 2) two = false;
+                if (dtype_size(L.dtype) == 8) eight = true;
+            }
+        const int VW = two ? 8 : eight ? 2 : 4, U = 4, T = 256;
+        const int64_t CH = (int64_t)T * VW * U, NCH = (N + CH - 1) / CH;
+        P = std::max<int64_t>(1, std::min<int64_t>(NCH, (target + C - 1) / C));
+        const int64_t CPP = (NCH + P - 1) / P;
+        P = (NCH + CPP - 1) / CPP;
+        k.grid[0] = (unsigned)(C * P);
+        k.block[0] = T;
+        k.lane_dim = best;
+        k.lds = 4 * 8;
+        // a lane's CPP * VW * U terms in order, 6 butterfly levels, 3 waves
+        depth = CPP * VW * U - 1 + 6 + 3;
+        snprintf(buf, sizeof buf, "\"threads_per_row\":%d,\"rows_per_block\":1,\"vec\":%d,\"unroll\":%d,"
+                 "\"chunks\":%lld,\"row_len\":%lld,\"rows\":%lld,\"online\":[],\"pieces\":%lld,"
+                 "\"chunks_per_piece\":%lld,\"partials\":\"cell-major\",\"sum_depth\":%lld",
+                 T, VW, U, (long long)NCH, (long long)N, (long long)C, (long long)P, (long long)CPP,
+                 (long long)depth);
+        k.split_cell_major = true;
+    } else {
+        k.plan = "split_cols";
+        const int64_t CT = (C + 255) / 256;
+        P = std::max<int64_t>(1, std::min<int64_t>(N / 16, (target + CT - 1) / CT));
+        const int64_t L = (N + P - 1) / P;
+        P = (N + L - 1) / L;
+        k.grid[0] = (unsigned)CT;
+        k.grid[1] = (unsigned)P;
+        k.block[0] = 256;
+        k.lane_dim = best;
+        depth = L - 1;
+        snprintf(buf, sizeof buf, "\"cells\":%lld,\"lane_dim\":%d,\"reduce_len\":%lld,\"pieces\":%lld,"
+                 "\"piece_len\":%lld,\"partials\":\"piece-major\",\"sum_depth\":%lld",
+                 (long long)C, best, (long long)N, (long long)P, (long long)L, (long long)depth);
+        k.split_cell_major = false;
+    }
+    k.split_pieces = P;
+    k.split_cells = C;
+    k.split_depth = depth;
+    k.plan_json = buf;
+    p.regions[k.partials_region].bytes = (size_t)(C * P * acc_bytes(k.red_dtype));
+}
+
+// FOLD of a split reduce: per output cell, the P partials in piece order
+// (cell-major partials: a wave per cell, lanes take pieces l, l + 64, ... in
+// order, then a butterfly; piece-major: a lane per cell), then the region's
+// elementwise tail.
+static void plan_fold_cells(Kernel& k, const Kernel& sp) {
+    char buf[512];
+    k.plan = "fold_cells";
+    k.fold_count = sp.split_pieces;
+    k.split_pieces = sp.split_pieces;
+    k.split_cells = sp.split_cells;
+    k.split_cell_major = sp.split_cell_major;
+    const int64_t C = sp.split_cells, P = sp.split_pieces;
+    int64_t depth;
+    if (k.split_cell_major) {
+        k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>((C + 3) / 4, 1 << 20));
+        depth = sp.split_depth + (P + 63) / 64 - 1 + 6 + 1;
+    } else {
+        k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>((C + 255) / 256, 1 << 20));
+        depth = sp.split_depth + P;
+    }
+    k.block[0] = 256;
+    k.lane_dim = (int)k.domain.size() - 1;
+    snprintf(buf, sizeof buf, "\"partials\":%lld,\"cells\":%lld,\"src_region\":%d,\"layout\":\"%s\",\"sum_depth\":%lld",
+             (long long)P, (long long)C, k.fold_src_region, k.split_cell_major ? "cell-major" : "piece-major",
+             (long long)depth);
+    k.plan_json = buf;
+}
+
+static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
     char buf[512];
     switch (k.cls) {
+        case KClass::SPLIT:
+            plan_split(p, k);
+            return;
         case KClass::FOLD: {
+            if (prev && prev->cls == KClass::SPLIT) {
+                plan_fold_cells(k, *prev);
+                return;
+            }
             k.plan = "fold";
-            k.fold_count = prev_partials;
+            k.fold_count = prev ? prev->n_partials : 0;
             k.grid[0] = 1;
             k.block[0] = 256;
             k.lds = 256 * 4;
@@ -587,11 +708,7 @@ void lower(Program& p) {
     }
     p.outputs.clear();
     for (int o : g.outputs) p.outputs.push_back(OutputInfo{g.nodes[o].shape, g.nodes[o].dtype, o});
-    int64_t prev_partials = 0;
-    for (auto& k : p.kernels) {
-        plan_kernel(p, k, prev_partials);
-        if (k.cls == KClass::MFMA) prev_partials = k.n_partials;
-    }
+    for (size_t i = 0; i < p.kernels.size(); ++i) plan_kernel(p, p.kernels[i], i ? &p.kernels[i - 1] : nullptr);
     size_t off = 0;
     for (auto& r : p.regions) {
         r.offset = off;

@@ -75,9 +75,10 @@ struct Builder {
     Ctx& c;
     Kernel& k;
     int root;
-    enum Mode { EW, ROW, REDUCE, MFMA } mode;
+    enum Mode { EW, ROW, REDUCE, MFMA, FOLDK } mode;
     uint32_t rmask = 0;  // ROW/REDUCE: reduced domain dims
     int mfma_y = -1;     // MFMA: the contraction node
+    int fold_red = -1;   // FOLDK: the split reduce whose folded partials this kernel reads
     std::map<std::pair<int, Map>, int> memo;
     std::map<std::pair<std::string, int>, int> leaf_memo;
 
@@ -222,6 +223,14 @@ struct Builder {
             Ex e;
             e.op = EX_MFMA_ACC;
             e.dtype = RV_F32;
+            e.node = i;
+            return add(e);
+        }
+        if (mode == FOLDK) {
+            if (i != fold_red) throw 1;
+            Ex e;
+            e.op = EX_FOLD_ACC;
+            e.dtype = nd.dtype;
             e.node = i;
             return add(e);
         }
@@ -473,6 +482,109 @@ static bool try_reduce_cells(Ctx& c, int root, Kernel& k) {
     }
     k = kk;
     return true;
+}
+
+// ---- split reduce ----------------------------------------------------------
+//
+// limn README, "Backends": a long reduce over few cells splits into strided
+// partial totals and a fold. A region whose only reduce has few output cells
+// for the length it reduces would leave most of the chip idle as one
+// workgroup per row (ROW) or one lane per cell (REDUCE); it becomes a SPLIT
+// kernel (each workgroup folds one piece of the reduce range for its cells,
+// in a fixed order, into a partials region) and a FOLD kernel (the pieces of
+// each cell folded in piece order, then the region's elementwise tail on the
+// result). No atomics: two runs give the same bits.
+
+// Output cells and reduce length of reduce node r.
+static void reduce_extent(const Ctx& c, int r, int64_t* cells, int64_t* len) {
+    const Node& R = c.g.nodes[r];
+    const Node& in = c.g.nodes[R.src[0]];
+    *cells = numel(R.shape);
+    *len = *cells > 0 ? numel(in.shape) / *cells : 0;
+}
+
+// Whether a reduce of `cells` outputs over `len` terms each pays for the
+// extra launch: enough work in total, and the one-kernel plans would start
+// fewer workgroups than the chip has CUs (256): ROW takes a workgroup per
+// row (long rows), REDUCE a workgroup per 256 cells.
+static bool split_pays(const Ctx& c, int r, int64_t cells, int64_t len) {
+    if (cells <= 0 || len < 512 || cells * len < ((int64_t)1 << 20)) return false;
+    uint32_t rm;
+    const Node& R = c.g.nodes[r];
+    const bool rowlike = row_space(R, c.g.nodes[R.src[0]], &rm) && len >= kRowMinLen;
+    if (rowlike) return cells < 256 && len >= 8192;
+    return (cells + 255) / 256 < 256;
+}
+
+static bool try_split(Ctx& c, int root, std::vector<Kernel>& out) {
+    if (env_int("RV_SPLIT", 1) == 0) return false;
+    std::set<int> red;
+    reach_reduces(c, root, red, false);
+    const Node& rn = c.g.nodes[root];
+    int r;
+    if (is_reduce(rn.op)) {
+        if (!red.empty()) return false;
+        r = root;
+    } else {
+        if (red.size() != 1) return false;
+        r = *red.begin();
+        if (rn.shape != c.g.nodes[r].shape) return false;
+    }
+    const Node& R = c.g.nodes[r];
+    const Node& in = c.g.nodes[R.src[0]];
+    int64_t cells, len;
+    reduce_extent(c, r, &cells, &len);
+    if (!split_pays(c, r, cells, len)) return false;
+    uint32_t rmask = 0;
+    for (size_t d = 0; d < in.shape.size(); ++d)
+        if (((R.axes >> d) & 1u) && in.shape[d] != 1) rmask |= 1u << d;
+    if (!rmask) return false;
+    Kernel kp;
+    kp.cls = KClass::SPLIT;
+    kp.domain = in.shape;
+    kp.rdims = rmask;
+    kp.red_op = R.op;
+    kp.red_dtype = R.dtype;
+    Kernel kf;
+    kf.cls = KClass::FOLD;
+    kf.domain = R.shape;
+    kf.red_op = R.op;
+    kf.red_dtype = R.dtype;
+    try {
+        Builder b{c, kp, r, Builder::REDUCE};
+        b.rmask = rmask;
+        b.build(r, root_map(R.shape, rmask));
+        Builder bf{c, kf, root, Builder::FOLDK};
+        bf.fold_red = r;
+        int e = bf.build(root, identity(R.shape.size()));
+        add_stores(c, kf, root, e, identity(R.shape.size()));
+    } catch (int) {
+        return false;
+    }
+    kp.partials_region = (int)c.p.regions.size();
+    c.p.regions.push_back(Region{});  // sized when the pieces are planned
+    kf.fold_src_region = kp.partials_region;
+    out.push_back(kp);
+    out.push_back(kf);
+    return true;
+}
+
+// A region with several reduces over few long rows (a softmax of a handful
+// of 1 MB rows): the ROW plan would run one workgroup per row. Its topmost
+// reduces are cut instead, so each becomes a split reduce.
+static bool cut_for_split(Ctx& c, int root, std::set<int>* top) {
+    if (env_int("RV_SPLIT", 1) == 0) return false;
+    std::set<int> red;
+    reach_reduces(c, root, red, false);
+    if (is_reduce(c.g.nodes[root].op)) red.insert(root);
+    if (red.size() < 2) return false;
+    for (int r : red) {
+        int64_t cells, len;
+        reduce_extent(c, r, &cells, &len);
+        if (!split_pays(c, r, cells, len)) return false;
+    }
+    reach_reduces(c, root, *top, true);
+    return !top->empty();
 }
 
 // ---- MFMA ----------------------------------------------------------------
@@ -871,6 +983,11 @@ void schedule(Program& p) {
                 kernels.push_back(k);
             } else if (try_mfma(c, i, mk, preg)) {
                 for (auto& x : mk) kernels.push_back(x);
+            } else if (try_split(c, i, mk)) {
+                for (auto& x : mk) kernels.push_back(x);
+            } else if (std::set<int> top; cut_for_split(c, i, &top)) {
+                for (int t : top) need[t] = 1;
+                again = true;
             } else if (try_row(c, i, k)) {
                 kernels.push_back(k);
             } else if (try_reduce_cells(c, i, k)) {

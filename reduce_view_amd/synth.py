@@ -554,3 +554,46 @@ def inputs_cast(n: int = 1024, seed: int = 10) -> dict:
                 mb = to_bf16_bits(mags.astype(np.float32))
                 out[f"x_{dt}"] = np.concatenate([wb, bits.astype(np.uint16), mb])[:n]
     return out
+
+
+def reduce(shape, axes, op: str = "SUM", dtype: str = "f32", permute=None, pad=None) -> Spec:
+    """y = SUM or MAX of x over ``axes`` (kept with size 1). ``permute`` and
+    ``pad`` (per-dim (before, after)) first view x through those movements,
+    in that order."""
+    g = Spec(f"{op.lower()}_{'x'.join(map(str, shape))}_{''.join(map(str, axes))}")
+    x = g.buffer("x", tuple(shape), dtype)
+    mv = []
+    if permute is not None:
+        mv.append(("permute", tuple(permute)))
+    if pad is not None:
+        mv.append(("pad", tuple(tuple(p) for p in pad)))
+    v = g.view(x, *mv) if mv else x
+    g.output(g.sum(v, axes) if op == "SUM" else g.max(v, axes))
+    return g
+
+
+def mean_rows(rows: int, n: int) -> Spec:
+    """Row means SUM(x) * (1/n) of a (rows, n) float32 x."""
+    g = Spec(f"mean_rows_{rows}x{n}")
+    x = g.buffer("x", (rows, n), "f32")
+    g.output(g.mul(g.sum(x, (1,)), g.const(1.0 / n, (rows, 1), "f32")))
+    return g
+
+
+def inputs_reduce(shape, dtype: str = "f32", seed: int = 11, dist: str = "normal") -> dict:
+    """x of ``shape``: floats N(0, 1) (``dist="normal"``) or U(-1, 1)
+    (``"uniform"``), drawn in float64 and rounded once into the dtype
+    (bfloat16 through float32); ints uniform over the whole range."""
+    rng = np.random.default_rng(seed)
+    shape = tuple(shape)
+    if dtype in ("i32", "i16", "i8"):
+        lo, hi = _INT_RANGE[dtype]
+        store = {"i32": np.int32, "i16": np.int16, "i8": np.int8}[dtype]
+        return {"x": rng.integers(lo, hi, size=shape, endpoint=True, dtype=np.int64).astype(store)}
+    x = rng.standard_normal(shape) if dist == "normal" else rng.uniform(-1.0, 1.0, shape)
+    if dtype == "f64":
+        return {"x": x}
+    if dtype == "f16":
+        return {"x": x.astype(np.float16)}
+    x32 = _f32(x)
+    return {"x": to_bf16_bits(x32) if dtype == "bf16" else x32}

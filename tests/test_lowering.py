@@ -447,3 +447,34 @@ def test_random_graphs_plan_matches_oracle(seed):
     d, got = _interp(g, inputs)
     ref = oracle.run(g, inputs)
     assert got[0].tobytes() == ref[0].tobytes()
+
+
+@pytest.mark.parametrize("spec,classes", [
+    (synth.reduce((1 << 24,), (0,)), ["SPLIT", "FOLD"]),
+    (synth.reduce((16384, 4096), (0,)), ["SPLIT", "FOLD"]),
+    (synth.reduce((6, 520, 700), (0, 2)), ["SPLIT", "FOLD"]),
+    (synth.mean_rows(8, 500000), ["SPLIT", "FOLD"]),
+    (synth.softmax(4, 300000), ["SPLIT", "FOLD", "SPLIT", "FOLD", "EW"]),
+    (synth.softmax(16384, 4096), ["ROW"]),               # many rows: one ROW kernel
+    (synth.softmax(256, 262144), ["ROW"]),               # a row per CU: the streaming ROW plan
+    (synth.reduce((64, 64, 64), (2,)), ["REDUCE"]),      # little work: one launch
+    (synth.reduce((1000, 100), (0,)), ["REDUCE"]),
+])
+def test_split_reduce_classes(spec, classes):
+    """A long reduce over few output cells splits into partials and a fold
+    (limn README, "Backends"); reduces with enough cells, or too little
+    work to pay for a second launch, keep one kernel."""
+    d = rv.compile_spec(spec).describe()
+    assert [k["class"] for k in d["kernels"]] == classes
+    for a, b in zip(d["kernels"], d["kernels"][1:]):
+        if a["class"] == "SPLIT":
+            assert b["class"] == "FOLD" and b["plan"] == "fold_cells"
+            pa, pb = a["plan_detail"], b["plan_detail"]
+            assert pb["partials"] == pa["pieces"] and pb["sum_depth"] > pa["sum_depth"]
+            assert a["grid"][0] * a["grid"][1] >= 256  # the chip is filled
+
+
+def test_split_off_switch(monkeypatch):
+    monkeypatch.setenv("RV_SPLIT", "0")
+    d = rv.compile_spec(synth.reduce((1 << 24,), (0,))).describe()
+    assert [k["plan"] for k in d["kernels"]] == ["row_stream"]
