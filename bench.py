@@ -257,6 +257,19 @@ def _report(err, bound):
 def _parity(name, inp, got, ref, extra):
     """max |err|, max bound, max err/bound of one program's GPU output
     against the oracle's, with the bound each workload's arithmetic implies."""
+    if name == "gemm_relu2_sum":
+        # y on sampled rows against the oracle's rows; S against the oracle's
+        # stored value for these inputs (its fp64 tolerance ingredients too)
+        rows, y_gpu, y_ref, gold, depth = extra
+        a = np.abs(_bf16_f64(inp["A"][rows]))
+        b = np.abs(_bf16_f64(inp["B"]))
+        dy = 4 * _gamma(4095) * (a @ b)
+        ry = _report(np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64)), dy)
+        ds = gold["propagated_y_term"] + U * gold["sum_q"] + 4 * _gamma(depth) * gold["sum_q"] + U * abs(gold["S"])
+        rs = _report(np.array([abs(float(got.ravel()[0]) - gold["S"])]), np.array([ds]))
+        rs["y_sampled_rows"] = ry
+        rs["S_bound_depth"] = depth
+        return rs
     g = got.astype(np.float64)
     r = ref.astype(np.float64)
     if name == "matmul64":
@@ -296,19 +309,6 @@ def _parity(name, inp, got, ref, extra):
         ulpb = 2.0 ** (np.floor(np.log2(np.maximum(m, 2.0 ** -133))) - 7)
         bound = prod * (0.5 * 4 * _gamma(n - 1) * ssq / (ssq + n * 1e-5) + 4 * U) + 2 * U * np.abs(y32) + ulpb + 2.0 ** -133
         return _report(np.abs(gg - rb), bound)
-    if name == "gemm_relu2_sum":
-        # y on sampled rows against the oracle's rows; S against the oracle's
-        # stored value for these inputs (its fp64 tolerance ingredients too)
-        rows, y_gpu, y_ref, gold, depth = extra
-        a = np.abs(_bf16_f64(inp["A"][rows]))
-        b = np.abs(_bf16_f64(inp["B"]))
-        dy = 4 * _gamma(4095) * (a @ b)
-        ry = _report(np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64)), dy)
-        ds = gold["propagated_y_term"] + U * gold["sum_q"] + 4 * _gamma(depth) * gold["sum_q"] + U * abs(gold["S"])
-        rs = _report(np.array([abs(float(got.ravel()[0]) - gold["S"])]), np.array([ds]))
-        rs["y_sampled_rows"] = ry
-        rs["S_bound_depth"] = depth
-        return rs
     raise KeyError(name)
 
 
