@@ -48,39 +48,16 @@ def check_device_header(verbose: bool = False) -> None:
         f.write("struct E { __device__ float operator()(float a, int, int) const { return a; }\n"
                 "  __device__ void store(int, int, float) const {} };\n"
                 "#define K extern \"C\" __global__ void __launch_bounds__(256)\n"
-                "K chk1(const unsigned short* a, const unsigned short* b, float* p) {\n"
-                "  rv_gemm_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
-                "K chk2(const unsigned short* a, const unsigned short* b, float* p) {\n"
-                "  rv_gemm_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
-                "K chk3(const unsigned short* a, const unsigned short* b, float* p) {\n"
-                "  rv_gemm256_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
-                "K chk4(const unsigned short* a, const unsigned short* b, float* p) {\n"
-                "  rv_gemm256_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
                 "K chk5(float* p) { p[0] = rv_fold_sum(p, 16); }\n"
-                "extern \"C\" __global__ void __launch_bounds__(512) chk6(const unsigned short* a, "
-                "const unsigned short* b, float* p) {\n"
-                "  rv_gemm_lds_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
-                "extern \"C\" __global__ void __launch_bounds__(512) chk7(const unsigned short* a, "
-                "const unsigned short* b, float* p) {\n"
-                "  rv_gemm_lds_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
-                "extern \"C\" __global__ void __launch_bounds__(512) chk8(const unsigned short* a, "
-                "const unsigned short* b, float* p) {\n"
-                "  rv_gemm_lds4_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
-                "extern \"C\" __global__ void __launch_bounds__(512) chk9(const unsigned short* a, "
-                "const unsigned short* b, float* p) {\n"
-                "  rv_gemm_lds4_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
-                "extern \"C\" __global__ void __launch_bounds__(512) chk10(const unsigned short* a, "
-                "const unsigned short* b, float* p) {\n"
-                "  rv_gemm_pp_bf16<true, 1, E>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
-                "extern \"C\" __global__ void __launch_bounds__(512) chk11(const unsigned short* a, "
-                "const unsigned short* b, float* p) {\n"
-                "  rv_gemm_pp_bf16<false, 0, E, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
                 "chk15(const unsigned short* a, const unsigned short* b, float* p) {\n"
                 "  rv_gemm_w4_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
                 "chk16(const unsigned short* a, const unsigned short* b, float* p) {\n"
                 "  rv_gemm_w4_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
+                "chk17(const unsigned short* a, const unsigned short* b, float* p) {\n"
+                "  rv_gemm_w4_bf16<true, 1, E, 2, 1, 5, true>(a, b, 0, 4104, 0, 4104, 4100, 4104, 4128, E{}, p, 4100, 4097); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(512) chk12(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
                 "float* l) { rv_attn_fwd_bf16<32, true, false>(q, k, v, o, l, 1000, 1000, 0.25f); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(512) chk13(const unsigned short* q, const unsigned short* k, const unsigned short* v, "

@@ -280,8 +280,7 @@ struct Gen {
     std::string header() {
         // a 256 x 256 contraction tile on 4 waves keeps 256 accumulators per
         // lane: one wave per SIMD, so the whole register file is the wave's
-        const bool one_wave =
-            k.cls == KClass::MFMA && ((k.plan == "gemm_lds" && k.block[0] == 256) || k.plan == "gemm_w4");
+        const bool one_wave = k.cls == KClass::MFMA;
         return "extern \"C\" __global__ void __launch_bounds__(" + std::to_string(k.block[0]) + ") " +
                (one_wave ? "__attribute__((amdgpu_waves_per_eu(1, 1))) " : "") + k.name + "(" + signature() + ")";
     }
@@ -1640,9 +1639,11 @@ std::string Gen::gen_split_cols() {
 // ---------------------------------------------------------------------------
 // FOLD of a split reduce: each output cell's P partials in piece order, the
 // reduce's one rounding to its dtype, then the region's elementwise tail at
-// that cell and its stores. Cell-major partials: a wave per cell (lane l
-// folds pieces l, l + 64, ... in order, then a butterfly); piece-major: a
-// lane per cell.
+// that cell and its stores. Cell-major partials: a workgroup per cell, lane t
+// folds pieces t, t + 256, ... in order, then a butterfly and the 4 waves in
+// order. Piece-major: 64 cells per workgroup, wave w folds the w-th quarter
+// of the pieces in order for its lane's cell, then the 4 waves in order.
+// Loads go 8 at a time ahead of their adds.
 // ---------------------------------------------------------------------------
 std::string Gen::gen_fold_cells() {
     const int64_t C = k.split_cells, P = k.split_pieces;
@@ -1654,27 +1655,42 @@ std::string Gen::gen_fold_cells() {
     };
     std::ostringstream b;
     std::string ind = "  ";
+    // acc folds pieces q in [q0, q1) stepping by `step`, partial index `pidx`
+    auto fold_range = [&](const std::string& q0, const std::string& q1, const std::string& step,
+                          const std::string& pidx) {
+        b << "  for (" << I << " q = " << q0 << "; q < " << q1 << "; q += 8 * " << step << ") {\n";
+        b << "    " << rt.t << " v[8];\n";
+        b << "#pragma unroll\n    for (int u = 0; u < 8; ++u) {\n";
+        b << "      const " << I << " qq = q + u * " << step << ";\n";
+        b << "      v[u] = qq < " << q1 << " ? " << rd_part(pidx) << " : " << rt.ident << ";\n    }\n";
+        b << "#pragma unroll\n    for (int u = 0; u < 8; ++u) acc = " << rt.fold("acc", "v[u]") << ";\n  }\n";
+    };
+    b << "  __shared__ " << (rt.isdbl ? "double" : rt.isint ? (rt.sum ? "unsigned" : "int") : "float") << " wv[4][64];\n";
+    b << "  const int t = threadIdx.x, lane = t & 63, w = t >> 6;\n";
+    b << "  " << rt.t << " acc = " << rt.ident << ";\n";
     if (k.split_cell_major) {
-        b << "  const " << I << " cell = (" << I << ")blockIdx.x * 4 + (threadIdx.x >> 6);\n";
-        b << "  const int lane = threadIdx.x & 63;\n";
-        b << "  if (cell >= " << lit(C) << ") return;\n";
-        b << "  " << rt.t << " acc = " << rt.ident << ";\n";
-        b << "  for (" << I << " q = lane; q < " << lit(P) << "; q += 64) acc = "
-          << rt.fold("acc", rd_part("cell * " + lit(P) + " + q")) << ";\n";
-        if (rt.isdbl || rt.isint) {
-            b << "  for (int o = 32; o >= 1; o >>= 1) { const " << rt.t << " w = __shfl_xor(acc, o, 64); acc = "
-              << rt.fold("acc", "w") << "; }\n";
-        } else {
+        b << "  const " << I << " cell = blockIdx.x;\n";
+        fold_range("(" + I + ")t", lit(P), "256", "cell * " + lit(P) + " + qq");
+        if (rt.isdbl || rt.isint)
+            b << "  for (int o = 32; o >= 1; o >>= 1) { const " << rt.t << " x = __shfl_xor(acc, o, 64); acc = "
+              << rt.fold("acc", "x") << "; }\n";
+        else
             b << "  acc = rv_group_" << (rt.sum ? "sum" : "max") << "<64>(acc);\n";
-        }
-        b << "  if (lane != 0) return;\n";
+        b << "  if (lane == 0) wv[w][0] = acc;\n  __syncthreads();\n";
+        b << "  if (t != 0) return;\n";
+        b << "  acc = wv[0][0];\n";
+        for (int j = 1; j < 4; ++j) b << "  acc = " << rt.fold("acc", fmt("wv[%d][0]", j)) << ";\n";
     } else {
-        b << "  const " << I << " cell = (" << I << ")blockIdx.x * 256 + threadIdx.x;\n";
-        b << "  if (cell >= " << lit(C) << ") return;\n";
-        b << "  " << rt.t << " acc = " << rt.ident << ";\n";
-        b << "#pragma unroll 8\n";
-        b << "  for (" << I << " q = 0; q < " << lit(P) << "; ++q) acc = "
-          << rt.fold("acc", rd_part("q * " + lit(C) + " + cell")) << ";\n";
+        const int64_t Q = (P + 3) / 4;
+        b << "  const " << I << " cell = (" << I << ")blockIdx.x * 64 + lane;\n";
+        b << "  const " << I << " cq = cell < " << lit(C) << " ? cell : " << lit(C - 1) << ";\n";
+        b << "  const " << I << " pc0 = (" << I << ")w * " << lit(Q) << ", pc1 = pc0 + " << lit(Q) << " < " << lit(P)
+          << " ? pc0 + " << lit(Q) << " : " << lit(P) << ";\n";
+        fold_range("pc0", "pc1", "1", "qq * " + lit(C) + " + cq");
+        b << "  wv[w][lane] = acc;\n  __syncthreads();\n";
+        b << "  if (w != 0 || cell >= " << lit(C) << ") return;\n";
+        b << "  acc = wv[0][lane];\n";
+        for (int j = 1; j < 4; ++j) b << "  acc = " << rt.fold("acc", fmt("wv[%d][lane]", j)) << ";\n";
     }
     // the cell's domain indices (row-major over the output shape)
     std::vector<std::string> idx(rank);
@@ -2155,25 +2171,11 @@ std::string Gen::gen_gemm() {
     b << "  const " << sname << " epi{";
     for (size_t i = 0; i < params.size(); ++i) b << (i ? ", " : "") << "p" << i;
     b << "};\n";
-    const int64_t M = k.domain[0], N = k.domain[1], K = k.domain[2];
+    const int64_t Mt = k.domain[0], Nt = k.domain[1];
+    const int64_t M = k.mfma_ext[0], N = k.mfma_ext[1], K = k.mfma_ext[2];
+    const bool ragged = M % 256 || N % 256 || M != Mt || N != Nt;
     const int64_t lda = A.v.strides[0];
     const int64_t ldb = kn ? B.v.strides[2] : B.v.strides[1];
-    const char* fn = k.plan == "gemm_lds"    ? "rv_gemm_lds_bf16<"
-                     : k.plan == "gemm_pp"   ? "rv_gemm_pp_bf16<"
-                     : k.plan == "gemm_lds4" ? "rv_gemm_lds4_bf16<"
-                     : k.plan == "gemm_w4"   ? "rv_gemm_w4_bf16<"
-                     : k.plan == "gemm256"   ? "rv_gemm256_bf16<"
-                                             : "rv_gemm_bf16<";
-    int TM = 2, TN = 4;
-    {
-        size_t at = k.plan_json.find("\"wave_tiles\":[");
-        if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"wave_tiles\":[%d,%d]", &TM, &TN);
-    }
-    int KH = 2;
-    {
-        size_t at = k.plan_json.find("\"phase_k16\":");
-        if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"phase_k16\":%d", &KH);
-    }
     int NV0 = 8, PIN = 1, NS = 4;
     {
         size_t st = k.plan_json.find("\"stages\":");
@@ -2183,14 +2185,10 @@ std::string Gen::gen_gemm() {
         size_t il = k.plan_json.find("\"interleave\":");
         if (il != std::string::npos) sscanf(k.plan_json.c_str() + il, "\"interleave\":%d", &PIN);
     }
-    const std::string targs = k.plan == "gemm_lds"  ? fmt(", %s, %d, %d", sname.c_str(), TM, TN)
-                              : k.plan == "gemm_pp" ? fmt(", %s, %d", sname.c_str(), KH)
-                              : k.plan == "gemm_w4"
-                                  ? fmt(", %s, %d, %d, %d", sname.c_str(), NV0, PIN, NS)
-                                                    : "";
-    b << "  " << fn << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << targs << ">(" << pa << ", " << pb
-      << ", " << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", "
-      << K << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ");\n";
+    b << "  rv_gemm_w4_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ", " << sname << ", "
+      << NV0 << ", " << PIN << ", " << NS << ", " << (ragged ? "true" : "false") << ">(" << pa << ", " << pb << ", "
+      << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", " << K
+      << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ", " << Mt << ", " << Nt << ");\n";
     return f.str() + "@@BODY@@" + b.str();
 }
 

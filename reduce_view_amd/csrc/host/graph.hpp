@@ -119,6 +119,11 @@ struct Kernel {
     // MFMA pattern (a, b: leaves of the bf16 operands; y: the contraction)
     int mfma_a = -1, mfma_b = -1, mfma_y = -1;
     bool mfma_partial = false;  // epilogue reduced to one partial per workgroup
+    // extents the operand buffers hold (M, N >= 256, K a multiple of 32;
+    // an operand that cannot be read in place is first copied, zero-padded,
+    // into workspace); the domain keeps the output's (M, N, K)
+    int64_t mfma_ext[3] = {0, 0, 0};
+    bool mfma_copied[2] = {false, false};
     int partials_region = -1;   // workspace region of the partials
     int64_t n_partials = 0;
     // FOLD ("fold": the contraction's partials to one scalar; "fold_cells":
@@ -227,6 +232,5 @@ std::vector<Loc> kernel_param_locs(const Program& p, const Kernel& k);
 std::vector<std::pair<int, int>> online_softmax_pairs(const Kernel& k);
 // Value `e` of kernel `k` is the same at every index along domain dim `d`.
 bool ex_invariant(const Kernel& k, int e, int d);
-bool mfma_supported(const Shape& dom, const rv_view& a, const rv_view& b, std::string* why);
 
 }  // namespace rv

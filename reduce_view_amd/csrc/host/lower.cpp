@@ -144,27 +144,6 @@ static void prove_in_bounds(const Program& p, const Kernel& k) {
         if (k.plan != "fold" && !(k.cls == KClass::MFMA && k.mfma_partial)) check(s.v, s.loc, s.dtype, "a store");
 }
 
-// MFMA tile plan. Operand A walks (m, k) with n-stride 0 and B walks (n, k)
-// with m-stride 0 over the (M, N, K) domain; A must be k-contiguous and B
-// either n-contiguous ([k][n] storage) or k-contiguous ([n][k] storage).
-bool mfma_supported(const Shape& dom, const rv_view& a, const rv_view& b, std::string* why) {
-    const int BM = 128, BN = 128, BK = 64;
-    auto no = [&](const char* w) {
-        if (why) *why = w;
-        return false;
-    };
-    if (dom.size() != 3) return no("rank");
-    if (dom[0] % BM || dom[1] % BN || dom[2] % BK) return no("M, N, K must be multiples of 128, 128, 64");
-    if (a.strides[2] != 1) return no("A must be contiguous along k");
-    if (a.offset % 8 || a.strides[0] % 8) return no("A rows must be 16-byte aligned");
-    bool kn = b.strides[1] == 1, nk = b.strides[2] == 1;
-    if (!kn && !nk) return no("B must be contiguous along n or k");
-    if (b.offset % 8) return no("B must be 16-byte aligned");
-    if (kn && b.strides[2] % 8) return no("B rows must be 16-byte aligned");
-    if (!kn && b.strides[1] % 8) return no("B rows must be 16-byte aligned");
-    return true;
-}
-
 std::vector<std::pair<int, int>> online_softmax_pairs(const Kernel& k) {
     std::vector<std::pair<int, int>> out;
     auto f32 = [&](int e) { return e >= 0 && k.ex[e].dtype == RV_F32; };
@@ -279,6 +258,7 @@ static void plan_split(Program& p, Kernel& k) {
 // order, then a butterfly; piece-major: a lane per cell), then the region's
 // elementwise tail.
 static void plan_fold_cells(Kernel& k, const Kernel& sp) {
+    if (sp.split_cells >= ((int64_t)1 << 31)) fail(RV_E_INVALID, "internal: split reduce with 2^31 cells");
     char buf[512];
     k.plan = "fold_cells";
     k.fold_count = sp.split_pieces;
@@ -287,13 +267,14 @@ static void plan_fold_cells(Kernel& k, const Kernel& sp) {
     k.split_cell_major = sp.split_cell_major;
     const int64_t C = sp.split_cells, P = sp.split_pieces;
     int64_t depth;
-    if (k.split_cell_major) {
-        k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>((C + 3) / 4, 1 << 20));
-        depth = sp.split_depth + (P + 63) / 64 - 1 + 6 + 1;
-    } else {
-        k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>((C + 255) / 256, 1 << 20));
-        depth = sp.split_depth + P;
+    if (k.split_cell_major) {  // a workgroup per cell: lane runs, butterfly, 4 waves
+        k.grid[0] = (unsigned)C;
+        depth = sp.split_depth + (P + 255) / 256 + 6 + 3;
+    } else {  // 64 cells per workgroup: a quarter of the pieces per wave, 4 waves
+        k.grid[0] = (unsigned)((C + 63) / 64);
+        depth = sp.split_depth + (P + 3) / 4 + 3;
     }
+    k.lds = 4 * 64 * 8;
     k.block[0] = 256;
     k.lane_dim = (int)k.domain.size() - 1;
     snprintf(buf, sizeof buf, "\"partials\":%lld,\"cells\":%lld,\"src_region\":%d,\"layout\":\"%s\",\"sum_depth\":%lld",
@@ -364,85 +345,44 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
             return;
         }
         case KClass::MFMA: {
-            int64_t M = k.domain[0], N = k.domain[1];
-            // 256 x 256 tiles when the shape allows, operands copied straight
-            // into LDS: 4 waves of 128 x 128 with their own software pipeline
-            // ("w4", the default), 8 waves of 64 x 128 ("lds"; "lds4" with four
-            // 32-deep stages; "pp" with the two wave groups in ping-pong), or
-            // register-staged copies and 4 waves ("reg"); otherwise 128 x 128
-            // register-staged tiles.
-            const bool big = M % 256 == 0 && N % 256 == 0;
-            const char* kind = getenv("RV_GEMM_KERNEL");
-            std::string kd = kind && *kind ? kind : "w4";
-            if (!big) kd = "reg128";
-            // the four-wave kernel keeps each lane's part of a copy address as
-            // a 32-bit byte offset (up to 15 A rows, or B rows): row pitches
-            // of 2^27 elements or more take the 8-wave kernel
-            {
-                const rv_view& av = k.leaves[k.mfma_a].v;
-                const rv_view& bv = k.leaves[k.mfma_b].v;
-                const int64_t ldb_ = bv.strides[1] == 1 ? bv.strides[2] : bv.strides[1];
-                if (kd == "w4" && (av.strides[0] >= ((int64_t)1 << 27) || ldb_ >= ((int64_t)1 << 27))) kd = "lds";
-            }
-            int BM = 128, BN = 128, waves = 4;
-            int TM = 2, TN = 4;
+            // 256 x 256 tiles, 4 waves of 128 x 128, operands copied straight
+            // into LDS (kernels/rv_device.hpp, rv_gemm_w4_bf16), over the
+            // extents the operand buffers hold (a ragged last tile is shifted
+            // back inside them); LDS stages (5: copies four k-tiles ahead;
+            // 4), copies issued in a k-tile's first k16 step (the rest after
+            // its barrier), and the MFMA/LDS/copy interleaving (1 pinned, 2
+            // reads front-loaded, 0 free). Measured on cold operands: 5
+            // stages with 2 or 3 early copies take 15% fewer cycles than 4
+            // stages with all 8 early.
+            const int64_t M = k.domain[0], N = k.domain[1];
+            const int64_t Me = k.mfma_ext[0], Ne = k.mfma_ext[1], Ke = k.mfma_ext[2];
             int nv0 = 2, pin = 1, stages = 5;
-            if (kd == "w4") {
-                k.plan = "gemm_w4";
-                BM = BN = 256;
-                TM = TN = 4;
-                // LDS stages (5: copies four k-tiles ahead; 4), copies issued in a
-                // k-tile's first k16 step (the rest after its barrier), and the
-                // MFMA/LDS/copy interleaving (1 pinned, 2 reads front-loaded, 0 free).
-                // Measured on cold operands: 5 stages with 2 or 3 early copies
-                // take 15% fewer cycles than 4 stages with all 8 early.
-                const char* sp = getenv("RV_GEMM_W4_SPLIT");
-                if (sp && *sp) nv0 = std::max(0, std::min(8, atoi(sp)));
-                const char* pn = getenv("RV_GEMM_W4_PIN");
-                if (pn && *pn) pin = std::max(0, std::min(2, atoi(pn)));
-                const char* st = getenv("RV_GEMM_W4_STAGES");
-                if (st && (atoi(st) == 4 || atoi(st) == 5)) stages = atoi(st);
-                k.lds = 2 * stages * 256 * 32 * 2;
-            } else if (kd == "lds" || kd == "lds4" || kd == "pp") {
-                k.plan = kd == "lds" ? "gemm_lds" : kd == "pp" ? "gemm_pp" : "gemm_lds4";
-                BM = BN = 256;
-                waves = 8;
-                k.lds = 4 * 256 * 64 * 2 + 32;
-                const char* wv = getenv("RV_GEMM_WAVES");
-                if (wv && std::string(wv) == "4x2") TM = 4, TN = 2;
-                if (wv && std::string(wv) == "4x4") TM = 4, TN = 4, waves = 4;
-                if (kd == "pp") TM = 2, TN = 4, waves = 8;
-            } else if (kd == "reg") {
-                k.plan = "gemm256";
-                BM = BN = 256;
-                k.lds = 2 * (BM * 72 + BN * 72) * 2 + 16;
-            } else {
-                k.plan = "gemm";
-                k.lds = 2 * (BM * 72 + BN * 72) * 2 + 16;
-            }
-            k.grid[0] = (unsigned)((M / BM) * (N / BN));
-            k.block[0] = 64 * waves;
+            const char* sp = getenv("RV_GEMM_W4_SPLIT");
+            if (sp && *sp) nv0 = std::max(0, std::min(8, atoi(sp)));
+            const char* pn = getenv("RV_GEMM_W4_PIN");
+            if (pn && *pn) pin = std::max(0, std::min(2, atoi(pn)));
+            const char* st = getenv("RV_GEMM_W4_STAGES");
+            if (st && (atoi(st) == 4 || atoi(st) == 5)) stages = atoi(st);
+            k.plan = "gemm_w4";
+            k.lds = 2 * stages * 256 * 32 * 2;
+            const int64_t tiles = ((Me + 255) / 256) * ((Ne + 255) / 256);
+            if (tiles >= ((int64_t)1 << 31)) fail(RV_E_UNSUPPORTED_LAYOUT, "contraction of 2^31 or more output tiles");
+            k.grid[0] = (unsigned)tiles;
+            k.block[0] = 256;
             k.n_partials = k.grid[0];
-            bool kn = k.leaves[k.mfma_b].v.strides[1] == 1;
-            // per lane: (BM * BN / threads) values summed in order, 6
-            // butterfly levels, (waves - 1) cross-wave additions; the fold
-            // adds its own depth
-            const int per_lane = BM * BN / (64 * waves);
+            const bool kn = k.leaves[k.mfma_b].v.strides[1] == 1;
+            const bool ragged = Me % 256 || Ne % 256 || Me != M || Ne != N;
+            // per lane: 256 values summed in order, 6 butterfly levels, 3
+            // cross-wave additions; the fold adds its own depth
             snprintf(buf, sizeof buf,
-                     "\"tile\":[%d,%d,64],\"waves\":%d,\"wave_tiles\":[%d,%d],\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
-                     "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d",
-                     BM, BN, waves, TM, TN, kn ? "kn" : "nk", per_lane - 1 + 6 + waves - 1);
+                     "\"tile\":[256,256,32],\"waves\":4,\"wave_tiles\":[4,4],\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
+                     "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d,\"stages\":%d,"
+                     "\"copies_first_step\":%d,\"interleave\":%d,\"extent\":[%lld,%lld,%lld],\"ragged\":%s,"
+                     "\"copied\":{\"A\":%s,\"B\":%s},\"operand_leaves\":[%d,%d]",
+                     kn ? "kn" : "nk", 256 - 1 + 6 + 3, stages, nv0, pin, (long long)Me, (long long)Ne, (long long)Ke,
+                     ragged ? "true" : "false", k.mfma_copied[0] ? "true" : "false", k.mfma_copied[1] ? "true" : "false",
+                     k.mfma_a, k.mfma_b);
             k.plan_json = buf;
-            if (k.plan == "gemm_w4") {
-                snprintf(buf, sizeof buf, ",\"stages\":%d,\"copies_first_step\":%d,\"interleave\":%d", stages, nv0,
-                         pin);
-                k.plan_json += buf;
-            }
-            if (k.plan == "gemm_pp") {
-                // k16 steps per ping-pong phase (2, or 1 with RV_GEMM_KH=1)
-                const char* kh = getenv("RV_GEMM_KH");
-                k.plan_json += (kh && atoi(kh) == 1) ? ",\"phase_k16\":1" : ",\"phase_k16\":2";
-            }
             if (k.mfma_partial) {
                 p.regions[k.partials_region].bytes = (size_t)k.n_partials * 4;
                 k.stores[0].loc = Loc{2, k.partials_region};

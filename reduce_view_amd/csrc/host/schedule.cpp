@@ -616,6 +616,121 @@ static bool is_contraction(Ctx& c, int y) {
     return bf16_operand(c, mul.src[0]) >= 0 && bf16_operand(c, mul.src[1]) >= 0;
 }
 
+// A zero-padded copy of a contraction operand into workspace region `region`:
+// `rows` x `cols` row-major, cell (r, c) = the operand at domain dims
+// (dr, dc) = (r, c) when r < R and c < C (and inside its View's mask), else
+// zero. An elementwise kernel of its own (a transposing copy when the
+// operand is stored the other way round).
+static Kernel operand_copy(const Leaf& L, int dr, int dc, int64_t rows, int64_t cols, int64_t R, int64_t C,
+                           int region) {
+    Kernel kc;
+    kc.cls = KClass::EW;
+    kc.domain = Shape{rows, cols};
+    Leaf s;
+    s.loc = L.loc;
+    s.dtype = RV_BF16;
+    s.zero = L.zero;
+    s.v.ndim = 2;
+    s.v.offset = L.v.offset;
+    const int ds[2] = {dr, dc};
+    const int64_t ext[2] = {R, C}, sz[2] = {rows, cols};
+    for (int j = 0; j < 2; ++j) {
+        s.v.shape[j] = sz[j];
+        s.v.strides[j] = L.v.strides[ds[j]];
+        s.v.mask_lo[j] = std::max<int64_t>(0, L.v.mask_lo[ds[j]]);
+        s.v.mask_hi[j] = std::min<int64_t>(ext[j], L.v.mask_hi[ds[j]]);
+        if (s.v.mask_hi[j] <= s.v.mask_lo[j]) s.zero = true;
+    }
+    kc.leaves.push_back(s);
+    Ex e;
+    e.op = RV_BUFFER;
+    e.dtype = RV_BF16;
+    e.leaf = 0;
+    kc.ex.push_back(e);
+    Store st;
+    st.ex = 0;
+    st.loc = Loc{2, region};
+    st.dtype = RV_BF16;
+    st.v = view_contiguous(Shape{rows, cols});
+    kc.stores.push_back(st);
+    return kc;
+}
+
+// Operands of the contraction kernel. One is read in place when the kernel's
+// copies can address it directly: contiguous along k (A; B along k or n),
+// 16-byte aligned rows, unmasked, at least one 256-wide tile along its
+// output dim, and K a multiple of the 32-deep k-tile. Any other operand
+// (ragged K, a narrow M or N, a transposed, padded, windowed or unaligned
+// View) is first copied into workspace, zero-padded to those extents, by an
+// elementwise kernel; every bf16 contraction thus runs on the matrix cores.
+// The copies are appended to `out`; the kernel's leaves and extents are
+// rewritten to read them.
+static void mfma_operands(Ctx& c, Kernel& k, std::vector<Kernel>& out) {
+    const int64_t M = k.domain[0], N = k.domain[1], K = k.domain[2];
+    const int64_t Kp = (K + 31) / 32 * 32, lim = (int64_t)1 << 27;
+    const Leaf A = k.leaves[k.mfma_a], B = k.leaves[k.mfma_b];
+    auto unmasked = [](const Leaf& L) {
+        if (L.zero) return false;
+        for (int d = 0; d < 3; ++d)
+            if (L.v.mask_lo[d] != 0 || L.v.mask_hi[d] != L.v.shape[d]) return false;
+        return true;
+    };
+    const rv_view &a = A.v, &b = B.v;
+    const bool a_direct = K % 32 == 0 && unmasked(A) && M >= 256 && a.strides[2] == 1 && a.offset % 8 == 0 &&
+                          a.strides[0] % 8 == 0 && a.strides[0] < lim;
+    const bool kn = b.strides[1] == 1;
+    const bool b_direct = K % 32 == 0 && unmasked(B) && N >= 256 && b.offset % 8 == 0 &&
+                          (kn ? (b.strides[2] % 8 == 0 && N % 8 == 0 && b.strides[2] < lim)
+                              : (b.strides[2] == 1 && b.strides[1] % 8 == 0 && b.strides[1] < lim));
+    int64_t Me = M, Ne = N;
+    auto region = [&](int64_t elems) {
+        c.p.regions.push_back(Region{0, (size_t)elems * 2});
+        return (int)c.p.regions.size() - 1;
+    };
+    if (!a_direct) {
+        Me = std::max<int64_t>(M, 256);
+        const int r = region(Me * Kp);
+        out.push_back(operand_copy(A, 0, 2, Me, Kp, M, K, r));
+        Leaf L;
+        L.loc = Loc{2, r};
+        L.dtype = RV_BF16;
+        L.v = view_contiguous(k.domain);
+        L.v.strides[0] = Kp;
+        L.v.strides[1] = 0;
+        L.v.strides[2] = 1;
+        k.leaves.push_back(L);
+        k.mfma_a = (int)k.leaves.size() - 1;
+        k.mfma_copied[0] = true;
+    }
+    if (!b_direct) {
+        Leaf L;
+        L.dtype = RV_BF16;
+        L.v = view_contiguous(k.domain);
+        L.v.strides[0] = 0;
+        if (b.strides[2] == 1) {  // stored along k: copied as [n][k]
+            Ne = std::max<int64_t>(N, 256);
+            const int r = region(Ne * Kp);
+            out.push_back(operand_copy(B, 1, 2, Ne, Kp, N, K, r));
+            L.loc = Loc{2, r};
+            L.v.strides[1] = Kp;
+            L.v.strides[2] = 1;
+        } else {  // as [k][n], rows padded to whole 16-byte chunks
+            Ne = std::max<int64_t>((N + 7) / 8 * 8, 256);
+            const int r = region(Kp * Ne);
+            out.push_back(operand_copy(B, 2, 1, Kp, Ne, K, N, r));
+            L.loc = Loc{2, r};
+            L.v.strides[1] = 1;
+            L.v.strides[2] = Ne;
+        }
+        k.leaves.push_back(L);
+        k.mfma_b = (int)k.leaves.size() - 1;
+        k.mfma_copied[1] = true;
+    }
+    k.mfma_ext[0] = Me;
+    k.mfma_ext[1] = Ne;
+    k.mfma_ext[2] = Kp;
+}
+
 static bool try_mfma(Ctx& c, int root, std::vector<Kernel>& out, int& partial_region) {
     const Node& rn = c.g.nodes[root];
     int y = -1, epi_root = -1;
@@ -665,13 +780,13 @@ static bool try_mfma(Ctx& c, int root, std::vector<Kernel>& out, int& partial_re
     // A walks (m, k) with n-stride 0; B walks (n, k) with m-stride 0
     if (sv(la, 1) != 0 || sv(lb, 0) != 0) std::swap(la, lb);
     if (sv(la, 1) != 0 || sv(lb, 0) != 0) return false;
-    for (int l : {la, lb}) {
-        const rv_view& v = k.leaves[l].v;
-        if (k.leaves[l].zero) return false;
-        for (int d = 0; d < 3; ++d)
-            if (v.mask_lo[d] != 0 || v.mask_hi[d] != v.shape[d]) return false;
-    }
-    if (!mfma_supported(k.domain, k.leaves[la].v, k.leaves[lb].v, nullptr)) return false;
+    const int64_t M = k.domain[0], N = k.domain[1], K = k.domain[2];
+    // an empty contraction has nothing for the matrix cores: the other
+    // classes write its identity
+    if (M == 0 || N == 0 || K == 0) return false;
+    if (M >= ((int64_t)1 << 30) || N >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 30))
+        fail(RV_E_UNSUPPORTED_LAYOUT, fmt("contraction (%lld, %lld, %lld): extents of 2^30 or more",
+                                          (long long)M, (long long)N, (long long)K));
     k.mfma_a = la;
     k.mfma_b = lb;
     // the epilogue over (M, N, 1): built on the contraction's output map
@@ -686,6 +801,7 @@ static bool try_mfma(Ctx& c, int root, std::vector<Kernel>& out, int& partial_re
     // epilogue leaves must not walk k
     for (size_t l = 0; l < k.leaves.size(); ++l)
         if ((int)l != la && (int)l != lb && k.leaves[l].v.strides[2] != 0) return false;
+    mfma_operands(c, k, out);
     if (partial) {
         k.mfma_partial = true;
         Store s;

@@ -170,599 +170,15 @@ __device__ __forceinline__ int rv_group_max(int v) {
 // bf16 contraction on MFMA: y[m][n] = sum_k A[m][k] * B[k][n] with a float32
 // accumulator (limn README, "Backends": a nest that reads as a matmul gets a
 // block per output tile, operands staged through on-chip memory and a patch
-// of cells held in registers per thread).
-//
-// Tile 128 x 128 x 64 per workgroup of 4 waves (2 x 2), each wave owning a
-// 64 x 64 patch as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16. A is read as
-// [m][k] rows; B is staged in LDS as [n][k] so that every lane's MFMA operand
-// (8 consecutive k of one row or column) is one 16-byte LDS read. A B stored
-// [k][n] is transposed on its way into LDS: each thread loads 4 k-rows of 8
-// n and writes 8 n-rows of 4 k. Two LDS stages: the global loads of tile
-// k+1 are in flight while tile k is multiplied. Workgroups are remapped so
-// that each of the 8 XCDs runs a contiguous block of output tiles (shared
-// A rows stay in that XCD's L2).
-//
-// Product exactness: a bf16 x bf16 product is exact in float32, so the
-// contraction equals SUM_k CAST(A) * CAST(B) up to the order of the adds.
+// of cells held in registers per thread). A bf16 x bf16 product is exact in
+// float32, so the contraction equals SUM_k CAST(A) * CAST(B) up to the order
+// of the adds.
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(8))) __bf16 rv_bf16x8;
 typedef __attribute__((ext_vector_type(16))) float rv_f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned rv_u32x4;
-
-#define RV_GEMM_BM 128
-#define RV_GEMM_BN 128
-#define RV_GEMM_BK 64
-#define RV_GEMM_LDK 72  // LDS row pitch in bf16 (64 + 8 pad)
-
-template <bool B_KN>
-struct rv_gemm_stage {
-    rv_u32x4 a[4];
-    rv_u32x4 b[4];
-};
-
-// Global -> registers for one k-tile.
-template <bool B_KN>
-__device__ __forceinline__ void rv_gemm_load(rv_gemm_stage<B_KN>& s, const unsigned short* __restrict__ A,
-                                             const unsigned short* __restrict__ B, long long a_base, long long lda,
-                                             long long b_base, long long ldb, int k0, int tid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int v = tid + 256 * i;
-        int row = v >> 3, kc = (v & 7) * 8;
-        s.a[i] = *reinterpret_cast<const rv_u32x4*>(A + a_base + (long long)row * lda + k0 + kc);
-    }
-    if (B_KN) {
-        int nc = (tid & 15) * 8, kg = (tid >> 4) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            s.b[j] = *reinterpret_cast<const rv_u32x4*>(B + b_base + (long long)(k0 + kg + j) * ldb + nc);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int v = tid + 256 * i;
-            int row = v >> 3, kc = (v & 7) * 8;
-            s.b[i] = *reinterpret_cast<const rv_u32x4*>(B + b_base + (long long)row * ldb + k0 + kc);
-        }
-    }
-}
-
-// Registers -> LDS stage (A as [m][k], B as [n][k]).
-template <bool B_KN>
-__device__ __forceinline__ void rv_gemm_store(const rv_gemm_stage<B_KN>& s, unsigned short* As, unsigned short* Bs,
-                                              int tid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int v = tid + 256 * i;
-        int row = v >> 3, kc = (v & 7) * 8;
-        *reinterpret_cast<rv_u32x4*>(As + row * RV_GEMM_LDK + kc) = s.a[i];
-    }
-    if (B_KN) {
-        int nc = (tid & 15) * 8, kg = (tid >> 4) * 4;
-        // s.b[j] holds B[kg + j][nc .. nc + 7]; write column nc + e as the 4
-        // consecutive k values (kg .. kg + 3).
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            int w = e >> 1, hi = e & 1;
-            unsigned k01, k23;
-            unsigned x0 = s.b[0][w], x1 = s.b[1][w], x2 = s.b[2][w], x3 = s.b[3][w];
-            if (hi) {
-                k01 = (x0 >> 16) | (x1 & 0xffff0000u);
-                k23 = (x2 >> 16) | (x3 & 0xffff0000u);
-            } else {
-                k01 = (x0 & 0xffffu) | (x1 << 16);
-                k23 = (x2 & 0xffffu) | (x3 << 16);
-            }
-            typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-            u32x2 pk;
-            pk[0] = k01;
-            pk[1] = k23;
-            *reinterpret_cast<u32x2*>(Bs + (nc + e) * RV_GEMM_LDK + kg) = pk;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int v = tid + 256 * i;
-            int row = v >> 3, kc = (v & 7) * 8;
-            *reinterpret_cast<rv_u32x4*>(Bs + row * RV_GEMM_LDK + kc) = s.b[i];
-        }
-    }
-}
-
-// Runs the contraction for the tile of this workgroup and hands every
-// (m, n, y) to `epi`, which returns the value the epilogue stores or sums.
-// MODE 0: epi.store(m, n, v); MODE 1: per-workgroup sum of v written to
-// partials[blockIdx.x].
-template <bool B_KN, int MODE, class Epi>
-__device__ __forceinline__ void rv_gemm_bf16(const unsigned short* __restrict__ A, const unsigned short* __restrict__ B,
-                                             long long a_off, long long lda, long long b_off, long long ldb, int M,
-                                             int N, int K, const Epi& epi, float* __restrict__ partials) {
-    __shared__ __attribute__((aligned(16))) unsigned short lds_a[2][RV_GEMM_BM * RV_GEMM_LDK];
-    __shared__ __attribute__((aligned(16))) unsigned short lds_b[2][RV_GEMM_BN * RV_GEMM_LDK];
-    __shared__ float lds_red[4];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_n = N / RV_GEMM_BN;
-    const int ntiles = (M / RV_GEMM_BM) * tiles_n;
-    int bid = blockIdx.x;
-    if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous tiles
-    const int m0 = (bid / tiles_n) * RV_GEMM_BM, n0 = (bid % tiles_n) * RV_GEMM_BN;
-    const long long a_base = a_off + (long long)m0 * lda;
-    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
-
-    rv_f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    rv_gemm_stage<B_KN> st;
-    rv_gemm_load<B_KN>(st, A, B, a_base, lda, b_base, ldb, 0, tid);
-    rv_gemm_store<B_KN>(st, lds_a[0], lds_b[0], tid);
-    __syncthreads();
-    const int KT = K / RV_GEMM_BK;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) rv_gemm_load<B_KN>(st, A, B, a_base, lda, b_base, ldb, (kt + 1) * RV_GEMM_BK, tid);
-        const unsigned short* As = lds_a[cur];
-        const unsigned short* Bs = lds_b[cur];
-#pragma unroll
-        for (int kk = 0; kk < RV_GEMM_BK; kk += 16) {
-            rv_bf16x8 af[2], bf[2];
-            const int kq = kk + (lane >> 5) * 8;
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const rv_bf16x8*>(As + (wm * 64 + i * 32 + (lane & 31)) * RV_GEMM_LDK + kq);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bf[j] = *reinterpret_cast<const rv_bf16x8*>(Bs + (wn * 64 + j * 32 + (lane & 31)) * RV_GEMM_LDK + kq);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < KT) rv_gemm_store<B_KN>(st, lds_a[cur ^ 1], lds_b[cur ^ 1], tid);
-        __syncthreads();
-    }
-
-    // epilogue: lane holds y at rows (r/4)*8 + (lane/32)*4 + r%4, column lane%32
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-                const float v = epi(acc[i][j][r], m, n);
-                if (MODE == 0)
-                    epi.store(m, n, v);
-                else
-                    part = part + v;
-            }
-    if (MODE == 1) {
-        part = rv_group_sum<64>(part);
-        if (lane == 0) lds_red[wave] = part;
-        __syncthreads();
-        if (tid == 0) partials[blockIdx.x] = ((lds_red[0] + lds_red[1]) + lds_red[2]) + lds_red[3];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// The large-tile contraction: 256 x 256 x 64 per workgroup of 4 waves (one per
-// SIMD), each wave a 128 x 128 patch as 4 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16 (256 float32 accumulators per lane). Per k16 step a
-// wave reads 8 operand fragments from LDS for 16 MFMAs, half the LDS traffic
-// per MFMA of the 128 x 128 tile. The next k-tile's global loads are issued
-// before the current tile's MFMAs and written to the other LDS stage halfway
-// through them. A 4096^3 problem is 256 workgroups: one per CU; each XCD gets
-// a 4 x 8 block of tiles so its L2 holds the A rows and B columns it shares.
-// ---------------------------------------------------------------------------
-#define RV_G2_BM 256
-#define RV_G2_BN 256
-#define RV_G2_BK 64
-#define RV_G2_LDK 72
-
-template <bool B_KN>
-struct rv_g2_regs {
-    rv_u32x4 a[8];
-    rv_u32x4 b[8];
-};
-
-template <bool B_KN>
-__device__ __forceinline__ void rv_g2_load(rv_g2_regs<B_KN>& s, const unsigned short* __restrict__ A,
-                                           const unsigned short* __restrict__ B, long long a_base, long long lda,
-                                           long long b_base, long long ldb, int k0, int tid) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        int v = tid + 256 * i;
-        int row = v >> 3, kc = (v & 7) * 8;
-        s.a[i] = *reinterpret_cast<const rv_u32x4*>(A + a_base + (long long)row * lda + k0 + kc);
-    }
-    if (B_KN) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            int unit = tid + 256 * u;
-            int nc = (unit & 31) * 8, kg = (unit >> 5) * 4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                s.b[u * 4 + j] = *reinterpret_cast<const rv_u32x4*>(B + b_base + (long long)(k0 + kg + j) * ldb + nc);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int v = tid + 256 * i;
-            int row = v >> 3, kc = (v & 7) * 8;
-            s.b[i] = *reinterpret_cast<const rv_u32x4*>(B + b_base + (long long)row * ldb + k0 + kc);
-        }
-    }
-}
-
-// Writes half `h` (0 or 1) of the prefetched registers into an LDS stage.
-template <bool B_KN>
-__device__ __forceinline__ void rv_g2_store(const rv_g2_regs<B_KN>& s, unsigned short* As, unsigned short* Bs, int tid,
-                                            int h) {
-#pragma unroll
-    for (int i = 4 * h; i < 4 * h + 4; ++i) {
-        int v = tid + 256 * i;
-        int row = v >> 3, kc = (v & 7) * 8;
-        *reinterpret_cast<rv_u32x4*>(As + row * RV_G2_LDK + kc) = s.a[i];
-    }
-    if (B_KN) {
-        const int u = h;
-        int unit = tid + 256 * u;
-        int nc = (unit & 31) * 8, kg = (unit >> 5) * 4;
-        typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            int w = e >> 1;
-            unsigned x0 = s.b[u * 4 + 0][w], x1 = s.b[u * 4 + 1][w], x2 = s.b[u * 4 + 2][w], x3 = s.b[u * 4 + 3][w];
-            u32x2 pk;
-            if (e & 1) {
-                pk[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-                pk[1] = (x2 >> 16) | (x3 & 0xffff0000u);
-            } else {
-                pk[0] = (x0 & 0xffffu) | (x1 << 16);
-                pk[1] = (x2 & 0xffffu) | (x3 << 16);
-            }
-            *reinterpret_cast<u32x2*>(Bs + (nc + e) * RV_G2_LDK + kg) = pk;
-        }
-    } else {
-#pragma unroll
-        for (int i = 4 * h; i < 4 * h + 4; ++i) {
-            int v = tid + 256 * i;
-            int row = v >> 3, kc = (v & 7) * 8;
-            *reinterpret_cast<rv_u32x4*>(Bs + row * RV_G2_LDK + kc) = s.b[i];
-        }
-    }
-}
-
-template <class Acc>
-__device__ __forceinline__ void rv_g2_mma(Acc& acc, const unsigned short* As, const unsigned short* Bs, int wm, int wn,
-                                          int lane, int kk) {
-    rv_bf16x8 af[4], bf[4];
-    const int kq = kk + (lane >> 5) * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const rv_bf16x8*>(As + (wm * 128 + i * 32 + (lane & 31)) * RV_G2_LDK + kq);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const rv_bf16x8*>(Bs + (wn * 128 + j * 32 + (lane & 31)) * RV_G2_LDK + kq);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-}
-
-template <bool B_KN, int MODE, class Epi>
-__device__ __forceinline__ void rv_gemm256_bf16(const unsigned short* __restrict__ A,
-                                                const unsigned short* __restrict__ B, long long a_off, long long lda,
-                                                long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
-                                                float* __restrict__ partials) {
-    __shared__ __attribute__((aligned(16))) unsigned short lds_a[2][RV_G2_BM * RV_G2_LDK];
-    __shared__ __attribute__((aligned(16))) unsigned short lds_b[2][RV_G2_BN * RV_G2_LDK];
-    __shared__ float lds_red[4];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_m = M / RV_G2_BM, tiles_n = N / RV_G2_BN;
-    const int ntiles = tiles_m * tiles_n;
-    int tm, tn;
-    {
-        int bid = blockIdx.x;
-        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
-            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
-            const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
-            tm = group * 4 + (within & 3);
-            tn = within >> 2;
-        } else {
-            tm = bid / tiles_n;
-            tn = bid % tiles_n;
-        }
-    }
-    const int m0 = tm * RV_G2_BM, n0 = tn * RV_G2_BN;
-    const long long a_base = a_off + (long long)m0 * lda;
-    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
-
-    rv_f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    rv_g2_regs<B_KN> st;
-    rv_g2_load<B_KN>(st, A, B, a_base, lda, b_base, ldb, 0, tid);
-    rv_g2_store<B_KN>(st, lds_a[0], lds_b[0], tid, 0);
-    rv_g2_store<B_KN>(st, lds_a[0], lds_b[0], tid, 1);
-    __syncthreads();
-    const int KT = K / RV_G2_BK;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) rv_g2_load<B_KN>(st, A, B, a_base, lda, b_base, ldb, (kt + 1) * RV_G2_BK, tid);
-        rv_g2_mma(acc, lds_a[cur], lds_b[cur], wm, wn, lane, 0);
-        rv_g2_mma(acc, lds_a[cur], lds_b[cur], wm, wn, lane, 16);
-        if (more) rv_g2_store<B_KN>(st, lds_a[cur ^ 1], lds_b[cur ^ 1], tid, 0);
-        rv_g2_mma(acc, lds_a[cur], lds_b[cur], wm, wn, lane, 32);
-        rv_g2_mma(acc, lds_a[cur], lds_b[cur], wm, wn, lane, 48);
-        if (more) rv_g2_store<B_KN>(st, lds_a[cur ^ 1], lds_b[cur ^ 1], tid, 1);
-        __syncthreads();
-    }
-
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n0 + wn * 128 + j * 32 + (lane & 31);
-                const float v = epi(acc[i][j][r], m, n);
-                if (MODE == 0)
-                    epi.store(m, n, v);
-                else
-                    part = part + v;
-            }
-    if (MODE == 1) {
-        part = rv_group_sum<64>(part);
-        if (lane == 0) lds_red[wave] = part;
-        __syncthreads();
-        if (tid == 0) partials[blockIdx.x] = ((lds_red[0] + lds_red[1]) + lds_red[2]) + lds_red[3];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// The direct-to-LDS contraction: 256 x 256 x 64 per workgroup of 8 waves (2
-// per SIMD: one issues MFMAs while the other waits on LDS), each wave a
-// 64 x 128 patch as 2 x 4 tiles of v_mfma_f32_32x32x16_bf16 (128 float32
-// accumulators per lane). Operands go global -> LDS with
-// global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS base +
-// 16 * lane), so no VGPRs stage them and no VALU work rearranges them:
-//   - A (and a [n][k] B) keep [row][k] rows of 128 bytes in LDS with the 16-byte
-//     chunks XOR-swizzled by (row ^ row >> 3) & 7, so 16 consecutive rows
-//     read at one k-chunk hit distinct banks; a fragment is one ds_read_b128.
-//   - a [k][n] B keeps its [k][n] rows of 512 bytes with chunks XOR-swizzled by
-//     4 * (k & 3); a fragment (8 consecutive k of one column) is two
-//     ds_read_b64_tr_b16, the gfx950 transposing LDS read: within each 16-lane
-//     group, lane i receives element i of the 4 x 16 block whose rows the 16
-//     lanes' 8-byte addresses name.
-// Two LDS stages held in four distinct arrays (the k loop is unrolled by two
-// so every access names its array), the next k-tile's copies in flight while
-// the current one is multiplied.
-// ---------------------------------------------------------------------------
-#define RV_G3_BM 256
-#define RV_G3_BN 256
-#define RV_G3_BK 64
-
 typedef __attribute__((address_space(3))) void rv_lds_void;
 typedef __attribute__((ext_vector_type(4))) short rv_s16x4;
-
-__device__ __forceinline__ int rv_g3_swz_rows(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int rv_g3_swz_kn(int kr) { return (kr & 3) * 4; }
-
-// Global -> LDS copy of one k-tile by NW waves: A rows [m0, m0+256) x
-// [k0, k0+64) into As (256 x 64), B into Bs ([k][n] 64 x 256, or [n][k]
-// 256 x 64). Each instruction moves 1 KB (8 A rows, or 2 B k-rows).
-template <bool B_KN, int NW>
-__device__ __forceinline__ void rv_g3_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
-                                           const unsigned short* __restrict__ B, long long a_base, long long lda,
-                                           long long b_base, long long ldb, int k0, int wave, int lane) {
-    constexpr int AR = 256 / NW;  // A rows per wave
-#pragma unroll
-    for (int i = 0; i < AR / 8; ++i) {
-        const int r0 = wave * AR + i * 8;
-        const int r = r0 + (lane >> 3);
-        const int c = (lane & 7) ^ rv_g3_swz_rows(r);
-        __builtin_amdgcn_global_load_lds((const void*)(A + a_base + (long long)r * lda + k0 + c * 8),
-                                         (rv_lds_void*)(As + r0 * 64), 16, 0, 0);
-    }
-    if (B_KN) {
-        constexpr int BR = 64 / NW;  // B k-rows per wave
-#pragma unroll
-        for (int i = 0; i < BR / 2; ++i) {
-            const int kr0 = wave * BR + i * 2;
-            const int kr = kr0 + (lane >> 5);
-            const int c = (lane & 31) ^ rv_g3_swz_kn(kr);
-            __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)(k0 + kr) * ldb + c * 8),
-                                             (rv_lds_void*)(Bs + kr0 * 256), 16, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < AR / 8; ++i) {
-            const int r0 = wave * AR + i * 8;
-            const int r = r0 + (lane >> 3);
-            const int c = (lane & 7) ^ rv_g3_swz_rows(r);
-            __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)r * ldb + k0 + c * 8),
-                                             (rv_lds_void*)(Bs + r0 * 64), 16, 0, 0);
-        }
-    }
-}
-
-__device__ __forceinline__ rv_bf16x8 rv_g3_frag_rows(const unsigned short* S, int r, int c) {
-    return *reinterpret_cast<const rv_bf16x8*>(S + r * 64 + ((c ^ rv_g3_swz_rows(r)) << 3));
-}
-
-// B fragment from a [k][n] tile: 8 consecutive k (kk + (lane >> 5) * 8 ..) of
-// column nt + (lane & 31), as two transposing reads of 4 k each.
-__device__ __forceinline__ rv_bf16x8 rv_g3_frag_kn(const unsigned short* S, int nt, int kk, int lane) {
-    const int g = lane >> 4, j = lane & 15;
-    const int nb = nt + (g & 1) * 16, kb = kk + (g >> 1) * 8;
-    const int n = nb + (j & 3) * 4;
-    rv_s16x4 h[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int kr = kb + half * 4 + (j >> 2);
-        const int off = kr * 256 + (((n >> 3) ^ rv_g3_swz_kn(kr)) << 3) + (n & 7);
-        h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) rv_s16x4*)((__attribute__((address_space(3))) unsigned short*)S + off));
-    }
-    typedef __attribute__((ext_vector_type(8))) short s16x8;
-    s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-    return __builtin_bit_cast(rv_bf16x8, v);
-}
-
-// Operand fragments of one k16 step for a wave owning TM x TN 32 x 32 tiles
-// at rows r0.., cols c0...
-template <bool B_KN, int TM, int TN>
-__device__ __forceinline__ void rv_g3_frags(rv_bf16x8 (&af)[TM], rv_bf16x8 (&bf)[TN], const unsigned short* As,
-                                            const unsigned short* Bs, int r0, int c0, int lane, int kk) {
-    const int c = (kk >> 3) + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = rv_g3_frag_rows(As, r0 + i * 32 + (lane & 31), c);
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-        bf[j] = B_KN ? rv_g3_frag_kn(Bs, c0 + j * 32, kk, lane) : rv_g3_frag_rows(Bs, c0 + j * 32 + (lane & 31), c);
-}
-
-template <int TM, int TN>
-__device__ __forceinline__ void rv_g3_step(rv_f32x16 (&acc)[TM][TN], const rv_bf16x8 (&af)[TM],
-                                           const rv_bf16x8 (&bf)[TN]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-}
-
-// The four k16 steps of a 64-deep k-tile.
-template <bool B_KN, int TM, int TN>
-__device__ __forceinline__ void rv_g3_mma(rv_f32x16 (&acc)[TM][TN], const unsigned short* As, const unsigned short* Bs,
-                                          int r0, int c0, int lane) {
-#pragma unroll
-    for (int kk = 0; kk < RV_G3_BK; kk += 16) {
-        rv_bf16x8 af[TM], bf[TN];
-        rv_g3_frags<B_KN, TM, TN>(af, bf, As, Bs, r0, c0, lane, kk);
-        rv_g3_step<TM, TN>(acc, af, bf);
-    }
-}
-
-template <bool B_KN, int MODE, class Epi, int TM = 2, int TN = 4>
-__device__ __forceinline__ void rv_gemm_lds_bf16(const unsigned short* __restrict__ A,
-                                                 const unsigned short* __restrict__ B, long long a_off, long long lda,
-                                                 long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
-                                                 float* __restrict__ partials) {
-    __shared__ __attribute__((aligned(1024))) unsigned short a0[RV_G3_BM * RV_G3_BK];
-    __shared__ __attribute__((aligned(1024))) unsigned short a1[RV_G3_BM * RV_G3_BK];
-    __shared__ __attribute__((aligned(1024))) unsigned short b0[RV_G3_BN * RV_G3_BK];
-    __shared__ __attribute__((aligned(1024))) unsigned short b1[RV_G3_BN * RV_G3_BK];
-    constexpr int WAVES_N = RV_G3_BN / (32 * TN);
-    constexpr int NW = WAVES_N * (RV_G3_BM / (32 * TM));
-    __shared__ float lds_red[NW];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int r0 = (wave / WAVES_N) * (32 * TM), c0 = (wave % WAVES_N) * (32 * TN);
-    const int tiles_m = M / RV_G3_BM, tiles_n = N / RV_G3_BN;
-    const int ntiles = tiles_m * tiles_n;
-    int tm, tn;
-    {
-        int bid = blockIdx.x;
-        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
-            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
-            const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
-            tm = group * 4 + (within & 3);
-            tn = within >> 2;
-        } else {
-            tm = bid / tiles_n;
-            tn = bid % tiles_n;
-        }
-    }
-    const int m0 = tm * RV_G3_BM, n0 = tn * RV_G3_BN;
-    const long long a_base = a_off + (long long)m0 * lda;
-    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
-
-    rv_f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int KT = K / RV_G3_BK;
-    rv_g3_copy<B_KN, NW>(a0, b0, A, B, a_base, lda, b_base, ldb, 0, wave, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // the scheduling barriers keep the next k-tile's copies at the top of the
-    // step: left alone, the scheduler sinks them below the LDS reads of the
-    // other stage (they cannot alias) and the copy latency is exposed
-    for (int kt = 0; kt < KT; kt += 2) {
-        if (kt + 1 < KT) rv_g3_copy<B_KN, NW>(a1, b1, A, B, a_base, lda, b_base, ldb, (kt + 1) * RV_G3_BK, wave, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        rv_g3_mma<B_KN, TM, TN>(acc, a0, b0, r0, c0, lane);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (kt + 1 >= KT) break;
-        if (kt + 2 < KT) rv_g3_copy<B_KN, NW>(a0, b0, A, B, a_base, lda, b_base, ldb, (kt + 2) * RV_G3_BK, wave, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        rv_g3_mma<B_KN, TM, TN>(acc, a1, b1, r0, c0, lane);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + r0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n0 + c0 + j * 32 + (lane & 31);
-                const float v = epi(acc[i][j][r], m, n);
-                if (MODE == 0)
-                    epi.store(m, n, v);
-                else
-                    part = part + v;
-            }
-    if (MODE == 1) {
-        part = rv_group_sum<64>(part);
-        if (lane == 0) lds_red[wave] = part;
-        __syncthreads();
-        if (tid == 0) {
-            float s = lds_red[0];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) s = s + lds_red[w];
-            partials[blockIdx.x] = s;
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Four-stage variant of the direct-to-LDS contraction: k-tiles of 32, four
-// LDS stages of 32 KB (eight distinct arrays, the k loop unrolled by four),
-// copies issued three k-tiles ahead; a stage is waited for with an exact
-// vmcnt (the copies of the later in-flight stages may stay outstanding).
-// A rows are 64 bytes (4 chunks) with chunks XOR-swizzled by (row >> 2) & 3,
-// so 16 consecutive rows read at one chunk cover all 64 banks.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int rv_g4_swz_rows(int r) { return (r >> 2) & 3; }
 
 // s_waitcnt vmcnt(N) leaving the LDS/export counters free (gfx9 encoding).
 #define RV_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | ((((N) >> 4) & 3) << 14))
@@ -773,163 +189,34 @@ __device__ __forceinline__ int rv_g4_swz_rows(int r) { return (r >> 2) & 3; }
 // are waited for explicitly with RV_WAIT_VM before it.
 #define RV_LDS_BARRIER() rv_lds_barrier()
 
-template <bool B_KN>
-__device__ __forceinline__ void rv_g4_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
-                                           const unsigned short* __restrict__ B, long long a_base, long long lda,
-                                           long long b_base, long long ldb, int k0, int wave, int lane) {
+// One k16 step of a wave's TM x TN tiles of v_mfma_f32_32x32x16_bf16.
+template <int TM, int TN>
+__device__ __forceinline__ void rv_g5_step(rv_f32x16 (&acc)[TM][TN], const rv_bf16x8 (&af)[TM],
+                                           const rv_bf16x8 (&bf)[TN]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r0 = wave * 32 + i * 16;
-        const int r = r0 + (lane >> 2);
-        const int c = (lane & 3) ^ rv_g4_swz_rows(r);
-        __builtin_amdgcn_global_load_lds((const void*)(A + a_base + (long long)r * lda + k0 + c * 8),
-                                         (rv_lds_void*)(As + r0 * 32), 16, 0, 0);
-    }
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        if (B_KN) {
-            const int kr0 = wave * 4 + i * 2;
-            const int kr = kr0 + (lane >> 5);
-            const int c = (lane & 31) ^ rv_g3_swz_kn(kr);
-            __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)(k0 + kr) * ldb + c * 8),
-                                             (rv_lds_void*)(Bs + kr0 * 256), 16, 0, 0);
-        } else {
-            const int r0 = wave * 32 + i * 16;
-            const int r = r0 + (lane >> 2);
-            const int c = (lane & 3) ^ rv_g4_swz_rows(r);
-            __builtin_amdgcn_global_load_lds((const void*)(B + b_base + (long long)r * ldb + k0 + c * 8),
-                                             (rv_lds_void*)(Bs + r0 * 32), 16, 0, 0);
-        }
-    }
-}
-
-__device__ __forceinline__ rv_bf16x8 rv_g4_frag_rows(const unsigned short* S, int r, int c) {
-    return *reinterpret_cast<const rv_bf16x8*>(S + r * 32 + ((c ^ rv_g4_swz_rows(r)) << 3));
-}
-
-template <bool B_KN>
-__device__ __forceinline__ void rv_g4_mma(rv_f32x16 (&acc)[2][4], const unsigned short* As, const unsigned short* Bs,
-                                          int wm, int wn, int lane) {
-#pragma unroll
-    for (int kk = 0; kk < 32; kk += 16) {
-        rv_bf16x8 af[2], bf[4];
-        const int c = (kk >> 3) + (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = rv_g4_frag_rows(As, wm * 64 + i * 32 + (lane & 31), c);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bf[j] = B_KN ? rv_g3_frag_kn(Bs, wn * 128 + j * 32, kk, lane)
-                         : rv_g4_frag_rows(Bs, wn * 128 + j * 32 + (lane & 31), c);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-}
-
-template <bool B_KN, int MODE, class Epi>
-__device__ __forceinline__ void rv_gemm_lds4_bf16(const unsigned short* __restrict__ A,
-                                                  const unsigned short* __restrict__ B, long long a_off, long long lda,
-                                                  long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
-                                                  float* __restrict__ partials) {
-    __shared__ __attribute__((aligned(1024))) unsigned short a0[256 * 32], a1[256 * 32], a2[256 * 32], a3[256 * 32];
-    __shared__ __attribute__((aligned(1024))) unsigned short b0[256 * 32], b1[256 * 32], b2[256 * 32], b3[256 * 32];
-    __shared__ float lds_red[8];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_m = M / 256, tiles_n = N / 256;
-    const int ntiles = tiles_m * tiles_n;
-    int tm, tn;
-    {
-        int bid = blockIdx.x;
-        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
-            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
-            const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
-            tm = group * 4 + (within & 3);
-            tn = within >> 2;
-        } else {
-            tm = bid / tiles_n;
-            tn = bid % tiles_n;
-        }
-    }
-    const int m0 = tm * 256, n0 = tn * 256;
-    const long long a_base = a_off + (long long)m0 * lda;
-    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
-
-    rv_f32x16 acc[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int KT = K / 32;
-    // every step issues exactly one stage of copies (past the end it reloads
-    // the last k-tile into a stage nobody reads), so "this stage is done" is
-    // always vmcnt <= 8: the two later stages' 4 + 4 copies may stay in flight
-#define RV_G4_KT(t) (((t) < KT ? (t) : KT - 1) * 32)
-    rv_g4_copy<B_KN>(a0, b0, A, B, a_base, lda, b_base, ldb, RV_G4_KT(0), wave, lane);
-    rv_g4_copy<B_KN>(a1, b1, A, B, a_base, lda, b_base, ldb, RV_G4_KT(1), wave, lane);
-    rv_g4_copy<B_KN>(a2, b2, A, B, a_base, lda, b_base, ldb, RV_G4_KT(2), wave, lane);
-#define RV_G4_STEP(CA, CB, NA, NB, T)                                                                  \
-    {                                                                                                  \
-        const int t_ = (T);                                                                            \
-        if (t_ >= KT) break;                                                                           \
-        RV_WAIT_VM(8);                                                                                 \
-        RV_LDS_BARRIER();                                                                              \
-        rv_g4_copy<B_KN>(NA, NB, A, B, a_base, lda, b_base, ldb, RV_G4_KT(t_ + 3), wave, lane);        \
-        __builtin_amdgcn_sched_barrier(0);                                                             \
-        rv_g4_mma<B_KN>(acc, CA, CB, wm, wn, lane);                                                   \
-    }
-    for (int kt = 0; kt < KT; kt += 4) {
-        RV_G4_STEP(a0, b0, a3, b3, kt)
-        RV_G4_STEP(a1, b1, a0, b0, kt + 1)
-        RV_G4_STEP(a2, b2, a1, b1, kt + 2)
-        RV_G4_STEP(a3, b3, a2, b2, kt + 3)
-    }
-#undef RV_G4_STEP
-#undef RV_G4_KT
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n0 + wn * 128 + j * 32 + (lane & 31);
-                const float v = epi(acc[i][j][r], m, n);
-                if (MODE == 0)
-                    epi.store(m, n, v);
-                else
-                    part = part + v;
-            }
-    if (MODE == 1) {
-        part = rv_group_sum<64>(part);
-        if (lane == 0) lds_red[wave] = part;
-        __syncthreads();
-        if (tid == 0) {
-            float s = lds_red[0];
-#pragma unroll
-            for (int w = 1; w < 8; ++w) s = s + lds_red[w];
-            partials[blockIdx.x] = s;
-        }
-    }
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// Four-wave variant: 256 x 256 tile, each wave a 128 x 128 patch (4 x 4 tiles
-// of v_mfma_f32_32x32x16_bf16, 256 accumulators per lane: one wave per SIMD,
-// the accumulators fill the accumulation registers). A wave reads 8 KB of
-// fragments for 16 MFMAs per k16 step where the 8-wave kernel reads 6 KB for
-// 8, so the LDS moves 192 KB per 64 of k (64 KB copied in, 128 KB read out)
-// instead of 256 KB, against the same 2048 MFMA cycles per SIMD.
+// The contraction kernel: a 256 x 256 output tile per workgroup of 4 waves,
+// each wave a 128 x 128 patch (4 x 4 tiles of v_mfma_f32_32x32x16_bf16, 256
+// float32 accumulators per lane: one wave per SIMD, the accumulators fill the
+// accumulation registers). Operands go global -> LDS with
+// global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS base
+// + 16 * lane), so no VGPRs stage them:
+//   - A (and a [n][k] B) keep [row][k] rows of 64 bytes per 32-deep k-tile,
+//     the 16-byte chunks XOR-swizzled by (row / 4) % 4, so 16 consecutive
+//     rows read at one chunk cover all 64 banks; a fragment (8 consecutive k
+//     of one row) is one ds_read_b128.
+//   - a [k][n] B keeps its [k][n] rows of 512 bytes with chunks XOR-swizzled
+//     by 4 * (k % 4); a fragment (8 consecutive k of one column) is two
+//     ds_read_b64_tr_b16, the gfx950 transposing LDS read.
+// A wave reads 8 KB of fragments for 16 MFMAs per k16 step, so the LDS moves
+// 192 KB per 64 of k (64 KB copied in, 128 KB read out) against 2048 MFMA
+// cycles per SIMD.
 // With one wave per SIMD nothing else hides latency, so the wave pipelines
 // itself: k-tiles of 32 in NS LDS stages of 32 KB (five fill the LDS; the
 // copies run NS - 1 k-tiles ahead), and the fragments double buffered in
@@ -941,6 +228,13 @@ __device__ __forceinline__ void rv_gemm_lds4_bf16(const unsigned short* __restri
 // reading the next stage's x and issuing the other copies.
 // sched_group_barrier pins one LDS read and one copy after each MFMA so the
 // reads hide under the matrix work.
+//
+// Extents: M, N (each >= 256) and K (a multiple of 32) are the extents the
+// operand buffers hold; Mt <= M and Nt <= N are the output's. With RAGGED, a
+// last tile that would run past M (or N) starts at M - 256 instead, so every
+// copy stays inside the operands and the loop has no edge cases; its cells
+// below the nominal tile start belong to the tile before it and, like cells
+// at or beyond Mt (Nt), are left out of the epilogue.
 // ---------------------------------------------------------------------------
 // Per-lane byte offsets of the fragment reads inside one stage (loop
 // invariant; the stage's array base, the 32-row tile i (2048 bytes) and, for a
@@ -1069,11 +363,11 @@ __device__ __forceinline__ void rv_g5_keep(rv_f32x16 (&acc)[4][4]) {
         for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
-template <bool B_KN, int MODE, class Epi, int NV0 = 8, int PIN = 1, int NS = 4>
+template <bool B_KN, int MODE, class Epi, int NV0 = 8, int PIN = 1, int NS = 4, bool RAGGED = false>
 __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict__ A,
                                                 const unsigned short* __restrict__ B, long long a_off, long long lda,
                                                 long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
-                                                float* __restrict__ partials) {
+                                                float* __restrict__ partials, int Mt = 0, int Nt = 0) {
     static_assert(NS == 4 || NS == 5, "four or five LDS stages");
     // NS stages of 32 KB (five fill the 160 KB of LDS; the fifth pair is a
     // single element when unused)
@@ -1087,7 +381,7 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
     // are then wave-uniform without a readfirstlane per copy
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_m = M / 256, tiles_n = N / 256;
+    const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
     const int ntiles = tiles_m * tiles_n;
     int tm, tn;
     {
@@ -1102,7 +396,9 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
             tn = bid % tiles_n;
         }
     }
-    const int m0 = tm * 256, n0 = tn * 256;
+    // a ragged last tile is shifted back to end at the operands' last row
+    const int mlo = tm * 256, nlo = tn * 256;
+    const int m0 = RAGGED ? min(mlo, M - 256) : mlo, n0 = RAGGED ? min(nlo, N - 256) : nlo;
     const long long a_base = a_off + (long long)m0 * lda;
     const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
     // lane parts of the copy addresses (bytes): A row lane / 4 of 16, chunk
@@ -1148,7 +444,7 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
         __builtin_amdgcn_sched_barrier(0);                                                             \
         rv_g5_frags<B_KN, 1>(ya, yb, CA, CB, fo);                                                     \
         rv_g5_copy<B_KN, 0, NV0>(WA, WB, A, B, a_base, lda, b_base, ldb, RV_G5_KT(t_ + NS - 1), wave, va, vb); \
-        rv_g3_step<4, 4>(acc, xa, xb);                                                                 \
+        rv_g5_step<4, 4>(acc, xa, xb);                                                                 \
         if (PIN) rv_g5_pin<NDS, NV0, PIN>();                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                             \
         RV_WAIT_VM(8 * (NS - 2) + NV0);                                                                \
@@ -1156,7 +452,7 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
         __builtin_amdgcn_sched_barrier(0);                                                             \
         rv_g5_frags<B_KN, 0>(xa, xb, XA, XB, fo);                                                     \
         rv_g5_copy<B_KN, NV0, 8>(WA, WB, A, B, a_base, lda, b_base, ldb, RV_G5_KT(t_ + NS - 1), wave, va, vb); \
-        rv_g3_step<4, 4>(acc, ya, yb);                                                                 \
+        rv_g5_step<4, 4>(acc, ya, yb);                                                                 \
         if (PIN) rv_g5_pin<NDS, 8 - NV0, PIN>();                                                       \
         __builtin_amdgcn_sched_barrier(0);                                                             \
         rv_g5_keep(acc);                                                                               \
@@ -1218,6 +514,7 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
             for (int r = 0; r < 16; ++r) {
                 const int m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+                if (RAGGED && !(m >= mlo && m < Mt && n >= nlo && n < Nt)) continue;
                 const float v = epi(acc[i][j][r], m, n);
                 if (MODE == 0)
                     epi.store(m, n, v);
@@ -1232,137 +529,6 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
         if (tid == 0) partials[blockIdx.x] = ((lds_red[0] + lds_red[1]) + lds_red[2]) + lds_red[3];
     }
 }
-
-// ---------------------------------------------------------------------------
-// Ping-pong variant of the direct-to-LDS contraction (256 x 256 tile, 64-deep
-// k-tiles, two LDS stages, 8 waves of 64 x 128). The waves form two groups,
-// one wave of each per SIMD; group 1 starts one barrier late, so at every
-// barrier-delimited phase one group reads its operand fragments from LDS
-// while the other runs a pure MFMA burst on fragments already in registers,
-// and each SIMD's matrix unit is fed by alternating waves. A phase covers KH
-// k16 steps. Group 0 alone copies k-tiles: tile T+1 is issued in group 0's
-// first read phase of tile T (T >= 1; tiles 0 and 1 in the prologue), after
-// group 1 has finished reading tile T-1 from that stage, and is waited for at
-// the end of group 0's last MFMA phase of tile T, before anyone reads it.
-// ---------------------------------------------------------------------------
-#define RV_PP_BARRIER()                    \
-    do {                                   \
-        __builtin_amdgcn_sched_barrier(0); \
-        RV_LDS_BARRIER();                  \
-        __builtin_amdgcn_sched_barrier(0); \
-    } while (0)
-
-template <bool B_KN, int MODE, class Epi, int KH = 2>
-__device__ __forceinline__ void rv_gemm_pp_bf16(const unsigned short* __restrict__ A,
-                                                const unsigned short* __restrict__ B, long long a_off, long long lda,
-                                                long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
-                                                float* __restrict__ partials) {
-    constexpr int TM = 2, TN = 4, NW = 8;
-    constexpr int HALVES = (RV_G3_BK / 16) / KH;  // phases per k-tile and group
-    static_assert(HALVES * KH * 16 == RV_G3_BK, "KH must divide the k16 steps of a k-tile");
-    __shared__ __attribute__((aligned(1024))) unsigned short a0[RV_G3_BM * RV_G3_BK];
-    __shared__ __attribute__((aligned(1024))) unsigned short a1[RV_G3_BM * RV_G3_BK];
-    __shared__ __attribute__((aligned(1024))) unsigned short b0[RV_G3_BN * RV_G3_BK];
-    __shared__ __attribute__((aligned(1024))) unsigned short b1[RV_G3_BN * RV_G3_BK];
-    __shared__ float lds_red[NW];
-    const int tid = threadIdx.x;
-    // the wave index in a scalar register: the group tests below are then
-    // scalar branches, so a wave outside a group never reaches its s_barrier
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int group = wave >> 2, gw = wave & 3;
-    const int r0 = (wave >> 1) * (32 * TM), c0 = (wave & 1) * (32 * TN);
-    const int tiles_m = M / RV_G3_BM, tiles_n = N / RV_G3_BN;
-    const int ntiles = tiles_m * tiles_n;
-    int tm, tn;
-    {
-        int bid = blockIdx.x;
-        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
-            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
-            const int grp = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
-            tm = grp * 4 + (within & 3);
-            tn = within >> 2;
-        } else {
-            tm = bid / tiles_n;
-            tn = bid % tiles_n;
-        }
-    }
-    const int m0 = tm * RV_G3_BM, n0 = tn * RV_G3_BN;
-    const long long a_base = a_off + (long long)m0 * lda;
-    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
-
-    rv_f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int KT = K / RV_G3_BK;
-    if (group == 0) {
-        // 16 copies per wave and k-tile: tile 0 is complete at vmcnt <= 16
-        rv_g3_copy<B_KN, 4>(a0, b0, A, B, a_base, lda, b_base, ldb, 0, gw, lane);
-        if (KT > 1) {
-            rv_g3_copy<B_KN, 4>(a1, b1, A, B, a_base, lda, b_base, ldb, RV_G3_BK, gw, lane);
-            RV_WAIT_VM(16);
-        } else {
-            RV_WAIT_VM(0);
-        }
-    }
-    RV_PP_BARRIER();
-    if (group == 1) RV_PP_BARRIER();
-    for (int t = 0; t < KT; ++t) {
-        const unsigned short* As = (t & 1) ? a1 : a0;
-        const unsigned short* Bs = (t & 1) ? b1 : b0;
-#pragma unroll
-        for (int h = 0; h < HALVES; ++h) {
-            if (h == 0 && group == 0 && t >= 1 && t + 1 < KT) {
-                if (t & 1)
-                    rv_g3_copy<B_KN, 4>(a0, b0, A, B, a_base, lda, b_base, ldb, (t + 1) * RV_G3_BK, gw, lane);
-                else
-                    rv_g3_copy<B_KN, 4>(a1, b1, A, B, a_base, lda, b_base, ldb, (t + 1) * RV_G3_BK, gw, lane);
-            }
-            rv_bf16x8 af[KH][TM], bf[KH][TN];
-#pragma unroll
-            for (int q = 0; q < KH; ++q)
-                rv_g3_frags<B_KN, TM, TN>(af[q], bf[q], As, Bs, r0, c0, lane, (h * KH + q) * 16);
-            RV_PP_BARRIER();
-#pragma unroll
-            for (int q = 0; q < KH; ++q) rv_g3_step<TM, TN>(acc, af[q], bf[q]);
-            if (h == HALVES - 1 && group == 0) RV_WAIT_VM(0);
-            RV_PP_BARRIER();
-        }
-    }
-    if (group == 0) RV_PP_BARRIER();
-
-    float part = 0.0f;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + r0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n0 + c0 + j * 32 + (lane & 31);
-                const float v = epi(acc[i][j][r], m, n);
-                if (MODE == 0)
-                    epi.store(m, n, v);
-                else
-                    part = part + v;
-            }
-    if (MODE == 1) {
-        part = rv_group_sum<64>(part);
-        if (lane == 0) lds_red[wave] = part;
-        __syncthreads();
-        if (tid == 0) {
-            float s = lds_red[0];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) s = s + lds_red[w];
-            partials[blockIdx.x] = s;
-        }
-    }
-}
-#undef RV_PP_BARRIER
 
 // ---------------------------------------------------------------------------
 // Fused attention forward, the CUSTOM sdpa_fwd kernel (limn README, "The op

@@ -224,8 +224,6 @@ def st_ex(k, st):
 
 
 def _mfma_leaf(k, which):
-    # the operand leaves are the bf16 loads that walk k (stride along dim 2 > 0)
-    cands = [i for i, L in enumerate(k["leaves"]) if L["dtype"] == "bf16" and L["view"]["strides"][2] != 0]
-    a = [i for i in cands if k["leaves"][i]["view"]["strides"][1] == 0]
-    b = [i for i in cands if k["leaves"][i]["view"]["strides"][0] == 0]
-    return a[0] if which == "a" else b[0]
+    # the leaves the contraction reads (an operand copied into workspace
+    # first is read from its copy)
+    return k["plan_detail"]["operand_leaves"][0 if which == "a" else 1]

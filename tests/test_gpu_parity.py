@@ -241,19 +241,14 @@ def test_gemm_operand_windows_bit_exact(m, n, k, pa, pb, oa, ob):
     assert got.tobytes() == ref.tobytes()
 
 
-# the contraction kernels and pipeline settings the plan's environment knobs
-# select (the default is the four-wave kernel, five stages, 2 early copies,
-# pinned interleaving): every one stays bit-exact on integer-valued operands,
-# with B stored [k][n] and [n][k]
+# the pipeline settings the plan's environment knobs select (the default is
+# five stages, 2 early copies, pinned interleaving): every one stays
+# bit-exact on integer-valued operands, with B stored [k][n] and [n][k]
 @pytest.mark.parametrize("knobs", [
     {"RV_GEMM_W4_STAGES": "4", "RV_GEMM_W4_SPLIT": "8"},
     {"RV_GEMM_W4_SPLIT": "0"},
     {"RV_GEMM_W4_PIN": "0"},
     {"RV_GEMM_W4_PIN": "2"},
-    {"RV_GEMM_KERNEL": "lds"},
-    {"RV_GEMM_KERNEL": "lds4"},
-    {"RV_GEMM_KERNEL": "pp"},
-    {"RV_GEMM_KERNEL": "reg"},
 ])
 def test_gemm_kernel_variants_bit_exact(monkeypatch, knobs):
     m, n, k = 512, 256, 448
@@ -402,3 +397,93 @@ def test_graph_replay_matches_eager():
                 torch.cuda.synchronize()
                 for a, b in zip(ref, graph_out):
                     assert a.tobytes() == to_host(b).tobytes(), (spec.name, rep)
+
+
+# ---- ragged contractions: still on the matrix cores ----------------------------
+
+@pytest.mark.parametrize("m,n,k,bt", [(257, 129, 65, False), (255, 257, 31, False), (300, 257, 64, False),
+                                      (520, 300, 96, True), (1, 1, 1, False), (33, 300, 200, True),
+                                      (256, 256, 32, False)])
+def test_gemm_ragged_integer_bit_exact(m, n, k, bt):
+    """Every tile width and tail (limn README, "Correctness"): a last tile
+    shifted back inside the operands, operands copied zero-padded into
+    workspace; integer-valued operands are exact in any order."""
+    _case(f"gemm ragged int {m}x{n}x{k} bt={bt}")
+    from tests.test_lowering import _gemm_views
+    spec = _gemm_views(m, n, k, bt=bt)
+    prog = _prog(spec)
+    assert [kk["class"] for kk in prog.describe()["kernels"]].count("MFMA") == 1
+    inp = synth.inputs_gemm_integer(m, n, k)
+    if bt:
+        inp = {"A": inp["A"], "B": np.ascontiguousarray(inp["B"].T)}
+    got, = run(prog, inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
+def test_gemm_ragged_full_rows_sampled():
+    """4095 x 4096 x 4096: the last row tile starts at 3839 and leaves its
+    first row to the tile before it; sampled rows on both sides of the seam
+    against the oracle (integer-valued operands: exact in any order)."""
+    _case("gemm ragged 4095x4096x4096")
+    m = 4095
+    n = k = 4096
+    inp = synth.inputs_gemm_integer(m, n, k)
+    prog = _prog(synth.gemm_bf16(m, n, k))
+    pd = [kk for kk in prog.describe()["kernels"] if kk["class"] == "MFMA"][0]["plan_detail"]
+    assert pd["ragged"] and pd["copied"] == {"A": False, "B": False}
+    got, = run(prog, inp)
+    rows = [0, 3838, 3839, 3840, 4094]
+    ref, = oracle.run(synth.gemm_bf16(len(rows), n, k), {"A": inp["A"][rows], "B": inp["B"]})
+    assert got[rows].tobytes() == ref.tobytes()
+
+
+def test_gemm_transposed_padded_operands_bit_exact():
+    """A read through a transposing View and B through a padding View: both
+    are copied (transposed / zero-padded) into workspace, then contracted."""
+    _case("gemm transposed + padded operands")
+    g = synth.Spec("gemm_t")
+    a = g.buffer("A", (96, 300), "bf16")
+    b = g.buffer("B", (90, 260), "bf16")
+    a2 = g.view(a, ("permute", (1, 0)))
+    b2 = g.view(b, ("pad", ((3, 3), (0, 0))))
+    a3 = g.cast(g.view(a2, ("reshape", (300, 1, 96)), ("expand", (300, 260, 96))), "f32")
+    b3 = g.cast(g.view(b2, ("permute", (1, 0)), ("reshape", (1, 260, 96)), ("expand", (300, 260, 96))), "f32")
+    g.output(g.sum(g.mul(a3, b3), (2,)))
+    rng = np.random.default_rng(29)
+    inp = {"A": synth.to_bf16_bits(rng.integers(-2, 3, (96, 300)).astype(np.float32)),
+           "B": synth.to_bf16_bits(rng.integers(-2, 3, (90, 260)).astype(np.float32))}
+    got, = run(_prog(g), inp)
+    ref, = oracle.run(g, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
+@pytest.mark.parametrize("m,n,k", [(520, 300, 96), (257, 129, 65)])
+def test_gemm_ragged_relu2_sum(m, n, k):
+    """The relu^2 + SUM epilogue over ragged tiles: cells a shifted tile
+    shares with the tile before it, and padded rows and columns, are left out
+    of the partials."""
+    _case(f"gemm ragged relu2 sum {m}x{n}x{k}")
+    inp = synth.inputs_gemm(m, n, k)
+    spec = synth.gemm_relu2_sum(m, n, k)
+    prog = _prog(spec)
+    desc = prog.describe()
+    assert [kk["class"] for kk in desc["kernels"]][-2:] == ["MFMA", "FOLD"]
+    s_gpu, = run(prog, inp)
+    s_ref, = oracle.run(spec, inp)
+    y_gpu, = run(_prog(synth.gemm_bf16(m, n, k)), inp)
+    y_ref, = oracle.run(synth.gemm_bf16(m, n, k), inp)
+    a = np.abs(interp.bf16_to_f32(inp["A"]).astype(np.float64))
+    b = np.abs(interp.bf16_to_f32(inp["B"]).astype(np.float64))
+    dy = 4 * gamma(k - 1) * (a @ b)
+    assert np.all(np.abs(y_gpu - y_ref)[:, :, 0] <= dy)
+    y = y_ref[:, :, 0].astype(np.float64)
+    q = np.maximum(y, 0) ** 2
+    mf = [kk for kk in desc["kernels"] if kk["class"] == "MFMA"][0]
+    fo = [kk for kk in desc["kernels"] if kk["class"] == "FOLD"]
+    depth = mf["plan_detail"]["partial_sum_depth"] + (fo[0]["plan_detail"]["sum_depth"] if fo else 0)
+    ds = (np.sum((2 * np.abs(y) * dy + dy ** 2) * (y > -dy)) + U * q.sum() + 4 * gamma(depth) * q.sum()
+          + U * abs(float(s_ref.ravel()[0])))
+    e = abs(float(s_gpu.ravel()[0]) - float(s_ref.ravel()[0]))
+    report(f"gemm_ragged_S_{m}x{n}x{k}", np.array([e]), np.array([ds]))
+    assert e <= ds

@@ -63,9 +63,14 @@ CLASSES = {
     "softmax": (lambda: synth.softmax(6, 300), lambda: synth.inputs_softmax(6, 300), ["ROW"]),
     "rmsnorm": (lambda: synth.rmsnorm(6, 300), lambda: synth.inputs_rmsnorm(6, 300), ["ROW"]),
     "layernorm": (lambda: synth.layernorm(5, 256), lambda: synth.inputs_layernorm(5, 256), ["ROW"]),
-    "gemm": (lambda: synth.gemm_relu2_sum(128, 128, 64), lambda: synth.inputs_gemm(128, 128, 64),
+    "gemm": (lambda: synth.gemm_relu2_sum(256, 256, 64), lambda: synth.inputs_gemm(256, 256, 64),
              ["MFMA", "FOLD"]),
-    "gemm_y": (lambda: synth.gemm_bf16(128, 256, 128), lambda: synth.inputs_gemm(128, 256, 128), ["MFMA"]),
+    "gemm_y": (lambda: synth.gemm_bf16(256, 256, 128), lambda: synth.inputs_gemm(256, 256, 128), ["MFMA"]),
+    # narrow and ragged extents: the operands are copied, zero-padded, first
+    "gemm_copied": (lambda: synth.gemm_relu2_sum(100, 130, 70), lambda: synth.inputs_gemm(100, 130, 70),
+                    ["EW", "EW", "MFMA", "FOLD"]),
+    "gemm_y_ragged": (lambda: synth.gemm_bf16(257, 260, 96), lambda: synth.inputs_gemm(257, 260, 96),
+                      ["EW", "MFMA"]),
     # operands as windows of wider buffers, each a View of a View: the two
     # compose into one View of the buffer, so nothing is copied first
     "gemm_windows": (lambda: _gemm_windows(), lambda: _gemm_windows_inputs(), ["MFMA"]),
@@ -112,20 +117,20 @@ def _scatter_general():
 
 def _gemm_windows():
     g = synth.Spec("gemm_windows")
-    a = g.buffer("A", (128, 96), "bf16")
-    b = g.buffer("B", (64, 160), "bf16")
-    aw = g.view(a, ("shrink", ((0, 128), (16, 80))))
-    bw = g.view(b, ("shrink", ((0, 64), (8, 136))))
-    a3 = g.cast(g.view(aw, ("reshape", (128, 1, 64)), ("expand", (128, 128, 64))), "f32")
-    b3 = g.cast(g.view(bw, ("permute", (1, 0)), ("reshape", (1, 128, 64)), ("expand", (128, 128, 64))), "f32")
+    a = g.buffer("A", (256, 96), "bf16")
+    b = g.buffer("B", (64, 320), "bf16")
+    aw = g.view(a, ("shrink", ((0, 256), (16, 80))))
+    bw = g.view(b, ("shrink", ((0, 64), (8, 264))))
+    a3 = g.cast(g.view(aw, ("reshape", (256, 1, 64)), ("expand", (256, 256, 64))), "f32")
+    b3 = g.cast(g.view(bw, ("permute", (1, 0)), ("reshape", (1, 256, 64)), ("expand", (256, 256, 64))), "f32")
     g.output(g.sum(g.mul(a3, b3), (2,)))
     return g
 
 
 def _gemm_windows_inputs():
     rng = np.random.default_rng(23)
-    return {"A": synth.to_bf16_bits(rng.integers(-2, 3, (128, 96)).astype(np.float32)),
-            "B": synth.to_bf16_bits(rng.integers(-2, 3, (64, 160)).astype(np.float32))}
+    return {"A": synth.to_bf16_bits(rng.integers(-2, 3, (256, 96)).astype(np.float32)),
+            "B": synth.to_bf16_bits(rng.integers(-2, 3, (64, 320)).astype(np.float32))}
 
 
 @pytest.mark.parametrize("name", list(CLASSES))
@@ -137,7 +142,7 @@ def test_plan_interpreter_matches_oracle(name):
     ref = oracle.run(spec, inp)
     for g, r in zip(got, ref):
         assert g.shape == r.shape
-        if name in ("gemm",):
+        if name in ("gemm", "gemm_copied"):
             # the plan folds the epilogue in one order, the oracle widens: close
             assert abs(float(g.ravel()[0]) - float(r.ravel()[0])) <= 1e-4 * abs(float(r.ravel()[0]))
         else:
@@ -289,16 +294,17 @@ def test_attention_contract_errors():
 
 
 def test_contraction_plans():
-    """256-multiples take the four-wave 256 x 256 kernel (five 32-deep LDS
-    stages, 160 KB), other shapes the 128 x 128 one; float16 rows give each
-    ROW lane 32 cells, float32 rows 16."""
+    """Every bf16 contraction takes the four-wave 256 x 256 kernel (five
+    32-deep LDS stages, 160 KB); float16 rows give each ROW lane 32 cells,
+    float32 rows 16."""
     big = rv.compile_spec(synth.gemm_relu2_sum(4096, 4096, 4096)).describe()["kernels"][0]
     assert big["plan"] == "gemm_w4" and big["block"][0] == 256 and big["grid"][0] == 256
     pd = big["plan_detail"]
-    assert pd["tile"] == [256, 256, 64] and pd["wave_tiles"] == [4, 4] and pd["stages"] == 5
+    assert pd["tile"] == [256, 256, 32] and pd["wave_tiles"] == [4, 4] and pd["stages"] == 5
     assert pd["copies_first_step"] == 2 and big["lds_bytes"] == 5 * 2 * 256 * 32 * 2
+    assert pd["ragged"] is False and pd["copied"] == {"A": False, "B": False}
     small = rv.compile_spec(synth.gemm_bf16(256, 384, 192)).describe()["kernels"][0]
-    assert small["plan"] == "gemm" and small["grid"][0] == 2 * 3
+    assert small["plan"] == "gemm_w4" and small["grid"][0] == 2 and small["plan_detail"]["ragged"] is True
     f16 = rv.compile_spec(synth.rmsnorm(64, 4096, dtype="f16")).describe()["kernels"][0]
     f32 = rv.compile_spec(synth.rmsnorm(64, 4096)).describe()["kernels"][0]
     assert f16["plan_detail"]["threads_per_row"] == 128 and f32["plan_detail"]["threads_per_row"] == 256
@@ -478,3 +484,58 @@ def test_split_off_switch(monkeypatch):
     monkeypatch.setenv("RV_SPLIT", "0")
     d = rv.compile_spec(synth.reduce((1 << 24,), (0,))).describe()
     assert [k["plan"] for k in d["kernels"]] == ["row_stream"]
+
+
+def _gemm_views(m, n, k, a_mv=(), b_mv=(), bt=False):
+    """y = SUM_k CAST(A) * CAST(B) with A (m, k) and B (k, n) reached through
+    extra movements of their buffers (B stored [n][k] when ``bt``)."""
+    g = synth.Spec(f"gemm_views_{m}x{n}x{k}")
+    a = g.buffer("A", (m, k), "bf16")
+    a2 = g.view(a, *a_mv) if a_mv else a
+    b = g.buffer("B", (n, k) if bt else (k, n), "bf16")
+    b2 = g.view(b, *b_mv) if b_mv else b
+    bkn = g.view(b2, ("permute", (1, 0))) if bt else b2
+    a3 = g.cast(g.view(a2, ("reshape", (m, 1, k)), ("expand", (m, n, k))), "f32")
+    b3 = g.cast(g.view(bkn, ("permute", (1, 0)), ("reshape", (1, n, k)), ("expand", (m, n, k))), "f32")
+    g.output(g.sum(g.mul(a3, b3), (2,)))
+    return g
+
+
+RAGGED_GEMMS = [
+    ((4095, 4096, 4096), {}, False, False),      # one row short: the last tile shifts, no copy
+    ((257, 129, 65), {}, True, True),            # every extent ragged: both operands copied
+    ((255, 257, 31), {}, True, True),
+    ((300, 257, 64), {}, False, True),           # N not a multiple of 8: B copied
+    ((520, 300, 96), {"bt": True}, False, False),  # B stored [n][k], ragged N in place
+    ((1, 1, 1), {}, True, True),
+    ((256, 256, 32), {}, False, False),
+]
+
+
+@pytest.mark.parametrize("mnk,kw,ca,cb", RAGGED_GEMMS)
+def test_every_bf16_contraction_runs_on_mfma(mnk, kw, ca, cb):
+    """No bf16 CAST * MUL * SUM contraction leaves the matrix cores: ragged
+    extents shift the last tile or copy an operand, zero-padded, into
+    workspace first (limn README, "Correctness": matmuls across every tile
+    width and tail)."""
+    m, n, k = mnk
+    d = rv.compile_spec(_gemm_views(m, n, k, **kw)).describe()
+    cls = [kk["class"] for kk in d["kernels"]]
+    assert cls.count("MFMA") == 1 and set(cls) <= {"MFMA", "EW"}, cls
+    mf = [kk for kk in d["kernels"] if kk["class"] == "MFMA"][0]["plan_detail"]
+    assert mf["copied"] == {"A": ca, "B": cb}
+    assert cls.count("EW") == ca + cb
+
+
+def test_transposed_and_padded_operands_run_on_mfma():
+    # A read transposed (stored [k][m]) and B through a pad: both copied
+    g = synth.Spec("gemm_t")
+    a = g.buffer("A", (96, 300), "bf16")
+    b = g.buffer("B", (90, 260), "bf16")
+    a2 = g.view(a, ("permute", (1, 0)))
+    b2 = g.view(b, ("pad", ((3, 3), (0, 0))))
+    a3 = g.cast(g.view(a2, ("reshape", (300, 1, 96)), ("expand", (300, 260, 96))), "f32")
+    b3 = g.cast(g.view(b2, ("permute", (1, 0)), ("reshape", (1, 260, 96)), ("expand", (300, 260, 96))), "f32")
+    g.output(g.sum(g.mul(a3, b3), (2,)))
+    d = rv.compile_spec(g).describe()
+    assert [kk["class"] for kk in d["kernels"]] == ["EW", "EW", "MFMA"]
