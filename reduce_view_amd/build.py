@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "_lib", "librv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-HOST_SOURCES = ["view.cpp", "graph.cpp", "schedule.cpp", "lower.cpp", "codegen.cpp", "runtime.cpp", "abi.cpp"]
+HOST_SOURCES = ["view.cpp", "graph.cpp", "schedule.cpp", "lower.cpp", "codegen.cpp", "runtime.cpp", "codeobj.cpp",
+                "abi.cpp"]
 # hipcc flag set for any GPU code it compiles (packed FP32 instructions off)
 GPU_FLAGS = ["--offload-arch=gfx950", "-O3", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -216,6 +216,15 @@ struct Program {
     std::vector<std::vector<Loc>> kparams;               // kernel parameter order
 };
 
+// Register and memory budget of one compiled kernel (-1: not recorded).
+struct KernelResources {
+    int64_t vgpr = -1, agpr = -1, sgpr = -1, vgpr_spill = -1, sgpr_spill = -1;
+    int64_t scratch = -1;  // private (scratch) bytes per lane
+    int64_t lds = -1;      // static LDS bytes per workgroup
+};
+// Per kernel name, from the metadata note of a gfx950 code object.
+std::map<std::string, KernelResources> kernel_resources(const std::vector<char>& code);
+
 void schedule(Program& p);                 // fills kernels + regions
 void lower(Program& p);                    // merges dims, picks plans and launch shapes
 std::string codegen(const Program& p);     // HIP source of every kernel

@@ -690,6 +690,7 @@ static std::string json_loc(const Loc& L) {
 }
 
 std::string describe(const Program& p) {
+    const std::map<std::string, KernelResources> res = kernel_resources(p.code);
     std::string s = "{\"n_inputs\":" + std::to_string(p.g.n_inputs) + ",\"workspace_bytes\":" +
                     std::to_string(p.ws_bytes) + ",\"cache_key\":\"" + p.key + "\",\"kernels\":[";
     for (size_t i = 0; i < p.kernels.size(); ++i) {
@@ -709,6 +710,15 @@ std::string describe(const Program& p) {
         s += fmt(",\"grid\":[%u,%u,%u],\"block\":[%u,%u,%u],\"lds_bytes\":%zu", k.grid[0], k.grid[1], k.grid[2],
                  k.block[0], k.block[1], k.block[2], k.lds);
         if (!k.plan_json.empty()) s += ",\"plan_detail\":{" + k.plan_json + "}";
+        // the compiled kernel's budget (Tiki README, "The architecture we
+        // want": visible before launch)
+        auto r = res.find(k.name);
+        if (r != res.end())
+            s += fmt(",\"resources\":{\"vgpr\":%lld,\"agpr\":%lld,\"sgpr\":%lld,\"vgpr_spill\":%lld,"
+                     "\"sgpr_spill\":%lld,\"scratch_bytes\":%lld,\"lds_bytes\":%lld}",
+                     (long long)r->second.vgpr, (long long)r->second.agpr, (long long)r->second.sgpr,
+                     (long long)r->second.vgpr_spill, (long long)r->second.sgpr_spill, (long long)r->second.scratch,
+                     (long long)r->second.lds);
         s += ",\"leaves\":[";
         for (size_t l = 0; l < k.leaves.size(); ++l) {
             const Leaf& L = k.leaves[l];

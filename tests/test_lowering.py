@@ -539,3 +539,25 @@ def test_transposed_and_padded_operands_run_on_mfma():
     g.output(g.sum(g.mul(a3, b3), (2,)))
     d = rv.compile_spec(g).describe()
     assert [kk["class"] for kk in d["kernels"]] == ["EW", "EW", "MFMA"]
+
+
+@pytest.mark.parametrize("spec", [
+    synth.ew_chain(4096, 4096), synth.ew_chain(4096, 4096, masked=True), synth.transpose(4096, 4096),
+    synth.softmax(16384, 4096), synth.rmsnorm(16384, 4096), synth.layernorm(8192, 8192),
+    synth.matmul_broadcast(64, 64, 64), synth.gemm_relu2_sum(4096, 4096, 4096), synth.gemm_relu2_sum(257, 129, 65),
+    synth.softmax(256, 262144), synth.attention(6, 8192, 8192, 32, True), synth.reduce((1 << 24,), (0,)),
+    synth.reduce((16384, 4096), (0,)), synth.embedding_gather(65536, 1024, 32768),
+    synth.embedding_scatter(65536, 1024, 32768), synth.rmsnorm(16384, 4096, dtype="f64"),
+], ids=lambda s: s.name)
+def test_kernel_budgets_visible_and_spill_free(spec):
+    """rv_describe reports each compiled kernel's registers, scratch and LDS
+    (Tiki README, "The architecture we want": budgets visible before
+    launch); the kernels of every workload keep everything in registers and
+    LDS: no scratch, no spills, LDS within the CU's 160 KB."""
+    d = rv.compile_spec(spec).describe()
+    for k in d["kernels"]:
+        r = k["resources"]
+        assert r["scratch_bytes"] == 0 and r["vgpr_spill"] == 0 and r["sgpr_spill"] == 0, (k["name"], r)
+        assert 0 < r["vgpr"] <= 512 and r["lds_bytes"] <= 160 * 1024, (k["name"], r)
+        if k["class"] == "MFMA":
+            assert r["agpr"] == 256  # the 256 accumulators per lane stay in the accumulation registers
