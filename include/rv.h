@@ -219,7 +219,9 @@ rv_status rv_launch(const rv_program* prog, const rv_buffer* bufs, int32_t nbufs
                     void* workspace, size_t ws_bytes, void* stream);
 
 /* Writes a JSON description of the program (kernel classes, lowered index
- * expressions, tile plans, launch shapes, LDS bytes) into out[0..cap), NUL
+ * expressions, tile plans, launch shapes, LDS bytes, and per compiled kernel
+ * its VGPR / AGPR / SGPR counts, spills, scratch and LDS bytes read from the
+ * gfx950 code object) into out[0..cap), NUL
  * terminated. If `needed` is not NULL it receives the full length + 1.
  * Truncates silently when cap is too small. */
 rv_status rv_describe(const rv_program* prog, char* out, size_t cap, size_t* needed);
