@@ -218,6 +218,19 @@ rv_status rv_workspace_size(const rv_program* prog, size_t* bytes);
 rv_status rv_launch(const rv_program* prog, const rv_buffer* bufs, int32_t nbufs,
                     void* workspace, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): rv_launch
+ * with the library's own workspace in place of a caller's. That workspace is
+ * one device array of RV_SCRATCH_BYTES per GPU, reserved when the library's
+ * code is first loaded on the GPU and held until the process ends; this call
+ * allocates nothing. A program needing more workspace than that fails with
+ * RV_E_WORKSPACE before anything is enqueued. Every call on a GPU shares
+ * that GPU's array and it keeps the last call's contents (no kernel here
+ * needs it cleared); calls that overlap on one GPU (other streams, other
+ * host threads) race on it. Buffers and stream as for rv_launch. */
+#define RV_SCRATCH_BYTES ((size_t)64 << 20)
+rv_status rv_launch_noalloc(const rv_program* prog, const rv_buffer* bufs, int32_t nbufs, void* stream);
+
 /* Writes a JSON description of the program (kernel classes, lowered index
  * expressions, tile plans, launch shapes, LDS bytes, and per compiled kernel
  * its VGPR / AGPR / SGPR counts, spills, scratch and LDS bytes read from the

@@ -77,6 +77,16 @@ def build(verbose: bool = False) -> str:
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
     embed = _embed_header(out_dir)
     srcs = [os.path.join(CSRC, "host", s) for s in HOST_SOURCES] + [embed]
+    # the library's own device workspace (a gfx950 device array): compiled as
+    # HIP for gfx950, linked beside the host code
+    scratch_o = os.path.join(out_dir, "scratch.o")
+    cmd = [HIPCC] + GPU_FLAGS + ["-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I",
+                                 os.path.join(CSRC, "host"), "-c", os.path.join(CSRC, "host", "scratch.hip"),
+                                 "-o", scratch_o]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    srcs += ["-x", "none", scratch_o]  # an object, whatever language the sources before it were taken as
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wno-unused-function",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(CSRC, "host")] + srcs + [

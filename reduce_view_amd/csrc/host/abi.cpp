@@ -119,6 +119,13 @@ rv_status rv_launch(const rv_program* prog, const rv_buffer* bufs, int32_t nbufs
     });
 }
 
+rv_status rv_launch_noalloc(const rv_program* prog, const rv_buffer* bufs, int32_t nbufs, void* stream) {
+    return guard([&] {
+        if (!prog) rv::fail(RV_E_INVALID, "NULL program");
+        rv::launch_noalloc(const_cast<rv::Program&>(prog->p), bufs, nbufs, stream);
+    });
+}
+
 rv_status rv_describe(const rv_program* prog, char* out, size_t cap, size_t* needed) {
     std::string s;
     rv_status st = guard([&] {

@@ -231,6 +231,11 @@ std::string codegen(const Program& p);     // HIP source of every kernel
 std::string describe(const Program& p);    // JSON
 void compile_code(Program& p);             // hiprtc -> p.code (runtime.cpp)
 void launch(Program& p, const rv_buffer* bufs, int32_t nbufs, void* ws, size_t ws_bytes, void* stream);
+// The library's own workspace (scratch.hip): a device array of
+// kScratchBytes per GPU, for callers that cannot allocate.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+void* scratch_ptr(int dev);
+void launch_noalloc(Program& p, const rv_buffer* bufs, int32_t nbufs, void* stream);
 void device_check(int device);
 
 std::string json_view(const rv_view& v);

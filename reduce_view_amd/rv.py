@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "librv.so")
 
 RV_MAX_DIMS = 8
+RV_SCRATCH_BYTES = 64 << 20  # the library's own workspace per GPU (rv_launch_noalloc)
 STATUS = {0: "RV_OK", -1: "RV_E_INVALID", -2: "RV_E_UNSUPPORTED_OP", -3: "RV_E_UNSUPPORTED_LAYOUT",
           -4: "RV_E_DTYPE", -5: "RV_E_OUT_OF_BOUNDS", -6: "RV_E_WORKSPACE", -7: "RV_E_DEVICE",
           -8: "RV_E_COMPILE", -9: "RV_E_LAUNCH"}
@@ -81,6 +82,7 @@ def _load():
         "rv_output_desc": [vp, ctypes.c_int32, P(rv_view), P(ctypes.c_int32)],
         "rv_workspace_size": [vp, P(ctypes.c_size_t)],
         "rv_launch": [vp, P(rv_buffer), ctypes.c_int32, vp, ctypes.c_size_t, vp],
+        "rv_launch_noalloc": [vp, P(rv_buffer), ctypes.c_int32, vp],
         "rv_describe": [vp, ctypes.c_char_p, ctypes.c_size_t, P(ctypes.c_size_t)],
         "rv_source": [vp, ctypes.c_char_p, ctypes.c_size_t, P(ctypes.c_size_t)],
         "rv_view_contiguous": [P(ctypes.c_int64), ctypes.c_int32, P(rv_view)],
@@ -105,7 +107,7 @@ _lib = _load()
 
 # every symbol include/rv.h declares
 EXPORTS = ("rv_init", "rv_compile", "rv_node_shape", "rv_program_io", "rv_output_desc",
-           "rv_workspace_size", "rv_launch", "rv_describe", "rv_source", "rv_program_free",
+           "rv_workspace_size", "rv_launch", "rv_launch_noalloc", "rv_describe", "rv_source", "rv_program_free",
            "rv_last_error", "rv_view_contiguous", "rv_view_reshape", "rv_view_permute",
            "rv_view_expand", "rv_view_pad", "rv_view_shrink")
 
@@ -200,6 +202,13 @@ def rv_launch(h, bufs, workspace_ptr: int, ws_bytes: int, stream_ptr: int) -> No
     arr = (rv_buffer * max(1, len(bufs)))(*bufs)
     _check(_lib.rv_launch(h, arr, len(bufs), ctypes.c_void_p(workspace_ptr or None), ws_bytes,
                           ctypes.c_void_p(stream_ptr or None)))
+
+
+def rv_launch_noalloc(h, bufs, stream_ptr: int) -> None:
+    """rv_launch with the library's own workspace (for callers that cannot
+    allocate)."""
+    arr = (rv_buffer * max(1, len(bufs)))(*bufs)
+    _check(_lib.rv_launch_noalloc(h, arr, len(bufs), ctypes.c_void_p(stream_ptr or None)))
 
 
 def _text(fn, h) -> str:
