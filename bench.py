@@ -150,6 +150,18 @@ def workloads():
             programs=[("sum_cols", synth.reduce((16384, 4096), (0,)), 16384 * 4096 * F32 + 4096 * F32)],
             inputs=lambda seed: synth.inputs_reduce((16384, 4096), seed=seed),
             unit="GB/s", dtype="f32", bound="hbm", seed=12),
+        "vendor_copy": dict(
+            desc=("torch.Tensor.copy_ of contiguous fp32 buffers (the HIP runtime's device-to-device copy), "
+                  "4096x4096 (64 MiB each way) and 1 GiB: an HBM ceiling measured outside this library"),
+            programs=[], vendor=[("copy_4096x4096", 4096 * 4096), ("copy_1GiB", 1 << 28)],
+            inputs=lambda seed: {}, unit="GB/s", dtype="f32", bound="hbm", seed=1),
+        "launch_overhead": dict(
+            desc=("host time per rv_launch of the 64^3 broadcast-matmul program (one kernel) and of the split "
+                  "full SUM (two kernels), 2000 launches each through the prepared binding, against the "
+                  "kernels' own time"),
+            programs=[], launch=[("matmul64", synth.matmul_broadcast(64, 64, 64), lambda: synth.inputs_matmul(64, 64, 64)),
+                                 ("sum_full", synth.reduce((1 << 24,), (0,)), lambda: synth.inputs_reduce((1 << 24,)))],
+            inputs=lambda seed: {}, unit="us", dtype="f32", bound="latency", seed=0),
         "copy": dict(
             desc="plain 4096x4096 fp32 copy (bandwidth reference; not a hot-path workload)",
             programs=[("copy", synth.copy(4096, 4096), 2 * 4096 * 4096 * F32)],
@@ -481,6 +493,71 @@ def measure_configs(args, stream, timer, headline_ms):
     return entries, keep
 
 
+def _launch_overhead(args, wl):
+    """Host microseconds per launch (the prepared call: one C call that
+    validates the buffers and enqueues the program's kernels), measured over
+    back-to-back launches whose enqueueing outruns the GPU only when the
+    kernels are short; and the GPU time per launch from events."""
+    import torch
+    from reduce_view_amd import rv
+    rv.rv_init(0)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    timer = _Timer(stream)
+    res = {}
+    for name, spec, mk in wl["launch"]:
+        prog = rv.compile_spec(spec)
+        dev = {k: _to_device(v) for k, v in mk().items() if k in prog.slots}
+        out = prog.alloc_outputs()
+        go = prog.prepare(dev, out, stream, prog.workspace(stream=stream))
+        for _ in range(50):
+            go()
+        torch.cuda.synchronize()
+        n = 2000
+        t0 = time.perf_counter()
+        for _ in range(n):
+            go()
+        host_us = (time.perf_counter() - t0) / n * 1e6
+        torch.cuda.synchronize()
+        gpu_ms = timer(lambda i: go(), n)
+        res[name] = {"host_us_per_launch": round(host_us, 2), "gpu_us_per_launch": round(gpu_ms * 1e3, 2),
+                     "kernels": len(prog.describe()["kernels"])}
+    return {"metric": "host launch overhead", "value": max(v["host_us_per_launch"] for v in res.values()),
+            "unit": "us", "n_gpus": 1, "higher_is_better": False, "data": "synthetic",
+            "config": {"workload": args.workload + ": " + wl["desc"]}, "launches": res}
+
+
+def _vendor_copy(args, wl):
+    """HBM ceiling from the runtime's own copy: torch.Tensor.copy_ between
+    contiguous device buffers (a device-to-device hipMemcpyAsync), rotating
+    through enough buffers that no copy re-reads what the Infinity Cache
+    holds; bytes = read + write. Not a library workload."""
+    import torch
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    timer = _Timer(stream)
+    res = {}
+    for name, n in wl["vendor"]:
+        nb = max(2, int(np.ceil(1.0e9 / (n * 4))) + 1)
+        src = [torch.empty(n, dtype=torch.float32, device="cuda").uniform_() for _ in range(nb)]
+        dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(nb)]
+        go = lambda i: dst[i % nb].copy_(src[(i + 1) % nb])  # noqa: E731
+        probe = timer(go, 3)
+        reps = max(args.steps, int(np.ceil(30.0 / max(probe, 1e-3))))
+        timer(go, reps)
+        ms = timer(go, reps)
+        res[name] = {"ms": round(ms, 5), "GB/s": round(2 * n * 4 / (ms * 1e-3) * 1e-9, 2),
+                     "frac": round(2 * n * 4 / (ms * 1e-3) * 1e-9 / HBM_PEAK_GBS, 4), "reps": reps}
+        del src, dst
+        torch.cuda.empty_cache()
+    best = max(v["GB/s"] for v in res.values())
+    return {"metric": METRIC, "value": best, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": args.workload + ": " + wl["desc"]}, "copies": res,
+            "roofline": {"bound": "hbm", "achieved": best, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(best / HBM_PEAK_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,6 +580,12 @@ def main():
     from reduce_view_amd import rv
 
     wl = workloads()[args.workload]
+    if wl.get("vendor"):
+        print(json.dumps(_vendor_copy(args, wl)), flush=True)
+        return
+    if wl.get("launch"):
+        print(json.dumps(_launch_overhead(args, wl)), flush=True)
+        return
     rv.rv_init(0)
     progs = [(n, rv.compile_spec(s), b) for n, s, b in wl["programs"]]
     # rotating input sets: enough that a launch never re-reads what the

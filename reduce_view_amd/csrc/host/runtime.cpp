@@ -229,22 +229,26 @@ void launch(Program& p, const rv_buffer* bufs, int32_t nbufs, void* ws, size_t w
     if (hipGetDevice(&dev) != hipSuccess) fail(RV_E_DEVICE, "no current HIP device");
     std::vector<void*>* fns = nullptr;
     ensure_loaded(p, dev, &fns);
+    // every kernel parameter is a pointer: the kernel-argument block is the
+    // packed array of them, handed over whole (no per-argument lookups)
+    constexpr size_t kMaxParams = 64;
     for (size_t i = 0; i < p.kernels.size(); ++i) {
         const Kernel& k = p.kernels[i];
         if (k.plan == "empty" || k.grid[0] == 0) continue;
-        std::vector<void*> ptrs;
-        for (const Loc& L : p.kparams[i]) {
-            if (L.kind == 0)
-                ptrs.push_back(bufs[L.index].ptr);
-            else if (L.kind == 1)
-                ptrs.push_back(bufs[nin + L.index].ptr);
-            else
-                ptrs.push_back((char*)ws + p.regions[L.index].offset);
+        const std::vector<Loc>& locs = p.kparams[i];
+        if (locs.size() > kMaxParams) fail(RV_E_LAUNCH, fmt("kernel %s has %zu parameters", k.name.c_str(), locs.size()));
+        void* ptrs[kMaxParams];
+        for (size_t a = 0; a < locs.size(); ++a) {
+            const Loc& L = locs[a];
+            ptrs[a] = L.kind == 0 ? bufs[L.index].ptr
+                      : L.kind == 1 ? bufs[nin + L.index].ptr
+                                    : (void*)((char*)ws + p.regions[L.index].offset);
         }
-        std::vector<void*> args(ptrs.size());
-        for (size_t a = 0; a < ptrs.size(); ++a) args[a] = &ptrs[a];
+        size_t arg_bytes = locs.size() * sizeof(void*);
+        void* extra[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, ptrs, HIP_LAUNCH_PARAM_BUFFER_SIZE, &arg_bytes,
+                         HIP_LAUNCH_PARAM_END};
         hipError_t e = hipModuleLaunchKernel((hipFunction_t)(*fns)[i], k.grid[0], k.grid[1], k.grid[2], k.block[0],
-                                             k.block[1], k.block[2], 0, (hipStream_t)stream, args.data(), nullptr);
+                                             k.block[1], k.block[2], 0, (hipStream_t)stream, nullptr, extra);
         if (e != hipSuccess)
             fail(RV_E_LAUNCH, fmt("launch of %s failed: %s", k.name.c_str(), hipGetErrorString(e)));
     }
