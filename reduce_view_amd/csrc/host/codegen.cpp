@@ -2185,8 +2185,14 @@ std::string Gen::gen_gemm() {
         size_t il = k.plan_json.find("\"interleave\":");
         if (il != std::string::npos) sscanf(k.plan_json.c_str() + il, "\"interleave\":%d", &PIN);
     }
+    int KROT = 0, REMAP = 1;
+    {
+        size_t kr = k.plan_json.find("\"krot\":");
+        if (kr != std::string::npos) sscanf(k.plan_json.c_str() + kr, "\"krot\":%d,\"remap\":%d", &KROT, &REMAP);
+    }
     b << "  rv_gemm_w4_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ", " << sname << ", "
-      << NV0 << ", " << PIN << ", " << NS << ", " << (ragged ? "true" : "false") << ">(" << pa << ", " << pb << ", "
+      << NV0 << ", " << PIN << ", " << NS << ", " << (ragged ? "true" : "false") << ", " << KROT << ", "
+      << (REMAP ? "true" : "false") << ">(" << pa << ", " << pb << ", "
       << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", " << K
       << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ", " << Mt << ", " << Nt << ");\n";
     return f.str() + "@@BODY@@" + b.str();

@@ -363,6 +363,10 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
             if (pn && *pn) pin = std::max(0, std::min(2, atoi(pn)));
             const char* st = getenv("RV_GEMM_W4_STAGES");
             if (st && (atoi(st) == 4 || atoi(st) == 5)) stages = atoi(st);
+            // k-tile stagger among workgroups sharing panels, and the
+            // XCD-contiguous tile order (1) or the plain one (0)
+            const int krot = std::max(0, std::min(64, env_int("RV_GEMM_KROT", 0)));
+            const int remap = env_int("RV_GEMM_REMAP", 1) ? 1 : 0;
             k.plan = "gemm_w4";
             k.lds = 2 * stages * 256 * 32 * 2;
             const int64_t tiles = ((Me + 255) / 256) * ((Ne + 255) / 256);
@@ -378,10 +382,10 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
                      "\"tile\":[256,256,32],\"waves\":4,\"wave_tiles\":[4,4],\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
                      "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d,\"stages\":%d,"
                      "\"copies_first_step\":%d,\"interleave\":%d,\"extent\":[%lld,%lld,%lld],\"ragged\":%s,"
-                     "\"copied\":{\"A\":%s,\"B\":%s},\"operand_leaves\":[%d,%d]",
+                     "\"copied\":{\"A\":%s,\"B\":%s},\"operand_leaves\":[%d,%d],\"krot\":%d,\"remap\":%d",
                      kn ? "kn" : "nk", 256 - 1 + 6 + 3, stages, nv0, pin, (long long)Me, (long long)Ne, (long long)Ke,
                      ragged ? "true" : "false", k.mfma_copied[0] ? "true" : "false", k.mfma_copied[1] ? "true" : "false",
-                     k.mfma_a, k.mfma_b);
+                     k.mfma_a, k.mfma_b, krot, remap);
             k.plan_json = buf;
             if (k.mfma_partial) {
                 p.regions[k.partials_region].bytes = (size_t)k.n_partials * 4;

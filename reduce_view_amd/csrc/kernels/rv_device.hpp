@@ -363,7 +363,8 @@ __device__ __forceinline__ void rv_g5_keep(rv_f32x16 (&acc)[4][4]) {
         for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
-template <bool B_KN, int MODE, class Epi, int NV0 = 8, int PIN = 1, int NS = 4, bool RAGGED = false>
+template <bool B_KN, int MODE, class Epi, int NV0 = 8, int PIN = 1, int NS = 4, bool RAGGED = false, int KROT = 0,
+          bool REMAP = true>
 __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict__ A,
                                                 const unsigned short* __restrict__ B, long long a_off, long long lda,
                                                 long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
@@ -386,7 +387,7 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
     int tm, tn;
     {
         int bid = blockIdx.x;
-        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
+        if (REMAP && (ntiles & 7) == 0 && (tiles_m & 3) == 0) {
             const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
             const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
             tm = group * 4 + (within & 3);
@@ -425,11 +426,15 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int KT = K / 32;
+    // KROT staggers the workgroups that share operand panels: each walks the
+    // k-tiles from its own starting tile (KROT times its index among the
+    // XCD's workgroups), wrapping around; the sum is the same up to order.
+    const int rot = KROT ? (KROT * (int)(blockIdx.x >> 3)) % KT : 0;
     // copies past the last k-tile reload it into a stage nobody reads, so
     // every k-tile issues exactly 8 copies per wave, and "the next stage has
     // landed" is always vmcnt <= 8 (NS - 2) + NV0: the later stages' copies
     // may stay in flight
-#define RV_G5_KT(t) (((t) < KT ? (t) : KT - 1) * 32)
+#define RV_G5_KT(t) (KROT ? ((((t) < KT ? (t) : KT - 1) + rot) % KT) * 32 : ((t) < KT ? (t) : KT - 1) * 32)
     rv_g5_copy<B_KN, 0, 8>(a0, b0, A, B, a_base, lda, b_base, ldb, RV_G5_KT(0), wave, va, vb);
     rv_g5_copy<B_KN, 0, 8>(a1, b1, A, B, a_base, lda, b_base, ldb, RV_G5_KT(1), wave, va, vb);
     rv_g5_copy<B_KN, 0, 8>(a2, b2, A, B, a_base, lda, b_base, ldb, RV_G5_KT(2), wave, va, vb);
