@@ -487,12 +487,21 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
             k.grid[1] = 1;
             k.grid[2] = (unsigned)B;
             k.block[0] = 256;
-            int nt = 0;
+            int nt = 0, tbytes = 0;
             for (auto& L : k.leaves)
-                if (!L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) ++nt;
-            k.lds = 0;
+                if (!L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) {
+                    ++nt;
+                    tbytes += 32 * WY * 32 * WX * dtype_size(L.dtype);
+                }
+            if (WY != 1) tbytes = 1 << 30;  // the staged block assumes a 32-row tile
+            // RV_EW_TRANSPOSE=lds: interior tiles stage each transposed
+            // operand through LDS (row-wise coalesced loads, 16-byte chunks
+            // XOR-swizzled, read back along the other dim) instead of
+            // transposing 4 x 4 blocks in registers
+            const bool lds_t = nt > 0 && env_int("RV_EW_TRANSPOSE_LDS", 0) != 0 && tbytes <= 64 * 1024;
+            k.lds = lds_t ? (size_t)tbytes : 0;
             snprintf(buf, sizeof buf, "\"tile\":[%d,%d],\"waves\":[%d,%d],\"order\":%d,\"lane_block\":[4,4],"
-                     "\"register_transposed_leaves\":%d", 32 * WY, 32 * WX, WY, WX, order, nt);
+                     "\"%s_transposed_leaves\":%d", 32 * WY, 32 * WX, WY, WX, order, lds_t ? "lds" : "register", nt);
         } else {
             k.plan = "rowmajor";
             int maxsz = 1;

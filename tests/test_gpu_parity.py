@@ -489,3 +489,23 @@ def test_gemm_ragged_relu2_sum(m, n, k):
     e = abs(float(s_gpu.ravel()[0]) - float(s_ref.ravel()[0]))
     report(f"gemm_ragged_S_{m}x{n}x{k}", np.array([e]), np.array([ds]))
     assert e <= ds
+
+
+@pytest.mark.parametrize("case", ["transpose", "chain", "chain_masked"])
+def test_lds_staged_transpose_variant_bit_exact(monkeypatch, case):
+    """The LDS-staged transposed read (RV_EW_TRANSPOSE_LDS=1: row-coalesced
+    loads, XOR-swizzled LDS block, column reads back; measured slower than
+    the register transpose, kept selectable) gives the same bits."""
+    monkeypatch.setenv("RV_EW_TRANSPOSE_LDS", "1")
+    for r, c in [(4096, 4096), (131, 77), (64, 256)]:
+        _case(f"lds transpose {case} {r}x{c}")
+        if case == "transpose":
+            spec = synth.transpose(r, c)
+            prog = _prog(spec)
+            assert "lds_transposed_leaves" in prog.describe()["kernels"][0]["plan_detail"]
+            inp = {"X": synth.inputs_ew(r, c)["X"]}
+            got, = run(prog, inp)
+            ref, = oracle.run(spec, inp)
+            assert got.tobytes() == ref.tobytes()
+        else:
+            _chain_check(synth.ew_chain(r, c, masked=case == "chain_masked"), synth.inputs_ew(r, c), f"lds_{case}_{r}x{c}")
