@@ -2226,23 +2226,16 @@ std::string Gen::gen_gemm() {
     const bool ragged = M % 256 || N % 256 || M != Mt || N != Nt;
     const int64_t lda = A.v.strides[0];
     const int64_t ldb = kn ? B.v.strides[2] : B.v.strides[1];
-    int NV0 = 8, PIN = 1, NS = 4;
-    {
-        size_t st = k.plan_json.find("\"stages\":");
-        if (st != std::string::npos) sscanf(k.plan_json.c_str() + st, "\"stages\":%d", &NS);
-        size_t at = k.plan_json.find("\"copies_first_step\":");
-        if (at != std::string::npos) sscanf(k.plan_json.c_str() + at, "\"copies_first_step\":%d", &NV0);
-        size_t il = k.plan_json.find("\"interleave\":");
-        if (il != std::string::npos) sscanf(k.plan_json.c_str() + il, "\"interleave\":%d", &PIN);
-    }
-    int KROT = 0, REMAP = 1;
-    {
-        size_t kr = k.plan_json.find("\"krot\":");
-        if (kr != std::string::npos) sscanf(k.plan_json.c_str() + kr, "\"krot\":%d,\"remap\":%d", &KROT, &REMAP);
-    }
-    b << "  rv_gemm_w4_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ", " << sname << ", "
-      << NV0 << ", " << PIN << ", " << NS << ", " << (ragged ? "true" : "false") << ", " << KROT << ", "
-      << (REMAP ? "true" : "false") << ">(" << pa << ", " << pb << ", "
+    const Kernel::GemmSched& g = k.gemm;
+    if (k.plan == "gemm_w6")
+        b << "  rv_gemm_w6_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ", " << sname
+          << ", " << g.pin << ", " << (ragged ? "true" : "false") << ", " << g.pe << ", " << g.po << ">(" << pa << ", " << pb
+          << ", ";
+    else
+        b << "  rv_gemm_w4_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ", " << sname
+          << ", " << g.nv0 << ", " << g.pin << ", " << g.stages << ", " << (ragged ? "true" : "false") << ", "
+          << g.krot << ", " << (g.remap ? "true" : "false") << ">(" << pa << ", " << pb << ", ";
+    b
       << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", " << K
       << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ", " << Mt << ", " << Nt << ");\n";
     return f.str() + "@@BODY@@" + b.str();

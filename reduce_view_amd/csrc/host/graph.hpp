@@ -119,11 +119,20 @@ struct Kernel {
     // MFMA pattern (a, b: leaves of the bf16 operands; y: the contraction)
     int mfma_a = -1, mfma_b = -1, mfma_y = -1;
     bool mfma_partial = false;  // epilogue reduced to one partial per workgroup
-    // extents the operand buffers hold (M, N >= 256, K a multiple of 32;
+    // extents the operand buffers hold (M, N >= 256, K a multiple of the kernel's k-step;
     // an operand that cannot be read in place is first copied, zero-padded,
     // into workspace); the domain keeps the output's (M, N, K)
     int64_t mfma_ext[3] = {0, 0, 0};
     bool mfma_copied[2] = {false, false};
+    // the kernel's schedule (chosen at lowering, baked in at codegen):
+    // interleave mode, tile order; gemm_w4: stages, copies in a k-tile's
+    // first step, k-tile stagger; gemm_w6: copies in an even / odd k-tile's
+    // first step
+    struct GemmSched {
+        int pin = 1, remap = 1;
+        int stages = 5, nv0 = 2, krot = 0;
+        int pe = 3, po = 1;
+    } gemm;
     int partials_region = -1;   // workspace region of the partials
     int64_t n_partials = 0;
     // FOLD ("fold": the contraction's partials to one scalar; "fold_cells":
@@ -244,6 +253,9 @@ std::vector<Loc> kernel_param_locs(const Program& p, const Kernel& k);
 // float32, which the streaming plan folds in one pass with the online
 // max/denominator recurrence.
 std::vector<std::pair<int, int>> online_softmax_pairs(const Kernel& k);
+// k-depth the contraction kernel steps by (its operands hold a multiple of
+// it): 64 for the kernel staging A 64 deep ("w6"), 32 for "w4".
+int mfma_kstep();
 // Value `e` of kernel `k` is the same at every index along domain dim `d`.
 bool ex_invariant(const Kernel& k, int e, int d);
 

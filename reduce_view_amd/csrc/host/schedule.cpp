@@ -667,7 +667,9 @@ static Kernel operand_copy(const Leaf& L, int dr, int dc, int64_t rows, int64_t 
 // rewritten to read them.
 static void mfma_operands(Ctx& c, Kernel& k, std::vector<Kernel>& out) {
     const int64_t M = k.domain[0], N = k.domain[1], K = k.domain[2];
-    const int64_t Kp = (K + 31) / 32 * 32, lim = (int64_t)1 << 27;
+    // the kernel's k step: 64 for the A-staged-64-deep kernel, else 32
+    const int64_t KS = mfma_kstep();
+    const int64_t Kp = (K + KS - 1) / KS * KS, lim = (int64_t)1 << 27;
     const Leaf A = k.leaves[k.mfma_a], B = k.leaves[k.mfma_b];
     auto unmasked = [](const Leaf& L) {
         if (L.zero) return false;
@@ -676,10 +678,10 @@ static void mfma_operands(Ctx& c, Kernel& k, std::vector<Kernel>& out) {
         return true;
     };
     const rv_view &a = A.v, &b = B.v;
-    const bool a_direct = K % 32 == 0 && unmasked(A) && M >= 256 && a.strides[2] == 1 && a.offset % 8 == 0 &&
+    const bool a_direct = K % KS == 0 && unmasked(A) && M >= 256 && a.strides[2] == 1 && a.offset % 8 == 0 &&
                           a.strides[0] % 8 == 0 && a.strides[0] < lim;
     const bool kn = b.strides[1] == 1;
-    const bool b_direct = K % 32 == 0 && unmasked(B) && N >= 256 && b.offset % 8 == 0 &&
+    const bool b_direct = K % KS == 0 && unmasked(B) && N >= 256 && b.offset % 8 == 0 &&
                           (kn ? (b.strides[2] % 8 == 0 && N % 8 == 0 && b.strides[2] < lim)
                               : (b.strides[2] == 1 && b.strides[1] % 8 == 0 && b.strides[1] < lim));
     int64_t Me = M, Ne = N;

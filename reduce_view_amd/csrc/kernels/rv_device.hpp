@@ -536,6 +536,259 @@ __device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// The same contraction with A staged 64 deep: A rows of 128 bytes (whole
+// lines) per copy instead of 64-byte halves, so A takes half the L2 requests
+// for its bytes. Each of the 3 A stages (32 KB) holds two 32-deep k-tiles;
+// B keeps its 32-deep k-tiles in 4 stages (16 KB), together the 160 KB of
+// LDS. At an even k-tile t a wave copies the A stage of tiles t + 4, t + 5
+// (8 copies) and B of tile t + 3 (4); at an odd one only B (4). A rows in an
+// A stage are 8 chunks of 16 bytes XOR-swizzled by (row / 2) % 8: a fragment
+// read (16 rows at one chunk per quarter wave) covers all 64 banks once.
+// Requires K a multiple of 64.
+// ---------------------------------------------------------------------------
+struct rv_g6_offs {
+    unsigned a[4];  // [parity of the k-tile within its A stage][k16 step]
+};
+
+__device__ __forceinline__ rv_g6_offs rv_g6_lane_offs(int wm, int lane) {
+    rv_g6_offs o;
+    const int ra = wm * 128 + (lane & 31), swz = (ra >> 1) & 7, h = lane >> 5;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) o.a[2 * p + q] = (unsigned)(ra * 128 + (((4 * p + 2 * q + h) ^ swz) << 4));
+    return o;
+}
+
+template <bool B_KN, int Q, int P>
+__device__ __forceinline__ void rv_g6_frags(rv_bf16x8 (&af)[4], rv_bf16x8 (&bf)[4], const unsigned short* As,
+                                            const unsigned short* Bs, const rv_g6_offs& oa, const rv_g5_offs& o) {
+    const char* pa = reinterpret_cast<const char*>(As) + oa.a[2 * P + Q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const rv_bf16x8*>(pa + i * 4096);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (B_KN) {
+            const char* pb = reinterpret_cast<const char*>(Bs) + o.b[j] + Q * 8192;
+            rv_s16x4 h[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+                h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) rv_s16x4*)(pb + half * 2048));
+            typedef __attribute__((ext_vector_type(8))) short s16x8;
+            s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+            bf[j] = __builtin_bit_cast(rv_bf16x8, v);
+        } else {
+            bf[j] = *reinterpret_cast<const rv_bf16x8*>(reinterpret_cast<const char*>(Bs) + o.b[Q] + j * 2048);
+        }
+    }
+}
+
+// The copies of one k-tile, numbered in issue order: with A (an even tile)
+// 0..7 copy the A stage (8 rows of 128 bytes each, rows 64 wave + 8 i), then
+// 8..11 B's k-tile; without, 0..3 B's k-tile. Issues those numbered [C0, C1).
+template <bool B_KN, bool WITH_A, int C0, int C1>
+__device__ __forceinline__ void rv_g6_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
+                                           const unsigned short* __restrict__ B, long long a_base, long long lda,
+                                           long long b_base, long long ldb, int ka, int kb, int wave,
+                                           const unsigned (&va)[2], const unsigned (&vb)[2]) {
+    constexpr int NA = WITH_A ? 8 : 0;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        if (i < C0 || i >= C1) continue;
+        const int r0 = wave * 64 + i * 8;
+        const char* g = reinterpret_cast<const char*>(A + a_base + (long long)r0 * lda + ka);
+        __builtin_amdgcn_global_load_lds((const void*)(g + va[i & 1]), (rv_lds_void*)(As + r0 * 64), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (NA + i < C0 || NA + i >= C1) continue;
+        if (B_KN) {
+            const int kr0 = wave * 8 + i * 2;
+            const char* g = reinterpret_cast<const char*>(B + b_base + (long long)(kb + kr0) * ldb);
+            __builtin_amdgcn_global_load_lds((const void*)(g + vb[i & 1]), (rv_lds_void*)(Bs + kr0 * 256), 16, 0, 0);
+        } else {
+            const int r0 = wave * 64 + i * 16;
+            const char* g = reinterpret_cast<const char*>(B + b_base + (long long)r0 * ldb + kb);
+            __builtin_amdgcn_global_load_lds((const void*)(g + vb[0]), (rv_lds_void*)(Bs + r0 * 32), 16, 0, 0);
+        }
+    }
+}
+
+template <bool B_KN, int MODE, class Epi, int PIN = 1, bool RAGGED = false, int PE = 3, int PO = 1>
+__device__ __forceinline__ void rv_gemm_w6_bf16(const unsigned short* __restrict__ A,
+                                                const unsigned short* __restrict__ B, long long a_off, long long lda,
+                                                long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
+                                                float* __restrict__ partials, int Mt = 0, int Nt = 0) {
+    __shared__ __attribute__((aligned(1024))) unsigned short a0[256 * 64], a1[256 * 64], a2[256 * 64];
+    __shared__ __attribute__((aligned(1024))) unsigned short b0[256 * 32], b1[256 * 32], b2[256 * 32], b3[256 * 32];
+    constexpr int NDS = B_KN ? 12 : 8;  // LDS read instructions per k16 step
+    // copies per k-tile (even: A stage + B tile, odd: B tile), those issued
+    // in its first k16 step, and the vmcnt that leaves only copies issued
+    // after the next k-tile's B tile in flight (the tile before, and this
+    // tile's first-step copies)
+    constexpr int CE = 12, CO = 4;
+    static_assert(PE >= 0 && PE <= CE && PO >= 0 && PO <= CO, "copies issued in a tile's first step");
+    constexpr int WAIT_E = CO + PE, WAIT_O = CE + PO;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+    const int ntiles = tiles_m * tiles_n;
+    int tm, tn;
+    {
+        int bid = blockIdx.x;
+        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
+            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
+            const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
+            tm = group * 4 + (within & 3);
+            tn = within >> 2;
+        } else {
+            tm = bid / tiles_n;
+            tn = bid % tiles_n;
+        }
+    }
+    const int mlo = tm * 256, nlo = tn * 256;
+    const int m0 = RAGGED ? min(mlo, M - 256) : mlo, n0 = RAGGED ? min(nlo, N - 256) : nlo;
+    const long long a_base = a_off + (long long)m0 * lda;
+    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
+    // lane parts of the copy addresses (bytes): A row lane / 8 of 8, chunk
+    // lane % 8 swizzled by (row / 2) % 8 = 4 (instruction parity) + lane / 16
+    unsigned va[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+        va[p] = (unsigned)(2 * ((lane >> 3) * lda + (((lane & 7) ^ (4 * p + (lane >> 4))) << 3)));
+    unsigned vb[2];
+    if (B_KN) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            vb[p] = (unsigned)(2 * ((lane >> 5) * ldb + (((lane & 31) ^ ((2 * p + (lane >> 5)) * 4)) << 3)));
+    } else {
+        vb[0] = vb[1] = (unsigned)(2 * ((lane >> 2) * ldb + (((lane & 3) ^ ((lane >> 4) & 3)) << 3)));
+    }
+    const rv_g5_offs fo = rv_g5_lane_offs<B_KN>(wm, wn, lane);
+    const rv_g6_offs fa = rv_g6_lane_offs(wm, lane);
+
+    rv_f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int KT = K / 32, KD = K / 64;
+    // copies past the end reload the last tile into a stage nobody reads,
+    // so every k-tile issues its fixed number of copies
+#define RV_G6_KA(d) (((d) < KD ? (d) : KD - 1) * 64)
+#define RV_G6_KB(t) (((t) < KT ? (t) : KT - 1) * 32)
+    // prologue: A stages of tiles 0-1 and 2-3, B tiles 0, 1, 2
+    rv_g6_copy<B_KN, true, 0, 8>(a0, b0, A, B, a_base, lda, b_base, ldb, RV_G6_KA(0), 0, wave, va, vb);
+    rv_g6_copy<B_KN, false, 0, 4>(a0, b0, A, B, a_base, lda, b_base, ldb, 0, RV_G6_KB(0), wave, va, vb);
+    rv_g6_copy<B_KN, true, 0, 8>(a1, b0, A, B, a_base, lda, b_base, ldb, RV_G6_KA(1), 0, wave, va, vb);
+    rv_g6_copy<B_KN, false, 0, 4>(a0, b1, A, B, a_base, lda, b_base, ldb, 0, RV_G6_KB(1), wave, va, vb);
+    rv_g6_copy<B_KN, false, 0, 4>(a0, b2, A, B, a_base, lda, b_base, ldb, 0, RV_G6_KB(2), wave, va, vb);
+    RV_WAIT_VM(16);  // A of tiles 0-1 and B of tile 0 have landed
+    RV_LDS_BARRIER();
+    rv_bf16x8 xa[4], xb[4], ya[4], yb[4];
+    rv_g6_frags<B_KN, 0, 0>(xa, xb, a0, b0, fa, fo);
+    // one k-tile: CA/PA/CB its A stage, parity and B stage; NA/PN/NB the next
+    // tile's; WA the A stage an even tile copies (tiles t + 4, t + 5), WB the
+    // B stage of tile t + 3
+#define RV_G6_STEP(EVEN, CA, PA, CB, NA, PN, NB, WA, WB, T)                                               \
+    {                                                                                                   \
+        const int t_ = (T);                                                                             \
+        __builtin_amdgcn_sched_barrier(0);                                                              \
+        rv_g6_frags<B_KN, 1, PA>(ya, yb, CA, CB, fa, fo);                                               \
+        rv_g6_copy<B_KN, EVEN, 0, (EVEN ? PE : PO)>(WA, WB, A, B, a_base, lda, b_base, ldb,             \
+                                                    RV_G6_KA(t_ / 2 + 2), RV_G6_KB(t_ + 3), wave, va, vb); \
+        rv_g5_step<4, 4>(acc, xa, xb);                                                                  \
+        if (PIN) rv_g5_pin<NDS, (EVEN ? PE : PO), PIN>();                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                              \
+        RV_WAIT_VM(EVEN ? WAIT_E : WAIT_O);                                                             \
+        RV_LDS_BARRIER();                                                                               \
+        __builtin_amdgcn_sched_barrier(0);                                                              \
+        rv_g6_frags<B_KN, 0, PN>(xa, xb, NA, NB, fa, fo);                                               \
+        rv_g6_copy<B_KN, EVEN, (EVEN ? PE : PO), (EVEN ? CE : CO)>(WA, WB, A, B, a_base, lda, b_base, ldb, \
+                                                                   RV_G6_KA(t_ / 2 + 2), RV_G6_KB(t_ + 3), wave, \
+                                                                   va, vb);                           \
+        rv_g5_step<4, 4>(acc, ya, yb);                                                                  \
+        if (PIN) rv_g5_pin<NDS, (EVEN ? CE - PE : CO - PO), PIN>();                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                              \
+        rv_g5_keep(acc);                                                                                \
+    }
+    // whole rounds of 12 k-tiles (A stages cycle every 6, B every 4), then
+    // the remaining KT % 12 (even) in order
+    int kt = 0;
+    for (; kt + 12 <= KT; kt += 12) {
+        RV_G6_STEP(true, a0, 0, b0, a0, 1, b1, a2, b3, kt)
+        RV_G6_STEP(false, a0, 1, b1, a1, 0, b2, a2, b0, kt + 1)
+        RV_G6_STEP(true, a1, 0, b2, a1, 1, b3, a0, b1, kt + 2)
+        RV_G6_STEP(false, a1, 1, b3, a2, 0, b0, a0, b2, kt + 3)
+        RV_G6_STEP(true, a2, 0, b0, a2, 1, b1, a1, b3, kt + 4)
+        RV_G6_STEP(false, a2, 1, b1, a0, 0, b2, a1, b0, kt + 5)
+        RV_G6_STEP(true, a0, 0, b2, a0, 1, b3, a2, b1, kt + 6)
+        RV_G6_STEP(false, a0, 1, b3, a1, 0, b0, a2, b2, kt + 7)
+        RV_G6_STEP(true, a1, 0, b0, a1, 1, b1, a0, b3, kt + 8)
+        RV_G6_STEP(false, a1, 1, b1, a2, 0, b2, a0, b0, kt + 9)
+        RV_G6_STEP(true, a2, 0, b2, a2, 1, b3, a1, b1, kt + 10)
+        RV_G6_STEP(false, a2, 1, b3, a0, 0, b0, a1, b2, kt + 11)
+    }
+    if (kt < KT) {
+        RV_G6_STEP(true, a0, 0, b0, a0, 1, b1, a2, b3, kt)
+        RV_G6_STEP(false, a0, 1, b1, a1, 0, b2, a2, b0, kt + 1)
+        if (kt + 2 < KT) {
+            RV_G6_STEP(true, a1, 0, b2, a1, 1, b3, a0, b1, kt + 2)
+            RV_G6_STEP(false, a1, 1, b3, a2, 0, b0, a0, b2, kt + 3)
+            if (kt + 4 < KT) {
+                RV_G6_STEP(true, a2, 0, b0, a2, 1, b1, a1, b3, kt + 4)
+                RV_G6_STEP(false, a2, 1, b1, a0, 0, b2, a1, b0, kt + 5)
+                if (kt + 6 < KT) {
+                    RV_G6_STEP(true, a0, 0, b2, a0, 1, b3, a2, b1, kt + 6)
+                    RV_G6_STEP(false, a0, 1, b3, a1, 0, b0, a2, b2, kt + 7)
+                    if (kt + 8 < KT) {
+                        RV_G6_STEP(true, a1, 0, b0, a1, 1, b1, a0, b3, kt + 8)
+                        RV_G6_STEP(false, a1, 1, b1, a2, 0, b2, a0, b0, kt + 9)
+                    }
+                }
+            }
+        }
+    }
+#undef RV_G6_STEP
+#undef RV_G6_KA
+#undef RV_G6_KB
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float* lds_red = reinterpret_cast<float*>(a0);
+
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("" : "+a"(acc[i][j]));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int n = n0 + wn * 128 + j * 32 + (lane & 31);
+                if (RAGGED && !(m >= mlo && m < Mt && n >= nlo && n < Nt)) continue;
+                const float v = epi(acc[i][j][r], m, n);
+                if (MODE == 0)
+                    epi.store(m, n, v);
+                else
+                    part = part + v;
+            }
+        }
+    if (MODE == 1) {
+        part = rv_group_sum<64>(part);
+        if (lane == 0) lds_red[wave] = part;
+        __syncthreads();
+        if (tid == 0) partials[blockIdx.x] = ((lds_red[0] + lds_red[1]) + lds_red[2]) + lds_red[3];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Fused attention forward, the CUSTOM sdpa_fwd kernel (limn README, "The op
 // set": the one CUSTOM kernel, saving the row's logsumexp beside the output;
 // Tiki README, "Write the attention kernel at the algorithm level": a

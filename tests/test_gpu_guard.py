@@ -73,11 +73,11 @@ CASES = {
     "split_cols": (lambda: synth.reduce((40009, 77), (0,)), lambda: synth.inputs_reduce((40009, 77)),
                    {("SPLIT", "split_cols"), ("FOLD", "fold_cells")}),
     "mfma_fold_ragged": (lambda: synth.gemm_relu2_sum(257, 129, 65), lambda: synth.inputs_gemm(257, 129, 65),
-                         {("EW", "rowmajor"), ("MFMA", "gemm_w4"), ("FOLD", "fold")}),
+                         {("EW", "rowmajor"), ("MFMA", "gemm_w6"), ("FOLD", "fold")}),
     "mfma_store_ragged": (lambda: synth.gemm_bf16(300, 257, 64), lambda: synth.inputs_gemm(300, 257, 64),
-                          {("MFMA", "gemm_w4")}),
+                          {("MFMA", "gemm_w6")}),
     "mfma_store_shifted": (lambda: synth.gemm_bf16(520, 264, 96), lambda: synth.inputs_gemm(520, 264, 96),
-                           {("MFMA", "gemm_w4")}),
+                           {("MFMA", "gemm_w6")}),
     "attn": (lambda: synth.attention(2, 300, 333, 64, True),
              lambda: synth.inputs_attention(2, 300, 333, 64), {("ATTN", "attn_fwd")}),
     "attn_chunked": (lambda: synth.attention(1, 4100, 4100, 32, True),

@@ -233,7 +233,7 @@ def test_gemm_operand_windows_bit_exact(m, n, k, pa, pb, oa, ob):
     spec = _gemm_strided(m, n, k, pa, pb, oa, ob)
     prog = _prog(spec)
     kd = prog.describe()["kernels"][0]
-    assert kd["class"] == "MFMA" and kd["plan"] == "gemm_w4"
+    assert kd["class"] == "MFMA" and kd["plan"] in ("gemm_w4", "gemm_w6")
     rng = np.random.default_rng(17)
     inp = {"A": synth.to_bf16_bits(rng.integers(-2, 3, (m, k + pa)).astype(np.float32)),
            "B": synth.to_bf16_bits(rng.integers(-2, 3, (k, n + pb)).astype(np.float32))}
@@ -242,14 +242,18 @@ def test_gemm_operand_windows_bit_exact(m, n, k, pa, pb, oa, ob):
     assert got.tobytes() == ref.tobytes()
 
 
-# the pipeline settings the plan's environment knobs select (the default is
-# five stages, 2 early copies, pinned interleaving): every one stays
-# bit-exact on integer-valued operands, with B stored [k][n] and [n][k]
+# the kernels and pipeline settings the plan's environment knobs select (the
+# default: A 64 deep, 3 + 1 early copies, pinned interleaving; the 32-deep
+# kernel: five stages, 2 early copies): every one stays bit-exact on
+# integer-valued operands, with B stored [k][n] and [n][k]
 @pytest.mark.parametrize("knobs", [
-    {"RV_GEMM_W4_STAGES": "4", "RV_GEMM_W4_SPLIT": "8"},
-    {"RV_GEMM_W4_SPLIT": "0"},
-    {"RV_GEMM_W4_PIN": "0"},
-    {"RV_GEMM_W4_PIN": "2"},
+    {"RV_GEMM_W6_PE": "0", "RV_GEMM_W6_PO": "0"},
+    {"RV_GEMM_W6_PE": "12", "RV_GEMM_W6_PO": "4"},
+    {"RV_GEMM_PIN": "0"},
+    {"RV_GEMM_PIN": "2"},
+    {"RV_GEMM_KERNEL": "w4"},
+    {"RV_GEMM_KERNEL": "w4", "RV_GEMM_W4_STAGES": "4", "RV_GEMM_W4_SPLIT": "8"},
+    {"RV_GEMM_KERNEL": "w4", "RV_GEMM_W4_SPLIT": "0", "RV_GEMM_KROT": "3", "RV_GEMM_REMAP": "0"},
 ])
 def test_gemm_kernel_variants_bit_exact(monkeypatch, knobs):
     m, n, k = 512, 256, 448
