@@ -59,12 +59,12 @@ def check_device_header(verbose: bool = False) -> None:
                 "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
                 "chk17(const unsigned short* a, const unsigned short* b, float* p) {\n"
                 "  rv_gemm_w4_bf16<true, 1, E, 2, 1, 5, true>(a, b, 0, 4104, 0, 4104, 4100, 4104, 4128, E{}, p, 4100, 4097); }\n"
-                "extern \"C\" __global__ void __launch_bounds__(512) chk12(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
-                "float* l) { rv_attn_fwd_bf16<32, true, false>(q, k, v, o, l, 1000, 1000, 0.25f); }\n"
-                "extern \"C\" __global__ void __launch_bounds__(512) chk13(const unsigned short* q, const unsigned short* k, const unsigned short* v, "
-                "unsigned short* o, float* l) { rv_attn_fwd_bf16<64, false, true>(q, k, v, o, l, 100, 333, 0.18f); }\n"
-                "extern \"C\" __global__ void __launch_bounds__(512) chk14(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
-                "float* l) { rv_attn_fwd_bf16<128, true, false>(q, k, v, o, nullptr, 130, 130, 0.1f); }\n")
+                "extern \"C\" __global__ void __launch_bounds__(256) chk12(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
+                "float* l) { rv_attn_fwd_bf16<32, true, false, 4>(q, k, v, o, l, 1000, 1000, 0.25f); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(256) chk13(const unsigned short* q, const unsigned short* k, const unsigned short* v, "
+                "unsigned short* o, float* l) { rv_attn_fwd_bf16<64, false, true, 3>(q, k, v, o, l, 100, 333, 0.18f); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(256) chk14(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
+                "float* l) { rv_attn_fwd_bf16<128, true, false, 2>(q, k, v, o, nullptr, 130, 130, 0.1f); }\n")
     cmd = [HIPCC] + GPU_FLAGS + ["--cuda-device-only", "-c", tu, "-o", os.path.join(out_dir, "device_check.o")]
     if verbose:
         print(" ".join(cmd))

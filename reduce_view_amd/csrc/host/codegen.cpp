@@ -279,10 +279,20 @@ struct Gen {
 
     std::string header() {
         // a 256 x 256 contraction tile on 4 waves keeps 256 accumulators per
-        // lane: one wave per SIMD, so the whole register file is the wave's
-        const bool one_wave = k.cls == KClass::MFMA;
-        return "extern \"C\" __global__ void __launch_bounds__(" + std::to_string(k.block[0]) + ") " +
-               (one_wave ? "__attribute__((amdgpu_waves_per_eu(1, 1))) " : "") + k.name + "(" + signature() + ")";
+        // lane: one wave per SIMD, so the whole register file is the wave's.
+        // The attention forward (4 waves, one per SIMD) asks for several
+        // waves per SIMD: 4 at head width 32, 3 at 64, 2 at 128, which also
+        // keeps its matrix results in ordinary vector registers (with a
+        // budget of more than 256 registers the compiler places them in the
+        // accumulation registers and moves every score in and out)
+        std::string occ;
+        if (k.cls == KClass::MFMA) occ = "__attribute__((amdgpu_waves_per_eu(1, 1))) ";
+        if (k.cls == KClass::ATTN && !k.attn_merge) {
+            const int64_t D = k.domain[2];
+            occ = fmt("__attribute__((amdgpu_waves_per_eu(%d))) ", D == 32 ? 4 : D == 64 ? 3 : 2);
+        }
+        return "extern \"C\" __global__ void __launch_bounds__(" + std::to_string(k.block[0]) + ") " + occ + k.name +
+               "(" + signature() + ")";
     }
 
     // a load is streaming (nontemporal) when no domain dim of size > 1 has
@@ -2127,15 +2137,7 @@ std::string Gen::gen_attn() {
           << ", " << ml << ", " << Tq << ", " << Tk << ", " << k.attn_chunk << ", " << k.attn_cmax << ");\n";
         return "@@BODY@@" + b.str();
     }
-    int NG = 2, KT = 64;  // plan values (lower.cpp)
-    {
-        const char* c = k.plan_json.c_str();
-        const char* at = strstr(c, "\"key_groups\":");
-        if (at) NG = atoi(at + strlen("\"key_groups\":"));
-        at = strstr(c, "\"key_tile\":");
-        if (at) KT = atoi(at + strlen("\"key_tile\":"));
-    }
-    b << "  rv_attn_fwd_bf16<" << D << ", " << causal << ", " << obf << ", " << NG << ", " << KT << ">(" << q << ", "
+    b << "  rv_attn_fwd_bf16<" << D << ", " << causal << ", " << obf << ", " << k.attn_stages << ">(" << q << ", "
       << kp << ", " << v << ", " << o << ", " << l << ", " << Tq << ", " << Tk << ", " << fmt("%a", sl2) << "f";
     if (k.attn_chunk > 0) {
         // the (query block, key chunk) of every workgroup, longest blocks first

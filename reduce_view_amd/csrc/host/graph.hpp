@@ -160,6 +160,7 @@ struct Kernel {
     std::vector<unsigned> attn_map;
     int attn_reg_o = -1, attn_reg_ml = -1;
     bool attn_merge = false;
+    int attn_stages = 0;  // LDS stages of 64-key K/V tiles
     // SCATTER: one step of a scatter-add into `sc_out`. Domain: the index's
     // shape; ex sc_index / sc_values over it, sc_base over the output's.
     //   "atomic": every position adds its value with an atomic add (the

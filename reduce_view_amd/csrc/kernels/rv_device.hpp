@@ -798,27 +798,39 @@ __device__ __forceinline__ void rv_gemm_w6_bf16(const unsigned short* __restrict
 // The scores are formed transposed, S^T = K Q^T on v_mfma_f32_32x32x16_bf16,
 // so a lane of the 32 x 32 result holds 16 scores of ONE query (its column):
 // a query's max and sum need one exchange with lane ^ 32 (v_permlane32_swap),
-// and rescaling the
-// output accumulator (also transposed, O^T += V^T P^T) is a scalar per lane.
-// The probabilities never leave registers: rounded to bfloat16 they are the
-// B operand of the second product as they stand. The key order the result
-// layout leaves in a lane (keys 4 h .. 4 h + 3 and 8 + 4 h .. of each 16,
-// h = lane / 32) is matched by reading V^T from LDS in that order.
-// Scores are carried in base 2: the reference m follows the running maximum
-// of s * scale * log2 e (moved only when a score passes it by more than 8),
-// and each exponential is v_exp_f32 of one fma.
+// and rescaling the output accumulator (also transposed, O^T += V^T P^T) is a
+// scalar per lane. The probabilities never leave registers: rounded to
+// bfloat16 they are the B operand of the second product as they stand. The
+// key order the result layout leaves in a lane (keys 4 h .. 4 h + 3 and
+// 8 + 4 h .. of each 16, h = lane / 32) is matched by reading V^T from LDS in
+// that order. Scores are carried in base 2 (s * scale * log2 e), and each
+// exponential is v_exp_f32 of one fma against the reference m.
 //
-// Workgroup: NG groups of 4 waves (NG = 2; 4 measured no faster). Waves
-// w, w + 4, .. own the same 32 queries and split the keys: 64-key steps go
-// round the groups, each keeping its own (m, l, accumulator); at the end the
-// other groups hand their states through LDS and the first merges them in
-// group order (rescaling to the larger maximum) and writes O and L. K and V
-// tiles of KT keys (128 for head widths up to 64) are staged in LDS
-// key-major with padded pitches, double buffered; the V^T operand comes out
-// of the transposing LDS read. With CAUSAL, key j is hidden from query i
-// when j > i: a workgroup stops at the tile holding its last query, a wave
-// skips steps past its queries, and the workgroups with the most keys are
-// started first.
+// The reference m is not the running maximum: the probabilities of a tile
+// are taken against the m in hand, and only when a query's sum over the tile
+// passes 2^8 (or is not finite) does the wave find that tile's maximum, move
+// m there, rescale (l, accumulator) and take the tile again; a wave's first
+// tile (m = -inf) takes that path directly, so m starts at a maximum and
+// later scores far below it fall away as they would against the running
+// one. Every probability stays below 2^8, which float32 sums and the bf16
+// operand carry with the same relative rounding, and O / l and m + log2 l do
+// not depend on which m was used; the per-tile maximum is gone from the
+// common path, whose vector work per score is one fma, one exponential, one
+// add and half a conversion.
+//
+// Workgroup: 4 waves, 32 queries each (128 per workgroup). K and V tiles of
+// 64 keys go global -> LDS with global_load_lds_dwordx4 (no VGPR staging, no
+// LDS stores), NS stages deep, the copies of a tile spread over the 4 waves
+// (each copy moves 1 KB: 512 / D key rows). A key row's 16-byte chunks are
+// XOR-swizzled (rv_attn_swz): a K fragment read (16 rows at one chunk per
+// quarter wave) and a transposing V read (4 rows x 4 chunks per half wave)
+// each cover the 64 banks once. Rows past Tk are copies of row Tk - 1, their
+// scores masked to -inf. With CAUSAL, key j is hidden from query i when
+// j > i: a workgroup stops at the tile holding its last query, a wave skips
+// tiles past its queries, and the workgroups with the most keys start first.
+// Long rows are split into key chunks over workgroups (wmap); a chunk writes
+// its (m, l) and unnormalised accumulator, and rv_attn_merge_chunks folds
+// them in chunk order.
 // ---------------------------------------------------------------------------
 // max and sum over the lane pair (l, l ^ 32) with v_permlane32_swap (no LDS
 // round trip): swapped with itself, the pair of results is (lower half's
@@ -841,7 +853,22 @@ __device__ __forceinline__ void rv_attn_merge(float& m, float& l, float m2, floa
     m = mn;
 }
 
-template <int D, bool CAUSAL, bool OUT_BF16, int NG = 2, int KT = 64>
+// XOR swizzle of key row r's 16-byte chunks in a tile (D / 8 chunks a row,
+// rows 2 D bytes apart): chunk c sits at slot c ^ rv_attn_swz<D>(r). A bit
+// permutation of the row's position within its 256-byte line run, chosen so
+// that rows sharing banks take disjoint chunk slots for both read patterns.
+template <int D>
+__device__ __forceinline__ int rv_attn_swz(int r) {
+    if (D == 32) return (r >> 2) & 3;
+    if (D == 64) {
+        const int x = (r >> 1) & 7;
+        return ((x & 1) << 2) | (x & 2) | (x >> 2);
+    }
+    const int x = r & 15;
+    return ((x & 3) << 2) | (x >> 2);
+}
+
+template <int D, bool CAUSAL, bool OUT_BF16, int NS>
 __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restrict__ Q,
                                                  const unsigned short* __restrict__ K,
                                                  const unsigned short* __restrict__ V, void* __restrict__ O,
@@ -849,23 +876,19 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
                                                  const unsigned* __restrict__ wmap = nullptr, int CK = 0,
                                                  float* __restrict__ opart = nullptr,
                                                  float* __restrict__ mlpart = nullptr, int CMAX = 1) {
-    // NG groups of 4 waves split the keys; KT (a multiple of 64) keys per tile
-    constexpr int NT = 256 * NG;              // threads
-    constexpr int KP = D + 8;                 // K tile pitch (bf16): conflict-free 16-byte fragment reads
-    constexpr int VP = D + 16;                // V tile pitch (bf16): the 4 rows of a transposing read hit
-                                              // disjoint banks (row stride D/2 + 8 banks)
-    constexpr int CH = KT * D / 8;            // 16-byte chunks per tile
-    constexpr int NCH = (CH + NT - 1) / NT;   // chunks per thread
-    constexpr int TILE_BYTES = 2 * (KT * KP + KT * VP) * 2;
-    constexpr int MERGE_BYTES = (NG - 1) * 4 * 64 * (16 * (D / 32) + 2) * 4;
-    constexpr int SMEM_BYTES = TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES;
-    __shared__ __attribute__((aligned(16))) unsigned short smem[SMEM_BYTES / 2];
-    unsigned short* ks = smem;                     // [2][KT * KP]
-    unsigned short* vs = smem + 2 * KT * KP;       // [2][KT * VP], key-major
+    static_assert(D == 32 || D == 64 || D == 128, "head width");
+    static_assert(NS >= 2 && NS <= 4, "stages");
+    constexpr int TB = 64 * D * 2;  // bytes of one 64-key K (or V) tile
+    constexpr int CPW = D / 32;     // copies of each of K and V per wave per tile
+    constexpr int CPR = D / 8;      // 16-byte chunks per key row
+    // one array per stage: the compiler tells the copies into one stage from
+    // reads of another only by the array they address (a read of an array
+    // with copies in flight waits for all of them)
+    __shared__ __attribute__((aligned(1024))) unsigned char s0[2 * TB], s1[2 * TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char s2[NS > 2 ? 2 * TB : 16], s3[NS > 3 ? 2 * TB : 16];
     // the wave index in a scalar register: the per-wave bounds below are
     // scalar branches, with no divergent control flow around the MFMAs
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave >> 2, wq = wave & 3;  // key group, query wave
     const int ql = lane & 31, hh = lane >> 5;
     // which query block and which chunk of its keys: from the map when the
     // keys are split over workgroups (longest blocks first), else one
@@ -879,60 +902,74 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
         jb = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
     }
     const int qb = jb * 128;
-    const int q0 = qb + wq * 32;
+    const int q0 = qb + wave * 32;
     const int qi = q0 + ql;
     const long long qbase = (long long)blockIdx.y * Tq;
     const long long kbase = (long long)blockIdx.y * Tk;
-    const rv_u32x4 zero4 = {0u, 0u, 0u, 0u};
     const float ninf = -__builtin_inff();
 
-    // Loads are unconditional, with rows clamped into range, so no branch
-    // surrounds them: a query row past Tq computes on row Tq - 1 and is never
-    // stored; a key past Tk is masked to -inf (its V row is stored as zeros).
+    int kend = Tk;
+    if (CAUSAL) kend = min(Tk, min(Tq, qb + 128));
+    // this workgroup's keys: [k0, k1), nt tiles of 64
+    const int nchunks = wmap != nullptr ? (kend + CK - 1) / CK : 1;
+    const int k0 = wmap != nullptr ? ch * CK : 0;
+    const int k1 = wmap != nullptr ? min(kend, k0 + CK) : kend;
+    const int nt = (k1 - k0 + 63) / 64;
+
+    // copy i of this wave (copy j = wave + 4 i of the tile, 1 KB of LDS at
+    // 1024 j): its lane's key row within the tile and global byte column
+    int crow[CPW], ccol[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int n = 64 * (wave + 4 * i) + lane, r = n / CPR;
+        crow[i] = r;
+        ccol[i] = 16 * ((n % CPR) ^ rv_attn_swz<D>(r));
+    }
+    auto issue = [&](unsigned char* ks, int t) {  // the copies of tile t into stage ks
+        const int kt0 = k0 + 64 * t;
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const long long row = kbase + min(kt0 + crow[i], Tk - 1);
+            const char* gk = reinterpret_cast<const char*>(K) + row * (2 * D) + ccol[i];
+            const char* gv = reinterpret_cast<const char*>(V) + row * (2 * D) + ccol[i];
+            __builtin_amdgcn_global_load_lds((const void*)gk, (rv_lds_void*)(ks + 1024 * (wave + 4 * i)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)gv, (rv_lds_void*)(ks + TB + 1024 * (wave + 4 * i)), 16, 0,
+                                             0);
+        }
+    };
+    // Loads are unconditional, with rows clamped into range: a query row
+    // past Tq computes on row Tq - 1 and is never stored. q is
+    // loaded before the first copies: the loop's first wait covers it.
     rv_bf16x8 qf[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
         rv_u32x4 w = *reinterpret_cast<const rv_u32x4*>(Q + (qbase + min(qi, Tq - 1)) * D + 16 * s + 8 * hh);
-        // pinned here (an empty asm that takes the value): q must have arrived
-        // before the key loop, or the wait for it inside the loop would also
-        // wait for the next tile's loads
-        asm volatile("" : "+v"(w));
         qf[s] = __builtin_bit_cast(rv_bf16x8, w);
     }
 
-    rv_u32x4 kr[NCH], vr[NCH];
-    auto load_tile = [&](int kb) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + NT * i;
-            if (CH % NT == 0 || c < CH) {
-                const int key = c / (D / 8), dc = c % (D / 8);
-                const long long off = (kbase + min(kb + key, Tk - 1)) * D + dc * 8;
-                kr[i] = *reinterpret_cast<const rv_u32x4*>(K + off);
-                vr[i] = *reinterpret_cast<const rv_u32x4*>(V + off);
-            }
-        }
-    };
-    auto store_tile = [&](int b, int kb) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = tid + NT * i;
-            if (CH % NT == 0 || c < CH) {
-                const int key = c / (D / 8), dc = c % (D / 8);
-                *reinterpret_cast<rv_u32x4*>(&ks[b * KT * KP + key * KP + dc * 8]) = kr[i];
-                const rv_u32x4 vv = kb + key < Tk ? vr[i] : zero4;
-                *reinterpret_cast<rv_u32x4*>(&vs[b * KT * VP + key * VP + dc * 8]) = vv;
-            }
-        }
-    };
+    issue(s0, 0);
+    if (NS > 2) issue(s1, min(1, nt - 1));
+    if (NS > 3) issue(s2, min(2, nt - 1));
 
-    int kend = Tk;
-    if (CAUSAL) kend = min(Tk, min(Tq, qb + 128));
-    // this workgroup's keys: [k0, k1)
-    const int nchunks = wmap != nullptr ? (kend + CK - 1) / CK : 1;
-    const int k0 = wmap != nullptr ? ch * CK : 0;
-    const int k1 = wmap != nullptr ? min(kend, k0 + CK) : kend;
-    const int nt = (k1 - k0 + KT - 1) / KT;
+    // fragment offsets within a stage: K (row ql of a 32-key half, chunk
+    // 2 s + hh; the half adds 64 D bytes) and the two transposing V reads
+    // of head-dim tile dt (rows 4 (g / 2) + j / 4 (+ 8) of each 16 keys,
+    // 4 dims at 16 (g % 2) + 4 (j % 4); the 16-key step adds 32 D bytes)
+    unsigned koff[D / 16], voff[D / 32][2];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) koff[s] = (unsigned)(ql * 2 * D + 16 * ((2 * s + hh) ^ rv_attn_swz<D>(ql)));
+    {
+        const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = 4 * (g >> 1) + (j >> 2) + 8 * h;
+                const int col = dt * 32 + (g & 1) * 16 + (j & 3) * 4;
+                voff[dt][h] = (unsigned)(TB + row * 2 * D + 16 * ((col >> 3) ^ rv_attn_swz<D>(row)) + (col & 7) * 2);
+            }
+    }
+
     rv_f32x16 oacc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -940,149 +977,165 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
         for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
     float m = ninf, l = 0.0f;
 
-    load_tile(k0);
-    store_tile(0, k0);
-    __syncthreads();
-    for (int t = 0; t < nt; ++t) {
-        const int b = t & 1;
-        if (t + 1 < nt) load_tile(k0 + (t + 1) * KT);
+    // S^T for the 64 keys of tile t (stage st) as two 32 x 32 tiles (A = K
+    // rows: lane = key ql of the half, head dims 16 s + 8 hh ..; B = Q^T),
+    // hidden keys set to -inf
+    auto scores = [&](const unsigned char* st, int kb, float (&sv)[32]) {
+        rv_f32x16 sacc[2];
 #pragma unroll
-        for (int sub = 0; sub < KT / 64; ++sub) {
-            const int step = t * (KT / 64) + sub;
-            const int kb = k0 + step * 64;
-            // alternate 64-key steps between the two groups; skip steps whose
-            // keys are all hidden from this wave's queries (both wave-uniform)
-            if (step % NG != grp || kb >= k1 || (CAUSAL && kb > q0 + 31)) continue;
-            const unsigned short* kt = ks + b * KT * KP + sub * 64 * KP;
-            const unsigned short* vt = vs + b * KT * VP + sub * 64 * VP;
-            // S^T for 64 keys as two 32 x 32 tiles: A = K rows (lane: key ql
-            // of the tile, head dims 16 s + 8 hh ..), B = Q^T
-            rv_f32x16 sacc[2];
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int r = 0; r < 16; ++r) sacc[u][r] = 0.0f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[u][r] = 0.0f;
-#pragma unroll
-                for (int s = 0; s < D / 16; ++s) {
-                    const rv_bf16x8 af = *reinterpret_cast<const rv_bf16x8*>(&kt[(u * 32 + ql) * KP + 16 * s + 8 * hh]);
-                    sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[u], 0, 0, 0);
-                }
+            for (int s = 0; s < D / 16; ++s) {
+                const rv_bf16x8 af = *reinterpret_cast<const rv_bf16x8*>(st + koff[s] + u * 64 * D);
+                sacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[s], sacc[u], 0, 0, 0);
             }
-            // online softmax of this lane's query over the 64 keys
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sv[16 * u + r] = sacc[u][r];
+        if (kb + 64 > k1 || (CAUSAL && kb + 63 > q0)) {  // wave-uniform
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                const int key = kb + (r >> 4) * 32 + ((r & 15) >> 2) * 8 + hh * 4 + (r & 3);
+                if (key >= k1 || (CAUSAL && key > qi)) sv[r] = ninf;
+            }
+        }
+    };
+    // probabilities of the scores against m, and their sum over the
+    // query's 64 keys (four interleaved partial sums, then a tree: four
+    // short dependency chains instead of one of 32 adds); while every key
+    // seen is hidden (m = -inf) every score is -inf and exp2(-inf - 0) = 0
+    auto probs = [&](const float (&sv)[32], float (&pr)[32]) {
+        const float mns = m == ninf ? 0.0f : m;
+        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sl2, -mns));
+            ps[r & 3] = ps[r & 3] + pr[r];
+        }
+        return rv_pair_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    };
+    // one tile: cur its stage, nxt the stage of tile t + NS - 1
+    auto step = [&](const unsigned char* cur, unsigned char* nxt, int t) {
+        // tile t has landed for this wave (the NS - 2 after it may still
+        // fly), then for every wave; after the barrier nobody reads tile
+        // t - 1's stage, which the copies of tile t + NS - 1 overwrite. Past
+        // the last tile the copies repeat it into stages nobody reads again:
+        // with no branch around them, every copy names its stage's array
+        // (copies under a branch get merged across stages, and a read of any
+        // stage then waits for all of them).
+        RV_WAIT_VM(2 * CPW * (NS - 2));
+        RV_LDS_BARRIER();
+        issue(nxt, min(t + NS - 1, nt - 1));
+        const int kb = k0 + 64 * t;
+        // keys all hidden from this wave's queries (wave-uniform)
+        if (CAUSAL && kb > q0 + 31) return;
+        float pr[32];
+        float ps = 0.0f;
+        // the first tile a wave takes (m still -inf; it holds a key every
+        // query of the wave sees) goes straight to the exact path
+        bool over = m == ninf;
+        bool slow = __builtin_amdgcn_ballot_w64(over) != 0;
+        if (!slow) {
             float sv[32];
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sv[16 * u + r] = sacc[u][r];
-            if (kb + 64 > k1 || (CAUSAL && kb + 63 > q0)) {  // wave-uniform
-#pragma unroll
-                for (int r = 0; r < 32; ++r) {
-                    const int key = kb + (r >> 4) * 32 + ((r & 15) >> 2) * 8 + hh * 4 + (r & 3);
-                    if (key >= k1 || (CAUSAL && key > qi)) sv[r] = ninf;
-                }
-            }
+            scores(cur, kb, sv);
+            ps = probs(sv, pr);
+            over = !(ps <= 256.0f);
+            slow = __builtin_amdgcn_ballot_w64(over) != 0;
+        }
+        if (slow) {  // wave-uniform, rare
+            // the scores again (cheaper than holding them), the tile's
+            // maximum, the rescale, the probabilities against the new m
+            float sv[32];
+            scores(cur, kb, sv);
             float cm = sv[0];
 #pragma unroll
             for (int r = 1; r < 32; ++r) cm = fmaxf(cm, sv[r]);
-            cm = rv_pair_max(cm);
-            // max(s) * c equals max(s * c) for c > 0 (rounding is monotonic)
-            const float cm2 = cm * sl2;
-            // The reference m moves only when a score passes it by more than
-            // 8 (base 2): below that the probabilities stay under 2^8, which
-            // float32 sums and the bf16 operand carry with the same relative
-            // rounding, and O / l and m + log2 l do not depend on which m was
-            // used. So the rescale (an exponential and a multiply per
-            // accumulator) runs only on the rare steps that move m; the first
-            // step with a visible key always does (m = -inf).
-            const bool grow = cm2 > m + 8.0f;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
-                const float mn = grow ? cm2 : m;
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;  // exp2(-inf) = 0
-                l = l * alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-                m = mn;
-            }
-            // while every key seen is hidden (m = -inf) every score is -inf
-            // and exp2(-inf - 0) = 0: no branch, no separate zero fill
-            const float mns = m == ninf ? 0.0f : m;
-            float pr[32];
-            float ps = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sl2, -mns));
-                ps = ps + pr[r];
-            }
-            ps = rv_pair_sum(ps);
-            l = l + ps;
-            // O^T += V^T P^T over the 64 keys (four k16 steps)
-            // P to bf16 two at a time (one v_cvt_pk_bf16_f32 per pair)
-            rv_bf16x8 pb[4];
-            typedef __attribute__((ext_vector_type(2))) float f32x2;
-            typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x2 f = {pr[8 * s + 2 * i], pr[8 * s + 2 * i + 1]};
-                    const bf16x2 h = __builtin_convertvector(f, bf16x2);
-                    pb[s][2 * i] = h[0];
-                    pb[s][2 * i + 1] = h[1];
-                }
+            // max(s) * c equals max(s * c) for c > 0 (rounding is monotonic);
+            // a sum past 2^8 has a probability past 4, so cm2 > m there
+            const float cm2 = rv_pair_max(cm) * sl2;
+            const bool grow = over && cm2 > m;
+            const float mn = grow ? cm2 : m;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m - mn) : 1.0f;  // exp2(-inf) = 0
+            l = l * alpha;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    // k16 step s covers the tile u = s / 2, keys 16 (s % 2) + 4 hh + 0..3
-                    // and + 8: two transposing reads of the key-major V tile, in
-                    // each group of 16 lanes one row of 4 keys per 4 lanes and one
-                    // column (head dim) per lane
-                    const int g = lane >> 4, j = lane & 15;
-                    const int row = (s >> 1) * 32 + 16 * (s & 1) + 4 * (g >> 1) + (j >> 2);
-                    const int col = dt * 32 + (g & 1) * 16 + (j & 3) * 4;
-                    typedef __attribute__((address_space(3))) rv_s16x4 lds_s16x4;
-                    typedef __attribute__((address_space(3))) unsigned short lds_u16;
-                    const rv_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)((lds_u16*)vt + row * VP + col));
-                    const rv_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4*)((lds_u16*)vt + (row + 8) * VP + col));
-                    typedef __attribute__((ext_vector_type(8))) short s16x8;
-                    const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(rv_bf16x8, a8), pb[s],
-                                                                       oacc[dt], 0, 0, 0);
-                }
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            m = mn;
+            ps = probs(sv, pr);
         }
-        if (t + 1 < nt) store_tile(b ^ 1, k0 + (t + 1) * KT);
-        __syncthreads();
-    }
-    // merge: groups 1 .. NG-1 hand (m, l, accumulator) to group 0 through
-    // LDS (the tile buffers are free after the loop's last barrier), which
-    // folds them in group order
-    float* xs = reinterpret_cast<float*>(smem);
-    constexpr int PER = 16 * (D / 32) + 2;
-    if (grp > 0) {
-        float* mine = xs + (((grp - 1) * 4 + wq) * 64 + lane) * PER;
-        mine[0] = m;
-        mine[1] = l;
+        l = l + ps;
+        // O^T += V^T P^T over the 64 keys (four k16 steps); P to bf16 two
+        // at a time (one v_cvt_pk_bf16_f32 per pair)
+        rv_bf16x8 pb[4];
+        typedef __attribute__((ext_vector_type(2))) float f32x2;
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x2 f = {pr[8 * s + 2 * i], pr[8 * s + 2 * i + 1]};
+                const bf16x2 h = __builtin_convertvector(f, bf16x2);
+                pb[s][2 * i] = h[0];
+                pb[s][2 * i + 1] = h[1];
+            }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mine[2 + 16 * dt + r] = oacc[dt][r];
+            for (int s = 0; s < 4; ++s) {
+                // k16 step s: keys 16 s + 4 hh + 0..3 and + 8, two
+                // transposing reads of the key-major V tile
+                typedef __attribute__((address_space(3))) rv_s16x4 lds_s16x4;
+                typedef __attribute__((address_space(3))) unsigned char lds_u8;
+                const lds_u8* vb = (const lds_u8*)(cur + s * 32 * D);
+                const rv_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[dt][0]));
+                const rv_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + voff[dt][1]));
+                typedef __attribute__((ext_vector_type(8))) short s16x8;
+                const s16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(rv_bf16x8, a8), pb[s], oacc[dt],
+                                                                   0, 0, 0);
+            }
+    };
+    // the stages cycle every NS tiles: unrolled so that every LDS access
+    // names its stage's array
+    int t = 0;
+    if (NS == 2) {
+        for (; t + 2 <= nt; t += 2) {
+            step(s0, s1, t);
+            step(s1, s0, t + 1);
+        }
+        if (t < nt) step(s0, s1, t);
+    } else if (NS == 3) {
+        for (; t + 3 <= nt; t += 3) {
+            step(s0, s2, t);
+            step(s1, s0, t + 1);
+            step(s2, s1, t + 2);
+        }
+        if (t < nt) {
+            step(s0, s2, t);
+            if (t + 1 < nt) step(s1, s0, t + 1);
+        }
+    } else {
+        for (; t + 4 <= nt; t += 4) {
+            step(s0, s3, t);
+            step(s1, s0, t + 1);
+            step(s2, s1, t + 2);
+            step(s3, s2, t + 3);
+        }
+        if (t < nt) {
+            step(s0, s3, t);
+            if (t + 1 < nt) {
+                step(s1, s0, t + 1);
+                if (t + 2 < nt) step(s2, s1, t + 2);
+            }
+        }
     }
-    __syncthreads();
-    if (grp > 0) return;
-#pragma unroll
-    for (int g = 1; g < NG; ++g) {
-        const float* other = xs + (((g - 1) * 4 + wq) * 64 + lane) * PER;
-        float a1, a2;
-        rv_attn_merge(m, l, other[0], other[1], a1, a2);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][r] = oacc[dt][r] * a1 + other[2 + 16 * dt + r] * a2;
-    }
+    // no copy into LDS outlives the workgroup
+    RV_WAIT_VM(0);
     if (qi < Tq && nchunks > 1) {  // a partial: (m, l) and the unnormalised accumulator
         const long long slot = ((long long)blockIdx.y * ((Tq + 127) / 128) + jb) * CMAX + ch;
         float* op = opart + (slot * 128 + (qi - qb)) * D;

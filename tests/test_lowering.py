@@ -251,8 +251,10 @@ def test_attention_is_one_custom_kernel():
     ks = prog.describe()["kernels"]
     assert [k["class"] for k in ks] == ["ATTN"]
     k = ks[0]
-    assert k["grid"] == [2, 3, 1] and k["block"] == [512, 1, 1]
+    assert k["grid"] == [2, 3, 1] and k["block"] == [256, 1, 1]
     assert k["plan_detail"]["head_dim"] == 64 and k["plan_detail"]["keys"] == 333
+    # 64-key K and V tiles, 3 stages at head width 64 (48 KB), no VGPR staging
+    assert k["plan_detail"]["stages"] == 3 and k["lds_bytes"] == 3 * 2 * 64 * 64 * 2
     assert sorted(s["loc"]["index"] for s in k["stores"]) == [0, 1]
     assert prog.out_desc == [((3, 200, 64), "bf16"), ((3, 200, 1), "f32")]
 
