@@ -1725,7 +1725,11 @@ std::string Gen::gen_fold_cells() {
         b << "      v[u] = qq < " << q1 << " ? " << rd_part(pidx) << " : " << rt.ident << ";\n    }\n";
         b << "#pragma unroll\n    for (int u = 0; u < 8; ++u) acc = " << rt.fold("acc", "v[u]") << ";\n  }\n";
     };
-    b << "  __shared__ " << (rt.isdbl ? "double" : rt.isint ? (rt.sum ? "unsigned" : "int") : "float") << " wv[4][64];\n";
+    const std::string lt = rt.isdbl ? "double" : rt.isint ? (rt.sum ? "unsigned" : "int") : "float";
+    if (k.split_cell_major)
+        b << "  __shared__ " << lt << " wv[4][64];\n";
+    else
+        b << "  __shared__ " << lt << " wg[" << 256 / k.fold_cells_per_wg << "][" << k.fold_cells_per_wg << "];\n";
     b << "  const int t = threadIdx.x, lane = t & 63, w = t >> 6;\n";
     b << "  " << rt.t << " acc = " << rt.ident << ";\n";
     if (k.split_cell_major) {
@@ -1741,16 +1745,18 @@ std::string Gen::gen_fold_cells() {
         b << "  acc = wv[0][0];\n";
         for (int j = 1; j < 4; ++j) b << "  acc = " << rt.fold("acc", fmt("wv[%d][0]", j)) << ";\n";
     } else {
-        const int64_t Q = (P + 3) / 4;
-        b << "  const " << I << " cell = (" << I << ")blockIdx.x * 64 + lane;\n";
+        const int G = k.fold_cells_per_wg, NG = 256 / G;
+        const int64_t Q = (P + NG - 1) / NG;
+        b << "  const int cl = t % " << G << ", g = t / " << G << ";\n";
+        b << "  const " << I << " cell = (" << I << ")blockIdx.x * " << G << " + cl;\n";
         b << "  const " << I << " cq = cell < " << lit(C) << " ? cell : " << lit(C - 1) << ";\n";
-        b << "  const " << I << " pc0 = (" << I << ")w * " << lit(Q) << ", pc1 = pc0 + " << lit(Q) << " < " << lit(P)
+        b << "  const " << I << " pc0 = (" << I << ")g * " << lit(Q) << ", pc1 = pc0 + " << lit(Q) << " < " << lit(P)
           << " ? pc0 + " << lit(Q) << " : " << lit(P) << ";\n";
         fold_range("pc0", "pc1", "1", "qq * " + lit(C) + " + cq");
-        b << "  wv[w][lane] = acc;\n  __syncthreads();\n";
-        b << "  if (w != 0 || cell >= " << lit(C) << ") return;\n";
-        b << "  acc = wv[0][lane];\n";
-        for (int j = 1; j < 4; ++j) b << "  acc = " << rt.fold("acc", fmt("wv[%d][lane]", j)) << ";\n";
+        b << "  wg[g][cl] = acc;\n  __syncthreads();\n";
+        b << "  if (g != 0 || cell >= " << lit(C) << ") return;\n";
+        b << "  acc = wg[0][cl];\n";
+        for (int j = 1; j < NG; ++j) b << "  acc = " << rt.fold("acc", fmt("wg[%d][cl]", j)) << ";\n";
     }
     // the cell's domain indices (row-major over the output shape)
     std::vector<std::string> idx(rank);

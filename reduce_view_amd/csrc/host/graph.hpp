@@ -148,6 +148,7 @@ struct Kernel {
     int64_t split_pieces = 0, split_cells = 0;
     bool split_cell_major = false;
     int64_t split_depth = 0;  // additions any term passes through in the partial
+    int fold_cells_per_wg = 64;  // fold_cells over piece-major partials: cells per workgroup
     // ATTN (leaves q, k, v; domain (H, Tq, D); Tk = leaves[1].v.shape[1])
     double attn_scale = 0.0;
     bool attn_causal = false;

@@ -275,16 +275,27 @@ static void plan_fold_cells(Kernel& k, const Kernel& sp) {
     if (k.split_cell_major) {  // a workgroup per cell: lane runs, butterfly, 4 waves
         k.grid[0] = (unsigned)C;
         depth = sp.split_depth + (P + 255) / 256 + 6 + 3;
-    } else {  // 64 cells per workgroup: a quarter of the pieces per wave, 4 waves
-        k.grid[0] = (unsigned)((C + 63) / 64);
-        depth = sp.split_depth + (P + 3) / 4 + 3;
+    } else {
+        // G cells per workgroup (a lane per cell, consecutive lanes on
+        // consecutive cells), 256 / G lane groups each folding a run of the
+        // pieces, the groups folded in order: G = 64, or fewer where that
+        // leaves the CUs short of workgroups (4096 cells: G = 16, 256
+        // workgroups)
+        int G = 64;
+        while (G > 16 && (C + G - 1) / G < 256) G /= 2;
+        const int64_t groups = 256 / G, Q = (P + groups - 1) / groups;
+        k.fold_cells_per_wg = G;
+        k.grid[0] = (unsigned)((C + G - 1) / G);
+        depth = sp.split_depth + Q + groups - 1;
     }
     k.lds = 4 * 64 * 8;
     k.block[0] = 256;
     k.lane_dim = (int)k.domain.size() - 1;
-    snprintf(buf, sizeof buf, "\"partials\":%lld,\"cells\":%lld,\"src_region\":%d,\"layout\":\"%s\",\"sum_depth\":%lld",
+    snprintf(buf, sizeof buf,
+             "\"partials\":%lld,\"cells\":%lld,\"src_region\":%d,\"layout\":\"%s\",\"cells_per_workgroup\":%d,"
+             "\"sum_depth\":%lld",
              (long long)P, (long long)C, k.fold_src_region, k.split_cell_major ? "cell-major" : "piece-major",
-             (long long)depth);
+             k.split_cell_major ? 1 : k.fold_cells_per_wg, (long long)depth);
     k.plan_json = buf;
 }
 
