@@ -224,7 +224,9 @@ rv_status rv_launch(const rv_program* prog, const rv_buffer* bufs, int32_t nbufs
  * one device array of RV_SCRATCH_BYTES per GPU, reserved when the library's
  * code is first loaded on the GPU and held until the process ends; this call
  * allocates nothing. A program needing more workspace than that fails with
- * RV_E_WORKSPACE before anything is enqueued. Every call on a GPU shares
+ * RV_E_WORKSPACE before anything is enqueued, and a program whose code is not
+ * yet loaded on the current device (loading allocates; the first rv_launch on
+ * a device does it) fails with RV_E_INVALID. Every call on a GPU shares
  * that GPU's array and it keeps the last call's contents (no kernel here
  * needs it cleared); calls that overlap on one GPU (other streams, other
  * host threads) race on it. Buffers and stream as for rv_launch. */

@@ -242,6 +242,9 @@ std::string codegen(const Program& p);     // HIP source of every kernel
 std::string describe(const Program& p);    // JSON
 void compile_code(Program& p);             // hiprtc -> p.code (runtime.cpp)
 void launch(Program& p, const rv_buffer* bufs, int32_t nbufs, void* ws, size_t ws_bytes, void* stream);
+// whether the program's code object is loaded on device `dev` (loading it
+// allocates device memory; the first rv_launch on a device does it)
+bool loaded_on(Program& p, int dev);
 // The library's own workspace (scratch.hip): a device array of
 // kScratchBytes per GPU, for callers that cannot allocate.
 constexpr size_t kScratchBytes = (size_t)64 << 20;

@@ -186,6 +186,11 @@ static void ensure_loaded(Program& p, int dev, std::vector<void*>** fns) {
     *fns = &p.functions[dev];
 }
 
+bool loaded_on(Program& p, int dev) {
+    std::lock_guard<std::mutex> lk(p.mu);
+    return p.functions.find(dev) != p.functions.end();
+}
+
 void launch(Program& p, const rv_buffer* bufs, int32_t nbufs, void* ws, size_t ws_bytes, void* stream) {
     const int nin = p.g.n_inputs, nout = (int)p.outputs.size();
     if (nbufs != nin + nout || (!bufs && nbufs))

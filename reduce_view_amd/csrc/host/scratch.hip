@@ -44,6 +44,12 @@ void launch_noalloc(Program& p, const rv_buffer* bufs, int32_t nbufs, void* stre
                                  kScratchBytes));
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) fail(RV_E_DEVICE, "no current HIP device");
+    // loading the code object allocates device memory: this call only runs
+    // programs already loaded on the device
+    if (!loaded_on(p, dev))
+        fail(RV_E_INVALID, fmt("rv_launch_noalloc: the program is not loaded on device %d yet (loading allocates "
+                               "device memory; one rv_launch on that device loads it)",
+                               dev));
     void* ws = p.ws_bytes ? scratch_ptr(dev) : nullptr;
     launch(p, bufs, nbufs, ws, p.ws_bytes ? kScratchBytes : 0, stream);
 }

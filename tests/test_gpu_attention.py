@@ -104,6 +104,9 @@ def _check(name, spec, inp, h, tq, tk, d, causal, out_dtype="f32", outputs="ol")
     (2, 300, 300, 64, True, "bf16"),
     (1, 1, 1, 32, False, "f32"),
     (1, 5, 37, 128, False, "f32"),
+    # causal with more queries than keys: rows past the last key see all keys
+    (2, 300, 200, 32, True, "f32"),
+    (1, 70, 5, 64, True, "bf16"),
 ])
 def test_attention_matches_composition(h, tq, tk, d, causal, odt):
     _case(f"attention {h}x{tq}x{tk}x{d} causal={causal} out={odt}")

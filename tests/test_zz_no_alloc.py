@@ -86,6 +86,25 @@ def test_noalloc_matches_launch_on_consecutive_calls(pair):
             assert a.tobytes() == b.tobytes(), spec.name
 
 
+def test_noalloc_refuses_a_program_not_loaded_on_the_device():
+    # loading a code object allocates device memory: rv_launch_noalloc runs
+    # only programs one rv_launch has loaded on the device
+    import torch
+    spec, inp = PAIRS[2][1]
+    prog = rv.compile_spec(spec)
+    dev_in = {k: to_device(v) for k, v in inp.items() if k in prog.slots}
+    outs = prog.alloc_outputs()
+    stream = torch.cuda.current_stream().cuda_stream
+    with pytest.raises(rv.RVError) as e:
+        rv.rv_launch_noalloc(prog.h, _bufs(prog, dev_in, outs), stream)
+    assert e.value.name == "RV_E_INVALID"
+    ref = prog.launch(dev_in)
+    rv.rv_launch_noalloc(prog.h, _bufs(prog, dev_in, outs), stream)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, outs):
+        assert to_host(a).tobytes() == to_host(b).tobytes()
+
+
 def test_noalloc_refuses_a_program_beyond_its_size():
     import torch
     prog = rv.compile_spec(_cut(8192, 4096))  # a 128 MiB cut value
