@@ -544,13 +544,23 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
             int maxsz = 1;
             for (auto& s : k.stores) maxsz = std::max(maxsz, dtype_size(s.dtype));
             // 16-byte accesses per lane; about 32 cells of every value in
-            // flight per lane (4 vectors of float32, 2 of int8)
+            // flight per lane (2 vectors of int8, 4 of the wider types)
             int vw = std::max(1, std::min(16, 16 / maxsz));
             int64_t cpr = (k.domain[X] + vw - 1) / vw;
             int64_t chunks = cpr * (numel(k.domain) / k.domain[X]);
-            const int U = std::max(1, std::min(4, 32 / vw));
+            // 4-byte cells that are read and written: one vector per lane
+            // per grid step (measured 2-3% faster than 4 on the 4096^2 copy
+            // and the embedding gather; a pure fill keeps 4, 7% faster)
+            bool reads = false;
+            for (auto& L : k.leaves)
+                if (!L.zero) reads = true;
+            int U = vw == 4 && reads ? 1 : std::max(1, std::min(4, 32 / vw));
+            U = env_int("RV_EW_UNROLL", U);
+            if (U < 1 || U > 16) fail(RV_E_INVALID, "RV_EW_UNROLL must be in 1..16");
+            const int64_t cap = env_int("RV_EW_GRID_CAP", 256 * 32);
+            if (cap < 1) fail(RV_E_INVALID, "RV_EW_GRID_CAP must be positive");
             int64_t blocks = (chunks + 256 * U - 1) / (256 * U);
-            k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 256 * 32));
+            k.grid[0] = (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, cap));
             k.block[0] = 256;
             snprintf(buf, sizeof buf, "\"vec\":%d,\"unroll\":%d,\"chunks\":%lld", vw, U, (long long)chunks);
         }
