@@ -1010,11 +1010,11 @@ __device__ __forceinline__ void rv_attn_fwd_bf16(const unsigned short* __restric
     // seen is hidden (m = -inf) every score is -inf and exp2(-inf - 0) = 0
     auto probs = [&](const float (&sv)[32], float (&pr)[32]) {
         const float mns = m == ninf ? 0.0f : m;
-        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float ps[4];
 #pragma unroll
         for (int r = 0; r < 32; ++r) {
             pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], sl2, -mns));
-            ps[r & 3] = ps[r & 3] + pr[r];
+            ps[r & 3] = r < 4 ? pr[r] : ps[r & 3] + pr[r];
         }
         return rv_pair_sum((ps[0] + ps[1]) + (ps[2] + ps[3]));
     };
