@@ -52,13 +52,13 @@ def check_device_header(verbose: bool = False) -> None:
                 "K chk5(float* p) { p[0] = rv_fold_sum(p, 16); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
                 "chk15(const unsigned short* a, const unsigned short* b, float* p) {\n"
-                "  rv_gemm_w4_bf16<true, 1>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "  rv_gemm_w6_bf16<true, 1, E>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
                 "chk16(const unsigned short* a, const unsigned short* b, float* p) {\n"
-                "  rv_gemm_w4_bf16<false, 0>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
+                "  rv_gemm_w6_bf16<false, 0, E, 2>(a, b, 0, 4096, 0, 4096, 4096, 4096, 4096, E{}, p); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
                 "chk17(const unsigned short* a, const unsigned short* b, float* p) {\n"
-                "  rv_gemm_w4_bf16<true, 1, E, 2, 1, 5, true>(a, b, 0, 4104, 0, 4104, 4100, 4104, 4128, E{}, p, 4100, 4097); }\n"
+                "  rv_gemm_w6_bf16<true, 1, E, 1, true>(a, b, 0, 4104, 0, 4104, 4100, 4104, 4160, E{}, p, 4100, 4097); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(256) chk12(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
                 "float* l) { rv_attn_fwd_bf16<32, true, false, 4>(q, k, v, o, l, 1000, 1000, 0.25f); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(256) chk13(const unsigned short* q, const unsigned short* k, const unsigned short* v, "

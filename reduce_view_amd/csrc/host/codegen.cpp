@@ -653,51 +653,8 @@ std::string Gen::gen_tiled() {
         }
     }
     b << "  const bool interior = " << inter << ";\n";
-    // LDS-staged transposed operands of 4-byte types (interior tiles): the
-    // workgroup loads the (TX source rows) x (TY = 32 source columns) block
-    // of each leaf read along Y with 16-byte vectors along the source rows
-    // (8 lanes per row: whole 128-byte lines), writes it to LDS and each lane
-    // reads its 4 x 4 block back as 4 column vectors. Layout: two source rows
-    // per 256-byte LDS line (all 64 banks), chunk (row % 2) * 8 + ch of line
-    // row / 2 XOR-swizzled by 2 * ((row / 4) % 8), so each 16-lane quarter of
-    // a read (8 row groups x 2 chunks) and of a write (2 rows x 8 chunks)
-    // covers all 64 banks once.
-    const bool lds_t = k.plan_json.find("\"lds_transposed_leaves\"") != std::string::npos;
-    std::vector<int> lds_off(k.leaves.size(), -1);
-    if (lds_t) {
-        int off = 0;
-        for (size_t l = 0; l < k.leaves.size(); ++l) {
-            const Leaf& L = k.leaves[l];
-            if (!used[l] || L.zero || !leaf_vec_ok(L, Y, 4) || leaf_vec_ok(L, X, 4) || dtype_size(L.dtype) != 4)
-                continue;
-            if (L.v.strides[X] == 0 && !masked(L.v, X)) continue;  // broadcast along X: no transpose
-            lds_off[l] = off;
-            off += TX * TY * dtype_size(L.dtype);
-        }
-        if (off > 0) b << "  __shared__ __attribute__((aligned(16))) unsigned char tlds[" << off << "];\n";
-    }
     for (int edge = 0; edge < 2; ++edge) {
         b << (edge ? "  else {\n" : "  if (interior) {\n");
-        if (!edge && lds_t) {
-            bool any = false;
-            for (size_t l = 0; l < k.leaves.size(); ++l) {
-                if (lds_off[l] < 0) continue;
-                any = true;
-                const Leaf& L = k.leaves[l];
-                const std::string T = st(L.dtype), P = pname(L.loc, L.dtype, false);
-                // TX source rows (output x) of TY / 4 chunks (output y) each;
-                // 256 lanes, chunk = t % (TY / 4), row = t / (TY / 4) + step
-                const int CPR = TY / 4, RPS = 256 / CPR;
-                b << "    {\n      " << T << "* tl = (" << T << "*)(tlds + " << lds_off[l] << ");\n";
-                b << "      for (int s0 = 0; s0 < " << TX << "; s0 += " << RPS << ") {\n";
-                b << "        const int row = s0 + t / " << CPR << ", ch = t % " << CPR << ";\n";
-                b << "        const rv_pack<" << T << ", 4> v = "
-                  << vload(L, 4, P + " + " + addr(L.v, idx_at("Y0 + 4 * ch", "X0 + row"))) << ";\n";
-                b << "        rv_stv<" << T << ", 4>(tl + 4 * ((row >> 1) * 16 + (((row & 1) * 8 + ch) ^ (2 * ((row >> 2) & 7)))), "
-                  << "v);\n      }\n    }\n";
-            }
-            if (any) b << "    __syncthreads();\n";
-        }
         // loads: cell (r, c) of the lane's block is (y + r, x + c). In edge
         // tiles a lane whose 4 x 4 block lies inside the domain and the mask
         // still takes the vector path; only blocks on a boundary go cell by cell.
@@ -747,14 +704,7 @@ std::string Gen::gen_tiled() {
             sc << "      " << V << "[r][c] = " << (cond.empty() ? "" : "(" + cond + ") ? ")
                << ld(L.dtype, P + "[" + addr(L.v, idq) + "]") << (cond.empty() ? "" : " : " + zero_of(L.dtype))
                << ";\n    }\n";
-            if (!edge && lds_off[l] >= 0) {
-                // the staged block: row (x + c - X0), chunk (y - Y0) / 4
-                b << "    { const " << T << "* tl = (const " << T << "*)(tlds + " << lds_off[l] << ");\n";
-                b << "      for (int c = 0; c < 4; ++c) { const int row = (int)(x + c - X0), ch = (int)(y - Y0) >> 2;\n";
-                b << "        const rv_pack<" << T << ", 4> v = rv_ldv<" << T
-                  << ", 4>(tl + 4 * ((row >> 1) * 16 + (((row & 1) * 8 + ch) ^ (2 * ((row >> 2) & 7)))));\n";
-                b << "        for (int r = 0; r < 4; ++r) " << V << "[r][c] = " << ld(L.dtype, "v.v[r]") << "; } }\n";
-            } else if (!along_x && !along_y) {
+            if (!along_x && !along_y) {
                 b << sc.str();
             } else if (!edge) {
                 b << vec.str();
@@ -2235,14 +2185,8 @@ std::string Gen::gen_gemm() {
     const int64_t lda = A.v.strides[0];
     const int64_t ldb = kn ? B.v.strides[2] : B.v.strides[1];
     const Kernel::GemmSched& g = k.gemm;
-    if (k.plan == "gemm_w6")
-        b << "  rv_gemm_w6_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ", " << sname
-          << ", " << g.pin << ", " << (ragged ? "true" : "false") << ", " << g.pe << ", " << g.po << ">(" << pa << ", " << pb
-          << ", ";
-    else
-        b << "  rv_gemm_w4_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ", " << sname
-          << ", " << g.nv0 << ", " << g.pin << ", " << g.stages << ", " << (ragged ? "true" : "false") << ", "
-          << g.krot << ", " << (g.remap ? "true" : "false") << ">(" << pa << ", " << pb << ", ";
+    b << "  rv_gemm_w6_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ", " << sname << ", "
+      << g.pin << ", " << (ragged ? "true" : "false") << ", " << g.pe << ", " << g.po << ">(" << pa << ", " << pb << ", ";
     b
       << A.v.offset << "LL, " << lda << "LL, " << B.v.offset << "LL, " << ldb << "LL, " << M << ", " << N << ", " << K
       << ", epi, " << (k.mfma_partial ? partials : std::string("nullptr")) << ", " << Mt << ", " << Nt << ");\n";

@@ -124,13 +124,11 @@ struct Kernel {
     // into workspace); the domain keeps the output's (M, N, K)
     int64_t mfma_ext[3] = {0, 0, 0};
     bool mfma_copied[2] = {false, false};
-    // the kernel's schedule (chosen at lowering, baked in at codegen):
-    // interleave mode, tile order; gemm_w4: stages, copies in a k-tile's
-    // first step, k-tile stagger; gemm_w6: copies in an even / odd k-tile's
-    // first step
+    // the kernel's schedule (chosen at lowering, baked in at codegen): the
+    // MFMA / LDS-read / copy interleaving, and the copies issued in an even
+    // / odd k-tile's first k16 step
     struct GemmSched {
-        int pin = 1, remap = 1;
-        int stages = 5, nv0 = 2, krot = 0;
+        int pin = 1;
         int pe = 3, po = 1;
     } gemm;
     int partials_region = -1;   // workspace region of the partials
@@ -259,8 +257,8 @@ std::vector<Loc> kernel_param_locs(const Program& p, const Kernel& k);
 // max/denominator recurrence.
 std::vector<std::pair<int, int>> online_softmax_pairs(const Kernel& k);
 // k-depth the contraction kernel steps by (its operands hold a multiple of
-// it): 64 for the kernel staging A 64 deep ("w6"), 32 for "w4".
-int mfma_kstep();
+// it): 64, A being staged 64 deep.
+constexpr int64_t kMfmaKStep = 64;
 // Value `e` of kernel `k` is the same at every index along domain dim `d`.
 bool ex_invariant(const Kernel& k, int e, int d);
 

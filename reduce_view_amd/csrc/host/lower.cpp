@@ -144,11 +144,6 @@ static void prove_in_bounds(const Program& p, const Kernel& k) {
         if (k.plan != "fold" && !(k.cls == KClass::MFMA && k.mfma_partial)) check(s.v, s.loc, s.dtype, "a store");
 }
 
-int mfma_kstep() {
-    const char* kind = getenv("RV_GEMM_KERNEL");
-    return kind && std::string(kind) == "w4" ? 32 : 64;
-}
-
 std::vector<std::pair<int, int>> online_softmax_pairs(const Kernel& k) {
     std::vector<std::pair<int, int>> out;
     auto f32 = [&](int e) { return e >= 0 && k.ex[e].dtype == RV_F32; };
@@ -361,40 +356,25 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
             return;
         }
         case KClass::MFMA: {
-            const bool w6 = mfma_kstep() == 64;
             // 256 x 256 tiles, 4 waves of 128 x 128, operands copied straight
             // into LDS (kernels/rv_device.hpp), over the extents the operand
-            // buffers hold (a ragged last tile is shifted back inside them).
-            // gemm_w6 (default): A staged 64 deep in 3 stages, B 32 deep in
-            // 4; pe / po copies issued in an even / odd k-tile's first k16
-            // step. gemm_w4 (RV_GEMM_KERNEL=w4): both 32 deep in 4 or 5
-            // stages, nv0 copies in a k-tile's first step, k-tile stagger
-            // krot, tile order remap (1 XCD-contiguous, 0 plain; gemm_w6
-            // always the former). Both: the MFMA/LDS/copy interleaving (1
-            // pinned, 2 reads front-loaded, 0 free). Measured on cold 4096^3 operands: gemm_w6 105 us,
-            // gemm_w4 112 us at their best settings (the defaults).
+            // buffers hold (a ragged last tile is shifted back inside them),
+            // tiles in XCD-contiguous order: A staged 64 deep in 3 stages, B
+            // 32 deep in 4; pe / po copies issued in an even / odd k-tile's
+            // first k16 step (RV_GEMM_W6_PE, RV_GEMM_W6_PO); the MFMA / LDS /
+            // copy interleaving (RV_GEMM_PIN: 1 pinned, 2 reads front-loaded,
+            // 0 free). Measured on cold 4096^3 operands: 105 us (the same
+            // tiles staged 32 deep in 4 or 5 stages took 112 us at best).
             const int64_t M = k.domain[0], N = k.domain[1];
             const int64_t Me = k.mfma_ext[0], Ne = k.mfma_ext[1], Ke = k.mfma_ext[2];
-            int nv0 = 2, pin = 1, stages = 5;
-            const char* sp = getenv("RV_GEMM_W4_SPLIT");
-            if (sp && *sp) nv0 = std::max(0, std::min(8, atoi(sp)));
-            const char* pn = getenv("RV_GEMM_PIN");
-            if (pn && *pn) pin = std::max(0, std::min(2, atoi(pn)));
-            const char* st = getenv("RV_GEMM_W4_STAGES");
-            if (st && (atoi(st) == 4 || atoi(st) == 5)) stages = atoi(st);
-            const int krot = std::max(0, std::min(64, env_int("RV_GEMM_KROT", 0)));
+            const int pin = std::max(0, std::min(2, env_int("RV_GEMM_PIN", 1)));
             const int pe = std::max(0, std::min(12, env_int("RV_GEMM_W6_PE", 3)));
             const int po = std::max(0, std::min(4, env_int("RV_GEMM_W6_PO", 1)));
-            const int remap = env_int("RV_GEMM_REMAP", 1) ? 1 : 0;
-            k.plan = w6 ? "gemm_w6" : "gemm_w4";
+            k.plan = "gemm_w6";
             k.gemm.pin = pin;
-            k.gemm.remap = remap;
-            k.gemm.stages = stages;
-            k.gemm.nv0 = nv0;
-            k.gemm.krot = krot;
             k.gemm.pe = pe;
             k.gemm.po = po;
-            k.lds = w6 ? 3 * 256 * 64 * 2 + 4 * 256 * 32 * 2 : 2 * stages * 256 * 32 * 2;
+            k.lds = 3 * 256 * 64 * 2 + 4 * 256 * 32 * 2;
             const int64_t tiles = ((Me + 255) / 256) * ((Ne + 255) / 256);
             if (tiles >= ((int64_t)1 << 31)) fail(RV_E_UNSUPPORTED_LAYOUT, "contraction of 2^31 or more output tiles");
             k.grid[0] = (unsigned)tiles;
@@ -403,16 +383,10 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
             const bool kn = k.leaves[k.mfma_b].v.strides[1] == 1;
             const bool ragged = Me % 256 || Ne % 256 || Me != M || Ne != N;
             char stage_buf[160];
-            if (w6)
-                snprintf(stage_buf, sizeof stage_buf,
-                         "\"stages\":{\"A\":3,\"B\":4},\"stage_depth\":{\"A\":64,\"B\":32},"
-                         "\"early_copies\":[%d,%d]",
-                         pe, po);
-            else
-                snprintf(stage_buf, sizeof stage_buf,
-                         "\"stages\":{\"A\":%d,\"B\":%d},\"stage_depth\":{\"A\":32,\"B\":32},"
-                         "\"copies_first_step\":%d,\"krot\":%d,\"remap\":%d",
-                         stages, stages, nv0, krot, remap);
+            snprintf(stage_buf, sizeof stage_buf,
+                     "\"stages\":{\"A\":3,\"B\":4},\"stage_depth\":{\"A\":64,\"B\":32},"
+                     "\"early_copies\":[%d,%d]",
+                     pe, po);
             // per lane: 256 values summed in order, 6 butterfly levels, 3
             // cross-wave additions; the fold adds its own depth
             snprintf(buf, sizeof buf,
@@ -524,21 +498,15 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
             k.grid[1] = 1;
             k.grid[2] = (unsigned)B;
             k.block[0] = 256;
-            int nt = 0, tbytes = 0;
+            // operands read along Y are transposed in registers: each lane
+            // loads 4 vectors along Y and uses them as the columns of its
+            // 4 x 4 block (an LDS-staged transpose measured 2% slower)
+            int nt = 0;
             for (auto& L : k.leaves)
-                if (!L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) {
-                    ++nt;
-                    tbytes += 32 * WY * 32 * WX * dtype_size(L.dtype);
-                }
-            if (WY != 1) tbytes = 1 << 30;  // the staged block assumes a 32-row tile
-            // RV_EW_TRANSPOSE=lds: interior tiles stage each transposed
-            // operand through LDS (row-wise coalesced loads, 16-byte chunks
-            // XOR-swizzled, read back along the other dim) instead of
-            // transposing 4 x 4 blocks in registers
-            const bool lds_t = nt > 0 && env_int("RV_EW_TRANSPOSE_LDS", 0) != 0 && tbytes <= 64 * 1024;
-            k.lds = lds_t ? (size_t)tbytes : 0;
+                if (!L.zero && L.v.strides[Y] == 1 && L.v.strides[X] != 1) ++nt;
+            k.lds = 0;
             snprintf(buf, sizeof buf, "\"tile\":[%d,%d],\"waves\":[%d,%d],\"order\":%d,\"lane_block\":[4,4],"
-                     "\"%s_transposed_leaves\":%d", 32 * WY, 32 * WX, WY, WX, order, lds_t ? "lds" : "register", nt);
+                     "\"register_transposed_leaves\":%d", 32 * WY, 32 * WX, WY, WX, order, nt);
         } else {
             k.plan = "rowmajor";
             int maxsz = 1;

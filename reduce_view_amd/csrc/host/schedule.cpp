@@ -667,8 +667,7 @@ static Kernel operand_copy(const Leaf& L, int dr, int dc, int64_t rows, int64_t 
 // rewritten to read them.
 static void mfma_operands(Ctx& c, Kernel& k, std::vector<Kernel>& out) {
     const int64_t M = k.domain[0], N = k.domain[1], K = k.domain[2];
-    // the kernel's k step: 64 for the A-staged-64-deep kernel, else 32
-    const int64_t KS = mfma_kstep();
+    const int64_t KS = kMfmaKStep;
     const int64_t Kp = (K + KS - 1) / KS * KS, lim = (int64_t)1 << 27;
     const Leaf A = k.leaves[k.mfma_a], B = k.leaves[k.mfma_b];
     auto unmasked = [](const Leaf& L) {

@@ -207,34 +207,28 @@ __device__ __forceinline__ void rv_g5_step(rv_f32x16 (&acc)[TM][TN], const rv_bf
 // accumulation registers). Operands go global -> LDS with
 // global_load_lds_dwordx4 (each lane's 16 bytes land at the wave's LDS base
 // + 16 * lane), so no VGPRs stage them:
-//   - A (and a [n][k] B) keep [row][k] rows of 64 bytes per 32-deep k-tile,
-//     the 16-byte chunks XOR-swizzled by (row / 4) % 4, so 16 consecutive
-//     rows read at one chunk cover all 64 banks; a fragment (8 consecutive k
-//     of one row) is one ds_read_b128.
+//   - A is staged 64 deep, in rows of 128 bytes (whole lines) per copy; a
+//     fragment (8 consecutive k of one row) is one ds_read_b128;
+//   - an [n][k] B keeps [row][k] rows of 64 bytes per 32-deep k-tile, the
+//     16-byte chunks XOR-swizzled by (row / 4) % 4, so 16 consecutive rows
+//     read at one chunk cover all 64 banks; a fragment is one ds_read_b128;
 //   - a [k][n] B keeps its [k][n] rows of 512 bytes with chunks XOR-swizzled
 //     by 4 * (k % 4); a fragment (8 consecutive k of one column) is two
 //     ds_read_b64_tr_b16, the gfx950 transposing LDS read.
-// A wave reads 8 KB of fragments for 16 MFMAs per k16 step, so the LDS moves
-// 192 KB per 64 of k (64 KB copied in, 128 KB read out) against 2048 MFMA
-// cycles per SIMD.
 // With one wave per SIMD nothing else hides latency, so the wave pipelines
-// itself: k-tiles of 32 in NS LDS stages of 32 KB (five fill the LDS; the
-// copies run NS - 1 k-tiles ahead), and the fragments double buffered in
-// registers (x for a k-tile's first k16 step, y for its second). Step 0
-// multiplies x while reading y and issuing NV0 of the 8 copies of the k-tile
-// NS - 1 ahead; step 1 waits for its own copies of the next stage, passes the
-// barrier (after which every wave's copies of that stage have landed and
-// nobody reads the stage the copies overwrite), and multiplies y while
-// reading the next stage's x and issuing the other copies.
-// sched_group_barrier pins one LDS read and one copy after each MFMA so the
-// reads hide under the matrix work.
+// itself: the copies run several k-tiles ahead in LDS stages, and the
+// fragments are double buffered in registers (one set for a k-tile's first
+// k16 step, one for its second); each k-tile passes one barrier, after which
+// every wave's copies of the stage it waited for have landed and nobody reads
+// the stage the next copies overwrite. sched_group_barrier pins LDS reads and
+// copies between the MFMAs so they hide under the matrix work.
 //
-// Extents: M, N (each >= 256) and K (a multiple of 32) are the extents the
-// operand buffers hold; Mt <= M and Nt <= N are the output's. With RAGGED, a
-// last tile that would run past M (or N) starts at M - 256 instead, so every
-// copy stays inside the operands and the loop has no edge cases; its cells
-// below the nominal tile start belong to the tile before it and, like cells
-// at or beyond Mt (Nt), are left out of the epilogue.
+// Extents: M, N (each >= 256) and K are the extents the operand buffers
+// hold; Mt <= M and Nt <= N are the output's. With RAGGED, a last tile that
+// would run past M (or N) starts at M - 256 instead, so every copy stays
+// inside the operands and the loop has no edge cases; its cells below the
+// nominal tile start belong to the tile before it and, like cells at or
+// beyond Mt (Nt), are left out of the epilogue.
 // ---------------------------------------------------------------------------
 // Per-lane byte offsets of the fragment reads inside one stage (loop
 // invariant; the stage's array base, the 32-row tile i (2048 bytes) and, for a
@@ -266,62 +260,6 @@ __device__ __forceinline__ rv_g5_offs rv_g5_lane_offs(int wm, int wn, int lane) 
         o.b[2] = o.b[3] = 0;
     }
     return o;
-}
-
-template <bool B_KN, int Q>
-__device__ __forceinline__ void rv_g5_frags(rv_bf16x8 (&af)[4], rv_bf16x8 (&bf)[4], const unsigned short* As,
-                                            const unsigned short* Bs, const rv_g5_offs& o) {
-    const char* pa = reinterpret_cast<const char*>(As) + o.a[Q];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const rv_bf16x8*>(pa + i * 2048);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (B_KN) {
-            const char* pb = reinterpret_cast<const char*>(Bs) + o.b[j] + Q * 8192;
-            rv_s16x4 h[2];
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-                h[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) rv_s16x4*)(pb + half * 2048));
-            typedef __attribute__((ext_vector_type(8))) short s16x8;
-            s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-            bf[j] = __builtin_bit_cast(rv_bf16x8, v);
-        } else {
-            bf[j] = *reinterpret_cast<const rv_bf16x8*>(reinterpret_cast<const char*>(Bs) + o.b[Q] + j * 2048);
-        }
-    }
-}
-
-// Global -> LDS copy of one 32-deep k-tile by 4 waves: 4 + 4 instructions of
-// 1 KB per wave, of which this call issues those numbered [C0, C1), A's
-// first. The row part of each address is a wave-uniform base; the lane part
-// (row within 16 A rows or 2 B k-rows, swizzled chunk) is a loop-invariant
-// 32-bit offset, so the copies take the scalar-base form.
-template <bool B_KN, int C0, int C1>
-__device__ __forceinline__ void rv_g5_copy(unsigned short* As, unsigned short* Bs, const unsigned short* __restrict__ A,
-                                           const unsigned short* __restrict__ B, long long a_base, long long lda,
-                                           long long b_base, long long ldb, int k0, int wave, unsigned va,
-                                           const unsigned (&vb)[2]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (i < C0 || i >= C1) continue;
-        const int r0 = wave * 64 + i * 16;
-        const char* g = reinterpret_cast<const char*>(A + a_base + (long long)r0 * lda + k0);
-        __builtin_amdgcn_global_load_lds((const void*)(g + va), (rv_lds_void*)(As + r0 * 32), 16, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (4 + i < C0 || 4 + i >= C1) continue;
-        if (B_KN) {
-            const int kr0 = wave * 8 + i * 2;
-            const char* g = reinterpret_cast<const char*>(B + b_base + (long long)(k0 + kr0) * ldb);
-            __builtin_amdgcn_global_load_lds((const void*)(g + vb[i & 1]), (rv_lds_void*)(Bs + kr0 * 256), 16, 0, 0);
-        } else {
-            const int r0 = wave * 64 + i * 16;
-            const char* g = reinterpret_cast<const char*>(B + b_base + (long long)r0 * ldb + k0);
-            __builtin_amdgcn_global_load_lds((const void*)(g + vb[0]), (rv_lds_void*)(Bs + r0 * 32), 16, 0, 0);
-        }
-    }
 }
 
 // interleaving of one k16 step's 16 MFMAs with its NDS LDS reads and NVM
@@ -363,188 +301,15 @@ __device__ __forceinline__ void rv_g5_keep(rv_f32x16 (&acc)[4][4]) {
         for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
 }
 
-template <bool B_KN, int MODE, class Epi, int NV0 = 8, int PIN = 1, int NS = 4, bool RAGGED = false, int KROT = 0,
-          bool REMAP = true>
-__device__ __forceinline__ void rv_gemm_w4_bf16(const unsigned short* __restrict__ A,
-                                                const unsigned short* __restrict__ B, long long a_off, long long lda,
-                                                long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
-                                                float* __restrict__ partials, int Mt = 0, int Nt = 0) {
-    static_assert(NS == 4 || NS == 5, "four or five LDS stages");
-    // NS stages of 32 KB (five fill the 160 KB of LDS; the fifth pair is a
-    // single element when unused)
-    constexpr int S5 = NS == 5 ? 256 * 32 : 1;
-    __shared__ __attribute__((aligned(1024))) unsigned short a0[256 * 32], a1[256 * 32], a2[256 * 32], a3[256 * 32];
-    __shared__ __attribute__((aligned(1024))) unsigned short b0[256 * 32], b1[256 * 32], b2[256 * 32], b3[256 * 32];
-    __shared__ __attribute__((aligned(16))) unsigned short a4[S5], b4[S5];
-    constexpr int NDS = B_KN ? 12 : 8;  // LDS read instructions per k16 step
-    const int tid = threadIdx.x;
-    // the wave index in a scalar register: copy bases and LDS destinations
-    // are then wave-uniform without a readfirstlane per copy
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
-    const int ntiles = tiles_m * tiles_n;
-    int tm, tn;
-    {
-        int bid = blockIdx.x;
-        if (REMAP && (ntiles & 7) == 0 && (tiles_m & 3) == 0) {
-            const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
-            const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
-            tm = group * 4 + (within & 3);
-            tn = within >> 2;
-        } else {
-            tm = bid / tiles_n;
-            tn = bid % tiles_n;
-        }
-    }
-    // a ragged last tile is shifted back to end at the operands' last row
-    const int mlo = tm * 256, nlo = tn * 256;
-    const int m0 = RAGGED ? min(mlo, M - 256) : mlo, n0 = RAGGED ? min(nlo, N - 256) : nlo;
-    const long long a_base = a_off + (long long)m0 * lda;
-    const long long b_base = B_KN ? b_off + n0 : b_off + (long long)n0 * ldb;
-    // lane parts of the copy addresses (bytes): A row lane / 4 of 16, chunk
-    // lane % 4 swizzled by (row / 4) % 4; a [k][n] B k-row lane / 32 of 2,
-    // chunk lane % 32 swizzled by 4 * (k-row % 4), which alternates with the
-    // instruction's k-row pair (its first k-row is 0 or 2 mod 4)
-    const unsigned va = (unsigned)(2 * ((lane >> 2) * lda + (((lane & 3) ^ ((lane >> 4) & 3)) << 3)));
-    unsigned vb[2];
-    if (B_KN) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-            vb[p] = (unsigned)(2 * ((lane >> 5) * ldb + (((lane & 31) ^ ((2 * p + (lane >> 5)) * 4)) << 3)));
-    } else {
-        vb[0] = vb[1] = (unsigned)(2 * ((lane >> 2) * ldb + (((lane & 3) ^ ((lane >> 4) & 3)) << 3)));
-    }
-    const rv_g5_offs fo = rv_g5_lane_offs<B_KN>(wm, wn, lane);
-
-    rv_f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    const int KT = K / 32;
-    // KROT staggers the workgroups that share operand panels: each walks the
-    // k-tiles from its own starting tile (KROT times its index among the
-    // XCD's workgroups), wrapping around; the sum is the same up to order.
-    const int rot = KROT ? (KROT * (int)(blockIdx.x >> 3)) % KT : 0;
-    // copies past the last k-tile reload it into a stage nobody reads, so
-    // every k-tile issues exactly 8 copies per wave, and "the next stage has
-    // landed" is always vmcnt <= 8 (NS - 2) + NV0: the later stages' copies
-    // may stay in flight
-#define RV_G5_KT(t) (KROT ? ((((t) < KT ? (t) : KT - 1) + rot) % KT) * 32 : ((t) < KT ? (t) : KT - 1) * 32)
-    rv_g5_copy<B_KN, 0, 8>(a0, b0, A, B, a_base, lda, b_base, ldb, RV_G5_KT(0), wave, va, vb);
-    rv_g5_copy<B_KN, 0, 8>(a1, b1, A, B, a_base, lda, b_base, ldb, RV_G5_KT(1), wave, va, vb);
-    rv_g5_copy<B_KN, 0, 8>(a2, b2, A, B, a_base, lda, b_base, ldb, RV_G5_KT(2), wave, va, vb);
-    if (NS == 5) rv_g5_copy<B_KN, 0, 8>(a3, b3, A, B, a_base, lda, b_base, ldb, RV_G5_KT(3), wave, va, vb);
-    RV_WAIT_VM(8 * (NS - 2));
-    RV_LDS_BARRIER();
-    rv_bf16x8 xa[4], xb[4], ya[4], yb[4];
-    rv_g5_frags<B_KN, 0>(xa, xb, a0, b0, fo);
-#define RV_G5_STEP(CA, CB, WA, WB, XA, XB, T)                                                          \
-    {                                                                                                  \
-        const int t_ = (T);                                                                            \
-        __builtin_amdgcn_sched_barrier(0);                                                             \
-        rv_g5_frags<B_KN, 1>(ya, yb, CA, CB, fo);                                                     \
-        rv_g5_copy<B_KN, 0, NV0>(WA, WB, A, B, a_base, lda, b_base, ldb, RV_G5_KT(t_ + NS - 1), wave, va, vb); \
-        rv_g5_step<4, 4>(acc, xa, xb);                                                                 \
-        if (PIN) rv_g5_pin<NDS, NV0, PIN>();                                                           \
-        __builtin_amdgcn_sched_barrier(0);                                                             \
-        RV_WAIT_VM(8 * (NS - 2) + NV0);                                                                \
-        RV_LDS_BARRIER();                                                                              \
-        __builtin_amdgcn_sched_barrier(0);                                                             \
-        rv_g5_frags<B_KN, 0>(xa, xb, XA, XB, fo);                                                     \
-        rv_g5_copy<B_KN, NV0, 8>(WA, WB, A, B, a_base, lda, b_base, ldb, RV_G5_KT(t_ + NS - 1), wave, va, vb); \
-        rv_g5_step<4, 4>(acc, ya, yb);                                                                 \
-        if (PIN) rv_g5_pin<NDS, 8 - NV0, PIN>();                                                       \
-        __builtin_amdgcn_sched_barrier(0);                                                             \
-        rv_g5_keep(acc);                                                                               \
-    }
-    // whole rounds of NS k-tiles, then the remaining KT % NS in stage order
-    // (no exits from inside a round: they tangle the accumulators' live ranges)
-    int kt = 0;
-    if (NS == 4) {
-        for (; kt + 4 <= KT; kt += 4) {
-            RV_G5_STEP(a0, b0, a3, b3, a1, b1, kt)
-            RV_G5_STEP(a1, b1, a0, b0, a2, b2, kt + 1)
-            RV_G5_STEP(a2, b2, a1, b1, a3, b3, kt + 2)
-            RV_G5_STEP(a3, b3, a2, b2, a0, b0, kt + 3)
-        }
-        if (kt < KT) {
-            RV_G5_STEP(a0, b0, a3, b3, a1, b1, kt)
-            if (kt + 1 < KT) {
-                RV_G5_STEP(a1, b1, a0, b0, a2, b2, kt + 1)
-                if (kt + 2 < KT) RV_G5_STEP(a2, b2, a1, b1, a3, b3, kt + 2)
-            }
-        }
-    } else {
-        for (; kt + 5 <= KT; kt += 5) {
-            RV_G5_STEP(a0, b0, a4, b4, a1, b1, kt)
-            RV_G5_STEP(a1, b1, a0, b0, a2, b2, kt + 1)
-            RV_G5_STEP(a2, b2, a1, b1, a3, b3, kt + 2)
-            RV_G5_STEP(a3, b3, a2, b2, a4, b4, kt + 3)
-            RV_G5_STEP(a4, b4, a3, b3, a0, b0, kt + 4)
-        }
-        if (kt < KT) {
-            RV_G5_STEP(a0, b0, a4, b4, a1, b1, kt)
-            if (kt + 1 < KT) {
-                RV_G5_STEP(a1, b1, a0, b0, a2, b2, kt + 1)
-                if (kt + 2 < KT) {
-                    RV_G5_STEP(a2, b2, a1, b1, a3, b3, kt + 2)
-                    if (kt + 3 < KT) RV_G5_STEP(a3, b3, a2, b2, a4, b4, kt + 3)
-                }
-            }
-        }
-    }
-#undef RV_G5_STEP
-#undef RV_G5_KT
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // every copy has landed and every wave is past its last read: the first
-    // stage holds the per-wave partial sums
-    float* lds_red = reinterpret_cast<float*>(a0);
-
-    float part = 0.0f;
-    // one 32 x 32 tile at a time: left alone, the scheduler hoists all 256
-    // accumulator reads above the epilogue and runs out of registers
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("" : "+a"(acc[i][j]));
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int n = n0 + wn * 128 + j * 32 + (lane & 31);
-                if (RAGGED && !(m >= mlo && m < Mt && n >= nlo && n < Nt)) continue;
-                const float v = epi(acc[i][j][r], m, n);
-                if (MODE == 0)
-                    epi.store(m, n, v);
-                else
-                    part = part + v;
-            }
-        }
-    if (MODE == 1) {
-        part = rv_group_sum<64>(part);
-        if (lane == 0) lds_red[wave] = part;
-        __syncthreads();
-        if (tid == 0) partials[blockIdx.x] = ((lds_red[0] + lds_red[1]) + lds_red[2]) + lds_red[3];
-    }
-}
-
 // ---------------------------------------------------------------------------
-// The same contraction with A staged 64 deep: A rows of 128 bytes (whole
-// lines) per copy instead of 64-byte halves, so A takes half the L2 requests
-// for its bytes. Each of the 3 A stages (32 KB) holds two 32-deep k-tiles;
-// B keeps its 32-deep k-tiles in 4 stages (16 KB), together the 160 KB of
+// The stages: each of the 3 A stages (32 KB) holds two 32-deep k-tiles of
+// A; B keeps its 32-deep k-tiles in 4 stages (16 KB), together the 160 KB of
 // LDS. At an even k-tile t a wave copies the A stage of tiles t + 4, t + 5
 // (8 copies) and B of tile t + 3 (4); at an odd one only B (4). A rows in an
 // A stage are 8 chunks of 16 bytes XOR-swizzled by (row / 2) % 8: a fragment
 // read (16 rows at one chunk per quarter wave) covers all 64 banks once.
-// Requires K a multiple of 64.
+// Staging A 64 deep takes half the L2 requests for its bytes that 64-byte
+// halves would. Requires K a multiple of 64.
 // ---------------------------------------------------------------------------
 struct rv_g6_offs {
     unsigned a[4];  // [parity of the k-tile within its A stage][k16 step]
