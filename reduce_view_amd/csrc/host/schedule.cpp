@@ -368,16 +368,34 @@ static void attn_kernel(Ctx& c, const std::vector<int>& nodes, Kernel& k) {
             k.stores.push_back(st);
         }
     }
-    // Under the causal mask with long rows the keys are split into chunks of
-    // CK over workgroups: a 128-query block of 8192 keys becomes 8
-    // workgroups at CK = 1024, so the long blocks no longer set the time
-    // alone. Measured on 6 heads x 8192 tokens: 1.4x (head width 32) and
-    // 1.2x (64) faster; slower for width 128, for non-causal rows and for
-    // rows of 2048 keys, which keep one workgroup per query block.
+    // Keys are split into chunks of CK over workgroups when one workgroup
+    // per 128-query block leaves the chip's workgroup slots empty (256 CUs,
+    // each holding 4 of these workgroups at head width 32, 3 at 64, 2 at
+    // 128: one wave per SIMD each), CK the smallest of 1024, 2048 and 4096
+    // keeping the workgroups within twice the slots; under the causal mask
+    // a block's chunks stop at its last key. Measured (one workgroup per
+    // block against the chosen split): 6 x 8192 x 32 causal 1.4x faster,
+    // non-causal 1.2x; 2 x 8192 x 128 causal 2.1x; 6 x 8192 x 128 causal
+    // 1.27x; 4 x 4096 x 128 causal 1.8x; 16 x 2048 x 128 causal 5%.
     // RV_ATTN_CHUNK overrides (0: never split).
     const int64_t H = q[0], Tq = q[1], Tk = c.g.nodes[nd.src[1]].shape[1], D = q[2];
-    const bool split_pays = k.attn_causal && D <= 64 && std::min(Tk, Tq) >= 4096;
-    int64_t CK = env_int("RV_ATTN_CHUNK", split_pays ? 1024 : 0);
+    const int64_t nqb0 = (Tq + 127) / 128, slots = 256 * (D == 32 ? 4 : D == 64 ? 3 : 2);
+    auto workgroups = [&](int64_t ck) {
+        int64_t n = 0;
+        for (int64_t j = 0; j < nqb0; ++j) {
+            const int64_t kend = k.attn_causal ? std::min(Tk, std::min(Tq, 128 * (j + 1))) : Tk;
+            n += std::max<int64_t>(1, (kend + ck - 1) / ck);
+        }
+        return n * H;
+    };
+    int64_t CKd = 0;
+    if (H * nqb0 < slots)
+        for (int64_t ck : {1024, 2048, 4096})
+            if (workgroups(ck) <= 2 * slots || ck == 4096) {
+                CKd = ck;
+                break;
+            }
+    int64_t CK = env_int("RV_ATTN_CHUNK", (int)CKd);
     if (CK < 0) fail(RV_E_INVALID, "RV_ATTN_CHUNK must be 0 or positive");
     if (CK > 0) {
         CK = (CK + 127) / 128 * 128;

@@ -259,6 +259,21 @@ def test_attention_is_one_custom_kernel():
     assert prog.out_desc == [((3, 200, 64), "bf16"), ((3, 200, 1), "f32")]
 
 
+def test_attention_key_chunk_choice():
+    """Keys split over workgroups only when one workgroup per 128-query block
+    leaves the chip's slots empty (256 CUs x 4, 3, 2 workgroups at head width
+    32, 64, 128), in the smallest of 1024 / 2048 / 4096-key chunks that keeps
+    the workgroups within twice the slots; a row no longer than one chunk is
+    never split."""
+    cases = [((6, 8192, 32, True), 1024, 288), ((6, 8192, 32, False), 2048, 256), ((6, 8192, 128, True), 2048, 160),
+             ((6, 8192, 128, False), 4096, 128), ((16, 2048, 128, True), 1024, 24), ((96, 4096, 32, False), 0, 32),
+             ((2, 300, 64, True), 0, 3)]
+    for (h, t, d, causal), ck, grid in cases:
+        ks = rv.compile_spec(synth.attention(h, t, t, d, causal)).describe()["kernels"]
+        assert ks[0]["plan_detail"]["key_chunk"] == ck and ks[0]["grid"][:2] == [grid, h], (h, t, d, causal, ks[0])
+        assert [k["plan"] for k in ks] == (["attn_fwd", "attn_merge"] if ck else ["attn_fwd"])
+
+
 def test_attention_operand_view_is_materialised():
     # k given as a permuted View of a (H, D, Tk) buffer: copied to workspace first
     g = synth.Spec()
