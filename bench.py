@@ -472,7 +472,9 @@ def measure_configs(args, stream, timer, headline_ms):
             y_rows = _to_host(y_out[0])[rows, :, 0]
             del y_out
             gold = _json.load(open(os.path.join(ROOT, "tests", "golden", "gemm_relu2_sum_4096.json")))
-            depth = desc["kernels"][0]["plan_detail"]["partial_sum_depth"] + desc["kernels"][1]["plan_detail"]["sum_depth"]
+            mf = [kk for kk in desc["kernels"] if kk["class"] == "MFMA"][-1]
+            fo = [kk for kk in desc["kernels"] if kk["class"] == "FOLD"][0]
+            depth = mf["plan_detail"]["partial_sum_depth"] + fo["plan_detail"]["sum_depth"]
             extra = (rows, y_rows, gold, depth)
         scale = 1e-12 if unit == "TFLOP/s" else 1e-9
         achieved = work / (ms * 1e-3) * scale

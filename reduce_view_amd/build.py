@@ -59,6 +59,11 @@ def check_device_header(verbose: bool = False) -> None:
                 "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
                 "chk17(const unsigned short* a, const unsigned short* b, float* p) {\n"
                 "  rv_gemm_w6_bf16<true, 1, E, 1, true>(a, b, 0, 4104, 0, 4104, 4100, 4104, 4160, E{}, p, 4100, 4097); }\n"
+                "extern \"C\" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) "
+                "chk18(const unsigned short* a, const unsigned short* b, float* w) {\n"
+                "  rv_gemm_w6_bf16<false, 0, rv_slice_epi, 1, false, 3, 1, 8>(a, b, 0, 8192, 0, 8192, 1024, 1024, 1024, "
+                "rv_slice_epi{w, 1024}, nullptr, 1024, 1024); }\n"
+                "K chk19(const float* w, float* p) { rv_gemm_slices<1, E>(w, 8, 1048576, 1000, 1000, E{}, p); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(256) chk12(const unsigned short* q, const unsigned short* k, const unsigned short* v, float* o, "
                 "float* l) { rv_attn_fwd_bf16<32, true, false, 4>(q, k, v, o, l, 1000, 1000, 0.25f); }\n"
                 "extern \"C\" __global__ void __launch_bounds__(256) chk13(const unsigned short* q, const unsigned short* k, const unsigned short* v, "

@@ -286,7 +286,7 @@ struct Gen {
         // budget of more than 256 registers the compiler places them in the
         // accumulation registers and moves every score in and out)
         std::string occ;
-        if (k.cls == KClass::MFMA) occ = "__attribute__((amdgpu_waves_per_eu(1, 1))) ";
+        if (k.cls == KClass::MFMA && !k.mfma_slices) occ = "__attribute__((amdgpu_waves_per_eu(1, 1))) ";
         if (k.cls == KClass::ATTN && !k.attn_merge) {
             const int64_t D = k.domain[2];
             occ = fmt("__attribute__((amdgpu_waves_per_eu(%d))) ", D == 32 ? 4 : D == 64 ? 3 : 2);
@@ -2128,8 +2128,33 @@ std::string Gen::gen_gemm() {
     const Leaf& A = k.leaves[k.mfma_a];
     const Leaf& B = k.leaves[k.mfma_b];
     const bool kn = B.v.strides[1] == 1;
-    std::string pa = pname(A.loc, RV_BF16, false);
-    std::string pb = pname(B.loc, RV_BF16, false);
+    const int64_t Mt = k.domain[0], Nt = k.domain[1];
+    const int64_t M = k.mfma_ext[0], N = k.mfma_ext[1], K = k.mfma_ext[2];
+    const bool ragged = M % 256 || N % 256 || M != Mt || N != Nt;
+    const int64_t lda = A.v.strides[0];
+    const int64_t ldb = kn ? B.v.strides[2] : B.v.strides[1];
+    const int64_t plane = (Mt * Nt + 63) / 64 * 64;
+    const Kernel::GemmSched& g = k.gemm;
+    if (k.mfma_split > 1 && !k.mfma_slices) {
+        // slice s = blockIdx % S of the k-range: its operand offsets, depth
+        // and plane
+        const int S = k.mfma_split;
+        const int64_t Ks = K / S;
+        std::string pa = pname(A.loc, RV_BF16, false);
+        std::string pb = pname(B.loc, RV_BF16, false);
+        std::string pw = pname(Loc{2, k.slices_region}, RV_F32, true);
+        std::ostringstream b;
+        b << "  const long long s_ = (long long)(blockIdx.x % " << S << "u);\n";
+        b << "  const rv_slice_epi epi{" << pw << " + s_ * " << plane << "LL, " << Nt << "};\n";
+        b << "  rv_gemm_w6_bf16<" << (kn ? "true" : "false") << ", 0, rv_slice_epi, " << g.pin << ", "
+          << (ragged ? "true" : "false") << ", " << g.pe << ", " << g.po << ", " << S << ">(" << pa << ", " << pb
+          << ", " << A.v.offset << "LL + s_ * " << Ks << "LL, " << lda << "LL, " << B.v.offset << "LL + s_ * "
+          << Ks * (kn ? ldb : 1) << "LL, " << ldb << "LL, " << M << ", " << N << ", " << Ks << ", epi, nullptr, " << Mt
+          << ", " << Nt << ");\n";
+        return "@@BODY@@" + b.str();
+    }
+    std::string pa = k.mfma_slices ? std::string() : pname(A.loc, RV_BF16, false);
+    std::string pb = k.mfma_slices ? std::string() : pname(B.loc, RV_BF16, false);
     std::ostringstream f;  // functor body
     std::string sname = k.name + "_epi";
     std::vector<std::string> idx = {"m", "n", ""};
@@ -2179,12 +2204,13 @@ std::string Gen::gen_gemm() {
     b << "  const " << sname << " epi{";
     for (size_t i = 0; i < params.size(); ++i) b << (i ? ", " : "") << "p" << i;
     b << "};\n";
-    const int64_t Mt = k.domain[0], Nt = k.domain[1];
-    const int64_t M = k.mfma_ext[0], N = k.mfma_ext[1], K = k.mfma_ext[2];
-    const bool ragged = M % 256 || N % 256 || M != Mt || N != Nt;
-    const int64_t lda = A.v.strides[0];
-    const int64_t ldb = kn ? B.v.strides[2] : B.v.strides[1];
-    const Kernel::GemmSched& g = k.gemm;
+    if (k.mfma_slices) {
+        std::string pw = pname(Loc{2, k.slices_region}, RV_F32, false);
+        b << "  rv_gemm_slices<" << (k.mfma_partial ? 1 : 0) << ", " << sname << ">(" << pw << ", " << k.mfma_split
+          << ", " << plane << "LL, " << Mt << ", " << Nt << ", epi, "
+          << (k.mfma_partial ? partials : std::string("nullptr")) << ");\n";
+        return f.str() + "@@BODY@@" + b.str();
+    }
     b << "  rv_gemm_w6_bf16<" << (kn ? "true" : "false") << ", " << (k.mfma_partial ? 1 : 0) << ", " << sname << ", "
       << g.pin << ", " << (ragged ? "true" : "false") << ", " << g.pe << ", " << g.po << ">(" << pa << ", " << pb << ", ";
     b

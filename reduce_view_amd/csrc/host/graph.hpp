@@ -124,6 +124,14 @@ struct Kernel {
     // into workspace); the domain keeps the output's (M, N, K)
     int64_t mfma_ext[3] = {0, 0, 0};
     bool mfma_copied[2] = {false, false};
+    // split over k (mfma_split > 1 slices, kMfmaKStep-aligned): the slice
+    // kernel stores every slice's raw float32 accumulators, [slice][m][n] over
+    // the output's extents, in region slices_region; the kernel after it
+    // (mfma_slices, plan "gemm_slices") sums them in slice order and runs the
+    // epilogue
+    int mfma_split = 1;
+    bool mfma_slices = false;
+    int slices_region = -1;
     // the kernel's schedule (chosen at lowering, baked in at codegen): the
     // MFMA / LDS-read / copy interleaving, and the copies issued in an even
     // / odd k-tile's first k16 step

@@ -295,7 +295,7 @@ static void plan_fold_cells(Kernel& k, const Kernel& sp) {
 }
 
 static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
-    char buf[512];
+    char buf[1024];
     switch (k.cls) {
         case KClass::SPLIT:
             plan_split(p, k);
@@ -367,6 +367,29 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
             // tiles staged 32 deep in 4 or 5 stages took 112 us at best).
             const int64_t M = k.domain[0], N = k.domain[1];
             const int64_t Me = k.mfma_ext[0], Ne = k.mfma_ext[1], Ke = k.mfma_ext[2];
+            const int S = k.mfma_split;
+            if (k.mfma_slices) {
+                // the slices' fold: 4 consecutive cells a lane, each the S
+                // planes in slice order, then the epilogue; a partial adds a
+                // lane's 4 cells, 6 butterfly levels and 3 cross-wave
+                // additions (the slices' own sum is part of the contraction)
+                const int64_t cells = M * N;
+                k.plan = "gemm_slices";
+                k.grid[0] = (unsigned)((cells + 1023) / 1024);
+                k.block[0] = 256;
+                k.lds = 16;
+                k.n_partials = k.grid[0];
+                snprintf(buf, sizeof buf,
+                         "\"split_k\":%d,\"slices_region\":%d,\"plane\":%lld,\"cells_per_lane\":4,"
+                         "\"partial_sum_depth\":%d",
+                         S, k.slices_region, (long long)((cells + 63) / 64 * 64), 3 + 6 + 3);
+                k.plan_json = buf;
+                if (k.mfma_partial) {
+                    p.regions[k.partials_region].bytes = (size_t)k.n_partials * 4;
+                    k.stores[0].loc = Loc{2, k.partials_region};
+                }
+                return;
+            }
             const int pin = std::max(0, std::min(2, env_int("RV_GEMM_PIN", 1)));
             const int pe = std::max(0, std::min(12, env_int("RV_GEMM_W6_PE", 3)));
             const int po = std::max(0, std::min(4, env_int("RV_GEMM_W6_PO", 1)));
@@ -377,7 +400,7 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
             k.lds = 3 * 256 * 64 * 2 + 4 * 256 * 32 * 2;
             const int64_t tiles = ((Me + 255) / 256) * ((Ne + 255) / 256);
             if (tiles >= ((int64_t)1 << 31)) fail(RV_E_UNSUPPORTED_LAYOUT, "contraction of 2^31 or more output tiles");
-            k.grid[0] = (unsigned)tiles;
+            k.grid[0] = (unsigned)(tiles * S);
             k.block[0] = 256;
             k.n_partials = k.grid[0];
             const bool kn = k.leaves[k.mfma_b].v.strides[1] == 1;
@@ -393,10 +416,11 @@ static void plan_kernel(Program& p, Kernel& k, const Kernel* prev) {
                      "\"tile\":[256,256,32],\"waves\":4,\"wave_tiles\":[4,4],\"mfma\":\"v_mfma_f32_32x32x16_bf16\","
                      "\"b_layout\":\"%s\",\"xcd_remap\":8,\"partial_sum_depth\":%d,%s,"
                      "\"interleave\":%d,\"extent\":[%lld,%lld,%lld],\"ragged\":%s,"
-                     "\"copied\":{\"A\":%s,\"B\":%s},\"operand_leaves\":[%d,%d]",
+                     "\"copied\":{\"A\":%s,\"B\":%s},\"operand_leaves\":[%d,%d],\"split_k\":%d,"
+                     "\"slices_region\":%d",
                      kn ? "kn" : "nk", 256 - 1 + 6 + 3, stage_buf, pin, (long long)Me, (long long)Ne, (long long)Ke,
                      ragged ? "true" : "false", k.mfma_copied[0] ? "true" : "false", k.mfma_copied[1] ? "true" : "false",
-                     k.mfma_a, k.mfma_b);
+                     k.mfma_a, k.mfma_b, S, k.slices_region);
             k.plan_json = buf;
             if (k.mfma_partial) {
                 p.regions[k.partials_region].bytes = (size_t)k.n_partials * 4;

@@ -750,6 +750,31 @@ static void mfma_operands(Ctx& c, Kernel& k, std::vector<Kernel>& out) {
     k.mfma_ext[2] = Kp;
 }
 
+// Slices over k for a contraction whose output tiles leave most of the 256
+// CUs idle: S slices put S x tiles workgroups on the chip, at the cost of S
+// float32 accumulator planes written and read back. The count minimises a
+// time estimate: one workgroup's k-loop at a measured per-CU rate, plus, once
+// split, the second kernel's launch and the planes' traffic. Planes stay
+// within 32 MiB unless RV_GEMM_SPLITK forces a count (1: no split).
+static int mfma_split_count(const Kernel& k) {
+    const int64_t M = k.domain[0], N = k.domain[1];
+    const int64_t Me = k.mfma_ext[0], Ne = k.mfma_ext[1], Ke = k.mfma_ext[2];
+    const int64_t tiles = ((Me + 255) / 256) * ((Ne + 255) / 256);
+    auto fits = [&](int64_t S) { return tiles * S <= 256 && Ke % (kMfmaKStep * S) == 0 && Ke / S >= 4 * kMfmaKStep; };
+    const int forced = env_int("RV_GEMM_SPLITK", 0);
+    if (forced >= 1) return forced > 1 && (forced & (forced - 1)) == 0 && fits(forced) ? forced : 1;
+    auto fits_ws = [&](int64_t S) { return fits(S) && S * M * N * 4 <= ((int64_t)32 << 20); };
+    const double cu_flops = 7e12, plane_bw = 5e12, launch_us = 3.0;
+    auto est_us = [&](int64_t S) {
+        const double loop = 2.0 * 256 * 256 * (double)(Ke / S) / cu_flops * 1e6;
+        return S == 1 ? loop : loop + launch_us + (double)(S * M * N * 8) / plane_bw * 1e6;
+    };
+    int64_t best = 1;
+    for (int64_t S = 2; fits_ws(S); S *= 2)
+        if (est_us(S) < est_us(best)) best = S;
+    return (int)best;
+}
+
 static bool try_mfma(Ctx& c, int root, std::vector<Kernel>& out, int& partial_region) {
     const Node& rn = c.g.nodes[root];
     int y = -1, epi_root = -1;
@@ -821,6 +846,19 @@ static bool try_mfma(Ctx& c, int root, std::vector<Kernel>& out, int& partial_re
     for (size_t l = 0; l < k.leaves.size(); ++l)
         if ((int)l != la && (int)l != lb && k.leaves[l].v.strides[2] != 0) return false;
     mfma_operands(c, k, out);
+    const int S = mfma_split_count(k);
+    if (S > 1) {
+        // the slice kernel (operands in, raw planes out), then this one
+        // folding the planes into the epilogue
+        Kernel ks = k;
+        ks.mfma_split = S;
+        ks.slices_region = (int)c.p.regions.size();
+        c.p.regions.push_back(Region{0, (size_t)(S * ((M * N + 63) / 64 * 64)) * 4});
+        out.push_back(ks);
+        k.mfma_split = S;
+        k.mfma_slices = true;
+        k.slices_region = ks.slices_region;
+    }
     if (partial) {
         k.mfma_partial = true;
         Store s;

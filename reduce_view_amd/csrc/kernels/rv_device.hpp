@@ -380,7 +380,8 @@ __device__ __forceinline__ void rv_g6_copy(unsigned short* As, unsigned short* B
     }
 }
 
-template <bool B_KN, int MODE, class Epi, int PIN = 1, bool RAGGED = false, int PE = 3, int PO = 1>
+template <bool B_KN, int MODE, class Epi, int PIN = 1, bool RAGGED = false, int PE = 3, int PO = 1,
+          int SPLIT = 1>
 __device__ __forceinline__ void rv_gemm_w6_bf16(const unsigned short* __restrict__ A,
                                                 const unsigned short* __restrict__ B, long long a_off, long long lda,
                                                 long long b_off, long long ldb, int M, int N, int K, const Epi& epi,
@@ -402,8 +403,12 @@ __device__ __forceinline__ void rv_gemm_w6_bf16(const unsigned short* __restrict
     const int ntiles = tiles_m * tiles_n;
     int tm, tn;
     {
-        int bid = blockIdx.x;
-        if ((ntiles & 7) == 0 && (tiles_m & 3) == 0) {
+        // SPLIT k-slices: workgroup b takes tile b / SPLIT (in row-major
+        // order) of slice b % SPLIT, whose operand offsets and depth K the
+        // caller passes; consecutive workgroups run on different XCDs, so the
+        // workgroups on one XCD share their slices' A and B panels
+        const int bid = (int)blockIdx.x / SPLIT;
+        if (SPLIT == 1 && (ntiles & 7) == 0 && (tiles_m & 3) == 0) {
             const int sb = (bid & 7) * (ntiles >> 3) + (bid >> 3);  // XCD-contiguous
             const int group = sb / (4 * tiles_n), within = sb % (4 * tiles_n);
             tm = group * 4 + (within & 3);
@@ -545,6 +550,66 @@ __device__ __forceinline__ void rv_gemm_w6_bf16(const unsigned short* __restrict
                     part = part + v;
             }
         }
+    if (MODE == 1) {
+        part = rv_group_sum<64>(part);
+        if (lane == 0) lds_red[wave] = part;
+        __syncthreads();
+        if (tid == 0) partials[blockIdx.x] = ((lds_red[0] + lds_red[1]) + lds_red[2]) + lds_red[3];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// A contraction split over k: the workgroups of slice s store their float32
+// accumulators at [s][m][n] (rv_slice_epi, the raw epilogue; planes `plane`
+// floats apart, a multiple of 4), and rv_gemm_slices sums the S slices of
+// every output cell in slice order, then evaluates the epilogue: stored
+// (MODE 0) or summed per workgroup into partials[blockIdx.x] (MODE 1: a
+// lane's 4 cells in order, a butterfly over the wave, the 4 waves in order).
+// 256 lanes, 4 consecutive cells a lane.
+// ---------------------------------------------------------------------------
+struct rv_slice_epi {
+    float* ws;
+    int ld;
+    __device__ __forceinline__ float operator()(float acc, int, int) const { return acc; }
+    __device__ __forceinline__ void store(int m, int n, float v) const { ws[(long long)m * ld + n] = v; }
+};
+
+template <int MODE, class Epi>
+__device__ __forceinline__ void rv_gemm_slices(const float* __restrict__ ws, int S, long long plane, int Mt, int Nt,
+                                               const Epi& epi, float* __restrict__ partials) {
+    __shared__ float lds_red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const long long cells = (long long)Mt * Nt;
+    const long long c0 = ((long long)blockIdx.x * 256 + tid) * 4;
+    float y[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c0 + 4 <= cells) {
+        rv_pack<float, 4> v = rv_ldv<float, 4>(ws + c0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = v.v[j];
+        for (int s = 1; s < S; ++s) {
+            v = rv_ldv<float, 4>(ws + s * plane + c0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = y[j] + v.v[j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (c0 + j < cells) {
+                y[j] = ws[c0 + j];
+                for (int s = 1; s < S; ++s) y[j] = y[j] + ws[s * plane + c0 + j];
+            }
+    }
+    float part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (c0 + j >= cells) break;
+        const int m = (int)((c0 + j) / Nt), n = (int)((c0 + j) % Nt);
+        const float v = epi(y[j], m, n);
+        if (MODE == 0)
+            epi.store(m, n, v);
+        else
+            part = part + v;
+    }
     if (MODE == 1) {
         part = rv_group_sum<64>(part);
         if (lane == 0) lds_red[wave] = part;

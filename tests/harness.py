@@ -59,3 +59,12 @@ def report(name: str, err: np.ndarray, bound: np.ndarray) -> dict:
              max_err_over_bound=float(ratio.max(initial=0.0)))
     print("BOUND", r, flush=True)
     return r
+
+
+def contraction_sum_depth(desc: dict) -> int:
+    """Additions a relu^2-sum partial passes through after the contraction:
+    the epilogue's partial sum in the last MFMA kernel (the slice fold when
+    the contraction is split over k) plus the fold of the partials."""
+    mf = [k for k in desc["kernels"] if k["class"] == "MFMA"][-1]
+    fo = [k for k in desc["kernels"] if k["class"] == "FOLD"]
+    return mf["plan_detail"]["partial_sum_depth"] + (fo[0]["plan_detail"]["sum_depth"] if fo else 0)

@@ -73,6 +73,9 @@ def run_plan(desc: dict, inputs: list, out_specs: list) -> list:
         if k["plan"] == "empty":
             continue
         vals: dict[int, np.ndarray] = {}
+        if k["class"] == "MFMA" and k["plan"] == "gemm_w6" and k["plan_detail"]["split_k"] > 1:
+            _mfma_slices(k, dom, mem)
+            continue
         if k["class"] == "SCATTER":
             _scatter_step(k, dom, mem)
             continue
@@ -134,6 +137,15 @@ def _evaluate(k, dom, red, mem, vals, only=None):
             else:
                 c = v.astype(STORAGE[dt])
             vals[i] = np.broadcast_to(c.reshape((1,) * len(dom)), dom)
+        elif name == "MFMA_ACC" and k["plan"] == "gemm_slices":
+            # the k-slices' planes summed in slice order
+            pd = k["plan_detail"]
+            ws = mem({"kind": "workspace", "index": pd["slices_region"]}, "f32")
+            cells = dom[0] * dom[1]
+            acc = ws[:cells].copy()
+            for sl in range(1, pd["split_k"]):
+                acc = (acc + ws[sl * pd["plane"]: sl * pd["plane"] + cells]).astype(np.float32)
+            vals[i] = np.broadcast_to(acc.reshape(dom[0], dom[1], 1), dom)
         elif name == "MFMA_ACC":
             a_leaf = leaves[_mfma_leaf(k, "a")]
             b_leaf = leaves[_mfma_leaf(k, "b")]
@@ -221,6 +233,28 @@ def _scatter_step(k, dom, mem):
 def st_ex(k, st):
     """The op a store writes."""
     return st["ex"]
+
+
+def _mfma_slices(k, dom, mem):
+    """A contraction's k-slice kernel: slice s covers k in [s Ks, (s + 1) Ks)
+    of the padded depth (the cells past the output's depth are zero padding);
+    each slice's float32 accumulators, k in order, go to plane s of the
+    slices region ([slice][m][n], planes ``plane`` floats apart)."""
+    pd, leaves = k["plan_detail"], k["leaves"]
+    S, Ke = pd["split_k"], pd["extent"][2]
+    Ks = Ke // S
+    a_leaf = leaves[_mfma_leaf(k, "a")]
+    b_leaf = leaves[_mfma_leaf(k, "b")]
+    A = O.bf16_to_f32(_gather(mem(a_leaf["loc"], "bf16"), a_leaf["view"], dom))
+    B = O.bf16_to_f32(_gather(mem(b_leaf["loc"], "bf16"), b_leaf["view"], dom))
+    cells = dom[0] * dom[1]
+    plane = (cells + 63) // 64 * 64
+    ws = mem({"kind": "workspace", "index": pd["slices_region"]}, "f32", S * plane)
+    for sl in range(S):
+        acc = np.zeros(dom[:2], np.float32)
+        for kk in range(sl * Ks, min((sl + 1) * Ks, dom[2])):
+            acc = (acc + (A[:, :, kk] * B[:, :, kk]).astype(np.float32)).astype(np.float32)
+        ws[sl * plane: sl * plane + cells] = acc.ravel()
 
 
 def _mfma_leaf(k, which):

@@ -10,7 +10,7 @@ import pytest
 import oracle
 from oracle import interp
 from reduce_view_amd import synth
-from tests.harness import U, gamma, report, run, ulp32, ulp_bf16
+from tests.harness import U, contraction_sum_depth, gamma, report, run, ulp32, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -287,7 +287,7 @@ def test_gemm_relu2_sum(m, n, k):
     s_ref, = oracle.run(spec, inp)
     y = y_ref[:, :, 0].astype(np.float64)
     q = np.maximum(y, 0) ** 2
-    depth = desc["kernels"][0]["plan_detail"]["partial_sum_depth"] + desc["kernels"][1]["plan_detail"]["sum_depth"]
+    depth = contraction_sum_depth(desc)
     ds = (np.sum((2 * np.abs(y) * dy + dy ** 2) * (y > -dy)) + U * q.sum() + 4 * gamma(depth) * q.sum()
           + U * abs(float(s_ref.ravel()[0])))
     report(f"gemm_S_{m}x{n}x{k}", np.array([abs(float(s_gpu.ravel()[0]) - float(s_ref.ravel()[0]))]), np.array([ds]))
@@ -354,7 +354,7 @@ def test_gemm_full_size_sampled_rows_and_scalar():
     prog = _prog(synth.gemm_relu2_sum(m, n, k))
     desc = prog.describe()
     s_gpu, = run(prog, inp)
-    depth = desc["kernels"][0]["plan_detail"]["partial_sum_depth"] + desc["kernels"][1]["plan_detail"]["sum_depth"]
+    depth = contraction_sum_depth(desc)
     ds = gold["propagated_y_term"] + U * gold["sum_q"] + 4 * gamma(depth) * gold["sum_q"] + U * abs(gold["S"])
     e = abs(float(s_gpu.ravel()[0]) - gold["S"])
     report("gemm_full_S", np.array([e]), np.array([ds]))
@@ -460,6 +460,77 @@ def test_gemm_transposed_padded_operands_bit_exact():
     assert got.tobytes() == ref.tobytes()
 
 
+def _split_k(desc):
+    mf = [kk for kk in desc["kernels"] if kk["class"] == "MFMA"]
+    return mf[0]["plan_detail"]["split_k"], [kk["plan"] for kk in mf]
+
+
+# few output tiles over a deep k: the contraction is split into k-slices
+# whose raw planes a second kernel folds in slice order before the
+# epilogue; integer-valued operands are exact in any order. Ragged tiles,
+# copied operands, B stored [n][k], and forced slice counts.
+@pytest.mark.parametrize("m,n,k,bt,force", [(256, 512, 2048, False, None), (300, 520, 2048, False, None),
+                                            (256, 768, 1024, True, None), (40, 24, 1024, False, None),
+                                            (256, 512, 2048, False, "2"), (256, 256, 4096, True, "16"),
+                                            (1000, 700, 1536, False, "4")])
+def test_gemm_split_k_integer_bit_exact(monkeypatch, m, n, k, bt, force):
+    _case(f"gemm split-k int {m}x{n}x{k} bt={bt} force={force}")
+    if force:
+        monkeypatch.setenv("RV_GEMM_SPLITK", force)
+    from tests.test_lowering import _gemm_views
+    spec = _gemm_views(m, n, k, bt=bt)
+    prog = _prog(spec)
+    S, plans = _split_k(prog.describe())
+    assert plans == ["gemm_w6", "gemm_slices"] and S == (int(force) if force else S) and S > 1, (S, plans)
+    inp = synth.inputs_gemm_integer(m, n, k)
+    if bt:
+        inp = {"A": inp["A"], "B": np.ascontiguousarray(inp["B"].T)}
+    got, = run(prog, inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 512, 2048), (300, 520, 2048)])
+def test_gemm_split_k_relu2_sum_integer_bit_exact(m, n, k):
+    """The relu^2 + SUM epilogue on the slices' fold: its per-workgroup
+    partials and their fold, exact while the total stays below 2^24."""
+    _case(f"gemm split-k relu2 sum int {m}x{n}x{k}")
+    # sparse -1 / 0 / 1 operands keep the deep sums small
+    rng = np.random.default_rng(31)
+    inp = {"A": synth.to_bf16_bits(rng.choice([-1.0, 0.0, 1.0], (m, k), p=[0.05, 0.9, 0.05]).astype(np.float32)),
+           "B": synth.to_bf16_bits(rng.choice([-1.0, 0.0, 1.0], (k, n), p=[0.05, 0.9, 0.05]).astype(np.float32))}
+    yi = (interp.bf16_to_f32(inp["A"]).astype(np.int64) @ interp.bf16_to_f32(inp["B"]).astype(np.int64))
+    assert (np.maximum(yi, 0) ** 2).sum() < 2 ** 24
+    spec = synth.gemm_relu2_sum(m, n, k)
+    prog = _prog(spec)
+    desc = prog.describe()
+    assert _split_k(desc)[0] > 1 and [kk["class"] for kk in desc["kernels"]][-3:] == ["MFMA", "MFMA", "FOLD"]
+    got, = run(prog, inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
+def test_gemm_split_k_1024x1024x8192_sampled():
+    """1024 x 1024 x 8192 (16 output tiles, split over k) on random operands:
+    sampled rows, on both sides of a tile seam, within the contraction's
+    rounding bound against the oracle."""
+    _case("gemm split-k 1024x1024x8192")
+    m, n, k = 1024, 1024, 8192
+    inp = synth.inputs_gemm(m, n, k, seed=9)
+    prog = _prog(synth.gemm_bf16(m, n, k))
+    assert _split_k(prog.describe())[0] > 1
+    y_gpu, = run(prog, inp)
+    rows = [0, 255, 256, 1023]
+    sub = {"A": inp["A"][rows], "B": inp["B"]}
+    y_ref, = oracle.run(synth.gemm_bf16(len(rows), n, k), sub)
+    a = np.abs(interp.bf16_to_f32(sub["A"]).astype(np.float64))
+    b = np.abs(interp.bf16_to_f32(inp["B"]).astype(np.float64))
+    dy = 4 * gamma(k - 1) * (a @ b)
+    err = np.abs(y_gpu[rows, :, 0].astype(np.float64) - y_ref[:, :, 0])
+    report("gemm_split_y_rows", err, dy)
+    assert np.all(err <= dy)
+
+
 @pytest.mark.parametrize("m,n,k", [(520, 300, 96), (257, 129, 65)])
 def test_gemm_ragged_relu2_sum(m, n, k):
     """The relu^2 + SUM epilogue over ragged tiles: cells a shifted tile
@@ -481,9 +552,7 @@ def test_gemm_ragged_relu2_sum(m, n, k):
     assert np.all(np.abs(y_gpu - y_ref)[:, :, 0] <= dy)
     y = y_ref[:, :, 0].astype(np.float64)
     q = np.maximum(y, 0) ** 2
-    mf = [kk for kk in desc["kernels"] if kk["class"] == "MFMA"][0]
-    fo = [kk for kk in desc["kernels"] if kk["class"] == "FOLD"]
-    depth = mf["plan_detail"]["partial_sum_depth"] + (fo[0]["plan_detail"]["sum_depth"] if fo else 0)
+    depth = contraction_sum_depth(desc)
     ds = (np.sum((2 * np.abs(y) * dy + dy ** 2) * (y > -dy)) + U * q.sum() + 4 * gamma(depth) * q.sum()
           + U * abs(float(s_ref.ravel()[0])))
     e = abs(float(s_gpu.ravel()[0]) - float(s_ref.ravel()[0]))

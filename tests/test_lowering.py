@@ -77,6 +77,13 @@ CLASSES = {
     # operands as windows of wider buffers, each a View of a View: the two
     # compose into one View of the buffer, so nothing is copied first
     "gemm_windows": (lambda: _gemm_windows(), lambda: _gemm_windows_inputs(), ["MFMA"]),
+    # one output tile, k deep enough to split: k-slices (raw planes), then
+    # their fold with the epilogue; small integers make every sum exact, so
+    # the slices' order matches the oracle's bit for bit
+    "gemm_splitk": (lambda: synth.gemm_relu2_sum(40, 24, 1024), lambda: synth.inputs_gemm(40, 24, 1024),
+                    ["EW", "EW", "MFMA", "MFMA", "FOLD"]),
+    "gemm_y_splitk": (lambda: synth.gemm_bf16(40, 24, 512), lambda: synth.inputs_gemm_integer(40, 24, 512),
+                      ["EW", "EW", "MFMA", "MFMA"]),
     "gather": (lambda: synth.embedding_gather(50, 6, 30), lambda: synth.inputs_embedding(50, 6, 30), ["EW"]),
     "gather_general": (lambda: _gather_general(), lambda: _indexed_inputs(), ["EW", "EW"]),
     "scatter": (lambda: synth.embedding_scatter(20, 6, 100), lambda: synth.inputs_embedding(20, 6, 100),
@@ -145,7 +152,7 @@ def test_plan_interpreter_matches_oracle(name):
     ref = oracle.run(spec, inp)
     for g, r in zip(got, ref):
         assert g.shape == r.shape
-        if name in ("gemm", "gemm_copied"):
+        if name in ("gemm", "gemm_copied", "gemm_splitk"):
             # the plan folds the epilogue in one order, the oracle widens: close
             assert abs(float(g.ravel()[0]) - float(r.ravel()[0])) <= 1e-4 * abs(float(r.ravel()[0]))
         else:
