@@ -78,6 +78,10 @@ CASES = {
                           {("MFMA", "gemm_w6")}),
     "mfma_store_shifted": (lambda: synth.gemm_bf16(520, 264, 96), lambda: synth.inputs_gemm(520, 264, 96),
                            {("MFMA", "gemm_w6")}),
+    "mfma_split_fold": (lambda: synth.gemm_relu2_sum(300, 520, 2048), lambda: synth.inputs_gemm(300, 520, 2048),
+                        {("MFMA", "gemm_w6"), ("MFMA", "gemm_slices"), ("FOLD", "fold")}),
+    "mfma_split_store": (lambda: synth.gemm_bf16(40, 24, 1024), lambda: synth.inputs_gemm(40, 24, 1024),
+                         {("EW", "rowmajor"), ("MFMA", "gemm_w6"), ("MFMA", "gemm_slices")}),
     "attn": (lambda: synth.attention(2, 300, 333, 64, True),
              lambda: synth.inputs_attention(2, 300, 333, 64), {("ATTN", "attn_fwd")}),
     "attn_chunked": (lambda: synth.attention(1, 4100, 4100, 32, True),
