@@ -281,6 +281,38 @@ def test_attention_key_chunk_choice():
         assert [k["plan"] for k in ks] == (["attn_fwd", "attn_merge"] if ck else ["attn_fwd"])
 
 
+def test_contraction_split_choice(monkeypatch):
+    """A contraction splits over k only while its tiles leave CUs idle: the
+    slice count is the power of two with the smallest estimated time, every
+    slice at least 256 deep, at most 256 workgroups, planes within 32 MiB;
+    RV_GEMM_SPLITK forces a count that fits (1, or one that does not fit,
+    leaves the contraction whole)."""
+    def plan(m, n, k):
+        ks = rv.compile_spec(synth.gemm_bf16(m, n, k)).describe()["kernels"]
+        mf = [kk for kk in ks if kk["class"] == "MFMA"]
+        return mf[0]["plan_detail"]["split_k"], [kk["plan"] for kk in mf], mf[0]["grid"][0], ks
+    cases = [((4096, 4096, 4096), 1), ((4096, 4096, 1024), 1), ((1024, 1024, 8192), 8), ((512, 512, 16384), 32),
+             ((1024, 1024, 2048), 4), ((768, 768, 4096), 8), ((2048, 2048, 4096), 2), ((256, 256, 256), 1),
+             ((256, 256, 512), 2)]
+    for (m, n, k), want in cases:
+        S, plans, grid, ks = plan(m, n, k)
+        tiles = -(-m // 256) * -(-n // 256)
+        assert S == want and grid == tiles * S, ((m, n, k), S, grid)
+        assert plans == (["gemm_w6", "gemm_slices"] if S > 1 else ["gemm_w6"])
+        if S > 1:
+            pd = ks[-1]["plan_detail"]
+            assert pd["split_k"] == S and pd["plane"] % 64 == 0 and pd["plane"] >= m * n
+            assert pd["plane"] * S * 4 <= 32 << 20
+    monkeypatch.setenv("RV_GEMM_SPLITK", "16")
+    assert plan(1024, 1024, 8192)[0] == 16  # forced past the plane limit
+    monkeypatch.setenv("RV_GEMM_SPLITK", "64")
+    assert plan(1024, 1024, 8192)[0] == 1   # 16 tiles x 64 > 256 workgroups
+    monkeypatch.setenv("RV_GEMM_SPLITK", "3")
+    assert plan(1024, 1024, 8192)[0] == 1   # not a power of two
+    monkeypatch.setenv("RV_GEMM_SPLITK", "1")
+    assert plan(512, 512, 16384)[:2] == (1, ["gemm_w6"])
+
+
 def test_attention_operand_view_is_materialised():
     # k given as a permuted View of a (H, D, Tk) buffer: copied to workspace first
     g = synth.Spec()
