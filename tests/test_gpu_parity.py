@@ -531,6 +531,23 @@ def test_gemm_split_k_1024x1024x8192_sampled():
     assert np.all(err <= dy)
 
 
+# the generated epilogue reading operands of its own at (m, n), one through a
+# masked View, in place, over ragged tiles and on the slices' fold:
+# integer-valued, so y * s + c is exact and the bf16 rounding is the oracle's
+@pytest.mark.parametrize("m,n,k,plans", [(1024, 768, 256, ["gemm_w6"]), (300, 260, 192, ["gemm_w6"]),
+                                         (256, 512, 2048, ["gemm_w6", "gemm_slices"])])
+def test_gemm_epilogue_operands_bit_exact(m, n, k, plans):
+    _case(f"gemm epilogue operands {m}x{n}x{k}")
+    from tests.test_lowering import _gemm_affine, _gemm_affine_inputs
+    spec = _gemm_affine(m, n, k)
+    prog = _prog(spec)
+    assert [kk["plan"] for kk in prog.describe()["kernels"] if kk["class"] == "MFMA"] == plans
+    inp = _gemm_affine_inputs(m, n, k)
+    got, = run(prog, inp)
+    ref, = oracle.run(spec, inp)
+    assert got.tobytes() == ref.tobytes()
+
+
 @pytest.mark.parametrize("m,n,k", [(520, 300, 96), (257, 129, 65)])
 def test_gemm_ragged_relu2_sum(m, n, k):
     """The relu^2 + SUM epilogue over ragged tiles: cells a shifted tile

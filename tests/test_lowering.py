@@ -84,6 +84,10 @@ CLASSES = {
                     ["EW", "EW", "MFMA", "MFMA", "FOLD"]),
     "gemm_y_splitk": (lambda: synth.gemm_bf16(40, 24, 512), lambda: synth.inputs_gemm_integer(40, 24, 512),
                       ["EW", "EW", "MFMA", "MFMA"]),
+    # an epilogue reading operands of its own, one through a padding View
+    "gemm_affine": (lambda: _gemm_affine(40, 24, 64), lambda: _gemm_affine_inputs(40, 24, 64), ["EW", "EW", "MFMA"]),
+    "gemm_affine_splitk": (lambda: _gemm_affine(40, 24, 1024), lambda: _gemm_affine_inputs(40, 24, 1024),
+                           ["EW", "EW", "MFMA", "MFMA"]),
     "gather": (lambda: synth.embedding_gather(50, 6, 30), lambda: synth.inputs_embedding(50, 6, 30), ["EW"]),
     "gather_general": (lambda: _gather_general(), lambda: _indexed_inputs(), ["EW", "EW"]),
     "scatter": (lambda: synth.embedding_scatter(20, 6, 100), lambda: synth.inputs_embedding(20, 6, 100),
@@ -547,6 +551,32 @@ def test_split_off_switch(monkeypatch):
     monkeypatch.setenv("RV_SPLIT", "0")
     d = rv.compile_spec(synth.reduce((1 << 24,), (0,))).describe()
     assert [k["plan"] for k in d["kernels"]] == ["row_stream"]
+
+
+def _gemm_affine(m, n, k):
+    """z = CAST_bf16(y * s[n] + c'[m]) on the contraction y: a column scale and
+    a row bias read by the epilogue, the bias through a padding View (rows
+    before 3 and from m - 7 on read zero)."""
+    g = synth.Spec(f"gemm_affine_{m}x{n}x{k}")
+    a = g.buffer("A", (m, k), "bf16")
+    b = g.buffer("B", (k, n), "bf16")
+    sc = g.buffer("S", (n,), "f32")
+    c = g.buffer("C", (m - 10,), "f32")
+    a3 = g.cast(g.view(a, ("reshape", (m, 1, k)), ("expand", (m, n, k))), "f32")
+    b3 = g.cast(g.view(b, ("permute", (1, 0)), ("reshape", (1, n, k)), ("expand", (m, n, k))), "f32")
+    y = g.sum(g.mul(a3, b3), (2,))
+    sv = g.view(sc, ("reshape", (1, n, 1)), ("expand", (m, n, 1)))
+    cv = g.view(c, ("pad", ((3, 7),)), ("reshape", (m, 1, 1)), ("expand", (m, n, 1)))
+    g.output(g.cast(g.add(g.mul(y, sv), cv), "bf16"))
+    return g
+
+
+def _gemm_affine_inputs(m, n, k):
+    rng = np.random.default_rng(41)
+    inp = dict(synth.inputs_gemm_integer(m, n, k))
+    inp["S"] = rng.integers(-3, 4, n).astype(np.float32)
+    inp["C"] = rng.integers(-50, 51, m - 10).astype(np.float32)
+    return inp
 
 
 def _gemm_views(m, n, k, a_mv=(), b_mv=(), bt=False):
