@@ -13,7 +13,7 @@ classes it compiled to (checked), and its parity against the CPU oracle run
 in the CPU-baseline leg (max |err|, max bound, max err/bound).
 
 ``--workload`` times one other kernel alone instead (softmax, softmax_long,
-rmsnorm, rmsnorm_f16, rmsnorm_f64, chain_i8, layernorm, gemm, attention,
+rmsnorm, rmsnorm_f16, rmsnorm_f64, chain_i8, layernorm, gemm, gemm_zero, attention,
 gather, scatter, scatter_atomic, sum_full, sum_cols, matmul64, copy).
 
 Inputs are seeded, synthetic and already resident in HBM when timing starts;
@@ -109,6 +109,13 @@ def workloads():
                   "epilogue, full SUM to an fp32 scalar; A ~ N(0,1/64), B ~ N(0,1), seed 5"),
             programs=[("gemm_relu2_sum", synth.gemm_relu2_sum(4096, 4096, 4096), 2 * 4096 ** 3)],
             inputs=lambda seed: synth.inputs_gemm(4096, 4096, 4096, seed),
+            unit="TFLOP/s", dtype="bf16", bound="mfma", seed=5),
+        "gemm_zero": dict(
+            desc=("the gemm workload's program (bf16 4096x4096x4096 contraction, relu(y)^2, full SUM) on all-zero "
+                  "operands: the same kernels, loop and copies, without the matrix cores' data-dependent "
+                  "switching power; what the schedule reaches at the clock the chip holds without it"),
+            programs=[("gemm_relu2_sum_zero", synth.gemm_relu2_sum(4096, 4096, 4096), 2 * 4096 ** 3)],
+            inputs=lambda seed: {"A": np.zeros((4096, 4096), np.uint16), "B": np.zeros((4096, 4096), np.uint16)},
             unit="TFLOP/s", dtype="bf16", bound="mfma", seed=5),
         "attention": dict(
             desc=("fused attention forward (CUSTOM sdpa_fwd), 6 heads x 8192 tokens x 32, causal, bf16 q/k/v, "
@@ -361,7 +368,7 @@ def _cpu_baseline(wl, name, budget_s):
     ru0 = resource.getrusage(resource.RUSAGE_SELF)
     w0 = time.perf_counter()
     sample = ""
-    if name == "gemm":
+    if name in ("gemm", "gemm_zero"):
         rows = 16
         inp = synth.inputs_gemm(4096, 4096, 4096, 5)
         sub = {"A": inp["A"][:rows], "B": inp["B"]}
