@@ -493,6 +493,18 @@ def measure_configs(args, stream, timer, headline_ms):
                           "work_per_launch": work}}
         if name == "gemm_relu2_sum":
             e["note"] = "time per launch of the contraction and its fold (two kernels)"
+            # the same program on all-zero operands: same kernels and cycles,
+            # without the matrix cores' data-dependent switching power
+            zin = {k: _to_device(np.zeros_like(v)) for k, v in inputs.items() if k in prog.slots}
+            zgo = prog.prepare(zin, out, stream, ws)
+            reps = max(args.steps, 50, int(np.ceil(30.0 / max(ms, 1e-3))))
+            timer(lambda i: zgo(), reps)
+            zms = timer(lambda i: zgo(), reps)
+            zach = work / (zms * 1e-3) * scale
+            e["zero_operands"] = {"ms": round(zms, 5), "value": round(zach, 2), "frac": round(zach / peak, 4),
+                                  "note": ("all-zero A and B: the gap to the random-operand time is the clock the "
+                                           "matrix cores' switching power on random bf16 costs")}
+            del zin, zgo
         if bound == "latency":
             e["note"] = "48 KB of data: bound by launch latency, not a roofline"
         entries[name] = e
